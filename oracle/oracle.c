@@ -1,0 +1,466 @@
+/*
+ * oracle.c -- plain CPU oracle for speculative-decoding draft verification.
+ *
+ * TEST INFRASTRUCTURE. Only the test suite, the smoke check and the CPU-baseline
+ * leg of the benchmark load this file's library. The GPU library neither links
+ * nor calls it, and the two share no source, header, table or helper.
+ *
+ * Source of every rule below: the web page "大模型投机解码：Medusa、MTP、EAGLE、
+ * DFlash、DDTree 与 DSpark" (chzhyang.github.io), cited as [SD §n]:
+ *   [SD §1]  what speculative decoding guarantees: acceptance probability
+ *            alpha = min(1, p/q) (the displayed equation), everything after the
+ *            first rejection is dropped (the A B C D example), the correction
+ *            token comes from the normalised positive residual [p - q]+, an
+ *            extra token comes from p when every draft passes, greedy results
+ *            follow the target argmax, and temperature / truncation must be
+ *            folded into both p and q.
+ *   [SD §2]  cost model: A excludes the correction / extra token.
+ *   [SD §5 DDTree]  factorised score Q(u) = prod_i q_i(u_i) (displayed
+ *            equation), best-first selection of prefixes under a node budget,
+ *            a walk that follows the target's token and stops at the first node
+ *            with no matching child, whose target token becomes the extra token.
+ *   [SD §5 DSpark]  prefix survival s_j = prod_{i<=j} c_i and expected advance
+ *            1 + sum_{j<=k} s_j for verify length k.
+ *
+ * Plain scalar loops, fp64 arithmetic. Two quantities are computed in fp32
+ * because an fp32 rounding decides an ordering and both sides must take the
+ * same integer decision: the tree score Q (fp32 product, left to right in depth
+ * order) and the prefix survival s_j (fp32 running product). OpenMP is used only
+ * across independent sequences; it changes no arithmetic.
+ *
+ * Readings where the page leaves a step open (each one is listed in the design
+ * notes of the repository):
+ *   - uniforms: per sequence K+1 of them; u_i drives accept test i, u_k drives
+ *     the one final sample (correction or extra token);
+ *   - accept iff p(y) > 0 and u*q(y) <= p(y);
+ *   - inverse CDF in token-id order: the first j whose running mass exceeds
+ *     the scaled uniform;
+ *   - top-k keeps exactly k ids, ordered by (logit desc, id asc) on the raw
+ *     logits; NaN logits are never kept;
+ *   - T == 0 means greedy;
+ *   - a row whose kept logits have no finite maximum, or whose exponential sum
+ *     is not a finite positive number, is "non-finite": all its probabilities
+ *     are 0 and the sequence is flagged;
+ *   - tree ties: (Q desc, depth asc, rank tuple lexicographic asc);
+ *   - verify length: the smallest k maximising 1 + sum_{j<=k} s_j - cost*k.
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+
+#define ORC_BAD_TOKEN 1
+#define ORC_NONFINITE 2
+#define ORC_MARGIN_ACCEPT 1
+#define ORC_MARGIN_SAMPLE 2
+
+int orc_version(void) { return 1; }
+
+/* ------------------------------------------------------------------------ */
+/* Top-k ordering: (logit desc, id asc).                                     */
+/* ------------------------------------------------------------------------ */
+typedef struct { double x; int id; } orc_key;
+
+static int orc_cmp_desc(const void* a, const void* b) {
+    const orc_key* p = (const orc_key*)a;
+    const orc_key* q = (const orc_key*)b;
+    if (p->x > q->x) return -1;
+    if (p->x < q->x) return 1;
+    return (p->id < q->id) ? -1 : (p->id > q->id);
+}
+
+/*
+ * Distribution shaping [SD §1: temperature and truncation belong inside p and q].
+ * p[t] = exp(z_t - m) / sum_{s in S} exp(z_s - m) for t in S, 0 elsewhere, where
+ * z = x / T and S is the kept set (all ids, or the first top_k ids under
+ * (x desc, id asc), NaN never kept). Returns 1 for a valid row, 0 for a
+ * non-finite one (then p is all zeros).
+ */
+int orc_transform_row(const float* logits, int V, double T, int top_k, double* p) {
+    unsigned char* keep = (unsigned char*)calloc((size_t)V, 1);
+    if (top_k >= 1 && top_k < V) {
+        orc_key* ks = (orc_key*)malloc(sizeof(orc_key) * (size_t)V);
+        int n = 0;
+        for (int t = 0; t < V; ++t) {
+            double x = (double)logits[t];
+            if (isnan(x)) continue;
+            ks[n].x = x; ks[n].id = t; ++n;
+        }
+        qsort(ks, (size_t)n, sizeof(orc_key), orc_cmp_desc);
+        int take = n < top_k ? n : top_k;
+        for (int r = 0; r < take; ++r) keep[ks[r].id] = 1;
+        free(ks);
+    } else {
+        for (int t = 0; t < V; ++t) keep[t] = 1;
+    }
+    double m = -INFINITY;
+    int any = 0;
+    for (int t = 0; t < V; ++t) {
+        if (!keep[t]) continue;
+        double z = (double)logits[t] / T;
+        if (!any || z > m) m = z;           /* NaN never raises m */
+        any = 1;
+    }
+    for (int t = 0; t < V; ++t) p[t] = 0.0;
+    int valid = any && isfinite(m);
+    if (valid) {
+        double S = 0.0;
+        for (int t = 0; t < V; ++t) {
+            if (!keep[t]) continue;
+            double e = exp((double)logits[t] / T - m);
+            p[t] = e;
+            S += e;
+        }
+        if (!(isfinite(S) && S > 0.0)) {
+            valid = 0;
+        } else {
+            for (int t = 0; t < V; ++t) p[t] /= S;
+        }
+        if (!valid) for (int t = 0; t < V; ++t) p[t] = 0.0;
+    }
+    free(keep);
+    return valid;
+}
+
+/*
+ * Greedy choice [SD §1: greedy results follow the target argmax]: the lowest id
+ * among the maxima of the raw logits, NaN ignored; -1 if every entry is NaN.
+ */
+int orc_argmax_row(const float* logits, int V) {
+    int best = -1;
+    double bx = 0.0;
+    for (int t = 0; t < V; ++t) {
+        double x = (double)logits[t];
+        if (isnan(x)) continue;
+        if (best < 0 || x > bx) { best = t; bx = x; }
+    }
+    return best;
+}
+
+/*
+ * Inverse CDF in token-id order: the first j with sum_{t<=j} w_t > target
+ * (target >= 0, so that j always carries positive mass). If rounding leaves the
+ * total at or below target, the last j with w_j > 0.
+ * Returns -1 if w has no positive entry. *margin is set when target lies within
+ * tol of the running mass just before or just after the chosen token.
+ */
+static int orc_inverse_cdf(const double* w, int V, double target, double tol, int* margin) {
+    double C = 0.0;
+    int last_pos = -1;
+    for (int j = 0; j < V; ++j) {
+        double prev = C;
+        C += w[j];
+        if (w[j] > 0.0) last_pos = j;
+        if (C > target) {
+            if (fabs(target - prev) < tol || fabs(target - C) < tol) *margin = 1;
+            return j;
+        }
+    }
+    if (last_pos >= 0) *margin = 1;     /* reached only through rounding */
+    return last_pos;
+}
+
+/*
+ * Stochastic chain verification [SD §1].
+ *
+ * Layout: sequence b has k_b = cu[b+1]-cu[b] draft positions (k_b = K_max for
+ * every b when cu == NULL, with cu[b] = b*K_max). Draft row i of b is draft row
+ * cu[b]+i; target row i is target row cu[b]+b+i for i = 0..k_b (row k_b is the
+ * extra-token row). uniforms[cu[b]+b+i] drives accept test i; uniforms[cu[b]+b+k_b]
+ * drives the final sample.
+ *
+ * Per sequence:
+ *   acc_i = p_i(y_i) > 0 && u_i q_i(y_i) <= p_i(y_i)   (the ratio test alpha = min(1, p/q))
+ *   A     = first i with !acc_i, else k                 (nothing after a rejection is kept)
+ *   A < k: r = max(p_A - q_A, 0), R = sum r, next = inverse CDF of r at u_k R
+ *          (if R == 0 through rounding: inverse CDF of p_A at u_k)
+ *   A = k: next = inverse CDF of p_k at u_k             (the extra token)
+ * T == 0 selects the greedy rule of orc_verify_greedy.
+ *
+ * Outputs: A_out[b], next_out[b] (-1 if no token can be drawn), probs_out[2*r]
+ * = (p_i(y_i), q_i(y_i)) for every draft row r (NULL to skip), R_out[b] (0 for the
+ * extra token), status_out[b] (ORC_BAD_TOKEN / ORC_NONFINITE bits, raised only by
+ * positions 0..A and the row the final token is drawn from), margin_out[b]
+ * (ORC_MARGIN_* bits: an accept test with |u q - p| < margin_rel * p, or a
+ * sampled token whose scaled uniform lies within margin_rel * total of a CDF step).
+ */
+void orc_verify_chain(const float* target, const float* draft, const int32_t* tokens,
+                      const float* uniforms, const int32_t* cu, int B, int K_max, int V,
+                      double T, int top_k, double margin_rel,
+                      int32_t* A_out, int32_t* next_out, double* probs_out, double* R_out,
+                      int32_t* status_out, int32_t* margin_out, int nthreads) {
+    (void)nthreads;
+#pragma omp parallel for schedule(dynamic, 1) num_threads(nthreads > 0 ? nthreads : 1)
+    for (int b = 0; b < B; ++b) {
+        int d0 = cu ? cu[b] : b * K_max;
+        int k = cu ? cu[b + 1] - cu[b] : K_max;
+        int t0 = d0 + b;
+        int status = 0, margin = 0;
+        double* p = (double*)malloc(sizeof(double) * (size_t)V);
+        double* q = (double*)malloc(sizeof(double) * (size_t)V);
+        double* r = (double*)malloc(sizeof(double) * (size_t)V);
+        int A = k;
+        int next = -1;
+        double Rm = 0.0;
+
+        if (T == 0.0) {
+            /* greedy semantics */
+            for (int i = 0; i < k; ++i) {
+                int g = orc_argmax_row(target + (size_t)(t0 + i) * V, V);
+                int y = tokens[d0 + i];
+                if (probs_out) { probs_out[2 * (d0 + i)] = 0.0; probs_out[2 * (d0 + i) + 1] = 0.0; }
+                if (A == k) {
+                    if (y < 0 || y >= V) status |= ORC_BAD_TOKEN;
+                    if (g < 0) status |= ORC_NONFINITE;
+                    if (!(g >= 0 && y == g)) A = i;
+                }
+            }
+            next = orc_argmax_row(target + (size_t)(t0 + A) * V, V);
+            if (next < 0) status |= ORC_NONFINITE;
+        } else {
+            double u_fin = (double)uniforms[t0 + k];
+            int acc_done = 0;
+            for (int i = 0; i < k; ++i) {
+                int vp = orc_transform_row(target + (size_t)(t0 + i) * V, V, T, top_k, p);
+                int vq = orc_transform_row(draft + (size_t)(d0 + i) * V, V, T, top_k, q);
+                int y = tokens[d0 + i];
+                int yok = (y >= 0 && y < V);
+                double py = yok ? p[y] : 0.0, qy = yok ? q[y] : 0.0;
+                if (probs_out) { probs_out[2 * (d0 + i)] = py; probs_out[2 * (d0 + i) + 1] = qy; }
+                if (acc_done) continue;
+                double u = (double)uniforms[t0 + i];
+                int acc = vp && vq && yok && py > 0.0 && u * qy <= py;
+                if (!yok) status |= ORC_BAD_TOKEN;
+                if (!vp || !vq) status |= ORC_NONFINITE;
+                if (vp && vq && yok && py > 0.0 && fabs(u * qy - py) < margin_rel * py)
+                    margin |= ORC_MARGIN_ACCEPT;
+                if (!acc) {
+                    A = i;
+                    acc_done = 1;
+                    /* residual at the first rejection */
+                    double R = 0.0;
+                    if (!vp) {
+                        next = -1;
+                    } else {
+                        for (int t = 0; t < V; ++t) {
+                            double qt = vq ? q[t] : 0.0;
+                            double d = p[t] - qt;
+                            r[t] = d > 0.0 ? d : 0.0;
+                            R += r[t];
+                        }
+                        int mg = 0;
+                        if (R > 0.0) {
+                            next = orc_inverse_cdf(r, V, u_fin * R, margin_rel * R, &mg);
+                        } else {
+                            next = orc_inverse_cdf(p, V, u_fin, margin_rel, &mg);
+                        }
+                        if (mg) margin |= ORC_MARGIN_SAMPLE;
+                    }
+                    Rm = R;
+                }
+            }
+            if (A == k) {
+                int vp = orc_transform_row(target + (size_t)(t0 + k) * V, V, T, top_k, p);
+                if (!vp) {
+                    status |= ORC_NONFINITE;
+                    next = -1;
+                } else {
+                    int mg = 0;
+                    next = orc_inverse_cdf(p, V, u_fin, margin_rel, &mg);
+                    if (mg) margin |= ORC_MARGIN_SAMPLE;
+                }
+                Rm = 0.0;
+            }
+        }
+        A_out[b] = A;
+        next_out[b] = next;
+        if (R_out) R_out[b] = Rm;
+        if (status_out) status_out[b] = status;
+        if (margin_out) margin_out[b] = margin;
+        free(p); free(q); free(r);
+    }
+}
+
+/*
+ * Greedy chain verification [SD §1: greedy results follow the target argmax]:
+ * g_i = lowest-id argmax of target row i, acc_i = (y_i == g_i), A = first
+ * mismatch (else k), next = g_A. Same layout as orc_verify_chain. argmax_out
+ * (optional, [R_t]) receives g for every target row.
+ */
+void orc_verify_greedy(const float* target, const int32_t* tokens, const int32_t* cu,
+                       int B, int K_max, int V, int32_t* A_out, int32_t* next_out,
+                       int32_t* status_out, int32_t* argmax_out, int nthreads) {
+#pragma omp parallel for schedule(dynamic, 1) num_threads(nthreads > 0 ? nthreads : 1)
+    for (int b = 0; b < B; ++b) {
+        int d0 = cu ? cu[b] : b * K_max;
+        int k = cu ? cu[b + 1] - cu[b] : K_max;
+        int t0 = d0 + b;
+        int A = k, status = 0;
+        for (int i = 0; i <= k; ++i) {
+            int g = orc_argmax_row(target + (size_t)(t0 + i) * V, V);
+            if (argmax_out) argmax_out[t0 + i] = g;
+            if (i < k && A == k) {
+                int y = tokens[d0 + i];
+                if (y < 0 || y >= V) status |= ORC_BAD_TOKEN;
+                if (g < 0) status |= ORC_NONFINITE;
+                if (!(g >= 0 && y == g)) A = i;
+            }
+        }
+        int next = orc_argmax_row(target + (size_t)(t0 + A) * V, V);
+        if (next < 0) status |= ORC_NONFINITE;
+        A_out[b] = A;
+        next_out[b] = next;
+        if (status_out) status_out[b] = status;
+    }
+}
+
+/*
+ * DDTree candidate tree [SD §5 DDTree].
+ *
+ * marg: [B, K, V] per-depth draft marginals (q_1 .. q_K; row d is depth d+1).
+ * L_d = ids of row d sorted by (q desc, id asc), cut to N-1 entries. A prefix is
+ * a tuple of ranks (r_1..r_m), m <= K, naming tokens L_1[r_1] .. L_m[r_m]; its
+ * score is Q = fl32(...fl32(q_1(L_1[r_1]) * q_2(L_2[r_2]))... * q_m(L_m[r_m])).
+ * Order of prefixes: Q desc, then m asc, then the rank tuple lexicographically asc.
+ *
+ * The tree is the root (node 0: token -1, parent -1, depth 0, score 1, mask bit 0)
+ * plus the first N-1 prefixes in that order, numbered in that order. The order
+ * puts every parent before its children, so the plain way to list it is a
+ * frontier scan: repeatedly take the best unselected child of any selected node
+ * (no heap). anc_mask[n] has bit n and the bits of all ancestors.
+ * Returns nothing; n_nodes[b] is N unless the whole trie has fewer prefixes.
+ */
+void orc_build_tree(const float* marg, int B, int K, int V, int N,
+                    int32_t* node_token, int32_t* node_parent, int32_t* node_depth,
+                    float* node_score, uint64_t* node_anc, int32_t* n_nodes, int nthreads) {
+#pragma omp parallel for schedule(dynamic, 1) num_threads(nthreads > 0 ? nthreads : 1)
+    for (int b = 0; b < B; ++b) {
+        int W = (N - 1) < V ? (N - 1) : V;       /* candidates kept per depth */
+        int* L = (int*)malloc(sizeof(int) * (size_t)K * (size_t)(W > 0 ? W : 1));
+        orc_key* ks = (orc_key*)malloc(sizeof(orc_key) * (size_t)V);
+        for (int d = 0; d < K; ++d) {
+            const float* row = marg + ((size_t)b * K + d) * V;
+            for (int t = 0; t < V; ++t) { ks[t].x = (double)row[t]; ks[t].id = t; }
+            qsort(ks, (size_t)V, sizeof(orc_key), orc_cmp_desc);
+            for (int r = 0; r < W; ++r) L[d * W + r] = ks[r].id;
+        }
+        free(ks);
+        /* per node: rank tuple, score, child table */
+        int* ranks = (int*)calloc((size_t)N * (size_t)(K > 0 ? K : 1), sizeof(int));
+        int* child = (int*)malloc(sizeof(int) * (size_t)N * (size_t)(W > 0 ? W : 1));
+        for (int i = 0; i < N * (W > 0 ? W : 1); ++i) child[i] = -1;
+        int32_t* tok = node_token + (size_t)b * N;
+        int32_t* par = node_parent + (size_t)b * N;
+        int32_t* dep = node_depth + (size_t)b * N;
+        float* sc = node_score + (size_t)b * N;
+        uint64_t* an = node_anc + (size_t)b * N;
+        for (int n = 0; n < N; ++n) { tok[n] = -1; par[n] = -1; dep[n] = 0; sc[n] = 0.0f; an[n] = 0; }
+        tok[0] = -1; par[0] = -1; dep[0] = 0; sc[0] = 1.0f; an[0] = 1ull;
+        int n = 1;
+        while (n < N) {
+            int bs = -1, br = -1;
+            float bq = 0.0f;
+            for (int s = 0; s < n; ++s) {
+                int m = dep[s];
+                if (m >= K) continue;
+                for (int r = 0; r < W; ++r) {
+                    if (child[s * W + r] >= 0) continue;
+                    float qv = marg[((size_t)b * K + m) * V + L[m * W + r]];
+                    float Qc = sc[s] * qv;                  /* fp32 product */
+                    int better = 0;
+                    if (bs < 0) better = 1;
+                    else if (Qc > bq) better = 1;
+                    else if (Qc == bq) {
+                        int mc = m + 1, mb = dep[bs] + 1;
+                        if (mc < mb) better = 1;
+                        else if (mc == mb) {
+                            /* lexicographic compare of (ranks[s][0..m-1], r) vs (ranks[bs][..], br) */
+                            int cmp = 0;
+                            for (int j = 0; j < m && cmp == 0; ++j) {
+                                int a = ranks[s * K + j], c = ranks[bs * K + j];
+                                cmp = (a < c) ? -1 : (a > c);
+                            }
+                            if (cmp == 0) cmp = (r < br) ? -1 : (r > br);
+                            if (cmp < 0) better = 1;
+                        }
+                    }
+                    if (better) { bs = s; br = r; bq = Qc; }
+                }
+            }
+            if (bs < 0) break;                              /* trie exhausted */
+            int m = dep[bs];
+            for (int j = 0; j < m; ++j) ranks[n * K + j] = ranks[bs * K + j];
+            ranks[n * K + m] = br;
+            tok[n] = L[m * W + br];
+            par[n] = bs;
+            dep[n] = m + 1;
+            sc[n] = bq;
+            an[n] = an[bs] | (1ull << n);
+            child[bs * W + br] = n;
+            ++n;
+        }
+        n_nodes[b] = n;
+        free(L); free(ranks); free(child);
+    }
+}
+
+/*
+ * Tree walk [SD §5 DDTree]: from the root, take the target's token g = argmax
+ * of the current node's target row (lowest id on ties); if a child carries g,
+ * move there and record it; otherwise g is the extra token. target: [B, N, V],
+ * row n = node n. path_out: [B, N] accepted node ids, -1 padded.
+ */
+void orc_verify_tree(const float* target, const int32_t* node_token, const int32_t* node_parent,
+                     const int32_t* n_nodes, int B, int N, int V,
+                     int32_t* path_out, int32_t* A_out, int32_t* next_out, int nthreads) {
+#pragma omp parallel for schedule(dynamic, 1) num_threads(nthreads > 0 ? nthreads : 1)
+    for (int b = 0; b < B; ++b) {
+        const int32_t* tok = node_token + (size_t)b * N;
+        const int32_t* par = node_parent + (size_t)b * N;
+        int nn = n_nodes[b];
+        int32_t* path = path_out + (size_t)b * N;
+        for (int i = 0; i < N; ++i) path[i] = -1;
+        int node = 0, len = 0, next = -1;
+        for (;;) {
+            int g = orc_argmax_row(target + ((size_t)b * N + node) * V, V);
+            int found = -1;
+            for (int c = 1; c < nn && g >= 0; ++c)
+                if (par[c] == node && tok[c] == g) { found = c; break; }
+            if (found < 0) { next = g; break; }
+            path[len++] = found;
+            node = found;
+        }
+        A_out[b] = len;
+        next_out[b] = next;
+    }
+}
+
+/*
+ * Verify-length choice [SD §5 DSpark]: s_0 = 1, s_j = fl32(s_{j-1} * c_j);
+ * k* = the smallest k in [0, K] maximising f(k) = 1 + sum_{j<=k} s_j - cost*k
+ * (f in fp64 over the fp32 s_j); expected advance 1 + sum_{j<=k*} s_j;
+ * cu_sel = exclusive prefix sum of k* ([B+1], optional). margin_out[b] = 1 when
+ * some |s_j - cost| < 1e-6.
+ */
+void orc_select_len(const float* conf, int B, int K, float cost, int32_t* k_sel,
+                    double* adv_out, int32_t* cu_sel, int32_t* margin_out) {
+    for (int b = 0; b < B; ++b) {
+        float s = 1.0f;
+        double sum = 0.0, best_f = 1.0, best_sum = 0.0;
+        int best_k = 0, margin = 0;
+        for (int j = 1; j <= K; ++j) {
+            s = s * conf[(size_t)b * K + (j - 1)];
+            sum += (double)s;
+            double f = 1.0 + sum - (double)cost * (double)j;
+            if (f > best_f) { best_f = f; best_k = j; best_sum = sum; }
+            if (fabs((double)s - (double)cost) < 1e-6) margin = 1;
+        }
+        k_sel[b] = best_k;
+        if (adv_out) adv_out[b] = 1.0 + best_sum;
+        if (margin_out) margin_out[b] = margin;
+    }
+    if (cu_sel) {
+        cu_sel[0] = 0;
+        for (int b = 0; b < B; ++b) cu_sel[b + 1] = cu_sel[b] + k_sel[b];
+    }
+}

@@ -1,0 +1,562 @@
+"""Pins of the CPU oracle to facts the page and the mathematics fix.
+
+Page: chzhyang.github.io, "大模型投机解码：Medusa、MTP、EAGLE、DFlash、DDTree 与 DSpark",
+cited as [SD §n]. Each test names the fact it checks. None of them re-types the
+oracle's own formula: they use a worked example, closed forms, distribution tests,
+library routines for special cases and brute force on tiny inputs.
+"""
+import itertools
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+from scipy import special, stats
+
+import oracle
+
+GOLD = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def logits_of(probs):
+    with np.errstate(divide="ignore"):
+        return np.log(np.asarray(probs, dtype=np.float64)).astype(np.float32)
+
+
+def sample_from(rng, probs, n):
+    """n iid draws from a discrete distribution (test-side sampler)."""
+    c = np.cumsum(np.asarray(probs, dtype=np.float64))
+    c /= c[-1]
+    return np.minimum(np.searchsorted(c, rng.random(n), side="right"), len(c) - 1).astype(np.int32)
+
+
+def grid_u(rng, shape):
+    return (rng.integers(0, 1 << 24, size=shape) / float(1 << 24)).astype(np.float32)
+
+
+# --------------------------------------------------------------------------
+# Distribution shaping: special cases that reduce to a library routine.
+# --------------------------------------------------------------------------
+
+def test_transform_matches_scipy_softmax():
+    rng = np.random.default_rng(7)
+    for T in (1.0, 0.7, 2.5):
+        x = (rng.standard_normal(257) * 3).astype(np.float32)
+        ok, p = oracle.transform_row(x, T)
+        ref = special.softmax(x.astype(np.float64) / np.float64(np.float32(T)))
+        assert ok
+        np.testing.assert_allclose(p, ref, rtol=1e-12, atol=0)
+
+
+def test_transform_topk_keeps_exactly_k_lowest_id_on_ties():
+    # ids 3, 5, 8 tie at the kth value; k = 4 keeps the best (id 1) and 3, 5, 8 ... then
+    # with k = 3 only ids 1, 3, 5 survive (lower ids win the tie).
+    x = np.full(10, -1.0, np.float32)
+    x[1] = 5.0
+    x[[3, 5, 8]] = 2.0
+    ok, p = oracle.transform_row(x, 1.0, top_k=3)
+    assert ok
+    assert set(np.nonzero(p)[0].tolist()) == {1, 3, 5}
+    ref = special.softmax(np.array([5.0, 2.0, 2.0]))
+    np.testing.assert_allclose(p[[1, 3, 5]], ref, rtol=1e-12)
+    # top_k = 1 is one-hot at the lowest-id maximum
+    y = np.array([0.0, 3.0, 1.0, 3.0], np.float32)
+    ok, p = oracle.transform_row(y, 0.3, top_k=1)
+    assert ok and p.tolist() == [0.0, 1.0, 0.0, 0.0]
+    # top_k >= V and top_k == 0 are both "off"
+    ok0, p0 = oracle.transform_row(y, 0.3, top_k=0)
+    ok1, p1 = oracle.transform_row(y, 0.3, top_k=4)
+    np.testing.assert_array_equal(p0, p1)
+    np.testing.assert_allclose(p0, special.softmax(y.astype(np.float64) / np.float64(np.float32(0.3))), rtol=1e-12)
+
+
+def test_transform_neg_inf_and_nonfinite_rows():
+    x = np.array([-np.inf, 0.0, -np.inf, 0.0], np.float32)
+    ok, p = oracle.transform_row(x, 1.0)
+    assert ok and p.tolist() == [0.0, 0.5, 0.0, 0.5]
+    for bad in ([-np.inf] * 4, [0.0, np.nan, 1.0, 2.0], [0.0, np.inf, 1.0, 2.0]):
+        ok, p = oracle.transform_row(np.array(bad, np.float32), 1.0)
+        assert not ok and not p.any()
+    # top-k never keeps NaN: a NaN outside the kept set leaves the row valid
+    ok, p = oracle.transform_row(np.array([0.0, np.nan, 1.0, 2.0], np.float32), 1.0, top_k=2)
+    assert ok
+    np.testing.assert_allclose(p, [0, 0, *special.softmax([1.0, 2.0])], rtol=1e-12)
+
+
+def test_argmax_lowest_id_and_nan():
+    assert oracle.argmax_row(np.array([1, 4, 4, 2], np.float32)) == 1
+    assert oracle.argmax_row(np.array([np.nan, -np.inf, -np.inf], np.float32)) == 1
+    assert oracle.argmax_row(np.array([np.nan, np.nan], np.float32)) == -1
+    rng = np.random.default_rng(3)
+    x = rng.standard_normal(1000).astype(np.float32)
+    assert oracle.argmax_row(x) == int(np.argmax(x))
+
+
+# --------------------------------------------------------------------------
+# [SD §1] worked example: A B C D -> A B R.
+# --------------------------------------------------------------------------
+
+def test_worked_example_golden():
+    g = json.load(open(os.path.join(GOLD, "worked_example.json")))
+    V = g["V"]
+    tgt = np.stack([logits_of(r) for r in g["target_probs"]])
+    dft = np.stack([logits_of(r) for r in g["draft_probs"]])
+    y = np.array(g["draft_tokens"], np.int32)
+    for u in g["uniform_sets"]:
+        out = oracle.verify_chain(tgt, dft, y, np.array(u, np.float32), None, 1, len(y), V, 1.0)
+        A, nxt = int(out["A"][0]), int(out["next"][0])
+        committed = y[:A].tolist() + [nxt]
+        assert A == g["expected"]["accepted_len"]
+        assert nxt == g["expected"]["next_token"]
+        assert committed == g["expected"]["committed"]
+        assert 3 not in committed          # D is never kept
+        assert out["status"][0] == 0
+
+
+def test_truncation_property_random():
+    """Nothing after the first rejection is used: changing the rows and the
+    tokens after position A changes neither A nor the final token."""
+    rng = np.random.default_rng(11)
+    B, K, V = 400, 5, 12
+    tgt = (rng.standard_normal((B * (K + 1), V)) * 2).astype(np.float32)
+    dft = (rng.standard_normal((B * K, V)) * 2).astype(np.float32)
+    y = rng.integers(0, V, B * K).astype(np.int32)
+    u = grid_u(rng, B * (K + 1))
+    out = oracle.verify_chain(tgt, dft, y, u, None, B, K, V, 1.0)
+    tgt2, dft2, y2 = tgt.copy(), dft.copy(), y.copy()
+    for b in range(B):
+        A = int(out["A"][b])
+        if A < K:
+            # scramble every later draft position (rows A+1.., tokens A+1..) and later target rows
+            for i in range(A + 1, K):
+                dft2[b * K + i] = rng.standard_normal(V) * 5
+                y2[b * K + i] = rng.integers(0, V)
+            for i in range(A + 1, K + 1):
+                tgt2[b * (K + 1) + i] = rng.standard_normal(V) * 5
+    out2 = oracle.verify_chain(tgt2, dft2, y2, u, None, B, K, V, 1.0)
+    np.testing.assert_array_equal(out["A"], out2["A"])
+    np.testing.assert_array_equal(out["next"], out2["next"])
+    assert (out["A"] < K).any() and (out["A"] == K).any()
+
+
+# --------------------------------------------------------------------------
+# [SD §1] distribution-identical sampling: chi-square on tiny vocabularies.
+# --------------------------------------------------------------------------
+
+def _chi2_ok(obs, expected_p, n, pmin=1e-3):
+    expected_p = np.asarray(expected_p, dtype=np.float64)
+    zero = expected_p == 0
+    assert obs[zero].sum() == 0, "a zero-probability token was emitted"
+    e = expected_p[~zero] * n
+    o = obs[~zero]
+    if len(o) < 2:
+        return True
+    stat, pv = stats.chisquare(o, e)
+    return pv >= pmin
+
+
+CHI_CASES = {
+    # name: (p rows [K+1], q rows [K])
+    "q_equals_p": ([[.1, .2, .3, .4], [.25, .25, .25, .25], [.7, .1, .1, .1], [.4, .3, .2, .1]],
+                   [[.1, .2, .3, .4], [.25, .25, .25, .25], [.7, .1, .1, .1]]),
+    "q_uniform": ([[.05, .15, .5, .3, 0, 0], [.6, .1, .1, .1, .05, .05], [0, 0, 0, .5, .5, 0], [.3, .3, .1, .1, .1, .1]],
+                  [[1 / 6] * 6, [1 / 6] * 6, [1 / 6] * 6]),
+    "q_one_hot": ([[.2, .3, .5], [.5, .25, .25], [.1, .1, .8], [.3, .3, .4]],
+                  [[0, 1, 0], [1, 0, 0], [0, 0, 1]]),
+    "disjoint_support": ([[.5, .5, 0, 0], [0, .2, .8, 0], [.25, .25, .25, .25], [.1, .2, .3, .4]],
+                         [[0, 0, .5, .5], [.9, 0, 0, .1], [.25, .25, .25, .25]]),
+    "disjoint_later": ([[.4, .3, .2, .1], [0, .2, .8, 0], [.25, .25, .25, .25], [.1, .2, .3, .4]],
+                       [[.1, .2, .3, .4], [.9, 0, 0, .1], [.25, .25, .25, .25]]),
+    "zeros_both_sides": ([[0, .3, .7, 0, 0, 0, 0, 0], [.1, 0, 0, .4, .5, 0, 0, 0], [0, 0, 0, 0, 0, 0, .5, .5],
+                          [.125] * 8],
+                         [[.5, .5, 0, 0, 0, 0, 0, 0], [0, 0, .2, .3, .5, 0, 0, 0], [0, 0, 0, 0, 0, .2, .3, .5]]),
+}
+
+
+@pytest.mark.parametrize("name", sorted(CHI_CASES))
+def test_chi_square_outputs_follow_target(name):
+    P, Q = CHI_CASES[name]
+    K = len(Q)
+    V = len(P[0])
+    n = 400_000
+    rng = np.random.default_rng(abs(hash(name)) % (1 << 31))
+    tgt_row = np.stack([logits_of(r) for r in P])
+    dft_row = np.stack([logits_of(r) for r in Q])
+    tgt = np.tile(tgt_row, (n, 1))
+    dft = np.tile(dft_row, (n, 1))
+    y = np.stack([sample_from(rng, Q[i], n) for i in range(K)], axis=1).reshape(-1)
+    u = grid_u(rng, n * (K + 1))
+    out = oracle.verify_chain(tgt, dft, y, u, None, n, K, V, 1.0, want_probs=False)
+    A, nxt = out["A"], out["next"]
+    yk = y.reshape(n, K)
+    assert (out["status"] == 0).all()
+    # token emitted at position j among trials that reach j, j = 0..K
+    tested = 0
+    for j in range(K + 1):
+        reach = A >= j
+        if reach.sum() < 2000:
+            continue                    # e.g. disjoint supports never pass position 0
+        tok = np.where(A[reach] > j, yk[reach][:, j] if j < K else -1, nxt[reach])
+        obs = np.bincount(tok, minlength=V)
+        assert _chi2_ok(obs, P[j], int(reach.sum())), f"position {j}"
+        tested += 1
+    assert tested >= 1
+    # Given that position 1 is reached, the token there follows p1 whatever token
+    # was committed at position 0: expected[a, b] = #(t0 = a, reached) * p1(b).
+    reach = A >= 1
+    if reach.sum() < 2000:
+        return
+    t0 = yk[reach][:, 0]
+    t1 = np.where(A[reach] > 1, yk[reach][:, 1], nxt[reach])
+    obs = np.bincount(t0 * V + t1, minlength=V * V).reshape(V, V)
+    n_a = obs.sum(1)
+    for a in range(V):
+        if n_a[a] >= 2000:
+            assert _chi2_ok(obs[a], P[1], int(n_a[a])), f"t1 given t0={a}"
+
+
+def test_chi_square_detects_a_planted_mistake():
+    """Sanity of the test itself: drawing the correction with the accept test's
+    uniform (u_A instead of u_k) must fail the same chi-square check."""
+    P, Q = CHI_CASES["q_uniform"]
+    K, V, n = len(Q), len(P[0]), 400_000
+    rng = np.random.default_rng(5)
+    tgt = np.tile(np.stack([logits_of(r) for r in P]), (n, 1))
+    dft = np.tile(np.stack([logits_of(r) for r in Q]), (n, 1))
+    y = np.stack([sample_from(rng, Q[i], n) for i in range(K)], axis=1).reshape(-1)
+    u = grid_u(rng, (n, K + 1))
+    out = oracle.verify_chain(tgt, dft, y, u.reshape(-1), None, n, K, V, 1.0, want_probs=False)
+    A = out["A"]
+    # re-run with u_k replaced by u_A for the rejected trials (the planted mistake)
+    u_bad = u.copy()
+    rej = A < K
+    u_bad[rej, K] = u[rej, A[rej]]
+    bad = oracle.verify_chain(tgt, dft, y, u_bad.reshape(-1), None, n, K, V, 1.0, want_probs=False)
+    j = 0
+    reach = bad["A"] >= j
+    tok = np.where(bad["A"][reach] > j, y.reshape(n, K)[reach][:, j], bad["next"][reach])
+    assert not _chi2_ok(np.bincount(tok, minlength=V), P[j], int(reach.sum()))
+
+
+def test_special_case_q_equals_p_accepts_everything():
+    rng = np.random.default_rng(2)
+    B, K, V = 300, 4, 16
+    D = (rng.standard_normal((B, K + 1, V)) * 2).astype(np.float32)
+    tgt = D.reshape(-1, V)
+    dft = D[:, :K].reshape(-1, V)
+    y = rng.integers(0, V, B * K).astype(np.int32)
+    u = grid_u(rng, B * (K + 1))
+    out = oracle.verify_chain(tgt, dft, y, u, None, B, K, V, 0.8)
+    assert (out["A"] == K).all()
+    assert (out["R"] == 0).all()
+
+
+def test_special_case_one_hot_draft():
+    """q one-hot at y: acceptance probability p(y); the correction follows
+    p(. | t != y)."""
+    p = np.array([.1, .35, .2, .05, .3])
+    V, n, yv = 5, 300_000, 1
+    q = np.zeros(V); q[yv] = 1
+    rng = np.random.default_rng(8)
+    tgt = np.tile(np.stack([logits_of(p), logits_of(p)]), (n, 1))
+    dft = np.tile(logits_of(q)[None], (n, 1))
+    y = np.full(n, yv, np.int32)
+    u = grid_u(rng, 2 * n)
+    out = oracle.verify_chain(tgt, dft, y, u, None, n, 1, V, 1.0, want_probs=False)
+    acc = (out["A"] == 1).mean()
+    assert abs(acc - p[yv]) < 4 * math.sqrt(p[yv] * (1 - p[yv]) / n)
+    rej = out["A"] == 0
+    cond = p.copy(); cond[yv] = 0; cond /= cond.sum()
+    assert _chi2_ok(np.bincount(out["next"][rej], minlength=V), cond, int(rej.sum()))
+
+
+def test_special_case_k0_draws_from_row0():
+    p = np.array([.5, .125, .125, .25])
+    n, V = 200_000, 4
+    rng = np.random.default_rng(9)
+    tgt = np.tile(logits_of(p)[None], (n, 1))
+    cu = np.zeros(n + 1, np.int32)
+    out = oracle.verify_chain(tgt, np.zeros((0, V), np.float32), np.zeros(0, np.int32),
+                              grid_u(rng, n), cu, n, 0, V, 1.0, want_probs=False)
+    assert (out["A"] == 0).all()
+    assert _chi2_ok(np.bincount(out["next"], minlength=V), p, n)
+
+
+def test_margin_flags():
+    # p(y) = 0.5, q(y) = 1.0, u = 0.5 exactly: u*q == p -> accepted, flagged as a margin case
+    V = 2
+    tgt = np.stack([logits_of([.5, .5]), logits_of([.5, .5])])
+    dft = logits_of([1.0, 0.0])[None]
+    out = oracle.verify_chain(tgt, dft, np.array([0], np.int32), np.array([0.5, 0.3], np.float32),
+                              None, 1, 1, V, 1.0)
+    assert out["A"][0] == 1 and out["margin"][0] & oracle.MARGIN_ACCEPT
+    out = oracle.verify_chain(tgt, dft, np.array([0], np.int32), np.array([0.25, 0.3], np.float32),
+                              None, 1, 1, V, 1.0)
+    assert out["A"][0] == 1 and out["margin"][0] == 0
+    # the extra-token draw at u = 0.5 sits exactly on the CDF step between ids 0 and 1
+    out = oracle.verify_chain(tgt, dft, np.array([0], np.int32), np.array([0.25, 0.5], np.float32),
+                              None, 1, 1, V, 1.0)
+    assert out["next"][0] == 1 and out["margin"][0] & oracle.MARGIN_SAMPLE
+
+
+def test_bad_token_and_nonfinite_rows():
+    V = 4
+    tgt = np.zeros((3, V), np.float32)
+    dft = np.zeros((2, V), np.float32)
+    out = oracle.verify_chain(tgt, dft, np.array([7, 0], np.int32), np.zeros(3, np.float32),
+                              None, 1, 2, V, 1.0)
+    assert out["A"][0] == 0 and out["status"][0] == oracle.BAD_TOKEN
+    # residual at a bad token: r = max(p - q, 0) with p == q uniform -> R = 0 -> drawn from p
+    assert 0 <= out["next"][0] < V
+    tgt[1] = np.nan
+    out = oracle.verify_chain(tgt, dft, np.array([1, 1], np.int32), np.zeros(3, np.float32),
+                              None, 1, 2, V, 1.0)
+    assert out["A"][0] == 1 and out["status"][0] == oracle.NONFINITE and out["next"][0] == -1
+    # a non-finite row after the first rejection is not reported
+    tgt2 = np.zeros((3, V), np.float32); tgt2[2] = np.nan
+    dft2 = np.zeros((2, V), np.float32); dft2[0, 0] = 10.0   # q0 peaks at 0, p0 uniform
+    u = np.array([0.99999994, 0, 0], np.float32)
+    out = oracle.verify_chain(tgt2, dft2, np.array([0, 1], np.int32), u, None, 1, 2, V, 1.0)
+    assert out["A"][0] == 0 and out["status"][0] == 0
+
+
+# --------------------------------------------------------------------------
+# [SD §1] greedy: T = 0 is the argmax rule; tiny T reaches it too.
+# --------------------------------------------------------------------------
+
+def test_greedy_equivalence_T0_and_tiny_T():
+    rng = np.random.default_rng(4)
+    B, K, V = 200, 4, 64
+    # tie-free rows with min gap delta = 1/64 (distinct multiples of delta)
+    delta = 1.0 / 64
+    perm = np.stack([rng.permutation(V) for _ in range(B * (K + 1))])
+    tgt = (perm * delta).astype(np.float32)
+    dperm = np.stack([rng.permutation(V) for _ in range(B * K)])
+    dft = (dperm * delta).astype(np.float32)
+    g = np.argmax(tgt, axis=1).reshape(B, K + 1)
+    take = rng.random((B, K)) < 0.6
+    y = np.where(take, g[:, :K], rng.integers(0, V, (B, K))).astype(np.int32).reshape(-1)
+    u = grid_u(rng, B * (K + 1))
+    ref = oracle.verify_greedy(tgt, y, None, B, K, V)
+    # the argmax rule by hand
+    yk = y.reshape(B, K)
+    for b in range(B):
+        A = next((i for i in range(K) if yk[b, i] != g[b, i]), K)
+        assert ref["A"][b] == A and ref["next"][b] == g[b, A]
+    t0 = oracle.verify_chain(tgt, dft, y, u, None, B, K, V, 0.0)
+    np.testing.assert_array_equal(t0["A"], ref["A"])
+    np.testing.assert_array_equal(t0["next"], ref["next"])
+    tiny = np.float32(delta / 800)
+    tt = oracle.verify_chain(tgt, dft, y, u, None, B, K, V, float(tiny))
+    np.testing.assert_array_equal(tt["A"], ref["A"])
+    np.testing.assert_array_equal(tt["next"], ref["next"])
+
+
+# --------------------------------------------------------------------------
+# [SD §5 DSpark] prefix survival and expected advance.
+# --------------------------------------------------------------------------
+
+def test_expected_advance_closed_form_matches_monte_carlo():
+    """On V = 2 with q = (1, 0) and p_i = (c_i, 1 - c_i) the chain accepts
+    position i with probability c_i, so E[A + 1] = 1 + sum_j prod_{i<=j} c_i,
+    which is the expected advance of the length chooser at k = K."""
+    c = np.array([0.9, 0.8, 0.75, 0.6, 0.95], np.float32)
+    K, V, n = len(c), 2, 400_000
+    rng = np.random.default_rng(12)
+    P = [[float(ci), 1 - float(ci)] for ci in c] + [[0.5, 0.5]]
+    tgt = np.tile(np.stack([logits_of(r) for r in P]), (n, 1))
+    dft = np.tile(np.stack([logits_of([1.0, 0.0])] * K), (n, 1))
+    y = np.zeros(n * K, np.int32)
+    out = oracle.verify_chain(tgt, dft, y, grid_u(rng, n * (K + 1)), None, n, K, V, 1.0, want_probs=False)
+    closed = 1 + sum(np.prod(c[:j + 1].astype(np.float64)) for j in range(K))
+    mc = (out["A"] + 1).astype(np.float64)
+    assert abs(mc.mean() - closed) < 4 * mc.std() / math.sqrt(n)
+    sel = oracle.select_len(c[None], 1, K, 0.0)
+    assert sel["k"][0] == K
+    assert abs(sel["adv"][0] - closed) < 1e-6
+
+
+def test_select_len_properties():
+    rng = np.random.default_rng(13)
+    B, K = 2000, 8
+    six = rng.random((B, K, 6))
+    conf = np.sort(six, axis=-1)[..., 4].astype(np.float32)   # Beta(5, 2)
+    sel = oracle.select_len(conf, B, K, 0.15)
+    # survival is non-increasing, so the best k is the number of positions whose
+    # fp32 survival exceeds the cost (the increments s_j - cost change sign once)
+    s = np.multiply.accumulate(conf, axis=1, dtype=np.float32)
+    np.testing.assert_array_equal(sel["k"], (s > np.float32(0.15)).sum(1))
+    for b in range(50):
+        k = sel["k"][b]
+        np.testing.assert_allclose(sel["adv"][b], 1 + s[b, :k].astype(np.float64).sum(), rtol=1e-12)
+    np.testing.assert_array_equal(sel["cu"], np.concatenate([[0], np.cumsum(sel["k"])]))
+    # c == 1 and cost < 1 -> K; cost >= 1 -> 0; raising the cost never raises k
+    ones = np.ones((3, K), np.float32)
+    assert (oracle.select_len(ones, 3, K, 0.99)["k"] == K).all()
+    assert (oracle.select_len(ones, 3, K, 1.0)["k"] == 0).all()
+    prev = None
+    for cost in (0.0, 0.05, 0.15, 0.3, 0.6, 0.9):
+        k = oracle.select_len(conf, B, K, cost)["k"]
+        if prev is not None:
+            assert (k <= prev).all()
+        prev = k
+    # E[k*] for Beta(5,2) at cost 0.15 is about 4.9
+    assert 4.6 < sel["k"].mean() < 5.2
+
+
+def test_cost_model_example():
+    """[SD §2] illustrative numbers: a 3 + 13 + 2 ms round gives 18/4 = 4.5 ms per
+    token with 3 accepted drafts and 18/2 = 9 ms with 1 (A excludes the extra token)."""
+    per_round = 3 + 13 + 2
+    assert per_round / (3 + 1) == 4.5
+    assert per_round / (1 + 1) == 9.0
+
+
+# --------------------------------------------------------------------------
+# [SD §5 DDTree] best-first tree under a node budget, and the walk.
+# --------------------------------------------------------------------------
+
+def _all_prefix_closed_sets(V, K, size):
+    """Every prefix-closed set of `size` prefixes (tuples of token ids) of the
+    V-ary trie of depth K."""
+    start = frozenset()
+    seen = {start}
+    frontier = [start]
+    for _ in range(size):
+        nxt = []
+        for s in frontier:
+            cands = [(t,) for t in range(V)] + [u + (t,) for u in s if len(u) < K for t in range(V)]
+            for c in cands:
+                if c in s:
+                    continue
+                ns = s | {c}
+                if ns not in seen:
+                    seen.add(ns)
+                    nxt.append(ns)
+        frontier = nxt
+    return frontier
+
+
+def _Q(marg, u):
+    return float(np.prod([float(marg[d][t]) for d, t in enumerate(u)]))
+
+
+@pytest.mark.parametrize("V,K,N", [(2, 2, 4), (3, 2, 5), (3, 3, 7), (2, 3, 7), (3, 3, 5)])
+def test_tree_brute_force_optimal(V, K, N):
+    rng = np.random.default_rng(V * 100 + K * 10 + N)
+    for trial in range(6):
+        Z = rng.standard_normal((K, V)) * 1.5
+        marg = special.softmax(Z, axis=1).astype(np.float32)
+        out = oracle.build_tree(marg[None], 1, K, V, N)
+        n = int(out["n_nodes"][0])
+        total = sum(V ** m for m in range(1, K + 1))
+        assert n == min(N, total + 1)
+        tok, par, dep = out["token"][0], out["parent"][0], out["depth"][0]
+        # reconstruct prefixes
+        pref = {0: ()}
+        for i in range(1, n):
+            assert 0 <= par[i] < i
+            assert dep[i] == dep[par[i]] + 1
+            pref[i] = pref[par[i]] + (int(tok[i]),)
+        chosen = frozenset(pref[i] for i in range(1, n))
+        best = max(_all_prefix_closed_sets(V, K, n - 1), key=lambda s: sum(_Q(marg, u) for u in s))
+        got = sum(_Q(marg, u) for u in chosen)
+        want = sum(_Q(marg, u) for u in best)
+        assert got >= want * (1 - 1e-6)
+
+
+def test_tree_invariants_and_full_trie():
+    rng = np.random.default_rng(21)
+    B, K, V, N = 6, 4, 50, 64
+    marg = special.softmax(rng.standard_normal((B, K, V)) * 2.5, axis=2).astype(np.float32)
+    out = oracle.build_tree(marg, B, K, V, N)
+    for b in range(B):
+        n = out["n_nodes"][b]
+        assert n == N
+        sc, par, dep, anc, tok = (out[k][b] for k in ("score", "parent", "depth", "anc_mask", "token"))
+        assert sc[0] == 1.0 and par[0] == -1 and anc[0] == 1
+        for i in range(1, n):
+            p = par[i]
+            assert p < i and dep[i] == dep[p] + 1 <= K
+            assert sc[i] <= sc[i - 1]                        # scores never increase in node order
+            assert int(anc[i]) == int(anc[p]) | (1 << i)      # mask follows the parent chain
+            assert sc[i] == np.float32(sc[p] * marg[b, dep[p], tok[i]])
+        # siblings carry distinct tokens
+        for p in range(n):
+            kids = [tok[i] for i in range(1, n) if par[i] == p]
+            assert len(kids) == len(set(kids))
+    # trie smaller than the budget: everything is taken
+    m2 = special.softmax(rng.standard_normal((1, 2, 3)), axis=2).astype(np.float32)
+    o2 = oracle.build_tree(m2, 1, 2, 3, 64)
+    assert o2["n_nodes"][0] == 1 + 3 + 9
+
+
+def test_tree_depth1_is_top_list():
+    """With budget N the depth-1 children are a prefix of the sorted marginal
+    (q desc, id asc): a tree never skips a better sibling."""
+    rng = np.random.default_rng(22)
+    K, V, N = 3, 40, 20
+    marg = special.softmax(rng.standard_normal((1, K, V)) * 2.5, axis=2).astype(np.float32)
+    marg[0, 0, 7] = marg[0, 0, 3]          # a tie: id 3 must come first
+    out = oracle.build_tree(marg, 1, K, V, N)
+    kids = [int(out["token"][0][i]) for i in range(1, N) if out["parent"][0][i] == 0]
+    order = sorted(range(V), key=lambda t: (-float(marg[0, 0, t]), t))
+    assert kids == order[:len(kids)]
+
+
+def _one_hot_rows(tokens, V):
+    r = np.full((len(tokens), V), -5.0, np.float32)
+    r[np.arange(len(tokens)), tokens] = 5.0
+    return r
+
+
+def test_tree_walk_hand_built():
+    # root 0 -> 1 (tok 4), 2 (tok 7); 1 -> 3 (tok 2); 3 -> 4 (tok 9)
+    V, N = 12, 6
+    token = np.array([[-1, 4, 7, 2, 9, -1]], np.int32)
+    parent = np.array([[-1, 0, 0, 1, 3, -1]], np.int32)
+    nn = np.array([5], np.int32)
+    # full walk to the deepest node, then the extra token from node 4's row
+    rows = _one_hot_rows([4, 2, 0, 9, 11, 0], V)[None]
+    out = oracle.verify_tree(rows, token, parent, nn, 1, N, V)
+    assert out["A"][0] == 3 and out["path"][0][:4].tolist() == [1, 3, 4, -1] and out["next"][0] == 11
+    # walk ending early at node 2 (a leaf): next is node 2's argmax
+    rows = _one_hot_rows([7, 0, 5, 0, 0, 0], V)[None]
+    out = oracle.verify_tree(rows, token, parent, nn, 1, N, V)
+    assert out["A"][0] == 1 and out["path"][0][0] == 2 and out["next"][0] == 5
+    # immediate miss
+    rows = _one_hot_rows([3, 0, 0, 0, 0, 0], V)[None]
+    out = oracle.verify_tree(rows, token, parent, nn, 1, N, V)
+    assert out["A"][0] == 0 and (out["path"][0] == -1).all() and out["next"][0] == 3
+    # a tie in the target row goes to the lower id (4 over 7)
+    rows = _one_hot_rows([4, 0, 0, 0, 0, 0], V)
+    rows[0, 7] = 5.0
+    rows[1, 2] = 5.0
+    out = oracle.verify_tree(rows[None], token, parent, nn, 1, N, V)
+    assert out["path"][0][0] == 1
+
+
+def test_tree_walk_expected_length_monte_carlo():
+    """If the target's token at depth d is drawn from q_{d+1} independently, the
+    walk reaches node u with probability Q(u), so E[accepted] = sum_u Q(u)."""
+    rng = np.random.default_rng(23)
+    K, V, N, n = 3, 4, 9, 60_000
+    marg = special.softmax(rng.standard_normal((1, K, V)) * 1.2, axis=2).astype(np.float32)
+    tree = oracle.build_tree(marg, 1, K, V, N)
+    nn = int(tree["n_nodes"][0])
+    dep = tree["depth"][0]
+    rows = np.full((n, N, V), -5.0, np.float32)
+    for node in range(nn):
+        d = dep[node]
+        if d < K:
+            draws = sample_from(rng, marg[0, d].astype(np.float64), n)
+        else:
+            draws = rng.integers(0, V, n)
+        rows[np.arange(n), node, draws] = 5.0
+    tok = np.tile(tree["token"], (n, 1))
+    par = np.tile(tree["parent"], (n, 1))
+    out = oracle.verify_tree(rows, tok, par, np.full(n, nn, np.int32), n, N, V)
+    expect = sum(float(tree["score"][0][i]) for i in range(1, nn))
+    a = out["A"].astype(np.float64)
+    assert abs(a.mean() - expect) < 4 * a.std() / math.sqrt(n)
