@@ -1,0 +1,217 @@
+/*
+ * sd.h -- C ABI of libsd, batched speculative-decoding draft verification on
+ * AMD Instinct MI355X (gfx950).
+ *
+ * What each call computes is defined on the web page "大模型投机解码：Medusa、
+ * MTP、EAGLE、DFlash、DDTree 与 DSpark" (chzhyang.github.io), cited as [SD §n]:
+ * §1 (the acceptance-probability equation alpha = min(1, p/q), the A B C D
+ * example of first-rejection truncation, the correction token from the
+ * normalised positive residual, the extra token from p, greedy = target argmax,
+ * temperature and truncation inside p and q), §2 (A excludes the correction /
+ * extra token), §5 DDTree (the factorised score Q(u) = prod q_i(u_i), the
+ * best-first tree under a node budget, the walk along the target's token) and
+ * §5 DSpark (prefix survival s_j = prod c_i, expected advance 1 + sum s_j).
+ *
+ * Conventions shared by every call
+ * --------------------------------
+ * - All array arguments are DEVICE pointers (memory the caller allocated on the
+ *   current HIP device), except `bytes` of sd_workspace_bytes (host). The caller
+ *   owns every buffer; the library never allocates, frees or synchronises.
+ * - Every call enqueues its kernels on `hip_stream` (a hipStream_t; NULL = the
+ *   null stream) and returns. Outputs are valid once the stream has reached
+ *   that point. Calls are stateless and may run concurrently on different
+ *   streams when their workspaces and outputs are distinct.
+ * - Rows are contiguous V-long vectors, row-major, int32 indices everywhere.
+ *   Logits are fp32 (SD_F32) or bf16 (SD_BF16, raw 16-bit patterns).
+ * - Batch layout of the chain calls. Sequence b has k_b draft positions:
+ *   k_b = cu[b+1] - cu[b] when a `cu` array ([B+1], non-decreasing, cu[0] = 0)
+ *   is given, else k_b = K_max with cu[b] = b*K_max. Draft row i of b is draft
+ *   row cu[b]+i (i < k_b); target row i of b is target row cu[b]+b+i for
+ *   i = 0..k_b, row k_b being the extra-token ("bonus") row. So a padded batch
+ *   (cu == NULL) has B*(K_max+1) target rows and B*K_max draft rows, and a
+ *   packed batch has cu[B]+B target rows and cu[B] draft rows, only the
+ *   selected rows being read.
+ * - Uniforms (chain, T > 0): uniforms[cu[b]+b+i] drives the accept test of
+ *   position i; uniforms[cu[b]+b+k_b] drives the one final draw (correction or
+ *   extra token). Values must lie in [0, 1).
+ * - Errors. Invalid scalars or a NULL required pointer return SD_EINVAL before
+ *   any HIP call, with nothing launched. A workspace smaller than
+ *   sd_workspace_bytes returns SD_EWORKSPACE (nothing launched). A dtype that is
+ *   not built for an op returns SD_EUNSUPPORTED. A failed launch returns SD_EHIP.
+ *   Problems only the device can see do not abort a call: a draft token outside
+ *   [0, V) or a non-finite row (its kept logits have no finite maximum or a NaN
+ *   reaches its exponential sum) makes that position a rejection with p(y) = 0
+ *   and sets bits in seq_status[b]; only positions 0..A and the row the final
+ *   token is drawn from can set them. next_token is -1 when no token can be
+ *   drawn (a non-finite decision row).
+ * - Limits: 1 <= V < 2^24; 0 <= K_max <= 64; 1 <= B <= 2^20; tree budget
+ *   2 <= N <= 64 and K <= 16; top_k <= 256; T >= 0 and finite.
+ */
+#ifndef SD_H_
+#define SD_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define SD_ABI_VERSION 1
+
+typedef enum {
+    SD_OK = 0,
+    SD_EINVAL = 1,
+    SD_EUNSUPPORTED = 2,
+    SD_EWORKSPACE = 3,
+    SD_EHIP = 4
+} sd_status_t;
+
+typedef enum { SD_F32 = 0, SD_BF16 = 1 } sd_dtype_t;
+
+typedef enum {
+    SD_OP_CHAIN = 0,
+    SD_OP_GREEDY = 1,
+    SD_OP_BUILD_TREE = 2,
+    SD_OP_VERIFY_TREE = 3,
+    SD_OP_SELECT_LEN = 4
+} sd_op_t;
+
+/* seq_status bits */
+#define SD_SEQ_BAD_TOKEN 1   /* a draft token outside [0, V) on the decision path */
+#define SD_SEQ_NONFINITE 2   /* a non-finite row on the decision path             */
+
+/* Largest supported values. */
+#define SD_MAX_K 64
+#define SD_MAX_TREE_N 64
+#define SD_MAX_TREE_K 16
+#define SD_MAX_TOPK 256
+
+/* Returns SD_ABI_VERSION. */
+int sd_abi_version(void);
+
+/* Static, human-readable name of a status code (never NULL). */
+const char* sd_status_str(int status);
+
+/*
+ * Workspace size in bytes (written to the HOST pointer `bytes`) that op needs
+ * for these sizes. Pass the same B, K_max (tree: K), V, top_k and N as the call
+ * itself (unused ones are ignored). Returns SD_EINVAL for out-of-range sizes.
+ * The workspace is device memory, 256-byte aligned, owned by the caller, and
+ * needs no initialisation; a call overwrites the part it uses.
+ */
+sd_status_t sd_workspace_bytes(sd_op_t op, int32_t B, int32_t K_max, int32_t V,
+                               int32_t top_k, int32_t N, size_t* bytes);
+
+/*
+ * Chain verification [SD §1].
+ *
+ * T > 0 (stochastic speculative sampling). With p_i = softmax of target row i
+ * and q_i = softmax of draft row i, both after dividing the logits by T and,
+ * when 1 <= top_k < V, keeping only the top_k logits ordered by (logit desc,
+ * id asc) (NaN never kept):
+ *   position i is accepted iff p_i(y_i) > 0 and u_i * q_i(y_i) <= p_i(y_i);
+ *   A = the first rejected position, or k_b when all pass;
+ *   if A < k_b the next token is drawn from the normalised residual
+ *   max(p_A - q_A, 0) by inverse CDF in token-id order at u_{k_b} * R
+ *   (R = the residual's total mass); if A == k_b it is drawn from p_{k_b} the
+ *   same way at u_{k_b}.
+ * T == 0 (greedy): position i is accepted iff y_i is the lowest-id argmax of
+ * the raw target row i; next_token is that argmax at row A. draft_logits and
+ * uniforms may then be NULL, top_k is ignored, probs_out / resid_mass_out are
+ * not written.
+ *
+ *   target_logits  [R_t, V] dtype          (see "Batch layout")
+ *   draft_logits   [R_d, V] dtype
+ *   draft_tokens   [R_d] int32             y_i
+ *   uniforms       [R_t] fp32 in [0,1)
+ *   cu_draft       [B+1] int32 or NULL     packed offsets (device)
+ *   accepted_len   [B] int32 out           A (excludes the correction/extra token)
+ *   next_token     [B] int32 out           correction if A < k_b, else extra token
+ *   probs_out      [R_d, 2] fp32 out or NULL   (p_i(y_i), q_i(y_i)) for every position
+ *   resid_mass_out [B] fp32 out or NULL    R (0 for an extra token)
+ *   seq_status     [B] int32 out or NULL   SD_SEQ_* bits
+ */
+sd_status_t sd_verify_chain(const void* target_logits, const void* draft_logits,
+                            sd_dtype_t dtype, const int32_t* draft_tokens,
+                            const float* uniforms, const int32_t* cu_draft,
+                            int32_t B, int32_t K_max, int32_t V,
+                            float temperature, int32_t top_k,
+                            int32_t* accepted_len, int32_t* next_token,
+                            float* probs_out, float* resid_mass_out, int32_t* seq_status,
+                            void* workspace, size_t workspace_bytes, void* hip_stream);
+
+/*
+ * Greedy chain verification [SD §1: greedy results follow the target argmax].
+ * g_i = lowest-id argmax of raw target row i (NaN ignored); position i is
+ * accepted iff y_i == g_i; A = first mismatch (or k_b); next_token = g_A.
+ * Same layout and outputs as sd_verify_chain with T == 0.
+ */
+sd_status_t sd_verify_greedy(const void* target_logits, sd_dtype_t dtype,
+                             const int32_t* draft_tokens, const int32_t* cu_draft,
+                             int32_t B, int32_t K_max, int32_t V,
+                             int32_t* accepted_len, int32_t* next_token, int32_t* seq_status,
+                             void* workspace, size_t workspace_bytes, void* hip_stream);
+
+/*
+ * DDTree candidate tree [SD §5 DDTree].
+ *
+ *   marginals  [B, K, V] fp32 probabilities; row d is the draft marginal of
+ *              depth d+1 (q_{d+1}); entries must be >= 0 and not NaN.
+ * L_d = the ids of row d ordered by (q desc, id asc), cut to N-1 entries. A
+ * prefix (r_1..r_m) (m <= K) names tokens L_1[r_1]..L_m[r_m] and scores
+ * Q = fl32(...fl32(q_1 * q_2)... * q_m) (fp32, left to right). Prefixes are
+ * ordered by (Q desc, m asc, rank tuple lexicographically asc); the tree is the
+ * root (node 0: token -1, parent -1, depth 0, score 1, mask bit 0) plus the
+ * first N-1 prefixes of that order, found best-first with a priority queue and
+ * numbered in pop order (fewer when the whole trie is smaller).
+ *
+ *   node_token, node_parent, node_depth [B, N] int32 out (unused slots: -1, -1, 0)
+ *   node_score   [B, N] fp32 out            Q (unused slots: 0)
+ *   node_anc_mask[B, N] uint64 out          bit j set iff node j is the node or an
+ *                                           ancestor of it (unused slots: 0)
+ *   n_nodes      [B] int32 out
+ */
+sd_status_t sd_build_tree(const float* marginals, int32_t B, int32_t K, int32_t V, int32_t N,
+                          int32_t* node_token, int32_t* node_parent, int32_t* node_depth,
+                          float* node_score, uint64_t* node_anc_mask, int32_t* n_nodes,
+                          void* workspace, size_t workspace_bytes, void* hip_stream);
+
+/*
+ * DDTree walk [SD §5 DDTree]. target_logits [B, N, V] dtype: row n is the target
+ * distribution after node n (row 0 after the root/anchor). From the root, take
+ * g = lowest-id argmax of the current node's row; if a child of the node carries
+ * token g, move there and record it; otherwise g is next_token.
+ *
+ *   node_token, node_parent [B, N] int32, n_nodes [B] int32 (as built)
+ *   path_nodes   [B, N] int32 out   accepted node ids in walk order (root
+ *                                   excluded), -1 padded
+ *   accepted_len [B] int32 out      path length
+ *   next_token   [B] int32 out      the target's token after the path
+ */
+sd_status_t sd_verify_tree(const void* target_logits, sd_dtype_t dtype,
+                           const int32_t* node_token, const int32_t* node_parent,
+                           const int32_t* n_nodes, int32_t B, int32_t N, int32_t V,
+                           int32_t* path_nodes, int32_t* accepted_len, int32_t* next_token,
+                           void* workspace, size_t workspace_bytes, void* hip_stream);
+
+/*
+ * DSpark verify length [SD §5 DSpark]. s_0 = 1, s_j = fl32(s_{j-1} * c_j);
+ * k_sel[b] = the largest k with s_j > cost_per_position for every j <= k
+ * (for c in [0, 1] this is the smallest k maximising 1 + sum_{j<=k} s_j - cost*k);
+ * expected_advance[b] = 1 + sum_{j <= k_sel} s_j; cu_sel = exclusive prefix sum
+ * of k_sel ([B+1], usable directly as cu_draft of a packed sd_verify_chain).
+ *
+ *   conf [B, K_max] fp32 in [0, 1]
+ *   k_sel [B] int32 out; expected_advance [B] fp32 out or NULL; cu_sel [B+1] int32 out or NULL
+ * Needs no workspace.
+ */
+sd_status_t sd_select_len(const float* conf, int32_t B, int32_t K_max, float cost_per_position,
+                          int32_t* k_sel, float* expected_advance, int32_t* cu_sel,
+                          void* hip_stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SD_H_ */

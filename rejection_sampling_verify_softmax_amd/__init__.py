@@ -1,0 +1,305 @@
+"""Python binding of libsd: batched speculative-decoding draft verification on
+AMD Instinct MI355X (gfx950).
+
+Argument marshalling only. Every step of the verification runs in the HIP
+kernels of libsd.so behind the C ABI of include/sd.h; torch provides device
+memory (inputs, outputs, workspace) and the current HIP stream. There is no
+CPU fallback: if libsd.so is missing or no GPU is present, the calls raise.
+
+Functions mirror the C entry points:
+  verify_chain   sd_verify_chain   (stochastic chain, or greedy when T == 0)
+  verify_greedy  sd_verify_greedy
+  build_tree     sd_build_tree     (DDTree best-first tree from marginals)
+  verify_tree    sd_verify_tree    (walk along the target's argmax)
+  select_len     sd_select_len     (DSpark verify length, packed offsets)
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libsd.so")
+
+SD_OK, SD_EINVAL, SD_EUNSUPPORTED, SD_EWORKSPACE, SD_EHIP = 0, 1, 2, 3, 4
+SD_F32, SD_BF16 = 0, 1
+OP_CHAIN, OP_GREEDY, OP_BUILD_TREE, OP_VERIFY_TREE, OP_SELECT_LEN = 0, 1, 2, 3, 4
+SEQ_BAD_TOKEN, SEQ_NONFINITE = 1, 2
+
+_lib = None
+
+
+class SDError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        msg = _load().sd_status_str(status).decode() if _lib is not None else str(status)
+        super().__init__(f"{where}: {msg}")
+        self.status = status
+
+
+def _load():
+    """Load libsd.so (built in-tree by `_build.build()`); fails loudly if absent."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError(f"libsd.so not found at {LIB_PATH}: build it with "
+                           "rejection_sampling_verify_softmax_amd._build.build()")
+    lib = ctypes.CDLL(LIB_PATH)
+    P, I, F, Z = ctypes.c_void_p, ctypes.c_int32, ctypes.c_float, ctypes.c_size_t
+    lib.sd_abi_version.argtypes = []
+    lib.sd_abi_version.restype = ctypes.c_int
+    lib.sd_status_str.argtypes = [ctypes.c_int]
+    lib.sd_status_str.restype = ctypes.c_char_p
+    lib.sd_workspace_bytes.argtypes = [ctypes.c_int, I, I, I, I, I, ctypes.POINTER(Z)]
+    lib.sd_workspace_bytes.restype = ctypes.c_int
+    lib.sd_verify_chain.argtypes = [P, P, ctypes.c_int, P, P, P, I, I, I, F, I, P, P, P, P, P, P, Z, P]
+    lib.sd_verify_chain.restype = ctypes.c_int
+    lib.sd_verify_greedy.argtypes = [P, ctypes.c_int, P, P, I, I, I, P, P, P, P, Z, P]
+    lib.sd_verify_greedy.restype = ctypes.c_int
+    lib.sd_build_tree.argtypes = [P, I, I, I, I, P, P, P, P, P, P, P, Z, P]
+    lib.sd_build_tree.restype = ctypes.c_int
+    lib.sd_verify_tree.argtypes = [P, ctypes.c_int, P, P, P, I, I, I, P, P, P, P, Z, P]
+    lib.sd_verify_tree.restype = ctypes.c_int
+    lib.sd_select_len.argtypes = [P, I, I, F, P, P, P, P]
+    lib.sd_select_len.restype = ctypes.c_int
+    _lib = lib
+    return lib
+
+
+def lib():
+    return _load()
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream=None):
+    s = torch.cuda.current_stream() if stream is None else stream
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def _dtype_code(t: torch.Tensor) -> int:
+    if t.dtype == torch.bfloat16:
+        return SD_BF16
+    if t.dtype == torch.float32:
+        return SD_F32
+    raise TypeError(f"logits must be float32 or bfloat16, got {t.dtype}")
+
+
+def _check(t: Optional[torch.Tensor], name: str, dtype=None, device=None):
+    if t is None:
+        return
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a GPU tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if dtype is not None and t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if device is not None and t.device != device:
+        raise ValueError(f"{name} is on {t.device}, expected {device}")
+
+
+def _get(d: dict, key: str, make):
+    t = d.get(key)
+    return make() if t is None else t
+
+
+def _raise(status: int, where: str):
+    if status != SD_OK:
+        raise SDError(status, where)
+
+
+def workspace_bytes(op: int, B: int, K_max: int = 0, V: int = 1, top_k: int = 0, N: int = 2) -> int:
+    out = ctypes.c_size_t(0)
+    _raise(_load().sd_workspace_bytes(int(op), int(B), int(K_max), int(V), int(top_k), int(N),
+                                      ctypes.byref(out)), "sd_workspace_bytes")
+    return int(out.value)
+
+
+def _workspace(nbytes: int, device, ws: Optional[torch.Tensor]):
+    n = max(int(nbytes), 256)
+    if ws is not None:
+        if ws.numel() * ws.element_size() < n:
+            raise ValueError(f"workspace of {ws.numel() * ws.element_size()} bytes < {n} needed")
+        return ws
+    return torch.empty(n, dtype=torch.uint8, device=device)
+
+
+def _check_rows(t: Optional[torch.Tensor], name: str, rows: int, V: int):
+    if t is not None and t.numel() < rows * V:
+        raise ValueError(f"{name} holds {t.numel()} elements, the batch layout needs {rows * V}")
+
+
+def _check_layout(target, draft, tokens, uniforms, cu, B, K_max, V, greedy, validate):
+    """Size checks of the batch layout (include/sd.h) so that no kernel reads
+    past a tensor. A packed layout costs one device->host read of cu unless
+    validate=False (then the caller vouches for cu)."""
+    if cu is not None:
+        if cu.numel() != B + 1:
+            raise ValueError(f"cu must hold B+1 = {B + 1} offsets")
+        if not validate:
+            return
+        c = cu.cpu()
+        lens = c[1:] - c[:-1]
+        if int(c[0]) != 0 or (B > 0 and (int(lens.min()) < 0 or int(lens.max()) > K_max)):
+            raise ValueError("cu must start at 0 and have lengths in [0, K_max]")
+        R_d = int(c[-1])
+    else:
+        R_d = B * K_max
+    _check_rows(target, "target", R_d + B, V)
+    _check_rows(tokens, "tokens", R_d, 1)
+    if not greedy:
+        _check_rows(draft, "draft", R_d, V)
+        _check_rows(uniforms, "uniforms", R_d + B, 1)
+
+
+def verify_chain(target: torch.Tensor, draft: Optional[torch.Tensor], tokens: torch.Tensor,
+                 uniforms: Optional[torch.Tensor], temperature: float, top_k: int = 0,
+                 cu: Optional[torch.Tensor] = None, B: Optional[int] = None,
+                 K_max: Optional[int] = None, want_probs: bool = False,
+                 want_resid: bool = False, workspace: Optional[torch.Tensor] = None,
+                 out: Optional[dict] = None, stream=None, validate: bool = True) -> dict:
+    """sd_verify_chain. Dense batch (cu None): target [B*(K+1), V], draft [B*K, V],
+    tokens [B*K] (or [B, K]). Packed batch: pass cu [B+1] (device int32) and K_max.
+    Returns dict with accepted_len, next_token, status (+ probs [R_d, 2], resid)."""
+    dev = target.device
+    _check(target, "target", device=dev)
+    dt = _dtype_code(target)
+    V = int(target.shape[-1])
+    if cu is not None:
+        _check(cu, "cu", torch.int32, dev)
+        if B is None:
+            B = cu.numel() - 1
+        if K_max is None:
+            K_max = int((cu[1:] - cu[:-1]).max().item()) if B > 0 else 0
+    else:
+        if K_max is None:
+            K_max = int(tokens.shape[-1]) if tokens.dim() == 2 else None
+        if B is None:
+            if K_max is None:
+                raise ValueError("pass K_max (or 2-D tokens) for a dense batch")
+            B = target.numel() // V // (K_max + 1)
+    _check(tokens, "tokens", torch.int32, dev)
+    greedy = float(temperature) == 0.0
+    if not greedy:
+        _check(draft, "draft", target.dtype, dev)
+        _check(uniforms, "uniforms", torch.float32, dev)
+    _check_layout(target, draft, tokens, uniforms, cu, B, K_max, V, greedy, validate)
+    o = out or {}
+    A = _get(o, "accepted_len", lambda: torch.empty(B, dtype=torch.int32, device=dev))
+    nxt = _get(o, "next_token", lambda: torch.empty(B, dtype=torch.int32, device=dev))
+    st = _get(o, "status", lambda: torch.empty(B, dtype=torch.int32, device=dev))
+    probs = None
+    if want_probs and not greedy:
+        probs = _get(o, "probs", lambda: torch.empty(max(tokens.numel(), 1), 2, dtype=torch.float32, device=dev))
+    resid = None
+    if want_resid and not greedy:
+        resid = _get(o, "resid", lambda: torch.empty(B, dtype=torch.float32, device=dev))
+    nbytes = workspace_bytes(OP_CHAIN, B, K_max, V, top_k)
+    ws = _workspace(nbytes, dev, workspace)
+    r = _load().sd_verify_chain(_ptr(target), _ptr(draft) if not greedy else None, dt, _ptr(tokens),
+                                _ptr(uniforms) if not greedy else None, _ptr(cu), int(B), int(K_max),
+                                int(V), ctypes.c_float(float(temperature)), int(top_k), _ptr(A),
+                                _ptr(nxt), _ptr(probs), _ptr(resid), _ptr(st), _ptr(ws),
+                                ctypes.c_size_t(ws.numel()), _stream(stream))
+    _raise(r, "sd_verify_chain")
+    res = {"accepted_len": A, "next_token": nxt, "status": st}
+    if probs is not None:
+        res["probs"] = probs
+    if resid is not None:
+        res["resid"] = resid
+    return res
+
+
+def verify_greedy(target: torch.Tensor, tokens: torch.Tensor, cu: Optional[torch.Tensor] = None,
+                  B: Optional[int] = None, K_max: Optional[int] = None,
+                  workspace: Optional[torch.Tensor] = None, stream=None) -> dict:
+    """sd_verify_greedy; same layout as verify_chain."""
+    dev = target.device
+    _check(target, "target", device=dev)
+    _check(tokens, "tokens", torch.int32, dev)
+    dt = _dtype_code(target)
+    V = int(target.shape[-1])
+    if cu is not None:
+        _check(cu, "cu", torch.int32, dev)
+        B = cu.numel() - 1 if B is None else B
+        if K_max is None:
+            K_max = int((cu[1:] - cu[:-1]).max().item()) if B > 0 else 0
+    else:
+        if K_max is None:
+            if tokens.dim() != 2:
+                raise ValueError("pass K_max (or 2-D tokens) for a dense batch")
+            K_max = int(tokens.shape[-1])
+        B = target.numel() // V // (K_max + 1) if B is None else B
+    _check_layout(target, None, tokens, None, cu, B, K_max, V, True, True)
+    A = torch.empty(B, dtype=torch.int32, device=dev)
+    nxt = torch.empty(B, dtype=torch.int32, device=dev)
+    st = torch.empty(B, dtype=torch.int32, device=dev)
+    ws = _workspace(workspace_bytes(OP_GREEDY, B, K_max, V), dev, workspace)
+    r = _load().sd_verify_greedy(_ptr(target), dt, _ptr(tokens), _ptr(cu), int(B), int(K_max), int(V),
+                                 _ptr(A), _ptr(nxt), _ptr(st), _ptr(ws), ctypes.c_size_t(ws.numel()),
+                                 _stream(stream))
+    _raise(r, "sd_verify_greedy")
+    return {"accepted_len": A, "next_token": nxt, "status": st}
+
+
+def build_tree(marginals: torch.Tensor, N: int, workspace: Optional[torch.Tensor] = None,
+               stream=None) -> dict:
+    """sd_build_tree. marginals [B, K, V] float32 on the GPU."""
+    dev = marginals.device
+    _check(marginals, "marginals", torch.float32, dev)
+    B, K, V = (int(s) for s in marginals.shape)
+    out = {
+        "token": torch.empty(B, N, dtype=torch.int32, device=dev),
+        "parent": torch.empty(B, N, dtype=torch.int32, device=dev),
+        "depth": torch.empty(B, N, dtype=torch.int32, device=dev),
+        "score": torch.empty(B, N, dtype=torch.float32, device=dev),
+        "anc_mask": torch.empty(B, N, dtype=torch.int64, device=dev),
+        "n_nodes": torch.empty(B, dtype=torch.int32, device=dev),
+    }
+    ws = _workspace(workspace_bytes(OP_BUILD_TREE, B, K, V, 0, N), dev, workspace)
+    r = _load().sd_build_tree(_ptr(marginals), B, K, V, int(N), _ptr(out["token"]), _ptr(out["parent"]),
+                              _ptr(out["depth"]), _ptr(out["score"]), _ptr(out["anc_mask"]),
+                              _ptr(out["n_nodes"]), _ptr(ws), ctypes.c_size_t(ws.numel()),
+                              _stream(stream))
+    _raise(r, "sd_build_tree")
+    return out
+
+
+def verify_tree(target: torch.Tensor, tree: dict, workspace: Optional[torch.Tensor] = None,
+                stream=None) -> dict:
+    """sd_verify_tree. target [B, N, V] (bf16 or fp32); tree from build_tree."""
+    dev = target.device
+    _check(target, "target", device=dev)
+    dt = _dtype_code(target)
+    B, N, V = (int(s) for s in target.shape)
+    for k in ("token", "parent", "n_nodes"):
+        _check(tree[k], k, torch.int32, dev)
+    path = torch.empty(B, N, dtype=torch.int32, device=dev)
+    A = torch.empty(B, dtype=torch.int32, device=dev)
+    nxt = torch.empty(B, dtype=torch.int32, device=dev)
+    ws = _workspace(workspace_bytes(OP_VERIFY_TREE, B, 0, V, 0, N), dev, workspace)
+    r = _load().sd_verify_tree(_ptr(target), dt, _ptr(tree["token"]), _ptr(tree["parent"]),
+                               _ptr(tree["n_nodes"]), B, N, V, _ptr(path), _ptr(A), _ptr(nxt),
+                               _ptr(ws), ctypes.c_size_t(ws.numel()), _stream(stream))
+    _raise(r, "sd_verify_tree")
+    return {"path": path, "accepted_len": A, "next_token": nxt}
+
+
+def select_len(conf: torch.Tensor, cost: float, out: Optional[dict] = None, stream=None) -> dict:
+    """sd_select_len. conf [B, K_max] float32 on the GPU."""
+    dev = conf.device
+    _check(conf, "conf", torch.float32, dev)
+    B, K = (int(s) for s in conf.shape)
+    o = out or {}
+    k = _get(o, "k", lambda: torch.empty(B, dtype=torch.int32, device=dev))
+    adv = _get(o, "adv", lambda: torch.empty(B, dtype=torch.float32, device=dev))
+    cu = _get(o, "cu", lambda: torch.empty(B + 1, dtype=torch.int32, device=dev))
+    r = _load().sd_select_len(_ptr(conf), B, K, ctypes.c_float(float(cost)), _ptr(k), _ptr(adv),
+                              _ptr(cu), _stream(stream))
+    _raise(r, "sd_select_len")
+    return {"k": k, "adv": adv, "cu": cu}

@@ -1,0 +1,189 @@
+// sd_abi.hip -- the extern "C" entry points of libsd (declared in include/sd.h).
+//
+// Every entry point validates its scalars and required pointers before the
+// first HIP call, sizes the workspace, and enqueues the kernels of its path on
+// the caller's stream. It never allocates, frees or synchronises.
+#include "sd.h"
+#include "sd_internal.hpp"
+
+#include <math.h>
+
+namespace {
+
+constexpr int kMaxB = 1 << 20;
+constexpr int kMaxV = (1 << 24) - 1;
+
+bool bad_size(int B, int K_max, int V) {
+    return B < 1 || B > kMaxB || K_max < 0 || K_max > SD_MAX_K || V < 1 || V > kMaxV;
+}
+bool bad_dtype(sd_dtype_t dt) { return dt != SD_F32 && dt != SD_BF16; }
+bool topk_on(int top_k, int V) { return top_k >= 1 && top_k < V; }
+
+sd_status_t from_hip(hipError_t e) { return e == hipSuccess ? SD_OK : SD_EHIP; }
+
+size_t chain_ws(int B, int K_max, int V, int dtype, float T, int top_k) {
+    if (T == 0.0f) return sd::greedy_ws_bytes(B, K_max, V, dtype);
+    if (topk_on(top_k, V)) return sd::chain_topk_ws_bytes(B, K_max, V, top_k);
+    return sd::chain_full_ws_bytes(B, K_max, V, dtype);
+}
+
+}  // namespace
+
+extern "C" {
+
+int sd_abi_version(void) { return SD_ABI_VERSION; }
+
+const char* sd_status_str(int status) {
+    switch (status) {
+        case SD_OK: return "SD_OK";
+        case SD_EINVAL: return "SD_EINVAL: invalid argument";
+        case SD_EUNSUPPORTED: return "SD_EUNSUPPORTED: dtype/op combination not built";
+        case SD_EWORKSPACE: return "SD_EWORKSPACE: workspace too small";
+        case SD_EHIP: return "SD_EHIP: HIP launch failure";
+        default: return "unknown sd status";
+    }
+}
+
+sd_status_t sd_workspace_bytes(sd_op_t op, int32_t B, int32_t K_max, int32_t V, int32_t top_k,
+                               int32_t N, size_t* bytes) {
+    if (bytes == nullptr) return SD_EINVAL;
+    *bytes = 0;
+    switch (op) {
+        case SD_OP_CHAIN:
+            if (bad_size(B, K_max, V) || top_k < 0 || top_k > SD_MAX_TOPK) return SD_EINVAL;
+            // the larger of the full-vocabulary, top-k and greedy layouts for bf16
+            {
+                size_t a = sd::chain_full_ws_bytes(B, K_max, V, 0);
+                size_t b = sd::chain_full_ws_bytes(B, K_max, V, 1);
+                size_t c = topk_on(top_k, V) ? sd::chain_topk_ws_bytes(B, K_max, V, top_k) : 0;
+                size_t d = sd::greedy_ws_bytes(B, K_max, V, 0);
+                size_t m = a > b ? a : b;
+                m = m > c ? m : c;
+                *bytes = m > d ? m : d;
+            }
+            return SD_OK;
+        case SD_OP_GREEDY:
+            if (bad_size(B, K_max, V)) return SD_EINVAL;
+            *bytes = sd::greedy_ws_bytes(B, K_max, V, 0);   // f32 chunks are the smaller ones
+            return SD_OK;
+        case SD_OP_BUILD_TREE:
+            if (B < 1 || B > kMaxB || K_max < 0 || K_max > SD_MAX_TREE_K || V < 1 || V > kMaxV ||
+                N < 2 || N > SD_MAX_TREE_N)
+                return SD_EINVAL;
+            *bytes = sd::tree_build_ws_bytes(B, K_max, V, N);
+            return SD_OK;
+        case SD_OP_VERIFY_TREE:
+            if (B < 1 || B > kMaxB || V < 1 || V > kMaxV || N < 2 || N > SD_MAX_TREE_N)
+                return SD_EINVAL;
+            *bytes = sd::tree_verify_ws_bytes(B, N, V, 0);
+            return SD_OK;
+        case SD_OP_SELECT_LEN:
+            if (B < 1 || B > kMaxB || K_max < 0 || K_max > SD_MAX_K) return SD_EINVAL;
+            *bytes = 0;
+            return SD_OK;
+    }
+    return SD_EINVAL;
+}
+
+sd_status_t sd_verify_chain(const void* target_logits, const void* draft_logits, sd_dtype_t dtype,
+                            const int32_t* draft_tokens, const float* uniforms,
+                            const int32_t* cu_draft, int32_t B, int32_t K_max, int32_t V,
+                            float temperature, int32_t top_k, int32_t* accepted_len,
+                            int32_t* next_token, float* probs_out, float* resid_mass_out,
+                            int32_t* seq_status, void* workspace, size_t workspace_bytes,
+                            void* hip_stream) {
+    if (bad_size(B, K_max, V) || bad_dtype(dtype)) return SD_EINVAL;
+    if (!(temperature >= 0.0f) || !isfinite(temperature)) return SD_EINVAL;
+    if (top_k < 0 || top_k > SD_MAX_TOPK) return SD_EINVAL;
+    if (!target_logits || !accepted_len || !next_token || !workspace) return SD_EINVAL;
+    const bool greedy = temperature == 0.0f;
+    if (K_max > 0 && !draft_tokens) return SD_EINVAL;
+    if (!greedy && (!uniforms || (K_max > 0 && !draft_logits))) return SD_EINVAL;
+    const size_t need = chain_ws(B, K_max, V, (int)dtype, temperature, top_k);
+    if (workspace_bytes < need) return SD_EWORKSPACE;
+    hipStream_t st = static_cast<hipStream_t>(hip_stream);
+    if (greedy)
+        return from_hip(sd::launch_greedy(target_logits, (int)dtype, draft_tokens, cu_draft, B, K_max,
+                                          V, accepted_len, next_token, seq_status, workspace, st));
+    sd::ChainArgs a;
+    a.target = target_logits;
+    a.draft = draft_logits;
+    a.dtype = (int)dtype;
+    a.tokens = draft_tokens;
+    a.uniforms = uniforms;
+    a.cu = cu_draft;
+    a.B = B;
+    a.K_max = K_max;
+    a.V = V;
+    a.temperature = temperature;
+    a.top_k = top_k;
+    a.accepted_len = accepted_len;
+    a.next_token = next_token;
+    a.probs_out = probs_out;
+    a.resid_mass_out = resid_mass_out;
+    a.seq_status = seq_status;
+    a.ws = workspace;
+    a.stream = st;
+    if (topk_on(top_k, V)) return from_hip(sd::launch_chain_topk(a));
+    return from_hip(sd::launch_chain_full(a));
+}
+
+sd_status_t sd_verify_greedy(const void* target_logits, sd_dtype_t dtype,
+                             const int32_t* draft_tokens, const int32_t* cu_draft, int32_t B,
+                             int32_t K_max, int32_t V, int32_t* accepted_len, int32_t* next_token,
+                             int32_t* seq_status, void* workspace, size_t workspace_bytes,
+                             void* hip_stream) {
+    if (bad_size(B, K_max, V) || bad_dtype(dtype)) return SD_EINVAL;
+    if (!target_logits || !accepted_len || !next_token || !workspace) return SD_EINVAL;
+    if (K_max > 0 && !draft_tokens) return SD_EINVAL;
+    if (workspace_bytes < sd::greedy_ws_bytes(B, K_max, V, (int)dtype)) return SD_EWORKSPACE;
+    return from_hip(sd::launch_greedy(target_logits, (int)dtype, draft_tokens, cu_draft, B, K_max, V,
+                                      accepted_len, next_token, seq_status, workspace,
+                                      static_cast<hipStream_t>(hip_stream)));
+}
+
+sd_status_t sd_build_tree(const float* marginals, int32_t B, int32_t K, int32_t V, int32_t N,
+                          int32_t* node_token, int32_t* node_parent, int32_t* node_depth,
+                          float* node_score, uint64_t* node_anc_mask, int32_t* n_nodes,
+                          void* workspace, size_t workspace_bytes, void* hip_stream) {
+    if (B < 1 || B > kMaxB || K < 0 || K > SD_MAX_TREE_K || V < 1 || V > kMaxV || N < 2 ||
+        N > SD_MAX_TREE_N)
+        return SD_EINVAL;
+    if ((K > 0 && !marginals) || !node_token || !node_parent || !node_depth || !node_score ||
+        !node_anc_mask || !n_nodes)
+        return SD_EINVAL;
+    const size_t need = sd::tree_build_ws_bytes(B, K, V, N);
+    if (need > 0 && !workspace) return SD_EINVAL;
+    if (workspace_bytes < need) return SD_EWORKSPACE;
+    return from_hip(sd::launch_tree_build(marginals, B, K, V, N, node_token, node_parent, node_depth,
+                                          node_score, node_anc_mask, n_nodes, workspace,
+                                          static_cast<hipStream_t>(hip_stream)));
+}
+
+sd_status_t sd_verify_tree(const void* target_logits, sd_dtype_t dtype, const int32_t* node_token,
+                           const int32_t* node_parent, const int32_t* n_nodes, int32_t B, int32_t N,
+                           int32_t V, int32_t* path_nodes, int32_t* accepted_len,
+                           int32_t* next_token, void* workspace, size_t workspace_bytes,
+                           void* hip_stream) {
+    if (B < 1 || B > kMaxB || V < 1 || V > kMaxV || N < 2 || N > SD_MAX_TREE_N || bad_dtype(dtype))
+        return SD_EINVAL;
+    if (!target_logits || !node_token || !node_parent || !n_nodes || !path_nodes || !accepted_len ||
+        !next_token || !workspace)
+        return SD_EINVAL;
+    if (workspace_bytes < sd::tree_verify_ws_bytes(B, N, V, (int)dtype)) return SD_EWORKSPACE;
+    return from_hip(sd::launch_tree_verify(target_logits, (int)dtype, node_token, node_parent,
+                                           n_nodes, B, N, V, path_nodes, accepted_len, next_token,
+                                           workspace, static_cast<hipStream_t>(hip_stream)));
+}
+
+sd_status_t sd_select_len(const float* conf, int32_t B, int32_t K_max, float cost_per_position,
+                          int32_t* k_sel, float* expected_advance, int32_t* cu_sel,
+                          void* hip_stream) {
+    if (B < 1 || B > kMaxB || K_max < 0 || K_max > SD_MAX_K) return SD_EINVAL;
+    if (!isfinite(cost_per_position)) return SD_EINVAL;
+    if ((K_max > 0 && !conf) || !k_sel) return SD_EINVAL;
+    return from_hip(sd::launch_select_len(conf, B, K_max, cost_per_position, k_sel, expected_advance,
+                                          cu_sel, static_cast<hipStream_t>(hip_stream)));
+}
+
+}  // extern "C"

@@ -1,0 +1,179 @@
+// sd_device.hpp -- device helpers shared by the libsd kernels (gfx950, wave64).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace sd {
+
+constexpr int kWave = 64;
+constexpr int kBlock = 256;            // threads per workgroup for the streaming kernels
+constexpr int kWavesPerBlock = kBlock / kWave;
+
+// ---------------------------------------------------------------------------
+// Element access. Logit rows are fp32 or raw bf16 bit patterns; both are read
+// in 16-byte vectors (8 bf16 or 4 fp32 per lane per load).
+// ---------------------------------------------------------------------------
+struct Bf16 {
+    using raw = uint16_t;
+    static constexpr int kVec = 8;
+    __device__ static inline float at(const raw* p, int64_t i) {
+        return __uint_as_float(static_cast<uint32_t>(p[i]) << 16);
+    }
+    __device__ static inline void unpack(const uint4& v, float (&f)[kVec]) {
+        f[0] = __uint_as_float(v.x << 16); f[1] = __uint_as_float(v.x & 0xffff0000u);
+        f[2] = __uint_as_float(v.y << 16); f[3] = __uint_as_float(v.y & 0xffff0000u);
+        f[4] = __uint_as_float(v.z << 16); f[5] = __uint_as_float(v.z & 0xffff0000u);
+        f[6] = __uint_as_float(v.w << 16); f[7] = __uint_as_float(v.w & 0xffff0000u);
+    }
+    // A vector of -inf (fills lanes past the end of a range).
+    __device__ static inline uint4 neg_inf() {
+        return make_uint4(0xff80ff80u, 0xff80ff80u, 0xff80ff80u, 0xff80ff80u);
+    }
+};
+
+struct F32 {
+    using raw = float;
+    static constexpr int kVec = 4;
+    __device__ static inline float at(const raw* p, int64_t i) { return p[i]; }
+    __device__ static inline void unpack(const uint4& v, float (&f)[kVec]) {
+        f[0] = __uint_as_float(v.x); f[1] = __uint_as_float(v.y);
+        f[2] = __uint_as_float(v.z); f[3] = __uint_as_float(v.w);
+    }
+    __device__ static inline uint4 neg_inf() {
+        return make_uint4(0xff800000u, 0xff800000u, 0xff800000u, 0xff800000u);
+    }
+};
+
+__device__ __forceinline__ uint4 load16(const void* base, int64_t vec_index) {
+    return reinterpret_cast<const uint4*>(base)[vec_index];
+}
+
+// 2^x on the hardware transcendental unit (v_exp_f32).
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// NaN-ignoring maximum.
+__device__ __forceinline__ float nmax(float a, float b) { return (b > a || a != a) ? b : a; }
+
+// ---------------------------------------------------------------------------
+// Wave and block reductions (fixed order, deterministic).
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ double wave_sum(double v) {
+#pragma unroll
+    for (int o = kWave / 2; o > 0; o >>= 1) v += __shfl_xor(v, o, kWave);
+    return v;
+}
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+    for (int o = kWave / 2; o > 0; o >>= 1) v = nmax(v, __shfl_xor(v, o, kWave));
+    return v;
+}
+__device__ __forceinline__ int wave_min_int(int v) {
+#pragma unroll
+    for (int o = kWave / 2; o > 0; o >>= 1) v = min(v, __shfl_xor(v, o, kWave));
+    return v;
+}
+__device__ __forceinline__ int wave_max_int(int v) {
+#pragma unroll
+    for (int o = kWave / 2; o > 0; o >>= 1) v = max(v, __shfl_xor(v, o, kWave));
+    return v;
+}
+
+// Block-wide reductions for kBlock threads; `scratch` holds kWavesPerBlock entries.
+// Every thread receives the result. Contains __syncthreads().
+__device__ inline double block_sum(double v, double* scratch) {
+    v = wave_sum(v);
+    const int w = threadIdx.x / kWave;
+    __syncthreads();
+    if ((threadIdx.x & (kWave - 1)) == 0) scratch[w] = v;
+    __syncthreads();
+    double r = 0.0;
+#pragma unroll
+    for (int i = 0; i < kWavesPerBlock; ++i) r += scratch[i];
+    return r;
+}
+__device__ inline float block_max(float v, float* scratch) {
+    v = wave_max(v);
+    const int w = threadIdx.x / kWave;
+    __syncthreads();
+    if ((threadIdx.x & (kWave - 1)) == 0) scratch[w] = v;
+    __syncthreads();
+    float r = scratch[0];
+#pragma unroll
+    for (int i = 1; i < kWavesPerBlock; ++i) r = nmax(r, scratch[i]);
+    return r;
+}
+__device__ inline int block_min_int(int v, int* scratch) {
+    v = wave_min_int(v);
+    const int w = threadIdx.x / kWave;
+    __syncthreads();
+    if ((threadIdx.x & (kWave - 1)) == 0) scratch[w] = v;
+    __syncthreads();
+    int r = scratch[0];
+#pragma unroll
+    for (int i = 1; i < kWavesPerBlock; ++i) r = min(r, scratch[i]);
+    return r;
+}
+__device__ inline int block_max_int(int v, int* scratch) {
+    v = wave_max_int(v);
+    const int w = threadIdx.x / kWave;
+    __syncthreads();
+    if ((threadIdx.x & (kWave - 1)) == 0) scratch[w] = v;
+    __syncthreads();
+    int r = scratch[0];
+#pragma unroll
+    for (int i = 1; i < kWavesPerBlock; ++i) r = max(r, scratch[i]);
+    return r;
+}
+
+// Exclusive prefix sum over the block (fp64, thread order). Contains barriers.
+// `scratch` holds kWavesPerBlock entries.
+__device__ inline double block_exclusive_scan(double v, double* scratch, double* total) {
+    const int lane = threadIdx.x & (kWave - 1);
+    const int w = threadIdx.x / kWave;
+    double incl = v;
+#pragma unroll
+    for (int o = 1; o < kWave; o <<= 1) {
+        double t = __shfl_up(incl, o, kWave);
+        if (lane >= o) incl += t;
+    }
+    __syncthreads();
+    if (lane == kWave - 1) scratch[w] = incl;
+    __syncthreads();
+    double base = 0.0, tot = 0.0;
+#pragma unroll
+    for (int i = 0; i < kWavesPerBlock; ++i) {
+        if (i < w) base += scratch[i];
+        tot += scratch[i];
+    }
+    *total = tot;
+    return base + incl - v;
+}
+
+// Draft-row offset and length of sequence b. A packed length outside
+// [0, K_max] (an inconsistent cu) is clamped so that no kernel can index past
+// the K_max+1 slots it was sized for.
+__device__ __forceinline__ void seq_range(const int32_t* cu, int b, int K_max, int& d0, int& k) {
+    if (cu) {
+        d0 = cu[b];
+        k = cu[b + 1] - d0;
+        k = k < 0 ? 0 : (k > K_max ? K_max : k);
+    } else {
+        d0 = b * K_max;
+        k = K_max;
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Softmax partials. A partial (o, S) of a set of logits x says
+//   sum_x 2^(x*c - o) = S,  c = log2(e)/T rounded to fp32,
+// where the reference o is an fp32 value (normally fl32(m*c) for some logit m).
+// Partials of disjoint sets combine exactly in fp64 (see combine()).
+// ---------------------------------------------------------------------------
+struct Partial {
+    float o;        // reference (fp32); -inf for an empty set
+    float pad;
+    double S;       // sum relative to o; 0 for an empty set, non-finite for a bad set
+};
+
+}  // namespace sd

@@ -1,0 +1,302 @@
+// sd_greedy.hip -- greedy chain verification and the DDTree walk.
+//
+// Page "大模型投机解码：Medusa、MTP、EAGLE、DFlash、DDTree 与 DSpark"
+// (chzhyang.github.io): §1 (greedy results follow the target argmax; the first
+// mismatch ends the accepted prefix) and §5 DDTree (the walk follows the token
+// the target picks and stops at the first node without a matching child; that
+// token becomes the extra token).
+//
+// Both need the lowest-id argmax of many V-long rows: k_argmax streams each
+// (row, chunk) once with 16-byte loads and writes a (value, index) partial; a
+// one-wave kernel per sequence then combines partials and decides (ballot over
+// the chain, or a walk over at most 64 tree nodes).
+#include "sd_device.hpp"
+#include "sd_internal.hpp"
+
+#include <math.h>
+
+namespace sd {
+
+namespace {
+
+struct ArgPartial {
+    float v;      // maximum value (NaN ignored)
+    int32_t i;    // lowest index reaching it; kNone if the chunk is all NaN
+};
+constexpr int32_t kNone = 0x7fffffff;
+constexpr int kArgUnroll = 4;
+
+__device__ __forceinline__ bool arg_better(float v, int i, float bv, int bi) {
+    // (value desc, index asc); an empty candidate (kNone) never wins
+    if (i == kNone) return false;
+    if (bi == kNone) return true;
+    return v > bv || (v == bv && i < bi);
+}
+
+enum RowMapKind { kMapChain = 0, kMapTree = 1 };
+
+// grid: (sequence, slot, chunk). Chain: slot s <= k_b is target row cu[b]+b+s.
+// Tree: slot n < n_nodes[b] is row b*N+n.
+template <class E, bool VEC, int MAP>
+__global__ __launch_bounds__(kBlock) void k_argmax(const typename E::raw* __restrict__ rows,
+                                                   const int32_t* __restrict__ aux, int slots,
+                                                   int K_max, int V, int chunk, int n_chunks,
+                                                   ArgPartial* __restrict__ out) {
+    __shared__ float sv[kWavesPerBlock];
+    __shared__ int si[kWavesPerBlock];
+    constexpr int EV = E::kVec;
+    constexpr int U = kArgUnroll;
+    const int ch = blockIdx.x % n_chunks;
+    const int rest = blockIdx.x / n_chunks;
+    const int s = rest % slots;
+    const int b = rest / slots;
+    int64_t row;
+    if (MAP == kMapChain) {
+        int d0, k;
+        seq_range(aux, b, K_max, d0, k);
+        if (s > k) return;
+        row = (int64_t)d0 + b + s;
+    } else {
+        if (s >= aux[b]) return;
+        row = (int64_t)b * slots + s;
+    }
+    const typename E::raw* rp = rows + row * (int64_t)V;
+    const int beg = ch * chunk;
+    const int end = min(V, beg + chunk);
+    const int nvec = (end - beg + EV - 1) / EV;
+    float best = -INFINITY;
+    int bidx = kNone;
+    for (int v0 = threadIdx.x; v0 < nvec; v0 += kBlock * U) {
+        float f[U][EV];
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int vi = v0 + u * kBlock;
+            if (VEC) {
+                E::unpack(vi < nvec ? load16(rp + beg, vi) : E::neg_inf(), f[u]);
+            } else {
+#pragma unroll
+                for (int e = 0; e < EV; ++e) {
+                    const int j = beg + vi * EV + e;
+                    f[u][e] = (vi < nvec && j < end) ? E::at(rp, j) : NAN;
+                }
+            }
+        }
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int vi = v0 + u * kBlock;
+            float vmax = f[u][0];
+#pragma unroll
+            for (int e = 1; e < EV; ++e) vmax = nmax(vmax, f[u][e]);
+            // NaN-only vectors leave vmax NaN and never win; the -inf padding
+            // past the range has index >= end and is ignored below.
+            if (vi < nvec && (vmax > best || (bidx == kNone && vmax == vmax))) {
+                int e_hit = EV - 1;
+#pragma unroll
+                for (int e = EV - 1; e >= 0; --e)
+                    if (f[u][e] == vmax) e_hit = e;
+                const int j = beg + vi * EV + e_hit;
+                if (j < end) {
+                    best = vmax;
+                    bidx = j;
+                }
+            }
+        }
+    }
+    // wave then block reduction of (value desc, index asc)
+#pragma unroll
+    for (int o = kWave / 2; o > 0; o >>= 1) {
+        const float ov = __shfl_xor(best, o, kWave);
+        const int oi = __shfl_xor(bidx, o, kWave);
+        if (arg_better(ov, oi, best, bidx)) {
+            best = ov;
+            bidx = oi;
+        }
+    }
+    const int w = threadIdx.x / kWave;
+    if ((threadIdx.x & (kWave - 1)) == 0) {
+        sv[w] = best;
+        si[w] = bidx;
+    }
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        float bv = sv[0];
+        int bi = si[0];
+        for (int i = 1; i < kWavesPerBlock; ++i)
+            if (arg_better(sv[i], si[i], bv, bi)) {
+                bv = sv[i];
+                bi = si[i];
+            }
+        ArgPartial p;
+        p.v = bv;
+        p.i = bi;
+        out[((int64_t)b * slots + s) * n_chunks + ch] = p;
+    }
+}
+
+__device__ int combine_arg(const ArgPartial* p, int n_chunks) {
+    float bv = -INFINITY;
+    int bi = kNone;
+    for (int i = 0; i < n_chunks; ++i) {
+        const ArgPartial q = p[i];
+        if (arg_better(q.v, q.i, bv, bi)) {
+            bv = q.v;
+            bi = q.i;
+        }
+    }
+    return bi == kNone ? -1 : bi;
+}
+
+__global__ __launch_bounds__(kWave) void k_greedy_decide(
+    const ArgPartial* __restrict__ part, const int32_t* __restrict__ tok,
+    const int32_t* __restrict__ cu, int K_max, int V, int n_chunks, int32_t* __restrict__ A_out,
+    int32_t* __restrict__ next_out, int32_t* __restrict__ status_out) {
+    const int b = blockIdx.x;
+    const int lane = threadIdx.x;
+    const int slots = K_max + 1;
+    int d0, k;
+    seq_range(cu, b, K_max, d0, k);
+    const int64_t slot0 = (int64_t)b * slots;
+    bool acc = true;
+    int st = 0, g = -1;
+    if (lane < k) {
+        g = combine_arg(part + (slot0 + lane) * n_chunks, n_chunks);
+        const int y = tok[d0 + lane];
+        const bool yok = (y >= 0 && y < V);
+        acc = yok && g >= 0 && y == g;
+        st = (yok ? 0 : 1) | (g >= 0 ? 0 : 2);
+    }
+    const unsigned long long rej = __ballot(!acc);
+    const int A = rej ? (__ffsll(rej) - 1) : k;
+    int mine = (lane < k && lane <= A) ? st : 0;
+#pragma unroll
+    for (int o = kWave / 2; o > 0; o >>= 1) mine |= __shfl_xor(mine, o, kWave);
+    int next;
+    if (A < k) {
+        next = __shfl(g, A, kWave);
+    } else {
+        next = combine_arg(part + (slot0 + k) * n_chunks, n_chunks);
+    }
+    if (next < 0) mine |= 2;
+    if (lane == 0) {
+        A_out[b] = A;
+        next_out[b] = next;
+        if (status_out) status_out[b] = mine;
+    }
+}
+
+__global__ __launch_bounds__(kWave) void k_tree_walk(
+    const ArgPartial* __restrict__ part, const int32_t* __restrict__ node_token,
+    const int32_t* __restrict__ node_parent, const int32_t* __restrict__ n_nodes, int N,
+    int n_chunks, int32_t* __restrict__ path, int32_t* __restrict__ A_out,
+    int32_t* __restrict__ next_out) {
+    const int b = blockIdx.x;
+    const int lane = threadIdx.x;
+    const int nn = n_nodes[b];
+    int my_tok = -1, my_par = -2, my_g = -1;
+    if (lane < nn && lane < N) {
+        my_tok = node_token[(int64_t)b * N + lane];
+        my_par = node_parent[(int64_t)b * N + lane];
+        my_g = combine_arg(part + ((int64_t)b * N + lane) * n_chunks, n_chunks);
+    }
+    if (lane < N) path[(int64_t)b * N + lane] = -1;
+    int node = 0, len = 0, next = -1;
+    for (int step = 0; step < N; ++step) {
+        const int g = __shfl(my_g, node, kWave);
+        const bool hit = (lane >= 1) && (lane < nn) && (my_par == node) && (my_tok == g) && (g >= 0);
+        const unsigned long long m = __ballot(hit);
+        if (!m) {
+            next = g;
+            break;
+        }
+        const int child = __ffsll(m) - 1;
+        if (lane == 0) path[(int64_t)b * N + len] = child;
+        ++len;
+        node = child;
+    }
+    if (lane == 0) {
+        A_out[b] = len;
+        next_out[b] = next;
+    }
+}
+
+}  // namespace
+
+size_t greedy_ws_bytes(int B, int K_max, int V, int dtype) {
+    Carve cv;
+    cv.take((size_t)B * (K_max + 1) * n_chunks_for(V, dtype) * sizeof(ArgPartial));
+    return cv.off;
+}
+
+size_t tree_verify_ws_bytes(int B, int N, int V, int dtype) {
+    Carve cv;
+    cv.take((size_t)B * N * n_chunks_for(V, dtype) * sizeof(ArgPartial));
+    return cv.off;
+}
+
+template <class E, bool VEC>
+static hipError_t greedy_impl(const void* target, const int32_t* tokens, const int32_t* cu, int B,
+                              int K_max, int V, int dtype, int32_t* A, int32_t* next, int32_t* st,
+                              void* ws, hipStream_t stream) {
+    const int nc = n_chunks_for(V, dtype);
+    const int chunk = chunk_elems(dtype);
+    ArgPartial* part = static_cast<ArgPartial*>(ws);
+    const unsigned grid = (unsigned)((size_t)B * (K_max + 1) * nc);
+    hipLaunchKernelGGL((k_argmax<E, VEC, kMapChain>), dim3(grid), dim3(kBlock), 0, stream,
+                       static_cast<const typename E::raw*>(target), cu, K_max + 1, K_max, V, chunk,
+                       nc, part);
+    hipLaunchKernelGGL(k_greedy_decide, dim3(B), dim3(kWave), 0, stream, part, tokens, cu, K_max, V,
+                       nc, A, next, st);
+    return hipGetLastError();
+}
+
+hipError_t launch_greedy(const void* target, int dtype, const int32_t* tokens, const int32_t* cu,
+                         int B, int K_max, int V, int32_t* accepted_len, int32_t* next_token,
+                         int32_t* seq_status, void* ws, hipStream_t stream) {
+    if (dtype == 1) {
+        if (V % Bf16::kVec == 0)
+            return greedy_impl<Bf16, true>(target, tokens, cu, B, K_max, V, dtype, accepted_len,
+                                           next_token, seq_status, ws, stream);
+        return greedy_impl<Bf16, false>(target, tokens, cu, B, K_max, V, dtype, accepted_len,
+                                        next_token, seq_status, ws, stream);
+    }
+    if (V % F32::kVec == 0)
+        return greedy_impl<F32, true>(target, tokens, cu, B, K_max, V, dtype, accepted_len,
+                                      next_token, seq_status, ws, stream);
+    return greedy_impl<F32, false>(target, tokens, cu, B, K_max, V, dtype, accepted_len, next_token,
+                                   seq_status, ws, stream);
+}
+
+template <class E, bool VEC>
+static hipError_t tree_verify_impl(const void* target, const int32_t* tok, const int32_t* par,
+                                   const int32_t* nn, int B, int N, int V, int dtype, int32_t* path,
+                                   int32_t* A, int32_t* next, void* ws, hipStream_t stream) {
+    const int nc = n_chunks_for(V, dtype);
+    const int chunk = chunk_elems(dtype);
+    ArgPartial* part = static_cast<ArgPartial*>(ws);
+    const unsigned grid = (unsigned)((size_t)B * N * nc);
+    hipLaunchKernelGGL((k_argmax<E, VEC, kMapTree>), dim3(grid), dim3(kBlock), 0, stream,
+                       static_cast<const typename E::raw*>(target), nn, N, 0, V, chunk, nc, part);
+    hipLaunchKernelGGL(k_tree_walk, dim3(B), dim3(kWave), 0, stream, part, tok, par, nn, N, nc,
+                       path, A, next);
+    return hipGetLastError();
+}
+
+hipError_t launch_tree_verify(const void* target, int dtype, const int32_t* tok, const int32_t* par,
+                              const int32_t* n_nodes, int B, int N, int V, int32_t* path,
+                              int32_t* accepted_len, int32_t* next_token, void* ws,
+                              hipStream_t stream) {
+    if (dtype == 1) {
+        if (V % Bf16::kVec == 0)
+            return tree_verify_impl<Bf16, true>(target, tok, par, n_nodes, B, N, V, dtype, path,
+                                                accepted_len, next_token, ws, stream);
+        return tree_verify_impl<Bf16, false>(target, tok, par, n_nodes, B, N, V, dtype, path,
+                                             accepted_len, next_token, ws, stream);
+    }
+    if (V % F32::kVec == 0)
+        return tree_verify_impl<F32, true>(target, tok, par, n_nodes, B, N, V, dtype, path,
+                                           accepted_len, next_token, ws, stream);
+    return tree_verify_impl<F32, false>(target, tok, par, n_nodes, B, N, V, dtype, path,
+                                        accepted_len, next_token, ws, stream);
+}
+
+}  // namespace sd

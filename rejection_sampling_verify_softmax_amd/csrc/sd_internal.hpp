@@ -1,0 +1,76 @@
+// sd_internal.hpp -- host-side launch interface between the ABI layer and the
+// kernel files of libsd. Not installed; not part of the C ABI.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace sd {
+
+// Elements of one row handled by one workgroup of the streaming kernels.
+// Multiples of kBlock * 16-byte vectors so that chunk boundaries are vector
+// aligned.
+constexpr int kMaxTopk = 256;
+constexpr int kMaxTreeK = 16;
+constexpr int kChunkBf16 = 16384;
+constexpr int kChunkF32 = 8192;
+
+inline int chunk_elems(int dtype) { return dtype == 1 ? kChunkBf16 : kChunkF32; }
+inline int n_chunks_for(int V, int dtype) {
+    const int c = chunk_elems(dtype);
+    return (V + c - 1) / c;
+}
+
+// Sub-allocation of the caller's workspace: 256-byte aligned regions.
+struct Carve {
+    size_t off = 0;
+    size_t take(size_t bytes) {
+        size_t o = off;
+        off += (bytes + 255) & ~size_t(255);
+        return o;
+    }
+};
+
+struct ChainArgs {
+    const void* target;
+    const void* draft;
+    int dtype;                 // 0 f32, 1 bf16
+    const int32_t* tokens;
+    const float* uniforms;
+    const int32_t* cu;
+    int B, K_max, V;
+    float temperature;
+    int top_k;
+    int32_t* accepted_len;
+    int32_t* next_token;
+    float* probs_out;
+    float* resid_mass_out;
+    int32_t* seq_status;
+    void* ws;
+    hipStream_t stream;
+};
+
+// Workspace bytes of each path (all sizes already validated).
+size_t chain_full_ws_bytes(int B, int K_max, int V, int dtype);
+size_t chain_topk_ws_bytes(int B, int K_max, int V, int top_k);
+size_t greedy_ws_bytes(int B, int K_max, int V, int dtype);
+size_t tree_build_ws_bytes(int B, int K, int V, int N);
+size_t tree_verify_ws_bytes(int B, int N, int V, int dtype);
+
+hipError_t launch_chain_full(const ChainArgs& a);
+hipError_t launch_chain_topk(const ChainArgs& a);
+hipError_t launch_greedy(const void* target, int dtype, const int32_t* tokens, const int32_t* cu,
+                         int B, int K_max, int V, int32_t* accepted_len, int32_t* next_token,
+                         int32_t* seq_status, void* ws, hipStream_t stream);
+hipError_t launch_tree_build(const float* marg, int B, int K, int V, int N, int32_t* tok,
+                             int32_t* par, int32_t* dep, float* score, uint64_t* anc,
+                             int32_t* n_nodes, void* ws, hipStream_t stream);
+hipError_t launch_tree_verify(const void* target, int dtype, const int32_t* tok, const int32_t* par,
+                              const int32_t* n_nodes, int B, int N, int V, int32_t* path,
+                              int32_t* accepted_len, int32_t* next_token, void* ws,
+                              hipStream_t stream);
+hipError_t launch_select_len(const float* conf, int B, int K_max, float cost, int32_t* k_sel,
+                             float* adv, int32_t* cu_sel, hipStream_t stream);
+
+}  // namespace sd

@@ -1,0 +1,68 @@
+// sd_select.hip -- DSpark-style choice of verify length.
+//
+// Page "大模型投机解码：Medusa、MTP、EAGLE、DFlash、DDTree 与 DSpark"
+// (chzhyang.github.io), §5 DSpark: with per-position confidences c_i, the
+// chance that the prefix survives to position j is s_j = prod_{i<=j} c_i and the
+// expected advance for verify length k is 1 + sum_{j<=k} s_j; the scheduler asks
+// whether one more verified position is worth its cost.
+//
+// One workgroup: each thread takes a contiguous run of sequences, forms the
+// fp32 running product, extends k while s_j beats the per-position cost, then a
+// block scan turns the lengths into packed offsets cu_sel (ready for a packed
+// chain verify on the same stream, without a host round trip).
+#include "sd_device.hpp"
+#include "sd_internal.hpp"
+
+namespace sd {
+
+namespace {
+
+__global__ __launch_bounds__(kBlock) void k_select_len(const float* __restrict__ conf, int B,
+                                                       int K_max, float cost,
+                                                       int32_t* __restrict__ k_sel,
+                                                       float* __restrict__ adv,
+                                                       int32_t* __restrict__ cu_sel) {
+    __shared__ double scan_scratch[kWavesPerBlock];
+    const int per = (B + kBlock - 1) / kBlock;
+    const int b0 = threadIdx.x * per;
+    const int b1 = min(B, b0 + per);
+    int local = 0;
+    for (int b = b0; b < b1; ++b) {
+        float s = 1.0f;
+        double sum = 0.0;
+        int k = 0;
+        bool go = true;
+        for (int j = 0; j < K_max; ++j) {
+            s = s * conf[(int64_t)b * K_max + j];     // fp32, left to right
+            if (go && s > cost) {
+                k = j + 1;
+                sum += (double)s;
+            } else {
+                go = false;
+            }
+        }
+        k_sel[b] = k;
+        if (adv) adv[b] = (float)(1.0 + sum);
+        local += k;
+    }
+    if (cu_sel == nullptr) return;
+    double total;
+    const double excl = block_exclusive_scan((double)local, scan_scratch, &total);
+    int run = (int)excl;
+    for (int b = b0; b < b1; ++b) {
+        cu_sel[b] = run;
+        run += k_sel[b];
+    }
+    if (threadIdx.x == kBlock - 1) cu_sel[B] = (int)total;
+}
+
+}  // namespace
+
+hipError_t launch_select_len(const float* conf, int B, int K_max, float cost, int32_t* k_sel,
+                             float* adv, int32_t* cu_sel, hipStream_t stream) {
+    hipLaunchKernelGGL(k_select_len, dim3(1), dim3(kBlock), 0, stream, conf, B, K_max, cost, k_sel,
+                       adv, cu_sel);
+    return hipGetLastError();
+}
+
+}  // namespace sd

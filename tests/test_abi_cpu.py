@@ -1,0 +1,125 @@
+"""Host-side checks of the C ABI (no GPU): the library loads, exports every
+entry point include/sd.h declares, and rejects invalid calls before any HIP call."""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "sd.h")
+
+
+@pytest.fixture(scope="module")
+def L():
+    import rejection_sampling_verify_softmax_amd as sd
+    if not os.path.exists(sd.LIB_PATH):
+        from rejection_sampling_verify_softmax_amd import _build
+        _build.build()
+    return sd.lib()
+
+
+def declared_symbols():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(sd_[a-z_]+)\s*\(", text)))
+
+
+def test_header_declares_the_five_calls():
+    names = declared_symbols()
+    for n in ("sd_verify_chain", "sd_verify_greedy", "sd_build_tree", "sd_verify_tree", "sd_select_len",
+              "sd_workspace_bytes", "sd_abi_version", "sd_status_str"):
+        assert n in names
+
+
+def test_library_exports_every_declared_symbol(L):
+    import rejection_sampling_verify_softmax_amd as sd
+    out = os.popen(f"nm -D --defined-only {sd.LIB_PATH}").read()
+    exported = set(re.findall(r" T (sd_\w+)", out))
+    missing = [n for n in declared_symbols() if n not in exported]
+    assert not missing, missing
+    for n in declared_symbols():
+        assert hasattr(L, n)
+
+
+def test_version_and_status_strings(L):
+    assert L.sd_abi_version() == 1
+    for s in range(5):
+        assert L.sd_status_str(s).startswith(b"SD_")
+    assert L.sd_status_str(99) == b"unknown sd status"
+
+
+def _chain(L, **kw):
+    a = dict(target=1, draft=1, dtype=1, tokens=1, uni=1, cu=None, B=2, K=3, V=100, T=1.0, top_k=0,
+             A=1, nxt=1, probs=None, resid=None, st=None, ws=1, wsb=1 << 30, stream=None)
+    a.update(kw)
+    f = lambda v: None if v is None else ctypes.c_void_p(v)
+    return L.sd_verify_chain(f(a["target"]), f(a["draft"]), a["dtype"], f(a["tokens"]), f(a["uni"]),
+                             f(a["cu"]), a["B"], a["K"], a["V"], ctypes.c_float(a["T"]), a["top_k"],
+                             f(a["A"]), f(a["nxt"]), f(a["probs"]), f(a["resid"]), f(a["st"]),
+                             f(a["ws"]), ctypes.c_size_t(a["wsb"]), f(a["stream"]))
+
+
+@pytest.mark.parametrize("bad", [
+    dict(B=0), dict(B=-1), dict(V=0), dict(V=1 << 24), dict(K=65), dict(K=-1),
+    dict(T=-1.0), dict(T=float("nan")), dict(T=float("inf")), dict(top_k=-1), dict(top_k=257),
+    dict(dtype=7), dict(target=None), dict(A=None), dict(nxt=None), dict(ws=None),
+    dict(tokens=None), dict(uni=None), dict(draft=None),
+])
+def test_chain_rejects_invalid_arguments(L, bad):
+    assert _chain(L, **bad) == 1          # SD_EINVAL, nothing launched
+
+
+def test_chain_greedy_needs_no_draft_or_uniforms_but_checks_workspace(L):
+    # T == 0: draft and uniforms may be NULL; a 1-byte workspace is too small
+    assert _chain(L, T=0.0, draft=None, uni=None, wsb=1) == 3      # SD_EWORKSPACE
+
+
+def test_workspace_too_small(L):
+    assert _chain(L, wsb=16) == 3
+
+
+def test_workspace_bytes(L):
+    import rejection_sampling_verify_softmax_amd as sd
+    n = sd.workspace_bytes(sd.OP_CHAIN, 512, 8, 128256, 0)
+    assert n > 0 and n % 256 == 0
+    assert sd.workspace_bytes(sd.OP_CHAIN, 256, 5, 151936, 50) >= 256 * 6 * 2 * 50 * 8
+    assert sd.workspace_bytes(sd.OP_BUILD_TREE, 32, 16, 32000, 0, 64) >= 32 * 16 * 63 * 8
+    assert sd.workspace_bytes(sd.OP_SELECT_LEN, 512, 8) == 0
+    out = ctypes.c_size_t(0)
+    assert L.sd_workspace_bytes(0, 0, 8, 100, 0, 0, ctypes.byref(out)) == 1
+    assert L.sd_workspace_bytes(2, 4, 17, 100, 0, 64, ctypes.byref(out)) == 1   # tree K > 16
+    assert L.sd_workspace_bytes(2, 4, 16, 100, 0, 65, ctypes.byref(out)) == 1   # N > 64
+    assert L.sd_workspace_bytes(9, 4, 16, 100, 0, 64, ctypes.byref(out)) == 1   # unknown op
+    assert L.sd_workspace_bytes(0, 4, 4, 100, 0, 0, None) == 1
+
+
+def test_other_calls_reject_invalid_arguments(L):
+    v = ctypes.c_void_p
+    one = v(1)
+    # greedy
+    assert L.sd_verify_greedy(None, 1, one, None, 2, 3, 100, one, one, None, one, 1 << 30, None) == 1
+    assert L.sd_verify_greedy(one, 1, one, None, 2, 3, 100, one, one, None, one, 8, None) == 3
+    # tree build: N out of range, K out of range, null outputs
+    assert L.sd_build_tree(one, 2, 4, 100, 1, one, one, one, one, one, one, one, 1 << 30, None) == 1
+    assert L.sd_build_tree(one, 2, 17, 100, 8, one, one, one, one, one, one, one, 1 << 30, None) == 1
+    assert L.sd_build_tree(one, 2, 4, 100, 8, None, one, one, one, one, one, one, 1 << 30, None) == 1
+    assert L.sd_build_tree(one, 2, 4, 100, 8, one, one, one, one, one, one, one, 8, None) == 3
+    # tree verify
+    assert L.sd_verify_tree(one, 1, one, one, one, 2, 65, 100, one, one, one, one, 1 << 30, None) == 1
+    assert L.sd_verify_tree(one, 5, one, one, one, 2, 8, 100, one, one, one, one, 1 << 30, None) == 1
+    # select_len
+    assert L.sd_select_len(one, 0, 8, ctypes.c_float(0.1), one, None, None, None) == 1
+    assert L.sd_select_len(one, 4, 65, ctypes.c_float(0.1), one, None, None, None) == 1
+    assert L.sd_select_len(one, 4, 8, ctypes.c_float(float("nan")), one, None, None, None) == 1
+    assert L.sd_select_len(one, 4, 8, ctypes.c_float(0.1), None, None, None, None) == 1
+
+
+def test_binding_fails_loudly_without_gpu():
+    import torch
+    import rejection_sampling_verify_softmax_amd as sd
+    if torch.cuda.is_available():
+        pytest.skip("GPU present")
+    x = torch.zeros(8, 16)
+    with pytest.raises(ValueError):
+        sd.verify_chain(x, x, torch.zeros(4, dtype=torch.int32), torch.zeros(8), 1.0, K_max=1)

@@ -1,0 +1,341 @@
+"""GPU parity: the HIP path through the C ABI against the CPU oracle.
+
+Small cases (several 16-byte-vector tiles, several chunks, ragged tails) run
+the oracle on every sequence; the five full-size workloads run the oracle on a
+sample of sequences, in the launch configuration the benchmark times.
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import rejection_sampling_verify_softmax_amd as sd
+from rejection_sampling_verify_softmax_amd import workloads as wl
+
+from parity import compare_chain, oracle_chain, sample_seqs, subset_host
+
+pytestmark = pytest.mark.gpu
+
+
+def _say(msg):
+    print(msg, flush=True)
+
+
+def run_chain(case, **kw):
+    return sd.verify_chain(case.target, case.draft, case.tokens, case.uniforms, case.temperature,
+                           top_k=case.top_k, cu=case.cu, B=case.B, K_max=case.K_max,
+                           want_probs=True, want_resid=True, **kw)
+
+
+# --------------------------------------------------------------------------
+# stochastic chain, full vocabulary
+# --------------------------------------------------------------------------
+
+def test_config1_chain_f32():
+    _say("config 1: B=1 K=4 V=1000 fp32")
+    case = wl.gen_config1(device="cuda")
+    out = run_chain(case)
+    info = compare_chain(out, oracle_chain(case))
+    _say(f"  {info}")
+
+
+@pytest.mark.parametrize("dtype,V,T", [("bf16", 40000, 0.9), ("bf16", 16384 * 2 + 8, 1.0),
+                                       ("f32", 20000, 1.3), ("f32", 1001, 1.0), ("bf16", 777, 0.6)])
+def test_chain_small_all_sequences(dtype, V, T):
+    _say(f"chain small {dtype} V={V} T={T}")
+    case = wl.gen_base_noise_chain(11 + V, B=24, K=5, V=V, base_sigma=2.0, noise_sigma=0.6,
+                                   temperature=T, dtype=dtype, device="cuda")
+    out = run_chain(case)
+    info = compare_chain(out, oracle_chain(case))
+    _say(f"  {info}")
+    A = out["accepted_len"].cpu().numpy()
+    assert (A < case.K_max).any()
+
+
+def test_chain_packed_ragged_lengths():
+    lengths = [0, 3, 1, 5, 0, 2, 8, 4, 1, 0, 6, 7]
+    _say(f"packed chain lengths {lengths}")
+    case = wl.ragged_chain(5, lengths, 30000, dtype="bf16", device="cuda")
+    out = run_chain(case)
+    info = compare_chain(out, oracle_chain(case))
+    _say(f"  {info}")
+    # a packed call matches the dense call of the same rows sequence by sequence
+    for b, k in enumerate(lengths):
+        cu = case.cu.cpu().numpy()
+        sub = wl.ChainCase(B=1, K_max=k, V=case.V, temperature=case.temperature, top_k=0,
+                           target=case.target[cu[b] + b: cu[b + 1] + b + 1].contiguous(),
+                           draft=case.draft[cu[b]: cu[b + 1]].contiguous(),
+                           tokens=case.tokens[cu[b]: cu[b + 1]].contiguous(),
+                           uniforms=case.uniforms[cu[b] + b: cu[b + 1] + b + 1].contiguous())
+        o1 = run_chain(sub)
+        assert int(o1["accepted_len"][0]) == int(out["accepted_len"][b])
+        assert int(o1["next_token"][0]) == int(out["next_token"][b])
+
+
+def test_chain_edge_cases():
+    _say("chain edge cases")
+    V, K, B = 4096, 3, 6
+    g = torch.Generator(device="cuda").manual_seed(3)
+    tgt = torch.randn(B * (K + 1), V, generator=g, device="cuda") * 2
+    dft = torch.randn(B * K, V, generator=g, device="cuda") * 2
+    tok = torch.randint(0, V, (B * K,), generator=g, device="cuda", dtype=torch.int32)
+    uni = wl.grid_uniforms((B * (K + 1),), g, "cuda")
+    # seq 0: draft equals target -> everything accepted
+    dft[0:K] = tgt[0:K]
+    # seq 1: bad token at position 1
+    tok[K + 1] = V + 5
+    # seq 2: NaN target row at position 0
+    tgt[2 * (K + 1)] = float("nan")
+    # seq 3: -inf except one entry in its target row 1, and a -inf-only draft chunk region
+    tgt[3 * (K + 1) + 1] = float("-inf")
+    tgt[3 * (K + 1) + 1, 17] = 0.0
+    dft[3 * K + 2, :2048] = float("-inf")
+    # seq 4: +inf in the extra-token row
+    tgt[4 * (K + 1) + K, 5] = float("inf")
+    # seq 5: extreme logits (one-pass reference far below the max)
+    tgt[5 * (K + 1), 3000] = 400.0
+    dft[5 * K, 100] = -300.0
+    for dtype in (torch.float32, torch.bfloat16):
+        case = wl.ChainCase(B=B, K_max=K, V=V, temperature=1.0, top_k=0, target=tgt.to(dtype),
+                            draft=dft.to(dtype), tokens=tok, uniforms=uni)
+        out = run_chain(case)
+        ref = oracle_chain(case)
+        info = compare_chain(out, ref)
+        _say(f"  {dtype}: {info} A={out['accepted_len'].tolist()} st={out['status'].tolist()}")
+        assert int(out["accepted_len"][0]) == K
+        assert int(out["status"][1]) & sd.SEQ_BAD_TOKEN or int(out["accepted_len"][1]) < 1
+        assert int(out["status"][2]) & sd.SEQ_NONFINITE and int(out["next_token"][2]) == -1
+
+
+def test_chain_tiny_vocab_and_k0():
+    _say("V=1, K_max=0 and all-zero packed lengths")
+    for V in (1, 2, 8):
+        case = wl.gen_base_noise_chain(1, B=5, K=2, V=V, base_sigma=1.0, noise_sigma=0.5,
+                                       temperature=1.0, dtype="f32", device="cuda")
+        compare_chain(run_chain(case), oracle_chain(case))
+    case = wl.gen_base_noise_chain(2, B=7, K=0, V=300, base_sigma=1.0, noise_sigma=0.5,
+                                   temperature=1.0, dtype="bf16", device="cuda")
+    compare_chain(run_chain(case), oracle_chain(case))
+    case = wl.ragged_chain(3, [0, 0, 0], 500, dtype="bf16", device="cuda")
+    compare_chain(run_chain(case), oracle_chain(case))
+
+
+def test_chain_run_twice_bit_identical():
+    case = wl.gen_base_noise_chain(9, B=16, K=6, V=50000, base_sigma=2.0, noise_sigma=0.7,
+                                   temperature=1.0, dtype="bf16", device="cuda")
+    a = run_chain(case)
+    b = run_chain(case)
+    for k in a:
+        assert torch.equal(a[k], b[k]), k
+
+
+# --------------------------------------------------------------------------
+# greedy
+# --------------------------------------------------------------------------
+
+def _greedy_ref(case):
+    h = subset_host(case, range(case.B))
+    return oracle.verify_greedy(h["target"], h["tokens"], h["cu"], case.B, case.K_max, case.V)
+
+
+def test_config2_greedy_full():
+    _say("config 2: greedy B=64 K=3 V=128256 bf16 (all sequences)")
+    case = wl.gen_config2(device="cuda")
+    out = sd.verify_greedy(case.target, case.tokens, K_max=case.K_max, B=case.B)
+    ref = _greedy_ref(case)
+    np.testing.assert_array_equal(out["accepted_len"].cpu().numpy(), ref["A"])
+    np.testing.assert_array_equal(out["next_token"].cpu().numpy(), ref["next"])
+    np.testing.assert_array_equal(out["status"].cpu().numpy(), ref["status"])
+    # the same through sd_verify_chain with T = 0
+    o2 = sd.verify_chain(case.target, None, case.tokens, None, 0.0, K_max=case.K_max, B=case.B)
+    assert torch.equal(o2["accepted_len"], out["accepted_len"])
+    assert torch.equal(o2["next_token"], out["next_token"])
+    _say(f"  mean A = {ref['A'].mean():.3f}")
+
+
+def test_greedy_ties_and_nan():
+    V, K, B = 3000, 2, 4
+    t = torch.zeros(B * (K + 1), V, device="cuda")
+    t[0, [5, 2900, 17]] = 3.0           # tie: lowest id 5
+    t[1, :] = float("-inf")             # all -inf: argmax 0
+    t[2, :] = float("nan")              # all NaN: no argmax
+    t[3, 1000] = float("nan"); t[3, 999] = 1.0
+    tok = torch.tensor([5, 0, 1, 0, 0, 0, 0, 0], dtype=torch.int32, device="cuda")
+    for dtype in (torch.float32, torch.bfloat16):
+        case = wl.GreedyCase(B=B, K_max=K, V=V, target=t.to(dtype), tokens=tok)
+        out = sd.verify_greedy(case.target, case.tokens, K_max=K, B=B)
+        ref = _greedy_ref(case)
+        np.testing.assert_array_equal(out["accepted_len"].cpu().numpy(), ref["A"])
+        np.testing.assert_array_equal(out["next_token"].cpu().numpy(), ref["next"])
+        np.testing.assert_array_equal(out["status"].cpu().numpy(), ref["status"])
+
+
+# --------------------------------------------------------------------------
+# top-k chain
+# --------------------------------------------------------------------------
+
+@pytest.mark.parametrize("top_k,V", [(50, 3000), (1, 2000), (7, 151), (256, 40000), (50, 999)])
+def test_topk_small_all_sequences(top_k, V):
+    _say(f"top-k {top_k} V={V}")
+    case = wl.gen_config3(device="cuda", seed=77 + top_k, B=12, K=4, V=V, top_k=top_k)
+    out = run_chain(case)
+    info = compare_chain(out, oracle_chain(case))
+    _say(f"  {info}")
+
+
+def test_topk_ties_at_kth_value():
+    # many equal bf16 values straddle the k-th position
+    V, K, B = 5000, 3, 8
+    g = torch.Generator(device="cuda").manual_seed(4)
+    base = torch.randint(-4, 5, (B * (K + 1), V), generator=g, device="cuda").float()
+    dft = torch.randint(-4, 5, (B * K, V), generator=g, device="cuda").float()
+    case = wl.ChainCase(B=B, K_max=K, V=V, temperature=0.8, top_k=50,
+                        target=base.to(torch.bfloat16), draft=dft.to(torch.bfloat16),
+                        tokens=wl.gumbel_draft_tokens(dft.to(torch.bfloat16), 0.8, 50, g),
+                        uniforms=wl.grid_uniforms((B * (K + 1),), g, "cuda"))
+    info = compare_chain(run_chain(case), oracle_chain(case))
+    _say(f"  ties: {info}")
+
+
+def test_config3_topk_full_sampled():
+    _say("config 3: B=256 K=5 V=151936 bf16 T=0.7 top-k 50 (sampled)")
+    case = wl.gen_config3(device="cuda")
+    out = run_chain(case)
+    seqs = sample_seqs(case.B, 40, seed=3)
+    info = compare_chain(out, oracle_chain(case, seqs))
+    A = out["accepted_len"].float().mean().item()
+    _say(f"  {info} mean A={A:.3f}")
+
+
+# --------------------------------------------------------------------------
+# DDTree build and walk
+# --------------------------------------------------------------------------
+
+def _tree_compare(out, ref):
+    for k in ("token", "parent", "depth", "n_nodes"):
+        np.testing.assert_array_equal(out[k].cpu().numpy(), ref[k], err_msg=k)
+    np.testing.assert_array_equal(out["anc_mask"].cpu().numpy().view(np.uint64), ref["anc_mask"])
+    np.testing.assert_array_equal(out["score"].cpu().numpy(), ref["score"])   # same fp32 products
+
+
+@pytest.mark.parametrize("B,K,V,N", [(4, 3, 5, 20), (6, 16, 700, 64), (3, 2, 3, 64), (5, 16, 31, 64),
+                                     (2, 1, 1000, 10)])
+def test_tree_build_small(B, K, V, N):
+    case = wl.gen_config4(device="cuda", seed=5 + V, B=B, K=K, V=V, N=N, sigma=1.5)
+    out = sd.build_tree(case.marginals, N)
+    ref = oracle.build_tree(wl.to_host_f32(case.marginals), B, K, V, N)
+    _tree_compare(out, ref)
+
+
+def test_tree_build_ties():
+    B, K, V, N = 3, 4, 40, 30
+    m = torch.full((B, K, V), 1.0 / V, device="cuda")        # every score ties
+    m[1, :, :8] = 0.05
+    out = sd.build_tree(m, N)
+    ref = oracle.build_tree(m.cpu().numpy(), B, K, V, N)
+    _tree_compare(out, ref)
+
+
+def test_config4_tree_full():
+    _say("config 4: tree B=32 K=16 V=32000 N=64")
+    case = wl.gen_config4(device="cuda")
+    tree = sd.build_tree(case.marginals, case.N)
+    ref = oracle.build_tree(wl.to_host_f32(case.marginals), case.B, case.K, case.V, case.N)
+    _tree_compare(tree, ref)
+    target = case.target_for_depths(tree["depth"], tree["n_nodes"])
+    walk = sd.verify_tree(target, tree)
+    wref = oracle.verify_tree(wl.to_host_f32(target), ref["token"], ref["parent"], ref["n_nodes"],
+                              case.B, case.N, case.V)
+    np.testing.assert_array_equal(walk["accepted_len"].cpu().numpy(), wref["A"])
+    np.testing.assert_array_equal(walk["next_token"].cpu().numpy(), wref["next"])
+    np.testing.assert_array_equal(walk["path"].cpu().numpy(), wref["path"])
+    _say(f"  mean depth-1 nodes {(ref['depth'] == 1).sum() / case.B:.1f}, mean walk {wref['A'].mean():.2f}")
+
+
+def test_tree_walk_planted():
+    V, N, B = 12, 6, 2
+    tok = torch.tensor([[-1, 4, 7, 2, 9, -1]] * B, dtype=torch.int32, device="cuda")
+    par = torch.tensor([[-1, 0, 0, 1, 3, -1]] * B, dtype=torch.int32, device="cuda")
+    nn = torch.tensor([5, 5], dtype=torch.int32, device="cuda")
+    rows = torch.full((B, N, V), -5.0, device="cuda")
+    for n, t in enumerate([4, 2, 0, 9, 11, 0]):
+        rows[0, n, t] = 5.0
+    for n, t in enumerate([3, 0, 0, 0, 0, 0]):
+        rows[1, n, t] = 5.0
+    out = sd.verify_tree(rows.to(torch.bfloat16), {"token": tok, "parent": par, "n_nodes": nn})
+    assert out["accepted_len"].tolist() == [3, 0]
+    assert out["next_token"].tolist() == [11, 3]
+    assert out["path"][0].tolist()[:4] == [1, 3, 4, -1]
+
+
+# --------------------------------------------------------------------------
+# DSpark length selection and the packed verify of the selected windows
+# --------------------------------------------------------------------------
+
+def test_select_len_parity():
+    g = torch.Generator(device="cuda").manual_seed(8)
+    for B, K, cost in ((512, 8, 0.15), (3, 64, 0.01), (1000, 5, 0.5), (700, 0, 0.1)):
+        conf = torch.sort(torch.rand(B, K, 6, generator=g, device="cuda"), dim=-1).values[..., 4].contiguous() \
+            if K > 0 else torch.zeros(B, 0, device="cuda")
+        out = sd.select_len(conf, cost)
+        ref = oracle.select_len(conf.cpu().numpy(), B, K, cost)
+        np.testing.assert_array_equal(out["k"].cpu().numpy(), ref["k"])
+        np.testing.assert_array_equal(out["cu"].cpu().numpy(), ref["cu"])
+        np.testing.assert_allclose(out["adv"].cpu().numpy(), ref["adv"], rtol=1e-5)
+
+
+def test_config5_adaptive_full_sampled():
+    _say("config 5: select_len + packed chain B=512 K_max=8 V=128256 bf16 (sampled)")
+    case = wl.gen_config5(device="cuda")
+    sel = sd.select_len(case.conf, case.cost)
+    ref_sel = oracle.select_len(case.conf.cpu().numpy(), case.B, case.K_max, case.cost)
+    np.testing.assert_array_equal(sel["k"].cpu().numpy(), ref_sel["k"])
+    np.testing.assert_array_equal(sel["cu"].cpu().numpy(), ref_sel["cu"])
+    np.testing.assert_allclose(sel["adv"].cpu().numpy(), ref_sel["adv"], rtol=1e-5)
+    packed = case.packed(sel["k"])
+    # launch exactly as the benchmark does: device cu from select_len, no host read
+    out = sd.verify_chain(packed.target, packed.draft, packed.tokens, packed.uniforms, 1.0,
+                          cu=sel["cu"], B=case.B, K_max=case.K_max, want_probs=True,
+                          want_resid=True, validate=False)
+    seqs = sample_seqs(case.B, 48, seed=5)
+    info = compare_chain(out, oracle_chain(packed, seqs))
+    _say(f"  {info} E[k*]={ref_sel['k'].mean():.3f} mean A={out['accepted_len'].float().mean().item():.3f}")
+
+
+# --------------------------------------------------------------------------
+# distribution: chi-square on a large batch of tiny-vocabulary sequences
+# --------------------------------------------------------------------------
+
+def test_gpu_chi_square_tokens_follow_target():
+    from scipy import stats
+    P = np.array([[.05, .15, .5, .3, 0, 0], [.6, .1, .1, .1, .05, .05], [0, 0, 0, .5, .5, 0],
+                  [.3, .3, .1, .1, .1, .1]])
+    Q = np.array([[1 / 6] * 6, [.5, .5, 0, 0, 0, 0], [0, 0, .2, .2, .3, .3]])
+    K, V, n = 3, 6, 1 << 18
+    with np.errstate(divide="ignore"):
+        lp = torch.tensor(np.log(P), dtype=torch.float32, device="cuda")
+        lq = torch.tensor(np.log(Q), dtype=torch.float32, device="cuda")
+    g = torch.Generator(device="cuda").manual_seed(99)
+    tgt = lp.repeat(n, 1).contiguous()
+    dft = lq.repeat(n, 1).contiguous()
+    y = torch.stack([torch.multinomial(torch.tensor(Q[i], device="cuda", dtype=torch.float32), n,
+                                       replacement=True, generator=g) for i in range(K)], 1)
+    tok = y.to(torch.int32).reshape(-1).contiguous()
+    uni = wl.grid_uniforms((n * (K + 1),), g, "cuda")
+    out = sd.verify_chain(tgt, dft, tok, uni, 1.0, K_max=K, B=n)
+    A = out["accepted_len"].cpu().numpy()
+    nx = out["next_token"].cpu().numpy()
+    yk = y.cpu().numpy()
+    for j in range(K + 1):
+        reach = A >= j
+        if reach.sum() < 5000:
+            continue
+        t = np.where(A[reach] > j, yk[reach][:, j] if j < K else -1, nx[reach])
+        obs = np.bincount(t, minlength=V)
+        z = P[j] == 0
+        assert obs[z].sum() == 0
+        pv = stats.chisquare(obs[~z], P[j][~z] * reach.sum()).pvalue
+        _say(f"  position {j}: n={reach.sum()} p-value {pv:.3g}")
+        assert pv >= 1e-3
