@@ -1,0 +1,356 @@
+#!/usr/bin/env python3
+"""Benchmark of the verify hot path on one MI355X.
+
+Default workload (the one the headline metric is quoted on, V = 128256 bf16):
+DSpark-style adaptive chain verification. One step is the whole path over one
+batch: sd_select_len on the per-position confidences (B = 512, K_max = 8,
+cost 0.15 per position), then a packed stochastic sd_verify_chain (T = 1) over
+the selected windows only, with the packed offsets read by the kernels from
+device memory (no host round trip). Inputs are seeded synthetic arrays already
+resident in HBM when timing starts.
+
+Printed: one JSON line with the throughput in verified draft positions per
+second, the roofline of the dominant kernel (the streaming pass over the logit
+rows, timed with HIP events on its own stream) and the CPU oracle timed on a
+bounded sample of the same workload.
+
+Other workloads (--workload greedy|topk|tree|chain1) measure the other kernels
+for the design notes; their inputs are rotated across copies so that the
+working set exceeds the 256 MB last-level cache.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "verified draft positions/sec and achieved HBM GB/s (% of peak), V=128256 bf16"
+PEAK_HBM_GBPS = 8000.0
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.txt")
+
+
+def log(msg):
+    print(msg, file=sys.stderr, flush=True)
+
+
+def source_digest() -> str:
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "rejection_sampling_verify_softmax_amd", "csrc")
+    for name in sorted(os.listdir(csrc)):
+        with open(os.path.join(csrc, name), "rb") as f:
+            h.update(name.encode() + b"\0" + f.read())
+    return h.hexdigest()[:16]
+
+
+def load_traffic(kernel: str, workload: str):
+    """HBM bytes per launch measured by rocprofv3 counters (FETCH_SIZE and
+    WRITE_SIZE, scaled by a copy-kernel calibration), if recorded for the
+    current kernel sources; else None."""
+    if not os.path.exists(TRAFFIC_FILE):
+        return None
+    digest = source_digest()
+    for line in open(TRAFFIC_FILE):
+        line = line.strip()
+        if not line or line.startswith("#"):
+            continue
+        f = dict(kv.split("=", 1) for kv in line.split())
+        if f.get("kernel") == kernel and f.get("workload") == workload and f.get("sources") == digest:
+            return float(f["bytes_per_launch"])
+    return None
+
+
+# --------------------------------------------------------------------------
+# workloads: each returns (step_fn, meta) where step_fn(i, timer_events) runs
+# one step on the current stream.
+# --------------------------------------------------------------------------
+
+def setup_adaptive(torch, sd, wl):
+    case = wl.gen_config5(device="cuda")
+    sel = sd.select_len(case.conf, case.cost)
+    torch.cuda.synchronize()
+    packed = case.packed(sel["k"])
+    B, K, V = case.B, case.K_max, case.V
+    positions = int(sel["cu"][-1].item())
+    R_d, R_t = positions, positions + B
+    out = {k: v for k, v in sd.verify_chain(packed.target, packed.draft, packed.tokens,
+                                            packed.uniforms, 1.0, cu=sel["cu"], B=B, K_max=K,
+                                            validate=True).items()}
+    ws = torch.empty(sd.workspace_bytes(sd.OP_CHAIN, B, K, V), dtype=torch.uint8, device="cuda")
+    sel_out = {"k": sel["k"], "adv": sel["adv"], "cu": sel["cu"]}
+    logit_bytes = (R_t + R_d) * V * 2
+    stats_bytes = logit_bytes + R_d * 4                       # rows once + draft tokens
+    step_bytes = (logit_bytes + R_d * 4 + R_t * 4              # rows, tokens, uniforms
+                  + B * K * 4 + B * (4 + 4 + 4) + (B + 1) * 4  # conf in; k, adv, cu out
+                  + B * 12)                                    # A, next, status out
+
+    def step(ev=None):
+        s = sd.select_len(case.conf, case.cost, out=sel_out)
+        if ev is not None:
+            sd.time_next_stream_pass(*ev)
+        sd.verify_chain(packed.target, packed.draft, packed.tokens, packed.uniforms, 1.0,
+                        cu=s["cu"], B=B, K_max=K, workspace=ws, out=out, validate=False)
+
+    meta = {
+        "workload": (f"DSpark-adaptive chain verify: select_len (Beta(5,2) confidences, cost 0.15) "
+                     f"+ packed stochastic verify over the selected windows, B={B}, K_max={K}, "
+                     f"V={V}, bf16 logits, T=1.0"),
+        "global_batch": B, "K_max": K, "V": V, "logits": "bf16", "temperature": 1.0,
+        "positions_per_step": positions, "target_rows": R_t, "draft_rows": R_d,
+        "kernel": "k_chain_stats", "kernel_bytes": stats_bytes, "step_bytes": step_bytes,
+        "mean_k": positions / B,
+    }
+    cpu = {"case": case, "packed": packed, "k": sel["k"].cpu().numpy(), "cu": sel["cu"].cpu().numpy()}
+    return step, meta, cpu
+
+
+def setup_greedy(torch, sd, wl):
+    case = wl.gen_config2(device="cuda")
+    B, K, V = case.B, case.K_max, case.V
+    copies = [case.target] + [case.target.clone() for _ in range(7)]    # 8 x 66 MB > LLC
+    ws = torch.empty(sd.workspace_bytes(sd.OP_GREEDY, B, K, V), dtype=torch.uint8, device="cuda")
+    st = {"i": 0}
+
+    def step(ev=None):
+        if ev is not None:
+            sd.time_next_stream_pass(*ev)
+        t = copies[st["i"] % len(copies)]
+        st["i"] += 1
+        sd.verify_greedy(t, case.tokens, B=B, K_max=K, workspace=ws)
+
+    rows = B * (K + 1)
+    meta = {"workload": f"greedy chain verify B={B} K={K} V={V} bf16 (8 rotated input copies)",
+            "global_batch": B, "K_max": K, "V": V, "positions_per_step": B * K,
+            "kernel": "k_argmax", "kernel_bytes": rows * V * 2, "step_bytes": rows * V * 2 + B * K * 4}
+    return step, meta, None
+
+
+def setup_topk(torch, sd, wl):
+    case = wl.gen_config3(device="cuda")
+    B, K, V = case.B, case.K_max, case.V
+    ws = torch.empty(sd.workspace_bytes(sd.OP_CHAIN, B, K, V, case.top_k), dtype=torch.uint8, device="cuda")
+
+    def step(ev=None):
+        if ev is not None:
+            sd.time_next_stream_pass(*ev)
+        sd.verify_chain(case.target, case.draft, case.tokens, case.uniforms, case.temperature,
+                        top_k=case.top_k, B=B, K_max=K, workspace=ws, validate=False)
+
+    rows = B * (K + 1) + B * K
+    meta = {"workload": f"top-k chain verify B={B} K={K} V={V} bf16 T=0.7 top-k 50",
+            "global_batch": B, "K_max": K, "V": V, "positions_per_step": B * K,
+            "kernel": "k_topk_rows", "kernel_bytes": rows * V * 2,
+            "step_bytes": rows * V * 2 + B * K * 4 + B * (K + 1) * 4}
+    return step, meta, None
+
+
+def setup_tree(torch, sd, wl):
+    case = wl.gen_config4(device="cuda")
+    B, K, V, N = case.B, case.K, case.V, case.N
+    tree = sd.build_tree(case.marginals, N)
+    target = case.target_for_depths(tree["depth"], tree["n_nodes"])
+    margs = [case.marginals] + [case.marginals.clone() for _ in range(2)]
+    targets = [target] + [target.clone() for _ in range(2)]
+    st = {"i": 0}
+    ws_b = torch.empty(sd.workspace_bytes(sd.OP_BUILD_TREE, B, K, V, 0, N), dtype=torch.uint8, device="cuda")
+    ws_v = torch.empty(sd.workspace_bytes(sd.OP_VERIFY_TREE, B, 0, V, 0, N), dtype=torch.uint8, device="cuda")
+
+    def step(ev=None):
+        i = st["i"] % 3
+        st["i"] += 1
+        if ev is not None:
+            sd.time_next_stream_pass(*ev)
+        t = sd.build_tree(margs[i], N, workspace=ws_b)
+        sd.verify_tree(targets[i], tree, workspace=ws_v)
+
+    meta = {"workload": f"DDTree build (B={B}, K={K}, V={V} fp32 marginals, N={N}) + walk over bf16 target rows",
+            "global_batch": B, "K_max": K, "V": V, "positions_per_step": B * (N - 1),
+            "kernel": "k_topk_rows(f32 marginals)", "kernel_bytes": B * K * V * 4,
+            "step_bytes": B * K * V * 4 + B * N * V * 2}
+    return step, meta, None
+
+
+def setup_chain1(torch, sd, wl):
+    case = wl.gen_config1(device="cuda")
+    ws = torch.empty(sd.workspace_bytes(sd.OP_CHAIN, 1, 4, 1000), dtype=torch.uint8, device="cuda")
+
+    def step(ev=None):
+        if ev is not None:
+            sd.time_next_stream_pass(*ev)
+        sd.verify_chain(case.target, case.draft, case.tokens, case.uniforms, 1.0, B=1, K_max=4,
+                        workspace=ws, validate=False)
+
+    meta = {"workload": "chain verify B=1 K=4 V=1000 fp32 (latency-bound)", "global_batch": 1,
+            "K_max": 4, "V": 1000, "positions_per_step": 4, "kernel": "k_chain_stats",
+            "kernel_bytes": 9 * 1000 * 4 + 16, "step_bytes": 9 * 1000 * 4 + 16 + 20}
+    return step, meta, None
+
+
+WORKLOADS = {"adaptive": setup_adaptive, "greedy": setup_greedy, "topk": setup_topk,
+             "tree": setup_tree, "chain1": setup_chain1}
+
+
+def run_cpu_baseline(cpu, target_seconds: float):
+    import numpy as np
+    import torch
+
+    import oracle
+    from rejection_sampling_verify_softmax_amd import workloads as wl
+
+    case, packed = cpu["case"], cpu["packed"]
+    threads = int(os.environ.get("OMP_NUM_THREADS", "0")) or oracle.default_threads()
+    threads = min(threads, oracle.default_threads())
+    conf = case.conf.cpu().numpy()
+    t0 = time.perf_counter()
+    sel = oracle.select_len(conf, case.B, case.K_max, case.cost)
+    t_sel = time.perf_counter() - t0
+    cu = sel["cu"].astype(np.int64)
+    B, V = case.B, case.V
+    group = 16
+    done_pos, done_seq, spent = 0, 0, t_sel
+    b = 0
+    while spent < target_seconds and done_seq < 4 * B:
+        seqs = [(b + i) % B for i in range(group)]
+        b = (b + group) % B
+        t_rows = np.concatenate([np.arange(cu[s] + s, cu[s + 1] + s + 1) for s in seqs])
+        d_rows = np.concatenate([np.arange(cu[s], cu[s + 1]) for s in seqs])
+        ti = torch.as_tensor(t_rows, device="cuda")
+        di = torch.as_tensor(d_rows, device="cuda")
+        tgt = wl.to_host_f32(packed.target.index_select(0, ti))
+        dft = wl.to_host_f32(packed.draft.index_select(0, di))
+        tok = packed.tokens.index_select(0, di).cpu().numpy()
+        uni = packed.uniforms.index_select(0, ti).cpu().numpy()
+        lens = [int(cu[s + 1] - cu[s]) for s in seqs]
+        scu = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
+        t0 = time.perf_counter()
+        oracle.verify_chain(tgt, dft, tok, uni, scu, len(seqs), max(lens), V, 1.0, threads=threads,
+                            want_probs=False)
+        spent += time.perf_counter() - t0
+        done_pos += int(sum(lens))
+        done_seq += len(seqs)
+    return {"value": done_pos / spent, "unit": "positions/s", "cores": threads, "kind": "oracle",
+            "sample": (f"CPU oracle (fp64 C, OpenMP over sequences): length selection for all {B} "
+                       f"sequences plus packed chain verification of {done_seq} sequences "
+                       f"({done_pos} draft positions, groups of {group}, cycling through the batch), "
+                       f"{spent:.1f} s of oracle time; transfer and conversion not timed")}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="adaptive", choices=sorted(WORKLOADS))
+    ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="also run a plain 1 GiB device copy (for scaling HBM byte counters)")
+    args = ap.parse_args()
+
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}, WORLD_SIZE={world}); "
+              "sequences are independent and the batch shards with no communication, so the "
+              "single-GPU figure is the per-GPU throughput.", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import rejection_sampling_verify_softmax_amd as sd
+    from rejection_sampling_verify_softmax_amd import workloads as wl
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    sd.lib()
+    log(f"setting up workload {args.workload}")
+    step, meta, cpu = WORKLOADS[args.workload](torch, sd, wl)
+    torch.cuda.synchronize()
+
+    if args.copy_calibration:
+        n = 1 << 30
+        a = torch.empty(n, dtype=torch.uint8, device="cuda")
+        b = torch.empty(n, dtype=torch.uint8, device="cuda")
+        for _ in range(3):
+            b.copy_(a)
+        torch.cuda.synchronize()
+        log("copy calibration: 3 x 1 GiB device-to-device copies")
+        del a, b
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    log(f"warmup {args.warmup} done; timing {args.steps} steps")
+
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(args.steps)]
+    for s_ev, e_ev in evs:          # torch creates the HIP event on its first record
+        s_ev.record()
+        e_ev.record()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(evs[i])
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    kernel_ms = [s.elapsed_time(e) for s, e in evs]
+    kernel_ms_avg = sum(kernel_ms) / len(kernel_ms)
+    ms_per_step = elapsed * 1e3 / args.steps
+    positions = meta["positions_per_step"]
+    value = positions * args.steps / elapsed
+    achieved = meta["kernel_bytes"] / (kernel_ms_avg * 1e-3) / 1e9
+    traffic = load_traffic(meta["kernel"], args.workload)
+    log(f"{ms_per_step:.4f} ms/step, {meta['kernel']} {kernel_ms_avg * 1e3:.1f} us avg -> "
+        f"{achieved:.0f} GB/s ({achieved / PEAK_HBM_GBPS:.1%} of 8 TB/s)")
+
+    result = {
+        "metric": METRIC,
+        "value": value,
+        "unit": "positions/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {k: meta[k] for k in ("workload", "global_batch", "K_max", "V") if k in meta},
+        "roofline": {
+            "bound": "hbm",
+            "achieved": achieved,
+            "peak": PEAK_HBM_GBPS,
+            "unit": "GB/s",
+            "frac": achieved / PEAK_HBM_GBPS,
+            "traffic": traffic,
+            "kernel": meta["kernel"],
+            "kernel_us": kernel_ms_avg * 1e3,
+            "algorithmic_bytes_per_launch": meta["kernel_bytes"],
+        },
+        "step": {
+            "positions_per_step": positions,
+            "algorithmic_bytes": meta["step_bytes"],
+            "effective_GBps": meta["step_bytes"] / (ms_per_step * 1e-3) / 1e9,
+        },
+    }
+    result["config"]["parallelism"] = "none (one GPU)"
+    for k in ("logits", "temperature", "mean_k"):
+        if k in meta:
+            result["config"][k] = meta[k]
+    if cpu is not None and not args.no_cpu_baseline:
+        log("timing the CPU oracle on a bounded sample")
+        result["cpu_baseline"] = run_cpu_baseline(cpu, args.cpu_seconds)
+    else:
+        result["cpu_baseline"] = None
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -210,6 +210,17 @@ sd_status_t sd_select_len(const float* conf, int32_t B, int32_t K_max, float cos
                           int32_t* k_sel, float* expected_advance, int32_t* cu_sel,
                           void* hip_stream);
 
+/*
+ * Measurement support. The next sd_verify_chain, sd_verify_greedy,
+ * sd_build_tree or sd_verify_tree call made by the calling host thread records
+ * `start_event` on its stream immediately before its streaming kernel (the one
+ * pass over the logit / marginal rows, which dominates its time) and
+ * `stop_event` immediately after it; the hook then clears itself. Both are
+ * hipEvent_t handles created by the caller; hipEventElapsedTime of the pair is
+ * that kernel's duration. Passing NULL, NULL clears a pending hook. Returns SD_OK.
+ */
+sd_status_t sd_time_next_stream_pass(void* start_event, void* stop_event);
+
 #ifdef __cplusplus
 }
 #endif

@@ -65,6 +65,8 @@ def _load():
     lib.sd_verify_tree.restype = ctypes.c_int
     lib.sd_select_len.argtypes = [P, I, I, F, P, P, P, P]
     lib.sd_select_len.restype = ctypes.c_int
+    lib.sd_time_next_stream_pass.argtypes = [P, P]
+    lib.sd_time_next_stream_pass.restype = ctypes.c_int
     _lib = lib
     return lib
 
@@ -111,6 +113,17 @@ def _get(d: dict, key: str, make):
 def _raise(status: int, where: str):
     if status != SD_OK:
         raise SDError(status, where)
+
+
+def time_next_stream_pass(start: Optional["torch.cuda.Event"], stop: Optional["torch.cuda.Event"]):
+    """sd_time_next_stream_pass: the next call's streaming kernel is bracketed by
+    these events on its stream. torch creates an event's HIP handle on its first
+    record(), so both must have been recorded once before."""
+    s = None if start is None else ctypes.c_void_p(start.cuda_event)
+    e = None if stop is None else ctypes.c_void_p(stop.cuda_event)
+    if (start is not None and not s.value) or (stop is not None and not e.value):
+        raise ValueError("record() each event once before passing it (its HIP event is created lazily)")
+    _raise(_load().sd_time_next_stream_pass(s, e), "sd_time_next_stream_pass")
 
 
 def workspace_bytes(op: int, B: int, K_max: int = 0, V: int = 1, top_k: int = 0, N: int = 2) -> int:

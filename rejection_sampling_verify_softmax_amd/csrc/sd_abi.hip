@@ -29,9 +29,20 @@ size_t chain_ws(int B, int K_max, int V, int dtype, float T, int top_k) {
 
 }  // namespace
 
+namespace sd {
+thread_local hipEvent_t PassTimer::start = nullptr;
+thread_local hipEvent_t PassTimer::stop = nullptr;
+}  // namespace sd
+
 extern "C" {
 
 int sd_abi_version(void) { return SD_ABI_VERSION; }
+
+sd_status_t sd_time_next_stream_pass(void* start_event, void* stop_event) {
+    sd::PassTimer::start = static_cast<hipEvent_t>(start_event);
+    sd::PassTimer::stop = static_cast<hipEvent_t>(stop_event);
+    return SD_OK;
+}
 
 const char* sd_status_str(int status) {
     switch (status) {

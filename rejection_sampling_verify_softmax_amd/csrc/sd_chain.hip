@@ -8,22 +8,30 @@
 // p; temperature is folded into both p and q.
 //
 // Four launches on the caller's stream:
-//   1. k_chain_stats  grid (sequence, slot, chunk): one pass over every row.
+//   1. k_chain_stats  grid (sequence, slot, chunk): the one pass over every row.
 //      Slot i < k_b streams target row i and draft row i together; slot k_b
 //      streams the extra-token row. Each workgroup writes the softmax partial
 //      (o, S) of its chunk of each row and, for chunk 0, the two logits at y_i.
-//   2. k_chain_decide grid B, one wave: combines the partials of each row in
-//      fp64, evaluates p_i(y_i) and q_i(y_i) in fp64, the accept bits, a
-//      wave ballot for A, and the decision descriptor.
-//   3. k_chain_mass   grid (sequence, chunk): for sequences that stopped on a
-//      rejection only, the residual mass of each chunk of the decision row pair.
-//   4. k_chain_sample grid B: finds the chunk that holds the inverse-CDF point
-//      (chunk masses of the residual, or of p from the step-1 partials for an
-//      extra token) and scans inside that one chunk.
+//   2. k_chain_decide one wave per sequence: combines the partials of each row
+//      exactly (integer references: a power-of-two rescale), evaluates
+//      p_i(y_i), q_i(y_i) in fp64, the accept bits and A (wave ballot), and the
+//      descriptor of the decision row(s).
+//   3. k_chain_mass   grid (sequence, 32K-token chunk): re-reads only the
+//      decision row(s) for the weight mass of the residual (or of p for the
+//      extra token) per 512-token piece.
+//   4. k_chain_sample one wave per sequence: prefix over the piece masses, then
+//      one piece scan for the final token.
 #include "sd_device.hpp"
 #include "sd_internal.hpp"
 
 #include <math.h>
+
+#ifndef SD_STATS_UNROLL
+#define SD_STATS_UNROLL 4
+#endif
+#ifndef SD_STATS_PIPE
+#define SD_STATS_PIPE 1
+#endif
 
 namespace sd {
 
@@ -32,16 +40,19 @@ namespace {
 constexpr int kModeResidual = 0;
 constexpr int kModeExtra = 1;
 constexpr int kModeNone = 2;
-constexpr int kStatsUnroll = 4;
+constexpr int kU = SD_STATS_UNROLL;
+// A one-pass chunk sum is kept only below 2^64 (its reference was then close
+// enough to the chunk's maximum); otherwise the exact two-pass path runs.
+constexpr double kFastSumLimit = 18446744073709551616.0;
 
 struct ChainDesc {
     int32_t mode;
     int32_t A;
     int32_t t_row;      // target row the final token is drawn from
     int32_t d_row;      // draft row of the residual; -1 when q counts as 0
-    int32_t slot;       // slot of the decision row (partials lookup)
     float u;            // the final uniform
-    float O_p, O_q;     // row references
+    float O_p, O_q;     // row references (integers)
+    float pad;
     double S_p, S_q;    // row sums relative to the references
 };
 
@@ -66,9 +77,8 @@ __device__ __forceinline__ void load_vec(const typename E::raw* row, int beg, in
     }
 }
 
-// Exact two-pass partial of row[beg, end): max first (NaN ignored, NaN presence
-// recorded), then the sum relative to fl32(max * c). Used when the one-pass
-// estimate is not finite.
+// Exact two-pass partial of row[beg, end): maximum first (NaN ignored, NaN
+// presence recorded), then the sum relative to floor(max * c).
 template <class E, bool VEC>
 __device__ Partial chunk_stats_exact(const typename E::raw* row, int beg, int end, float c,
                                      double* redd, float* redf, int* redi) {
@@ -78,15 +88,7 @@ __device__ Partial chunk_stats_exact(const typename E::raw* row, int beg, int en
     int nan_seen = 0;
     for (int vi = threadIdx.x; vi < nvec; vi += kBlock) {
         float f[EV];
-        if (VEC) {
-            E::unpack(load16(row + beg, vi), f);
-        } else {
-#pragma unroll
-            for (int e = 0; e < EV; ++e) {
-                const int j = beg + vi * EV + e;
-                f[e] = (j < end) ? E::at(row, j) : -INFINITY;
-            }
-        }
+        load_vec<E, VEC>(row, beg, end, vi, f);
 #pragma unroll
         for (int e = 0; e < EV; ++e) {
             nan_seen |= (f[e] != f[e]);
@@ -107,7 +109,7 @@ __device__ Partial chunk_stats_exact(const typename E::raw* row, int beg, int en
         p.S = 0.0;
         return p;
     }
-    const float o = m * c;
+    const float o = floorf(m * c);
     double s = 0.0;
     for (int vi = threadIdx.x; vi < nvec; vi += kBlock) {
         float f[EV];
@@ -122,15 +124,28 @@ __device__ Partial chunk_stats_exact(const typename E::raw* row, int beg, int en
     return p;
 }
 
-// One-pass partials of NR rows over [beg, end). The reference of each row is
-// fl32(m0 * c) with m0 the largest of the chunk's first 16-byte vector (read by
-// every lane from one cache line); any overflow, -inf or NaN reference makes the
-// sum non-finite and sends that row to the exact two-pass path.
+template <class E, int NR>
+__device__ __forceinline__ void accumulate(const uint4 (&v)[NR][kU], const float (&o)[NR], float c,
+                                           float (&acc)[NR][E::kVec]) {
+#pragma unroll
+    for (int u = 0; u < kU; ++u)
+#pragma unroll
+        for (int r = 0; r < NR; ++r) {
+            float f[E::kVec];
+            E::unpack(v[r][u], f);
+#pragma unroll
+            for (int e = 0; e < E::kVec; ++e) acc[r][e] += fast_exp2(__builtin_fmaf(f[e], c, -o[r]));
+        }
+}
+
+// One-pass partials of NR rows over [beg, end). The reference of a row is the
+// integer floor(m0 * c), m0 the largest logit of the chunk's first 16-byte
+// vector (every lane reads that one cache line). A non-finite sum, a non-finite
+// reference or a sum beyond 2^64 sends that row to the exact two-pass path.
 template <class E, bool VEC, int NR>
 __device__ void chunk_stats(const typename E::raw* const (&rows)[NR], int beg, int end, float c,
                             Partial (&out)[NR], double* redd, float* redf, int* redi) {
     constexpr int EV = E::kVec;
-    constexpr int U = kStatsUnroll;
     const int nvec = (end - beg + EV - 1) / EV;
     float o[NR];
 #pragma unroll
@@ -140,7 +155,7 @@ __device__ void chunk_stats(const typename E::raw* const (&rows)[NR], int beg, i
         float m = f[0];
 #pragma unroll
         for (int e = 1; e < EV; ++e) m = fmaxf(m, f[e]);
-        o[r] = m * c;
+        o[r] = floorf(m * c);
     }
     float acc[NR][EV];
 #pragma unroll
@@ -148,33 +163,60 @@ __device__ void chunk_stats(const typename E::raw* const (&rows)[NR], int beg, i
 #pragma unroll
         for (int e = 0; e < EV; ++e) acc[r][e] = 0.f;
 
-    for (int v0 = threadIdx.x; v0 < nvec; v0 += kBlock * U) {
-        float f[NR][U][EV];
+    int vdone = 0;
+    if (VEC) {
+        constexpr int step = kBlock * kU;
+        const int full = nvec / step;
+        const typename E::raw* base[NR];
 #pragma unroll
-        for (int u = 0; u < U; ++u) {
-            const int vi = v0 + u * kBlock;
+        for (int r = 0; r < NR; ++r) base[r] = rows[r] + beg;
+        if (full > 0) {
+            uint4 cur[NR][kU];
 #pragma unroll
-            for (int r = 0; r < NR; ++r) {
-                if (VEC) {
-                    uint4 w = (vi < nvec) ? load16(rows[r] + beg, vi) : E::neg_inf();
-                    E::unpack(w, f[r][u]);
-                } else {
-                    if (vi < nvec) {
-                        load_vec<E, VEC>(rows[r], beg, end, vi, f[r][u]);
-                    } else {
+            for (int u = 0; u < kU; ++u)
 #pragma unroll
-                        for (int e = 0; e < EV; ++e) f[r][u][e] = -INFINITY;
-                    }
+                for (int r = 0; r < NR; ++r) cur[r][u] = load16(base[r], u * kBlock + threadIdx.x);
+            for (int rd = 0; rd < full; ++rd) {
+#if SD_STATS_PIPE
+                uint4 nxt[NR][kU];
+                const bool more = rd + 1 < full;
+                if (more) {
+#pragma unroll
+                    for (int u = 0; u < kU; ++u)
+#pragma unroll
+                        for (int r = 0; r < NR; ++r)
+                            nxt[r][u] = load16(base[r], (rd + 1) * step + u * kBlock + threadIdx.x);
                 }
+                accumulate<E, NR>(cur, o, c, acc);
+                if (more) {
+#pragma unroll
+                    for (int u = 0; u < kU; ++u)
+#pragma unroll
+                        for (int r = 0; r < NR; ++r) cur[r][u] = nxt[r][u];
+                }
+#else
+                accumulate<E, NR>(cur, o, c, acc);
+                if (rd + 1 < full) {
+#pragma unroll
+                    for (int u = 0; u < kU; ++u)
+#pragma unroll
+                        for (int r = 0; r < NR; ++r)
+                            cur[r][u] = load16(base[r], (rd + 1) * step + u * kBlock + threadIdx.x);
+                }
+#endif
             }
         }
+        vdone = full * step;
+    }
+    // ragged tail (the whole range in the element-wise path)
+    for (int vi = vdone + threadIdx.x; vi < nvec; vi += kBlock) {
 #pragma unroll
-        for (int u = 0; u < U; ++u)
+        for (int r = 0; r < NR; ++r) {
+            float f[EV];
+            load_vec<E, VEC>(rows[r], beg, end, vi, f);
 #pragma unroll
-            for (int r = 0; r < NR; ++r)
-#pragma unroll
-                for (int e = 0; e < EV; ++e)
-                    acc[r][e] += fast_exp2(__builtin_fmaf(f[r][u][e], c, -o[r]));
+            for (int e = 0; e < EV; ++e) acc[r][e] += fast_exp2(__builtin_fmaf(f[e], c, -o[r]));
+        }
     }
 #pragma unroll
     for (int r = 0; r < NR; ++r) {
@@ -182,7 +224,7 @@ __device__ void chunk_stats(const typename E::raw* const (&rows)[NR], int beg, i
 #pragma unroll
         for (int e = 0; e < EV; ++e) s += (double)acc[r][e];
         const double S = block_sum(s, redd);
-        if (isfinite(S) && isfinite(o[r])) {
+        if (isfinite(o[r]) && isfinite(S) && S < kFastSumLimit) {
             out[r].o = o[r];
             out[r].pad = 0.f;
             out[r].S = S;
@@ -242,7 +284,8 @@ __global__ __launch_bounds__(kBlock) void k_chain_stats(
     }
 }
 
-// Row statistics from its chunk partials (fixed chunk order, fp64).
+// Row statistics from its chunk partials. References are integers, so each
+// partial is rescaled exactly by a power of two (fixed chunk order, fp64).
 __device__ RowStat combine_row(const Partial* p, int n_chunks) {
     RowStat r;
     r.O = -INFINITY;
@@ -260,21 +303,275 @@ __device__ RowStat combine_row(const Partial* p, int n_chunks) {
     double S = 0.0;
     for (int i = 0; i < n_chunks; ++i) {
         const Partial q = p[i];
-        if (q.S > 0.0) S += q.S * exp2((double)q.o - (double)r.O);
+        if (q.S > 0.0) S += ldexp(q.S, (int)fmaxf(q.o - r.O, -4096.f));
     }
     r.S = S;
     r.valid = isfinite(S) && S > 0.0;
     return r;
 }
 
-__global__ __launch_bounds__(kWave) void k_chain_decide(
+// Sampling weight of one token in fp32: the normalised residual max(p - q, 0),
+// or p itself. The mass pass and the final scan use this one definition, so
+// both see bit-identical values.
+struct WeightFn {
+    float c, Op, ip, Oq, iq;
+    bool has_q, residual;
+    __device__ __forceinline__ float operator()(float xp, float xq) const {
+        const float ep = fast_exp2(__builtin_fmaf(xp, c, -Op));
+        if (!residual) return ep * ip;
+        const float q = has_q ? fast_exp2(__builtin_fmaf(xq, c, -Oq)) * iq : 0.f;
+        return fmaxf(__builtin_fmaf(ep, ip, -q), 0.f);          // max(p - q, 0)
+    }
+};
+
+__device__ __forceinline__ WeightFn weight_fn(const ChainDesc& d, float c, bool use_p) {
+    WeightFn w;
+    w.c = c;
+    w.Op = d.O_p;
+    w.ip = (float)(1.0 / d.S_p);
+    w.residual = !use_p && d.mode == kModeResidual;
+    w.has_q = w.residual && d.d_row >= 0;
+    w.Oq = d.O_q;
+    w.iq = w.has_q ? (float)(1.0 / d.S_q) : 0.f;
+    return w;
+}
+
+// Sum of the weights of one lane's 16-byte vector, in element order.
+template <class E>
+__device__ __forceinline__ float lane_weight_sum(const float (&fp)[E::kVec], const float (&fq)[E::kVec],
+                                                 const WeightFn& wf) {
+    float s = 0.f;
+#pragma unroll
+    for (int e = 0; e < E::kVec; ++e) s += wf(fp[e], fq[e]);
+    return s;
+}
+
+__device__ __forceinline__ double wave_excl_scan(double v) {
+    const int lane = threadIdx.x & (kWave - 1);
+    double incl = v;
+#pragma unroll
+    for (int o = 1; o < kWave; o <<= 1) {
+        const double t = __shfl_up(incl, o, kWave);
+        if (lane >= o) incl += t;
+    }
+    return incl - v;
+}
+
+constexpr int kResolveThreads = kBlock;
+constexpr int kMassChunkVecs = 4096;      // 16-byte vectors per mass workgroup
+constexpr int kResolveWaves = kResolveThreads / kWave;
+
+// Weight mass of every piece (64 consecutive 16-byte vectors: 512 bf16 or 256
+// fp32 tokens) of tokens [beg, end) of the decision row(s), written to
+// pieces[beg / piece_tokens ..]. Coalesced 16-byte loads, the next round in
+// flight while the current one is weighed; wave w of round rd, unroll u
+// covers piece (rd * U + u) * waves + w of the range. `beg` is a multiple of
+// the piece size.
+template <class E, bool VEC>
+__device__ void mass_pass(const typename E::raw* tp, const typename E::raw* dp, int beg, int end,
+                          const WeightFn& wf, double* pieces, int npieces) {
+    constexpr int EV = E::kVec;
+    constexpr int T = kResolveThreads;
+    constexpr int step = T * kU;
+    const int nvec = (end - beg + EV - 1) / EV;
+    const int w = threadIdx.x / kWave;
+    const int lane = threadIdx.x & (kWave - 1);
+    const int p0 = beg / (kWave * EV);
+    const int rounds = (nvec + step - 1) / step;
+    const typename E::raw* tb = tp + beg;
+    const typename E::raw* db = dp + beg;
+    auto fetch = [&](int rd, uint4 (&vt)[kU], uint4 (&vd)[kU]) {
+#pragma unroll
+        for (int u = 0; u < kU; ++u) {
+            const int vi = rd * step + u * T + threadIdx.x;
+            if (VEC) {
+                const bool in = vi < nvec;
+                vt[u] = in ? load16(tb, vi) : E::neg_inf();
+                vd[u] = (in && wf.has_q) ? load16(db, vi) : E::neg_inf();
+            }
+        }
+    };
+    auto weigh = [&](int rd, const uint4 (&vt)[kU], const uint4 (&vd)[kU]) {
+#pragma unroll
+        for (int u = 0; u < kU; ++u) {
+            float fp[EV], fq[EV];
+            if (VEC) {
+                E::unpack(vt[u], fp);
+                E::unpack(vd[u], fq);
+            } else {
+                const int vi = rd * step + u * T + threadIdx.x;
+#pragma unroll
+                for (int e = 0; e < EV; ++e) {
+                    const int j = beg + vi * EV + e;
+                    fp[e] = (vi < nvec && j < end) ? E::at(tp, j) : -INFINITY;
+                    fq[e] = (vi < nvec && j < end && wf.has_q) ? E::at(dp, j) : -INFINITY;
+                }
+            }
+            const double sb = wave_sum((double)lane_weight_sum<E>(fp, fq, wf));
+            const int piece = p0 + (rd * kU + u) * kResolveWaves + w;
+            if (lane == 0 && piece < npieces) pieces[piece] = sb;
+        }
+    };
+    uint4 cur_t[kU], cur_d[kU];
+    fetch(0, cur_t, cur_d);
+    for (int rd = 0; rd < rounds; ++rd) {
+        uint4 nxt_t[kU], nxt_d[kU];
+        const bool more = rd + 1 < rounds;
+        if (more) fetch(rd + 1, nxt_t, nxt_d);
+        weigh(rd, cur_t, cur_d);
+        if (more) {
+#pragma unroll
+            for (int u = 0; u < kU; ++u) {
+                cur_t[u] = nxt_t[u];
+                cur_d[u] = nxt_d[u];
+            }
+        }
+    }
+}
+
+// Scans one piece (64 lanes x one 16-byte vector, tokens e0 ..) from cumulative
+// mass `before`: the first token whose running mass exceeds `target`, or the
+// last token of the piece with positive weight. One wave.
+template <class E>
+__device__ int scan_piece(const typename E::raw* tp, const typename E::raw* dp, int e0, int V,
+                          const WeightFn& wf, double before, double target, bool take_last) {
+    constexpr int EV = E::kVec;
+    const int lane = threadIdx.x & (kWave - 1);
+    const int j0 = e0 + lane * EV;
+    float fp[EV], fq[EV];
+#pragma unroll
+    for (int e = 0; e < EV; ++e) {
+        const int j = j0 + e;
+        fp[e] = (j < V) ? E::at(tp, j) : -INFINITY;
+        fq[e] = (wf.has_q && j < V) ? E::at(dp, j) : -INFINITY;
+    }
+    float w[EV];
+    float ls = 0.f;
+    int lastpos = -1;
+#pragma unroll
+    for (int e = 0; e < EV; ++e) {
+        w[e] = wf(fp[e], fq[e]);
+        ls += w[e];
+        if (w[e] > 0.f) lastpos = j0 + e;
+    }
+    const int last_any = wave_max_int(lastpos);
+    if (take_last) return last_any;
+    const double start = before + wave_excl_scan((double)ls);
+    const unsigned long long m = __ballot(start + (double)ls > target);
+    if (!m) return last_any;
+    const int L = __ffsll(m) - 1;
+    int pick = -1;
+    if (lane == L) {
+        double run = start;
+        int lp = -1;
+#pragma unroll
+        for (int e = 0; e < EV; ++e) {
+            run += (double)w[e];
+            if (w[e] > 0.f) lp = j0 + e;
+            if (pick < 0 && run > target && w[e] > 0.f) pick = j0 + e;
+        }
+        if (pick < 0) pick = lp;
+    }
+    pick = __shfl(pick, L, kWave);
+    return pick >= 0 ? pick : last_any;
+}
+
+// Inverse CDF in token order from the piece masses: the first token whose
+// running mass exceeds u * total. One wave. Returns -1 when total is 0.
+template <class E>
+__device__ int sample_from_pieces(const double* S, int npieces, const typename E::raw* tp,
+                                  const typename E::raw* dp, int V, const WeightFn& wf, double u,
+                                  double* total_out) {
+    constexpr int EV = E::kVec;
+    const int lane = threadIdx.x & (kWave - 1);
+    const int per = (npieces + kWave - 1) / kWave;
+    const int s0 = min(npieces, lane * per), s1 = min(npieces, s0 + per);
+    double mine = 0.0;
+    int lastpos = -1;
+    for (int i = s0; i < s1; ++i) {
+        mine += S[i];
+        if (S[i] > 0.0) lastpos = i;
+    }
+    const double excl = wave_excl_scan(mine);
+    const double total = __shfl(excl + mine, kWave - 1, kWave);
+    *total_out = total;
+    if (!(total > 0.0)) return -1;
+    const double target = u * total;
+    int hit = -1;
+    double before = 0.0, run = excl;
+    for (int i = s0; i < s1; ++i) {
+        if (run + S[i] > target && S[i] > 0.0) {
+            hit = i;
+            before = run;
+            break;
+        }
+        run += S[i];
+    }
+    const unsigned long long m = __ballot(hit >= 0);
+    bool take_last = false;
+    int piece;
+    if (m) {
+        const int L = __ffsll(m) - 1;
+        piece = __shfl(hit, L, kWave);
+        before = __shfl(before, L, kWave);
+    } else {
+        piece = wave_max_int(lastpos);      // rounding left the point past the end
+        take_last = true;
+    }
+    return scan_piece<E>(tp, dp, piece * kWave * EV, V, wf, before, target, take_last);
+}
+
+// Inverse CDF over the whole decision row with the piece masses computed on
+// the fly by one wave (used only when the residual came out with no mass).
+template <class E>
+__device__ int sample_by_rescan(const typename E::raw* tp, int V, const WeightFn& wf, double u) {
+    constexpr int EV = E::kVec;
+    const int lane = threadIdx.x & (kWave - 1);
+    const int pe = kWave * EV;
+    const int np = (V + pe - 1) / pe;
+    auto piece_mass = [&](int i) -> double {
+        const int j0 = i * pe + lane * EV;
+        float fp[EV], fq[EV];
+#pragma unroll
+        for (int e = 0; e < EV; ++e) {
+            fp[e] = (j0 + e < V) ? E::at(tp, j0 + e) : -INFINITY;
+            fq[e] = -INFINITY;
+        }
+        return wave_sum((double)lane_weight_sum<E>(fp, fq, wf));
+    };
+    double total = 0.0;
+    int last = -1;
+    for (int i = 0; i < np; ++i) {
+        const double m = piece_mass(i);
+        total += m;
+        if (m > 0.0) last = i;
+    }
+    if (!(total > 0.0)) return -1;
+    const double target = u * total;
+    double run = 0.0;
+    for (int i = 0; i < np; ++i) {
+        const double m = piece_mass(i);
+        if (run + m > target && m > 0.0) return scan_piece<E>(tp, tp, i * pe, V, wf, run, target, false);
+        run += m;
+    }
+    return scan_piece<E>(tp, tp, last * pe, V, wf, 0.0, target, true);
+}
+
+constexpr int kSeqPerBlock = kBlock / kWave;    // decide / sample: one wave per sequence
+
+// The sequence's decision from the row partials (one wave per sequence):
+// combines the partials of each row, evaluates p_i(y_i) and q_i(y_i) in fp64, the
+// accept bits and A (wave ballot); stores A, the status bits, the probabilities
+// and the descriptor of the row(s) the final token is drawn from.
+__global__ __launch_bounds__(kBlock) void k_chain_decide(
     const Partial* __restrict__ part_t, const Partial* __restrict__ part_d,
     const float* __restrict__ xy, const int32_t* __restrict__ tok, const float* __restrict__ uni,
-    const int32_t* __restrict__ cu, int K_max, int V, int n_chunks, float c,
+    const int32_t* __restrict__ cu, int B, int K_max, int V, int n_chunks, float c,
     int32_t* __restrict__ A_out, float* __restrict__ probs_out, int32_t* __restrict__ status_out,
     ChainDesc* __restrict__ desc) {
-    const int b = blockIdx.x;
-    const int lane = threadIdx.x;
+    const int b = blockIdx.x * kSeqPerBlock + threadIdx.x / kWave;
+    if (b >= B) return;
+    const int lane = threadIdx.x & (kWave - 1);
     const int slots = K_max + 1;
     int d0, k;
     seq_range(cu, b, K_max, d0, k);
@@ -288,8 +585,11 @@ __global__ __launch_bounds__(kWave) void k_chain_decide(
         const int y = tok[d0 + lane];
         const bool yok = (y >= 0 && y < V);
         double py = 0.0, qy = 0.0;
-        if (yok && rp.valid) py = exp2((double)xy[(slot0 + lane) * 2] * (double)c - (double)rp.O) / rp.S;
-        if (yok && rq.valid) qy = exp2((double)xy[(slot0 + lane) * 2 + 1] * (double)c - (double)rq.O) / rq.S;
+        // the summed terms' fp32 reference, evaluated exactly in fp64
+        if (yok && rp.valid)
+            py = exp2((double)xy[(slot0 + lane) * 2] * (double)c - (double)rp.O) / rp.S;
+        if (yok && rq.valid)
+            qy = exp2((double)xy[(slot0 + lane) * 2 + 1] * (double)c - (double)rq.O) / rq.S;
         const double u = (double)uni[d0 + b + lane];
         acc = rp.valid && rq.valid && yok && py > 0.0 && u * qy <= py;
         st = (yok ? 0 : 1) | ((rp.valid && rq.valid) ? 0 : 2);
@@ -303,10 +603,10 @@ __global__ __launch_bounds__(kWave) void k_chain_decide(
     int mine = (lane < k && lane <= A) ? st : 0;
 #pragma unroll
     for (int o = kWave / 2; o > 0; o >>= 1) mine |= __shfl_xor(mine, o, kWave);
-    // decision row statistics
     ChainDesc d;
     d.A = A;
     d.u = uni[d0 + b + k];
+    d.pad = 0.f;
     if (A < k) {
         const float Op = __shfl(rp.O, A, kWave);
         const double Sp = __shfl(rp.S, A, kWave);
@@ -317,18 +617,16 @@ __global__ __launch_bounds__(kWave) void k_chain_decide(
         d.mode = vp ? kModeResidual : kModeNone;
         d.t_row = d0 + b + A;
         d.d_row = vq ? d0 + A : -1;
-        d.slot = A;
         d.O_p = Op;
         d.S_p = Sp;
         d.O_q = Oq;
         d.S_q = Sq;
     } else {
-        RowStat rb = combine_row(part_t + (slot0 + k) * n_chunks, n_chunks);
+        const RowStat rb = combine_row(part_t + (slot0 + k) * n_chunks, n_chunks);
         d.mode = rb.valid ? kModeExtra : kModeNone;
         if (!rb.valid) mine |= 2;
         d.t_row = d0 + b + k;
         d.d_row = -1;
-        d.slot = k;
         d.O_p = rb.O;
         d.S_p = rb.S;
         d.O_q = 0.f;
@@ -341,177 +639,56 @@ __global__ __launch_bounds__(kWave) void k_chain_decide(
     }
 }
 
-// Residual weight of one token: max(p - q, 0) in fp32 from the row statistics.
-// Shared by the mass and sample kernels so both see identical values.
-__device__ __forceinline__ float residual_w(float xp, float xq, float c, float Op, float ip,
-                                            float Oq, float iq, bool has_q) {
-    const float p = fast_exp2(__builtin_fmaf(xp, c, -Op)) * ip;
-    const float q = has_q ? fast_exp2(__builtin_fmaf(xq, c, -Oq)) * iq : 0.f;
-    return fmaxf(p - q, 0.f);
-}
-
+// grid (sequence, chunk of 16-byte vectors: 4096 per workgroup): re-reads only
+// the decision row(s) of the sequence and writes the weight mass of the
+// residual (or of p for the extra token) per 512-token piece.
 template <class E, bool VEC>
-__global__ __launch_bounds__(kBlock) void k_chain_mass(
+__global__ __launch_bounds__(kResolveThreads) void k_chain_mass(
     const typename E::raw* __restrict__ tgt, const typename E::raw* __restrict__ dft,
-    const ChainDesc* __restrict__ desc, int V, int chunk, int n_chunks, float c,
-    double* __restrict__ mass) {
-    __shared__ double redd[kWavesPerBlock];
+    const ChainDesc* __restrict__ desc, int V, int mchunk, int n_mchunks, float c,
+    double* __restrict__ piece_ws) {
     constexpr int EV = E::kVec;
-    const int b = blockIdx.x / n_chunks;
-    const int ch = blockIdx.x % n_chunks;
+    const int b = blockIdx.x / n_mchunks;
+    const int mc = blockIdx.x % n_mchunks;
     const ChainDesc d = desc[b];
-    if (d.mode != kModeResidual) return;
-    const int beg = ch * chunk;
-    const int end = min(V, beg + chunk);
-    const int nvec = (end - beg + EV - 1) / EV;
+    if (d.mode == kModeNone) return;
+    const int npieces = (V + kWave * EV - 1) / (kWave * EV);
     const typename E::raw* tp = tgt + (int64_t)d.t_row * V;
-    const bool has_q = d.d_row >= 0;
-    const typename E::raw* dp = has_q ? dft + (int64_t)d.d_row * V : tp;
-    const float ip = (float)(1.0 / d.S_p);
-    const float iq = has_q ? (float)(1.0 / d.S_q) : 0.f;
-    float acc[EV];
-#pragma unroll
-    for (int e = 0; e < EV; ++e) acc[e] = 0.f;
-    for (int vi = threadIdx.x; vi < nvec; vi += kBlock) {
-        float fp[EV], fq[EV];
-        load_vec<E, VEC>(tp, beg, end, vi, fp);
-        load_vec<E, VEC>(dp, beg, end, vi, fq);
-#pragma unroll
-        for (int e = 0; e < EV; ++e) acc[e] += residual_w(fp[e], fq[e], c, d.O_p, ip, d.O_q, iq, has_q);
-    }
-    double s = 0.0;
-#pragma unroll
-    for (int e = 0; e < EV; ++e) s += (double)acc[e];
-    s = block_sum(s, redd);
-    if (threadIdx.x == 0) mass[(int64_t)b * n_chunks + ch] = s;
+    const WeightFn wf = weight_fn(d, c, false);
+    const typename E::raw* dp = wf.has_q ? dft + (int64_t)d.d_row * V : tp;
+    const int beg = mc * mchunk;
+    const int end = min(V, beg + mchunk);
+    mass_pass<E, VEC>(tp, dp, beg, end, wf, piece_ws + (int64_t)b * npieces, npieces);
 }
 
+// One wave per sequence: the final token from the piece masses (inverse CDF in
+// token order at u_k times the total). The rare case of a residual with no
+// mass (rounding) is redrawn from p of the decision row by the same wave.
 template <class E, bool VEC>
 __global__ __launch_bounds__(kBlock) void k_chain_sample(
     const typename E::raw* __restrict__ tgt, const typename E::raw* __restrict__ dft,
-    const Partial* __restrict__ part_t, const ChainDesc* __restrict__ desc,
-    const double* __restrict__ mass, int K_max, int V, int chunk, int n_chunks, float c,
-    int32_t* __restrict__ next_out, float* __restrict__ R_out) {
-    __shared__ double redd[kWavesPerBlock];
-    __shared__ int redi[kWavesPerBlock];
-    __shared__ double sh_before, sh_target;
-    __shared__ int sh_chunk, sh_use_p;
+    const ChainDesc* __restrict__ desc, const double* __restrict__ piece_ws, int B, int V,
+    float c, int32_t* __restrict__ next_out, float* __restrict__ R_out) {
     constexpr int EV = E::kVec;
-    const int b = blockIdx.x;
+    const int b = blockIdx.x * kSeqPerBlock + threadIdx.x / kWave;
+    if (b >= B) return;
+    const int lane = threadIdx.x & (kWave - 1);
     const ChainDesc d = desc[b];
-    if (d.mode == kModeNone) {
-        if (threadIdx.x == 0) {
-            next_out[b] = -1;
-            if (R_out) R_out[b] = 0.f;
-        }
-        return;
+    int next = -1;
+    double total = 0.0;
+    if (d.mode != kModeNone) {
+        const int npieces = (V + kWave * EV - 1) / (kWave * EV);
+        const typename E::raw* tp = tgt + (int64_t)d.t_row * V;
+        const WeightFn wf = weight_fn(d, c, false);
+        const typename E::raw* dp = wf.has_q ? dft + (int64_t)d.d_row * V : tp;
+        next = sample_from_pieces<E>(piece_ws + (int64_t)b * npieces, npieces, tp, dp, V, wf,
+                                     (double)d.u, &total);
+        if (d.mode == kModeResidual && !(total > 0.0))
+            next = sample_by_rescan<E>(tp, V, weight_fn(d, c, true), (double)d.u);
     }
-    const int slots = K_max + 1;
-    if (threadIdx.x == 0) {
-        // chunk masses: residual, or p (extra token / residual with no mass)
-        double R = 0.0;
-        if (d.mode == kModeResidual)
-            for (int i = 0; i < n_chunks; ++i) R += mass[(int64_t)b * n_chunks + i];
-        const bool use_p = !(d.mode == kModeResidual && R > 0.0);
-        const Partial* pp = part_t + ((int64_t)b * slots + d.slot) * n_chunks;
-        double total = 0.0;
-        if (use_p) {
-            for (int i = 0; i < n_chunks; ++i)
-                if (pp[i].S > 0.0) total += pp[i].S * exp2((double)pp[i].o - (double)d.O_p);
-        } else {
-            total = R;
-        }
-        const double target = (double)d.u * total;
-        double cum = 0.0, before = 0.0;
-        int found = -1, last_pos = -1;
-        for (int i = 0; i < n_chunks; ++i) {
-            double m;
-            if (use_p)
-                m = pp[i].S > 0.0 ? pp[i].S * exp2((double)pp[i].o - (double)d.O_p) : 0.0;
-            else
-                m = mass[(int64_t)b * n_chunks + i];
-            if (m > 0.0) last_pos = i;
-            if (found < 0 && cum + m > target && m > 0.0) {
-                found = i;
-                before = cum;
-            }
-            cum += m;
-        }
-        if (found < 0) {
-            found = last_pos;
-            before = 0.0;
-            for (int i = 0; i < last_pos; ++i)
-                before += use_p ? (pp[i].S > 0.0 ? pp[i].S * exp2((double)pp[i].o - (double)d.O_p) : 0.0)
-                                : mass[(int64_t)b * n_chunks + i];
-        }
-        sh_before = before;
-        sh_target = target;
-        sh_chunk = found;
-        sh_use_p = use_p ? 1 : 0;
-        if (R_out) R_out[b] = (d.mode == kModeResidual) ? (float)R : 0.f;
-    }
-    __syncthreads();
-    const int ch = sh_chunk;
-    const bool use_p = sh_use_p != 0;
-    const double target = sh_target;
-    if (ch < 0) {
-        if (threadIdx.x == 0) next_out[b] = -1;
-        return;
-    }
-    // In-chunk scan: thread t owns a contiguous segment of `seg` elements.
-    const int beg = ch * chunk;
-    const int end = min(V, beg + chunk);
-    const int seg = chunk / kBlock;                   // multiple of EV
-    const int s0 = beg + threadIdx.x * seg;
-    const int s1 = min(end, s0 + seg);
-    const typename E::raw* tp = tgt + (int64_t)d.t_row * V;
-    const bool has_q = !use_p && d.d_row >= 0;
-    const typename E::raw* dp = has_q ? dft + (int64_t)d.d_row * V : tp;
-    const float ip = (float)(1.0 / d.S_p);
-    const float iq = has_q ? (float)(1.0 / d.S_q) : 0.f;
-    double mysum = 0.0;
-    int last_pos = -1;
-    for (int j0 = s0; j0 < s1; j0 += EV) {
-        float fp[EV], fq[EV];
-        load_vec<E, false>(tp, j0, s1, 0, fp);
-        if (has_q) load_vec<E, false>(dp, j0, s1, 0, fq);
-#pragma unroll
-        for (int e = 0; e < EV; ++e) {
-            if (j0 + e >= s1) break;
-            const float w = use_p ? fast_exp2(__builtin_fmaf(fp[e], c, -d.O_p))
-                                  : residual_w(fp[e], has_q ? fq[e] : 0.f, c, d.O_p, ip, d.O_q, iq, has_q);
-            mysum += (double)w;
-            if (w > 0.f) last_pos = j0 + e;
-        }
-    }
-    double total;
-    const double excl = block_exclusive_scan(mysum, redd, &total);
-    const double start = sh_before + excl;
-    const bool crosses = (s0 < s1) && (start + mysum > target);
-    const int first = block_min_int(crosses ? (int)threadIdx.x : 0x7fffffff, redi);
-    if (first == 0x7fffffff) {
-        const int lp = block_max_int(last_pos, redi);
-        if (threadIdx.x == 0) next_out[b] = lp;
-        return;
-    }
-    if ((int)threadIdx.x == first) {
-        double run = start;
-        int pick = -1, lastp = -1;
-        for (int j0 = s0; j0 < s1 && pick < 0; j0 += EV) {
-            float fp[EV], fq[EV];
-            load_vec<E, false>(tp, j0, s1, 0, fp);
-            if (has_q) load_vec<E, false>(dp, j0, s1, 0, fq);
-#pragma unroll
-            for (int e = 0; e < EV; ++e) {
-                if (j0 + e >= s1 || pick >= 0) break;
-                const float w = use_p ? fast_exp2(__builtin_fmaf(fp[e], c, -d.O_p))
-                                      : residual_w(fp[e], has_q ? fq[e] : 0.f, c, d.O_p, ip, d.O_q, iq, has_q);
-                run += (double)w;
-                if (w > 0.f) lastp = j0 + e;
-                if (run > target && w > 0.f) pick = j0 + e;
-            }
-        }
-        next_out[b] = pick >= 0 ? pick : lastp;
+    if (lane == 0) {
+        next_out[b] = next;
+        if (R_out) R_out[b] = (d.mode == kModeResidual) ? (float)total : 0.f;
     }
 }
 
@@ -520,12 +697,14 @@ __global__ __launch_bounds__(kBlock) void k_chain_sample(
 size_t chain_full_ws_bytes(int B, int K_max, int V, int dtype) {
     const int nc = n_chunks_for(V, dtype);
     const size_t slots = (size_t)B * (K_max + 1);
+    const int ev = dtype == 1 ? 8 : 4;
+    const size_t npieces = (size_t)(V + 64 * ev - 1) / (64 * ev);
     Carve cv;
-    cv.take(slots * nc * sizeof(Partial));      // part_t
-    cv.take(slots * nc * sizeof(Partial));      // part_d
-    cv.take(slots * 2 * sizeof(float));         // xy
-    cv.take((size_t)B * sizeof(ChainDesc));     // desc
-    cv.take((size_t)B * nc * sizeof(double));   // mass
+    cv.take(slots * nc * sizeof(Partial));          // part_t
+    cv.take(slots * nc * sizeof(Partial));          // part_d
+    cv.take(slots * 2 * sizeof(float));             // xy
+    cv.take((size_t)B * npieces * sizeof(double));  // piece masses
+    cv.take((size_t)B * sizeof(ChainDesc));         // decisions
     return cv.off;
 }
 
@@ -534,27 +713,34 @@ static hipError_t chain_full_impl(const ChainArgs& a) {
     const int nc = n_chunks_for(a.V, a.dtype);
     const int chunk = chunk_elems(a.dtype);
     const size_t slots = (size_t)a.B * (a.K_max + 1);
+    const size_t npieces = (size_t)(a.V + 64 * E::kVec - 1) / (64 * E::kVec);
     Carve cv;
     char* ws = static_cast<char*>(a.ws);
     Partial* part_t = reinterpret_cast<Partial*>(ws + cv.take(slots * nc * sizeof(Partial)));
     Partial* part_d = reinterpret_cast<Partial*>(ws + cv.take(slots * nc * sizeof(Partial)));
     float* xy = reinterpret_cast<float*>(ws + cv.take(slots * 2 * sizeof(float)));
+    double* pieces = reinterpret_cast<double*>(ws + cv.take((size_t)a.B * npieces * sizeof(double)));
     ChainDesc* desc = reinterpret_cast<ChainDesc*>(ws + cv.take((size_t)a.B * sizeof(ChainDesc)));
-    double* mass = reinterpret_cast<double*>(ws + cv.take((size_t)a.B * nc * sizeof(double)));
+    const int mchunk = kMassChunkVecs * E::kVec;
+    const int n_mchunks = (a.V + mchunk - 1) / mchunk;
     const float c = (float)(1.4426950408889634 / (double)a.temperature);
     using raw = typename E::raw;
     const raw* tgt = static_cast<const raw*>(a.target);
     const raw* dft = static_cast<const raw*>(a.draft);
     const unsigned grid1 = (unsigned)(slots * nc);
+    PassTimer::mark_before(a.stream);
     hipLaunchKernelGGL((k_chain_stats<E, VEC>), dim3(grid1), dim3(kBlock), 0, a.stream, tgt, dft,
                        a.tokens, a.cu, a.K_max, a.V, chunk, nc, c, part_t, part_d, xy);
-    hipLaunchKernelGGL(k_chain_decide, dim3(a.B), dim3(kWave), 0, a.stream, part_t, part_d, xy,
-                       a.tokens, a.uniforms, a.cu, a.K_max, a.V, nc, c, a.accepted_len, a.probs_out,
-                       a.seq_status, desc);
-    hipLaunchKernelGGL((k_chain_mass<E, VEC>), dim3((unsigned)((size_t)a.B * nc)), dim3(kBlock), 0,
-                       a.stream, tgt, dft, desc, a.V, chunk, nc, c, mass);
-    hipLaunchKernelGGL((k_chain_sample<E, VEC>), dim3(a.B), dim3(kBlock), 0, a.stream, tgt, dft,
-                       part_t, desc, mass, a.K_max, a.V, chunk, nc, c, a.next_token, a.resid_mass_out);
+    PassTimer::mark_after(a.stream);
+    const unsigned seq_blocks = (unsigned)((a.B + kSeqPerBlock - 1) / kSeqPerBlock);
+    hipLaunchKernelGGL(k_chain_decide, dim3(seq_blocks), dim3(kBlock), 0, a.stream, part_t, part_d,
+                       xy, a.tokens, a.uniforms, a.cu, a.B, a.K_max, a.V, nc, c, a.accepted_len,
+                       a.probs_out, a.seq_status, desc);
+    hipLaunchKernelGGL((k_chain_mass<E, VEC>), dim3((unsigned)((size_t)a.B * n_mchunks)),
+                       dim3(kResolveThreads), 0, a.stream, tgt, dft, desc, a.V, mchunk, n_mchunks, c,
+                       pieces);
+    hipLaunchKernelGGL((k_chain_sample<E, VEC>), dim3(seq_blocks), dim3(kBlock), 0, a.stream, tgt,
+                       dft, desc, pieces, a.B, a.V, c, a.next_token, a.resid_mass_out);
     return hipGetLastError();
 }
 

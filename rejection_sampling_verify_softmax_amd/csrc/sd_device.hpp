@@ -45,8 +45,19 @@ struct F32 {
     }
 };
 
+#ifndef SD_NT_LOADS
+#define SD_NT_LOADS 1
+#endif
+// 16-byte load of vector `vec_index` of a row. Logit rows are streamed once, so
+// the default marks the loads non-temporal (they bypass cache retention).
 __device__ __forceinline__ uint4 load16(const void* base, int64_t vec_index) {
+#if SD_NT_LOADS
+    typedef unsigned int v4u __attribute__((ext_vector_type(4)));
+    const v4u r = __builtin_nontemporal_load(reinterpret_cast<const v4u*>(base) + vec_index);
+    return make_uint4(r.x, r.y, r.z, r.w);
+#else
     return reinterpret_cast<const uint4*>(base)[vec_index];
+#endif
 }
 
 // 2^x on the hardware transcendental unit (v_exp_f32).

@@ -13,10 +13,22 @@ namespace sd {
 // aligned.
 constexpr int kMaxTopk = 256;
 constexpr int kMaxTreeK = 16;
-constexpr int kChunkBf16 = 16384;
-constexpr int kChunkF32 = 8192;
+#ifndef SD_CHUNK_BF16
+#define SD_CHUNK_BF16 32768
+#endif
+#ifndef SD_CHUNK_F32
+#define SD_CHUNK_F32 16384
+#endif
+constexpr int kChunkBf16 = SD_CHUNK_BF16;
+constexpr int kChunkF32 = SD_CHUNK_F32;
+static_assert(kChunkBf16 % (256 * 8) == 0, "bf16 chunk: whole workgroup rounds of 16-byte vectors");
+static_assert(kChunkF32 % (256 * 4) == 0, "fp32 chunk: whole workgroup rounds of 16-byte vectors");
 
 inline int chunk_elems(int dtype) { return dtype == 1 ? kChunkBf16 : kChunkF32; }
+// Sub-block: one wave's 64 consecutive 16-byte vectors (512 bf16 or 256 fp32
+// elements). Residual masses are kept per sub-block.
+inline int sub_block_elems(int dtype) { return dtype == 1 ? 512 : 256; }
+inline int sub_blocks_per_chunk(int dtype) { return chunk_elems(dtype) / sub_block_elems(dtype); }
 inline int n_chunks_for(int V, int dtype) {
     const int c = chunk_elems(dtype);
     return (V + c - 1) / c;
@@ -29,6 +41,22 @@ struct Carve {
         size_t o = off;
         off += (bytes + 255) & ~size_t(255);
         return o;
+    }
+};
+
+// Optional events around the streaming kernel of the next call on this thread
+// (set by sd_time_next_stream_pass). mark_before()/mark_after() record and then
+// clear them.
+struct PassTimer {
+    static thread_local hipEvent_t start;
+    static thread_local hipEvent_t stop;
+    static void mark_before(hipStream_t s) {
+        if (start) (void)hipEventRecord(start, s);
+        start = nullptr;
+    }
+    static void mark_after(hipStream_t s) {
+        if (stop) (void)hipEventRecord(stop, s);
+        stop = nullptr;
     }
 };
 

@@ -565,9 +565,11 @@ static hipError_t chain_topk_impl(const ChainArgs& a) {
     TopEntry* lists = reinterpret_cast<TopEntry*>(ws + cv.take(tasks * a.top_k * sizeof(TopEntry)));
     int32_t* counts = reinterpret_cast<int32_t*>(ws + cv.take(tasks * sizeof(int32_t)));
     using raw = typename E::raw;
+    PassTimer::mark_before(a.stream);
     hipLaunchKernelGGL((k_topk_rows<E, VEC>), dim3((unsigned)tasks), dim3(kBlock), 0, a.stream,
                        static_cast<const raw*>(a.target), static_cast<const raw*>(a.draft), a.cu,
                        a.K_max, a.V, a.top_k, 1, lists, counts);
+    PassTimer::mark_after(a.stream);
     hipLaunchKernelGGL(k_chain_topk_decide, dim3(a.B), dim3(kWave), 0, a.stream, lists, counts,
                        a.tokens, a.uniforms, a.cu, a.K_max, a.V, a.top_k, a.temperature,
                        a.accepted_len, a.next_token, a.probs_out, a.resid_mass_out, a.seq_status);
@@ -592,6 +594,7 @@ hipError_t launch_tree_build(const float* marg, int B, int K, int V, int N, int3
     char* w = static_cast<char*>(ws);
     TopEntry* lists = reinterpret_cast<TopEntry*>(w + cv.take(tasks * W * sizeof(TopEntry)));
     int32_t* counts = reinterpret_cast<int32_t*>(w + cv.take(tasks * sizeof(int32_t)));
+    PassTimer::mark_before(stream);
     if (tasks > 0) {
         if (V % F32::kVec == 0)
             hipLaunchKernelGGL((k_topk_rows<F32, true>), dim3((unsigned)tasks), dim3(kBlock), 0,
@@ -600,6 +603,7 @@ hipError_t launch_tree_build(const float* marg, int B, int K, int V, int N, int3
             hipLaunchKernelGGL((k_topk_rows<F32, false>), dim3((unsigned)tasks), dim3(kBlock), 0,
                                stream, marg, marg, nullptr, 0, V, W, 0, lists, counts);
     }
+    PassTimer::mark_after(stream);
     hipLaunchKernelGGL(k_tree_build, dim3(B), dim3(kWave), 0, stream, lists, counts, K, N, W, tok,
                        par, dep, score, reinterpret_cast<unsigned long long*>(anc), n_nodes);
     return hipGetLastError();
