@@ -60,6 +60,11 @@ __device__ __forceinline__ uint4 load16(const void* base, int64_t vec_index) {
 #endif
 }
 
+// 16-byte load that is kept in the caches (for data read twice in a row).
+__device__ __forceinline__ uint4 load16_cached(const void* base, int64_t vec_index) {
+    return reinterpret_cast<const uint4*>(base)[vec_index];
+}
+
 // 2^x on the hardware transcendental unit (v_exp_f32).
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
