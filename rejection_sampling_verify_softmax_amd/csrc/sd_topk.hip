@@ -44,36 +44,10 @@ __device__ __forceinline__ unsigned long long make_key(float x, int idx) {
     return ((unsigned long long)ordered_bits(x) << 32) | (unsigned long long)(0xffffffffu - (uint32_t)idx);
 }
 
-// Sorts buf[0..n) descending (bitonic network, n a power of two <= kCap). All
-// kBlock threads call it.
-__device__ void bitonic_desc(unsigned long long* buf, int n) {
-    for (int size = 2; size <= n; size <<= 1) {
-        for (int stride = size >> 1; stride > 0; stride >>= 1) {
-            for (int i = threadIdx.x; i < n / 2; i += kBlock) {
-                const int lo = 2 * stride * (i / stride) + (i % stride);
-                const int hi = lo + stride;
-                const bool desc = (lo & size) == 0;
-                const unsigned long long a = buf[lo], b = buf[hi];
-                if ((a < b) == desc) {
-                    buf[lo] = b;
-                    buf[hi] = a;
-                }
-            }
-            __syncthreads();
-        }
-    }
-}
-
 __device__ __forceinline__ int pow2_at_least(int n) {
     int p = 2;
     while (p < n) p <<= 1;
     return p;
-}
-
-// Sorts the first n keys of buf descending (entries n.. must be zero-filled up
-// to the next power of two). All threads call it.
-__device__ void sort_candidates(unsigned long long* buf, int n) {
-    bitonic_desc(buf, pow2_at_least(n < 2 ? 2 : n));
 }
 
 // Row task -> row pointer. Chain: task = ((b * slots) + s) * 2 + side, side 0 =
@@ -97,25 +71,77 @@ __device__ const typename E::raw* topk_row(const typename E::raw* tgt, const typ
 constexpr int kTopkSample = 8;           // vectors per thread held in registers for the threshold
 constexpr int kTopkU = 4;                // vectors per thread per main-pass step (as many more in flight)
 constexpr int kWaveCap = 512;            // per-wave candidate buffer (64-bit keys)
+constexpr int kQueue = 4 * kWave;        // per-wave queue of vector indices that may hold a candidate
+static_assert(kQueue >= kWave * kTopkU, "one offer step must fit an empty queue");
+static_assert(kTopkSample % kTopkU == 0, "the sample is offered in steps of kTopkU vectors");
 
+// 16-byte vector `gvi` of a row as raw element bits; elements past the row
+// (or past gvend) read as an all-ones NaN, which no test keeps.
 template <class E, bool VEC>
-__device__ __forceinline__ void topk_load(const typename E::raw* row, int V, int nvec, int vi,
-                                          float (&f)[E::kVec]) {
-    constexpr int EV = E::kVec;
+__device__ __forceinline__ uint4 topk_raw(const typename E::raw* row, int V, int gvend, int gvi) {
     if (VEC) {
-        if (vi < nvec) {
-            E::unpack(load16(row, vi), f);
+        if (gvi < gvend) return load16(row, gvi);
+        return make_uint4(0xffffffffu, 0xffffffffu, 0xffffffffu, 0xffffffffu);
+    }
+    constexpr int EV = E::kVec;
+    uint32_t wd[4] = {0xffffffffu, 0xffffffffu, 0xffffffffu, 0xffffffffu};
+    const int j0 = gvi * EV;
+    if (gvi < gvend) {
+        if (EV == 4) {
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+                if (j0 + e < V) wd[e] = __float_as_uint(E::at(row, j0 + e));
         } else {
 #pragma unroll
-            for (int e = 0; e < EV; ++e) f[e] = NAN;
-        }
-    } else {
-#pragma unroll
-        for (int e = 0; e < EV; ++e) {
-            const int j = vi * EV + e;
-            f[e] = (vi < nvec && j < V) ? E::at(row, j) : NAN;
+            for (int e = 0; e < EV; ++e) {
+                const uint32_t h = (j0 + e < V) ? (__float_as_uint(E::at(row, j0 + e)) >> 16) : 0xffffu;
+                wd[e / 2] = (e & 1) ? ((wd[e / 2] & 0xffffu) | (h << 16)) : ((wd[e / 2] & 0xffff0000u) | h);
+            }
         }
     }
+    return make_uint4(wd[0], wd[1], wd[2], wd[3]);
+}
+
+// Element e of a raw vector as a float.
+template <class E>
+__device__ __forceinline__ float raw_elem(const uint4& v, int e) {
+    if (E::kVec == 4) {
+        const uint32_t w = e == 0 ? v.x : e == 1 ? v.y : e == 2 ? v.z : v.w;
+        return __uint_as_float(w);
+    }
+    const int q = e >> 1;
+    const uint32_t w = q == 0 ? v.x : q == 1 ? v.y : q == 2 ? v.z : v.w;
+    return __uint_as_float((e & 1) ? (w & 0xffff0000u) : (w << 16));
+}
+
+typedef short short2_t __attribute__((ext_vector_type(2)));
+
+// Whether some element of v may reach t > 0 (t16 / t32: the threshold's bits).
+// For t > 0 a signed-integer compare of the raw bits orders the elements
+// correctly: negatives (sign bit set) compare below, NaN compares high and is
+// weeded out later by the float test. bf16 uses packed 16-bit maxima.
+template <class E>
+__device__ __forceinline__ bool vec_may_reach(const uint4& v, int32_t tbits) {
+    if (E::kVec == 4) {
+        const int32_t m = max(max((int32_t)v.x, (int32_t)v.y), max((int32_t)v.z, (int32_t)v.w));
+        return m >= tbits;
+    }
+    const short2_t a = __builtin_bit_cast(short2_t, v.x), b = __builtin_bit_cast(short2_t, v.y);
+    const short2_t c = __builtin_bit_cast(short2_t, v.z), d = __builtin_bit_cast(short2_t, v.w);
+    const short2_t m = __builtin_elementwise_max(__builtin_elementwise_max(a, b),
+                                                 __builtin_elementwise_max(c, d));
+    return max((int32_t)m.x, (int32_t)m.y) >= tbits;
+}
+
+// Whether some element of v reaches t (any t; NaN never does).
+template <class E>
+__device__ __forceinline__ bool vec_reaches(const uint4& v, float t) {
+    float f[E::kVec];
+    E::unpack(v, f);
+    bool r = false;
+#pragma unroll
+    for (int e = 0; e < E::kVec; ++e) r = r || (f[e] >= t);
+    return r;
 }
 
 // Orders the wave's LDS traffic: every lane's earlier LDS writes are visible
@@ -148,16 +174,17 @@ __device__ void wave_sort_desc(unsigned long long* a, int n) {
 }
 
 // A wave's running top-k: `cnt` keys in its LDS buffer, every kept key beats
-// `thr` (whose value part is `tf`). Uniform across the wave's lanes.
+// `thr` (whose value part is `tf`); `seen` counts every key ever appended.
+// Uniform across the wave's lanes.
 struct WaveTop {
     int cnt;
+    int seen;
     unsigned long long thr;
     float tf;
 };
 
 // Sorts the wave's buffer, keeps its best topk and raises the threshold to
-// the topk-th key (which topk real tokens reach). Out of line: it runs rarely
-// and keeps the per-token loop of the caller small enough to unroll.
+// the topk-th key (which topk real tokens reach). Out of line: it runs rarely.
 __device__ __noinline__ WaveTop wave_compact(unsigned long long* wb, WaveTop st, int topk) {
     const int lane = threadIdx.x & (kWave - 1);
     const int n = st.cnt;
@@ -172,61 +199,156 @@ __device__ __noinline__ WaveTop wave_compact(unsigned long long* wb, WaveTop st,
     return st;
 }
 
-// Offers one vector per lane (values f, 16-byte vector index vi): tokens whose
-// key beats the wave's threshold are appended to its buffer; slots come from a
-// wave ballot (no atomics). A float pre-check and wave-wide ballots skip the
-// 64-bit key work for token slots no lane needs.
-template <int EV>
-__device__ __forceinline__ void wave_offer(const float (&f)[EV], int vi, unsigned long long* wb,
-                                           WaveTop& st, int topk) {
-    float vm = f[0];
+// Per-wave state of the row pass: the running top-k, a queue of the 16-byte
+// vector indices that may hold a candidate, and the threshold's raw bits for
+// the integer pre-check.
+struct Offer {
+    WaveTop st;
+    int qn;
+    int32_t tbits;
+    int32_t* qi;
+    unsigned long long* wb;
+};
+
+template <class E>
+__device__ __forceinline__ int32_t threshold_bits(float tf) {
+    const uint32_t u = __float_as_uint(tf);
+    return E::kVec == 4 ? (int32_t)u : (int32_t)(u >> 16);
+}
+
+// Processes the queue, one vector per lane per round: the vector is read
+// again (queued vectors are a few per cent of the row) and each element whose
+// key beats the threshold is appended, one element per lane per step, slots
+// from a wave ballot. Before a step could overflow the buffer, and whenever it
+// holds 2*topk keys, the buffer is compacted, which raises the threshold.
+template <class E, bool VEC>
+__device__ __forceinline__ void wave_drain(Offer& o, const typename E::raw* row, int V, int gvend,
+                                           int topk) {
+    constexpr int EV = E::kVec;
+    const int lane = threadIdx.x & (kWave - 1);
+    const int trigger = min(2 * topk, kWaveCap - kWave);
+    wave_lds_sync();
+    for (int base = 0; base < o.qn; base += kWave) {
+        const bool live = base + lane < o.qn;
+        const int vi = live ? o.qi[base + lane] : gvend;
+        const uint4 v = topk_raw<E, VEC>(row, V, gvend, vi);
+        uint32_t mask = 0u;
 #pragma unroll
-    for (int e = 1; e < EV; ++e) vm = fmaxf(vm, f[e]);
-    if (__ballot(vm >= st.tf) == 0ull) return;        // NaN and sub-threshold vectors
+        for (int e = 0; e < EV; ++e) mask |= (raw_elem<E>(v, e) >= o.st.tf) ? (1u << e) : 0u;
+        while (true) {
+            const bool has = mask != 0u;
+            if (__ballot(has) == 0ull) break;
+            if (o.st.cnt >= trigger) o.st = wave_compact(o.wb, o.st, topk);
+            unsigned long long key = 0ull;
+            if (has) {
+                const int e = __builtin_ctz(mask);
+                mask &= mask - 1u;
+                key = make_key(raw_elem<E>(v, e), vi * EV + e);
+            }
+            const bool take = has && key > o.st.thr;
+            const unsigned long long bal = __ballot(take);
+            if (take) {
+                const int off = __builtin_amdgcn_mbcnt_hi((uint32_t)(bal >> 32),
+                                                          __builtin_amdgcn_mbcnt_lo((uint32_t)bal, 0u));
+                o.wb[o.st.cnt + off] = key;
+            }
+            o.st.cnt += __popcll(bal);
+            o.st.seen += __popcll(bal);
+        }
+    }
+    wave_lds_sync();                 // the queue is rewritten after this
+    o.qn = 0;
+    o.tbits = threshold_bits<E>(o.st.tf);
+}
+
+// Offers N raw vectors per lane (16-byte indices vi0 + u * kBlock): a
+// pre-check against the wave's threshold, then ballots; the vectors that may
+// hold a candidate are queued (their indices), after draining the queue if it
+// could overflow. POS: the threshold is positive, so the integer pre-check on
+// the raw bits applies.
+template <class E, bool VEC, bool POS, int N>
+__device__ __forceinline__ void offer_vecs(Offer& o, const uint4 (&v)[N], int vi0,
+                                           const typename E::raw* row, int V, int gvend, int topk) {
+    bool may[N];
+    unsigned long long bal[N];
+    int n = 0;
 #pragma unroll
-    for (int e = 0; e < EV; ++e) {
-        const float x = f[e];
-        const bool pass = x >= st.tf;
-        if (__ballot(pass) == 0ull) continue;
-        const unsigned long long key = pass ? make_key(x, vi * EV + e) : 0ull;
-        bool take = pass && key > st.thr;
-        unsigned long long bal = __ballot(take);
-        if (bal == 0ull) continue;
-        if (st.cnt + __popcll(bal) > kWaveCap) {
-            st = wave_compact(wb, st, topk);
-            take = take && key > st.thr;
-            bal = __ballot(take);
+    for (int u = 0; u < N; ++u) {
+        may[u] = POS ? vec_may_reach<E>(v[u], o.tbits) : vec_reaches<E>(v[u], o.st.tf);
+        bal[u] = __ballot(may[u]);
+        n += __popcll(bal[u]);
+    }
+    if (n == 0) return;
+    if (o.qn + n > kQueue) wave_drain<E, VEC>(o, row, V, gvend, topk);
+#pragma unroll
+    for (int u = 0; u < N; ++u) {
+        if (may[u]) {
+            const int slot = o.qn + __builtin_amdgcn_mbcnt_hi((uint32_t)(bal[u] >> 32),
+                                                              __builtin_amdgcn_mbcnt_lo((uint32_t)bal[u], 0u));
+            o.qi[slot] = vi0 + u * kBlock;
         }
-        if (take) {
-            const int off = __builtin_amdgcn_mbcnt_hi((uint32_t)(bal >> 32),
-                                                      __builtin_amdgcn_mbcnt_lo((uint32_t)bal, 0u));
-            wb[st.cnt + off] = key;
-        }
-        st.cnt += __popcll(bal);
-        if (st.cnt >= kWaveCap / 2) st = wave_compact(wb, st, topk);   // keep the threshold tight
+        o.qn += __popcll(bal[u]);
     }
 }
 
-// Reads 16-byte vector `gvi` (index within the row) of tokens [.., end) into f;
-// NaN past the end.
-template <class E, bool VEC>
-__device__ __forceinline__ void topk_load_range(const typename E::raw* row, int end, int gvend,
-                                                int gvi, float (&f)[E::kVec]) {
-    constexpr int EV = E::kVec;
-    if (VEC) {
-        if (gvi < gvend) {
-            E::unpack(load16(row, gvi), f);
-        } else {
+// Streams vectors [v_start, gvend) of the row through offer_vecs, kTopkU
+// vectors per thread per step with the next step's loads in flight.
+template <class E, bool VEC, bool POS>
+__device__ __forceinline__ void offer_range(Offer& o, const typename E::raw* row, int V, int gvend,
+                                            int v_start, int topk) {
+    const int tid = threadIdx.x;
+    uint4 cur[kTopkU], nxt[kTopkU];
 #pragma unroll
-            for (int e = 0; e < EV; ++e) f[e] = NAN;
-        }
-    } else {
+    for (int u = 0; u < kTopkU; ++u) cur[u] = topk_raw<E, VEC>(row, V, gvend, v_start + u * kBlock + tid);
+    for (int v0 = v_start; v0 < gvend; v0 += kBlock * kTopkU) {
+        const int vn = v0 + kBlock * kTopkU;
 #pragma unroll
-        for (int e = 0; e < EV; ++e) {
-            const int j = gvi * EV + e;
-            f[e] = (gvi < gvend && j < end) ? E::at(row, j) : NAN;
-        }
+        for (int u = 0; u < kTopkU; ++u) nxt[u] = topk_raw<E, VEC>(row, V, gvend, vn + u * kBlock + tid);
+        offer_vecs<E, VEC, POS, kTopkU>(o, cur, v0 + tid, row, V, gvend, topk);
+#pragma unroll
+        for (int u = 0; u < kTopkU; ++u) cur[u] = nxt[u];
     }
+    if (o.qn > 0) wave_drain<E, VEC>(o, row, V, gvend, topk);
+}
+
+// One pass over the row from threshold t: with SAMPLE, the held sample first
+// and then vectors from the end of the sample on; else the whole row. Leaves
+// each wave's best min(cnt, topk) keys sorted at the front of its buffer.
+template <class E, bool VEC, bool POS, bool SAMPLE>
+__device__ __forceinline__ WaveTop row_pass(const typename E::raw* row, int V, int gvend, float t,
+                                            const uint4 (&hs)[kTopkSample], int32_t* qi,
+                                            unsigned long long* wb, int topk) {
+    Offer o;
+    o.st.cnt = 0;
+    o.st.seen = 0;
+    o.st.thr = t == -INFINITY ? 0ull : ((unsigned long long)ordered_bits(t) << 32) - 1ull;
+    o.st.tf = t;
+    o.qn = 0;
+    o.tbits = threshold_bits<E>(t);
+    o.qi = qi;
+    o.wb = wb;
+    int v_start = 0;
+    if (SAMPLE) {
+#pragma unroll
+        for (int g = 0; g < kTopkSample; g += kTopkU)
+            offer_vecs<E, VEC, POS, kTopkU>(o, *reinterpret_cast<const uint4(*)[kTopkU]>(&hs[g]),
+                                            g * kBlock + threadIdx.x, row, V, gvend, topk);
+        v_start = kTopkSample * kBlock;
+    }
+    offer_range<E, VEC, POS>(o, row, V, gvend, v_start, topk);
+    return wave_compact(wb, o.st, topk);
+}
+
+// Number of keys in list[0..n) (sorted descending, distinct) above key.
+__device__ __forceinline__ int count_above(const unsigned long long* list, int n,
+                                           unsigned long long key) {
+    int lo = 0, hi = n;
+    while (lo < hi) {
+        const int mid = (lo + hi) >> 1;
+        if (list[mid] > key) lo = mid + 1;
+        else hi = mid;
+    }
+    return lo;
 }
 
 // Softmax statistics of a kept list and p(y) of one token (fp64).
@@ -238,19 +360,34 @@ struct RowTop {
     double py;          // p(y) of the position's draft token (0 if not kept)
 };
 
-// One workgroup per row task: the exact top-k of the row, in key order (value
+// Rank (from 0) of the sample maximum taken as the first threshold guess:
+// about twice the number of the row's top-k expected among the sampled
+// tokens, plus 4; the topk-th maximum (always a valid bound) when the sample
+// covers the row.
+__device__ __forceinline__ int guess_rank(int topk, int sampled, int V) {
+    if (sampled >= V) return topk - 1;
+    const int j = (int)ceilf(2.0f * (float)topk * (float)sampled / (float)V) + 4;
+    return min(j, topk) - 1;
+}
+
+// One workgroup per row task: the exact top-k of the row in key order (value
 // desc, then lower id first), written as TopEntry; for the rows of a chain
 // also the row's softmax statistics over the kept set and p(y) of the
 // position's draft token (fp64).
-//  1. Every thread holds kTopkSample vectors of the row's start in registers
-//     and takes their maximum. The topk-th largest of these 256 maxima (distinct
-//     tokens) is reached by at least topk tokens, so no token below it can be
-//     in the top-k: it is every wave's starting threshold.
-//  2. Each wave offers its held vectors and then its share of the rest of the
-//     row (streamed, next step in flight) to its own LDS buffer; when the
-//     buffer is half full the wave sorts it, keeps its best topk and raises its
-//     threshold. No workgroup barrier.
-//  3. The waves' lists are merged (sorted together) and the first topk written.
+//  1. Every thread holds kTopkSample vectors of the row's start and takes
+//     their maximum. Ranked among the 256 maxima (distinct tokens), the
+//     topk-th is a guaranteed bound (at least topk tokens reach it) and a
+//     higher one is a guess.
+//  2. With the guess as threshold, each wave streams its share of the row.
+//     A vector whose largest element may reach the threshold is queued; full
+//     queues are processed one vector per lane, appending each element that
+//     beats the wave's running k-th key to its LDS buffer, which is compacted
+//     (sorted, cut to topk) as it fills, raising the threshold.
+//  3. If fewer than topk tokens reached the guess, it was too high: the row is
+//     streamed again from the guaranteed bound (rare; the result is exact
+//     either way, since a token is dropped only when topk tokens beat it).
+//  4. The waves' sorted lists are merged by rank (binary search in the other
+//     lists) and the first topk written.
 template <class E, bool VEC>
 __global__ __launch_bounds__(kBlock) void k_topk_rows(const typename E::raw* __restrict__ tgt,
                                                       const typename E::raw* __restrict__ dft,
@@ -261,10 +398,12 @@ __global__ __launch_bounds__(kBlock) void k_topk_rows(const typename E::raw* __r
                                                       int32_t* __restrict__ counts,
                                                       RowTop* __restrict__ rowtop) {
     __shared__ unsigned long long wbuf[kWavesPerBlock][kWaveCap];
-    __shared__ unsigned long long mbuf[kWavesPerBlock * kMaxTopk];
+    __shared__ int32_t qi_all[kWavesPerBlock][kQueue];
     __shared__ float lmax[kBlock];
     __shared__ int wcnt[kWavesPerBlock];
-    __shared__ unsigned long long thr0;
+    __shared__ int wseen[kWavesPerBlock];
+    __shared__ float t_guess, t_safe;
+    __shared__ double red[kWavesPerBlock];
     constexpr int EV = E::kVec;
     const int task = blockIdx.x;
     const typename E::raw* row = topk_row<E>(tgt, dft, cu, K_max, V, task, chain != 0);
@@ -272,32 +411,11 @@ __global__ __launch_bounds__(kBlock) void k_topk_rows(const typename E::raw* __r
     const int tid = threadIdx.x;
     const int w = tid / kWave;
     const int lane = tid & (kWave - 1);
-    const int end = V;
-    const int vb = 0;
     const int gvend = (V + EV - 1) / EV;
-    const uint4 nanv = make_uint4(0xffffffffu, 0xffffffffu, 0xffffffffu, 0xffffffffu);
-    // 1. starting threshold from the held sample (kept packed)
+    // 1. thresholds from the held sample
     uint4 hs[kTopkSample];
 #pragma unroll
-    for (int i = 0; i < kTopkSample; ++i) {
-        const int gvi = vb + i * kBlock + tid;
-        if (VEC) {
-            hs[i] = gvi < gvend ? load16(row, gvi) : nanv;
-        } else {
-            float f[EV];
-            topk_load_range<E, VEC>(row, end, gvend, gvi, f);
-            uint32_t wd[4] = {0xffffffffu, 0xffffffffu, 0xffffffffu, 0xffffffffu};
-            if (EV == 4) {
-#pragma unroll
-                for (int e = 0; e < 4 && e < EV; ++e) wd[e] = __float_as_uint(f[e]);
-            } else {
-#pragma unroll
-                for (int e = 0; e < EV; e += 2)
-                    wd[e / 2] = (__float_as_uint(f[e]) >> 16) | (__float_as_uint(f[e + 1]) & 0xffff0000u);
-            }
-            hs[i] = make_uint4(wd[0], wd[1], wd[2], wd[3]);
-        }
-    }
+    for (int i = 0; i < kTopkSample; ++i) hs[i] = topk_raw<E, VEC>(row, V, gvend, i * kBlock + tid);
     float m = -INFINITY;
     bool any = false;
 #pragma unroll
@@ -312,99 +430,60 @@ __global__ __launch_bounds__(kBlock) void k_topk_rows(const typename E::raw* __r
             }
     }
     lmax[tid] = any ? m : NAN;
-    if (tid == 0) thr0 = 0ull;     // keeps every non-NaN token unless raised below
+    if (tid == 0) {
+        t_guess = -INFINITY;
+        t_safe = -INFINITY;
+    }
     __syncthreads();
+    const int jg = guess_rank(topk, min(V, kTopkSample * kBlock * EV), V);
     if (any) {
         int rank = 0;
         for (int j = 0; j < kBlock; ++j) {
-            const float o = lmax[j];
-            rank += (o > m) || (o == m && j < tid);
+            const float x = lmax[j];
+            rank += (x > m) || (x == m && j < tid);
         }
-        if (rank == topk - 1) {
-            const float t = (m == 0.f) ? 0.f : m;
-            thr0 = ((unsigned long long)ordered_bits(t) << 32) - 1ull;   // every x >= t passes
-        }
+        const float t = (m == 0.f) ? 0.f : m;
+        if (rank == jg) t_guess = t;
+        if (rank == topk - 1) t_safe = t;
     }
     __syncthreads();
-    WaveTop st;
-    st.cnt = 0;
-    st.thr = thr0;
-    st.tf = st.thr == 0ull ? -INFINITY : from_ordered((uint32_t)((st.thr + 1ull) >> 32));
-    unsigned long long* wb = wbuf[w];
-    // 2. offer the held sample, then stream the rest of the row
-#pragma unroll
-    for (int i = 0; i < kTopkSample; ++i) {
-        float f[EV];
-        E::unpack(hs[i], f);
-        wave_offer<EV>(f, vb + i * kBlock + tid, wb, st, topk);
+    // 2. the pass from the guess
+    const float tg = t_guess, ts = t_safe;
+    WaveTop st = tg > 0.f ? row_pass<E, VEC, true, true>(row, V, gvend, tg, hs, qi_all[w], wbuf[w], topk)
+                          : row_pass<E, VEC, false, true>(row, V, gvend, tg, hs, qi_all[w], wbuf[w], topk);
+    if (lane == 0) {
+        wcnt[w] = st.cnt;
+        wseen[w] = st.seen;
     }
-    const int v_start = vb + kTopkSample * kBlock;
-    if (VEC) {
-        uint4 cur[kTopkU], nxt[kTopkU];
-#pragma unroll
-        for (int u = 0; u < kTopkU; ++u) {
-            const int gvi = v_start + u * kBlock + tid;
-            cur[u] = gvi < gvend ? load16(row, gvi) : nanv;
-        }
-        for (int v0 = v_start; v0 < gvend; v0 += kBlock * kTopkU) {
-            const int vn = v0 + kBlock * kTopkU;
-#pragma unroll
-            for (int u = 0; u < kTopkU; ++u) {
-                const int gvi = vn + u * kBlock + tid;
-                nxt[u] = gvi < gvend ? load16(row, gvi) : nanv;
-            }
-#pragma unroll
-            for (int u = 0; u < kTopkU; ++u) {
-                float f[EV];
-                E::unpack(cur[u], f);
-                wave_offer<EV>(f, v0 + u * kBlock + tid, wb, st, topk);
-            }
-#pragma unroll
-            for (int u = 0; u < kTopkU; ++u) cur[u] = nxt[u];
-        }
-    } else {
-        for (int v0 = v_start; v0 < gvend; v0 += kBlock * kTopkU) {
-            float f[kTopkU][EV];
-#pragma unroll
-            for (int u = 0; u < kTopkU; ++u) topk_load_range<E, VEC>(row, end, gvend, v0 + u * kBlock + tid, f[u]);
-#pragma unroll
-            for (int u = 0; u < kTopkU; ++u) wave_offer<EV>(f[u], v0 + u * kBlock + tid, wb, st, topk);
-        }
-    }
-    st = wave_compact(wb, st, topk);         // each wave: its best min(cnt, topk), sorted
-    if (lane == 0) wcnt[w] = st.cnt;
     __syncthreads();
-    // 3. merge the waves' lists
-    int off = 0, total = 0;
+    int seen = 0;
+    for (int i = 0; i < kWavesPerBlock; ++i) seen += wseen[i];
+    // 3. exact unless fewer than topk tokens reached a guess above the bound
+    if (seen < topk && tg != -INFINITY && tg != ts) {
+        __syncthreads();
+        st = ts > 0.f ? row_pass<E, VEC, true, false>(row, V, gvend, ts, hs, qi_all[w], wbuf[w], topk)
+                      : row_pass<E, VEC, false, false>(row, V, gvend, ts, hs, qi_all[w], wbuf[w], topk);
+        if (lane == 0) wcnt[w] = st.cnt;
+        __syncthreads();
+    }
+    // 4. merge the waves' lists by rank
+    int total = 0;
+    float xmax = -INFINITY;
+    bool have = false;
     for (int i = 0; i < kWavesPerBlock; ++i) {
-        if (i < w) off += wcnt[i];
-        total += wcnt[i];
+        const int c = wcnt[i];
+        total += c;
+        if (c > 0) {
+            const float x0 = from_ordered((uint32_t)(wbuf[i][0] >> 32));
+            xmax = have ? fmaxf(xmax, x0) : x0;
+            have = true;
+        }
     }
-    unsigned long long* mb = mbuf;
-    for (int j = lane; j < st.cnt; j += kWave) mb[off + j] = wb[j];
-    const int np2 = pow2_at_least(total < 2 ? 2 : total);
-    for (int i = total + tid; i < np2; i += kBlock) mb[i] = 0ull;
-    __syncthreads();
-    bitonic_desc(mb, np2);
     const int kept = total < topk ? total : topk;
     TopEntry* L = lists + (int64_t)task * topk;
-    for (int i = tid; i < topk; i += kBlock) {
-        TopEntry te;
-        if (i < kept) {
-            const unsigned long long key = mb[i];
-            te.idx = (int32_t)(0xffffffffu - (uint32_t)(key & 0xffffffffull));
-            te.x = from_ordered((uint32_t)(key >> 32));
-        } else {
-            te.idx = -1;
-            te.x = -INFINITY;
-        }
-        L[i] = te;
-    }
-    if (tid == 0) counts[task] = kept;
-    if (rowtop == nullptr || w != 0) return;
-    // softmax statistics of the kept set and p(y) (wave 0, fp64)
-    int y = -1;                      // task = ((b * (K_max + 1) + s) * 2 + side)
-    {
+    const bool stats = rowtop != nullptr;
+    int y = -1;
+    if (stats) {                     // task = ((b * (K_max + 1) + s) * 2 + side)
         const int rest = task >> 1;
         const int s = rest % (K_max + 1);
         int d0, k;
@@ -412,22 +491,46 @@ __global__ __launch_bounds__(kBlock) void k_topk_rows(const typename E::raw* __r
         if (s < k) y = tok[d0 + s];
     }
     const double T = (double)temperature;
-    RowTop r;
-    r.count = kept;
-    r.m = kept > 0 ? (double)from_ordered((uint32_t)(mb[0] >> 32)) / T : 0.0;
+    const double mref = have ? (double)xmax / T : 0.0;
     double sum = 0.0, ey = 0.0;
-    for (int i = lane; i < kept; i += kWave) {
-        const unsigned long long key = mb[i];
-        const double e = exp((double)from_ordered((uint32_t)(key >> 32)) / T - r.m);
-        sum += e;
-        if ((int32_t)(0xffffffffu - (uint32_t)(key & 0xffffffffull)) == y) ey = e;
+    const int own = wcnt[w];
+    for (int i = lane; i < own; i += kWave) {
+        const unsigned long long key = wbuf[w][i];
+        int rank = i;
+#pragma unroll
+        for (int o2 = 0; o2 < kWavesPerBlock; ++o2)
+            if (o2 != w) rank += count_above(wbuf[o2], wcnt[o2], key);
+        if (rank < topk) {
+            TopEntry te;
+            te.idx = (int32_t)(0xffffffffu - (uint32_t)(key & 0xffffffffull));
+            te.x = from_ordered((uint32_t)(key >> 32));
+            L[rank] = te;
+            if (stats) {
+                const double e = exp((double)te.x / T - mref);
+                sum += e;
+                if (te.idx == y) ey = e;
+            }
+        }
     }
-    sum = wave_sum(sum);
-    ey = wave_sum(ey);               // at most one lane holds y
-    r.S = sum;
-    r.valid = (kept > 0 && isfinite(r.m) && isfinite(sum) && sum > 0.0) ? 1 : 0;
-    r.py = (r.valid && y >= 0 && y < V) ? ey / sum : 0.0;
-    if (lane == 0) rowtop[task] = r;
+    for (int i = kept + tid; i < topk; i += kBlock) {
+        TopEntry te;
+        te.idx = -1;
+        te.x = -INFINITY;
+        L[i] = te;
+    }
+    if (tid == 0) counts[task] = kept;
+    if (!stats) return;
+    sum = block_sum(sum, red);
+    ey = block_sum(ey, red);         // at most one thread holds y
+    if (tid == 0) {
+        RowTop r;
+        r.count = kept;
+        r.m = mref;
+        r.S = sum;
+        r.valid = (kept > 0 && isfinite(mref) && isfinite(sum) && sum > 0.0) ? 1 : 0;
+        r.py = (r.valid && y >= 0 && y < V) ? ey / sum : 0.0;
+        rowtop[task] = r;
+    }
 }
 
 // ---------------------------------------------------------------------------

@@ -199,6 +199,44 @@ def test_topk_ties_at_kth_value():
     _say(f"  ties: {info}")
 
 
+@pytest.mark.parametrize("layout", ["descending", "ascending", "front_heavy", "strided_top", "constant",
+                                    "few_finite"])
+def test_topk_structured_rows(layout):
+    # Rows whose largest values sit where a threshold guessed from the start of
+    # the row is too high (front-heavy, strided) or too low (ascending), or
+    # where every value ties or almost every logit is -inf.
+    _say(f"top-k structured rows: {layout}")
+    V, K, B, top_k = 40000, 2, 4, 50
+    R = B * (K + 1)
+    g = torch.Generator(device="cuda").manual_seed(11)
+    noise = torch.randn(R, V, generator=g, device="cuda")
+    ramp = torch.linspace(6.0, -6.0, V, device="cuda")
+    if layout == "descending":
+        tgt = ramp.expand(R, V) + 0.01 * noise
+    elif layout == "ascending":
+        tgt = ramp.flip(0).expand(R, V) + 0.01 * noise
+    elif layout == "front_heavy":
+        tgt = noise.clone()
+        tgt[:, :4000] += 8.0
+    elif layout == "strided_top":
+        # the row's 50 largest values one per 8-token vector at the row's
+        # start: a threshold guessed from the start's maxima is too high
+        tgt = noise.clone()
+        tgt[:, 0:400:8] += 20.0
+    elif layout == "constant":
+        tgt = torch.full((R, V), 1.5, device="cuda")
+    else:
+        tgt = torch.full((R, V), float("-inf"), device="cuda")
+        tgt[:, 100:130] = noise[:, 100:130]
+    tgt = tgt.contiguous().to(torch.bfloat16)
+    dft = tgt.view(B, K + 1, V)[:, :K].reshape(B * K, V).contiguous()
+    case = wl.ChainCase(B=B, K_max=K, V=V, temperature=1.0, top_k=top_k, target=tgt, draft=dft,
+                        tokens=wl.gumbel_draft_tokens(dft, 1.0, top_k, g),
+                        uniforms=wl.grid_uniforms((R,), g, "cuda"))
+    info = compare_chain(run_chain(case), oracle_chain(case))
+    _say(f"  {info}")
+
+
 def test_config3_topk_full_sampled():
     _say("config 3: B=256 K=5 V=151936 bf16 T=0.7 top-k 50 (sampled)")
     case = wl.gen_config3(device="cuda")
