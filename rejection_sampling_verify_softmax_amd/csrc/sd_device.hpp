@@ -65,6 +65,31 @@ __device__ __forceinline__ uint4 load16_cached(const void* base, int64_t vec_ind
     return reinterpret_cast<const uint4*>(base)[vec_index];
 }
 
+// Runs steps 0..nsteps-1 with the next step's loads in flight while the
+// current step is processed. Two buffers alternate by unrolling in pairs, so no
+// register copy joins the steps and each step waits only for its own loads.
+// load(buf, s) issues step s's loads into buf; proc(buf, s) consumes them.
+template <int U, class Load, class Proc>
+__device__ __forceinline__ void pipelined_steps(int nsteps, Load&& load, Proc&& proc) {
+    if (nsteps <= 0) return;
+    uint4 a[U], b[U];
+    load(a, 0);
+    int s = 0;
+    for (; s + 2 < nsteps; s += 2) {
+        load(b, s + 1);
+        proc(a, s);
+        load(a, s + 2);
+        proc(b, s + 1);
+    }
+    if (s + 1 < nsteps) {
+        load(b, s + 1);
+        proc(a, s);
+        proc(b, s + 1);
+    } else {
+        proc(a, s);
+    }
+}
+
 // 2^x on the hardware transcendental unit (v_exp_f32).
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 

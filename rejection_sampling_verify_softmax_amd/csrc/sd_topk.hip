@@ -71,9 +71,8 @@ __device__ const typename E::raw* topk_row(const typename E::raw* tgt, const typ
 constexpr int kTopkSample = 8;           // vectors per thread held in registers for the threshold
 constexpr int kTopkU = 4;                // vectors per thread per main-pass step (as many more in flight)
 constexpr int kWaveCap = 512;            // per-wave candidate buffer (64-bit keys)
-constexpr int kQueue = 4 * kWave;        // per-wave queue of vector indices that may hold a candidate
+constexpr int kQueue = kTopkSample * kWave;   // per-wave queue of vector indices that may hold a candidate
 static_assert(kQueue >= kWave * kTopkU, "one offer step must fit an empty queue");
-static_assert(kTopkSample % kTopkU == 0, "the sample is offered in steps of kTopkU vectors");
 
 // 16-byte vector `gvi` of a row as raw element bits; elements past the row
 // (or past gvend) read as an all-ones NaN, which no test keeps.
@@ -266,7 +265,7 @@ __device__ __forceinline__ void wave_drain(Offer& o, const typename E::raw* row,
 // hold a candidate are queued (their indices), after draining the queue if it
 // could overflow. POS: the threshold is positive, so the integer pre-check on
 // the raw bits applies.
-template <class E, bool VEC, bool POS, int N>
+template <class E, bool VEC, bool POS, int N, bool DRAIN = true>
 __device__ __forceinline__ void offer_vecs(Offer& o, const uint4 (&v)[N], int vi0,
                                            const typename E::raw* row, int V, int gvend, int topk) {
     bool may[N];
@@ -279,7 +278,7 @@ __device__ __forceinline__ void offer_vecs(Offer& o, const uint4 (&v)[N], int vi
         n += __popcll(bal[u]);
     }
     if (n == 0) return;
-    if (o.qn + n > kQueue) wave_drain<E, VEC>(o, row, V, gvend, topk);
+    if (DRAIN && o.qn + n > kQueue) wave_drain<E, VEC>(o, row, V, gvend, topk);
 #pragma unroll
     for (int u = 0; u < N; ++u) {
         if (may[u]) {
@@ -292,21 +291,29 @@ __device__ __forceinline__ void offer_vecs(Offer& o, const uint4 (&v)[N], int vi
 }
 
 // Streams vectors [v_start, gvend) of the row through offer_vecs, kTopkU
-// vectors per thread per step with the next step's loads in flight.
+// vectors per thread per step with the next step's loads in flight. Whole
+// steps load without bounds checks; one checked step takes the ragged end.
 template <class E, bool VEC, bool POS>
 __device__ __forceinline__ void offer_range(Offer& o, const typename E::raw* row, int V, int gvend,
                                             int v_start, int topk) {
+    constexpr int kStep = kBlock * kTopkU;
     const int tid = threadIdx.x;
-    uint4 cur[kTopkU], nxt[kTopkU];
+    const int nsteps = VEC ? (gvend - v_start) / kStep : 0;
+    const int full_end = v_start + nsteps * kStep;
+    pipelined_steps<kTopkU>(
+        nsteps,
+        [&](uint4 (&buf)[kTopkU], int st) {
 #pragma unroll
-    for (int u = 0; u < kTopkU; ++u) cur[u] = topk_raw<E, VEC>(row, V, gvend, v_start + u * kBlock + tid);
-    for (int v0 = v_start; v0 < gvend; v0 += kBlock * kTopkU) {
-        const int vn = v0 + kBlock * kTopkU;
+            for (int u = 0; u < kTopkU; ++u) buf[u] = load16(row, v_start + st * kStep + u * kBlock + tid);
+        },
+        [&](const uint4 (&buf)[kTopkU], int st) {
+            offer_vecs<E, VEC, POS, kTopkU>(o, buf, v_start + st * kStep + tid, row, V, gvend, topk);
+        });
+    for (int v0 = full_end; v0 < gvend; v0 += kStep) {
+        uint4 cur[kTopkU];
 #pragma unroll
-        for (int u = 0; u < kTopkU; ++u) nxt[u] = topk_raw<E, VEC>(row, V, gvend, vn + u * kBlock + tid);
+        for (int u = 0; u < kTopkU; ++u) cur[u] = topk_raw<E, VEC>(row, V, gvend, v0 + u * kBlock + tid);
         offer_vecs<E, VEC, POS, kTopkU>(o, cur, v0 + tid, row, V, gvend, topk);
-#pragma unroll
-        for (int u = 0; u < kTopkU; ++u) cur[u] = nxt[u];
     }
     if (o.qn > 0) wave_drain<E, VEC>(o, row, V, gvend, topk);
 }
@@ -329,10 +336,8 @@ __device__ __forceinline__ WaveTop row_pass(const typename E::raw* row, int V, i
     o.wb = wb;
     int v_start = 0;
     if (SAMPLE) {
-#pragma unroll
-        for (int g = 0; g < kTopkSample; g += kTopkU)
-            offer_vecs<E, VEC, POS, kTopkU>(o, *reinterpret_cast<const uint4(*)[kTopkU]>(&hs[g]),
-                                            g * kBlock + threadIdx.x, row, V, gvend, topk);
+        // the whole sample fits the empty queue: no drain while it is held
+        offer_vecs<E, VEC, POS, kTopkSample, false>(o, hs, threadIdx.x, row, V, gvend, topk);
         v_start = kTopkSample * kBlock;
     }
     offer_range<E, VEC, POS>(o, row, V, gvend, v_start, topk);
@@ -389,7 +394,7 @@ __device__ __forceinline__ int guess_rank(int topk, int sampled, int V) {
 //  4. The waves' sorted lists are merged by rank (binary search in the other
 //     lists) and the first topk written.
 template <class E, bool VEC>
-__global__ __launch_bounds__(kBlock) void k_topk_rows(const typename E::raw* __restrict__ tgt,
+__global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(4))) void k_topk_rows(const typename E::raw* __restrict__ tgt,
                                                       const typename E::raw* __restrict__ dft,
                                                       const int32_t* __restrict__ cu, int K_max,
                                                       int V, int topk, int chain,
@@ -414,22 +419,28 @@ __global__ __launch_bounds__(kBlock) void k_topk_rows(const typename E::raw* __r
     const int gvend = (V + EV - 1) / EV;
     // 1. thresholds from the held sample
     uint4 hs[kTopkSample];
+    if (VEC && kTopkSample * kBlock <= gvend) {      // the usual case: no bounds checks
 #pragma unroll
-    for (int i = 0; i < kTopkSample; ++i) hs[i] = topk_raw<E, VEC>(row, V, gvend, i * kBlock + tid);
-    float m = -INFINITY;
-    bool any = false;
+        for (int i = 0; i < kTopkSample; ++i) hs[i] = load16(row, i * kBlock + tid);
+    } else {
+#pragma unroll
+        for (int i = 0; i < kTopkSample; ++i) hs[i] = topk_raw<E, VEC>(row, V, gvend, i * kBlock + tid);
+    }
+    float m = NAN;                   // fmaxf skips NaN; stays NaN only if all are
 #pragma unroll
     for (int i = 0; i < kTopkSample; ++i) {
         float f[EV];
         E::unpack(hs[i], f);
 #pragma unroll
-        for (int e = 0; e < EV; ++e)
-            if (f[e] == f[e]) {
-                m = any ? fmaxf(m, f[e]) : f[e];
-                any = true;
-            }
+        for (int e = 0; e < EV; ++e) m = fmaxf(m, f[e]);
     }
-    lmax[tid] = any ? m : NAN;
+    // Opaque to the optimiser: the unpacked sample is not kept alive (in
+    // registers) until the sample is offered.
+#pragma unroll
+    for (int i = 0; i < kTopkSample; ++i)
+        asm volatile("" : "+v"(hs[i].x), "+v"(hs[i].y), "+v"(hs[i].z), "+v"(hs[i].w));
+    const bool any = m == m;
+    lmax[tid] = m;
     if (tid == 0) {
         t_guess = -INFINITY;
         t_safe = -INFINITY;
@@ -438,6 +449,7 @@ __global__ __launch_bounds__(kBlock) void k_topk_rows(const typename E::raw* __r
     const int jg = guess_rank(topk, min(V, kTopkSample * kBlock * EV), V);
     if (any) {
         int rank = 0;
+#pragma unroll 8
         for (int j = 0; j < kBlock; ++j) {
             const float x = lmax[j];
             rank += (x > m) || (x == m && j < tid);
