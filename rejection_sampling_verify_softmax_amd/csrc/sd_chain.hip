@@ -29,9 +29,6 @@
 #ifndef SD_STATS_UNROLL
 #define SD_STATS_UNROLL 4
 #endif
-#ifndef SD_STATS_PIPE
-#define SD_STATS_PIPE 1
-#endif
 
 namespace sd {
 
@@ -125,14 +122,14 @@ __device__ Partial chunk_stats_exact(const typename E::raw* row, int beg, int en
 }
 
 template <class E, int NR>
-__device__ __forceinline__ void accumulate(const uint4 (&v)[NR][kU], const float (&o)[NR], float c,
+__device__ __forceinline__ void accumulate(const uint4 (&v)[NR * kU], const float (&o)[NR], float c,
                                            float (&acc)[NR][E::kVec]) {
 #pragma unroll
     for (int u = 0; u < kU; ++u)
 #pragma unroll
         for (int r = 0; r < NR; ++r) {
             float f[E::kVec];
-            E::unpack(v[r][u], f);
+            E::unpack(v[r * kU + u], f);
 #pragma unroll
             for (int e = 0; e < E::kVec; ++e) acc[r][e] += fast_exp2(__builtin_fmaf(f[e], c, -o[r]));
         }
@@ -170,42 +167,16 @@ __device__ void chunk_stats(const typename E::raw* const (&rows)[NR], int beg, i
         const typename E::raw* base[NR];
 #pragma unroll
         for (int r = 0; r < NR; ++r) base[r] = rows[r] + beg;
-        if (full > 0) {
-            uint4 cur[NR][kU];
+        pipelined_steps<NR * kU>(
+            full,
+            [&](uint4 (&buf)[NR * kU], int rd) {
 #pragma unroll
-            for (int u = 0; u < kU; ++u)
+                for (int u = 0; u < kU; ++u)
 #pragma unroll
-                for (int r = 0; r < NR; ++r) cur[r][u] = load16(base[r], u * kBlock + threadIdx.x);
-            for (int rd = 0; rd < full; ++rd) {
-#if SD_STATS_PIPE
-                uint4 nxt[NR][kU];
-                const bool more = rd + 1 < full;
-                if (more) {
-#pragma unroll
-                    for (int u = 0; u < kU; ++u)
-#pragma unroll
-                        for (int r = 0; r < NR; ++r)
-                            nxt[r][u] = load16(base[r], (rd + 1) * step + u * kBlock + threadIdx.x);
-                }
-                accumulate<E, NR>(cur, o, c, acc);
-                if (more) {
-#pragma unroll
-                    for (int u = 0; u < kU; ++u)
-#pragma unroll
-                        for (int r = 0; r < NR; ++r) cur[r][u] = nxt[r][u];
-                }
-#else
-                accumulate<E, NR>(cur, o, c, acc);
-                if (rd + 1 < full) {
-#pragma unroll
-                    for (int u = 0; u < kU; ++u)
-#pragma unroll
-                        for (int r = 0; r < NR; ++r)
-                            cur[r][u] = load16(base[r], (rd + 1) * step + u * kBlock + threadIdx.x);
-                }
-#endif
-            }
-        }
+                    for (int r = 0; r < NR; ++r)
+                        buf[r * kU + u] = load16(base[r], rd * step + u * kBlock + threadIdx.x);
+            },
+            [&](const uint4 (&buf)[NR * kU], int) { accumulate<E, NR>(buf, o, c, acc); });
         vdone = full * step;
     }
     // ragged tail (the whole range in the element-wise path)

@@ -679,31 +679,39 @@ __global__ __launch_bounds__(kBlock) void k_chain_topk_decide(
 }
 
 // ---------------------------------------------------------------------------
-// DDTree best-first build: one wave per sequence. The frontier (at most 64
-// prefixes, one per lane) holds, for every popped node, its first child and
-// its next sibling; a pop is a wave argmax under (Q desc, depth asc, rank tuple
-// lexicographically asc). The rank tuple is packed 6 bits per depth, big-end
-// first, in two 64-bit words, so equal-depth tuples compare as integers.
+// DDTree best-first build: one wave per sequence. The frontier holds, for the
+// nodes popped so far, the first child and the next sibling not yet taken,
+// kept sorted best first under (Q desc, depth asc, rank tuple lexicographically
+// asc), one prefix per lane (lane 0 the best). A pop reads lane 0; its child
+// and its sibling are placed by two wave ballots (how many frontier entries
+// beat each), and one lane permutation removes the head and opens their
+// slots. The rank tuple is packed 6 bits per depth, big end first, in two
+// 64-bit words, so equal-depth tuples compare as integers. The frontier never
+// needs more than 64 entries: after n pops it holds at most n + 1.
 // ---------------------------------------------------------------------------
-struct Front {
+struct Prefix {
     float Q;
-    int depth;
-    unsigned long long w0, w1;
-    int parent;
-    int rank;        // rank at the last depth
-    int valid;
+    int meta;                   // depth | parent << 5 | rank << 11 (rank at the last depth)
+    unsigned long long w0, w1;  // rank tuple
 };
 
-__device__ __forceinline__ bool front_better(const Front& a, const Front& b) {
-    if (!a.valid) return false;
-    if (!b.valid) return true;
+__device__ __forceinline__ int meta_depth(int m) { return m & 31; }
+__device__ __forceinline__ int meta_parent(int m) { return (m >> 5) & 63; }
+__device__ __forceinline__ int meta_rank(int m) { return (m >> 11) & 63; }
+__device__ __forceinline__ int make_meta(int depth, int parent, int rank) {
+    return depth | (parent << 5) | (rank << 11);
+}
+
+// a before b in the pop order (distinct prefixes never compare equal)
+__device__ __forceinline__ bool prefix_before(const Prefix& a, const Prefix& b) {
     if (a.Q != b.Q) return a.Q > b.Q;
-    if (a.depth != b.depth) return a.depth < b.depth;
+    const int da = meta_depth(a.meta), db = meta_depth(b.meta);
+    if (da != db) return da < db;
     if (a.w0 != b.w0) return a.w0 < b.w0;
     return a.w1 < b.w1;
 }
 
-__device__ __forceinline__ void set_rank(Front& f, int pos, int r) {
+__device__ __forceinline__ void set_rank(Prefix& f, int pos, int r) {
     if (pos < 10) {
         const int sh = 54 - 6 * pos;
         f.w0 = (f.w0 & ~(0x3full << sh)) | ((unsigned long long)r << sh);
@@ -713,15 +721,18 @@ __device__ __forceinline__ void set_rank(Front& f, int pos, int r) {
     }
 }
 
-__device__ Front shfl_front(const Front& f, int src) {
-    Front r;
+__device__ __forceinline__ unsigned long long readlane64(unsigned long long v, int l) {
+    const uint32_t lo = __builtin_amdgcn_readlane((uint32_t)v, l);
+    const uint32_t hi = __builtin_amdgcn_readlane((uint32_t)(v >> 32), l);
+    return ((unsigned long long)hi << 32) | lo;
+}
+
+__device__ __forceinline__ Prefix lane_prefix(const Prefix& f, int src) {
+    Prefix r;
     r.Q = __shfl(f.Q, src, kWave);
-    r.depth = __shfl(f.depth, src, kWave);
+    r.meta = __shfl(f.meta, src, kWave);
     r.w0 = __shfl(f.w0, src, kWave);
     r.w1 = __shfl(f.w1, src, kWave);
-    r.parent = __shfl(f.parent, src, kWave);
-    r.rank = __shfl(f.rank, src, kWave);
-    r.valid = __shfl(f.valid, src, kWave);
     return r;
 }
 
@@ -735,6 +746,7 @@ __global__ __launch_bounds__(kWave) void k_tree_build(
     __shared__ int cntv[kMaxTreeK];
     __shared__ float nscore[64];
     __shared__ unsigned long long nanc[64];
+    __shared__ int otok[64], opar[64], odep[64];
     const int b = blockIdx.x;
     const int lane = threadIdx.x;
     for (int d = 0; d < K; ++d) {
@@ -745,89 +757,69 @@ __global__ __launch_bounds__(kWave) void k_tree_build(
         }
         if (lane == 0) cntv[d] = counts[(int64_t)b * K + d];
     }
-    __shared__ int otok[64], opar[64], odep[64];
-    if (lane < 64) {
-        otok[lane] = -1;
-        opar[lane] = -1;
-        odep[lane] = 0;
-        nscore[lane] = 0.f;
-        nanc[lane] = 0ull;
-    }
+    otok[lane] = -1;
+    opar[lane] = -1;
+    odep[lane] = 0;
+    nscore[lane] = lane == 0 ? 1.0f : 0.f;
+    nanc[lane] = lane == 0 ? 1ull : 0ull;
     __syncthreads();
-    if (lane == 0) {
-        nscore[0] = 1.0f;
-        nanc[0] = 1ull;
-    }
-    Front f;
-    f.valid = 0;
+    Prefix f;                        // this lane's frontier entry (valid below cnt)
     f.Q = 0.f;
-    f.depth = 0;
+    f.meta = 0;
     f.w0 = 0ull;
     f.w1 = 0ull;
-    f.parent = -1;
-    f.rank = 0;
-    if (lane == 0 && K > 0 && cntv[0] > 0) {
-        f.valid = 1;
-        f.Q = 1.0f * qv[0][0];
-        f.depth = 1;
-        f.parent = 0;
-        f.rank = 0;
-    }
-    __syncthreads();
-    int n = 1;
-    while (n < N) {
-        // wave argmax
-        Front best = f;
-        int best_lane = lane;
-#pragma unroll
-        for (int o = kWave / 2; o > 0; o >>= 1) {
-            const Front other = shfl_front(best, lane ^ o);
-            const int ol = __shfl_xor(best_lane, o, kWave);
-            if (front_better(other, best)) {
-                best = other;
-                best_lane = ol;
-            }
-        }
-        // every lane now holds the same winner
-        if (!best.valid) break;
-        const int m = best.depth;
-        const int tokn = tv[m - 1][best.rank];
-        const int par = best.parent;
-        const unsigned long long anc = nanc[par] | (1ull << n);
+    int cnt = 0;
+    if (K > 0 && cntv[0] > 0) {
         if (lane == 0) {
-            otok[n] = tokn;
+            f.Q = 1.0f * qv[0][0];
+            f.meta = make_meta(1, 0, 0);
+        }
+        cnt = 1;
+    }
+    int n = 1;
+    for (; n < N && cnt > 0; ++n) {
+        Prefix X;                    // the head: node n
+        X.Q = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(uint32_t, f.Q), 0));
+        X.meta = __builtin_amdgcn_readlane(f.meta, 0);
+        X.w0 = readlane64(f.w0, 0);
+        X.w1 = readlane64(f.w1, 0);
+        const int m = meta_depth(X.meta), par = meta_parent(X.meta), rk = meta_rank(X.meta);
+        if (lane == 0) {
+            otok[n] = tv[m - 1][rk];
             opar[n] = par;
             odep[n] = m;
-            nscore[n] = best.Q;
-            nanc[n] = anc;
+            nscore[n] = X.Q;
+            nanc[n] = nanc[par] | (1ull << n);
         }
-        __syncthreads();
-        // the winner's slot becomes the first child of node n
-        if (lane == best_lane) {
-            if (m < K && cntv[m] > 0) {
-                f.Q = best.Q * qv[m][0];
-                f.depth = m + 1;
-                set_rank(f, m, 0);
-                f.parent = n;
-                f.rank = 0;
-                f.valid = 1;
-            } else {
-                f.valid = 0;
-            }
+        // its first child and its next sibling
+        const bool hasC = m < K && cntv[m] > 0;
+        const bool hasS = rk + 1 < cntv[m - 1];
+        Prefix C = X, S = X;
+        if (hasC) {
+            C.Q = X.Q * qv[m][0];
+            C.meta = make_meta(m + 1, n, 0);     // rank 0 at depth m: its tuple slot is already 0
         }
-        // the next sibling goes to the lowest free lane
-        if (best.rank + 1 < cntv[m - 1]) {
-            const unsigned long long freem = __ballot(!f.valid);
-            const int dst = __ffsll(freem) - 1;
-            if (lane == dst) {
-                f = best;
-                f.Q = nscore[par] * qv[m - 1][best.rank + 1];
-                set_rank(f, m - 1, best.rank + 1);
-                f.rank = best.rank + 1;
-                f.valid = 1;
-            }
+        if (hasS) {
+            S.Q = nscore[par] * qv[m - 1][rk + 1];
+            S.meta = make_meta(m, par, rk + 1);
+            set_rank(S, m - 1, rk + 1);
         }
-        ++n;
+        // places among the rest of the frontier (lanes 1 .. cnt-1)
+        const bool rest = lane >= 1 && lane < cnt;
+        const int pc = hasC ? __popcll(__ballot(rest && prefix_before(f, C))) : 0;
+        const int ps = hasS ? __popcll(__ballot(rest && prefix_before(f, S))) : 0;
+        const bool s_first = hasC && hasS && prefix_before(S, C);
+        const int fC = hasC ? pc + (s_first ? 1 : 0) : -1;
+        const int fS = hasS ? ps + ((hasC && !s_first) ? 1 : 0) : -1;
+        const int i = lane - ((fC >= 0 && fC < lane) ? 1 : 0) - ((fS >= 0 && fS < lane) ? 1 : 0);
+        const Prefix g = lane_prefix(f, min(max(i + 1, 0), kWave - 1));
+        const bool tc = lane == fC, ts = lane == fS;
+        f.Q = tc ? C.Q : (ts ? S.Q : g.Q);
+        f.meta = tc ? C.meta : (ts ? S.meta : g.meta);
+        f.w0 = tc ? C.w0 : (ts ? S.w0 : g.w0);
+        f.w1 = tc ? C.w1 : (ts ? S.w1 : g.w1);
+        cnt = min(kWave, cnt - 1 + (hasC ? 1 : 0) + (hasS ? 1 : 0));
+        __syncthreads();             // node n's score and mask are read by later pops
     }
     __syncthreads();
     const int64_t o0 = (int64_t)b * N;
