@@ -351,24 +351,27 @@ __device__ void mass_pass(const typename E::raw* tp, const typename E::raw* dp, 
     const int rounds = (nvec + step - 1) / step;
     const typename E::raw* tb = tp + beg;
     const typename E::raw* db = dp + beg;
-    auto fetch = [&](int rd, uint4 (&vt)[kU], uint4 (&vd)[kU]) {
+    static_assert(kU == 4, "the piece reduction below sums four pieces at once");
+    // loads of one round: kU vectors of the target row, then kU of the draft row
+    auto fetch = [&](uint4 (&v)[2 * kU], int rd) {
 #pragma unroll
         for (int u = 0; u < kU; ++u) {
             const int vi = rd * step + u * T + threadIdx.x;
             if (VEC) {
                 const bool in = vi < nvec;
-                vt[u] = in ? load16(tb, vi) : E::neg_inf();
-                vd[u] = (in && wf.has_q) ? load16(db, vi) : E::neg_inf();
+                v[u] = in ? load16(tb, vi) : E::neg_inf();
+                v[kU + u] = (in && wf.has_q) ? load16(db, vi) : E::neg_inf();
             }
         }
     };
-    auto weigh = [&](int rd, const uint4 (&vt)[kU], const uint4 (&vd)[kU]) {
+    auto weigh = [&](const uint4 (&v)[2 * kU], int rd) {
+        double s[kU];
 #pragma unroll
         for (int u = 0; u < kU; ++u) {
             float fp[EV], fq[EV];
             if (VEC) {
-                E::unpack(vt[u], fp);
-                E::unpack(vd[u], fq);
+                E::unpack(v[u], fp);
+                E::unpack(v[kU + u], fq);
             } else {
                 const int vi = rd * step + u * T + threadIdx.x;
 #pragma unroll
@@ -378,26 +381,25 @@ __device__ void mass_pass(const typename E::raw* tp, const typename E::raw* dp, 
                     fq[e] = (vi < nvec && j < end && wf.has_q) ? E::at(dp, j) : -INFINITY;
                 }
             }
-            const double sb = wave_sum((double)lane_weight_sum<E>(fp, fq, wf));
-            const int piece = p0 + (rd * kU + u) * kResolveWaves + w;
-            if (lane == 0 && piece < npieces) pieces[piece] = sb;
+            s[u] = (double)lane_weight_sum<E>(fp, fq, wf);
         }
-    };
-    uint4 cur_t[kU], cur_d[kU];
-    fetch(0, cur_t, cur_d);
-    for (int rd = 0; rd < rounds; ++rd) {
-        uint4 nxt_t[kU], nxt_d[kU];
-        const bool more = rd + 1 < rounds;
-        if (more) fetch(rd + 1, nxt_t, nxt_d);
-        weigh(rd, cur_t, cur_d);
-        if (more) {
+        // Four wave sums at once (reduce-scatter): halves of the wave trade
+        // two of the sums, quarters one, then a 16-lane butterfly; lane
+        // 16 * i ends with the sum of piece i of this round.
+        const bool h32 = (lane & 32) != 0, h16 = (lane & 16) != 0;
+        const double r0 = __shfl_xor(h32 ? s[0] : s[2], 32, kWave);
+        const double r1 = __shfl_xor(h32 ? s[1] : s[3], 32, kWave);
+        const double a0 = (h32 ? s[2] : s[0]) + r0;
+        const double a1 = (h32 ? s[3] : s[1]) + r1;
+        const double r2 = __shfl_xor(h16 ? a0 : a1, 16, kWave);
+        double t = (h16 ? a1 : a0) + r2;
 #pragma unroll
-            for (int u = 0; u < kU; ++u) {
-                cur_t[u] = nxt_t[u];
-                cur_d[u] = nxt_d[u];
-            }
-        }
-    }
+        for (int o = 8; o > 0; o >>= 1) t += __shfl_xor(t, o, kWave);
+        const int u = (h32 ? 2 : 0) + (h16 ? 1 : 0);
+        const int piece = p0 + (rd * kU + u) * kResolveWaves + w;
+        if ((lane & 15) == 0 && piece < npieces) pieces[piece] = t;
+    };
+    pipelined_steps<2 * kU>(rounds, fetch, weigh);
 }
 
 // Scans one piece (64 lanes x one 16-byte vector, tokens e0 ..) from cumulative

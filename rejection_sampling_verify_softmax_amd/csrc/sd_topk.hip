@@ -727,13 +727,21 @@ __device__ __forceinline__ unsigned long long readlane64(unsigned long long v, i
     return ((unsigned long long)hi << 32) | lo;
 }
 
-__device__ __forceinline__ Prefix lane_prefix(const Prefix& f, int src) {
-    Prefix r;
-    r.Q = __shfl(f.Q, src, kWave);
-    r.meta = __shfl(f.meta, src, kWave);
-    r.w0 = __shfl(f.w0, src, kWave);
-    r.w1 = __shfl(f.w1, src, kWave);
-    return r;
+// DPP lane shifts of a 32-bit value across the whole wave: from the next lane
+// (lane 63 keeps its own) and from the previous lane (lane 0 keeps its own).
+__device__ __forceinline__ uint32_t from_next_lane(uint32_t v) {
+    return (uint32_t)__builtin_amdgcn_update_dpp((int)v, (int)v, 0x130, 0xf, 0xf, false);   // wave_shl:1
+}
+__device__ __forceinline__ uint32_t from_prev_lane(uint32_t v) {
+    return (uint32_t)__builtin_amdgcn_update_dpp((int)v, (int)v, 0x138, 0xf, 0xf, false);   // wave_shr:1
+}
+// v from lane+1 (nb == 0), this lane (nb == 1) or lane-1 (nb == 2)
+__device__ __forceinline__ uint32_t shift_pick(uint32_t v, int nb) {
+    const uint32_t up = from_next_lane(v), down = from_prev_lane(v);
+    return nb == 0 ? up : (nb == 1 ? v : down);
+}
+__device__ __forceinline__ unsigned long long shift_pick64(unsigned long long v, int nb) {
+    return ((unsigned long long)shift_pick((uint32_t)(v >> 32), nb) << 32) | shift_pick((uint32_t)v, nb);
 }
 
 __global__ __launch_bounds__(kWave) void k_tree_build(
@@ -743,35 +751,36 @@ __global__ __launch_bounds__(kWave) void k_tree_build(
     unsigned long long* __restrict__ node_anc, int32_t* __restrict__ n_nodes) {
     __shared__ float qv[kMaxTreeK][64];
     __shared__ int tv[kMaxTreeK][64];
-    __shared__ int cntv[kMaxTreeK];
-    __shared__ float nscore[64];
-    __shared__ unsigned long long nanc[64];
-    __shared__ int otok[64], opar[64], odep[64];
     const int b = blockIdx.x;
     const int lane = threadIdx.x;
-    for (int d = 0; d < K; ++d) {
-        const TopEntry* L = lists + ((int64_t)b * K + d) * W;
-        if (lane < W) {
-            qv[d][lane] = L[lane].x;
-            tv[d][lane] = L[lane].idx;
+    // all loads first (one memory latency), then the LDS copies
+    TopEntry e[kMaxTreeK];
+#pragma unroll
+    for (int d = 0; d < kMaxTreeK; ++d)
+        if (d < K && lane < W) e[d] = lists[((int64_t)b * K + d) * W + lane];
+    // lane d: the depth-d list's length and best probability (read by readlane)
+    const int cnt_d = lane < K ? counts[(int64_t)b * K + lane] : 0;
+#pragma unroll
+    for (int d = 0; d < kMaxTreeK; ++d)
+        if (d < K && lane < W) {
+            qv[d][lane] = e[d].x;
+            tv[d][lane] = e[d].idx;
         }
-        if (lane == 0) cntv[d] = counts[(int64_t)b * K + d];
-    }
-    otok[lane] = -1;
-    opar[lane] = -1;
-    odep[lane] = 0;
-    nscore[lane] = lane == 0 ? 1.0f : 0.f;
-    nanc[lane] = lane == 0 ? 1ull : 0ull;
     __syncthreads();
+    const float q0_d = lane < K ? qv[lane][0] : 0.f;
+    // lane n: node n's outputs (node 0 is the root)
+    int my_tok = -1, my_par = -1, my_dep = 0;
+    float my_score = lane == 0 ? 1.0f : 0.f;
+    unsigned long long my_anc = lane == 0 ? 1ull : 0ull;
     Prefix f;                        // this lane's frontier entry (valid below cnt)
     f.Q = 0.f;
     f.meta = 0;
     f.w0 = 0ull;
     f.w1 = 0ull;
     int cnt = 0;
-    if (K > 0 && cntv[0] > 0) {
+    if (K > 0 && __builtin_amdgcn_readlane(cnt_d, 0) > 0) {
         if (lane == 0) {
-            f.Q = 1.0f * qv[0][0];
+            f.Q = 1.0f * q0_d;
             f.meta = make_meta(1, 0, 0);
         }
         cnt = 1;
@@ -779,28 +788,33 @@ __global__ __launch_bounds__(kWave) void k_tree_build(
     int n = 1;
     for (; n < N && cnt > 0; ++n) {
         Prefix X;                    // the head: node n
-        X.Q = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(uint32_t, f.Q), 0));
+        X.Q = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, f.Q), 0));
         X.meta = __builtin_amdgcn_readlane(f.meta, 0);
         X.w0 = readlane64(f.w0, 0);
         X.w1 = readlane64(f.w1, 0);
         const int m = meta_depth(X.meta), par = meta_parent(X.meta), rk = meta_rank(X.meta);
-        if (lane == 0) {
-            otok[n] = tv[m - 1][rk];
-            opar[n] = par;
-            odep[n] = m;
-            nscore[n] = X.Q;
-            nanc[n] = nanc[par] | (1ull << n);
+        const unsigned long long anc = readlane64(my_anc, par) | (1ull << n);
+        const float par_score = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, my_score), par));
+        const int cnt_sib = __builtin_amdgcn_readlane(cnt_d, m - 1);
+        const bool hasS = rk + 1 < cnt_sib;
+        const float q_sib = hasS ? qv[m - 1][rk + 1] : 0.f;
+        const bool hasC = m < K && __builtin_amdgcn_readlane(cnt_d, m < K ? m : 0) > 0;
+        const float q_child = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, q0_d), m < K ? m : 0));
+        if (lane == n) {
+            my_tok = tv[m - 1][rk];
+            my_par = par;
+            my_dep = m;
+            my_score = X.Q;
+            my_anc = anc;
         }
         // its first child and its next sibling
-        const bool hasC = m < K && cntv[m] > 0;
-        const bool hasS = rk + 1 < cntv[m - 1];
         Prefix C = X, S = X;
         if (hasC) {
-            C.Q = X.Q * qv[m][0];
+            C.Q = X.Q * q_child;
             C.meta = make_meta(m + 1, n, 0);     // rank 0 at depth m: its tuple slot is already 0
         }
         if (hasS) {
-            S.Q = nscore[par] * qv[m - 1][rk + 1];
+            S.Q = par_score * q_sib;
             S.meta = make_meta(m, par, rk + 1);
             set_rank(S, m - 1, rk + 1);
         }
@@ -811,24 +825,26 @@ __global__ __launch_bounds__(kWave) void k_tree_build(
         const bool s_first = hasC && hasS && prefix_before(S, C);
         const int fC = hasC ? pc + (s_first ? 1 : 0) : -1;
         const int fS = hasS ? ps + ((hasC && !s_first) ? 1 : 0) : -1;
-        const int i = lane - ((fC >= 0 && fC < lane) ? 1 : 0) - ((fS >= 0 && fS < lane) ? 1 : 0);
-        const Prefix g = lane_prefix(f, min(max(i + 1, 0), kWave - 1));
+        // lane j takes C, S, or the entry that lands on j: from lane j+1 when
+        // neither was placed before j, lane j after one, lane j-1 after both
+        const int nb = ((fC >= 0 && fC < lane) ? 1 : 0) + ((fS >= 0 && fS < lane) ? 1 : 0);
         const bool tc = lane == fC, ts = lane == fS;
-        f.Q = tc ? C.Q : (ts ? S.Q : g.Q);
-        f.meta = tc ? C.meta : (ts ? S.meta : g.meta);
-        f.w0 = tc ? C.w0 : (ts ? S.w0 : g.w0);
-        f.w1 = tc ? C.w1 : (ts ? S.w1 : g.w1);
+        const float gQ = __builtin_bit_cast(float, shift_pick(__builtin_bit_cast(uint32_t, f.Q), nb));
+        const int gm = (int)shift_pick((uint32_t)f.meta, nb);
+        const unsigned long long g0 = shift_pick64(f.w0, nb), g1 = shift_pick64(f.w1, nb);
+        f.Q = tc ? C.Q : (ts ? S.Q : gQ);
+        f.meta = tc ? C.meta : (ts ? S.meta : gm);
+        f.w0 = tc ? C.w0 : (ts ? S.w0 : g0);
+        f.w1 = tc ? C.w1 : (ts ? S.w1 : g1);
         cnt = min(kWave, cnt - 1 + (hasC ? 1 : 0) + (hasS ? 1 : 0));
-        __syncthreads();             // node n's score and mask are read by later pops
     }
-    __syncthreads();
     const int64_t o0 = (int64_t)b * N;
     if (lane < N) {
-        node_token[o0 + lane] = otok[lane];
-        node_parent[o0 + lane] = opar[lane];
-        node_depth[o0 + lane] = odep[lane];
-        node_score[o0 + lane] = nscore[lane];
-        node_anc[o0 + lane] = nanc[lane];
+        node_token[o0 + lane] = my_tok;
+        node_parent[o0 + lane] = my_par;
+        node_depth[o0 + lane] = my_dep;
+        node_score[o0 + lane] = my_score;
+        node_anc[o0 + lane] = my_anc;
     }
     if (lane == 0) n_nodes[b] = n;
 }
