@@ -142,6 +142,37 @@ sd_status_t sd_verify_chain(const void* target_logits, const void* draft_logits,
                             void* workspace, size_t workspace_bytes, void* hip_stream);
 
 /*
+ * Cap-accept chain verification [SD §9 DSpark: the ragged-verify mode that
+ * keeps the full verification work but limits the committed length]. The
+ * batch is padded (no cu: sequence b owns target rows b*(K_max+1) ..
+ * b*(K_max+1)+K_max, draft rows b*K_max .., uniforms indexed as the target
+ * rows); every position of the window is evaluated, as in the "static" mode
+ * (sd_verify_chain with cu_draft == NULL). The committed result is that of
+ * sd_verify_chain over the first kc = clamp(k_cap[b], 0, K_max) positions
+ * only (accept tests with uniforms 0..kc-1, the final token drawn with uniform
+ * kc from the residual at A or, when all kc pass, from target row kc), i.e.
+ * the tokens the compact mode commits with k_b = kc.
+ *
+ *   k_cap          [B] int32 (device)      committed-length cap per sequence
+ *   accepted_len   [B] int32 out           committed A (<= kc)
+ *   next_token     [B] int32 out           correction if A < kc, else extra token
+ *   accepted_full  [B] int32 out or NULL   first rejection over all K_max positions
+ *   probs_out      [B*K_max, 2] fp32 out or NULL  (p_i(y_i), q_i(y_i)), every position
+ *   resid_mass_out, seq_status: as sd_verify_chain, for the committed decision
+ * T == 0 gives the greedy rule with the same cap. Workspace as sd_verify_chain
+ * (SD_OP_CHAIN). Errors as sd_verify_chain; k_cap == NULL is SD_EINVAL.
+ */
+sd_status_t sd_verify_chain_capped(const void* target_logits, const void* draft_logits,
+                                   sd_dtype_t dtype, const int32_t* draft_tokens,
+                                   const float* uniforms, const int32_t* k_cap,
+                                   int32_t B, int32_t K_max, int32_t V,
+                                   float temperature, int32_t top_k,
+                                   int32_t* accepted_len, int32_t* next_token,
+                                   int32_t* accepted_full, float* probs_out,
+                                   float* resid_mass_out, int32_t* seq_status,
+                                   void* workspace, size_t workspace_bytes, void* hip_stream);
+
+/*
  * Greedy chain verification [SD §1: greedy results follow the target argmax].
  * g_i = lowest-id argmax of raw target row i (NaN ignored); position i is
  * accepted iff y_i == g_i; A = first mismatch (or k_b); next_token = g_A.
@@ -209,6 +240,24 @@ sd_status_t sd_verify_tree(const void* target_logits, sd_dtype_t dtype,
 sd_status_t sd_select_len(const float* conf, int32_t B, int32_t K_max, float cost_per_position,
                           int32_t* k_sel, float* expected_advance, int32_t* cu_sel,
                           void* hip_stream);
+
+/*
+ * DSpark verify length with a per-position cost table [SD §5 DSpark: is one
+ * more verified position worth what it costs]. cost_table[j-1] is the cost of
+ * verifying position j (in tokens of advance, e.g. a measured per-position
+ * time over the time of one decoding round). k_sel[b] = the smallest k in
+ * [0, K_max] maximising f(k) = 1 + sum_{j<=k} s_j - sum_{j<=k} cost_table[j-1],
+ * the two sums running in fp64 in position order over the fp32 s_j and costs
+ * (a constant table gives sd_select_len's k for c in [0, 1]). Outputs as
+ * sd_select_len.
+ *
+ *   conf [B, K_max] fp32 in [0, 1]; cost_table [K_max] fp32 (device), finite
+ *   (a NaN or +inf cost makes every length that includes it lose; -inf wins)
+ * Needs no workspace. conf or cost_table NULL with K_max > 0 is SD_EINVAL.
+ */
+sd_status_t sd_select_len_table(const float* conf, int32_t B, int32_t K_max,
+                                const float* cost_table, int32_t* k_sel,
+                                float* expected_advance, int32_t* cu_sel, void* hip_stream);
 
 /*
  * Measurement support. The next sd_verify_chain, sd_verify_greedy,

@@ -62,6 +62,10 @@ def _load():
     lib.orc_verify_tree.restype = None
     lib.orc_select_len.argtypes = [P, I, I, ctypes.c_float, P, P, P, P]
     lib.orc_select_len.restype = None
+    lib.orc_verify_chain_capped.argtypes = [P, P, P, P, P, I, I, I, D, I, D, P, P, P, P, P, P, P, I]
+    lib.orc_verify_chain_capped.restype = None
+    lib.orc_select_len_table.argtypes = [P, I, I, P, P, P, P, P]
+    lib.orc_select_len_table.restype = None
     _lib = lib
     return lib
 
@@ -175,4 +179,46 @@ def select_len(conf, B, K, cost):
     mg = np.zeros(B, np.int32)
     _load().orc_select_len(_ptr(c), int(B), int(K), ctypes.c_float(cost), _ptr(k), _ptr(adv),
                            _ptr(cu), _ptr(mg))
+    return {"k": k, "adv": adv, "cu": cu, "margin": mg}
+
+
+def verify_chain_capped(target, draft, tokens, uniforms, cap, B, K, V, temperature, top_k=0,
+                        margin_rel=MARGIN_REL, threads=None):
+    """Cap-accept verification over a padded window (B sequences x K positions).
+
+    Returns A (committed, <= cap), next, A_full (first rejection over the whole
+    window), probs ([B*K, 2]), R, status, margin.
+    """
+    t = _f32(target).reshape(-1)
+    d = _f32(draft).reshape(-1)
+    y = _i32(tokens).reshape(-1)
+    u = _f32(uniforms).reshape(-1)
+    c = _i32(cap)
+    A = np.zeros(B, np.int32)
+    nxt = np.zeros(B, np.int32)
+    Af = np.zeros(B, np.int32)
+    probs = np.zeros((max(B * K, 1), 2), np.float64)
+    R = np.zeros(B, np.float64)
+    st = np.zeros(B, np.int32)
+    mg = np.zeros(B, np.int32)
+    _load().orc_verify_chain_capped(_ptr(t), _ptr(d), _ptr(y), _ptr(u), _ptr(c), int(B), int(K),
+                                    int(V), _t32(temperature), int(top_k), float(margin_rel),
+                                    _ptr(A), _ptr(nxt), _ptr(Af), _ptr(probs), _ptr(R), _ptr(st),
+                                    _ptr(mg), int(threads or default_threads()))
+    return {"A": A, "next": nxt, "A_full": Af, "probs": probs[:B * K], "R": R, "status": st,
+            "margin": mg}
+
+
+def select_len_table(conf, B, K, cost_table):
+    """Verify length with a per-position cost table (cost_table[j-1] for position j)."""
+    assert K <= 64
+    c = _f32(conf).reshape(-1)
+    tab = _f32(cost_table).reshape(-1)
+    assert tab.shape[0] >= K
+    k = np.zeros(B, np.int32)
+    adv = np.zeros(B, np.float64)
+    cu = np.zeros(B + 1, np.int32)
+    mg = np.zeros(B, np.int32)
+    _load().orc_select_len_table(_ptr(c), int(B), int(K), _ptr(tab), _ptr(k), _ptr(adv), _ptr(cu),
+                                 _ptr(mg))
     return {"k": k, "adv": adv, "cu": cu, "margin": mg}

@@ -282,6 +282,43 @@ void orc_verify_chain(const float* target, const float* draft, const int32_t* to
 }
 
 /*
+ * Cap-accept verification [SD §9 DSpark: the full window is verified, the
+ * committed length is limited]. Padded layout (sequence b: target rows
+ * b*(K+1) .. b*(K+1)+K, draft rows b*K .., uniforms as the target rows). The
+ * committed result is the chain verification of the first kc = clamp(cap[b],
+ * 0, K) positions (uniforms 0..kc-1 for the tests, uniform kc for the final
+ * draw); A_full_out[b] is the first rejection over all K positions. Both are
+ * plain calls of orc_verify_chain on one sequence; probs_out ([B*K, 2]) covers
+ * the whole window.
+ */
+void orc_verify_chain_capped(const float* target, const float* draft, const int32_t* tokens,
+                             const float* uniforms, const int32_t* cap, int B, int K, int V,
+                             double T, int top_k, double margin_rel, int32_t* A_out,
+                             int32_t* next_out, int32_t* A_full_out, double* probs_out,
+                             double* R_out, int32_t* status_out, int32_t* margin_out,
+                             int nthreads) {
+#pragma omp parallel for schedule(dynamic, 1) num_threads(nthreads > 0 ? nthreads : 1)
+    for (int b = 0; b < B; ++b) {
+        const float* tw = target + (size_t)b * (K + 1) * V;
+        const float* dw = draft + (size_t)b * K * V;
+        const int32_t* yw = tokens + (size_t)b * K;
+        const float* uw = uniforms + (size_t)b * (K + 1);
+        int kc = cap[b] < 0 ? 0 : (cap[b] > K ? K : cap[b]);
+        int32_t cu_c[2] = {0, kc}, cu_f[2] = {0, K};
+        int32_t A_f, next_f, st_f, mg_f;
+        double R_f;
+        /* the whole window: A over all K positions, and every p(y), q(y) */
+        orc_verify_chain(tw, dw, yw, uw, cu_f, 1, K, V, T, top_k, margin_rel, &A_f, &next_f,
+                         probs_out ? probs_out + (size_t)2 * b * K : NULL, &R_f, &st_f, &mg_f, 1);
+        /* the committed part: the first kc positions */
+        orc_verify_chain(tw, dw, yw, uw, cu_c, 1, kc, V, T, top_k, margin_rel, A_out + b,
+                         next_out + b, NULL, R_out ? R_out + b : NULL,
+                         status_out ? status_out + b : NULL, margin_out ? margin_out + b : NULL, 1);
+        A_full_out[b] = A_f;
+    }
+}
+
+/*
  * Greedy chain verification [SD §1: greedy results follow the target argmax]:
  * g_i = lowest-id argmax of target row i, acc_i = (y_i == g_i), A = first
  * mismatch (else k), next = g_A. Same layout as orc_verify_chain. argmax_out
@@ -455,6 +492,42 @@ void orc_select_len(const float* conf, int B, int K, float cost, int32_t* k_sel,
             if (f > best_f) { best_f = f; best_k = j; best_sum = sum; }
             if (fabs((double)s - (double)cost) < 1e-6) margin = 1;
         }
+        k_sel[b] = best_k;
+        if (adv_out) adv_out[b] = 1.0 + best_sum;
+        if (margin_out) margin_out[b] = margin;
+    }
+    if (cu_sel) {
+        cu_sel[0] = 0;
+        for (int b = 0; b < B; ++b) cu_sel[b + 1] = cu_sel[b] + k_sel[b];
+    }
+}
+
+/*
+ * Verify length with a per-position cost table [SD §5 DSpark: is one more
+ * verified position worth its cost]: cost[j-1] is the cost of verifying
+ * position j; k* = the smallest k in [0, K] maximising
+ * f(k) = 1 + sum_{j<=k} s_j - sum_{j<=k} cost[j-1], both sums running in fp64
+ * over the fp32 s_j and costs; expected advance 1 + sum_{j<=k*} s_j.
+ * margin_out[b] = 1 when another k comes within 1e-6 of the best f.
+ */
+void orc_select_len_table(const float* conf, int B, int K, const float* cost, int32_t* k_sel,
+                          double* adv_out, int32_t* cu_sel, int32_t* margin_out) {
+    for (int b = 0; b < B; ++b) {
+        float s = 1.0f;
+        double sum_s = 0.0, sum_c = 0.0, best_f = 1.0, best_sum = 0.0;
+        double fk[65];
+        int best_k = 0, margin = 0;
+        fk[0] = 1.0;
+        for (int j = 1; j <= K; ++j) {
+            s = s * conf[(size_t)b * K + (j - 1)];
+            sum_s += (double)s;
+            sum_c += (double)cost[j - 1];
+            double f = 1.0 + sum_s - sum_c;
+            fk[j] = f;
+            if (f > best_f) { best_f = f; best_k = j; best_sum = sum_s; }
+        }
+        for (int j = 0; j <= K; ++j)
+            if (j != best_k && fabs(fk[j] - best_f) < 1e-6) margin = 1;
         k_sel[b] = best_k;
         if (adv_out) adv_out[b] = 1.0 + best_sum;
         if (margin_out) margin_out[b] = margin;

@@ -65,6 +65,11 @@ def _load():
     lib.sd_verify_tree.restype = ctypes.c_int
     lib.sd_select_len.argtypes = [P, I, I, F, P, P, P, P]
     lib.sd_select_len.restype = ctypes.c_int
+    lib.sd_verify_chain_capped.argtypes = [P, P, ctypes.c_int, P, P, P, I, I, I, F, I, P, P, P, P, P,
+                                           P, P, Z, P]
+    lib.sd_verify_chain_capped.restype = ctypes.c_int
+    lib.sd_select_len_table.argtypes = [P, I, I, P, P, P, P, P]
+    lib.sd_select_len_table.restype = ctypes.c_int
     lib.sd_time_next_stream_pass.argtypes = [P, P]
     lib.sd_time_next_stream_pass.restype = ctypes.c_int
     _lib = lib
@@ -228,6 +233,52 @@ def verify_chain(target: torch.Tensor, draft: Optional[torch.Tensor], tokens: to
     return res
 
 
+def verify_chain_capped(target: torch.Tensor, draft: Optional[torch.Tensor], tokens: torch.Tensor,
+                        uniforms: Optional[torch.Tensor], k_cap: torch.Tensor, temperature: float,
+                        top_k: int = 0, want_probs: bool = False, want_resid: bool = False,
+                        workspace: Optional[torch.Tensor] = None, stream=None) -> dict:
+    """sd_verify_chain_capped (cap-accept). Padded window: target [B*(K+1), V],
+    draft [B*K, V], tokens [B, K], uniforms [B*(K+1)], k_cap [B] int32 (device).
+    Returns accepted_len (committed), next_token, accepted_full, status
+    (+ probs [B*K, 2], resid)."""
+    dev = target.device
+    _check(target, "target", device=dev)
+    dt = _dtype_code(target)
+    V = int(target.shape[-1])
+    if tokens.dim() != 2:
+        raise ValueError("tokens must be [B, K]")
+    B, K = (int(x) for x in tokens.shape)
+    _check(tokens, "tokens", torch.int32, dev)
+    _check(k_cap, "k_cap", torch.int32, dev)
+    if k_cap.numel() != B:
+        raise ValueError("k_cap must hold one entry per sequence")
+    greedy = float(temperature) == 0.0
+    if not greedy:
+        _check(draft, "draft", target.dtype, dev)
+        _check(uniforms, "uniforms", torch.float32, dev)
+    _check_layout(target, draft, tokens, uniforms, None, B, K, V, greedy, False)
+    A = torch.empty(B, dtype=torch.int32, device=dev)
+    nxt = torch.empty(B, dtype=torch.int32, device=dev)
+    Af = torch.empty(B, dtype=torch.int32, device=dev)
+    st = torch.empty(B, dtype=torch.int32, device=dev)
+    probs = torch.empty(max(B * K, 1), 2, dtype=torch.float32, device=dev) if want_probs and not greedy else None
+    resid = torch.empty(B, dtype=torch.float32, device=dev) if want_resid and not greedy else None
+    ws = _workspace(workspace_bytes(OP_CHAIN, B, K, V, top_k), dev, workspace)
+    r = _load().sd_verify_chain_capped(_ptr(target), _ptr(draft) if not greedy else None, dt,
+                                       _ptr(tokens), _ptr(uniforms) if not greedy else None,
+                                       _ptr(k_cap), B, K, V, ctypes.c_float(float(temperature)),
+                                       int(top_k), _ptr(A), _ptr(nxt), _ptr(Af), _ptr(probs),
+                                       _ptr(resid), _ptr(st), _ptr(ws), ctypes.c_size_t(ws.numel()),
+                                       _stream(stream))
+    _raise(r, "sd_verify_chain_capped")
+    res = {"accepted_len": A, "next_token": nxt, "accepted_full": Af, "status": st}
+    if probs is not None:
+        res["probs"] = probs
+    if resid is not None:
+        res["resid"] = resid
+    return res
+
+
 def verify_greedy(target: torch.Tensor, tokens: torch.Tensor, cu: Optional[torch.Tensor] = None,
                   B: Optional[int] = None, K_max: Optional[int] = None,
                   workspace: Optional[torch.Tensor] = None, stream=None) -> dict:
@@ -315,4 +366,23 @@ def select_len(conf: torch.Tensor, cost: float, out: Optional[dict] = None, stre
     r = _load().sd_select_len(_ptr(conf), B, K, ctypes.c_float(float(cost)), _ptr(k), _ptr(adv),
                               _ptr(cu), _stream(stream))
     _raise(r, "sd_select_len")
+    return {"k": k, "adv": adv, "cu": cu}
+
+
+def select_len_table(conf: torch.Tensor, cost_table: torch.Tensor, out: Optional[dict] = None,
+                     stream=None) -> dict:
+    """sd_select_len_table. conf [B, K_max] float32, cost_table [K_max] float32, on the GPU."""
+    dev = conf.device
+    _check(conf, "conf", torch.float32, dev)
+    _check(cost_table, "cost_table", torch.float32, dev)
+    B, K = (int(s) for s in conf.shape)
+    if cost_table.numel() < K:
+        raise ValueError("cost_table needs one entry per position")
+    o = out or {}
+    k = _get(o, "k", lambda: torch.empty(B, dtype=torch.int32, device=dev))
+    adv = _get(o, "adv", lambda: torch.empty(B, dtype=torch.float32, device=dev))
+    cu = _get(o, "cu", lambda: torch.empty(B + 1, dtype=torch.int32, device=dev))
+    r = _load().sd_select_len_table(_ptr(conf), B, K, _ptr(cost_table), _ptr(k), _ptr(adv), _ptr(cu),
+                                    _stream(stream))
+    _raise(r, "sd_select_len_table")
     return {"k": k, "adv": adv, "cu": cu}

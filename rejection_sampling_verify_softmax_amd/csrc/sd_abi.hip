@@ -96,13 +96,18 @@ sd_status_t sd_workspace_bytes(sd_op_t op, int32_t B, int32_t K_max, int32_t V, 
     return SD_EINVAL;
 }
 
-sd_status_t sd_verify_chain(const void* target_logits, const void* draft_logits, sd_dtype_t dtype,
-                            const int32_t* draft_tokens, const float* uniforms,
-                            const int32_t* cu_draft, int32_t B, int32_t K_max, int32_t V,
-                            float temperature, int32_t top_k, int32_t* accepted_len,
-                            int32_t* next_token, float* probs_out, float* resid_mass_out,
-                            int32_t* seq_status, void* workspace, size_t workspace_bytes,
-                            void* hip_stream) {
+}  // extern "C"
+
+namespace {
+
+// sd_verify_chain and sd_verify_chain_capped: checks, then the path's launches.
+sd_status_t verify_chain(const void* target_logits, const void* draft_logits, sd_dtype_t dtype,
+                         const int32_t* draft_tokens, const float* uniforms, const int32_t* cu_draft,
+                         const int32_t* cap, int32_t B, int32_t K_max, int32_t V, float temperature,
+                         int32_t top_k, int32_t* accepted_len, int32_t* next_token,
+                         int32_t* accepted_full, float* probs_out, float* resid_mass_out,
+                         int32_t* seq_status, void* workspace, size_t workspace_bytes,
+                         void* hip_stream) {
     if (bad_size(B, K_max, V) || bad_dtype(dtype)) return SD_EINVAL;
     if (!(temperature >= 0.0f) || !isfinite(temperature)) return SD_EINVAL;
     if (top_k < 0 || top_k > SD_MAX_TOPK) return SD_EINVAL;
@@ -115,7 +120,8 @@ sd_status_t sd_verify_chain(const void* target_logits, const void* draft_logits,
     hipStream_t st = static_cast<hipStream_t>(hip_stream);
     if (greedy)
         return from_hip(sd::launch_greedy(target_logits, (int)dtype, draft_tokens, cu_draft, B, K_max,
-                                          V, accepted_len, next_token, seq_status, workspace, st));
+                                          V, accepted_len, next_token, seq_status, cap, accepted_full,
+                                          workspace, st));
     sd::ChainArgs a;
     a.target = target_logits;
     a.draft = draft_logits;
@@ -133,10 +139,43 @@ sd_status_t sd_verify_chain(const void* target_logits, const void* draft_logits,
     a.probs_out = probs_out;
     a.resid_mass_out = resid_mass_out;
     a.seq_status = seq_status;
+    a.cap = cap;
+    a.accepted_full = accepted_full;
     a.ws = workspace;
     a.stream = st;
     if (topk_on(top_k, V)) return from_hip(sd::launch_chain_topk(a));
     return from_hip(sd::launch_chain_full(a));
+}
+
+}  // namespace
+
+extern "C" {
+
+sd_status_t sd_verify_chain(const void* target_logits, const void* draft_logits, sd_dtype_t dtype,
+                            const int32_t* draft_tokens, const float* uniforms,
+                            const int32_t* cu_draft, int32_t B, int32_t K_max, int32_t V,
+                            float temperature, int32_t top_k, int32_t* accepted_len,
+                            int32_t* next_token, float* probs_out, float* resid_mass_out,
+                            int32_t* seq_status, void* workspace, size_t workspace_bytes,
+                            void* hip_stream) {
+    return verify_chain(target_logits, draft_logits, dtype, draft_tokens, uniforms, cu_draft, nullptr,
+                        B, K_max, V, temperature, top_k, accepted_len, next_token, nullptr, probs_out,
+                        resid_mass_out, seq_status, workspace, workspace_bytes, hip_stream);
+}
+
+sd_status_t sd_verify_chain_capped(const void* target_logits, const void* draft_logits,
+                                   sd_dtype_t dtype, const int32_t* draft_tokens,
+                                   const float* uniforms, const int32_t* k_cap, int32_t B,
+                                   int32_t K_max, int32_t V, float temperature, int32_t top_k,
+                                   int32_t* accepted_len, int32_t* next_token,
+                                   int32_t* accepted_full, float* probs_out, float* resid_mass_out,
+                                   int32_t* seq_status, void* workspace, size_t workspace_bytes,
+                                   void* hip_stream) {
+    if (!k_cap) return SD_EINVAL;
+    return verify_chain(target_logits, draft_logits, dtype, draft_tokens, uniforms, nullptr, k_cap, B,
+                        K_max, V, temperature, top_k, accepted_len, next_token, accepted_full,
+                        probs_out, resid_mass_out, seq_status, workspace, workspace_bytes,
+                        hip_stream);
 }
 
 sd_status_t sd_verify_greedy(const void* target_logits, sd_dtype_t dtype,
@@ -149,8 +188,8 @@ sd_status_t sd_verify_greedy(const void* target_logits, sd_dtype_t dtype,
     if (K_max > 0 && !draft_tokens) return SD_EINVAL;
     if (workspace_bytes < sd::greedy_ws_bytes(B, K_max, V, (int)dtype)) return SD_EWORKSPACE;
     return from_hip(sd::launch_greedy(target_logits, (int)dtype, draft_tokens, cu_draft, B, K_max, V,
-                                      accepted_len, next_token, seq_status, workspace,
-                                      static_cast<hipStream_t>(hip_stream)));
+                                      accepted_len, next_token, seq_status, nullptr, nullptr,
+                                      workspace, static_cast<hipStream_t>(hip_stream)));
 }
 
 sd_status_t sd_build_tree(const float* marginals, int32_t B, int32_t K, int32_t V, int32_t N,
@@ -193,7 +232,17 @@ sd_status_t sd_select_len(const float* conf, int32_t B, int32_t K_max, float cos
     if (B < 1 || B > kMaxB || K_max < 0 || K_max > SD_MAX_K) return SD_EINVAL;
     if (!isfinite(cost_per_position)) return SD_EINVAL;
     if ((K_max > 0 && !conf) || !k_sel) return SD_EINVAL;
-    return from_hip(sd::launch_select_len(conf, B, K_max, cost_per_position, k_sel, expected_advance,
+    return from_hip(sd::launch_select_len(conf, B, K_max, cost_per_position, nullptr, k_sel,
+                                          expected_advance, cu_sel,
+                                          static_cast<hipStream_t>(hip_stream)));
+}
+
+sd_status_t sd_select_len_table(const float* conf, int32_t B, int32_t K_max,
+                                const float* cost_table, int32_t* k_sel, float* expected_advance,
+                                int32_t* cu_sel, void* hip_stream) {
+    if (B < 1 || B > kMaxB || K_max < 0 || K_max > SD_MAX_K) return SD_EINVAL;
+    if ((K_max > 0 && (!conf || !cost_table)) || !k_sel) return SD_EINVAL;
+    return from_hip(sd::launch_select_len(conf, B, K_max, 0.0f, cost_table, k_sel, expected_advance,
                                           cu_sel, static_cast<hipStream_t>(hip_stream)));
 }
 

@@ -541,7 +541,7 @@ __global__ __launch_bounds__(kBlock) void k_chain_decide(
     const float* __restrict__ xy, const int32_t* __restrict__ tok, const float* __restrict__ uni,
     const int32_t* __restrict__ cu, int B, int K_max, int V, int n_chunks, float c,
     int32_t* __restrict__ A_out, float* __restrict__ probs_out, int32_t* __restrict__ status_out,
-    ChainDesc* __restrict__ desc) {
+    ChainDesc* __restrict__ desc, const int32_t* __restrict__ cap, int32_t* __restrict__ A_full_out) {
     const int b = blockIdx.x * kSeqPerBlock + threadIdx.x / kWave;
     if (b >= B) return;
     const int lane = threadIdx.x & (kWave - 1);
@@ -572,15 +572,17 @@ __global__ __launch_bounds__(kBlock) void k_chain_decide(
         }
     }
     const unsigned long long rej = __ballot(!acc);
-    const int A = rej ? (__ffsll(rej) - 1) : k;
-    int mine = (lane < k && lane <= A) ? st : 0;
+    const int A_full = rej ? (__ffsll(rej) - 1) : k;
+    const int kc = committed_len(cap, b, k);
+    const int A = A_full < kc ? A_full : kc;
+    int mine = (lane < kc && lane <= A) ? st : 0;
 #pragma unroll
     for (int o = kWave / 2; o > 0; o >>= 1) mine |= __shfl_xor(mine, o, kWave);
     ChainDesc d;
     d.A = A;
-    d.u = uni[d0 + b + k];
+    d.u = uni[d0 + b + kc];
     d.pad = 0.f;
-    if (A < k) {
+    if (A < kc) {
         const float Op = __shfl(rp.O, A, kWave);
         const double Sp = __shfl(rp.S, A, kWave);
         const bool vp = __shfl((int)rp.valid, A, kWave) != 0;
@@ -595,10 +597,10 @@ __global__ __launch_bounds__(kBlock) void k_chain_decide(
         d.O_q = Oq;
         d.S_q = Sq;
     } else {
-        const RowStat rb = combine_row(part_t + (slot0 + k) * n_chunks, n_chunks);
+        const RowStat rb = combine_row(part_t + (slot0 + kc) * n_chunks, n_chunks);
         d.mode = rb.valid ? kModeExtra : kModeNone;
         if (!rb.valid) mine |= 2;
-        d.t_row = d0 + b + k;
+        d.t_row = d0 + b + kc;
         d.d_row = -1;
         d.O_p = rb.O;
         d.S_p = rb.S;
@@ -607,6 +609,7 @@ __global__ __launch_bounds__(kBlock) void k_chain_decide(
     }
     if (lane == 0) {
         A_out[b] = A;
+        if (A_full_out) A_full_out[b] = A_full;
         if (status_out) status_out[b] = mine;
         desc[b] = d;
     }
@@ -708,7 +711,7 @@ static hipError_t chain_full_impl(const ChainArgs& a) {
     const unsigned seq_blocks = (unsigned)((a.B + kSeqPerBlock - 1) / kSeqPerBlock);
     hipLaunchKernelGGL(k_chain_decide, dim3(seq_blocks), dim3(kBlock), 0, a.stream, part_t, part_d,
                        xy, a.tokens, a.uniforms, a.cu, a.B, a.K_max, a.V, nc, c, a.accepted_len,
-                       a.probs_out, a.seq_status, desc);
+                       a.probs_out, a.seq_status, desc, a.cap, a.accepted_full);
     hipLaunchKernelGGL((k_chain_mass<E, VEC>), dim3((unsigned)((size_t)a.B * n_mchunks)),
                        dim3(kResolveThreads), 0, a.stream, tgt, dft, desc, a.V, mchunk, n_mchunks, c,
                        pieces);

@@ -205,6 +205,14 @@ __device__ __forceinline__ void seq_range(const int32_t* cu, int b, int K_max, i
     }
 }
 
+// Committed window of sequence b: its draft length k, or cap[b] clamped to
+// [0, k] when a cap is given (the window is still verified in full).
+__device__ __forceinline__ int committed_len(const int32_t* cap, int b, int k) {
+    if (cap == nullptr) return k;
+    const int c = cap[b];
+    return c < 0 ? 0 : (c > k ? k : c);
+}
+
 // ---------------------------------------------------------------------------
 // Softmax partials. A partial (o, S) of a set of logits x says
 //   sum_x 2^(x*c - o) = S,  c = log2(e)/T rounded to fp32,

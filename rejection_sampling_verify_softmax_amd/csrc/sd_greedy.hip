@@ -149,7 +149,8 @@ __device__ int combine_arg(const ArgPartial* p, int n_chunks) {
 __global__ __launch_bounds__(kWave) void k_greedy_decide(
     const ArgPartial* __restrict__ part, const int32_t* __restrict__ tok,
     const int32_t* __restrict__ cu, int K_max, int V, int n_chunks, int32_t* __restrict__ A_out,
-    int32_t* __restrict__ next_out, int32_t* __restrict__ status_out) {
+    int32_t* __restrict__ next_out, int32_t* __restrict__ status_out, const int32_t* __restrict__ cap,
+    int32_t* __restrict__ A_full_out) {
     const int b = blockIdx.x;
     const int lane = threadIdx.x;
     const int slots = K_max + 1;
@@ -166,19 +167,22 @@ __global__ __launch_bounds__(kWave) void k_greedy_decide(
         st = (yok ? 0 : 1) | (g >= 0 ? 0 : 2);
     }
     const unsigned long long rej = __ballot(!acc);
-    const int A = rej ? (__ffsll(rej) - 1) : k;
-    int mine = (lane < k && lane <= A) ? st : 0;
+    const int A_full = rej ? (__ffsll(rej) - 1) : k;
+    const int kc = committed_len(cap, b, k);
+    const int A = A_full < kc ? A_full : kc;
+    int mine = (lane < kc && lane <= A) ? st : 0;
 #pragma unroll
     for (int o = kWave / 2; o > 0; o >>= 1) mine |= __shfl_xor(mine, o, kWave);
     int next;
-    if (A < k) {
+    if (A < kc) {
         next = __shfl(g, A, kWave);
     } else {
-        next = combine_arg(part + (slot0 + k) * n_chunks, n_chunks);
+        next = combine_arg(part + (slot0 + kc) * n_chunks, n_chunks);
     }
     if (next < 0) mine |= 2;
     if (lane == 0) {
         A_out[b] = A;
+        if (A_full_out) A_full_out[b] = A_full;
         next_out[b] = next;
         if (status_out) status_out[b] = mine;
     }
@@ -236,7 +240,7 @@ size_t tree_verify_ws_bytes(int B, int N, int V, int dtype) {
 template <class E, bool VEC>
 static hipError_t greedy_impl(const void* target, const int32_t* tokens, const int32_t* cu, int B,
                               int K_max, int V, int dtype, int32_t* A, int32_t* next, int32_t* st,
-                              void* ws, hipStream_t stream) {
+                              const int32_t* cap, int32_t* A_full, void* ws, hipStream_t stream) {
     const int nc = n_chunks_for(V, dtype);
     const int chunk = chunk_elems(dtype);
     ArgPartial* part = static_cast<ArgPartial*>(ws);
@@ -247,25 +251,26 @@ static hipError_t greedy_impl(const void* target, const int32_t* tokens, const i
                        nc, part);
     PassTimer::mark_after(stream);
     hipLaunchKernelGGL(k_greedy_decide, dim3(B), dim3(kWave), 0, stream, part, tokens, cu, K_max, V,
-                       nc, A, next, st);
+                       nc, A, next, st, cap, A_full);
     return hipGetLastError();
 }
 
 hipError_t launch_greedy(const void* target, int dtype, const int32_t* tokens, const int32_t* cu,
                          int B, int K_max, int V, int32_t* accepted_len, int32_t* next_token,
-                         int32_t* seq_status, void* ws, hipStream_t stream) {
+                         int32_t* seq_status, const int32_t* cap, int32_t* accepted_full, void* ws,
+                         hipStream_t stream) {
     if (dtype == 1) {
         if (V % Bf16::kVec == 0)
             return greedy_impl<Bf16, true>(target, tokens, cu, B, K_max, V, dtype, accepted_len,
-                                           next_token, seq_status, ws, stream);
+                                           next_token, seq_status, cap, accepted_full, ws, stream);
         return greedy_impl<Bf16, false>(target, tokens, cu, B, K_max, V, dtype, accepted_len,
-                                        next_token, seq_status, ws, stream);
+                                        next_token, seq_status, cap, accepted_full, ws, stream);
     }
     if (V % F32::kVec == 0)
         return greedy_impl<F32, true>(target, tokens, cu, B, K_max, V, dtype, accepted_len,
-                                      next_token, seq_status, ws, stream);
+                                      next_token, seq_status, cap, accepted_full, ws, stream);
     return greedy_impl<F32, false>(target, tokens, cu, B, K_max, V, dtype, accepted_len, next_token,
-                                   seq_status, ws, stream);
+                                   seq_status, cap, accepted_full, ws, stream);
 }
 
 template <class E, bool VEC>

@@ -75,6 +75,8 @@ struct ChainArgs {
     float* probs_out;
     float* resid_mass_out;
     int32_t* seq_status;
+    const int32_t* cap;        // per-sequence cap on the committed length, or nullptr
+    int32_t* accepted_full;    // first rejection over the whole window (with cap), or nullptr
     void* ws;
     hipStream_t stream;
 };
@@ -90,7 +92,8 @@ hipError_t launch_chain_full(const ChainArgs& a);
 hipError_t launch_chain_topk(const ChainArgs& a);
 hipError_t launch_greedy(const void* target, int dtype, const int32_t* tokens, const int32_t* cu,
                          int B, int K_max, int V, int32_t* accepted_len, int32_t* next_token,
-                         int32_t* seq_status, void* ws, hipStream_t stream);
+                         int32_t* seq_status, const int32_t* cap, int32_t* accepted_full, void* ws,
+                         hipStream_t stream);
 hipError_t launch_tree_build(const float* marg, int B, int K, int V, int N, int32_t* tok,
                              int32_t* par, int32_t* dep, float* score, uint64_t* anc,
                              int32_t* n_nodes, void* ws, hipStream_t stream);
@@ -98,7 +101,7 @@ hipError_t launch_tree_verify(const void* target, int dtype, const int32_t* tok,
                               const int32_t* n_nodes, int B, int N, int V, int32_t* path,
                               int32_t* accepted_len, int32_t* next_token, void* ws,
                               hipStream_t stream);
-hipError_t launch_select_len(const float* conf, int B, int K_max, float cost, int32_t* k_sel,
-                             float* adv, int32_t* cu_sel, hipStream_t stream);
+hipError_t launch_select_len(const float* conf, int B, int K_max, float cost, const float* table,
+                             int32_t* k_sel, float* adv, int32_t* cu_sel, hipStream_t stream);
 
 }  // namespace sd

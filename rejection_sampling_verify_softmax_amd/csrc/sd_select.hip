@@ -17,8 +17,14 @@ namespace sd {
 
 namespace {
 
+// With `table` (the cost of verifying position j+1 at table[j]) the length is
+// the smallest maximiser of f(k) = 1 + sum_{j<=k} s_j - sum_{j<=k} table[j-1],
+// both sums running in fp64 in position order; without it, the length extends
+// while s_j > cost, which is that maximiser for a constant cost since s_j never
+// increases.
 __global__ __launch_bounds__(kBlock) void k_select_len(const float* __restrict__ conf, int B,
                                                        int K_max, float cost,
+                                                       const float* __restrict__ table,
                                                        int32_t* __restrict__ k_sel,
                                                        float* __restrict__ adv,
                                                        int32_t* __restrict__ cu_sel) {
@@ -31,14 +37,29 @@ __global__ __launch_bounds__(kBlock) void k_select_len(const float* __restrict__
         float s = 1.0f;
         double sum = 0.0;
         int k = 0;
-        bool go = true;
-        for (int j = 0; j < K_max; ++j) {
-            s = s * conf[(int64_t)b * K_max + j];     // fp32, left to right
-            if (go && s > cost) {
-                k = j + 1;
-                sum += (double)s;
-            } else {
-                go = false;
+        if (table == nullptr) {
+            bool go = true;
+            for (int j = 0; j < K_max; ++j) {
+                s = s * conf[(int64_t)b * K_max + j];     // fp32, left to right
+                if (go && s > cost) {
+                    k = j + 1;
+                    sum += (double)s;
+                } else {
+                    go = false;
+                }
+            }
+        } else {
+            double run_s = 0.0, run_c = 0.0, best = 1.0;
+            for (int j = 0; j < K_max; ++j) {
+                s = s * conf[(int64_t)b * K_max + j];
+                run_s += (double)s;
+                run_c += (double)table[j];
+                const double f = 1.0 + run_s - run_c;
+                if (f > best) {
+                    best = f;
+                    k = j + 1;
+                    sum = run_s;
+                }
             }
         }
         k_sel[b] = k;
@@ -58,10 +79,10 @@ __global__ __launch_bounds__(kBlock) void k_select_len(const float* __restrict__
 
 }  // namespace
 
-hipError_t launch_select_len(const float* conf, int B, int K_max, float cost, int32_t* k_sel,
-                             float* adv, int32_t* cu_sel, hipStream_t stream) {
-    hipLaunchKernelGGL(k_select_len, dim3(1), dim3(kBlock), 0, stream, conf, B, K_max, cost, k_sel,
-                       adv, cu_sel);
+hipError_t launch_select_len(const float* conf, int B, int K_max, float cost, const float* table,
+                             int32_t* k_sel, float* adv, int32_t* cu_sel, hipStream_t stream) {
+    hipLaunchKernelGGL(k_select_len, dim3(1), dim3(kBlock), 0, stream, conf, B, K_max, cost, table,
+                       k_sel, adv, cu_sel);
     return hipGetLastError();
 }
 

@@ -605,7 +605,8 @@ __global__ __launch_bounds__(kBlock) void k_chain_topk_decide(
     const int32_t* __restrict__ tok, const float* __restrict__ uni, const int32_t* __restrict__ cu,
     int B, int K_max, int V, int topk, float temperature, int32_t* __restrict__ A_out,
     int32_t* __restrict__ next_out, float* __restrict__ probs_out, float* __restrict__ R_out,
-    int32_t* __restrict__ status_out) {
+    int32_t* __restrict__ status_out, const int32_t* __restrict__ cap,
+    int32_t* __restrict__ A_full_out) {
     __shared__ double wbuf_all[kWavesPerBlock][kMaxTopk];
     __shared__ int ibuf_all[kWavesPerBlock][kMaxTopk];
     __shared__ TopEntry pl_all[kWavesPerBlock][kMaxTopk];
@@ -636,18 +637,20 @@ __global__ __launch_bounds__(kBlock) void k_chain_topk_decide(
         }
     }
     const unsigned long long rej = __ballot(!acc);
-    const int A = rej ? (__ffsll(rej) - 1) : k;
-    int status = (lane < k && lane <= A) ? st : 0;
+    const int A_full = rej ? (__ffsll(rej) - 1) : k;
+    const int kc = committed_len(cap, b, k);
+    const int A = A_full < kc ? A_full : kc;
+    int status = (lane < kc && lane <= A) ? st : 0;
 #pragma unroll
     for (int o = kWave / 2; o > 0; o >>= 1) status |= __shfl_xor(status, o, kWave);
-    const double uf = (double)uni[d0 + b + k];
+    const double uf = (double)uni[d0 + b + kc];
     int next = -1;
     double R = 0.0;
     double* wbuf = wbuf_all[w];
     int* ibuf = ibuf_all[w];
     TopEntry* pl = pl_all[w];
     TopEntry* dl = dl_all[w];
-    if (A < k) {
+    if (A < kc) {
         const RowTop sp = rowtop[task_of(A, 0)];
         const RowTop sq = rowtop[task_of(A, 1)];
         if (sp.valid) {
@@ -660,10 +663,10 @@ __global__ __launch_bounds__(kBlock) void k_chain_topk_decide(
             }
         }
     } else {
-        const RowTop sp = rowtop[task_of(k, 0)];
+        const RowTop sp = rowtop[task_of(kc, 0)];
         if (sp.valid) {
             double unused;
-            next = list_inverse_cdf(lists + task_of(k, 0) * topk, sp, nullptr, sp, false, T, uf, wbuf,
+            next = list_inverse_cdf(lists + task_of(kc, 0) * topk, sp, nullptr, sp, false, T, uf, wbuf,
                                     ibuf, pl, dl, &unused);
         } else {
             status |= 2;
@@ -672,6 +675,7 @@ __global__ __launch_bounds__(kBlock) void k_chain_topk_decide(
     }
     if (lane == 0) {
         A_out[b] = A;
+        if (A_full_out) A_full_out[b] = A_full;
         next_out[b] = next;
         if (R_out) R_out[b] = (float)R;
         if (status_out) status_out[b] = status;
@@ -895,7 +899,7 @@ static hipError_t chain_topk_impl(const ChainArgs& a) {
     hipLaunchKernelGGL(k_chain_topk_decide, dim3((unsigned)((a.B + kWavesPerBlock - 1) / kWavesPerBlock)),
                        dim3(kBlock), 0, a.stream, L.lists, L.rowtop, a.tokens, a.uniforms, a.cu, a.B,
                        a.K_max, a.V, a.top_k, a.temperature, a.accepted_len, a.next_token, a.probs_out,
-                       a.resid_mass_out, a.seq_status);
+                       a.resid_mass_out, a.seq_status, a.cap, a.accepted_full);
     return hipGetLastError();
 }
 

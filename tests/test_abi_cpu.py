@@ -28,6 +28,7 @@ def declared_symbols():
 def test_header_declares_the_five_calls():
     names = declared_symbols()
     for n in ("sd_verify_chain", "sd_verify_greedy", "sd_build_tree", "sd_verify_tree", "sd_select_len",
+              "sd_verify_chain_capped", "sd_select_len_table",
               "sd_workspace_bytes", "sd_abi_version", "sd_status_str"):
         assert n in names
 
@@ -113,6 +114,26 @@ def test_other_calls_reject_invalid_arguments(L):
     assert L.sd_select_len(one, 4, 65, ctypes.c_float(0.1), one, None, None, None) == 1
     assert L.sd_select_len(one, 4, 8, ctypes.c_float(float("nan")), one, None, None, None) == 1
     assert L.sd_select_len(one, 4, 8, ctypes.c_float(0.1), None, None, None, None) == 1
+
+
+def test_capped_and_cost_table_reject_invalid_arguments(L):
+    one = ctypes.c_void_p(1)
+    f = ctypes.c_float
+
+    def capped(cap=one, B=2, K=3, A=one, wsb=1 << 30, T=1.0):
+        return L.sd_verify_chain_capped(one, one, 1, one, one, cap, B, K, 100, f(T), 0, A, one, None,
+                                        None, None, None, one, wsb, None)
+    assert capped(cap=None) == 1
+    assert capped(B=0) == 1
+    assert capped(K=65) == 1
+    assert capped(A=None) == 1
+    assert capped(T=-1.0) == 1
+    assert capped(wsb=16) == 3
+    assert L.sd_select_len_table(one, 4, 8, None, one, None, None, None) == 1
+    assert L.sd_select_len_table(None, 4, 8, one, one, None, None, None) == 1
+    assert L.sd_select_len_table(one, 4, 65, one, one, None, None, None) == 1
+    assert L.sd_select_len_table(one, 0, 8, one, one, None, None, None) == 1
+    assert L.sd_select_len_table(one, 4, 8, one, None, None, None, None) == 1
 
 
 def test_binding_fails_loudly_without_gpu():

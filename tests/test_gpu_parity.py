@@ -14,7 +14,7 @@ import oracle
 import rejection_sampling_verify_softmax_amd as sd
 from rejection_sampling_verify_softmax_amd import workloads as wl
 
-from parity import compare_chain, oracle_chain, sample_seqs, subset_host
+from parity import close_rel, compare_chain, oracle_chain, sample_seqs, subset_host
 
 pytestmark = pytest.mark.gpu
 
@@ -322,6 +322,86 @@ def test_select_len_parity():
         np.testing.assert_array_equal(out["k"].cpu().numpy(), ref["k"])
         np.testing.assert_array_equal(out["cu"].cpu().numpy(), ref["cu"])
         np.testing.assert_allclose(out["adv"].cpu().numpy(), ref["adv"], rtol=1e-5)
+
+
+def test_select_len_table_parity():
+    g = torch.Generator(device="cuda").manual_seed(9)
+    for B, K in ((512, 8), (5, 64), (300, 3), (40, 0)):
+        conf = torch.sort(torch.rand(B, K, 6, generator=g, device="cuda"), dim=-1).values[..., 4].contiguous() \
+            if K > 0 else torch.zeros(B, 0, device="cuda")
+        table = (torch.rand(max(K, 1), generator=g, device="cuda") * 0.4).contiguous()
+        out = sd.select_len_table(conf, table)
+        ref = oracle.select_len_table(conf.cpu().numpy(), B, K, table.cpu().numpy())
+        np.testing.assert_array_equal(out["k"].cpu().numpy(), ref["k"])
+        np.testing.assert_array_equal(out["cu"].cpu().numpy(), ref["cu"])
+        np.testing.assert_allclose(out["adv"].cpu().numpy(), ref["adv"], rtol=1e-5)
+        # a constant table selects what the scalar call selects
+        flat = torch.full((max(K, 1),), 0.15, device="cuda")
+        a = sd.select_len_table(conf, flat)["k"].cpu().numpy()
+        b = sd.select_len(conf, 0.15)["k"].cpu().numpy()
+        np.testing.assert_array_equal(a, b)
+
+
+def _padded_case(mode, seed):
+    if mode == "topk":
+        return wl.gen_config3(device="cuda", seed=seed, B=48, K=6, V=30000, top_k=20)
+    if mode == "greedy":
+        g = wl.gen_config2(device="cuda", seed=seed, B=48, K=6, V=30000)
+        return wl.ChainCase(B=g.B, K_max=g.K_max, V=g.V, temperature=0.0, top_k=0, target=g.target,
+                            draft=None, tokens=g.tokens, uniforms=None)
+    return wl.gen_base_noise_chain(seed, B=48, K=6, V=30000, base_sigma=2.0, noise_sigma=0.7,
+                                   temperature=1.0, dtype="bf16", device="cuda")
+
+
+@pytest.mark.parametrize("mode", ["full", "topk", "greedy"])
+def test_capped_commits_what_compact_commits(mode):
+    _say(f"cap-accept vs compact ({mode})")
+    case = _padded_case(mode, 31)
+    B, K, V = case.B, case.K_max, case.V
+    g = torch.Generator(device="cuda").manual_seed(12)
+    cap = torch.randint(0, K + 1, (B,), generator=g, device="cuda", dtype=torch.int32)
+    cap[:3] = torch.tensor([-2, K + 5, K], dtype=torch.int32)      # clamped to [0, K]
+    greedy = case.temperature == 0.0
+    out = sd.verify_chain_capped(case.target, case.draft, case.tokens.view(B, K), case.uniforms, cap,
+                                 case.temperature, top_k=case.top_k, want_probs=not greedy,
+                                 want_resid=not greedy)
+    # compact: the first kc positions only (rows gathered as an engine would)
+    kc = cap.clamp(0, K).long()
+    ar_d, ar_t = torch.arange(K, device="cuda"), torch.arange(K + 1, device="cuda")
+    dmask = (ar_d[None, :] < kc[:, None]).reshape(-1)
+    tmask = (ar_t[None, :] <= kc[:, None]).reshape(-1)
+    cu = torch.zeros(B + 1, dtype=torch.int32, device="cuda")
+    cu[1:] = torch.cumsum(kc, 0).to(torch.int32)
+    packed = wl.ChainCase(B=B, K_max=K, V=V, temperature=case.temperature, top_k=case.top_k,
+                          target=case.target[tmask].contiguous(),
+                          draft=None if greedy else case.draft[dmask].contiguous(),
+                          tokens=case.tokens[dmask].contiguous(),
+                          uniforms=None if greedy else case.uniforms[tmask].contiguous(), cu=cu)
+    comp = sd.verify_chain(packed.target, packed.draft, packed.tokens, packed.uniforms,
+                           case.temperature, top_k=case.top_k, cu=cu, B=B, K_max=K)
+    for key in ("accepted_len", "next_token", "status"):
+        np.testing.assert_array_equal(out[key].cpu().numpy(), comp[key].cpu().numpy(), err_msg=key)
+    full = sd.verify_chain(case.target, case.draft, case.tokens, case.uniforms, case.temperature,
+                           top_k=case.top_k, B=B, K_max=K)
+    np.testing.assert_array_equal(out["accepted_full"].cpu().numpy(), full["accepted_len"].cpu().numpy())
+    # and the oracle's cap-accept verification
+    t = wl.to_host_f32(case.target)
+    if greedy:
+        ref = oracle.verify_chain_capped(t, np.zeros((B * K, V), np.float32), case.tokens.cpu().numpy(),
+                                         np.zeros(B * (K + 1), np.float32), cap.cpu().numpy(), B, K, V,
+                                         0.0)
+    else:
+        ref = oracle.verify_chain_capped(t, wl.to_host_f32(case.draft), case.tokens.cpu().numpy(),
+                                         case.uniforms.cpu().numpy(), cap.cpu().numpy(), B, K, V,
+                                         case.temperature, case.top_k)
+    ok = ref["margin"] == 0
+    for key, rk in (("accepted_len", "A"), ("next_token", "next"), ("accepted_full", "A_full")):
+        got = out[key].cpu().numpy()
+        assert (got[ok] == ref[rk][ok]).all(), (key, np.nonzero(got[ok] != ref[rk][ok]))
+    if not greedy:
+        good, worst = close_rel(out["probs"].cpu().numpy(), ref["probs"])
+        assert good, worst
+    _say(f"  margin cases {int((~ok).sum())}, mean committed {out['accepted_len'].float().mean().item():.2f}")
 
 
 def test_config5_adaptive_full_sampled():

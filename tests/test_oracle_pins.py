@@ -560,3 +560,87 @@ def test_tree_walk_expected_length_monte_carlo():
     expect = sum(float(tree["score"][0][i]) for i in range(1, nn))
     a = out["A"].astype(np.float64)
     assert abs(a.mean() - expect) < 4 * a.std() / math.sqrt(n)
+
+
+# --------------------------------------------------------------------------
+# Ragged verify modes and a per-position cost table ([SD §9 DSpark], [SD §5 DSpark])
+# --------------------------------------------------------------------------
+
+def test_select_len_table_closed_form_and_constant_table():
+    # c == 1 gives s_j == 1, so f(k) = 1 + k - sum of the first k costs:
+    # costs (0.5, 2, 0.1, 0.1) give f = 1, 1.5, 0.5, 1.4, 2.3 -> k* = 4, advance 5
+    out = oracle.select_len_table(np.ones((1, 4), np.float32), 1, 4,
+                                  np.array([0.5, 2.0, 0.1, 0.1], np.float32))
+    assert out["k"][0] == 4 and out["adv"][0] == 5.0
+    # ... and with the last cost raised to 1.5: f = 1, 1.5, 0.5, 1.4, 0.9 -> k* = 1, advance 2
+    out = oracle.select_len_table(np.ones((1, 4), np.float32), 1, 4,
+                                  np.array([0.5, 2.0, 0.1, 1.5], np.float32))
+    assert out["k"][0] == 1 and out["adv"][0] == 2.0
+    # a constant table is the scalar rule (itself pinned to the survival closed form)
+    rng = np.random.default_rng(21)
+    B, K = 3000, 8
+    conf = np.sort(rng.random((B, K, 6)), axis=-1)[..., 4].astype(np.float32)
+    for cost in (0.0, 0.15, 0.5):
+        a = oracle.select_len_table(conf, B, K, np.full(K, cost, np.float32))
+        b = oracle.select_len(conf, B, K, cost)
+        np.testing.assert_array_equal(a["k"], b["k"])
+        np.testing.assert_array_equal(a["adv"], b["adv"])
+        np.testing.assert_array_equal(a["cu"], b["cu"])
+
+
+def test_select_len_table_monotone_in_cost():
+    # raising costs element-wise adds a non-decreasing amount to sum_{j<=k} cost,
+    # so the smallest maximiser can only move to a shorter length
+    rng = np.random.default_rng(22)
+    B, K = 2000, 8
+    conf = rng.random((B, K)).astype(np.float32) ** 0.2
+    base = (rng.random(K) * 0.3).astype(np.float32)
+    prev = oracle.select_len_table(conf, B, K, base)["k"]
+    for step in range(5):
+        base = (base + (rng.random(K) * 0.1).astype(np.float32)).astype(np.float32)
+        k = oracle.select_len_table(conf, B, K, base)["k"]
+        assert (k <= prev).all()
+        prev = k
+    assert (oracle.select_len_table(conf, B, K, np.full(K, -1.0, np.float32))["k"] == K).all()
+    assert (oracle.select_len_table(conf, B, K, np.full(K, 1.5, np.float32))["k"] == 0).all()
+
+
+def _window(rng, B, K, V, T=1.0):
+    D = rng.normal(0, 2, (B, K + 1, V))
+    tgt = (D + rng.normal(0, 0.5, D.shape)).astype(np.float32)
+    dft = D[:, :K].astype(np.float32)
+    y = np.zeros((B, K), np.int32)
+    for b in range(B):
+        for i in range(K):
+            z = dft[b, i].astype(np.float64) / T
+            p = np.exp(z - z.max())
+            y[b, i] = rng.choice(V, p=p / p.sum())
+    return tgt, dft, y, grid_u(rng, B * (K + 1))
+
+
+def test_capped_commits_what_compact_commits():
+    rng = np.random.default_rng(23)
+    B, K, V = 40, 6, 50
+    tgt, dft, y, u = _window(rng, B, K, V)
+    cap = rng.integers(0, K + 1, B).astype(np.int32)
+    cap[:3] = (-2, K + 5, K)                      # clamped to [0, K]
+    out = oracle.verify_chain_capped(tgt, dft, y, u, cap, B, K, V, 1.0)
+    full = oracle.verify_chain(tgt, dft, y, u, None, B, K, V, 1.0)
+    kc = np.clip(cap, 0, K)
+    # compact: only the first kc positions (and kc+1 target rows / uniforms) exist
+    t_rows = np.concatenate([tgt[b, :kc[b] + 1] for b in range(B)])
+    d_rows = np.concatenate([dft[b, :kc[b]] for b in range(B)])
+    y_c = np.concatenate([y[b, :kc[b]] for b in range(B)])
+    u_c = np.concatenate([u.reshape(B, K + 1)[b, :kc[b] + 1] for b in range(B)])
+    cu = np.concatenate([[0], np.cumsum(kc)]).astype(np.int32)
+    comp = oracle.verify_chain(t_rows, d_rows, y_c, u_c, cu, B, K, V, 1.0)
+    np.testing.assert_array_equal(out["A"], comp["A"])
+    np.testing.assert_array_equal(out["next"], comp["next"])
+    np.testing.assert_array_equal(out["A_full"], full["A"])
+    np.testing.assert_array_equal(out["probs"], full["probs"])
+    # the committed length is the full-window rejection point, capped
+    np.testing.assert_array_equal(out["A"], np.minimum(full["A"], kc))
+    # cap == K is the static (full-window) verification itself
+    allk = oracle.verify_chain_capped(tgt, dft, y, u, np.full(B, K, np.int32), B, K, V, 1.0)
+    np.testing.assert_array_equal(allk["A"], full["A"])
+    np.testing.assert_array_equal(allk["next"], full["next"])
