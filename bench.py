@@ -72,6 +72,8 @@ def load_traffic(kernel: str, workload: str):
 # --------------------------------------------------------------------------
 
 def setup_adaptive(torch, sd, wl):
+    import numpy as np
+
     case = wl.gen_config5(device="cuda")
     sel = sd.select_len(case.conf, case.cost)
     torch.cuda.synchronize()
@@ -84,9 +86,19 @@ def setup_adaptive(torch, sd, wl):
                                             validate=True).items()}
     ws = torch.empty(sd.workspace_bytes(sd.OP_CHAIN, B, K, V), dtype=torch.uint8, device="cuda")
     sel_out = {"k": sel["k"], "adv": sel["adv"], "cu": sel["cu"]}
-    logit_bytes = (R_t + R_d) * V * 2
-    stats_bytes = logit_bytes + R_d * 4                       # rows once + draft tokens
-    step_bytes = (logit_bytes + R_d * 4 + R_t * 4              # rows, tokens, uniforms
+    # Rows the verification streams: positions 0 and 1 (and the extra-token
+    # row of a shorter draft) of every sequence in the first phase, the rest of
+    # the window only for sequences whose first two drafts were both accepted.
+    k_sel = sel["k"].cpu().numpy().astype(np.int64)
+    A = out["accepted_len"].cpu().numpy().astype(np.int64)
+    split = 2
+    t1, d1 = np.minimum(k_sel + 1, split), np.minimum(k_sel, split)
+    alive = (k_sel >= split) & (A >= split)
+    t2 = np.where(alive, k_sel + 1 - split, 0)
+    d2 = np.where(alive, k_sel - split, 0)
+    rows1, rows2 = int(t1.sum() + d1.sum()), int(t2.sum() + d2.sum())
+    stats_bytes = rows1 * V * 2 + int(d1.sum()) * 4           # first-phase rows once + draft tokens
+    step_bytes = ((rows1 + rows2) * V * 2 + R_d * 4 + R_t * 4  # rows streamed, tokens, uniforms
                   + B * K * 4 + B * (4 + 4 + 4) + (B + 1) * 4  # conf in; k, adv, cu out
                   + B * 12)                                    # A, next, status out
 
@@ -104,7 +116,8 @@ def setup_adaptive(torch, sd, wl):
         "global_batch": B, "K_max": K, "V": V, "logits": "bf16", "temperature": 1.0,
         "positions_per_step": positions, "target_rows": R_t, "draft_rows": R_d,
         "kernel": "k_chain_stats", "kernel_bytes": stats_bytes, "step_bytes": step_bytes,
-        "mean_k": positions / B,
+        "mean_k": positions / B, "mean_A": float(A.mean()),
+        "rows_streamed": rows1 + rows2, "rows_in_windows": R_t + R_d,
     }
     cpu = {"case": case, "packed": packed, "k": sel["k"].cpu().numpy(), "cu": sel["cu"].cpu().numpy()}
     return step, meta, cpu
@@ -351,6 +364,9 @@ def main():
     for k in ("logits", "temperature", "mean_k"):
         if k in meta:
             result["config"][k] = meta[k]
+    for k in ("mean_A", "rows_streamed", "rows_in_windows"):
+        if k in meta:
+            result["step"][k] = meta[k]
     if cpu is not None and not args.no_cpu_baseline:
         log("timing the CPU oracle on a bounded sample")
         result["cpu_baseline"] = run_cpu_baseline(cpu, args.cpu_seconds)

@@ -38,6 +38,8 @@ constexpr int kModeResidual = 0;
 constexpr int kModeExtra = 1;
 constexpr int kModeNone = 2;
 constexpr int kU = SD_STATS_UNROLL;
+// Slots (positions) streamed in the first phase of a phased verification.
+constexpr int kPhaseSplit = 2;
 // A one-pass chunk sum is kept only below 2^64 (its reference was then close
 // enough to the chunk's maximum); otherwise the exact two-pass path runs.
 constexpr double kFastSumLimit = 18446744073709551616.0;
@@ -210,15 +212,16 @@ __global__ __launch_bounds__(kBlock) void k_chain_stats(
     const typename E::raw* __restrict__ tgt, const typename E::raw* __restrict__ dft,
     const int32_t* __restrict__ tok, const int32_t* __restrict__ cu, int K_max, int V, int chunk,
     int n_chunks, float c, Partial* __restrict__ part_t, Partial* __restrict__ part_d,
-    float* __restrict__ xy) {
+    float* __restrict__ xy, int slot_lo, int slot_span, const int32_t* __restrict__ alive) {
     __shared__ double redd[kWavesPerBlock];
     __shared__ float redf[kWavesPerBlock];
     __shared__ int redi[kWavesPerBlock];
     const int slots = K_max + 1;
     const int ch = blockIdx.x % n_chunks;
     const int rest = blockIdx.x / n_chunks;
-    const int s = rest % slots;
-    const int b = rest / slots;
+    const int s = slot_lo + rest % slot_span;
+    const int b = rest / slot_span;
+    if (alive != nullptr && alive[b] == 0) return;     // decided in an earlier phase
     int d0, k;
     seq_range(cu, b, K_max, d0, k);
     if (s > k) return;
@@ -541,18 +544,22 @@ __global__ __launch_bounds__(kBlock) void k_chain_decide(
     const float* __restrict__ xy, const int32_t* __restrict__ tok, const float* __restrict__ uni,
     const int32_t* __restrict__ cu, int B, int K_max, int V, int n_chunks, float c,
     int32_t* __restrict__ A_out, float* __restrict__ probs_out, int32_t* __restrict__ status_out,
-    ChainDesc* __restrict__ desc, const int32_t* __restrict__ cap, int32_t* __restrict__ A_full_out) {
+    ChainDesc* __restrict__ desc, const int32_t* __restrict__ cap, int32_t* __restrict__ A_full_out,
+    int hi, int32_t* __restrict__ alive, int alive_in) {
     const int b = blockIdx.x * kSeqPerBlock + threadIdx.x / kWave;
     if (b >= B) return;
     const int lane = threadIdx.x & (kWave - 1);
+    if (alive_in && alive[b] == 0) return;              // decided in an earlier phase
     const int slots = K_max + 1;
     int d0, k;
     seq_range(cu, b, K_max, d0, k);
     const int64_t slot0 = (int64_t)b * slots;
+    // positions evaluated so far: those of the slots streamed up to this phase
+    const int kk = k < hi ? k : hi;
     bool acc = true;
     int st = 0;
     RowStat rp{-INFINITY, 0.0, false}, rq{-INFINITY, 0.0, false};
-    if (lane < k) {
+    if (lane < kk) {
         rp = combine_row(part_t + (slot0 + lane) * n_chunks, n_chunks);
         rq = combine_row(part_d + (slot0 + lane) * n_chunks, n_chunks);
         const int y = tok[d0 + lane];
@@ -572,6 +579,11 @@ __global__ __launch_bounds__(kBlock) void k_chain_decide(
         }
     }
     const unsigned long long rej = __ballot(!acc);
+    if (rej == 0ull && k >= hi) {                       // every position so far passed: next phase
+        if (lane == 0) alive[b] = 1;
+        return;
+    }
+    if (alive != nullptr && lane == 0) alive[b] = 0;
     const int A_full = rej ? (__ffsll(rej) - 1) : k;
     const int kc = committed_len(cap, b, k);
     const int A = A_full < kc ? A_full : kc;
@@ -681,6 +693,7 @@ size_t chain_full_ws_bytes(int B, int K_max, int V, int dtype) {
     cv.take(slots * 2 * sizeof(float));             // xy
     cv.take((size_t)B * npieces * sizeof(double));  // piece masses
     cv.take((size_t)B * sizeof(ChainDesc));         // decisions
+    cv.take((size_t)B * sizeof(int32_t));           // still undecided after a phase
     return cv.off;
 }
 
@@ -697,21 +710,34 @@ static hipError_t chain_full_impl(const ChainArgs& a) {
     float* xy = reinterpret_cast<float*>(ws + cv.take(slots * 2 * sizeof(float)));
     double* pieces = reinterpret_cast<double*>(ws + cv.take((size_t)a.B * npieces * sizeof(double)));
     ChainDesc* desc = reinterpret_cast<ChainDesc*>(ws + cv.take((size_t)a.B * sizeof(ChainDesc)));
+    int32_t* alive = reinterpret_cast<int32_t*>(ws + cv.take((size_t)a.B * sizeof(int32_t)));
     const int mchunk = kMassChunkVecs * E::kVec;
     const int n_mchunks = (a.V + mchunk - 1) / mchunk;
     const float c = (float)(1.4426950408889634 / (double)a.temperature);
     using raw = typename E::raw;
     const raw* tgt = static_cast<const raw*>(a.target);
     const raw* dft = static_cast<const raw*>(a.draft);
-    const unsigned grid1 = (unsigned)(slots * nc);
-    PassTimer::mark_before(a.stream);
-    hipLaunchKernelGGL((k_chain_stats<E, VEC>), dim3(grid1), dim3(kBlock), 0, a.stream, tgt, dft,
-                       a.tokens, a.cu, a.K_max, a.V, chunk, nc, c, part_t, part_d, xy);
-    PassTimer::mark_after(a.stream);
+    // Positions are verified in phases: a sequence whose draft is rejected in
+    // an early phase never streams its later rows. One phase when every
+    // position's p(y), q(y) or the full-window rejection is asked for.
+    const bool phased = a.probs_out == nullptr && a.cap == nullptr && a.accepted_full == nullptr &&
+                        a.K_max + 1 > kPhaseSplit;
     const unsigned seq_blocks = (unsigned)((a.B + kSeqPerBlock - 1) / kSeqPerBlock);
-    hipLaunchKernelGGL(k_chain_decide, dim3(seq_blocks), dim3(kBlock), 0, a.stream, part_t, part_d,
-                       xy, a.tokens, a.uniforms, a.cu, a.B, a.K_max, a.V, nc, c, a.accepted_len,
-                       a.probs_out, a.seq_status, desc, a.cap, a.accepted_full);
+    const int bounds[3] = {0, phased ? kPhaseSplit : a.K_max + 1, a.K_max + 1};
+    const int n_phases = phased ? 2 : 1;
+    for (int ph = 0; ph < n_phases; ++ph) {
+        const int lo = bounds[ph], hi = bounds[ph + 1];
+        const unsigned grid1 = (unsigned)((size_t)a.B * (hi - lo) * nc);
+        if (ph == 0) PassTimer::mark_before(a.stream);
+        hipLaunchKernelGGL((k_chain_stats<E, VEC>), dim3(grid1), dim3(kBlock), 0, a.stream, tgt, dft,
+                           a.tokens, a.cu, a.K_max, a.V, chunk, nc, c, part_t, part_d, xy, lo,
+                           hi - lo, ph > 0 ? alive : nullptr);
+        if (ph == 0) PassTimer::mark_after(a.stream);
+        hipLaunchKernelGGL(k_chain_decide, dim3(seq_blocks), dim3(kBlock), 0, a.stream, part_t,
+                           part_d, xy, a.tokens, a.uniforms, a.cu, a.B, a.K_max, a.V, nc, c,
+                           a.accepted_len, a.probs_out, a.seq_status, desc, a.cap, a.accepted_full,
+                           hi, phased ? alive : nullptr, ph > 0 ? 1 : 0);
+    }
     hipLaunchKernelGGL((k_chain_mass<E, VEC>), dim3((unsigned)((size_t)a.B * n_mchunks)),
                        dim3(kResolveThreads), 0, a.stream, tgt, dft, desc, a.V, mchunk, n_mchunks, c,
                        pieces);

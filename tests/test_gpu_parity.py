@@ -23,10 +23,12 @@ def _say(msg):
     print(msg, flush=True)
 
 
-def run_chain(case, **kw):
+def run_chain(case, probs=True, **kw):
+    # probs=False is the serving configuration: positions are then verified in
+    # phases and rows after an early rejection are never read
     return sd.verify_chain(case.target, case.draft, case.tokens, case.uniforms, case.temperature,
                            top_k=case.top_k, cu=case.cu, B=case.B, K_max=case.K_max,
-                           want_probs=True, want_resid=True, **kw)
+                           want_probs=probs, want_resid=True, **kw)
 
 
 # --------------------------------------------------------------------------
@@ -41,24 +43,26 @@ def test_config1_chain_f32():
     _say(f"  {info}")
 
 
+@pytest.mark.parametrize("probs", [True, False])
 @pytest.mark.parametrize("dtype,V,T", [("bf16", 40000, 0.9), ("bf16", 16384 * 2 + 8, 1.0),
                                        ("f32", 20000, 1.3), ("f32", 1001, 1.0), ("bf16", 777, 0.6)])
-def test_chain_small_all_sequences(dtype, V, T):
-    _say(f"chain small {dtype} V={V} T={T}")
+def test_chain_small_all_sequences(dtype, V, T, probs):
+    _say(f"chain small {dtype} V={V} T={T} probs={probs}")
     case = wl.gen_base_noise_chain(11 + V, B=24, K=5, V=V, base_sigma=2.0, noise_sigma=0.6,
                                    temperature=T, dtype=dtype, device="cuda")
-    out = run_chain(case)
+    out = run_chain(case, probs)
     info = compare_chain(out, oracle_chain(case))
     _say(f"  {info}")
     A = out["accepted_len"].cpu().numpy()
     assert (A < case.K_max).any()
 
 
-def test_chain_packed_ragged_lengths():
+@pytest.mark.parametrize("probs", [True, False])
+def test_chain_packed_ragged_lengths(probs):
     lengths = [0, 3, 1, 5, 0, 2, 8, 4, 1, 0, 6, 7]
-    _say(f"packed chain lengths {lengths}")
+    _say(f"packed chain lengths {lengths} probs={probs}")
     case = wl.ragged_chain(5, lengths, 30000, dtype="bf16", device="cuda")
-    out = run_chain(case)
+    out = run_chain(case, probs)
     info = compare_chain(out, oracle_chain(case))
     _say(f"  {info}")
     # a packed call matches the dense call of the same rows sequence by sequence
@@ -69,13 +73,14 @@ def test_chain_packed_ragged_lengths():
                            draft=case.draft[cu[b]: cu[b + 1]].contiguous(),
                            tokens=case.tokens[cu[b]: cu[b + 1]].contiguous(),
                            uniforms=case.uniforms[cu[b] + b: cu[b + 1] + b + 1].contiguous())
-        o1 = run_chain(sub)
+        o1 = run_chain(sub, probs)
         assert int(o1["accepted_len"][0]) == int(out["accepted_len"][b])
         assert int(o1["next_token"][0]) == int(out["next_token"][b])
 
 
-def test_chain_edge_cases():
-    _say("chain edge cases")
+@pytest.mark.parametrize("probs", [True, False])
+def test_chain_edge_cases(probs):
+    _say(f"chain edge cases probs={probs}")
     V, K, B = 4096, 3, 6
     g = torch.Generator(device="cuda").manual_seed(3)
     tgt = torch.randn(B * (K + 1), V, generator=g, device="cuda") * 2
@@ -100,7 +105,7 @@ def test_chain_edge_cases():
     for dtype in (torch.float32, torch.bfloat16):
         case = wl.ChainCase(B=B, K_max=K, V=V, temperature=1.0, top_k=0, target=tgt.to(dtype),
                             draft=dft.to(dtype), tokens=tok, uniforms=uni)
-        out = run_chain(case)
+        out = run_chain(case, probs)
         ref = oracle_chain(case)
         info = compare_chain(out, ref)
         _say(f"  {dtype}: {info} A={out['accepted_len'].tolist()} st={out['status'].tolist()}")
@@ -109,17 +114,21 @@ def test_chain_edge_cases():
         assert int(out["status"][2]) & sd.SEQ_NONFINITE and int(out["next_token"][2]) == -1
 
 
-def test_chain_tiny_vocab_and_k0():
-    _say("V=1, K_max=0 and all-zero packed lengths")
+@pytest.mark.parametrize("probs", [True, False])
+def test_chain_tiny_vocab_and_k0(probs):
+    _say(f"V=1, K_max=0 and all-zero packed lengths probs={probs}")
     for V in (1, 2, 8):
-        case = wl.gen_base_noise_chain(1, B=5, K=2, V=V, base_sigma=1.0, noise_sigma=0.5,
-                                       temperature=1.0, dtype="f32", device="cuda")
-        compare_chain(run_chain(case), oracle_chain(case))
+        for K in (1, 2, 3):
+            case = wl.gen_base_noise_chain(1, B=5, K=K, V=V, base_sigma=1.0, noise_sigma=0.5,
+                                           temperature=1.0, dtype="f32", device="cuda")
+            compare_chain(run_chain(case, probs), oracle_chain(case))
     case = wl.gen_base_noise_chain(2, B=7, K=0, V=300, base_sigma=1.0, noise_sigma=0.5,
                                    temperature=1.0, dtype="bf16", device="cuda")
-    compare_chain(run_chain(case), oracle_chain(case))
+    compare_chain(run_chain(case, probs), oracle_chain(case))
     case = wl.ragged_chain(3, [0, 0, 0], 500, dtype="bf16", device="cuda")
-    compare_chain(run_chain(case), oracle_chain(case))
+    compare_chain(run_chain(case, probs), oracle_chain(case))
+    case = wl.ragged_chain(4, [1, 2, 3, 2, 1, 0, 9], 700, dtype="bf16", device="cuda")
+    compare_chain(run_chain(case, probs), oracle_chain(case))
 
 
 def test_chain_run_twice_bit_identical():
@@ -420,6 +429,13 @@ def test_config5_adaptive_full_sampled():
     seqs = sample_seqs(case.B, 48, seed=5)
     info = compare_chain(out, oracle_chain(packed, seqs))
     _say(f"  {info} E[k*]={ref_sel['k'].mean():.3f} mean A={out['accepted_len'].float().mean().item():.3f}")
+    # the benchmark's own call: no per-position probabilities, so positions are
+    # verified in phases; the decisions are those of the one-phase call
+    o2 = sd.verify_chain(packed.target, packed.draft, packed.tokens, packed.uniforms, 1.0,
+                         cu=sel["cu"], B=case.B, K_max=case.K_max, want_resid=True, validate=False)
+    for key in ("accepted_len", "next_token", "status"):
+        assert torch.equal(o2[key], out[key]), key
+    np.testing.assert_array_equal(o2["resid"].cpu().numpy(), out["resid"].cpu().numpy())
 
 
 # --------------------------------------------------------------------------
