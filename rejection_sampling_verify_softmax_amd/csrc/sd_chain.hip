@@ -38,8 +38,14 @@ constexpr int kModeResidual = 0;
 constexpr int kModeExtra = 1;
 constexpr int kModeNone = 2;
 constexpr int kU = SD_STATS_UNROLL;
-// Slots (positions) streamed in the first phase of a phased verification.
-constexpr int kPhaseSplit = 2;
+// Phase boundaries of a phased verification: phase i streams the slots
+// (positions) from the previous boundary up to this one; the last phase runs
+// to the end of the window.
+#ifndef SD_PHASE_BOUNDS
+#define SD_PHASE_BOUNDS 2
+#endif
+constexpr int kPhaseBounds[] = {SD_PHASE_BOUNDS};
+constexpr int kMaxPhases = (int)(sizeof(kPhaseBounds) / sizeof(int)) + 1;
 // A one-pass chunk sum is kept only below 2^64 (its reference was then close
 // enough to the chunk's maximum); otherwise the exact two-pass path runs.
 constexpr double kFastSumLimit = 18446744073709551616.0;
@@ -720,11 +726,16 @@ static hipError_t chain_full_impl(const ChainArgs& a) {
     // Positions are verified in phases: a sequence whose draft is rejected in
     // an early phase never streams its later rows. One phase when every
     // position's p(y), q(y) or the full-window rejection is asked for.
-    const bool phased = a.probs_out == nullptr && a.cap == nullptr && a.accepted_full == nullptr &&
-                        a.K_max + 1 > kPhaseSplit;
+    const bool phased = a.probs_out == nullptr && a.cap == nullptr && a.accepted_full == nullptr;
     const unsigned seq_blocks = (unsigned)((a.B + kSeqPerBlock - 1) / kSeqPerBlock);
-    const int bounds[3] = {0, phased ? kPhaseSplit : a.K_max + 1, a.K_max + 1};
-    const int n_phases = phased ? 2 : 1;
+    int bounds[kMaxPhases + 1];
+    int n_phases = 0;
+    bounds[0] = 0;
+    if (phased)
+        for (int i = 0; i < kMaxPhases - 1; ++i)
+            if (kPhaseBounds[i] > bounds[n_phases] && kPhaseBounds[i] < a.K_max + 1)
+                bounds[++n_phases] = kPhaseBounds[i];
+    bounds[++n_phases] = a.K_max + 1;
     for (int ph = 0; ph < n_phases; ++ph) {
         const int lo = bounds[ph], hi = bounds[ph + 1];
         const unsigned grid1 = (unsigned)((size_t)a.B * (hi - lo) * nc);
@@ -736,7 +747,7 @@ static hipError_t chain_full_impl(const ChainArgs& a) {
         hipLaunchKernelGGL(k_chain_decide, dim3(seq_blocks), dim3(kBlock), 0, a.stream, part_t,
                            part_d, xy, a.tokens, a.uniforms, a.cu, a.B, a.K_max, a.V, nc, c,
                            a.accepted_len, a.probs_out, a.seq_status, desc, a.cap, a.accepted_full,
-                           hi, phased ? alive : nullptr, ph > 0 ? 1 : 0);
+                           hi, n_phases > 1 ? alive : nullptr, ph > 0 ? 1 : 0);
     }
     hipLaunchKernelGGL((k_chain_mass<E, VEC>), dim3((unsigned)((size_t)a.B * n_mchunks)),
                        dim3(kResolveThreads), 0, a.stream, tgt, dft, desc, a.V, mchunk, n_mchunks, c,
