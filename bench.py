@@ -155,11 +155,20 @@ def setup_topk(torch, sd, wl):
         sd.verify_chain(case.target, case.draft, case.tokens, case.uniforms, case.temperature,
                         top_k=case.top_k, B=B, K_max=K, workspace=ws, validate=False)
 
-    rows = B * (K + 1) + B * K
+    # rows streamed: slots 0-1 of every sequence, the rest only where both
+    # first drafts were accepted (as in the adaptive workload)
+    A = sd.verify_chain(case.target, case.draft, case.tokens, case.uniforms, case.temperature,
+                        top_k=case.top_k, B=B, K_max=K, workspace=ws)["accepted_len"].cpu()
+    split = 2
+    rows1 = B * (split + split)
+    alive = int((A >= split).sum())
+    rows2 = alive * ((K + 1 - split) + (K - split))
     meta = {"workload": f"top-k chain verify B={B} K={K} V={V} bf16 T=0.7 top-k 50",
             "global_batch": B, "K_max": K, "V": V, "positions_per_step": B * K,
-            "kernel": "k_topk_rows", "kernel_bytes": rows * V * 2,
-            "step_bytes": rows * V * 2 + B * K * 4 + B * (K + 1) * 4}
+            "kernel": "k_topk_rows", "kernel_bytes": rows1 * V * 2,
+            "step_bytes": (rows1 + rows2) * V * 2 + B * K * 4 + B * (K + 1) * 4,
+            "mean_A": float(A.float().mean()), "rows_streamed": rows1 + rows2,
+            "rows_in_windows": B * (K + 1) + B * K}
     return step, meta, None
 
 

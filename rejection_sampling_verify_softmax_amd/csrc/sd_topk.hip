@@ -71,6 +71,7 @@ __device__ const typename E::raw* topk_row(const typename E::raw* tgt, const typ
 constexpr int kTopkSample = 8;           // vectors per thread held in registers for the threshold
 constexpr int kTopkU = 4;                // vectors per thread per main-pass step (as many more in flight)
 constexpr int kWaveCap = 512;            // per-wave candidate buffer (64-bit keys)
+constexpr int kTopkPhaseSplit = 2;       // slots streamed before the first decision
 constexpr int kQueue = kTopkSample * kWave;   // per-wave queue of vector indices that may hold a candidate
 static_assert(kQueue >= kWave * kTopkU, "one offer step must fit an empty queue");
 
@@ -401,7 +402,10 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(4))) voi
                                                       const int32_t* __restrict__ tok, float temperature,
                                                       TopEntry* __restrict__ lists,
                                                       int32_t* __restrict__ counts,
-                                                      RowTop* __restrict__ rowtop) {
+                                                      RowTop* __restrict__ rowtop, int slot_lo,
+                                                      int slot_span,
+                                                      const int32_t* __restrict__ state,
+                                                      int phase) {
     __shared__ unsigned long long wbuf[kWavesPerBlock][kWaveCap];
     __shared__ int32_t qi_all[kWavesPerBlock][kQueue];
     __shared__ float lmax[kBlock];
@@ -410,7 +414,15 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(4))) voi
     __shared__ float t_guess, t_safe;
     __shared__ double red[kWavesPerBlock];
     constexpr int EV = E::kVec;
-    const int task = blockIdx.x;
+    // chain: block -> (sequence, slot in [slot_lo, slot_lo + slot_span), side);
+    // the row's task number keeps the layout of the whole window
+    int task = blockIdx.x;
+    if (chain) {
+        const int r = (int)blockIdx.x >> 1;
+        const int b = r / slot_span;
+        if (state != nullptr && state[b] != phase) return;     // decided in an earlier phase
+        task = ((b * (K_max + 1) + slot_lo + r % slot_span) << 1) | ((int)blockIdx.x & 1);
+    }
     const typename E::raw* row = topk_row<E>(tgt, dft, cu, K_max, V, task, chain != 0);
     if (row == nullptr) return;
     const int tid = threadIdx.x;
@@ -606,7 +618,7 @@ __global__ __launch_bounds__(kBlock) void k_chain_topk_decide(
     int B, int K_max, int V, int topk, float temperature, int32_t* __restrict__ A_out,
     int32_t* __restrict__ next_out, float* __restrict__ probs_out, float* __restrict__ R_out,
     int32_t* __restrict__ status_out, const int32_t* __restrict__ cap,
-    int32_t* __restrict__ A_full_out) {
+    int32_t* __restrict__ A_full_out, int hi, int32_t* __restrict__ state, int phase) {
     __shared__ double wbuf_all[kWavesPerBlock][kMaxTopk];
     __shared__ int ibuf_all[kWavesPerBlock][kMaxTopk];
     __shared__ TopEntry pl_all[kWavesPerBlock][kMaxTopk];
@@ -615,14 +627,16 @@ __global__ __launch_bounds__(kBlock) void k_chain_topk_decide(
     const int lane = threadIdx.x & (kWave - 1);
     const int b = blockIdx.x * kWavesPerBlock + w;
     if (b >= B) return;
+    if (phase > 0 && state[b] != phase) return;        // decided in an earlier phase
     const int slots = K_max + 1;
     int d0, k;
     seq_range(cu, b, K_max, d0, k);
     const double T = (double)temperature;
     auto task_of = [&](int s, int side) { return (((int64_t)b * slots + s) * 2 + side); };
+    const int kk = k < hi ? k : hi;                     // positions whose rows are ready
     bool acc = true;
     int st = 0;
-    if (lane < k) {
+    if (lane < kk) {
         const RowTop rp = rowtop[task_of(lane, 0)];
         const RowTop rq = rowtop[task_of(lane, 1)];
         const int y = tok[d0 + lane];
@@ -637,6 +651,12 @@ __global__ __launch_bounds__(kBlock) void k_chain_topk_decide(
         }
     }
     const unsigned long long rej = __ballot(!acc);
+    // state[b]: p + 1 while undecided after phase p, -(p + 1) once decided in it
+    if (rej == 0ull && k >= hi) {                       // every position so far passed: next phase
+        if (lane == 0) state[b] = phase + 1;
+        return;
+    }
+    if (state != nullptr && lane == 0) state[b] = -(phase + 1);
     const int A_full = rej ? (__ffsll(rej) - 1) : k;
     const int kc = committed_len(cap, b, k);
     const int A = A_full < kc ? A_full : kc;
@@ -861,45 +881,67 @@ struct TopkLayout {
     RowTop* rowtop;
 };
 
-static size_t topk_layout(void* ws, size_t tasks, int topk, TopkLayout* L) {
+// Carves the workspace: per row task its kept list, count and statistics,
+// then `n_state` int32 (the per-sequence phase state). Returns the state
+// buffer; *bytes, if given, receives the total size.
+static int32_t* topk_layout(void* ws, size_t tasks, int topk, TopkLayout* L, size_t n_state,
+                            size_t* bytes = nullptr) {
     Carve cv;
     const size_t o_lists = cv.take(tasks * topk * sizeof(TopEntry));
     const size_t o_counts = cv.take(tasks * sizeof(int32_t));
     const size_t o_rowtop = cv.take(tasks * sizeof(RowTop));
-    if (L) {
-        char* w = static_cast<char*>(ws);
-        L->lists = reinterpret_cast<TopEntry*>(w + o_lists);
-        L->counts = reinterpret_cast<int32_t*>(w + o_counts);
-        L->rowtop = reinterpret_cast<RowTop*>(w + o_rowtop);
-    }
-    return cv.off;
+    const size_t o_state = cv.take(n_state * sizeof(int32_t));
+    if (bytes) *bytes = cv.off;
+    if (L == nullptr) return nullptr;
+    char* w = static_cast<char*>(ws);
+    L->lists = reinterpret_cast<TopEntry*>(w + o_lists);
+    L->counts = reinterpret_cast<int32_t*>(w + o_counts);
+    L->rowtop = reinterpret_cast<RowTop*>(w + o_rowtop);
+    return reinterpret_cast<int32_t*>(w + o_state);
 }
 
 size_t chain_topk_ws_bytes(int B, int K_max, int V, int top_k) {
     (void)V;
-    return topk_layout(nullptr, (size_t)B * (K_max + 1) * 2, top_k, nullptr);
+    size_t n = 0;
+    topk_layout(nullptr, (size_t)B * (K_max + 1) * 2, top_k, nullptr, (size_t)B, &n);
+    return n;
 }
 
 size_t tree_build_ws_bytes(int B, int K, int V, int N) {
     const int W = (N - 1) < V ? (N - 1) : V;
-    return topk_layout(nullptr, (size_t)B * K, W, nullptr);
+    size_t n = 0;
+    topk_layout(nullptr, (size_t)B * K, W, nullptr, 0, &n);
+    return n;
 }
 
 template <class E, bool VEC>
 static hipError_t chain_topk_impl(const ChainArgs& a) {
     const size_t tasks = (size_t)a.B * (a.K_max + 1) * 2;
     TopkLayout L;
-    topk_layout(a.ws, tasks, a.top_k, &L);
+    int32_t* phase_state = topk_layout(a.ws, tasks, a.top_k, &L, (size_t)a.B);
     using raw = typename E::raw;
-    PassTimer::mark_before(a.stream);
-    hipLaunchKernelGGL((k_topk_rows<E, VEC>), dim3((unsigned)tasks), dim3(kBlock), 0, a.stream,
-                       static_cast<const raw*>(a.target), static_cast<const raw*>(a.draft), a.cu,
-                       a.K_max, a.V, a.top_k, 1, a.tokens, a.temperature, L.lists, L.counts, L.rowtop);
-    PassTimer::mark_after(a.stream);
-    hipLaunchKernelGGL(k_chain_topk_decide, dim3((unsigned)((a.B + kWavesPerBlock - 1) / kWavesPerBlock)),
-                       dim3(kBlock), 0, a.stream, L.lists, L.rowtop, a.tokens, a.uniforms, a.cu, a.B,
-                       a.K_max, a.V, a.top_k, a.temperature, a.accepted_len, a.next_token, a.probs_out,
-                       a.resid_mass_out, a.seq_status, a.cap, a.accepted_full);
+    // Positions in two phases, as in the full-vocabulary path: slots 0-1 of
+    // every sequence, then the rest only where both first drafts passed.
+    const bool phased = a.probs_out == nullptr && a.cap == nullptr && a.accepted_full == nullptr &&
+                        kTopkPhaseSplit < a.K_max + 1;
+    const int bounds[3] = {0, phased ? kTopkPhaseSplit : a.K_max + 1, a.K_max + 1};
+    const int n_phases = phased ? 2 : 1;
+    int32_t* state = phased ? phase_state : nullptr;
+    const unsigned seq_blocks = (unsigned)((a.B + kWavesPerBlock - 1) / kWavesPerBlock);
+    for (int ph = 0; ph < n_phases; ++ph) {
+        const int lo = bounds[ph], hi = bounds[ph + 1];
+        const unsigned grid = (unsigned)((size_t)a.B * (hi - lo) * 2);
+        if (ph == 0) PassTimer::mark_before(a.stream);
+        hipLaunchKernelGGL((k_topk_rows<E, VEC>), dim3(grid), dim3(kBlock), 0, a.stream,
+                           static_cast<const raw*>(a.target), static_cast<const raw*>(a.draft), a.cu,
+                           a.K_max, a.V, a.top_k, 1, a.tokens, a.temperature, L.lists, L.counts,
+                           L.rowtop, lo, hi - lo, ph > 0 ? state : nullptr, ph);
+        if (ph == 0) PassTimer::mark_after(a.stream);
+        hipLaunchKernelGGL(k_chain_topk_decide, dim3(seq_blocks), dim3(kBlock), 0, a.stream, L.lists,
+                           L.rowtop, a.tokens, a.uniforms, a.cu, a.B, a.K_max, a.V, a.top_k,
+                           a.temperature, a.accepted_len, a.next_token, a.probs_out,
+                           a.resid_mass_out, a.seq_status, a.cap, a.accepted_full, hi, state, ph);
+    }
     return hipGetLastError();
 }
 
@@ -918,15 +960,17 @@ hipError_t launch_tree_build(const float* marg, int B, int K, int V, int N, int3
     const int W = (N - 1) < V ? (N - 1) : V;
     const size_t tasks = (size_t)B * K;
     TopkLayout L;
-    topk_layout(ws, tasks, W, &L);
+    topk_layout(ws, tasks, W, &L, 0);
     PassTimer::mark_before(stream);
     if (tasks > 0) {
         if (V % F32::kVec == 0)
             hipLaunchKernelGGL((k_topk_rows<F32, true>), dim3((unsigned)tasks), dim3(kBlock), 0, stream,
-                               marg, marg, nullptr, 0, V, W, 0, nullptr, 1.0f, L.lists, L.counts, nullptr);
+                               marg, marg, nullptr, 0, V, W, 0, nullptr, 1.0f, L.lists, L.counts, nullptr,
+                               0, 1, nullptr, 0);
         else
             hipLaunchKernelGGL((k_topk_rows<F32, false>), dim3((unsigned)tasks), dim3(kBlock), 0, stream,
-                               marg, marg, nullptr, 0, V, W, 0, nullptr, 1.0f, L.lists, L.counts, nullptr);
+                               marg, marg, nullptr, 0, V, W, 0, nullptr, 1.0f, L.lists, L.counts, nullptr,
+                               0, 1, nullptr, 0);
     }
     PassTimer::mark_after(stream);
     hipLaunchKernelGGL(k_tree_build, dim3(B), dim3(kWave), 0, stream, L.lists, L.counts, K, N, W, tok,

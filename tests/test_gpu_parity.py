@@ -189,9 +189,10 @@ def test_greedy_ties_and_nan():
 def test_topk_small_all_sequences(top_k, V):
     _say(f"top-k {top_k} V={V}")
     case = wl.gen_config3(device="cuda", seed=77 + top_k, B=12, K=4, V=V, top_k=top_k)
-    out = run_chain(case)
-    info = compare_chain(out, oracle_chain(case))
-    _say(f"  {info}")
+    ref = oracle_chain(case)
+    for probs in (True, False):
+        info = compare_chain(run_chain(case, probs), ref)
+        _say(f"  probs={probs}: {info}")
 
 
 def test_topk_ties_at_kth_value():
@@ -254,6 +255,10 @@ def test_config3_topk_full_sampled():
     info = compare_chain(out, oracle_chain(case, seqs))
     A = out["accepted_len"].float().mean().item()
     _say(f"  {info} mean A={A:.3f}")
+    # the benchmark's call (no per-position probabilities): verified in phases
+    o2 = run_chain(case, False)
+    for key in ("accepted_len", "next_token", "status", "resid"):
+        assert torch.equal(o2[key], out[key]), key
 
 
 # --------------------------------------------------------------------------
