@@ -25,6 +25,16 @@ struct ArgPartial {
 };
 constexpr int32_t kNone = 0x7fffffff;
 constexpr int kArgUnroll = 4;
+// Tokens per argmax workgroup: short rows of few sequences still give the
+// launch thousands of workgroups.
+#ifndef SD_ARG_CHUNK_BF16
+#define SD_ARG_CHUNK_BF16 32768
+#endif
+#ifndef SD_ARG_CHUNK_F32
+#define SD_ARG_CHUNK_F32 16384
+#endif
+inline int arg_chunk(int dtype) { return dtype == 1 ? SD_ARG_CHUNK_BF16 : SD_ARG_CHUNK_F32; }
+inline int arg_chunks(int V, int dtype) { return (V + arg_chunk(dtype) - 1) / arg_chunk(dtype); }
 
 __device__ __forceinline__ bool arg_better(float v, int i, float bv, int bi) {
     // (value desc, index asc); an empty candidate (kNone) never wins
@@ -66,41 +76,54 @@ __global__ __launch_bounds__(kBlock) void k_argmax(const typename E::raw* __rest
     const int nvec = (end - beg + EV - 1) / EV;
     float best = -INFINITY;
     int bidx = kNone;
-    for (int v0 = threadIdx.x; v0 < nvec; v0 += kBlock * U) {
-        float f[U][EV];
+    // the best of one vector's elements, first index on ties; NaN-only
+    // vectors leave vmax NaN and never win
+    auto consider = [&](const float (&f)[EV], int vi) {
+        float vmax = f[0];
 #pragma unroll
-        for (int u = 0; u < U; ++u) {
-            const int vi = v0 + u * kBlock;
-            if (VEC) {
-                E::unpack(vi < nvec ? load16(rp + beg, vi) : E::neg_inf(), f[u]);
-            } else {
+        for (int e = 1; e < EV; ++e) vmax = nmax(vmax, f[e]);
+        if (vmax > best || (bidx == kNone && vmax == vmax)) {
+            int e_hit = EV - 1;
 #pragma unroll
-                for (int e = 0; e < EV; ++e) {
-                    const int j = beg + vi * EV + e;
-                    f[u][e] = (vi < nvec && j < end) ? E::at(rp, j) : NAN;
-                }
+            for (int e = EV - 1; e >= 0; --e)
+                if (f[e] == vmax) e_hit = e;
+            const int j = beg + vi * EV + e_hit;
+            if (j < end) {
+                best = vmax;
+                bidx = j;
             }
         }
+    };
+    // whole steps: unchecked loads, the next step in flight
+    constexpr int kStep = kBlock * U;
+    const int nsteps = VEC ? nvec / kStep : 0;
+    pipelined_steps<U>(
+        nsteps,
+        [&](uint4 (&buf)[U], int st) {
 #pragma unroll
-        for (int u = 0; u < U; ++u) {
-            const int vi = v0 + u * kBlock;
-            float vmax = f[u][0];
+            for (int u = 0; u < U; ++u) buf[u] = load16(rp + beg, st * kStep + u * kBlock + threadIdx.x);
+        },
+        [&](const uint4 (&buf)[U], int st) {
 #pragma unroll
-            for (int e = 1; e < EV; ++e) vmax = nmax(vmax, f[u][e]);
-            // NaN-only vectors leave vmax NaN and never win; the -inf padding
-            // past the range has index >= end and is ignored below.
-            if (vi < nvec && (vmax > best || (bidx == kNone && vmax == vmax))) {
-                int e_hit = EV - 1;
+            for (int u = 0; u < U; ++u) {
+                float f[EV];
+                E::unpack(buf[u], f);
+                consider(f, st * kStep + u * kBlock + threadIdx.x);
+            }
+        });
+    // the ragged end (all of it in the element-wise path)
+    for (int vi = nsteps * kStep + threadIdx.x; vi < nvec; vi += kBlock) {
+        float f[EV];
+        if (VEC) {
+            E::unpack(load16(rp + beg, vi), f);
+        } else {
 #pragma unroll
-                for (int e = EV - 1; e >= 0; --e)
-                    if (f[u][e] == vmax) e_hit = e;
-                const int j = beg + vi * EV + e_hit;
-                if (j < end) {
-                    best = vmax;
-                    bidx = j;
-                }
+            for (int e = 0; e < EV; ++e) {
+                const int j = beg + vi * EV + e;
+                f[e] = j < end ? E::at(rp, j) : NAN;
             }
         }
+        consider(f, vi);
     }
     // wave then block reduction of (value desc, index asc)
 #pragma unroll
@@ -227,13 +250,13 @@ __global__ __launch_bounds__(kWave) void k_tree_walk(
 
 size_t greedy_ws_bytes(int B, int K_max, int V, int dtype) {
     Carve cv;
-    cv.take((size_t)B * (K_max + 1) * n_chunks_for(V, dtype) * sizeof(ArgPartial));
+    cv.take((size_t)B * (K_max + 1) * arg_chunks(V, dtype) * sizeof(ArgPartial));
     return cv.off;
 }
 
 size_t tree_verify_ws_bytes(int B, int N, int V, int dtype) {
     Carve cv;
-    cv.take((size_t)B * N * n_chunks_for(V, dtype) * sizeof(ArgPartial));
+    cv.take((size_t)B * N * arg_chunks(V, dtype) * sizeof(ArgPartial));
     return cv.off;
 }
 
@@ -241,8 +264,8 @@ template <class E, bool VEC>
 static hipError_t greedy_impl(const void* target, const int32_t* tokens, const int32_t* cu, int B,
                               int K_max, int V, int dtype, int32_t* A, int32_t* next, int32_t* st,
                               const int32_t* cap, int32_t* A_full, void* ws, hipStream_t stream) {
-    const int nc = n_chunks_for(V, dtype);
-    const int chunk = chunk_elems(dtype);
+    const int nc = arg_chunks(V, dtype);
+    const int chunk = arg_chunk(dtype);
     ArgPartial* part = static_cast<ArgPartial*>(ws);
     const unsigned grid = (unsigned)((size_t)B * (K_max + 1) * nc);
     PassTimer::mark_before(stream);
@@ -277,8 +300,8 @@ template <class E, bool VEC>
 static hipError_t tree_verify_impl(const void* target, const int32_t* tok, const int32_t* par,
                                    const int32_t* nn, int B, int N, int V, int dtype, int32_t* path,
                                    int32_t* A, int32_t* next, void* ws, hipStream_t stream) {
-    const int nc = n_chunks_for(V, dtype);
-    const int chunk = chunk_elems(dtype);
+    const int nc = arg_chunks(V, dtype);
+    const int chunk = arg_chunk(dtype);
     ArgPartial* part = static_cast<ArgPartial*>(ws);
     const unsigned grid = (unsigned)((size_t)B * N * nc);
     PassTimer::mark_before(stream);
