@@ -46,6 +46,7 @@ constexpr int kU = SD_STATS_UNROLL;
 #endif
 constexpr int kPhaseBounds[] = {SD_PHASE_BOUNDS};
 constexpr int kMaxPhases = (int)(sizeof(kPhaseBounds) / sizeof(int)) + 1;
+constexpr size_t kPhaseMinElems = size_t(1) << 24;     // logits in the window
 // A one-pass chunk sum is kept only below 2^64 (its reference was then close
 // enough to the chunk's maximum); otherwise the exact two-pass path runs.
 constexpr double kFastSumLimit = 18446744073709551616.0;
@@ -726,7 +727,10 @@ static hipError_t chain_full_impl(const ChainArgs& a) {
     // Positions are verified in phases: a sequence whose draft is rejected in
     // an early phase never streams its later rows. One phase when every
     // position's p(y), q(y) or the full-window rejection is asked for.
-    const bool phased = a.probs_out == nullptr && a.cap == nullptr && a.accepted_full == nullptr;
+    // (only for batches large enough to be bandwidth-bound: below that the
+    // extra launches cost more than the rows they save)
+    const bool phased = a.probs_out == nullptr && a.cap == nullptr && a.accepted_full == nullptr &&
+                        (size_t)a.B * (a.K_max + 1) * a.V >= kPhaseMinElems;
     const unsigned seq_blocks = (unsigned)((a.B + kSeqPerBlock - 1) / kSeqPerBlock);
     int bounds[kMaxPhases + 1];
     int n_phases = 0;

@@ -72,6 +72,7 @@ constexpr int kTopkSample = 8;           // vectors per thread held in registers
 constexpr int kTopkU = 4;                // vectors per thread per main-pass step (as many more in flight)
 constexpr int kWaveCap = 512;            // per-wave candidate buffer (64-bit keys)
 constexpr int kTopkPhaseSplit = 2;       // slots streamed before the first decision
+constexpr size_t kTopkPhaseMinElems = size_t(1) << 24;   // smaller windows: one phase
 constexpr int kQueue = kTopkSample * kWave;   // per-wave queue of vector indices that may hold a candidate
 static_assert(kQueue >= kWave * kTopkU, "one offer step must fit an empty queue");
 
@@ -923,7 +924,8 @@ static hipError_t chain_topk_impl(const ChainArgs& a) {
     // Positions in two phases, as in the full-vocabulary path: slots 0-1 of
     // every sequence, then the rest only where both first drafts passed.
     const bool phased = a.probs_out == nullptr && a.cap == nullptr && a.accepted_full == nullptr &&
-                        kTopkPhaseSplit < a.K_max + 1;
+                        kTopkPhaseSplit < a.K_max + 1 &&
+                        (size_t)a.B * (a.K_max + 1) * a.V >= kTopkPhaseMinElems;
     const int bounds[3] = {0, phased ? kTopkPhaseSplit : a.K_max + 1, a.K_max + 1};
     const int n_phases = phased ? 2 : 1;
     int32_t* state = phased ? phase_state : nullptr;

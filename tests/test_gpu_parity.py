@@ -43,26 +43,56 @@ def test_config1_chain_f32():
     _say(f"  {info}")
 
 
-@pytest.mark.parametrize("probs", [True, False])
 @pytest.mark.parametrize("dtype,V,T", [("bf16", 40000, 0.9), ("bf16", 16384 * 2 + 8, 1.0),
                                        ("f32", 20000, 1.3), ("f32", 1001, 1.0), ("bf16", 777, 0.6)])
-def test_chain_small_all_sequences(dtype, V, T, probs):
-    _say(f"chain small {dtype} V={V} T={T} probs={probs}")
+def test_chain_small_all_sequences(dtype, V, T):
+    _say(f"chain small {dtype} V={V} T={T}")
     case = wl.gen_base_noise_chain(11 + V, B=24, K=5, V=V, base_sigma=2.0, noise_sigma=0.6,
                                    temperature=T, dtype=dtype, device="cuda")
-    out = run_chain(case, probs)
+    out = run_chain(case)
     info = compare_chain(out, oracle_chain(case))
     _say(f"  {info}")
     A = out["accepted_len"].cpu().numpy()
     assert (A < case.K_max).any()
 
 
-@pytest.mark.parametrize("probs", [True, False])
-def test_chain_packed_ragged_lengths(probs):
+# Windows of at least 2^24 logits are verified in phases when no per-position
+# probabilities are asked for (smaller ones in one pass); these cases are sized
+# to take the phased path, and are checked against the oracle and against the
+# one-pass call.
+@pytest.mark.parametrize("dtype,V,T,B", [("bf16", 40000, 0.9, 96), ("bf16", 16384 * 2 + 8, 1.0, 96),
+                                         ("f32", 20000, 1.3, 160)])
+def test_chain_phased_all_sequences(dtype, V, T, B):
+    K = 5
+    assert B * (K + 1) * V >= 1 << 24
+    _say(f"chain phased {dtype} V={V} T={T} B={B}")
+    case = wl.gen_base_noise_chain(13 + V, B=B, K=K, V=V, base_sigma=2.0, noise_sigma=0.6,
+                                   temperature=T, dtype=dtype, device="cuda")
+    one = run_chain(case)
+    ph = run_chain(case, probs=False)
+    for key in ("accepted_len", "next_token", "status", "resid"):
+        assert torch.equal(one[key], ph[key]), key
+    info = compare_chain(ph, oracle_chain(case, sample_seqs(B, 32, seed=V)))
+    _say(f"  {info}")
+
+
+def test_chain_phased_ragged():
+    lengths = [0, 3, 1, 5, 0, 2, 8, 4, 1, 0, 6, 7, 8, 8, 2, 2, 3, 8, 1, 5]
+    V = 100000
+    assert len(lengths) * 9 * V >= 1 << 24
+    case = wl.ragged_chain(7, lengths, V, dtype="bf16", device="cuda")
+    one = run_chain(case)
+    ph = run_chain(case, probs=False)
+    for key in ("accepted_len", "next_token", "status", "resid"):
+        assert torch.equal(one[key], ph[key]), key
+    compare_chain(ph, oracle_chain(case))
+
+
+def test_chain_packed_ragged_lengths():
     lengths = [0, 3, 1, 5, 0, 2, 8, 4, 1, 0, 6, 7]
-    _say(f"packed chain lengths {lengths} probs={probs}")
+    _say(f"packed chain lengths {lengths}")
     case = wl.ragged_chain(5, lengths, 30000, dtype="bf16", device="cuda")
-    out = run_chain(case, probs)
+    out = run_chain(case)
     info = compare_chain(out, oracle_chain(case))
     _say(f"  {info}")
     # a packed call matches the dense call of the same rows sequence by sequence
@@ -73,15 +103,17 @@ def test_chain_packed_ragged_lengths(probs):
                            draft=case.draft[cu[b]: cu[b + 1]].contiguous(),
                            tokens=case.tokens[cu[b]: cu[b + 1]].contiguous(),
                            uniforms=case.uniforms[cu[b] + b: cu[b + 1] + b + 1].contiguous())
-        o1 = run_chain(sub, probs)
+        o1 = run_chain(sub)
         assert int(o1["accepted_len"][0]) == int(out["accepted_len"][b])
         assert int(o1["next_token"][0]) == int(out["next_token"][b])
 
 
 @pytest.mark.parametrize("probs", [True, False])
 def test_chain_edge_cases(probs):
+    # 64 sequences x 4 rows x 65536 = 2^24 logits: without probabilities the
+    # window is verified in phases
     _say(f"chain edge cases probs={probs}")
-    V, K, B = 4096, 3, 6
+    V, K, B = 65536, 3, 64
     g = torch.Generator(device="cuda").manual_seed(3)
     tgt = torch.randn(B * (K + 1), V, generator=g, device="cuda") * 2
     dft = torch.randn(B * K, V, generator=g, device="cuda") * 2
@@ -96,7 +128,7 @@ def test_chain_edge_cases(probs):
     # seq 3: -inf except one entry in its target row 1, and a -inf-only draft chunk region
     tgt[3 * (K + 1) + 1] = float("-inf")
     tgt[3 * (K + 1) + 1, 17] = 0.0
-    dft[3 * K + 2, :2048] = float("-inf")
+    dft[3 * K + 2, :40000] = float("-inf")
     # seq 4: +inf in the extra-token row
     tgt[4 * (K + 1) + K, 5] = float("inf")
     # seq 5: extreme logits (one-pass reference far below the max)
@@ -114,21 +146,20 @@ def test_chain_edge_cases(probs):
         assert int(out["status"][2]) & sd.SEQ_NONFINITE and int(out["next_token"][2]) == -1
 
 
-@pytest.mark.parametrize("probs", [True, False])
-def test_chain_tiny_vocab_and_k0(probs):
-    _say(f"V=1, K_max=0 and all-zero packed lengths probs={probs}")
+def test_chain_tiny_vocab_and_k0():
+    _say("V=1, K_max=0 and all-zero packed lengths")
     for V in (1, 2, 8):
         for K in (1, 2, 3):
             case = wl.gen_base_noise_chain(1, B=5, K=K, V=V, base_sigma=1.0, noise_sigma=0.5,
                                            temperature=1.0, dtype="f32", device="cuda")
-            compare_chain(run_chain(case, probs), oracle_chain(case))
+            compare_chain(run_chain(case), oracle_chain(case))
     case = wl.gen_base_noise_chain(2, B=7, K=0, V=300, base_sigma=1.0, noise_sigma=0.5,
                                    temperature=1.0, dtype="bf16", device="cuda")
-    compare_chain(run_chain(case, probs), oracle_chain(case))
+    compare_chain(run_chain(case), oracle_chain(case))
     case = wl.ragged_chain(3, [0, 0, 0], 500, dtype="bf16", device="cuda")
-    compare_chain(run_chain(case, probs), oracle_chain(case))
+    compare_chain(run_chain(case), oracle_chain(case))
     case = wl.ragged_chain(4, [1, 2, 3, 2, 1, 0, 9], 700, dtype="bf16", device="cuda")
-    compare_chain(run_chain(case, probs), oracle_chain(case))
+    compare_chain(run_chain(case), oracle_chain(case))
 
 
 def test_chain_run_twice_bit_identical():
@@ -189,10 +220,22 @@ def test_greedy_ties_and_nan():
 def test_topk_small_all_sequences(top_k, V):
     _say(f"top-k {top_k} V={V}")
     case = wl.gen_config3(device="cuda", seed=77 + top_k, B=12, K=4, V=V, top_k=top_k)
-    ref = oracle_chain(case)
-    for probs in (True, False):
-        info = compare_chain(run_chain(case, probs), ref)
-        _say(f"  probs={probs}: {info}")
+    info = compare_chain(run_chain(case), oracle_chain(case))
+    _say(f"  {info}")
+
+
+@pytest.mark.parametrize("top_k", [50, 3])
+def test_topk_phased_all_sequences(top_k):
+    # 64 x 6 x 50000 >= 2^24 logits: without probabilities, verified in phases
+    B, K, V = 64, 5, 50000
+    assert B * (K + 1) * V >= 1 << 24
+    case = wl.gen_config3(device="cuda", seed=91 + top_k, B=B, K=K, V=V, top_k=top_k)
+    one = run_chain(case)
+    ph = run_chain(case, probs=False)
+    for key in ("accepted_len", "next_token", "status", "resid"):
+        assert torch.equal(one[key], ph[key]), key
+    info = compare_chain(ph, oracle_chain(case))
+    _say(f"  top-k {top_k} phased: {info}")
 
 
 def test_topk_ties_at_kth_value():
