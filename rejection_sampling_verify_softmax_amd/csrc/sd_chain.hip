@@ -268,23 +268,38 @@ __global__ __launch_bounds__(kBlock) void k_chain_stats(
 // Row statistics from its chunk partials. References are integers, so each
 // partial is rescaled exactly by a power of two (fixed chunk order, fp64).
 __device__ RowStat combine_row(const Partial* p, int n_chunks) {
+    // the first kReg partials are loaded together (one memory latency)
+    constexpr int kReg = 8;
+    Partial q[kReg];
+#pragma unroll
+    for (int i = 0; i < kReg; ++i)
+        if (i < n_chunks) q[i] = p[i];
     RowStat r;
     r.O = -INFINITY;
     r.S = 0.0;
     r.valid = true;
-    for (int i = 0; i < n_chunks; ++i) {
-        const Partial q = p[i];
-        if (!isfinite(q.S)) r.valid = false;
-        if (q.S > 0.0) r.O = fmaxf(r.O, q.o);
+#pragma unroll
+    for (int i = 0; i < kReg; ++i)
+        if (i < n_chunks) {
+            if (!isfinite(q[i].S)) r.valid = false;
+            if (q[i].S > 0.0) r.O = fmaxf(r.O, q[i].o);
+        }
+    for (int i = kReg; i < n_chunks; ++i) {
+        const Partial t = p[i];
+        if (!isfinite(t.S)) r.valid = false;
+        if (t.S > 0.0) r.O = fmaxf(r.O, t.o);
     }
     if (!r.valid || r.O == -INFINITY) {
         r.valid = false;
         return r;
     }
     double S = 0.0;
-    for (int i = 0; i < n_chunks; ++i) {
-        const Partial q = p[i];
-        if (q.S > 0.0) S += ldexp(q.S, (int)fmaxf(q.o - r.O, -4096.f));
+#pragma unroll
+    for (int i = 0; i < kReg; ++i)
+        if (i < n_chunks && q[i].S > 0.0) S += ldexp(q[i].S, (int)fmaxf(q[i].o - r.O, -4096.f));
+    for (int i = kReg; i < n_chunks; ++i) {
+        const Partial t = p[i];
+        if (t.S > 0.0) S += ldexp(t.S, (int)fmaxf(t.o - r.O, -4096.f));
     }
     r.S = S;
     r.valid = isfinite(S) && S > 0.0;
@@ -558,26 +573,36 @@ __global__ __launch_bounds__(kBlock) void k_chain_decide(
     const int lane = threadIdx.x & (kWave - 1);
     if (alive_in && alive[b] == 0) return;              // decided in an earlier phase
     const int slots = K_max + 1;
+    const int64_t slot0 = (int64_t)b * slots;
+    // Lane s combines the partials of slot s (target, and draft below K_max)
+    // for every slot streamed so far; these loads do not wait for cu.
+    const int ns = slots < hi ? slots : hi;
+    RowStat rp{-INFINITY, 0.0, false}, rq{-INFINITY, 0.0, false};
+    float xt = 0.f, xd = 0.f;
+    if (lane < ns) {
+        rp = combine_row(part_t + (slot0 + lane) * n_chunks, n_chunks);
+        if (lane < K_max) {
+            rq = combine_row(part_d + (slot0 + lane) * n_chunks, n_chunks);
+            xt = xy[(slot0 + lane) * 2];
+            xd = xy[(slot0 + lane) * 2 + 1];
+        }
+    }
     int d0, k;
     seq_range(cu, b, K_max, d0, k);
-    const int64_t slot0 = (int64_t)b * slots;
     // positions evaluated so far: those of the slots streamed up to this phase
     const int kk = k < hi ? k : hi;
+    // uniform of position `lane` (lane k_b's is the final draw's for an uncapped window)
+    const float u_lane = lane <= k ? uni[d0 + b + lane] : 0.f;
     bool acc = true;
     int st = 0;
-    RowStat rp{-INFINITY, 0.0, false}, rq{-INFINITY, 0.0, false};
     if (lane < kk) {
-        rp = combine_row(part_t + (slot0 + lane) * n_chunks, n_chunks);
-        rq = combine_row(part_d + (slot0 + lane) * n_chunks, n_chunks);
         const int y = tok[d0 + lane];
         const bool yok = (y >= 0 && y < V);
         double py = 0.0, qy = 0.0;
         // the summed terms' fp32 reference, evaluated exactly in fp64
-        if (yok && rp.valid)
-            py = exp2((double)xy[(slot0 + lane) * 2] * (double)c - (double)rp.O) / rp.S;
-        if (yok && rq.valid)
-            qy = exp2((double)xy[(slot0 + lane) * 2 + 1] * (double)c - (double)rq.O) / rq.S;
-        const double u = (double)uni[d0 + b + lane];
+        if (yok && rp.valid) py = exp2((double)xt * (double)c - (double)rp.O) / rp.S;
+        if (yok && rq.valid) qy = exp2((double)xd * (double)c - (double)rq.O) / rq.S;
+        const double u = (double)u_lane;
         acc = rp.valid && rq.valid && yok && py > 0.0 && u * qy <= py;
         st = (yok ? 0 : 1) | ((rp.valid && rq.valid) ? 0 : 2);
         if (probs_out) {
@@ -599,7 +624,8 @@ __global__ __launch_bounds__(kBlock) void k_chain_decide(
     for (int o = kWave / 2; o > 0; o >>= 1) mine |= __shfl_xor(mine, o, kWave);
     ChainDesc d;
     d.A = A;
-    d.u = uni[d0 + b + kc];
+    // (a 64-position window puts its final uniform and extra row past the lanes)
+    d.u = kc < kWave ? __shfl(u_lane, kc, kWave) : uni[d0 + b + kc];
     d.pad = 0.f;
     if (A < kc) {
         const float Op = __shfl(rp.O, A, kWave);
@@ -616,7 +642,15 @@ __global__ __launch_bounds__(kBlock) void k_chain_decide(
         d.O_q = Oq;
         d.S_q = Sq;
     } else {
-        const RowStat rb = combine_row(part_t + (slot0 + kc) * n_chunks, n_chunks);
+        // the extra-token row: slot kc, streamed in this phase (kc <= k < hi)
+        RowStat rb;
+        if (kc < kWave) {
+            rb.O = __shfl(rp.O, kc, kWave);
+            rb.S = __shfl(rp.S, kc, kWave);
+            rb.valid = __shfl((int)rp.valid, kc, kWave) != 0;
+        } else {
+            rb = combine_row(part_t + (slot0 + kc) * n_chunks, n_chunks);
+        }
         d.mode = rb.valid ? kModeExtra : kModeNone;
         if (!rb.valid) mine |= 2;
         d.t_row = d0 + b + kc;

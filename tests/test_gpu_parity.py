@@ -162,6 +162,34 @@ def test_chain_tiny_vocab_and_k0():
     compare_chain(run_chain(case), oracle_chain(case))
 
 
+@pytest.mark.parametrize("mode", ["full", "topk", "greedy"])
+def test_chain_window_of_64_positions(mode):
+    # K_max = 64, the largest window: its final uniform and extra-token row sit
+    # at position 64, past the 64 lanes of the deciding wave
+    B, K, V = 3, 64, 600
+    T = 0.0 if mode == "greedy" else 1.0
+    case = wl.gen_base_noise_chain(41, B=B, K=K, V=V, base_sigma=2.0, noise_sigma=0.5,
+                                   temperature=max(T, 1.0), dtype="f32", device="cuda")
+    tgt = case.target.view(B, K + 1, V).clone()
+    dft = case.draft.view(B, K, V)
+    tgt[0, :K] = dft[0]                                   # sequence 0 accepts all 64 drafts
+    if mode == "greedy":
+        tok = case.tokens.view(B, K).clone()
+        tok[0] = torch.argmax(tgt[0, :K], dim=-1).to(torch.int32)
+        case.tokens = tok.reshape(-1).contiguous()
+    case.target = tgt.reshape(B * (K + 1), V).contiguous()
+    case.temperature = T
+    case.top_k = 20 if mode == "topk" else 0
+    if mode == "topk":
+        # sequence 0's drafts must come from the kept set: re-draw them
+        g = torch.Generator(device="cuda").manual_seed(3)
+        case.tokens = wl.gumbel_draft_tokens(case.draft, 1.0, 20, g)
+    out = run_chain(case, probs=mode != "greedy")
+    ref = oracle_chain(case)
+    compare_chain(out, ref, check_probs=mode != "greedy", check_resid=mode != "greedy")
+    assert int(out["accepted_len"][0]) == K
+
+
 def test_chain_run_twice_bit_identical():
     case = wl.gen_base_noise_chain(9, B=16, K=6, V=50000, base_sigma=2.0, noise_sigma=0.7,
                                    temperature=1.0, dtype="bf16", device="cuda")
