@@ -342,17 +342,6 @@ __device__ __forceinline__ float lane_weight_sum(const float (&fp)[E::kVec], con
     return s;
 }
 
-__device__ __forceinline__ double wave_excl_scan(double v) {
-    const int lane = threadIdx.x & (kWave - 1);
-    double incl = v;
-#pragma unroll
-    for (int o = 1; o < kWave; o <<= 1) {
-        const double t = __shfl_up(incl, o, kWave);
-        if (lane >= o) incl += t;
-    }
-    return incl - v;
-}
-
 constexpr int kResolveThreads = kBlock;
 constexpr int kMassChunkVecs = 4096;      // 16-byte vectors per mass workgroup
 constexpr int kResolveWaves = kResolveThreads / kWave;

@@ -120,6 +120,18 @@ __device__ __forceinline__ int wave_max_int(int v) {
     return v;
 }
 
+// Exclusive prefix sum across the wave (lane order).
+__device__ __forceinline__ double wave_excl_scan(double v) {
+    const int lane = threadIdx.x & (kWave - 1);
+    double incl = v;
+#pragma unroll
+    for (int o = 1; o < kWave; o <<= 1) {
+        const double t = __shfl_up(incl, o, kWave);
+        if (lane >= o) incl += t;
+    }
+    return incl - v;
+}
+
 // Block-wide reductions for kBlock threads; `scratch` holds kWavesPerBlock entries.
 // Every thread receives the result. Contains __syncthreads().
 __device__ inline double block_sum(double v, double* scratch) {

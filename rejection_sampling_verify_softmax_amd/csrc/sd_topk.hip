@@ -589,30 +589,57 @@ __device__ int list_inverse_cdf(const TopEntry* P, const RowTop& sp, const TopEn
         ibuf[rank] = id;
     }
     wave_lds_sync();
-    int pick = -1;
-    double R = 0.0;
-    if (lane == 0) {
-        for (int i = 0; i < np; ++i) R += wbuf[i];
-        const double target = u * R;
-        double C = 0.0;
-        int last = -1;
-        for (int i = 0; i < np; ++i) {
-            C += wbuf[i];
-            if (wbuf[i] > 0.0) last = ibuf[i];
-            if (C > target && wbuf[i] > 0.0) {
-                pick = ibuf[i];
-                break;
-            }
-        }
-        if (pick < 0) pick = last;
+    // inverse CDF over the id-sorted weights: lane l holds entries 4l .. 4l+3
+    // (np <= 256); lane sums, a wave prefix sum, then the first entry whose
+    // running mass exceeds u * R (else the last entry with positive mass)
+    double w4[4];
+    double ls = 0.0;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+        const int i = 4 * lane + e;
+        w4[e] = i < np ? wbuf[i] : 0.0;
+        ls += w4[e];
     }
+    const double before = wave_excl_scan(ls);
+    const double R = __shfl(before + ls, kWave - 1, kWave);
+    const double target = u * R;
+    int hit = -1, last = -1;
+    double C = before;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+        C += w4[e];
+        if (w4[e] > 0.0) {
+            last = 4 * lane + e;
+            if (hit < 0 && C > target) hit = 4 * lane + e;
+        }
+    }
+    const unsigned long long hb = __ballot(hit >= 0);
+    int at;
+    if (hb) {
+        at = __shfl(hit, __ffsll(hb) - 1, kWave);
+    } else {
+        at = last;
+#pragma unroll
+        for (int o = kWave / 2; o > 0; o >>= 1) at = max(at, __shfl_xor(at, o, kWave));
+    }
+    const int pick = at >= 0 ? ibuf[at] : -1;
     wave_lds_sync();
-    *R_out = __shfl(R, 0, kWave);
-    return __shfl(pick, 0, kWave);
+    *R_out = R;
+    return pick;
 }
 
 // One wave per sequence: accept bits from the rows' p(y) and q(y) (computed by
 // the row pass), A (ballot), and the final token from the decision row's lists.
+__device__ __forceinline__ RowTop shfl_rowtop(const RowTop& r, int src) {
+    RowTop o;
+    o.count = __shfl(r.count, src, kWave);
+    o.valid = __shfl(r.valid, src, kWave);
+    o.m = __shfl(r.m, src, kWave);
+    o.S = __shfl(r.S, src, kWave);
+    o.py = __shfl(r.py, src, kWave);
+    return o;
+}
+
 __global__ __launch_bounds__(kBlock) void k_chain_topk_decide(
     const TopEntry* __restrict__ lists, const RowTop* __restrict__ rowtop,
     const int32_t* __restrict__ tok, const float* __restrict__ uni, const int32_t* __restrict__ cu,
@@ -630,16 +657,22 @@ __global__ __launch_bounds__(kBlock) void k_chain_topk_decide(
     if (b >= B) return;
     if (phase > 0 && state[b] != phase) return;        // decided in an earlier phase
     const int slots = K_max + 1;
-    int d0, k;
-    seq_range(cu, b, K_max, d0, k);
     const double T = (double)temperature;
     auto task_of = [&](int s, int side) { return (((int64_t)b * slots + s) * 2 + side); };
+    // lane s reads the statistics of slot s's rows (every slot streamed so
+    // far); these loads do not wait for cu
+    const int ns = slots < hi ? slots : hi;
+    RowTop rp{0, 0, 0.0, 0.0, 0.0}, rq{0, 0, 0.0, 0.0, 0.0};
+    if (lane < ns) {
+        rp = rowtop[task_of(lane, 0)];
+        if (lane < K_max) rq = rowtop[task_of(lane, 1)];
+    }
+    int d0, k;
+    seq_range(cu, b, K_max, d0, k);
     const int kk = k < hi ? k : hi;                     // positions whose rows are ready
     bool acc = true;
     int st = 0;
     if (lane < kk) {
-        const RowTop rp = rowtop[task_of(lane, 0)];
-        const RowTop rq = rowtop[task_of(lane, 1)];
         const int y = tok[d0 + lane];
         const bool yok = (y >= 0 && y < V);
         const double py = yok ? rp.py : 0.0, qy = yok ? rq.py : 0.0;
@@ -672,8 +705,8 @@ __global__ __launch_bounds__(kBlock) void k_chain_topk_decide(
     TopEntry* pl = pl_all[w];
     TopEntry* dl = dl_all[w];
     if (A < kc) {
-        const RowTop sp = rowtop[task_of(A, 0)];
-        const RowTop sq = rowtop[task_of(A, 1)];
+        const RowTop sp = shfl_rowtop(rp, A);
+        const RowTop sq = shfl_rowtop(rq, A);
         if (sp.valid) {
             next = list_inverse_cdf(lists + task_of(A, 0) * topk, sp, lists + task_of(A, 1) * topk, sq,
                                     true, T, uf, wbuf, ibuf, pl, dl, &R);
@@ -684,7 +717,8 @@ __global__ __launch_bounds__(kBlock) void k_chain_topk_decide(
             }
         }
     } else {
-        const RowTop sp = rowtop[task_of(kc, 0)];
+        // the extra-token row: slot kc (past the lanes only in a 64-position window)
+        const RowTop sp = kc < kWave ? shfl_rowtop(rp, kc) : rowtop[task_of(kc, 0)];
         if (sp.valid) {
             double unused;
             next = list_inverse_cdf(lists + task_of(kc, 0) * topk, sp, nullptr, sp, false, T, uf, wbuf,
