@@ -14,7 +14,7 @@ second, the roofline of the dominant kernel (the streaming pass over the logit
 rows, timed with HIP events on its own stream) and the CPU oracle timed on a
 bounded sample of the same workload.
 
-Other workloads (--workload greedy|topk|tree|chain1) measure the other kernels
+Other workloads (--workload greedy|topk|tree|chain1|kv) measure the other kernels
 for the design notes; their inputs are rotated across copies so that the
 working set exceeds the 256 MB last-level cache.
 """
@@ -198,6 +198,33 @@ def setup_tree(torch, sd, wl):
     return step, meta, None
 
 
+def setup_kv(torch, sd, wl):
+    # accepted-path KV compaction after a tree walk of the tree workload: one
+    # 128 KB row per token (32 layers x 8 KV heads x 128 x (K, V) x bf16)
+    case = wl.gen_config4(device="cuda")
+    tree = sd.build_tree(case.marginals, case.N)
+    walk = sd.verify_tree(case.target_for_depths(tree["depth"], tree["n_nodes"]), tree)
+    B, N, row_bytes = case.B, case.N, 32 * 8 * 128 * 2 * 2
+    n_rows = B * (N - 1)
+    kv = torch.empty(n_rows, row_bytes, dtype=torch.uint8, device="cuda")
+    base = torch.arange(B, dtype=torch.int64, device="cuda") * (N - 1)
+    path, alen = walk["path"], walk["accepted_len"]
+    p, a = path.cpu(), alen.cpu()
+    moved = sum(1 for b in range(B) for i in range(int(a[b])) if int(p[b, i]) - 1 != i)
+
+    def step(ev=None):
+        if ev is not None:
+            sd.time_next_stream_pass(*ev)
+        sd.compact_kv(kv, base, path, alen)
+
+    meta = {"workload": (f"accepted-path KV compaction after the tree walk: B={B}, N={N}, "
+                         f"{row_bytes} B per token row"),
+            "global_batch": B, "positions_per_step": int(a.sum()),
+            "kernel": "k_compact_kv", "kernel_bytes": 2 * moved * row_bytes,
+            "step_bytes": 2 * moved * row_bytes}
+    return step, meta, None
+
+
 def setup_chain1(torch, sd, wl):
     case = wl.gen_config1(device="cuda")
     ws = torch.empty(sd.workspace_bytes(sd.OP_CHAIN, 1, 4, 1000), dtype=torch.uint8, device="cuda")
@@ -215,7 +242,7 @@ def setup_chain1(torch, sd, wl):
 
 
 WORKLOADS = {"adaptive": setup_adaptive, "greedy": setup_greedy, "topk": setup_topk,
-             "tree": setup_tree, "chain1": setup_chain1}
+             "tree": setup_tree, "chain1": setup_chain1, "kv": setup_kv}
 
 
 def run_cpu_baseline(cpu, target_seconds: float):

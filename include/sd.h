@@ -227,6 +227,29 @@ sd_status_t sd_verify_tree(const void* target_logits, sd_dtype_t dtype,
                            void* workspace, size_t workspace_bytes, void* hip_stream);
 
 /*
+ * Accepted-path KV compaction [SD §5 DDTree: after the walk the KV cache keeps
+ * only the accepted path]. `kv` holds n_rows rows of row_bytes bytes each (one
+ * token's keys and values, laid out as the caller likes; row_bytes a positive
+ * multiple of 16, kv 16-byte aligned). Draft node n (1 .. N-1) of sequence b
+ * wrote its row at row_base[b] + n - 1. The accepted path moves in place:
+ * afterwards row row_base[b] + i holds what row row_base[b] + path_nodes[b, i]
+ * - 1 held before the call, for i < accepted_len[b]; no other row changes.
+ * path_nodes / accepted_len are as sd_verify_tree writes them (node ids in walk
+ * order, which grow along a path: the moves rely on it). A sequence whose
+ * draft region [row_base[b], row_base[b] + N - 1) is not inside [0, n_rows) is
+ * left untouched; a path entry outside [1, N-1] is skipped.
+ *
+ *   kv            [n_rows, row_bytes] bytes (device), updated in place
+ *   row_base      [B] int64 (device)
+ *   path_nodes    [B, N] int32 (device)
+ *   accepted_len  [B] int32 (device)
+ * Needs no workspace. Bad sizes or NULL pointers are SD_EINVAL.
+ */
+sd_status_t sd_compact_kv(void* kv, int64_t row_bytes, int64_t n_rows, const int64_t* row_base,
+                          const int32_t* path_nodes, const int32_t* accepted_len, int32_t B,
+                          int32_t N, void* hip_stream);
+
+/*
  * DSpark verify length [SD §5 DSpark]. s_0 = 1, s_j = fl32(s_{j-1} * c_j);
  * k_sel[b] = the largest k with s_j > cost_per_position for every j <= k
  * (for c in [0, 1] this is the smallest k maximising 1 + sum_{j<=k} s_j - cost*k);
@@ -260,8 +283,9 @@ sd_status_t sd_select_len_table(const float* conf, int32_t B, int32_t K_max,
                                 float* expected_advance, int32_t* cu_sel, void* hip_stream);
 
 /*
- * Measurement support. The next sd_verify_chain, sd_verify_greedy,
- * sd_build_tree or sd_verify_tree call made by the calling host thread records
+ * Measurement support. The next sd_verify_chain, sd_verify_chain_capped,
+ * sd_verify_greedy, sd_build_tree, sd_verify_tree or sd_compact_kv call made by
+ * the calling host thread records
  * `start_event` on its stream immediately before its streaming kernel (the one
  * pass over the logit / marginal rows, which dominates its time) and
  * `stop_event` immediately after it; the hook then clears itself. Both are

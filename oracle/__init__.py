@@ -66,6 +66,8 @@ def _load():
     lib.orc_verify_chain_capped.restype = None
     lib.orc_select_len_table.argtypes = [P, I, I, P, P, P, P, P]
     lib.orc_select_len_table.restype = None
+    lib.orc_compact_kv.argtypes = [P, ctypes.c_longlong, ctypes.c_longlong, P, P, P, I, I]
+    lib.orc_compact_kv.restype = None
     _lib = lib
     return lib
 
@@ -222,3 +224,16 @@ def select_len_table(conf, B, K, cost_table):
     _load().orc_select_len_table(_ptr(c), int(B), int(K), _ptr(tab), _ptr(k), _ptr(adv), _ptr(cu),
                                  _ptr(mg))
     return {"k": k, "adv": adv, "cu": cu, "margin": mg}
+
+
+def compact_kv(kv, row_base, path, accepted_len, B, N):
+    """Accepted-path KV compaction on a host copy; kv is a 2-D uint8 array
+    [n_rows, row_bytes]. Returns the compacted copy."""
+    out = np.ascontiguousarray(np.array(kv, dtype=np.uint8, copy=True))
+    n_rows, row_bytes = out.shape
+    rb = np.ascontiguousarray(np.asarray(row_base, dtype=np.int64))
+    p = _i32(path).reshape(-1)
+    a = _i32(accepted_len)
+    _load().orc_compact_kv(_ptr(out), int(row_bytes), int(n_rows), _ptr(rb), _ptr(p), _ptr(a),
+                           int(B), int(N))
+    return out

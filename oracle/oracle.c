@@ -503,6 +503,36 @@ void orc_select_len(const float* conf, int B, int K, float cost, int32_t* k_sel,
 }
 
 /*
+ * Accepted-path KV compaction [SD §5 DDTree: the KV cache keeps only the
+ * accepted path]. kv: n_rows rows of row_bytes bytes; draft node n (1..N-1) of
+ * sequence b sits at row row_base[b] + n - 1. Afterwards row row_base[b] + i
+ * holds what row row_base[b] + path[b*N + i] - 1 held before the call (i <
+ * accepted_len[b]); nothing else changes. Sequences whose draft region is not
+ * inside [0, n_rows) are skipped, as are path entries outside [1, N-1]. Every
+ * source is read from a copy of the rows taken before any move.
+ */
+void orc_compact_kv(unsigned char* kv, long long row_bytes, long long n_rows,
+                    const long long* row_base, const int32_t* path, const int32_t* accepted_len,
+                    int B, int N) {
+    unsigned char* before = (unsigned char*)malloc((size_t)(row_bytes * n_rows));
+    memcpy(before, kv, (size_t)(row_bytes * n_rows));
+    for (int b = 0; b < B; ++b) {
+        long long r0 = row_base[b];
+        int A = accepted_len[b];
+        if (A < 0) A = 0;
+        if (A > N - 1) A = N - 1;
+        if (r0 < 0 || r0 + (N - 1) > n_rows) continue;
+        for (int i = 0; i < A; ++i) {
+            int n = path[(size_t)b * N + i];
+            if (n < 1 || n > N - 1) continue;
+            memcpy(kv + (size_t)((r0 + i) * row_bytes), before + (size_t)((r0 + n - 1) * row_bytes),
+                   (size_t)row_bytes);
+        }
+    }
+    free(before);
+}
+
+/*
  * Verify length with a per-position cost table [SD §5 DSpark: is one more
  * verified position worth its cost]: cost[j-1] is the cost of verifying
  * position j; k* = the smallest k in [0, K] maximising

@@ -70,6 +70,8 @@ def _load():
     lib.sd_verify_chain_capped.restype = ctypes.c_int
     lib.sd_select_len_table.argtypes = [P, I, I, P, P, P, P, P]
     lib.sd_select_len_table.restype = ctypes.c_int
+    lib.sd_compact_kv.argtypes = [P, ctypes.c_int64, ctypes.c_int64, P, P, P, I, I, P]
+    lib.sd_compact_kv.restype = ctypes.c_int
     lib.sd_time_next_stream_pass.argtypes = [P, P]
     lib.sd_time_next_stream_pass.restype = ctypes.c_int
     _lib = lib
@@ -386,3 +388,26 @@ def select_len_table(conf: torch.Tensor, cost_table: torch.Tensor, out: Optional
                                     _stream(stream))
     _raise(r, "sd_select_len_table")
     return {"k": k, "adv": adv, "cu": cu}
+
+
+def compact_kv(kv: torch.Tensor, row_base: torch.Tensor, path: torch.Tensor,
+               accepted_len: torch.Tensor, stream=None) -> torch.Tensor:
+    """sd_compact_kv, in place. kv: contiguous GPU tensor whose first dimension
+    is the row (token) index; row_base [B] int64; path [B, N] int32 and
+    accepted_len [B] int32 as returned by verify_tree. Returns kv."""
+    dev = kv.device
+    _check(kv, "kv", device=dev)
+    _check(row_base, "row_base", torch.int64, dev)
+    _check(path, "path", torch.int32, dev)
+    _check(accepted_len, "accepted_len", torch.int32, dev)
+    if path.dim() != 2:
+        raise ValueError("path must be [B, N]")
+    B, N = (int(x) for x in path.shape)
+    if row_base.numel() != B or accepted_len.numel() != B:
+        raise ValueError("row_base and accepted_len need one entry per sequence")
+    n_rows = int(kv.shape[0])
+    row_bytes = kv.numel() * kv.element_size() // max(n_rows, 1)
+    r = _load().sd_compact_kv(_ptr(kv), row_bytes, n_rows, _ptr(row_base), _ptr(path),
+                              _ptr(accepted_len), B, N, _stream(stream))
+    _raise(r, "sd_compact_kv")
+    return kv

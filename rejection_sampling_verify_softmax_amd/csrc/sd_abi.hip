@@ -246,4 +246,14 @@ sd_status_t sd_select_len_table(const float* conf, int32_t B, int32_t K_max,
                                           cu_sel, static_cast<hipStream_t>(hip_stream)));
 }
 
+sd_status_t sd_compact_kv(void* kv, int64_t row_bytes, int64_t n_rows, const int64_t* row_base,
+                          const int32_t* path_nodes, const int32_t* accepted_len, int32_t B,
+                          int32_t N, void* hip_stream) {
+    if (B < 1 || B > kMaxB || N < 2 || N > SD_MAX_TREE_N) return SD_EINVAL;
+    if (row_bytes < 16 || row_bytes % 16 != 0 || n_rows < 1) return SD_EINVAL;
+    if (!kv || !row_base || !path_nodes || !accepted_len) return SD_EINVAL;
+    return from_hip(sd::launch_compact_kv(kv, row_bytes, n_rows, row_base, path_nodes, accepted_len, B,
+                                          N, static_cast<hipStream_t>(hip_stream)));
+}
+
 }  // extern "C"

@@ -344,6 +344,10 @@ __device__ __forceinline__ float lane_weight_sum(const float (&fp)[E::kVec], con
 
 constexpr int kResolveThreads = kBlock;
 constexpr int kMassChunkVecs = 4096;      // 16-byte vectors per mass workgroup
+#ifndef SD_MASS_UNROLL
+#define SD_MASS_UNROLL 4
+#endif
+constexpr int kMU = SD_MASS_UNROLL;       // pieces per wave per round of the mass pass
 constexpr int kResolveWaves = kResolveThreads / kWave;
 
 // Weight mass of every piece (64 consecutive 16-byte vectors: 512 bf16 or 256
@@ -357,7 +361,7 @@ __device__ void mass_pass(const typename E::raw* tp, const typename E::raw* dp, 
                           const WeightFn& wf, double* pieces, int npieces) {
     constexpr int EV = E::kVec;
     constexpr int T = kResolveThreads;
-    constexpr int step = T * kU;
+    constexpr int step = T * kMU;
     const int nvec = (end - beg + EV - 1) / EV;
     const int w = threadIdx.x / kWave;
     const int lane = threadIdx.x & (kWave - 1);
@@ -365,27 +369,27 @@ __device__ void mass_pass(const typename E::raw* tp, const typename E::raw* dp, 
     const int rounds = (nvec + step - 1) / step;
     const typename E::raw* tb = tp + beg;
     const typename E::raw* db = dp + beg;
-    static_assert(kU == 4, "the piece reduction below sums four pieces at once");
-    // loads of one round: kU vectors of the target row, then kU of the draft row
-    auto fetch = [&](uint4 (&v)[2 * kU], int rd) {
+    static_assert(kMU == 2 || kMU == 4, "the piece reduction sums two or four pieces at once");
+    // loads of one round: kMU vectors of the target row, then kMU of the draft row
+    auto fetch = [&](uint4 (&v)[2 * kMU], int rd) {
 #pragma unroll
-        for (int u = 0; u < kU; ++u) {
+        for (int u = 0; u < kMU; ++u) {
             const int vi = rd * step + u * T + threadIdx.x;
             if (VEC) {
                 const bool in = vi < nvec;
                 v[u] = in ? load16(tb, vi) : E::neg_inf();
-                v[kU + u] = (in && wf.has_q) ? load16(db, vi) : E::neg_inf();
+                v[kMU + u] = (in && wf.has_q) ? load16(db, vi) : E::neg_inf();
             }
         }
     };
-    auto weigh = [&](const uint4 (&v)[2 * kU], int rd) {
-        double s[kU];
+    auto weigh = [&](const uint4 (&v)[2 * kMU], int rd) {
+        double s[kMU];
 #pragma unroll
-        for (int u = 0; u < kU; ++u) {
+        for (int u = 0; u < kMU; ++u) {
             float fp[EV], fq[EV];
             if (VEC) {
                 E::unpack(v[u], fp);
-                E::unpack(v[kU + u], fq);
+                E::unpack(v[kMU + u], fq);
             } else {
                 const int vi = rd * step + u * T + threadIdx.x;
 #pragma unroll
@@ -397,23 +401,34 @@ __device__ void mass_pass(const typename E::raw* tp, const typename E::raw* dp, 
             }
             s[u] = (double)lane_weight_sum<E>(fp, fq, wf);
         }
-        // Four wave sums at once (reduce-scatter): halves of the wave trade
-        // two of the sums, quarters one, then a 16-lane butterfly; lane
-        // 16 * i ends with the sum of piece i of this round.
-        const bool h32 = (lane & 32) != 0, h16 = (lane & 16) != 0;
-        const double r0 = __shfl_xor(h32 ? s[0] : s[2], 32, kWave);
-        const double r1 = __shfl_xor(h32 ? s[1] : s[3], 32, kWave);
-        const double a0 = (h32 ? s[2] : s[0]) + r0;
-        const double a1 = (h32 ? s[3] : s[1]) + r1;
-        const double r2 = __shfl_xor(h16 ? a0 : a1, 16, kWave);
-        double t = (h16 ? a1 : a0) + r2;
+        // kMU wave sums at once (reduce-scatter): halves of the wave trade half
+        // of the sums, (with four) quarters one, then a butterfly over the
+        // rest; lane (64 / kMU) * i ends with the sum of piece i of the round.
+        const bool h32 = (lane & 32) != 0;
+        double t;
+        int u;
+        if (kMU == 4) {
+            const bool h16 = (lane & 16) != 0;
+            const double r0 = __shfl_xor(h32 ? s[0] : s[kMU / 2], 32, kWave);
+            const double r1 = __shfl_xor(h32 ? s[1] : s[kMU - 1], 32, kWave);
+            const double a0 = (h32 ? s[kMU / 2] : s[0]) + r0;
+            const double a1 = (h32 ? s[kMU - 1] : s[1]) + r1;
+            const double r2 = __shfl_xor(h16 ? a0 : a1, 16, kWave);
+            t = (h16 ? a1 : a0) + r2;
+            u = (h32 ? 2 : 0) + (h16 ? 1 : 0);
+        } else {
+            const double r0 = __shfl_xor(h32 ? s[0] : s[kMU - 1], 32, kWave);
+            t = (h32 ? s[kMU - 1] : s[0]) + r0;
+            const double r1 = __shfl_xor(t, 16, kWave);
+            t += r1;
+            u = h32 ? 1 : 0;
+        }
 #pragma unroll
         for (int o = 8; o > 0; o >>= 1) t += __shfl_xor(t, o, kWave);
-        const int u = (h32 ? 2 : 0) + (h16 ? 1 : 0);
-        const int piece = p0 + (rd * kU + u) * kResolveWaves + w;
-        if ((lane & 15) == 0 && piece < npieces) pieces[piece] = t;
+        const int piece = p0 + (rd * kMU + u) * kResolveWaves + w;
+        if ((lane & (kWave / kMU - 1)) == 0 && piece < npieces) pieces[piece] = t;
     };
-    pipelined_steps<2 * kU>(rounds, fetch, weigh);
+    pipelined_steps<2 * kMU>(rounds, fetch, weigh);
 }
 
 // Scans one piece (64 lanes x one 16-byte vector, tokens e0 ..) from cumulative

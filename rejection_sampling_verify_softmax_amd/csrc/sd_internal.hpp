@@ -101,6 +101,9 @@ hipError_t launch_tree_verify(const void* target, int dtype, const int32_t* tok,
                               const int32_t* n_nodes, int B, int N, int V, int32_t* path,
                               int32_t* accepted_len, int32_t* next_token, void* ws,
                               hipStream_t stream);
+hipError_t launch_compact_kv(void* kv, int64_t row_bytes, int64_t n_rows, const int64_t* base,
+                             const int32_t* path, const int32_t* accepted_len, int B, int N,
+                             hipStream_t stream);
 hipError_t launch_select_len(const float* conf, int B, int K_max, float cost, const float* table,
                              int32_t* k_sel, float* adv, int32_t* cu_sel, hipStream_t stream);
 

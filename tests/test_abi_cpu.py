@@ -28,7 +28,7 @@ def declared_symbols():
 def test_header_declares_the_five_calls():
     names = declared_symbols()
     for n in ("sd_verify_chain", "sd_verify_greedy", "sd_build_tree", "sd_verify_tree", "sd_select_len",
-              "sd_verify_chain_capped", "sd_select_len_table",
+              "sd_verify_chain_capped", "sd_select_len_table", "sd_compact_kv",
               "sd_workspace_bytes", "sd_abi_version", "sd_status_str"):
         assert n in names
 
@@ -134,6 +134,17 @@ def test_capped_and_cost_table_reject_invalid_arguments(L):
     assert L.sd_select_len_table(one, 4, 65, one, one, None, None, None) == 1
     assert L.sd_select_len_table(one, 0, 8, one, one, None, None, None) == 1
     assert L.sd_select_len_table(one, 4, 8, one, None, None, None, None) == 1
+
+
+def test_compact_kv_rejects_invalid_arguments(L):
+    one = ctypes.c_void_p(1)
+    assert L.sd_compact_kv(None, 64, 10, one, one, one, 2, 8, None) == 1
+    assert L.sd_compact_kv(one, 24, 10, one, one, one, 2, 8, None) == 1      # not a multiple of 16
+    assert L.sd_compact_kv(one, 0, 10, one, one, one, 2, 8, None) == 1
+    assert L.sd_compact_kv(one, 64, 0, one, one, one, 2, 8, None) == 1
+    assert L.sd_compact_kv(one, 64, 10, one, one, one, 0, 8, None) == 1
+    assert L.sd_compact_kv(one, 64, 10, one, one, one, 2, 65, None) == 1
+    assert L.sd_compact_kv(one, 64, 10, None, one, one, 2, 8, None) == 1
 
 
 def test_binding_fails_loudly_without_gpu():

@@ -377,6 +377,38 @@ def test_config4_tree_full():
     _say(f"  mean depth-1 nodes {(ref['depth'] == 1).sum() / case.B:.1f}, mean walk {wref['A'].mean():.2f}")
 
 
+@pytest.mark.parametrize("row_bytes", [16, 4096, 131072 + 48])
+def test_compact_kv_matches_oracle(row_bytes):
+    # paths from a real tree walk plus synthetic increasing paths with gaps,
+    # chains where each destination is the previous move's source, full-depth
+    # and empty paths, and a region past the buffer (left alone)
+    g = torch.Generator(device="cuda").manual_seed(17)
+    case = wl.gen_config4(device="cuda", seed=23, B=6, K=16, V=3000, N=64, sigma=1.5)
+    tree = sd.build_tree(case.marginals, case.N)
+    walk = sd.verify_tree(case.target_for_depths(tree["depth"], tree["n_nodes"]), tree)
+    B, N = 12, 64
+    path = torch.full((B, N), -1, dtype=torch.int32, device="cuda")
+    alen = torch.zeros(B, dtype=torch.int32, device="cuda")
+    path[:6] = walk["path"]
+    alen[:6] = walk["accepted_len"]
+    for b in range(6, B):
+        A = [0, 5, 20, 63, 17, 9][b - 6]
+        nodes = torch.sort(torch.randperm(N - 1, generator=g, device="cuda")[:A] + 1).values
+        if b == 8:
+            nodes = torch.arange(2, 2 + A, device="cuda")        # each target is the last source
+        path[b, :A] = nodes.to(torch.int32)
+        alen[b] = A
+    n_rows = B * (N - 1) + 40
+    base = torch.arange(B, dtype=torch.int64, device="cuda") * (N - 1)
+    base[B - 1] = n_rows - (N - 1) + 1                        # one row past the end: untouched
+    kv = torch.randint(0, 256, (n_rows, row_bytes), generator=g, device="cuda", dtype=torch.int32)
+    kv = kv.to(torch.uint8)
+    ref = oracle.compact_kv(kv.cpu().numpy(), base.cpu().numpy(), path.cpu().numpy(),
+                            alen.cpu().numpy(), B, N)
+    sd.compact_kv(kv, base, path, alen)
+    np.testing.assert_array_equal(kv.cpu().numpy(), ref)
+
+
 def test_tree_walk_planted():
     V, N, B = 12, 6, 2
     tok = torch.tensor([[-1, 4, 7, 2, 9, -1]] * B, dtype=torch.int32, device="cuda")

@@ -644,3 +644,20 @@ def test_capped_commits_what_compact_commits():
     allk = oracle.verify_chain_capped(tgt, dft, y, u, np.full(B, K, np.int32), B, K, V, 1.0)
     np.testing.assert_array_equal(allk["A"], full["A"])
     np.testing.assert_array_equal(allk["next"], full["next"])
+
+
+def test_compact_kv_hand_example():
+    # [SD §5 DDTree]: only the accepted path stays in the KV cache. Rows hold
+    # their own index; draft node n sits at row base + n - 1.
+    kv = (np.arange(12)[:, None] * np.ones((1, 16))).astype(np.uint8)
+    path = np.full((2, 6), -1, np.int32)
+    path[0, :3] = (2, 4, 5)          # sequence 0: region rows 0..4
+    path[1, :2] = (1, 2)             # sequence 1: region rows 6..10, already in place
+    out = oracle.compact_kv(kv, [0, 6], path, [3, 2], 2, 6)
+    np.testing.assert_array_equal(out[:, 0], [1, 3, 4, 3, 4, 5, 6, 7, 8, 9, 10, 11])
+    # a region past the buffer is left alone (sequence 0: rows 8..12 of 12); an
+    # entry outside [1, N-1] is skipped (node 9, node 6 == N)
+    out = oracle.compact_kv(kv, [8, 0], np.array([[2, 3, -1, -1, -1, -1],
+                                                  [9, 6, 3, -1, -1, -1]], np.int32), [2, 3], 2, 6)
+    np.testing.assert_array_equal(out[:, 0], [0, 1, 2, 3, 4, 5, 6, 7, 8, 9, 10, 11][:2] + [2] +
+                                  [3, 4, 5, 6, 7, 8, 9, 10, 11])
