@@ -14,7 +14,7 @@ second, the roofline of the dominant kernel (the streaming pass over the logit
 rows, timed with HIP events on its own stream) and the CPU oracle timed on a
 bounded sample of the same workload.
 
-Other workloads (--workload greedy|topk|tree|chain1|kv) measure the other kernels
+Other workloads (--workload greedy|topk|tree|chain1|kv|rerank) measure the other kernels
 for the design notes; their inputs are rotated across copies so that the
 working set exceeds the 256 MB last-level cache.
 """
@@ -225,6 +225,50 @@ def setup_kv(torch, sd, wl):
     return step, meta, None
 
 
+def setup_rerank(torch, sd, wl):
+    # EAGLE-2-style tree choice: 32 sequences, 1024 expanded candidates each
+    # (8 layers, the 10 best of each layer expanded 10 ways), budget 64
+    import numpy as np
+    B, M, N = 32, 1024, 64
+    rng = np.random.default_rng(1006)
+    par = np.full((B, M), -1, np.int32)
+    tok = np.zeros((B, M), np.int32)
+    prob = np.zeros((B, M), np.float32)
+    n = np.zeros(B, np.int32)
+    for b in range(B):
+        conf, pl, tl, ql, layer = [1.0], [-1], [-1], [1.0], [0]
+        for _ in range(8):
+            grow = sorted(layer, key=lambda c: (-conf[c], c))[:10]
+            layer = []
+            for c in grow:
+                z = rng.normal(0, 2.0, 64)
+                q = np.exp(z - z.max())
+                q = (q / q.sum()).astype(np.float32)
+                for r in np.argsort(-q, kind="stable")[:10]:
+                    if len(pl) >= M:
+                        break
+                    pl.append(c)
+                    tl.append(int(rng.integers(0, 128256)))
+                    ql.append(float(q[r]))
+                    conf.append(float(np.float32(conf[c] * q[r])))
+                    layer.append(len(pl) - 1)
+        k = len(pl)
+        par[b, :k], tok[b, :k], prob[b, :k], n[b] = pl, tl, ql, k
+    t = lambda a: torch.as_tensor(a, device="cuda")
+    par_t, tok_t, prob_t, n_t = t(par), t(tok), t(prob), t(n)
+
+    def step(ev=None):
+        if ev is not None:
+            sd.time_next_stream_pass(*ev)
+        sd.rerank_tree(par_t, tok_t, prob_t, n_t, N)
+
+    meta = {"workload": f"EAGLE-2-style tree choice: B={B}, {M} candidates, budget N={N}",
+            "global_batch": B, "positions_per_step": B * (N - 1),
+            "kernel": "k_rerank_tree", "kernel_bytes": B * M * 12 + B * N * 28,
+            "step_bytes": B * M * 12 + B * N * 28}
+    return step, meta, None
+
+
 def setup_chain1(torch, sd, wl):
     case = wl.gen_config1(device="cuda")
     ws = torch.empty(sd.workspace_bytes(sd.OP_CHAIN, 1, 4, 1000), dtype=torch.uint8, device="cuda")
@@ -242,7 +286,7 @@ def setup_chain1(torch, sd, wl):
 
 
 WORKLOADS = {"adaptive": setup_adaptive, "greedy": setup_greedy, "topk": setup_topk,
-             "tree": setup_tree, "chain1": setup_chain1, "kv": setup_kv}
+             "tree": setup_tree, "chain1": setup_chain1, "kv": setup_kv, "rerank": setup_rerank}
 
 
 def run_cpu_baseline(cpu, target_seconds: float):

@@ -84,6 +84,7 @@ typedef enum {
 /* Largest supported values. */
 #define SD_MAX_K 64
 #define SD_MAX_TREE_N 64
+#define SD_MAX_CANDIDATES 1024
 #define SD_MAX_TREE_K 16
 #define SD_MAX_TOPK 256
 
@@ -227,6 +228,30 @@ sd_status_t sd_verify_tree(const void* target_logits, sd_dtype_t dtype,
                            void* workspace, size_t workspace_bytes, void* hip_stream);
 
 /*
+ * EAGLE-2-style verification tree [SD §4 EAGLE-2: candidates expanded along
+ * paths of high cumulative confidence are re-ranked and the final verification
+ * tree is chosen from them]. Per sequence, an expanded candidate tree in
+ * topological order: candidate 0 is the root; candidate i (1 <= i < n_cand[b])
+ * has a parent in [0, i), a token and a conditional draft probability in [0, 1]
+ * (a candidate with another parent or probability, or NaN, is left out with its
+ * subtree). Its confidence is the fp32 product of the probabilities along its
+ * path, root first. The tree is the root plus the first N-1 candidates by
+ * (confidence desc, depth asc, candidate index asc) -- a child never precedes
+ * its parent, so every kept node's parent is kept -- numbered in that order.
+ * Outputs as sd_build_tree (node 0 the root; unused slots: token -1, parent -1,
+ * depth 0, score 0, mask 0), plus node_cand[b, n], the candidate behind node n
+ * (0 for the root, -1 unused; may be NULL).
+ *
+ *   cand_parent, cand_token [B, M] int32; cand_prob [B, M] fp32; n_cand [B] int32
+ *   M <= SD_MAX_CANDIDATES, 2 <= N <= SD_MAX_TREE_N. Needs no workspace.
+ */
+sd_status_t sd_rerank_tree(const int32_t* cand_parent, const int32_t* cand_token,
+                           const float* cand_prob, const int32_t* n_cand, int32_t B, int32_t M,
+                           int32_t N, int32_t* node_token, int32_t* node_parent,
+                           int32_t* node_depth, float* node_score, uint64_t* node_anc_mask,
+                           int32_t* node_cand, int32_t* n_nodes, void* hip_stream);
+
+/*
  * Accepted-path KV compaction [SD §5 DDTree: after the walk the KV cache keeps
  * only the accepted path]. `kv` holds n_rows rows of row_bytes bytes each (one
  * token's keys and values, laid out as the caller likes; row_bytes a positive
@@ -284,8 +309,8 @@ sd_status_t sd_select_len_table(const float* conf, int32_t B, int32_t K_max,
 
 /*
  * Measurement support. The next sd_verify_chain, sd_verify_chain_capped,
- * sd_verify_greedy, sd_build_tree, sd_verify_tree or sd_compact_kv call made by
- * the calling host thread records
+ * sd_verify_greedy, sd_build_tree, sd_verify_tree, sd_compact_kv or
+ * sd_rerank_tree call made by the calling host thread records
  * `start_event` on its stream immediately before its streaming kernel (the one
  * pass over the logit / marginal rows, which dominates its time) and
  * `stop_event` immediately after it; the hook then clears itself. Both are

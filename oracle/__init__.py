@@ -68,6 +68,8 @@ def _load():
     lib.orc_select_len_table.restype = None
     lib.orc_compact_kv.argtypes = [P, ctypes.c_longlong, ctypes.c_longlong, P, P, P, I, I]
     lib.orc_compact_kv.restype = None
+    lib.orc_rerank_tree.argtypes = [P, P, P, P, I, I, I, P, P, P, P, P, P, P]
+    lib.orc_rerank_tree.restype = None
     _lib = lib
     return lib
 
@@ -236,4 +238,21 @@ def compact_kv(kv, row_base, path, accepted_len, B, N):
     a = _i32(accepted_len)
     _load().orc_compact_kv(_ptr(out), int(row_bytes), int(n_rows), _ptr(rb), _ptr(p), _ptr(a),
                            int(B), int(N))
+    return out
+
+
+def rerank_tree(cand_parent, cand_token, cand_prob, n_cand, B, M, N):
+    """EAGLE-2-style tree from an expanded candidate tree (see oracle.c)."""
+    par = _i32(cand_parent).reshape(-1)
+    tok = _i32(cand_token).reshape(-1)
+    prob = _f32(cand_prob).reshape(-1)
+    nc = _i32(n_cand)
+    out = {"token": np.zeros((B, N), np.int32), "parent": np.zeros((B, N), np.int32),
+           "depth": np.zeros((B, N), np.int32), "score": np.zeros((B, N), np.float32),
+           "anc_mask": np.zeros((B, N), np.uint64), "cand": np.zeros((B, N), np.int32),
+           "n_nodes": np.zeros(B, np.int32)}
+    _load().orc_rerank_tree(_ptr(par), _ptr(tok), _ptr(prob), _ptr(nc), int(B), int(M), int(N),
+                            _ptr(out["token"]), _ptr(out["parent"]), _ptr(out["depth"]),
+                            _ptr(out["score"]), _ptr(out["anc_mask"]), _ptr(out["cand"]),
+                            _ptr(out["n_nodes"]))
     return out

@@ -503,6 +503,82 @@ void orc_select_len(const float* conf, int B, int K, float cost, int32_t* k_sel,
 }
 
 /*
+ * EAGLE-2-style verification tree [SD §4 EAGLE-2: expanded candidates are
+ * re-ranked by cumulative confidence and the final tree is chosen from them].
+ * Candidates of sequence b (topological order, candidate 0 the root): parent,
+ * token and conditional probability; candidate i is usable if 0 <= parent < i,
+ * its parent is usable (the root is) and its probability lies in [0, 1]. Its
+ * confidence is the fp32 product of the probabilities from the root down. The
+ * tree: the root plus the first N-1 usable candidates by (confidence desc,
+ * depth asc, index asc), numbered in that order.
+ */
+typedef struct {
+    float conf;
+    int depth;
+    int idx;
+} OrcCand;
+
+static int orc_cand_cmp(const void* a, const void* b) {
+    const OrcCand* x = (const OrcCand*)a;
+    const OrcCand* y = (const OrcCand*)b;
+    if (x->conf != y->conf) return x->conf > y->conf ? -1 : 1;
+    if (x->depth != y->depth) return x->depth < y->depth ? -1 : 1;
+    return x->idx < y->idx ? -1 : (x->idx > y->idx);
+}
+
+void orc_rerank_tree(const int32_t* cand_parent, const int32_t* cand_token, const float* cand_prob,
+                     const int32_t* n_cand, int B, int M, int N, int32_t* node_token,
+                     int32_t* node_parent, int32_t* node_depth, float* node_score,
+                     uint64_t* node_anc, int32_t* node_cand, int32_t* n_nodes) {
+    for (int b = 0; b < B; ++b) {
+        const int32_t* par = cand_parent + (size_t)b * M;
+        const int32_t* tok = cand_token + (size_t)b * M;
+        const float* prob = cand_prob + (size_t)b * M;
+        int nc = n_cand[b] < 0 ? 0 : (n_cand[b] > M ? M : n_cand[b]);
+        float* conf = (float*)malloc(sizeof(float) * (size_t)(M + 1));
+        int* depth = (int*)malloc(sizeof(int) * (size_t)(M + 1));
+        int* usable = (int*)malloc(sizeof(int) * (size_t)(M + 1));
+        int* node_of = (int*)malloc(sizeof(int) * (size_t)(M + 1));
+        OrcCand* list = (OrcCand*)malloc(sizeof(OrcCand) * (size_t)(M + 1));
+        int nl = 0;
+        for (int i = 0; i < M; ++i) { usable[i] = 0; node_of[i] = -1; }
+        if (nc > 0) { usable[0] = 1; conf[0] = 1.0f; depth[0] = 0; node_of[0] = 0; }
+        for (int i = 1; i < nc; ++i) {
+            int p = par[i];
+            float q = prob[i];
+            if (p < 0 || p >= i || !usable[p] || !(q >= 0.0f && q <= 1.0f)) continue;
+            usable[i] = 1;
+            conf[i] = conf[p] * q;
+            depth[i] = depth[p] + 1;
+            list[nl].conf = conf[i];
+            list[nl].depth = depth[i];
+            list[nl].idx = i;
+            ++nl;
+        }
+        qsort(list, (size_t)nl, sizeof(OrcCand), orc_cand_cmp);
+        int kept = nl < N - 1 ? nl : N - 1;
+        size_t o = (size_t)b * N;
+        for (int n = 0; n < N; ++n) {
+            node_token[o + n] = -1; node_parent[o + n] = -1; node_depth[o + n] = 0;
+            node_score[o + n] = 0.0f; node_anc[o + n] = 0; if (node_cand) node_cand[o + n] = -1;
+        }
+        node_score[o] = 1.0f; node_anc[o] = 1; if (node_cand) node_cand[o] = 0;
+        for (int r = 0; r < kept; ++r) node_of[list[r].idx] = r + 1;
+        for (int r = 0; r < kept; ++r) {
+            int c = list[r].idx, n = r + 1;
+            node_token[o + n] = tok[c];
+            node_parent[o + n] = node_of[par[c]];
+            node_depth[o + n] = depth[c];
+            node_score[o + n] = conf[c];
+            node_anc[o + n] = node_anc[o + node_of[par[c]]] | ((uint64_t)1 << n);
+            if (node_cand) node_cand[o + n] = c;
+        }
+        n_nodes[b] = 1 + kept;
+        free(conf); free(depth); free(usable); free(node_of); free(list);
+    }
+}
+
+/*
  * Accepted-path KV compaction [SD §5 DDTree: the KV cache keeps only the
  * accepted path]. kv: n_rows rows of row_bytes bytes; draft node n (1..N-1) of
  * sequence b sits at row row_base[b] + n - 1. Afterwards row row_base[b] + i

@@ -72,6 +72,8 @@ def _load():
     lib.sd_select_len_table.restype = ctypes.c_int
     lib.sd_compact_kv.argtypes = [P, ctypes.c_int64, ctypes.c_int64, P, P, P, I, I, P]
     lib.sd_compact_kv.restype = ctypes.c_int
+    lib.sd_rerank_tree.argtypes = [P, P, P, P, I, I, I, P, P, P, P, P, P, P, P]
+    lib.sd_rerank_tree.restype = ctypes.c_int
     lib.sd_time_next_stream_pass.argtypes = [P, P]
     lib.sd_time_next_stream_pass.restype = ctypes.c_int
     _lib = lib
@@ -411,3 +413,27 @@ def compact_kv(kv: torch.Tensor, row_base: torch.Tensor, path: torch.Tensor,
                               _ptr(accepted_len), B, N, _stream(stream))
     _raise(r, "sd_compact_kv")
     return kv
+
+
+def rerank_tree(cand_parent: torch.Tensor, cand_token: torch.Tensor, cand_prob: torch.Tensor,
+                n_cand: torch.Tensor, N: int, stream=None) -> dict:
+    """sd_rerank_tree. cand_* [B, M] (int32, int32, float32) and n_cand [B] int32 on the GPU.
+    Returns the tree as build_tree does, plus "cand" (the candidate behind each node)."""
+    dev = cand_parent.device
+    _check(cand_parent, "cand_parent", torch.int32, dev)
+    _check(cand_token, "cand_token", torch.int32, dev)
+    _check(cand_prob, "cand_prob", torch.float32, dev)
+    _check(n_cand, "n_cand", torch.int32, dev)
+    B, M = (int(x) for x in cand_parent.shape)
+    if cand_token.shape != cand_parent.shape or cand_prob.shape != cand_parent.shape or n_cand.numel() != B:
+        raise ValueError("candidate arrays must be [B, M] and n_cand [B]")
+    out = {k: torch.empty(B, N, dtype=t, device=dev) for k, t in
+           (("token", torch.int32), ("parent", torch.int32), ("depth", torch.int32),
+            ("score", torch.float32), ("anc_mask", torch.int64), ("cand", torch.int32))}
+    out["n_nodes"] = torch.empty(B, dtype=torch.int32, device=dev)
+    r = _load().sd_rerank_tree(_ptr(cand_parent), _ptr(cand_token), _ptr(cand_prob), _ptr(n_cand), B, M,
+                               int(N), _ptr(out["token"]), _ptr(out["parent"]), _ptr(out["depth"]),
+                               _ptr(out["score"]), _ptr(out["anc_mask"]), _ptr(out["cand"]),
+                               _ptr(out["n_nodes"]), _stream(stream))
+    _raise(r, "sd_rerank_tree")
+    return out

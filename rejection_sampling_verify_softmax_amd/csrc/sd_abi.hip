@@ -256,4 +256,20 @@ sd_status_t sd_compact_kv(void* kv, int64_t row_bytes, int64_t n_rows, const int
                                           N, static_cast<hipStream_t>(hip_stream)));
 }
 
+sd_status_t sd_rerank_tree(const int32_t* cand_parent, const int32_t* cand_token,
+                           const float* cand_prob, const int32_t* n_cand, int32_t B, int32_t M,
+                           int32_t N, int32_t* node_token, int32_t* node_parent,
+                           int32_t* node_depth, float* node_score, uint64_t* node_anc_mask,
+                           int32_t* node_cand, int32_t* n_nodes, void* hip_stream) {
+    if (B < 1 || B > kMaxB || M < 1 || M > SD_MAX_CANDIDATES || N < 2 || N > SD_MAX_TREE_N)
+        return SD_EINVAL;
+    if (!cand_parent || !cand_token || !cand_prob || !n_cand || !node_token || !node_parent ||
+        !node_depth || !node_score || !node_anc_mask || !n_nodes)
+        return SD_EINVAL;
+    return from_hip(sd::launch_rerank_tree(cand_parent, cand_token, cand_prob, n_cand, B, M, N,
+                                           node_token, node_parent, node_depth, node_score,
+                                           node_anc_mask, node_cand, n_nodes,
+                                           static_cast<hipStream_t>(hip_stream)));
+}
+
 }  // extern "C"

@@ -104,6 +104,10 @@ hipError_t launch_tree_verify(const void* target, int dtype, const int32_t* tok,
 hipError_t launch_compact_kv(void* kv, int64_t row_bytes, int64_t n_rows, const int64_t* base,
                              const int32_t* path, const int32_t* accepted_len, int B, int N,
                              hipStream_t stream);
+hipError_t launch_rerank_tree(const int32_t* cand_parent, const int32_t* cand_token,
+                              const float* cand_prob, const int32_t* n_cand, int B, int M, int N,
+                              int32_t* tok, int32_t* par, int32_t* dep, float* score, uint64_t* anc,
+                              int32_t* node_cand, int32_t* n_nodes, hipStream_t stream);
 hipError_t launch_select_len(const float* conf, int B, int K_max, float cost, const float* table,
                              int32_t* k_sel, float* adv, int32_t* cu_sel, hipStream_t stream);
 

@@ -28,7 +28,7 @@ def declared_symbols():
 def test_header_declares_the_five_calls():
     names = declared_symbols()
     for n in ("sd_verify_chain", "sd_verify_greedy", "sd_build_tree", "sd_verify_tree", "sd_select_len",
-              "sd_verify_chain_capped", "sd_select_len_table", "sd_compact_kv",
+              "sd_verify_chain_capped", "sd_select_len_table", "sd_compact_kv", "sd_rerank_tree",
               "sd_workspace_bytes", "sd_abi_version", "sd_status_str"):
         assert n in names
 
@@ -145,6 +145,20 @@ def test_compact_kv_rejects_invalid_arguments(L):
     assert L.sd_compact_kv(one, 64, 10, one, one, one, 0, 8, None) == 1
     assert L.sd_compact_kv(one, 64, 10, one, one, one, 2, 65, None) == 1
     assert L.sd_compact_kv(one, 64, 10, None, one, one, 2, 8, None) == 1
+
+
+def test_rerank_tree_rejects_invalid_arguments(L):
+    one = ctypes.c_void_p(1)
+
+    def rr(B=2, M=100, N=64, first=one, out=one):
+        return L.sd_rerank_tree(first, one, one, one, B, M, N, out, one, one, one, one, None, one, None)
+    assert rr(B=0) == 1
+    assert rr(M=0) == 1
+    assert rr(M=1025) == 1
+    assert rr(N=1) == 1
+    assert rr(N=65) == 1
+    assert rr(first=None) == 1
+    assert rr(out=None) == 1
 
 
 def test_binding_fails_loudly_without_gpu():

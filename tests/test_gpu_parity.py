@@ -409,6 +409,53 @@ def test_compact_kv_matches_oracle(row_bytes):
     np.testing.assert_array_equal(kv.cpu().numpy(), ref)
 
 
+def _eagle2_candidates(rng, B, M, layers, topk, V=32000):
+    """Expanded candidate trees as an EAGLE-2 drafter would leave them: per
+    layer, the topk candidates of the newest layer by cumulative confidence each
+    get topk children (conditional probabilities of a random softmax)."""
+    par = np.full((B, M), -1, np.int32)
+    tok = np.zeros((B, M), np.int32)
+    prob = np.zeros((B, M), np.float32)
+    n = np.zeros(B, np.int32)
+    for b in range(B):
+        conf = [1.0]
+        par_l, tok_l, prob_l = [-1], [-1], [1.0]
+        layer = [0]
+        for _ in range(layers):
+            grow = sorted(layer, key=lambda c: (-conf[c], c))[:topk]
+            layer = []
+            for c in grow:
+                z = rng.normal(0, 2.0, 64)
+                q = np.exp(z - z.max())
+                q = (q / q.sum()).astype(np.float32)
+                for r in np.argsort(-q, kind="stable")[:topk]:
+                    if len(par_l) >= M:
+                        break
+                    par_l.append(c)
+                    tok_l.append(int(rng.integers(0, V)))
+                    prob_l.append(float(q[r]))
+                    conf.append(float(np.float32(conf[c] * np.float32(q[r]))))
+                    layer.append(len(par_l) - 1)
+        k = len(par_l)
+        par[b, :k], tok[b, :k], prob[b, :k], n[b] = par_l, tok_l, prob_l, k
+    return par, tok, prob, n
+
+
+@pytest.mark.parametrize("M,layers,topk,N", [(400, 6, 8, 64), (1024, 8, 10, 64), (60, 3, 4, 12)])
+def test_rerank_tree_matches_oracle(M, layers, topk, N):
+    rng = np.random.default_rng(M + N)
+    B = 16
+    par, tok, prob, n = _eagle2_candidates(rng, B, M, layers, topk)
+    par[3, 7] = 9                         # a bad parent and a bad probability drop subtrees
+    prob[4, 5] = 1.25
+    ref = oracle.rerank_tree(par, tok, prob, n, B, M, N)
+    t = lambda a: torch.as_tensor(a, device="cuda")
+    out = sd.rerank_tree(t(par), t(tok), t(prob), t(n), N)
+    for key in ("token", "parent", "depth", "score", "cand", "n_nodes"):
+        np.testing.assert_array_equal(out[key].cpu().numpy(), ref[key], err_msg=key)
+    np.testing.assert_array_equal(out["anc_mask"].cpu().numpy().view(np.uint64), ref["anc_mask"])
+
+
 def test_tree_walk_planted():
     V, N, B = 12, 6, 2
     tok = torch.tensor([[-1, 4, 7, 2, 9, -1]] * B, dtype=torch.int32, device="cuda")

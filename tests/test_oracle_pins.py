@@ -661,3 +661,78 @@ def test_compact_kv_hand_example():
                                                   [9, 6, 3, -1, -1, -1]], np.int32), [2, 3], 2, 6)
     np.testing.assert_array_equal(out[:, 0], [0, 1, 2, 3, 4, 5, 6, 7, 8, 9, 10, 11][:2] + [2] +
                                   [3, 4, 5, 6, 7, 8, 9, 10, 11])
+
+
+# --------------------------------------------------------------------------
+# EAGLE-2-style verification tree ([SD §4 EAGLE-2])
+# --------------------------------------------------------------------------
+
+def _trie_candidates(m):
+    """The full trie over the per-depth lists of marginals m [K, V]: BFS order,
+    each node's children by rank, so candidates of one depth are in
+    lexicographic rank-tuple order."""
+    K, V = m.shape
+    lists = [np.lexsort((np.arange(V), -m[d].astype(np.float64))) for d in range(K)]
+    par, tok, prob = [-1], [-1], [1.0]
+    level = [0]
+    for d in range(K):
+        nxt = []
+        for c in level:
+            for r in range(V):
+                par.append(c)
+                tok.append(int(lists[d][r]))
+                prob.append(float(m[d, lists[d][r]]))
+                nxt.append(len(par) - 1)
+        level = nxt
+    return np.array(par, np.int32), np.array(tok, np.int32), np.array(prob, np.float32)
+
+
+@pytest.mark.parametrize("N", [2, 5, 13, 40, 64])
+def test_rerank_of_the_full_trie_is_the_ddtree(N):
+    # re-ranking the whole factorised trie by cumulative confidence gives the
+    # best-first DDTree of the same marginals (itself pinned by brute force)
+    rng = np.random.default_rng(31 + N)
+    K, V = 4, 3
+    m = special.softmax(rng.normal(0, 1.5, (K, V)), axis=-1).astype(np.float32)
+    par, tok, prob = _trie_candidates(m)
+    M = len(par)
+    rr = oracle.rerank_tree(par[None], tok[None], prob[None], [M], 1, M, N)
+    bt = oracle.build_tree(m[None], 1, K, V, N)
+    for key in ("token", "parent", "depth", "score", "anc_mask", "n_nodes"):
+        np.testing.assert_array_equal(rr[key], bt[key], err_msg=key)
+
+
+def test_rerank_brute_force_and_bad_candidates():
+    rng = np.random.default_rng(32)
+    for trial in range(300):
+        M = int(rng.integers(2, 9))
+        N = int(rng.integers(2, 7))
+        par = np.array([-1] + [int(rng.integers(0, i)) for i in range(1, M)], np.int32)
+        prob = rng.random(M).astype(np.float32)
+        prob[0] = 1.0
+        tok = rng.integers(0, 50, M).astype(np.int32)
+        rr = oracle.rerank_tree(par[None], tok[None], prob[None], [M], 1, M, N)
+        conf = np.ones(M, np.float32)
+        for i in range(1, M):
+            conf[i] = np.float32(conf[par[i]] * prob[i])
+        kept = set(int(c) for c in rr["cand"][0, 1:rr["n_nodes"][0]])
+        size = min(N - 1, M - 1)
+        best = -1.0
+        for S in itertools.combinations(range(1, M), size):
+            if all(par[i] == 0 or par[i] in S for i in S):
+                best = max(best, float(sum(conf[i] for i in S)))
+        assert len(kept) == size
+        assert all(par[i] == 0 or par[i] in kept for i in kept)
+        assert abs(sum(float(conf[i]) for i in kept) - best) < 1e-6
+        # node order: confidence never increases, parents come first
+        sc = rr["score"][0, 1:rr["n_nodes"][0]]
+        assert (np.diff(sc) <= 0).all()
+        pr = rr["parent"][0, 1:rr["n_nodes"][0]]
+        assert (pr < np.arange(1, rr["n_nodes"][0])).all()
+    # a bad parent, a probability outside [0, 1] or NaN drops the subtree
+    par = np.array([-1, 0, 1, 0, 3, 5, 0], np.int32)
+    prob = np.array([1, 0.9, 0.8, 1.5, 0.9, 0.5, np.nan], np.float32)
+    tok = np.arange(7, dtype=np.int32)
+    rr = oracle.rerank_tree(par[None], tok[None], prob[None], [7], 1, 7, 10)
+    assert rr["n_nodes"][0] == 3
+    np.testing.assert_array_equal(rr["cand"][0, :3], [0, 1, 2])
