@@ -310,12 +310,15 @@ sd_status_t sd_select_len_table(const float* conf, int32_t B, int32_t K_max,
 /*
  * Measurement support. The next sd_verify_chain, sd_verify_chain_capped,
  * sd_verify_greedy, sd_build_tree, sd_verify_tree, sd_compact_kv or
- * sd_rerank_tree call made by the calling host thread records
- * `start_event` on its stream immediately before its streaming kernel (the one
- * pass over the logit / marginal rows, which dominates its time) and
- * `stop_event` immediately after it; the hook then clears itself. Both are
- * hipEvent_t handles created by the caller; hipEventElapsedTime of the pair is
- * that kernel's duration. Passing NULL, NULL clears a pending hook. Returns SD_OK.
+ * sd_rerank_tree call made by the calling host thread binds `start_event` and
+ * `stop_event` to its streaming kernel (the one pass over the logit / marginal
+ * rows, which dominates its time): the kernel is launched with
+ * hipExtLaunchKernel, so the events take that dispatch's own start and end
+ * times and add no marker packets to the stream. The hook then clears itself.
+ * Both are hipEvent_t handles created by the caller; hipEventElapsedTime of the
+ * pair is that kernel's duration. A call with no such kernel (no tree rows)
+ * records the two events back to back. Passing NULL, NULL clears a pending
+ * hook. Returns SD_OK.
  */
 sd_status_t sd_time_next_stream_pass(void* start_event, void* stop_event);
 

@@ -7,7 +7,7 @@
 // normalised positive residual [p - q]+ or, when all pass, the extra token from
 // p; temperature is folded into both p and q.
 //
-// Four launches on the caller's stream:
+// Launches on the caller's stream:
 //   1. k_chain_stats  grid (sequence, slot, chunk): the one pass over every row.
 //      Slot i < k_b streams target row i and draft row i together; slot k_b
 //      streams the extra-token row. Each workgroup writes the softmax partial
@@ -16,11 +16,15 @@
 //      exactly (integer references: a power-of-two rescale), evaluates
 //      p_i(y_i), q_i(y_i) in fp64, the accept bits and A (wave ballot), and the
 //      descriptor of the decision row(s).
-//   3. k_chain_mass   grid (sequence, 32K-token chunk): re-reads only the
+//   3. k_chain_mass   grid (sequence, 16K-token chunk): re-reads only the
 //      decision row(s) for the weight mass of the residual (or of p for the
 //      extra token) per 512-token piece.
 //   4. k_chain_sample one wave per sequence: prefix over the piece masses, then
 //      one piece scan for the final token.
+// A large batch runs 2-4 of the last phase as one launch, k_chain_resolve,
+// one workgroup per sequence. Phases: the positions are streamed in slot
+// ranges (1 and 2 per range); a sequence rejected in an early range streams
+// none of its later rows.
 #include "sd_device.hpp"
 #include "sd_internal.hpp"
 
@@ -306,49 +310,62 @@ __device__ RowStat combine_row(const Partial* p, int n_chunks) {
     return r;
 }
 
-// Sampling weight of one token in fp32: the normalised residual max(p - q, 0),
-// or p itself. The mass pass and the final scan use this one definition, so
-// both see bit-identical values.
+// Sampling weight of one token in fp32: the normalised residual max(p - q, 0)
+// (Q), or p itself (!Q: the extra token, and a residual whose q counts as 0,
+// since max(p - 0, 0) rounds to p). The mass pass and the final scan use this
+// one definition, so both see bit-identical values. Q is a template argument:
+// the streaming loops hold no per-token branch on the row kind.
 struct WeightFn {
     float c, Op, ip, Oq, iq;
-    bool has_q, residual;
-    __device__ __forceinline__ float operator()(float xp, float xq) const {
-        const float ep = fast_exp2(__builtin_fmaf(xp, c, -Op));
-        if (!residual) return ep * ip;
-        const float q = has_q ? fast_exp2(__builtin_fmaf(xq, c, -Oq)) * iq : 0.f;
-        return fmaxf(__builtin_fmaf(ep, ip, -q), 0.f);          // max(p - q, 0)
-    }
+    bool has_q;
 };
+
+template <bool Q>
+__device__ __forceinline__ float weight(const WeightFn& w, float xp, float xq) {
+    const float ep = fast_exp2(__builtin_fmaf(xp, w.c, -w.Op));
+    if (!Q) return ep * w.ip;
+    const float q = fast_exp2(__builtin_fmaf(xq, w.c, -w.Oq)) * w.iq;
+    return fmaxf(__builtin_fmaf(ep, w.ip, -q), 0.f);          // max(p - q, 0)
+}
 
 __device__ __forceinline__ WeightFn weight_fn(const ChainDesc& d, float c, bool use_p) {
     WeightFn w;
     w.c = c;
     w.Op = d.O_p;
     w.ip = (float)(1.0 / d.S_p);
-    w.residual = !use_p && d.mode == kModeResidual;
-    w.has_q = w.residual && d.d_row >= 0;
+    w.has_q = !use_p && d.mode == kModeResidual && d.d_row >= 0;
     w.Oq = d.O_q;
     w.iq = w.has_q ? (float)(1.0 / d.S_q) : 0.f;
     return w;
 }
 
 // Sum of the weights of one lane's 16-byte vector, in element order.
-template <class E>
+template <class E, bool Q>
 __device__ __forceinline__ float lane_weight_sum(const float (&fp)[E::kVec], const float (&fq)[E::kVec],
                                                  const WeightFn& wf) {
     float s = 0.f;
 #pragma unroll
-    for (int e = 0; e < E::kVec; ++e) s += wf(fp[e], fq[e]);
+    for (int e = 0; e < E::kVec; ++e) s += weight<Q>(wf, fp[e], fq[e]);
     return s;
 }
 
 constexpr int kResolveThreads = kBlock;
-constexpr int kMassChunkVecs = 4096;      // 16-byte vectors per mass workgroup
+constexpr int kMassChunkVecs = 2048;      // 16-byte vectors per mass workgroup
 #ifndef SD_MASS_UNROLL
-#define SD_MASS_UNROLL 4
+#define SD_MASS_UNROLL 2
 #endif
 constexpr int kMU = SD_MASS_UNROLL;       // pieces per wave per round of the mass pass
-constexpr int kResolveWaves = kResolveThreads / kWave;
+// One workgroup per sequence for the decision, the mass and the final draw,
+// when the batch alone fills the device (or one mass chunk covers the row).
+#ifndef SD_FUSED_THREADS
+#define SD_FUSED_THREADS 512
+#endif
+#ifndef SD_FUSED_MIN_B
+#define SD_FUSED_MIN_B 256
+#endif
+constexpr int kFusedThreads = SD_FUSED_THREADS;
+constexpr int kLdsPieces = 1024;          // piece masses kept in LDS up to this many
+constexpr int kFusedMinB = SD_FUSED_MIN_B;
 
 // Weight mass of every piece (64 consecutive 16-byte vectors: 512 bf16 or 256
 // fp32 tokens) of tokens [beg, end) of the decision row(s), written to
@@ -356,12 +373,13 @@ constexpr int kResolveWaves = kResolveThreads / kWave;
 // flight while the current one is weighed; wave w of round rd, unroll u
 // covers piece (rd * U + u) * waves + w of the range. `beg` is a multiple of
 // the piece size.
-template <class E, bool VEC>
+template <class E, bool VEC, int T, bool Q>
 __device__ void mass_pass(const typename E::raw* tp, const typename E::raw* dp, int beg, int end,
                           const WeightFn& wf, double* pieces, int npieces) {
     constexpr int EV = E::kVec;
-    constexpr int T = kResolveThreads;
+    constexpr int waves = T / kWave;
     constexpr int step = T * kMU;
+    constexpr int NR = Q ? 2 : 1;     // rows streamed: target, and draft for the residual
     const int nvec = (end - beg + EV - 1) / EV;
     const int w = threadIdx.x / kWave;
     const int lane = threadIdx.x & (kWave - 1);
@@ -371,35 +389,35 @@ __device__ void mass_pass(const typename E::raw* tp, const typename E::raw* dp, 
     const typename E::raw* db = dp + beg;
     static_assert(kMU == 2 || kMU == 4, "the piece reduction sums two or four pieces at once");
     // loads of one round: kMU vectors of the target row, then kMU of the draft row
-    auto fetch = [&](uint4 (&v)[2 * kMU], int rd) {
+    auto fetch = [&](uint4 (&v)[NR * kMU], int rd) {
 #pragma unroll
         for (int u = 0; u < kMU; ++u) {
             const int vi = rd * step + u * T + threadIdx.x;
             if (VEC) {
                 const bool in = vi < nvec;
                 v[u] = in ? load16(tb, vi) : E::neg_inf();
-                v[kMU + u] = (in && wf.has_q) ? load16(db, vi) : E::neg_inf();
+                if (Q) v[NR * kMU - kMU + u] = in ? load16(db, vi) : E::neg_inf();
             }
         }
     };
-    auto weigh = [&](const uint4 (&v)[2 * kMU], int rd) {
+    auto weigh = [&](const uint4 (&v)[NR * kMU], int rd) {
         double s[kMU];
 #pragma unroll
         for (int u = 0; u < kMU; ++u) {
             float fp[EV], fq[EV];
             if (VEC) {
                 E::unpack(v[u], fp);
-                E::unpack(v[kMU + u], fq);
+                if (Q) E::unpack(v[NR * kMU - kMU + u], fq);
             } else {
                 const int vi = rd * step + u * T + threadIdx.x;
 #pragma unroll
                 for (int e = 0; e < EV; ++e) {
                     const int j = beg + vi * EV + e;
                     fp[e] = (vi < nvec && j < end) ? E::at(tp, j) : -INFINITY;
-                    fq[e] = (vi < nvec && j < end && wf.has_q) ? E::at(dp, j) : -INFINITY;
+                    if (Q) fq[e] = (vi < nvec && j < end) ? E::at(dp, j) : -INFINITY;
                 }
             }
-            s[u] = (double)lane_weight_sum<E>(fp, fq, wf);
+            s[u] = (double)lane_weight_sum<E, Q>(fp, fq, wf);
         }
         // kMU wave sums at once (reduce-scatter): halves of the wave trade half
         // of the sums, (with four) quarters one, then a butterfly over the
@@ -425,16 +443,16 @@ __device__ void mass_pass(const typename E::raw* tp, const typename E::raw* dp, 
         }
 #pragma unroll
         for (int o = 8; o > 0; o >>= 1) t += __shfl_xor(t, o, kWave);
-        const int piece = p0 + (rd * kMU + u) * kResolveWaves + w;
+        const int piece = p0 + (rd * kMU + u) * waves + w;
         if ((lane & (kWave / kMU - 1)) == 0 && piece < npieces) pieces[piece] = t;
     };
-    pipelined_steps<2 * kMU>(rounds, fetch, weigh);
+    pipelined_steps<NR * kMU>(rounds, fetch, weigh);
 }
 
 // Scans one piece (64 lanes x one 16-byte vector, tokens e0 ..) from cumulative
 // mass `before`: the first token whose running mass exceeds `target`, or the
 // last token of the piece with positive weight. One wave.
-template <class E>
+template <class E, bool Q>
 __device__ int scan_piece(const typename E::raw* tp, const typename E::raw* dp, int e0, int V,
                           const WeightFn& wf, double before, double target, bool take_last) {
     constexpr int EV = E::kVec;
@@ -445,14 +463,14 @@ __device__ int scan_piece(const typename E::raw* tp, const typename E::raw* dp, 
     for (int e = 0; e < EV; ++e) {
         const int j = j0 + e;
         fp[e] = (j < V) ? E::at(tp, j) : -INFINITY;
-        fq[e] = (wf.has_q && j < V) ? E::at(dp, j) : -INFINITY;
+        fq[e] = (Q && j < V) ? E::at(dp, j) : -INFINITY;
     }
     float w[EV];
     float ls = 0.f;
     int lastpos = -1;
 #pragma unroll
     for (int e = 0; e < EV; ++e) {
-        w[e] = wf(fp[e], fq[e]);
+        w[e] = weight<Q>(wf, fp[e], fq[e]);
         ls += w[e];
         if (w[e] > 0.f) lastpos = j0 + e;
     }
@@ -480,7 +498,7 @@ __device__ int scan_piece(const typename E::raw* tp, const typename E::raw* dp, 
 
 // Inverse CDF in token order from the piece masses: the first token whose
 // running mass exceeds u * total. One wave. Returns -1 when total is 0.
-template <class E>
+template <class E, bool Q>
 __device__ int sample_from_pieces(const double* S, int npieces, const typename E::raw* tp,
                                   const typename E::raw* dp, int V, const WeightFn& wf, double u,
                                   double* total_out) {
@@ -520,7 +538,7 @@ __device__ int sample_from_pieces(const double* S, int npieces, const typename E
         piece = wave_max_int(lastpos);      // rounding left the point past the end
         take_last = true;
     }
-    return scan_piece<E>(tp, dp, piece * kWave * EV, V, wf, before, target, take_last);
+    return scan_piece<E, Q>(tp, dp, piece * kWave * EV, V, wf, before, target, take_last);
 }
 
 // Inverse CDF over the whole decision row with the piece masses computed on
@@ -539,7 +557,7 @@ __device__ int sample_by_rescan(const typename E::raw* tp, int V, const WeightFn
             fp[e] = (j0 + e < V) ? E::at(tp, j0 + e) : -INFINITY;
             fq[e] = -INFINITY;
         }
-        return wave_sum((double)lane_weight_sum<E>(fp, fq, wf));
+        return wave_sum((double)lane_weight_sum<E, false>(fp, fq, wf));
     };
     double total = 0.0;
     int last = -1;
@@ -553,29 +571,50 @@ __device__ int sample_by_rescan(const typename E::raw* tp, int V, const WeightFn
     double run = 0.0;
     for (int i = 0; i < np; ++i) {
         const double m = piece_mass(i);
-        if (run + m > target && m > 0.0) return scan_piece<E>(tp, tp, i * pe, V, wf, run, target, false);
+        if (run + m > target && m > 0.0) return scan_piece<E, false>(tp, tp, i * pe, V, wf, run, target, false);
         run += m;
     }
-    return scan_piece<E>(tp, tp, last * pe, V, wf, 0.0, target, true);
+    return scan_piece<E, false>(tp, tp, last * pe, V, wf, 0.0, target, true);
 }
 
 constexpr int kSeqPerBlock = kBlock / kWave;    // decide / sample: one wave per sequence
 
-// The sequence's decision from the row partials (one wave per sequence):
-// combines the partials of each row, evaluates p_i(y_i) and q_i(y_i) in fp64, the
-// accept bits and A (wave ballot); stores A, the status bits, the probabilities
-// and the descriptor of the row(s) the final token is drawn from.
-__global__ __launch_bounds__(kBlock) void k_chain_decide(
-    const Partial* __restrict__ part_t, const Partial* __restrict__ part_d,
-    const float* __restrict__ xy, const int32_t* __restrict__ tok, const float* __restrict__ uni,
-    const int32_t* __restrict__ cu, int B, int K_max, int V, int n_chunks, float c,
-    int32_t* __restrict__ A_out, float* __restrict__ probs_out, int32_t* __restrict__ status_out,
-    ChainDesc* __restrict__ desc, const int32_t* __restrict__ cap, int32_t* __restrict__ A_full_out,
-    int hi, int32_t* __restrict__ alive, int alive_in) {
-    const int b = blockIdx.x * kSeqPerBlock + threadIdx.x / kWave;
-    if (b >= B) return;
+// Inputs and outputs of the per-sequence decision.
+struct DecideArgs {
+    const Partial* part_t;
+    const Partial* part_d;
+    const float* xy;
+    const int32_t* tok;
+    const float* uni;
+    const int32_t* cu;
+    int K_max, V, n_chunks;
+    float c;
+    int32_t* A_out;
+    float* probs_out;
+    int32_t* status_out;
+    const int32_t* cap;
+    int32_t* A_full_out;
+    int hi;             // slots streamed so far (the phase's upper bound)
+    int32_t* alive;     // per-sequence flag across phases, or null
+};
+
+// The decision of sequence b from the row partials (one wave): combines the
+// partials of each row, evaluates p_i(y_i) and q_i(y_i) in fp64, the accept
+// bits and A (wave ballot); stores A, the status bits and the probabilities,
+// and returns in d the descriptor of the row(s) the final token is drawn
+// from. Returns false, with the sequence marked alive, when every position
+// streamed so far passed and later slots remain.
+__device__ __forceinline__ bool decide_sequence(const DecideArgs& g, int b, ChainDesc& d) {
+    const Partial* __restrict__ part_t = g.part_t;
+    const Partial* __restrict__ part_d = g.part_d;
+    const float* __restrict__ xy = g.xy;
+    const int32_t* __restrict__ tok = g.tok;
+    const float* __restrict__ uni = g.uni;
+    const int K_max = g.K_max, V = g.V, n_chunks = g.n_chunks, hi = g.hi;
+    const float c = g.c;
+    float* __restrict__ probs_out = g.probs_out;
+    int32_t* __restrict__ alive = g.alive;
     const int lane = threadIdx.x & (kWave - 1);
-    if (alive_in && alive[b] == 0) return;              // decided in an earlier phase
     const int slots = K_max + 1;
     const int64_t slot0 = (int64_t)b * slots;
     // Lane s combines the partials of slot s (target, and draft below K_max)
@@ -592,7 +631,7 @@ __global__ __launch_bounds__(kBlock) void k_chain_decide(
         }
     }
     int d0, k;
-    seq_range(cu, b, K_max, d0, k);
+    seq_range(g.cu, b, K_max, d0, k);
     // positions evaluated so far: those of the slots streamed up to this phase
     const int kk = k < hi ? k : hi;
     // uniform of position `lane` (lane k_b's is the final draw's for an uncapped window)
@@ -617,16 +656,15 @@ __global__ __launch_bounds__(kBlock) void k_chain_decide(
     const unsigned long long rej = __ballot(!acc);
     if (rej == 0ull && k >= hi) {                       // every position so far passed: next phase
         if (lane == 0) alive[b] = 1;
-        return;
+        return false;
     }
     if (alive != nullptr && lane == 0) alive[b] = 0;
     const int A_full = rej ? (__ffsll(rej) - 1) : k;
-    const int kc = committed_len(cap, b, k);
+    const int kc = committed_len(g.cap, b, k);
     const int A = A_full < kc ? A_full : kc;
     int mine = (lane < kc && lane <= A) ? st : 0;
 #pragma unroll
     for (int o = kWave / 2; o > 0; o >>= 1) mine |= __shfl_xor(mine, o, kWave);
-    ChainDesc d;
     d.A = A;
     // (a 64-position window puts its final uniform and extra row past the lanes)
     d.u = kc < kWave ? __shfl(u_lane, kc, kWave) : uni[d0 + b + kc];
@@ -665,11 +703,22 @@ __global__ __launch_bounds__(kBlock) void k_chain_decide(
         d.S_q = 0.0;
     }
     if (lane == 0) {
-        A_out[b] = A;
-        if (A_full_out) A_full_out[b] = A_full;
-        if (status_out) status_out[b] = mine;
-        desc[b] = d;
+        g.A_out[b] = A;
+        if (g.A_full_out) g.A_full_out[b] = A_full;
+        if (g.status_out) g.status_out[b] = mine;
     }
+    return true;
+}
+
+// One wave per sequence: the decision after a phase; the descriptor goes to
+// the workspace for the launches that draw the final token.
+__global__ __launch_bounds__(kBlock) void k_chain_decide(DecideArgs g, int B, int alive_in,
+                                                         ChainDesc* __restrict__ desc) {
+    const int b = blockIdx.x * kSeqPerBlock + threadIdx.x / kWave;
+    if (b >= B) return;
+    if (alive_in && g.alive[b] == 0) return;            // decided in an earlier phase
+    ChainDesc d;
+    if (decide_sequence(g, b, d) && (threadIdx.x & (kWave - 1)) == 0) desc[b] = d;
 }
 
 // grid (sequence, chunk of 16-byte vectors: 4096 per workgroup): re-reads only
@@ -691,7 +740,9 @@ __global__ __launch_bounds__(kResolveThreads) void k_chain_mass(
     const typename E::raw* dp = wf.has_q ? dft + (int64_t)d.d_row * V : tp;
     const int beg = mc * mchunk;
     const int end = min(V, beg + mchunk);
-    mass_pass<E, VEC>(tp, dp, beg, end, wf, piece_ws + (int64_t)b * npieces, npieces);
+    double* pieces = piece_ws + (int64_t)b * npieces;
+    if (wf.has_q) mass_pass<E, VEC, kResolveThreads, true>(tp, dp, beg, end, wf, pieces, npieces);
+    else mass_pass<E, VEC, kResolveThreads, false>(tp, dp, beg, end, wf, pieces, npieces);
 }
 
 // One wave per sequence: the final token from the piece masses (inverse CDF in
@@ -714,11 +765,63 @@ __global__ __launch_bounds__(kBlock) void k_chain_sample(
         const typename E::raw* tp = tgt + (int64_t)d.t_row * V;
         const WeightFn wf = weight_fn(d, c, false);
         const typename E::raw* dp = wf.has_q ? dft + (int64_t)d.d_row * V : tp;
-        next = sample_from_pieces<E>(piece_ws + (int64_t)b * npieces, npieces, tp, dp, V, wf,
-                                     (double)d.u, &total);
+        const double* pieces = piece_ws + (int64_t)b * npieces;
+        next = wf.has_q ? sample_from_pieces<E, true>(pieces, npieces, tp, dp, V, wf, (double)d.u, &total)
+                        : sample_from_pieces<E, false>(pieces, npieces, tp, dp, V, wf, (double)d.u, &total);
         if (d.mode == kModeResidual && !(total > 0.0))
             next = sample_by_rescan<E>(tp, V, weight_fn(d, c, true), (double)d.u);
     }
+    if (lane == 0) {
+        next_out[b] = next;
+        if (R_out) R_out[b] = (d.mode == kModeResidual) ? (float)total : 0.f;
+    }
+}
+
+// One workgroup per sequence, after the last phase: the decision (wave 0, or
+// the descriptor of an earlier phase), the weight mass per piece of the
+// decision row(s) by every wave, then the final draw by wave 0. The piece
+// masses stay in LDS (or, for a very long row, go through the workspace: the
+// workgroup's own stores are visible to it after the barrier).
+template <class E, bool VEC>
+__global__ __launch_bounds__(kFusedThreads) void k_chain_resolve(
+    const typename E::raw* __restrict__ tgt, const typename E::raw* __restrict__ dft,
+    DecideArgs g, int alive_in, const ChainDesc* __restrict__ desc,
+    double* __restrict__ piece_ws, int32_t* __restrict__ next_out, float* __restrict__ R_out) {
+    constexpr int EV = E::kVec;
+    __shared__ ChainDesc sdesc;
+    __shared__ double spieces[kLdsPieces];
+    const int b = blockIdx.x;
+    const int lane = threadIdx.x & (kWave - 1);
+    if (threadIdx.x < kWave) {
+        ChainDesc d;
+        if (alive_in && g.alive[b] == 0) d = desc[b];   // decided in an earlier phase
+        else decide_sequence(g, b, d);                  // the window ends here: always decides
+        if (lane == 0) sdesc = d;
+    }
+    __syncthreads();
+    const ChainDesc d = sdesc;
+    if (d.mode == kModeNone) {
+        if (threadIdx.x == 0) {
+            next_out[b] = -1;
+            if (R_out) R_out[b] = 0.f;
+        }
+        return;
+    }
+    const int V = g.V;
+    const int npieces = (V + kWave * EV - 1) / (kWave * EV);
+    const typename E::raw* tp = tgt + (int64_t)d.t_row * V;
+    const WeightFn wf = weight_fn(d, g.c, false);
+    const typename E::raw* dp = wf.has_q ? dft + (int64_t)d.d_row * V : tp;
+    double* pieces = npieces <= kLdsPieces ? spieces : piece_ws + (int64_t)b * npieces;
+    if (wf.has_q) mass_pass<E, VEC, kFusedThreads, true>(tp, dp, 0, V, wf, pieces, npieces);
+    else mass_pass<E, VEC, kFusedThreads, false>(tp, dp, 0, V, wf, pieces, npieces);
+    __syncthreads();
+    if (threadIdx.x >= kWave) return;
+    double total = 0.0;
+    int next = wf.has_q ? sample_from_pieces<E, true>(pieces, npieces, tp, dp, V, wf, (double)d.u, &total)
+                        : sample_from_pieces<E, false>(pieces, npieces, tp, dp, V, wf, (double)d.u, &total);
+    if (d.mode == kModeResidual && !(total > 0.0))
+        next = sample_by_rescan<E>(tp, V, weight_fn(d, g.c, true), (double)d.u);
     if (lane == 0) {
         next_out[b] = next;
         if (R_out) R_out[b] = (d.mode == kModeResidual) ? (float)total : 0.f;
@@ -778,18 +881,47 @@ static hipError_t chain_full_impl(const ChainArgs& a) {
             if (kPhaseBounds[i] > bounds[n_phases] && kPhaseBounds[i] < a.K_max + 1)
                 bounds[++n_phases] = kPhaseBounds[i];
     bounds[++n_phases] = a.K_max + 1;
+    // The last phase's decision, the mass and the final draw run as one
+    // workgroup per sequence when that fills the device, else as a decision
+    // launch, a chunked mass launch and a one-wave-per-sequence draw.
+    const bool fused = a.B >= kFusedMinB || n_mchunks == 1;
+    DecideArgs g;
+    g.part_t = part_t;
+    g.part_d = part_d;
+    g.xy = xy;
+    g.tok = a.tokens;
+    g.uni = a.uniforms;
+    g.cu = a.cu;
+    g.K_max = a.K_max;
+    g.V = a.V;
+    g.n_chunks = nc;
+    g.c = c;
+    g.A_out = a.accepted_len;
+    g.probs_out = a.probs_out;
+    g.status_out = a.seq_status;
+    g.cap = a.cap;
+    g.A_full_out = a.accepted_full;
+    g.alive = n_phases > 1 ? alive : nullptr;
     for (int ph = 0; ph < n_phases; ++ph) {
         const int lo = bounds[ph], hi = bounds[ph + 1];
         const unsigned grid1 = (unsigned)((size_t)a.B * (hi - lo) * nc);
-        if (ph == 0) PassTimer::mark_before(a.stream);
-        hipLaunchKernelGGL((k_chain_stats<E, VEC>), dim3(grid1), dim3(kBlock), 0, a.stream, tgt, dft,
-                           a.tokens, a.cu, a.K_max, a.V, chunk, nc, c, part_t, part_d, xy, lo,
-                           hi - lo, ph > 0 ? alive : nullptr);
-        if (ph == 0) PassTimer::mark_after(a.stream);
-        hipLaunchKernelGGL(k_chain_decide, dim3(seq_blocks), dim3(kBlock), 0, a.stream, part_t,
-                           part_d, xy, a.tokens, a.uniforms, a.cu, a.B, a.K_max, a.V, nc, c,
-                           a.accepted_len, a.probs_out, a.seq_status, desc, a.cap, a.accepted_full,
-                           hi, n_phases > 1 ? alive : nullptr, ph > 0 ? 1 : 0);
+        if (ph == 0)
+            PassTimer::launch(k_chain_stats<E, VEC>, dim3(grid1), dim3(kBlock), a.stream, tgt, dft,
+                              a.tokens, a.cu, a.K_max, a.V, chunk, nc, c, part_t, part_d, xy, lo,
+                              hi - lo, (int32_t*)nullptr);
+        else
+            hipLaunchKernelGGL((k_chain_stats<E, VEC>), dim3(grid1), dim3(kBlock), 0, a.stream, tgt,
+                               dft, a.tokens, a.cu, a.K_max, a.V, chunk, nc, c, part_t, part_d, xy,
+                               lo, hi - lo, alive);
+        g.hi = hi;
+        if (fused && ph == n_phases - 1) {
+            hipLaunchKernelGGL((k_chain_resolve<E, VEC>), dim3((unsigned)a.B), dim3(kFusedThreads), 0,
+                               a.stream, tgt, dft, g, ph > 0 ? 1 : 0, desc, pieces, a.next_token,
+                               a.resid_mass_out);
+            return hipGetLastError();
+        }
+        hipLaunchKernelGGL(k_chain_decide, dim3(seq_blocks), dim3(kBlock), 0, a.stream, g, a.B,
+                           ph > 0 ? 1 : 0, desc);
     }
     hipLaunchKernelGGL((k_chain_mass<E, VEC>), dim3((unsigned)((size_t)a.B * n_mchunks)),
                        dim3(kResolveThreads), 0, a.stream, tgt, dft, desc, a.V, mchunk, n_mchunks, c,

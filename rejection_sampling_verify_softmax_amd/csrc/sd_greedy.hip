@@ -268,11 +268,9 @@ static hipError_t greedy_impl(const void* target, const int32_t* tokens, const i
     const int chunk = arg_chunk(dtype);
     ArgPartial* part = static_cast<ArgPartial*>(ws);
     const unsigned grid = (unsigned)((size_t)B * (K_max + 1) * nc);
-    PassTimer::mark_before(stream);
-    hipLaunchKernelGGL((k_argmax<E, VEC, kMapChain>), dim3(grid), dim3(kBlock), 0, stream,
-                       static_cast<const typename E::raw*>(target), cu, K_max + 1, K_max, V, chunk,
-                       nc, part);
-    PassTimer::mark_after(stream);
+    PassTimer::launch(k_argmax<E, VEC, kMapChain>, dim3(grid), dim3(kBlock), stream,
+                      static_cast<const typename E::raw*>(target), cu, K_max + 1, K_max, V, chunk, nc,
+                      part);
     hipLaunchKernelGGL(k_greedy_decide, dim3(B), dim3(kWave), 0, stream, part, tokens, cu, K_max, V,
                        nc, A, next, st, cap, A_full);
     return hipGetLastError();
@@ -304,10 +302,8 @@ static hipError_t tree_verify_impl(const void* target, const int32_t* tok, const
     const int chunk = arg_chunk(dtype);
     ArgPartial* part = static_cast<ArgPartial*>(ws);
     const unsigned grid = (unsigned)((size_t)B * N * nc);
-    PassTimer::mark_before(stream);
-    hipLaunchKernelGGL((k_argmax<E, VEC, kMapTree>), dim3(grid), dim3(kBlock), 0, stream,
-                       static_cast<const typename E::raw*>(target), nn, N, 0, V, chunk, nc, part);
-    PassTimer::mark_after(stream);
+    PassTimer::launch(k_argmax<E, VEC, kMapTree>, dim3(grid), dim3(kBlock), stream,
+                      static_cast<const typename E::raw*>(target), nn, N, 0, V, chunk, nc, part);
     hipLaunchKernelGGL(k_tree_walk, dim3(B), dim3(kWave), 0, stream, part, tok, par, nn, N, nc,
                        path, A, next);
     return hipGetLastError();

@@ -2,6 +2,7 @@
 // kernel files of libsd. Not installed; not part of the C ABI.
 #pragma once
 
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 #include <stddef.h>
 #include <stdint.h>
@@ -44,12 +45,21 @@ struct Carve {
     }
 };
 
-// Optional events around the streaming kernel of the next call on this thread
-// (set by sd_time_next_stream_pass). mark_before()/mark_after() record and then
-// clear them.
+// Optional events for the streaming kernel of the next call on this thread
+// (set by sd_time_next_stream_pass). launch() binds them to that kernel's own
+// dispatch (hipExtLaunchKernel: the events take the kernel's start and end
+// times, with no marker packets between it and its neighbours on the stream)
+// and clears them; mark_before()/mark_after() record them directly, for a call
+// that launches no streaming kernel.
 struct PassTimer {
     static thread_local hipEvent_t start;
     static thread_local hipEvent_t stop;
+    template <typename F, typename... Args>
+    static void launch(F kernel, dim3 grid, dim3 block, hipStream_t s, Args... args) {
+        hipEvent_t a = start, b = stop;
+        start = stop = nullptr;
+        hipExtLaunchKernelGGL(kernel, grid, block, 0, s, a, b, 0, args...);
+    }
     static void mark_before(hipStream_t s) {
         if (start) (void)hipEventRecord(start, s);
         start = nullptr;

@@ -75,10 +75,8 @@ hipError_t launch_compact_kv(void* kv, int64_t row_bytes, int64_t n_rows, const 
                              hipStream_t stream) {
     const int64_t words = row_bytes / 16;
     const int n_tiles = (int)((words + kKvTile - 1) / kKvTile);
-    PassTimer::mark_before(stream);
-    hipLaunchKernelGGL(k_compact_kv, dim3((unsigned)((int64_t)B * n_tiles)), dim3(kBlock), 0, stream,
-                       static_cast<kv_word*>(kv), words, base, path, accepted_len, N, n_tiles, n_rows);
-    PassTimer::mark_after(stream);
+    PassTimer::launch(k_compact_kv, dim3((unsigned)((int64_t)B * n_tiles)), dim3(kBlock), stream,
+                      static_cast<kv_word*>(kv), words, base, path, accepted_len, N, n_tiles, n_rows);
     return hipGetLastError();
 }
 

@@ -170,11 +170,9 @@ hipError_t launch_rerank_tree(const int32_t* cand_parent, const int32_t* cand_to
                               const float* cand_prob, const int32_t* n_cand, int B, int M, int N,
                               int32_t* tok, int32_t* par, int32_t* dep, float* score, uint64_t* anc,
                               int32_t* node_cand, int32_t* n_nodes, hipStream_t stream) {
-    PassTimer::mark_before(stream);
-    hipLaunchKernelGGL(k_rerank_tree, dim3(B), dim3(kBlock), 0, stream, cand_parent, cand_token,
-                       cand_prob, n_cand, M, N, tok, par, dep, score,
-                       reinterpret_cast<unsigned long long*>(anc), node_cand, n_nodes);
-    PassTimer::mark_after(stream);
+    PassTimer::launch(k_rerank_tree, dim3(B), dim3(kBlock), stream, cand_parent, cand_token,
+                      cand_prob, n_cand, M, N, tok, par, dep, score,
+                      reinterpret_cast<unsigned long long*>(anc), node_cand, n_nodes);
     return hipGetLastError();
 }
 

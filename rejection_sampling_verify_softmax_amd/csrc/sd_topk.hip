@@ -967,12 +967,16 @@ static hipError_t chain_topk_impl(const ChainArgs& a) {
     for (int ph = 0; ph < n_phases; ++ph) {
         const int lo = bounds[ph], hi = bounds[ph + 1];
         const unsigned grid = (unsigned)((size_t)a.B * (hi - lo) * 2);
-        if (ph == 0) PassTimer::mark_before(a.stream);
-        hipLaunchKernelGGL((k_topk_rows<E, VEC>), dim3(grid), dim3(kBlock), 0, a.stream,
-                           static_cast<const raw*>(a.target), static_cast<const raw*>(a.draft), a.cu,
-                           a.K_max, a.V, a.top_k, 1, a.tokens, a.temperature, L.lists, L.counts,
-                           L.rowtop, lo, hi - lo, ph > 0 ? state : nullptr, ph);
-        if (ph == 0) PassTimer::mark_after(a.stream);
+        if (ph == 0)
+            PassTimer::launch(k_topk_rows<E, VEC>, dim3(grid), dim3(kBlock), a.stream,
+                              static_cast<const raw*>(a.target), static_cast<const raw*>(a.draft),
+                              a.cu, a.K_max, a.V, a.top_k, 1, a.tokens, a.temperature, L.lists,
+                              L.counts, L.rowtop, lo, hi - lo, (int32_t*)nullptr, ph);
+        else
+            hipLaunchKernelGGL((k_topk_rows<E, VEC>), dim3(grid), dim3(kBlock), 0, a.stream,
+                               static_cast<const raw*>(a.target), static_cast<const raw*>(a.draft),
+                               a.cu, a.K_max, a.V, a.top_k, 1, a.tokens, a.temperature, L.lists,
+                               L.counts, L.rowtop, lo, hi - lo, state, ph);
         hipLaunchKernelGGL(k_chain_topk_decide, dim3(seq_blocks), dim3(kBlock), 0, a.stream, L.lists,
                            L.rowtop, a.tokens, a.uniforms, a.cu, a.B, a.K_max, a.V, a.top_k,
                            a.temperature, a.accepted_len, a.next_token, a.probs_out,
@@ -997,18 +1001,19 @@ hipError_t launch_tree_build(const float* marg, int B, int K, int V, int N, int3
     const size_t tasks = (size_t)B * K;
     TopkLayout L;
     topk_layout(ws, tasks, W, &L, 0);
-    PassTimer::mark_before(stream);
     if (tasks > 0) {
         if (V % F32::kVec == 0)
-            hipLaunchKernelGGL((k_topk_rows<F32, true>), dim3((unsigned)tasks), dim3(kBlock), 0, stream,
-                               marg, marg, nullptr, 0, V, W, 0, nullptr, 1.0f, L.lists, L.counts, nullptr,
-                               0, 1, nullptr, 0);
+            PassTimer::launch(k_topk_rows<F32, true>, dim3((unsigned)tasks), dim3(kBlock), stream, marg,
+                              marg, nullptr, 0, V, W, 0, nullptr, 1.0f, L.lists, L.counts, nullptr, 0,
+                              1, nullptr, 0);
         else
-            hipLaunchKernelGGL((k_topk_rows<F32, false>), dim3((unsigned)tasks), dim3(kBlock), 0, stream,
-                               marg, marg, nullptr, 0, V, W, 0, nullptr, 1.0f, L.lists, L.counts, nullptr,
-                               0, 1, nullptr, 0);
+            PassTimer::launch(k_topk_rows<F32, false>, dim3((unsigned)tasks), dim3(kBlock), stream, marg,
+                              marg, nullptr, 0, V, W, 0, nullptr, 1.0f, L.lists, L.counts, nullptr, 0,
+                              1, nullptr, 0);
+    } else {
+        PassTimer::mark_before(stream);
+        PassTimer::mark_after(stream);
     }
-    PassTimer::mark_after(stream);
     hipLaunchKernelGGL(k_tree_build, dim3(B), dim3(kWave), 0, stream, L.lists, L.counts, K, N, W, tok,
                        par, dep, score, reinterpret_cast<unsigned long long*>(anc), n_nodes);
     return hipGetLastError();
