@@ -31,7 +31,7 @@
 #include <math.h>
 
 #ifndef SD_STATS_UNROLL
-#define SD_STATS_UNROLL 4
+#define SD_STATS_UNROLL 2
 #endif
 
 namespace sd {

@@ -44,7 +44,8 @@ def test_config1_chain_f32():
 
 
 @pytest.mark.parametrize("dtype,V,T", [("bf16", 40000, 0.9), ("bf16", 16384 * 2 + 8, 1.0),
-                                       ("f32", 20000, 1.3), ("f32", 1001, 1.0), ("bf16", 777, 0.6)])
+                                       ("f32", 20000, 1.3), ("f32", 1001, 1.0), ("bf16", 777, 0.6),
+                                       ("bf16", 40001, 0.8), ("f32", 20003, 1.1)])
 def test_chain_small_all_sequences(dtype, V, T):
     _say(f"chain small {dtype} V={V} T={T}")
     case = wl.gen_base_noise_chain(11 + V, B=24, K=5, V=V, base_sigma=2.0, noise_sigma=0.6,
@@ -74,6 +75,26 @@ def test_chain_phased_all_sequences(dtype, V, T, B):
         assert torch.equal(one[key], ph[key]), key
     info = compare_chain(ph, oracle_chain(case, sample_seqs(B, 32, seed=V)))
     _say(f"  {info}")
+
+
+# A batch of at least 256 sequences takes the last decision, the residual mass
+# and the final draw in one workgroup per sequence (smaller batches with rows
+# longer than one mass chunk use the chunked launches above); vocabularies
+# that are not a whole number of 16-byte vectors take the element-wise loads.
+@pytest.mark.parametrize("dtype,V,T,B,K", [("bf16", 40003, 0.8, 256, 2), ("bf16", 40000, 1.0, 300, 3),
+                                           ("f32", 12001, 1.0, 300, 3)])
+def test_chain_large_batch_all_sequences(dtype, V, T, B, K):
+    _say(f"chain large batch {dtype} V={V} T={T} B={B} K={K}")
+    case = wl.gen_base_noise_chain(17 + V, B=B, K=K, V=V, base_sigma=2.0, noise_sigma=0.6,
+                                   temperature=T, dtype=dtype, device="cuda")
+    one = run_chain(case)
+    ph = run_chain(case, probs=False)
+    for key in ("accepted_len", "next_token", "status", "resid"):
+        assert torch.equal(one[key], ph[key]), key
+    info = compare_chain(one, oracle_chain(case))
+    _say(f"  {info}")
+    A = one["accepted_len"].cpu().numpy()
+    assert (A < K).any() and (A == K).any()
 
 
 def test_chain_phased_ragged():
