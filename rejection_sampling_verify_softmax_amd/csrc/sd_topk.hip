@@ -761,23 +761,21 @@ __device__ __forceinline__ int make_meta(int depth, int parent, int rank) {
     return depth | (parent << 5) | (rank << 11);
 }
 
-// a before b in the pop order (distinct prefixes never compare equal)
+// a before b in the pop order (distinct prefixes never compare equal);
+// bitwise logic, so a wave evaluates it without branches
 __device__ __forceinline__ bool prefix_before(const Prefix& a, const Prefix& b) {
-    if (a.Q != b.Q) return a.Q > b.Q;
     const int da = meta_depth(a.meta), db = meta_depth(b.meta);
-    if (da != db) return da < db;
-    if (a.w0 != b.w0) return a.w0 < b.w0;
-    return a.w1 < b.w1;
+    const bool w_less = (a.w0 < b.w0) | ((a.w0 == b.w0) & (a.w1 < b.w1));
+    return (a.Q > b.Q) | ((a.Q == b.Q) & ((da < db) | ((da == db) & w_less)));
 }
 
 __device__ __forceinline__ void set_rank(Prefix& f, int pos, int r) {
-    if (pos < 10) {
-        const int sh = 54 - 6 * pos;
-        f.w0 = (f.w0 & ~(0x3full << sh)) | ((unsigned long long)r << sh);
-    } else {
-        const int sh = 54 - 6 * (pos - 10);
-        f.w1 = (f.w1 & ~(0x3full << sh)) | ((unsigned long long)r << sh);
-    }
+    const bool lo = pos < 10;
+    const int sh = 54 - 6 * (lo ? pos : pos - 10);
+    const unsigned long long w = lo ? f.w0 : f.w1;
+    const unsigned long long v = (w & ~(0x3full << sh)) | ((unsigned long long)r << sh);
+    f.w0 = lo ? v : f.w0;
+    f.w1 = lo ? f.w1 : v;
 }
 
 __device__ __forceinline__ unsigned long long readlane64(unsigned long long v, int l) {
@@ -846,7 +844,9 @@ __global__ __launch_bounds__(kWave) void k_tree_build(
     }
     int n = 1;
     for (; n < N && cnt > 0; ++n) {
-        Prefix X;                    // the head: node n
+        // The head (lane 0) is node n. Wave-uniform values live in scalar
+        // registers; the per-lane work is selects and compares, no branches.
+        Prefix X;
         X.Q = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, f.Q), 0));
         X.meta = __builtin_amdgcn_readlane(f.meta, 0);
         X.w0 = readlane64(f.w0, 0);
@@ -856,37 +856,37 @@ __global__ __launch_bounds__(kWave) void k_tree_build(
         const float par_score = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, my_score), par));
         const int cnt_sib = __builtin_amdgcn_readlane(cnt_d, m - 1);
         const bool hasS = rk + 1 < cnt_sib;
-        const float q_sib = hasS ? qv[m - 1][rk + 1] : 0.f;
-        const bool hasC = m < K && __builtin_amdgcn_readlane(cnt_d, m < K ? m : 0) > 0;
-        const float q_child = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, q0_d), m < K ? m : 0));
-        if (lane == n) {
-            my_tok = tv[m - 1][rk];
-            my_par = par;
-            my_dep = m;
-            my_score = X.Q;
-            my_anc = anc;
-        }
+        // (both LDS reads stay inside the list rows: rk + 1 <= 63)
+        const float q_sib = qv[m - 1][rk + 1 < 64 ? rk + 1 : 63];
+        const int tok_n = tv[m - 1][rk];
+        const int mc = m < K ? m : 0;
+        const bool hasC = m < K && __builtin_amdgcn_readlane(cnt_d, mc) > 0;
+        const float q_child = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, q0_d), mc));
+        const bool me = lane == n;
+        my_tok = me ? tok_n : my_tok;
+        my_par = me ? par : my_par;
+        my_dep = me ? m : my_dep;
+        my_score = me ? X.Q : my_score;
+        my_anc = me ? anc : my_anc;
         // its first child and its next sibling
-        Prefix C = X, S = X;
-        if (hasC) {
-            C.Q = X.Q * q_child;
-            C.meta = make_meta(m + 1, n, 0);     // rank 0 at depth m: its tuple slot is already 0
-        }
-        if (hasS) {
-            S.Q = par_score * q_sib;
-            S.meta = make_meta(m, par, rk + 1);
-            set_rank(S, m - 1, rk + 1);
-        }
+        Prefix C, S = X;
+        C.Q = X.Q * q_child;
+        C.meta = make_meta(m + 1, n, 0);         // rank 0 at depth m: its tuple slot is already 0
+        C.w0 = X.w0;
+        C.w1 = X.w1;
+        S.Q = par_score * q_sib;
+        S.meta = make_meta(m, par, rk + 1);
+        set_rank(S, m - 1, rk + 1);
         // places among the rest of the frontier (lanes 1 .. cnt-1)
         const bool rest = lane >= 1 && lane < cnt;
-        const int pc = hasC ? __popcll(__ballot(rest && prefix_before(f, C))) : 0;
-        const int ps = hasS ? __popcll(__ballot(rest && prefix_before(f, S))) : 0;
+        const int pc = __popcll(__ballot(hasC & rest & prefix_before(f, C)));
+        const int ps = __popcll(__ballot(hasS & rest & prefix_before(f, S)));
         const bool s_first = hasC && hasS && prefix_before(S, C);
         const int fC = hasC ? pc + (s_first ? 1 : 0) : -1;
         const int fS = hasS ? ps + ((hasC && !s_first) ? 1 : 0) : -1;
         // lane j takes C, S, or the entry that lands on j: from lane j+1 when
         // neither was placed before j, lane j after one, lane j-1 after both
-        const int nb = ((fC >= 0 && fC < lane) ? 1 : 0) + ((fS >= 0 && fS < lane) ? 1 : 0);
+        const int nb = ((fC >= 0) & (fC < lane) ? 1 : 0) + ((fS >= 0) & (fS < lane) ? 1 : 0);
         const bool tc = lane == fC, ts = lane == fS;
         const float gQ = __builtin_bit_cast(float, shift_pick(__builtin_bit_cast(uint32_t, f.Q), nb));
         const int gm = (int)shift_pick((uint32_t)f.meta, nb);
