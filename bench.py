@@ -193,7 +193,7 @@ def setup_tree(torch, sd, wl):
 
     meta = {"workload": f"DDTree build (B={B}, K={K}, V={V} fp32 marginals, N={N}) + walk over bf16 target rows",
             "global_batch": B, "K_max": K, "V": V, "positions_per_step": B * (N - 1),
-            "kernel": "k_topk_rows<f32>", "kernel_bytes": B * K * V * 4,
+            "kernel": "k_topk_short<f32>", "kernel_bytes": B * K * V * 4,
             "step_bytes": B * K * V * 4 + B * N * V * 2}
     return step, meta, None
 

@@ -14,6 +14,10 @@
 // is sorted (bitonic, LDS) and cut back to k, which raises the threshold. The
 // result is exact for any arrival order, because an element is dropped only
 // when k kept elements already beat it.
+//
+// k_topk_short: rows of up to 32768 fp32 marginals (the tree's) are held in
+// the registers of one workgroup, which bounds the top W from its threads'
+// maxima and ranks the few tokens above the bound.
 #include "sd_device.hpp"
 #include "sd_internal.hpp"
 
@@ -908,6 +912,242 @@ __global__ __launch_bounds__(kWave) void k_tree_build(
     if (lane == 0) n_nodes[b] = n;
 }
 
+// ---------------------------------------------------------------------------
+// Exact top-W of a short row held in registers (the tree's per-depth marginal
+// rows): one 512-thread workgroup per row, 16 vectors per thread, in the key
+// order above (value desc, id asc; NaN never kept).
+//  1. Every thread loads its vectors (all in flight together) and takes its
+//     largest value.
+//  2. Each wave's 8th-largest thread maximum (equal maxima leave together)
+//     is reached by at least 8 of the wave's tokens, so the smallest of them
+//     over the 8 waves (t) is reached by at least 64 > W tokens: every token
+//     of the top W has a value >= t.
+//  3. The tokens with a value >= t (about a hundred on a row of
+//     probabilities) go to LDS as keys by a block scan; each takes its rank
+//     by counting the larger keys, and the first W are written in rank order.
+//  4. Should more than kShortCap tokens reach t (mass ties), a key bound is
+//     found by bisection over the key space, reached by at least W and at
+//     most kShortCap keys (keys are distinct, so such a bound exists).
+// The passes compare plain values; 64-bit keys are formed for candidates only.
+// ---------------------------------------------------------------------------
+constexpr int kShortThreads = 512;
+constexpr int kShortVecs = 16;                  // 16-byte vectors per thread
+constexpr int kShortWaves = kShortThreads / kWave;
+constexpr int kShortRth = 8;                    // kShortRth * kShortWaves > W
+constexpr int kShortCap = 512;                  // candidates ranked by counting
+static_assert(kShortRth * kShortWaves >= 64, "the bound must be reached by W <= 63 tokens");
+
+// DPP row operations (no LDS round trip): v from lane i-n of the same row of
+// 16 (row_shr:n; 0 where there is none), and the last lane of the previous
+// row (row_bcast:15) or of the previous pair of rows (row_bcast:31) into the
+// rows selected by the mask (0 elsewhere). The whole wave must be active.
+template <int CTRL, int ROWS>
+__device__ __forceinline__ uint32_t dpp_from(uint32_t v) {
+    return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, CTRL, ROWS, 0xf, false);
+}
+
+// Maximum over the wave, returned to every lane.
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
+    v = max(v, dpp_from<0x111, 0xf>(v));
+    v = max(v, dpp_from<0x112, 0xf>(v));
+    v = max(v, dpp_from<0x114, 0xf>(v));
+    v = max(v, dpp_from<0x118, 0xf>(v));
+    v = max(v, dpp_from<0x142, 0xa>(v));
+    v = max(v, dpp_from<0x143, 0xc>(v));
+    return __builtin_amdgcn_readlane(v, kWave - 1);
+}
+
+// Inclusive prefix sum across the wave (lane order) of non-negative counts.
+__device__ __forceinline__ int wave_incl_scan_int(int c) {
+    uint32_t v = (uint32_t)c;
+    v += dpp_from<0x111, 0xf>(v);
+    v += dpp_from<0x112, 0xf>(v);
+    v += dpp_from<0x114, 0xf>(v);
+    v += dpp_from<0x118, 0xf>(v);
+    v += dpp_from<0x142, 0xa>(v);
+    v += dpp_from<0x143, 0xc>(v);
+    return (int)v;
+}
+
+template <class E, bool VEC>
+__global__ __launch_bounds__(kShortThreads) void k_topk_short(const typename E::raw* __restrict__ rows,
+                                                              int V, int W,
+                                                              TopEntry* __restrict__ lists,
+                                                              int32_t* __restrict__ counts) {
+    __shared__ unsigned long long cand[kShortCap];
+    __shared__ uint32_t wkey[kShortWaves];
+    __shared__ int wsum[kShortWaves];
+    constexpr int EV = E::kVec;
+    const int task = blockIdx.x;
+    const typename E::raw* row = rows + (int64_t)task * V;
+    const int tid = threadIdx.x;
+    const int w = tid / kWave;
+    const int lane = tid & (kWave - 1);
+    const int gvend = (V + EV - 1) / EV;
+    uint4 v[kShortVecs];
+#pragma unroll
+    for (int i = 0; i < kShortVecs; ++i) v[i] = topk_raw<E, VEC>(row, V, gvend, i * kShortThreads + tid);
+    // Each pass reads the raw data and a token base that are opaque to the
+    // optimiser, so that no per-token value is kept alive across passes.
+    int jb = tid * EV;
+    auto fresh = [&]() __attribute__((always_inline)) {
+#pragma unroll
+        for (int i = 0; i < kShortVecs; ++i)
+            asm volatile("" : "+v"(v[i].x), "+v"(v[i].y), "+v"(v[i].z), "+v"(v[i].w));
+        asm volatile("" : "+v"(jb));
+    };
+    // block sum of per-thread counts (every thread gets it) and, in *excl,
+    // the sum over the threads before this one
+    auto block_count = [&](int c, int* excl) __attribute__((always_inline)) -> int {
+        const int ws = wave_incl_scan_int(c);
+        __syncthreads();             // wsum is reused
+        if (lane == kWave - 1) wsum[w] = ws;
+        __syncthreads();
+        int tot = 0, before = ws - c;
+#pragma unroll
+        for (int i = 0; i < kShortWaves; ++i) {
+            before += i < w ? wsum[i] : 0;
+            tot += wsum[i];
+        }
+        *excl = before;
+        return tot;
+    };
+    // number of this thread's tokens with a value >= t (NaN never)
+    auto count_ge = [&](float t) __attribute__((always_inline)) -> int {
+        fresh();
+        int c = 0;
+#pragma unroll
+        for (int i = 0; i < kShortVecs; ++i) {
+#pragma unroll
+            for (int e = 0; e < EV; ++e) c += raw_elem<E>(v[i], e) >= t ? 1 : 0;
+            __builtin_amdgcn_sched_barrier(0);
+        }
+        return c;
+    };
+    // number of this thread's keys >= k (k > 0), for the bisection; it reads
+    // the row again, one vector at a time (the rare path keeps no second copy
+    // of the row in registers)
+    auto count_key_ge = [&](unsigned long long k) __attribute__((always_inline)) -> int {
+        int c = 0;
+#pragma unroll 1
+        for (int i = 0; i < kShortVecs; ++i) {
+            const int gvi = i * kShortThreads + tid;
+            const uint4 u = topk_raw<E, VEC>(row, V, gvend, gvi);
+#pragma unroll
+            for (int e = 0; e < EV; ++e) {
+                const float x = raw_elem<E>(u, e);
+                c += (x == x && make_key(x, gvi * EV + e) >= k) ? 1 : 0;
+            }
+        }
+        return c;
+    };
+    // 1. the thread's largest value (fmaxf skips NaN; NaN only if all are)
+    float m = NAN;
+#pragma unroll
+    for (int i = 0; i < kShortVecs; ++i)
+#pragma unroll
+        for (int e = 0; e < EV; ++e) m = fmaxf(m, raw_elem<E>(v[i], e));
+    // 2. each wave's kShortRth-th largest thread maximum, as order-preserving
+    // bits (0: none); each round retires every thread at the round's maximum
+    uint32_t mine = (m == m) ? ordered_bits(m) : 0u, rth = 0u;
+#pragma unroll
+    for (int r = 0; r < kShortRth; ++r) {
+        rth = wave_max_u32(mine);
+        if (mine == rth) mine = 0u;
+    }
+    if (lane == 0) wkey[w] = rth;
+    __syncthreads();
+    uint32_t tb = wkey[0];
+#pragma unroll
+    for (int i = 1; i < kShortWaves; ++i) tb = min(tb, wkey[i]);
+    // a wave without kShortRth kept maxima: every kept token competes
+    const float t = tb == 0u ? -INFINITY : from_ordered(tb);
+    int c = count_ge(t);
+    int off = 0;
+    int total = block_count(c, &off);
+    // candidate test: value >= t, or (after a bisection) key >= kb
+    bool by_key = false;
+    unsigned long long kb = 0ull;
+    if (total > kShortCap) {
+        // 4. mass ties: bisection over keys for a bound reached by W ..
+        // kShortCap keys; lo is reached by more than kShortCap keys, hi by none
+        // (the key of t's value at token 0 is not below any key of value >= t)
+        unsigned long long lo = make_key(t, 0) & 0xffffffff00000000ull;
+        unsigned long long hi = 0xffffffffffffffffull;
+        // Halving a 64-bit interval: at most 64 rounds. The interval never
+        // narrows to one key (one key separates counts that differ by at most
+        // one, and kShortCap >= W), so a bound is found before that.
+        for (int it = 0; it < 64; ++it) {
+            const unsigned long long mid = lo + ((hi - lo) >> 1);
+            int unused;
+            const int n = block_count(count_key_ge(mid), &unused);
+            if (n > kShortCap) {
+                lo = mid;
+            } else if (n >= W) {
+                kb = mid;
+                break;
+            } else {
+                hi = mid;
+            }
+        }
+        by_key = true;
+        c = count_key_ge(kb);
+        total = block_count(c, &off);
+    }
+    // 3. the candidates to LDS at their scanned offsets, then ranks by counting
+    {
+        fresh();
+#pragma unroll
+        for (int i = 0; i < kShortVecs; ++i) {
+#pragma unroll
+            for (int e = 0; e < EV; ++e) {
+                const float x = raw_elem<E>(v[i], e);
+                if (x >= t) {
+                    const unsigned long long k = make_key(x, jb + i * kShortThreads * EV + e);
+                    if ((!by_key || k >= kb) && off < kShortCap) cand[off++] = k;
+                }
+            }
+            __builtin_amdgcn_sched_barrier(0);
+        }
+    }
+    __syncthreads();
+    total = total < kShortCap ? total : kShortCap;
+    TopEntry* L = lists + (int64_t)task * W;
+    auto put = [&](unsigned long long k, int rank) __attribute__((always_inline)) {
+        if (rank < W) {
+            TopEntry te;
+            te.idx = (int32_t)(0xffffffffu - (uint32_t)(k & 0xffffffffull));
+            te.x = from_ordered((uint32_t)(k >> 32));
+            L[rank] = te;
+        }
+    };
+    if (total <= kShortThreads / 4) {
+        // four threads (a DPP quad) count a quarter of the larger keys each
+        const int ci = tid >> 2, part = tid & 3;
+        const unsigned long long k = ci < total ? cand[ci] : ~0ull;
+        int r = 0;
+        for (int j = part; j < total; j += 4) r += cand[j] > k ? 1 : 0;
+        r += __builtin_amdgcn_update_dpp(0, r, 0xb1, 0xf, 0xf, false);   // quad_perm [1,0,3,2]
+        r += __builtin_amdgcn_update_dpp(0, r, 0x4e, 0xf, 0xf, false);   // quad_perm [2,3,0,1]
+        if (ci < total && part == 0) put(k, r);
+    } else {
+        for (int ci = tid; ci < total; ci += kShortThreads) {
+            const unsigned long long k = cand[ci];
+            int rank = 0;
+            for (int j = 0; j < total; ++j) rank += cand[j] > k ? 1 : 0;
+            put(k, rank);
+        }
+    }
+    const int kept = total < W ? total : W;
+    for (int i = kept + tid; i < W; i += kShortThreads) {
+        TopEntry te;
+        te.idx = -1;
+        te.x = -INFINITY;
+        L[i] = te;
+    }
+    if (tid == 0) counts[task] = kept;
+}
+
 }  // namespace
 
 struct TopkLayout {
@@ -1001,7 +1241,14 @@ hipError_t launch_tree_build(const float* marg, int B, int K, int V, int N, int3
     const size_t tasks = (size_t)B * K;
     TopkLayout L;
     topk_layout(ws, tasks, W, &L, 0);
-    if (tasks > 0) {
+    if (tasks > 0 && V <= kShortThreads * kShortVecs * F32::kVec) {
+        if (V % F32::kVec == 0)
+            PassTimer::launch(k_topk_short<F32, true>, dim3((unsigned)tasks), dim3(kShortThreads), stream,
+                              marg, V, W, L.lists, L.counts);
+        else
+            PassTimer::launch(k_topk_short<F32, false>, dim3((unsigned)tasks), dim3(kShortThreads), stream,
+                              marg, V, W, L.lists, L.counts);
+    } else if (tasks > 0) {
         if (V % F32::kVec == 0)
             PassTimer::launch(k_topk_rows<F32, true>, dim3((unsigned)tasks), dim3(kBlock), stream, marg,
                               marg, nullptr, 0, V, W, 0, nullptr, 1.0f, L.lists, L.counts, nullptr, 0,

@@ -382,6 +382,31 @@ def test_tree_build_ties():
     _tree_compare(out, ref)
 
 
+# Rows of up to 32768 fp32 marginals take the register-resident top-k (one
+# workgroup holds the row); longer rows take the streaming top-k.
+@pytest.mark.parametrize("V", [32768, 32767, 32769, 40000])
+def test_tree_build_row_length_paths(V):
+    B, K, N = 3, 4, 64
+    case = wl.gen_config4(device="cuda", seed=9 + V, B=B, K=K, V=V, N=N, sigma=2.5)
+    out = sd.build_tree(case.marginals, N)
+    ref = oracle.build_tree(wl.to_host_f32(case.marginals), B, K, V, N)
+    _tree_compare(out, ref)
+
+
+def test_tree_build_mass_ties():
+    # thousands of equal marginals at the top of a row: more tokens than the
+    # short top-k ranks at once reach its first bound, which is then raised
+    B, K, V, N = 2, 3, 30000, 64
+    g = torch.Generator(device="cuda").manual_seed(3)
+    m = torch.rand(B, K, V, generator=g, device="cuda") * 1e-5
+    m[0, :, ::7] = 1e-4
+    m[1, 1, :] = 1.0 / V
+    m[1, 2, 5000:9000] = 2e-4
+    out = sd.build_tree(m, N)
+    ref = oracle.build_tree(m.cpu().numpy(), B, K, V, N)
+    _tree_compare(out, ref)
+
+
 def test_config4_tree_full():
     _say("config 4: tree B=32 K=16 V=32000 N=64")
     case = wl.gen_config4(device="cuda")
