@@ -17,6 +17,8 @@ namespace sd {
 
 namespace {
 
+constexpr int kSelectLds = 4096;         // lengths kept in LDS for the offsets
+
 // With `table` (the cost of verifying position j+1 at table[j]) the length is
 // the smallest maximiser of f(k) = 1 + sum_{j<=k} s_j - sum_{j<=k} table[j-1],
 // both sums running in fp64 in position order; without it, the length extends
@@ -29,6 +31,7 @@ __global__ __launch_bounds__(kBlock) void k_select_len(const float* __restrict__
                                                        float* __restrict__ adv,
                                                        int32_t* __restrict__ cu_sel) {
     __shared__ double scan_scratch[kWavesPerBlock];
+    __shared__ int32_t sk[kSelectLds];       // the lengths again, for the offsets
     const int per = (B + kBlock - 1) / kBlock;
     const int b0 = threadIdx.x * per;
     const int b1 = min(B, b0 + per);
@@ -39,6 +42,7 @@ __global__ __launch_bounds__(kBlock) void k_select_len(const float* __restrict__
         int k = 0;
         if (table == nullptr) {
             bool go = true;
+#pragma unroll 8
             for (int j = 0; j < K_max; ++j) {
                 s = s * conf[(int64_t)b * K_max + j];     // fp32, left to right
                 if (go && s > cost) {
@@ -63,6 +67,7 @@ __global__ __launch_bounds__(kBlock) void k_select_len(const float* __restrict__
             }
         }
         k_sel[b] = k;
+        if (b < kSelectLds) sk[b] = k;
         if (adv) adv[b] = (float)(1.0 + sum);
         local += k;
     }
@@ -72,7 +77,7 @@ __global__ __launch_bounds__(kBlock) void k_select_len(const float* __restrict__
     int run = (int)excl;
     for (int b = b0; b < b1; ++b) {
         cu_sel[b] = run;
-        run += k_sel[b];
+        run += b < kSelectLds ? sk[b] : k_sel[b];    // (this thread's own stores)
     }
     if (threadIdx.x == kBlock - 1) cu_sel[B] = (int)total;
 }
