@@ -581,9 +581,12 @@ __device__ int list_inverse_cdf(const TopEntry* P, const RowTop& sp, const TopEn
         const int id = pl[i].idx;
         double wgt = exp((double)pl[i].x / T - sp.m) / sp.S;
         if (residual) {
-            double q = 0.0;
-            for (int j = 0; j < nd; ++j)
-                if (dl[j].idx == id) q = exp((double)dl[j].x / T - sq.m) / sq.S;
+            // q_j from the draft list (ids are distinct within a list); the
+            // search first, then one exp, so the wave never runs an exp per
+            // list entry
+            int jm = -1;
+            for (int j = 0; j < nd; ++j) jm = (dl[j].idx == id) ? j : jm;
+            const double q = jm >= 0 ? exp((double)dl[jm].x / T - sq.m) / sq.S : 0.0;
             wgt = wgt - q;
             if (!(wgt > 0.0)) wgt = 0.0;
         }
