@@ -132,6 +132,50 @@ __device__ __forceinline__ double wave_excl_scan(double v) {
     return incl - v;
 }
 
+// ---------------------------------------------------------------------------
+// Wave-level LDS sorting and ranking of 64-bit keys.
+// ---------------------------------------------------------------------------
+// Orders the wave's LDS traffic: every lane's earlier LDS writes are visible
+// to every lane's later LDS reads.
+__device__ __forceinline__ void wave_lds_sync() {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+// Bitonic sort (descending) of a[0..n) by one wave, n a power of two.
+__device__ inline void wave_sort_desc(unsigned long long* a, int n) {
+    const int lane = threadIdx.x & (kWave - 1);
+    for (int size = 2; size <= n; size <<= 1) {
+        for (int stride = size >> 1; stride > 0; stride >>= 1) {
+            wave_lds_sync();
+            for (int i = lane; i < n / 2; i += kWave) {
+                const int lo = 2 * stride * (i / stride) + (i % stride);
+                const int hi = lo + stride;
+                const bool desc = (lo & size) == 0;
+                const unsigned long long x = a[lo], y = a[hi];
+                if ((x < y) == desc) {
+                    a[lo] = y;
+                    a[hi] = x;
+                }
+            }
+        }
+    }
+    wave_lds_sync();
+}
+
+// Number of keys in list[0..n) (sorted descending, distinct) above key.
+__device__ __forceinline__ int count_above(const unsigned long long* list, int n,
+                                           unsigned long long key) {
+    int lo = 0, hi = n;
+    while (lo < hi) {
+        const int mid = (lo + hi) >> 1;
+        if (list[mid] > key) lo = mid + 1;
+        else hi = mid;
+    }
+    return lo;
+}
+
 // Block-wide reductions for kBlock threads; `scratch` holds kWavesPerBlock entries.
 // Every thread receives the result. Contains __syncthreads().
 __device__ inline double block_sum(double v, double* scratch) {

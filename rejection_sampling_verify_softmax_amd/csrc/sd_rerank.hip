@@ -14,8 +14,9 @@
 // parent under that order, so the kept set is closed under taking parents.
 // Nodes are numbered in that order, with the outputs of the DDTree build.
 //
-// One workgroup per sequence: level-synchronous confidences in LDS, one
-// bitonic sort of 64-bit keys, then one thread per kept node.
+// One workgroup per sequence: level-synchronous confidences in LDS; each wave
+// sorts the 64-bit keys of its quarter of the candidates, and the four lists'
+// heads merge by rank into the kept nodes; then one thread per kept node.
 #include "sd_device.hpp"
 #include "sd_internal.hpp"
 
@@ -42,7 +43,8 @@ __global__ __launch_bounds__(kBlock) void k_rerank_tree(
     __shared__ int par[kMaxCand];
     __shared__ int depth[kMaxCand];
     __shared__ unsigned char ready[kMaxCand];
-    __shared__ unsigned long long keys[kMaxCand];
+    __shared__ unsigned long long wkeys[kWavesPerBlock][kWave * kCandPerThread];
+    __shared__ unsigned long long top[64];
     __shared__ int node_of[kMaxCand];
     const int b = blockIdx.x;
     const int tid = threadIdx.x;
@@ -99,34 +101,37 @@ __global__ __launch_bounds__(kBlock) void k_rerank_tree(
         }
         more = __syncthreads_or(any) != 0;
     }
-    // 3. keys: (confidence desc, depth asc, index asc); 0 = not a candidate
+    // 3. keys: (confidence desc, depth asc, index asc); 0 = not a candidate.
+    //    Each wave sorts its own candidates' keys; a key among the first N-1
+    //    of its wave's list takes its rank from its place there plus, by
+    //    binary search, the keys above it in the other waves' first N-1.
+    const int w = tid / kWave, lane = tid & (kWave - 1);
+    unsigned long long* wk = wkeys[w];
 #pragma unroll
     for (int j = 0; j < kCandPerThread; ++j) {
         const int i = j * kBlock + tid;
-        keys[i] = (i > 0 && ready[i]) ? ((unsigned long long)conf_bits(score[i]) << 32) |
-                                            ((unsigned long long)(0xffff - depth[i]) << 16) |
-                                            (unsigned long long)(0xffff - i)
-                                      : 0ull;
+        wk[lane * kCandPerThread + j] =
+            (i > 0 && ready[i]) ? ((unsigned long long)conf_bits(score[i]) << 32) |
+                                      ((unsigned long long)(0xffff - depth[i]) << 16) |
+                                      (unsigned long long)(0xffff - i)
+                                : 0ull;
     }
+    wave_sort_desc(wk, kWave * kCandPerThread);
+    const int kept_max = N - 1;
+    if (tid < 64) top[tid] = 0ull;
     __syncthreads();
-    for (int size = 2; size <= kMaxCand; size <<= 1) {
-        for (int stride = size >> 1; stride > 0; stride >>= 1) {
-            for (int t = tid; t < kMaxCand / 2; t += kBlock) {
-                const int lo = 2 * stride * (t / stride) + (t % stride);
-                const int hi = lo + stride;
-                const bool desc = (lo & size) == 0;
-                const unsigned long long x = keys[lo], y = keys[hi];
-                if ((x < y) == desc) {
-                    keys[lo] = y;
-                    keys[hi] = x;
-                }
-            }
-            __syncthreads();
+    for (int p = lane; p < kept_max; p += kWave) {
+        const unsigned long long key = wk[p];
+        if (key != 0ull) {
+            int rank = p;
+            for (int o = 0; o < kWavesPerBlock; ++o)
+                if (o != w) rank += count_above(wkeys[o], kept_max, key);
+            if (rank < kept_max) top[rank] = key;
         }
     }
+    __syncthreads();
     // 4. the first N-1 keys are the kept nodes, numbered in order
-    const int kept_max = N - 1;
-    if (tid < kept_max && keys[tid] != 0ull) node_of[0xffff - (int)(keys[tid] & 0xffffull)] = tid + 1;
+    if (tid < kept_max && top[tid] != 0ull) node_of[0xffff - (int)(top[tid] & 0xffffull)] = tid + 1;
     __syncthreads();
     const int64_t on = (int64_t)b * N;
     if (tid < N) {
@@ -134,7 +139,7 @@ __global__ __launch_bounds__(kBlock) void k_rerank_tree(
         float sc = 1.0f;
         unsigned long long anc = 1ull;
         if (tid > 0) {
-            const unsigned long long key = keys[tid - 1];
+            const unsigned long long key = top[tid - 1];
             if (key != 0ull) {
                 cand = 0xffff - (int)(key & 0xffffull);
                 tok = cand_token[o + cand];
@@ -159,7 +164,7 @@ __global__ __launch_bounds__(kBlock) void k_rerank_tree(
     }
     if (tid == 0) {
         int k = 0;
-        while (k < kept_max && keys[k] != 0ull) ++k;
+        while (k < kept_max && top[k] != 0ull) ++k;
         n_nodes[b] = 1 + k;
     }
 }

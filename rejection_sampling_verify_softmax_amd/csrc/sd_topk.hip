@@ -149,35 +149,6 @@ __device__ __forceinline__ bool vec_reaches(const uint4& v, float t) {
     return r;
 }
 
-// Orders the wave's LDS traffic: every lane's earlier LDS writes are visible
-// to every lane's later LDS reads.
-__device__ __forceinline__ void wave_lds_sync() {
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-    __builtin_amdgcn_wave_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-}
-
-// Bitonic sort (descending) of a[0..n) by one wave, n a power of two.
-__device__ void wave_sort_desc(unsigned long long* a, int n) {
-    const int lane = threadIdx.x & (kWave - 1);
-    for (int size = 2; size <= n; size <<= 1) {
-        for (int stride = size >> 1; stride > 0; stride >>= 1) {
-            wave_lds_sync();
-            for (int i = lane; i < n / 2; i += kWave) {
-                const int lo = 2 * stride * (i / stride) + (i % stride);
-                const int hi = lo + stride;
-                const bool desc = (lo & size) == 0;
-                const unsigned long long x = a[lo], y = a[hi];
-                if ((x < y) == desc) {
-                    a[lo] = y;
-                    a[hi] = x;
-                }
-            }
-        }
-    }
-    wave_lds_sync();
-}
-
 // A wave's running top-k: `cnt` keys in its LDS buffer, every kept key beats
 // `thr` (whose value part is `tf`); `seen` counts every key ever appended.
 // Uniform across the wave's lanes.
@@ -348,18 +319,6 @@ __device__ __forceinline__ WaveTop row_pass(const typename E::raw* row, int V, i
     }
     offer_range<E, VEC, POS>(o, row, V, gvend, v_start, topk);
     return wave_compact(wb, o.st, topk);
-}
-
-// Number of keys in list[0..n) (sorted descending, distinct) above key.
-__device__ __forceinline__ int count_above(const unsigned long long* list, int n,
-                                           unsigned long long key) {
-    int lo = 0, hi = n;
-    while (lo < hi) {
-        const int mid = (lo + hi) >> 1;
-        if (list[mid] > key) lo = mid + 1;
-        else hi = mid;
-    }
-    return lo;
 }
 
 // Softmax statistics of a kept list and p(y) of one token (fp64).
