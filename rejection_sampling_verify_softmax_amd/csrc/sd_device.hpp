@@ -132,6 +132,38 @@ __device__ __forceinline__ double wave_excl_scan(double v) {
     return incl - v;
 }
 
+// DPP row operations (no LDS round trip): v from lane i-n of the same row of
+// 16 (row_shr:n; 0 where there is none), and the last lane of the previous
+// row (row_bcast:15) or of the previous pair of rows (row_bcast:31) into the
+// rows selected by the mask (0 elsewhere). The whole wave must be active.
+template <int CTRL, int ROWS>
+__device__ __forceinline__ uint32_t dpp_from(uint32_t v) {
+    return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, CTRL, ROWS, 0xf, false);
+}
+
+// Maximum over the wave, returned to every lane.
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
+    v = max(v, dpp_from<0x111, 0xf>(v));
+    v = max(v, dpp_from<0x112, 0xf>(v));
+    v = max(v, dpp_from<0x114, 0xf>(v));
+    v = max(v, dpp_from<0x118, 0xf>(v));
+    v = max(v, dpp_from<0x142, 0xa>(v));
+    v = max(v, dpp_from<0x143, 0xc>(v));
+    return __builtin_amdgcn_readlane(v, kWave - 1);
+}
+
+// Inclusive prefix sum across the wave (lane order) of non-negative counts.
+__device__ __forceinline__ int wave_incl_scan_int(int c) {
+    uint32_t v = (uint32_t)c;
+    v += dpp_from<0x111, 0xf>(v);
+    v += dpp_from<0x112, 0xf>(v);
+    v += dpp_from<0x114, 0xf>(v);
+    v += dpp_from<0x118, 0xf>(v);
+    v += dpp_from<0x142, 0xa>(v);
+    v += dpp_from<0x143, 0xc>(v);
+    return (int)v;
+}
+
 // ---------------------------------------------------------------------------
 // Wave-level LDS sorting and ranking of 64-bit keys.
 // ---------------------------------------------------------------------------

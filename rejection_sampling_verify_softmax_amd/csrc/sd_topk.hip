@@ -372,10 +372,10 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(4))) voi
                                                       int phase) {
     __shared__ unsigned long long wbuf[kWavesPerBlock][kWaveCap];
     __shared__ int32_t qi_all[kWavesPerBlock][kQueue];
-    __shared__ float lmax[kBlock];
+    __shared__ uint32_t smax[kWavesPerBlock][kWave];
+    __shared__ uint32_t t_guess_b, t_safe_b;
     __shared__ int wcnt[kWavesPerBlock];
     __shared__ int wseen[kWavesPerBlock];
-    __shared__ float t_guess, t_safe;
     __shared__ double red[kWavesPerBlock];
     constexpr int EV = E::kVec;
     // chain: block -> (sequence, slot in [slot_lo, slot_lo + slot_span), side);
@@ -416,27 +416,57 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(4))) voi
     for (int i = 0; i < kTopkSample; ++i)
         asm volatile("" : "+v"(hs[i].x), "+v"(hs[i].y), "+v"(hs[i].z), "+v"(hs[i].w));
     const bool any = m == m;
-    lmax[tid] = m;
-    if (tid == 0) {
-        t_guess = -INFINITY;
-        t_safe = -INFINITY;
-    }
-    __syncthreads();
+    // The maxima's ranks (value desc; NaN not ranked) without comparing every
+    // pair: each wave sorts its 64 maxima as order-preserving bits (0 = none)
+    // in registers, and a lane finds the range of ranks its value holds among
+    // all four sorted lists by binary search. The value at rank jg is the
+    // guess; the one at rank topk - 1 is reached by topk sampled tokens, a
+    // guaranteed bound.
     const int jg = guess_rank(topk, min(V, kTopkSample * kBlock * EV), V);
-    if (any) {
-        int rank = 0;
-#pragma unroll 8
-        for (int j = 0; j < kBlock; ++j) {
-            const float x = lmax[j];
-            rank += (x > m) || (x == m && j < tid);
+    const uint32_t mb = any ? ordered_bits(m) : 0u;
+    uint32_t sv = mb;
+#pragma unroll
+    for (int k = 2; k <= kWave; k <<= 1)
+#pragma unroll
+        for (int j = k >> 1; j > 0; j >>= 1) {
+            const uint32_t o = (uint32_t)__shfl_xor((int)sv, j, kWave);
+            const bool keep_hi = ((lane & k) == 0) == ((lane & j) == 0);
+            sv = keep_hi ? max(sv, o) : min(sv, o);
         }
-        const float t = (m == 0.f) ? 0.f : m;
-        if (rank == jg) t_guess = t;
-        if (rank == topk - 1) t_safe = t;
+    smax[w][lane] = sv;
+    if (tid == 0) {
+        t_guess_b = 0u;
+        t_safe_b = 0u;
     }
     __syncthreads();
+    if (any) {
+        int gt = 0, ge = 0;          // maxima above mb, and at or above it
+#pragma unroll
+        for (int o = 0; o < kWavesPerBlock; ++o) {
+            int lo = 0, hi = kWave;
+            while (lo < hi) {
+                const int mid = (lo + hi) >> 1;
+                if (smax[o][mid] > mb) lo = mid + 1;
+                else hi = mid;
+            }
+            gt += lo;
+            hi = kWave;
+            while (lo < hi) {
+                const int mid = (lo + hi) >> 1;
+                if (smax[o][mid] >= mb) lo = mid + 1;
+                else hi = mid;
+            }
+            ge += lo;
+        }
+        // ranks gt .. ge-1 hold this value (equal maxima write the same bits)
+        if (gt <= jg && jg < ge) t_guess_b = mb;
+        if (gt <= topk - 1 && topk - 1 < ge) t_safe_b = mb;
+    }
+    __syncthreads();
+    const uint32_t gb = t_guess_b, sb = t_safe_b;
     // 2. the pass from the guess
-    const float tg = t_guess, ts = t_safe;
+    const float tg = gb == 0u ? -INFINITY : from_ordered(gb);
+    const float ts = sb == 0u ? -INFINITY : from_ordered(sb);
     WaveTop st = tg > 0.f ? row_pass<E, VEC, true, true>(row, V, gvend, tg, hs, qi_all[w], wbuf[w], topk)
                           : row_pass<E, VEC, false, true>(row, V, gvend, tg, hs, qi_all[w], wbuf[w], topk);
     if (lane == 0) {
@@ -898,38 +928,6 @@ constexpr int kShortWaves = kShortThreads / kWave;
 constexpr int kShortRth = 8;                    // kShortRth * kShortWaves > W
 constexpr int kShortCap = 512;                  // candidates ranked by counting
 static_assert(kShortRth * kShortWaves >= 64, "the bound must be reached by W <= 63 tokens");
-
-// DPP row operations (no LDS round trip): v from lane i-n of the same row of
-// 16 (row_shr:n; 0 where there is none), and the last lane of the previous
-// row (row_bcast:15) or of the previous pair of rows (row_bcast:31) into the
-// rows selected by the mask (0 elsewhere). The whole wave must be active.
-template <int CTRL, int ROWS>
-__device__ __forceinline__ uint32_t dpp_from(uint32_t v) {
-    return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, CTRL, ROWS, 0xf, false);
-}
-
-// Maximum over the wave, returned to every lane.
-__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
-    v = max(v, dpp_from<0x111, 0xf>(v));
-    v = max(v, dpp_from<0x112, 0xf>(v));
-    v = max(v, dpp_from<0x114, 0xf>(v));
-    v = max(v, dpp_from<0x118, 0xf>(v));
-    v = max(v, dpp_from<0x142, 0xa>(v));
-    v = max(v, dpp_from<0x143, 0xc>(v));
-    return __builtin_amdgcn_readlane(v, kWave - 1);
-}
-
-// Inclusive prefix sum across the wave (lane order) of non-negative counts.
-__device__ __forceinline__ int wave_incl_scan_int(int c) {
-    uint32_t v = (uint32_t)c;
-    v += dpp_from<0x111, 0xf>(v);
-    v += dpp_from<0x112, 0xf>(v);
-    v += dpp_from<0x114, 0xf>(v);
-    v += dpp_from<0x118, 0xf>(v);
-    v += dpp_from<0x142, 0xa>(v);
-    v += dpp_from<0x143, 0xc>(v);
-    return (int)v;
-}
 
 template <class E, bool VEC>
 __global__ __launch_bounds__(kShortThreads) void k_topk_short(const typename E::raw* __restrict__ rows,
