@@ -24,7 +24,7 @@ struct ArgPartial {
     int32_t i;    // lowest index reaching it; kNone if the chunk is all NaN
 };
 constexpr int32_t kNone = 0x7fffffff;
-constexpr int kArgUnroll = 4;
+constexpr int kArgUnroll = 1;
 // Tokens per argmax workgroup: short rows of few sequences still give the
 // launch thousands of workgroups.
 #ifndef SD_ARG_CHUNK_BF16
