@@ -60,6 +60,8 @@ def _load():
     lib.orc_build_tree.restype = None
     lib.orc_verify_tree.argtypes = [P, P, P, P, I, I, I, P, P, P, I]
     lib.orc_verify_tree.restype = None
+    lib.orc_verify_tree_sampled.argtypes = [P, P, P, P, P, I, I, I, D, I, D, P, P, P, P, P, I]
+    lib.orc_verify_tree_sampled.restype = None
     lib.orc_select_len.argtypes = [P, I, I, ctypes.c_float, P, P, P, P]
     lib.orc_select_len.restype = None
     lib.orc_verify_chain_capped.argtypes = [P, P, P, P, P, I, I, I, D, I, D, P, P, P, P, P, P, P, I]
@@ -173,6 +175,30 @@ def verify_tree(target, token, parent, n_nodes, B, N, V, threads=None):
     _load().orc_verify_tree(_ptr(t), _ptr(tok), _ptr(par), _ptr(nn), int(B), int(N), int(V),
                             _ptr(path), _ptr(A), _ptr(nxt), int(threads or default_threads()))
     return {"path": path, "A": A, "next": nxt}
+
+
+def verify_tree_sampled(target, token, parent, n_nodes, uniforms, B, N, V, temperature, top_k=0,
+                        margin_rel=MARGIN_REL, threads=None):
+    """Sampled tree walk: at each node the target's token is drawn from its own
+    transformed row with that node's uniform (uniforms [B, N]).
+
+    Returns path, A, next, status, margin.
+    """
+    t = _f32(target).reshape(-1)
+    tok = _i32(token).reshape(-1)
+    par = _i32(parent).reshape(-1)
+    nn = _i32(n_nodes)
+    u = _f32(uniforms).reshape(-1)
+    path = np.zeros((B, N), np.int32)
+    A = np.zeros(B, np.int32)
+    nxt = np.zeros(B, np.int32)
+    st = np.zeros(B, np.int32)
+    mg = np.zeros(B, np.int32)
+    _load().orc_verify_tree_sampled(_ptr(t), _ptr(tok), _ptr(par), _ptr(nn), _ptr(u), int(B), int(N),
+                                    int(V), ctypes.c_double(temperature), int(top_k),
+                                    ctypes.c_double(margin_rel), _ptr(path), _ptr(A), _ptr(nxt),
+                                    _ptr(st), _ptr(mg), int(threads or default_threads()))
+    return {"path": path, "A": A, "next": nxt, "status": st, "margin": mg}
 
 
 def select_len(conf, B, K, cost):

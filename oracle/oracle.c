@@ -473,6 +473,72 @@ void orc_verify_tree(const float* target, const int32_t* node_token, const int32
 }
 
 /*
+ * Sampled tree walk [SD §5 DDTree: the walk follows the token the target
+ * picks at each node, and the first node without a matching child turns that
+ * token into the extra token; SD §1: temperature and truncation belong inside
+ * p, and the chain's ratio test is not a rule for a tree]. The drafted tree is
+ * fixed (its nodes are not samples from q), so no draft probability enters:
+ * at node n the target picks its token by sampling p_n itself, the inverse
+ * CDF of the transformed row n (orc_transform_row with T, top_k) at
+ * uniforms[b*N + n]. Each node is visited at most once, so every pick uses a
+ * fresh uniform and each committed token is a draw from the target given the
+ * tokens before it. T == 0 is the argmax walk of orc_verify_tree.
+ *
+ * Outputs as orc_verify_tree, plus status_out[b] (ORC_NONFINITE when a
+ * visited row is non-finite; the walk then stops with next = -1) and
+ * margin_out[b] (ORC_MARGIN_SAMPLE when a pick's uniform lies within
+ * margin_rel of a CDF step).
+ */
+void orc_verify_tree_sampled(const float* target, const int32_t* node_token,
+                             const int32_t* node_parent, const int32_t* n_nodes,
+                             const float* uniforms, int B, int N, int V, double T, int top_k,
+                             double margin_rel, int32_t* path_out, int32_t* A_out,
+                             int32_t* next_out, int32_t* status_out, int32_t* margin_out,
+                             int nthreads) {
+    if (T == 0.0) {
+        orc_verify_tree(target, node_token, node_parent, n_nodes, B, N, V, path_out, A_out,
+                        next_out, nthreads);
+        for (int b = 0; b < B; ++b) {
+            if (status_out) status_out[b] = next_out[b] < 0 ? ORC_NONFINITE : 0;
+            if (margin_out) margin_out[b] = 0;
+        }
+        return;
+    }
+#pragma omp parallel for schedule(dynamic, 1) num_threads(nthreads > 0 ? nthreads : 1)
+    for (int b = 0; b < B; ++b) {
+        const int32_t* tok = node_token + (size_t)b * N;
+        const int32_t* par = node_parent + (size_t)b * N;
+        int nn = n_nodes[b];
+        int32_t* path = path_out + (size_t)b * N;
+        double* p = (double*)malloc(sizeof(double) * (size_t)V);
+        for (int i = 0; i < N; ++i) path[i] = -1;
+        int node = 0, len = 0, next = -1, status = 0, margin = 0;
+        for (;;) {
+            int valid = orc_transform_row(target + ((size_t)b * N + node) * V, V, T, top_k, p);
+            if (!valid) {
+                status |= ORC_NONFINITE;
+                next = -1;
+                break;
+            }
+            int mg = 0;
+            int g = orc_inverse_cdf(p, V, (double)uniforms[(size_t)b * N + node], margin_rel, &mg);
+            if (mg) margin |= ORC_MARGIN_SAMPLE;
+            int found = -1;
+            for (int c = 1; c < nn; ++c)
+                if (par[c] == node && tok[c] == g) { found = c; break; }
+            if (found < 0) { next = g; break; }
+            path[len++] = found;
+            node = found;
+        }
+        A_out[b] = len;
+        next_out[b] = next;
+        if (status_out) status_out[b] = status;
+        if (margin_out) margin_out[b] = margin;
+        free(p);
+    }
+}
+
+/*
  * Verify-length choice [SD §5 DSpark]: s_0 = 1, s_j = fl32(s_{j-1} * c_j);
  * k* = the smallest k in [0, K] maximising f(k) = 1 + sum_{j<=k} s_j - cost*k
  * (f in fp64 over the fp32 s_j); expected advance 1 + sum_{j<=k*} s_j;

@@ -563,6 +563,139 @@ def test_tree_walk_expected_length_monte_carlo():
 
 
 # --------------------------------------------------------------------------
+# Sampled tree walk ([SD §5 DDTree]: the walk follows the token the target
+# picks; here the target picks by sampling its own row at each node)
+# --------------------------------------------------------------------------
+
+# root 0 -> 1 (tok 1), 2 (tok 3); 1 -> 3 (tok 0), 4 (tok 2); 3 -> 5 (tok 1)
+WALK_TOKEN = np.array([-1, 1, 3, 0, 2, 1], np.int32)
+WALK_PARENT = np.array([-1, 0, 0, 1, 1, 3], np.int32)
+WALK_P = np.array([[.1, .4, .2, .3], [.5, .1, .3, .1], [.25, .25, .25, .25],
+                   [.2, .6, .1, .1], [.7, .1, .1, .1], [.1, .1, .1, .7]])
+
+
+def _walk_trials(n, rng, uniforms=None, T=1.0):
+    N, V = WALK_P.shape
+    rows = np.tile(logits_of(WALK_P)[None], (n, 1, 1))
+    u = grid_u(rng, (n, N)) if uniforms is None else uniforms
+    out = oracle.verify_tree_sampled(rows, np.tile(WALK_TOKEN, (n, 1)), np.tile(WALK_PARENT, (n, 1)),
+                                     np.full(n, N, np.int32), u, n, N, V, T)
+    return out, u
+
+
+def _committed(out, n):
+    """Token sequence each trial commits: the path's tokens, then next."""
+    seqs = []
+    for b in range(n):
+        a = out["A"][b]
+        seqs.append([int(WALK_TOKEN[c]) for c in out["path"][b][:a]] + [int(out["next"][b])])
+    return seqs
+
+
+def test_sampled_walk_tokens_follow_the_target():
+    """Committed tokens are draws from the target given the tokens before them:
+    the first follows p_root; given it lands on child c, the second follows p_c."""
+    n = 200_000
+    rng = np.random.default_rng(41)
+    out, _ = _walk_trials(n, rng)
+    assert (out["status"] == 0).all()
+    A, path = out["A"], out["path"]
+    first = np.where(A >= 1, WALK_TOKEN[np.maximum(path[:, 0], 0)], out["next"])
+    assert _chi2_ok(np.bincount(first, minlength=4), WALK_P[0], n)
+    for c in (1, 2):
+        sel = (A >= 1) & (path[:, 0] == c)
+        second = np.where(A[sel] >= 2, WALK_TOKEN[np.maximum(path[sel, 1], 0)], out["next"][sel])
+        assert _chi2_ok(np.bincount(second, minlength=4), WALK_P[c], int(sel.sum())), f"child {c}"
+    # third token given the path 1 -> 3
+    sel = (A >= 2) & (path[:, 0] == 1) & (path[:, 1] == 3)
+    third = np.where(A[sel] >= 3, WALK_TOKEN[np.maximum(path[sel, 2], 0)], out["next"][sel])
+    assert _chi2_ok(np.bincount(third, minlength=4), WALK_P[3], int(sel.sum()))
+
+
+def test_sampled_walk_planted_mistake_is_detected():
+    """Sanity of the test above: reusing the root's uniform at every node (one
+    draw instead of independent draws) must fail the conditional check."""
+    n = 200_000
+    rng = np.random.default_rng(43)
+    u = np.repeat(grid_u(rng, (n, 1)), WALK_P.shape[0], axis=1)
+    out, _ = _walk_trials(n, rng, uniforms=u)
+    A, path = out["A"], out["path"]
+    sel = (A >= 1) & (path[:, 0] == 1)
+    second = np.where(A[sel] >= 2, WALK_TOKEN[np.maximum(path[sel, 1], 0)], out["next"][sel])
+    assert not _chi2_ok(np.bincount(second, minlength=4), WALK_P[1], int(sel.sum()))
+
+
+def test_sampled_walk_expected_length_closed_form():
+    """The walk reaches node u iff the target's draws spell u's path, so
+    E[accepted] = sum over draft nodes of the product of p_parent(token) along
+    the path."""
+    n = 100_000
+    rng = np.random.default_rng(47)
+    out, _ = _walk_trials(n, rng)
+    reach = np.zeros(len(WALK_TOKEN))
+    reach[0] = 1.0
+    for c in range(1, len(WALK_TOKEN)):
+        reach[c] = reach[WALK_PARENT[c]] * WALK_P[WALK_PARENT[c], WALK_TOKEN[c]]
+    expect = reach[1:].sum()
+    a = out["A"].astype(np.float64)
+    assert abs(a.mean() - expect) < 4 * a.std() / math.sqrt(n)
+    # the path is a chain of parent -> child links starting at the root
+    for b in range(200):
+        node = 0
+        for c in out["path"][b][:out["A"][b]]:
+            assert WALK_PARENT[c] == node
+            node = c
+        assert (out["path"][b][out["A"][b]:] == -1).all()
+
+
+def test_sampled_walk_small_temperature_is_the_argmax_walk():
+    """For tie-free rows with minimum gap delta and T <= delta/800 every
+    non-maximal weight underflows, so the sampled walk is the argmax walk for
+    every uniform; T == 0 is the argmax walk by definition."""
+    rng = np.random.default_rng(53)
+    B, N, V = 64, 6, 9
+    rows = np.stack([rng.permutation(V) for _ in range(B * N)]).astype(np.float32).reshape(B, N, V)
+    # plant matches so that walks go deep
+    for b in range(B):
+        for n in range(N):
+            kids = [c for c in range(1, N) if WALK_PARENT[c] == n]
+            if kids and rng.random() < 0.7:
+                t = WALK_TOKEN[rng.choice(kids)]
+                rows[b, n, t] = V + 1.0
+    tok = np.tile(WALK_TOKEN, (B, 1))
+    par = np.tile(WALK_PARENT, (B, 1))
+    nn = np.full(B, N, np.int32)
+    ref = oracle.verify_tree(rows, tok, par, nn, B, N, V)
+    assert (ref["A"] >= 2).any()
+    for T in (0.0, 1.0 / 800):
+        u = grid_u(rng, (B, N))
+        u[:, 0] = 1.0 - 2.0 ** -24            # the extreme uniforms too
+        u[:, 1] = 0.0
+        out = oracle.verify_tree_sampled(rows, tok, par, nn, u, B, N, V, T)
+        assert (out["A"] == ref["A"]).all() and (out["next"] == ref["next"]).all()
+        assert (out["path"] == ref["path"]).all()
+
+
+def test_sampled_walk_nonfinite_row_and_one_hot_rows():
+    N, V = WALK_P.shape
+    # one-hot target rows spell the path root -> 1 -> 3 -> 5, then token 2
+    picks = [1, 0, 0, 1, 0, 2]
+    rows = np.full((1, N, V), -np.inf, np.float32)
+    for n, t in enumerate(picks):
+        rows[0, n, t] = 0.0
+    u = np.full((1, N), 0.999, np.float32)
+    out = oracle.verify_tree_sampled(rows, WALK_TOKEN[None], WALK_PARENT[None], np.array([N], np.int32),
+                                     u, 1, N, V, 0.8)
+    assert out["A"][0] == 3 and out["path"][0][:3].tolist() == [1, 3, 5] and out["next"][0] == 2
+    assert out["status"][0] == 0
+    # a NaN row on the path stops the walk there with next = -1 and the flag
+    rows[0, 3, :] = np.nan
+    out = oracle.verify_tree_sampled(rows, WALK_TOKEN[None], WALK_PARENT[None], np.array([N], np.int32),
+                                     u, 1, N, V, 0.8)
+    assert out["A"][0] == 2 and out["next"][0] == -1 and out["status"][0] == oracle.NONFINITE
+
+
+# --------------------------------------------------------------------------
 # Ragged verify modes and a per-position cost table ([SD §9 DSpark], [SD §5 DSpark])
 # --------------------------------------------------------------------------
 
