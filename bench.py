@@ -14,7 +14,7 @@ second, the roofline of the dominant kernel (the streaming pass over the logit
 rows, timed with HIP events on its own stream) and the CPU oracle timed on a
 bounded sample of the same workload.
 
-Other workloads (--workload greedy|topk|tree|chain1|kv|rerank) measure the other kernels
+Other workloads (--workload greedy|topk|tree|tree_sampled|chain1|kv|rerank) measure the other kernels
 for the design notes; their inputs are rotated across copies so that the
 working set exceeds the 256 MB last-level cache.
 """
@@ -181,20 +181,57 @@ def setup_tree(torch, sd, wl):
     targets = [target] + [target.clone() for _ in range(2)]
     st = {"i": 0}
     ws_b = torch.empty(sd.workspace_bytes(sd.OP_BUILD_TREE, B, K, V, 0, N), dtype=torch.uint8, device="cuda")
-    ws_v = torch.empty(sd.workspace_bytes(sd.OP_VERIFY_TREE, B, 0, V, 0, N), dtype=torch.uint8, device="cuda")
+    walk_out = sd.verify_tree(target, tree)
+    A = walk_out["accepted_len"].cpu()
+    rows_read = int(A.sum()) + B              # the walk reads the rows on its path only
 
     def step(ev=None):
         i = st["i"] % 3
         st["i"] += 1
         if ev is not None:
             sd.time_next_stream_pass(*ev)
-        t = sd.build_tree(margs[i], N, workspace=ws_b)
-        sd.verify_tree(targets[i], tree, workspace=ws_v)
+        sd.build_tree(margs[i], N, workspace=ws_b)
+        sd.verify_tree(targets[i], tree, out=walk_out)
 
-    meta = {"workload": f"DDTree build (B={B}, K={K}, V={V} fp32 marginals, N={N}) + walk over bf16 target rows",
+    meta = {"workload": (f"DDTree build (B={B}, K={K}, V={V} fp32 marginals, N={N}) + argmax walk over "
+                         f"bf16 target rows (read on demand)"),
             "global_batch": B, "K_max": K, "V": V, "positions_per_step": B * (N - 1),
             "kernel": "k_topk_short<f32>", "kernel_bytes": B * K * V * 4,
-            "step_bytes": B * K * V * 4 + B * N * V * 2}
+            "step_bytes": B * K * V * 4 + rows_read * V * 2, "mean_A": float(A.float().mean()),
+            "rows_streamed": rows_read}
+    return step, meta, None
+
+
+def setup_tree_sampled(torch, sd, wl):
+    # the tree workload's build, then the walk under a sampling target (T = 1):
+    # at each node the target draws its own token; only the walk's rows are read
+    case = wl.gen_config4(device="cuda")
+    B, K, V, N = case.B, case.K, case.V, case.N
+    tree = sd.build_tree(case.marginals, N)
+    target = case.target_for_depths(tree["depth"], tree["n_nodes"])
+    u = wl.grid_uniforms((B, N), torch.Generator(device="cuda").manual_seed(1004), "cuda")
+    margs = [case.marginals] + [case.marginals.clone() for _ in range(2)]
+    targets = [target] + [target.clone() for _ in range(2)]
+    st = {"i": 0}
+    ws_b = torch.empty(sd.workspace_bytes(sd.OP_BUILD_TREE, B, K, V, 0, N), dtype=torch.uint8, device="cuda")
+    walk_out = sd.verify_tree_sampled(target, tree, u, 1.0)
+    A = walk_out["accepted_len"].cpu()
+    rows_read = int(A.sum()) + B
+
+    def step(ev=None):
+        i = st["i"] % 3
+        st["i"] += 1
+        sd.build_tree(margs[i], N, workspace=ws_b)
+        if ev is not None:
+            sd.time_next_stream_pass(*ev)
+        sd.verify_tree_sampled(targets[i], tree, u, 1.0, out=walk_out)
+
+    meta = {"workload": (f"DDTree build (B={B}, K={K}, V={V} fp32 marginals, N={N}) + walk under a "
+                         f"sampling target (T=1, bf16 rows read on demand)"),
+            "global_batch": B, "K_max": K, "V": V, "positions_per_step": B * (N - 1),
+            "kernel": "k_tree_walk_rows", "kernel_bytes": rows_read * V * 2 + B * N * 12,
+            "step_bytes": B * K * V * 4 + rows_read * V * 2, "mean_A": float(A.float().mean()),
+            "rows_streamed": rows_read}
     return step, meta, None
 
 
@@ -286,7 +323,8 @@ def setup_chain1(torch, sd, wl):
 
 
 WORKLOADS = {"adaptive": setup_adaptive, "greedy": setup_greedy, "topk": setup_topk,
-             "tree": setup_tree, "chain1": setup_chain1, "kv": setup_kv, "rerank": setup_rerank}
+             "tree": setup_tree, "tree_sampled": setup_tree_sampled, "chain1": setup_chain1,
+             "kv": setup_kv, "rerank": setup_rerank}
 
 
 def run_cpu_baseline(cpu, target_seconds: float):

@@ -219,13 +219,53 @@ sd_status_t sd_build_tree(const float* marginals, int32_t B, int32_t K, int32_t 
  *   path_nodes   [B, N] int32 out   accepted node ids in walk order (root
  *                                   excluded), -1 padded
  *   accepted_len [B] int32 out      path length
- *   next_token   [B] int32 out      the target's token after the path
+ *   next_token   [B] int32 out      the target's token after the path (-1 if
+ *                                   that row is all NaN)
+ * Only the rows on the walk are read, one per step. The workspace arguments
+ * are unused (sd_workspace_bytes returns 0 for SD_OP_VERIFY_TREE; NULL is
+ * accepted).
  */
 sd_status_t sd_verify_tree(const void* target_logits, sd_dtype_t dtype,
                            const int32_t* node_token, const int32_t* node_parent,
                            const int32_t* n_nodes, int32_t B, int32_t N, int32_t V,
                            int32_t* path_nodes, int32_t* accepted_len, int32_t* next_token,
                            void* workspace, size_t workspace_bytes, void* hip_stream);
+
+/*
+ * DDTree walk under a sampling target [SD §5 DDTree: the walk follows the token
+ * the target selects at each node, and the first node without a child carrying
+ * it turns that token into the extra token; SD §1: temperature and truncation
+ * belong inside p, and the chain's ratio test is not a rule for a tree]. At
+ * node n the target selects its token by drawing from its own row: the inverse
+ * CDF, in token-id order, of p_n = softmax(target row n / T) at
+ * uniforms[b*N + n] (the first token whose running mass exceeds the uniform;
+ * if rounding leaves none, the last token with positive mass). The tree's
+ * nodes are fixed drafts, so no draft probability enters; a walk visits a node
+ * at most once, so every draw has a fresh uniform and each committed token is
+ * a draw from the target given the tokens before it. T == 0 takes the lowest-id
+ * argmax instead, the walk of sd_verify_tree. Only the rows on the walk are
+ * read, one per step.
+ *
+ *   target_logits [B, N, V] dtype     row n: target distribution after node n
+ *   node_token, node_parent [B, N] int32, n_nodes [B] int32 (as built)
+ *   uniforms     [B, N] fp32 in [0, 1) (ignored and may be NULL when T == 0)
+ *   temperature  T >= 0, finite; top_k 0 (or >= V) = no truncation; truncation
+ *                with T > 0 is not built (SD_EUNSUPPORTED)
+ *   path_nodes   [B, N] int32 out     accepted node ids in walk order (root
+ *                                     excluded), -1 padded
+ *   accepted_len [B] int32 out; next_token [B] int32 out (-1 when the row it
+ *                would be drawn from is non-finite)
+ *   seq_status   [B] int32 out or NULL: SD_SEQ_NONFINITE when a visited row is
+ *                non-finite (no finite maximum, or a NaN in its sum); the walk
+ *                stops there
+ * Needs no workspace.
+ */
+sd_status_t sd_verify_tree_sampled(const void* target_logits, sd_dtype_t dtype,
+                                   const int32_t* node_token, const int32_t* node_parent,
+                                   const int32_t* n_nodes, const float* uniforms, int32_t B,
+                                   int32_t N, int32_t V, float temperature, int32_t top_k,
+                                   int32_t* path_nodes, int32_t* accepted_len,
+                                   int32_t* next_token, int32_t* seq_status, void* hip_stream);
 
 /*
  * EAGLE-2-style verification tree [SD §4 EAGLE-2: candidates expanded along

@@ -11,6 +11,7 @@ Functions mirror the C entry points:
   verify_greedy  sd_verify_greedy
   build_tree     sd_build_tree     (DDTree best-first tree from marginals)
   verify_tree    sd_verify_tree    (walk along the target's argmax)
+  verify_tree_sampled  sd_verify_tree_sampled  (walk along the target's own draws)
   select_len     sd_select_len     (DSpark verify length, packed offsets)
 """
 from __future__ import annotations
@@ -63,6 +64,8 @@ def _load():
     lib.sd_build_tree.restype = ctypes.c_int
     lib.sd_verify_tree.argtypes = [P, ctypes.c_int, P, P, P, I, I, I, P, P, P, P, Z, P]
     lib.sd_verify_tree.restype = ctypes.c_int
+    lib.sd_verify_tree_sampled.argtypes = [P, ctypes.c_int, P, P, P, P, I, I, I, F, I, P, P, P, P, P]
+    lib.sd_verify_tree_sampled.restype = ctypes.c_int
     lib.sd_select_len.argtypes = [P, I, I, F, P, P, P, P]
     lib.sd_select_len.restype = ctypes.c_int
     lib.sd_verify_chain_capped.argtypes = [P, P, ctypes.c_int, P, P, P, I, I, I, F, I, P, P, P, P, P,
@@ -339,23 +342,56 @@ def build_tree(marginals: torch.Tensor, N: int, workspace: Optional[torch.Tensor
 
 
 def verify_tree(target: torch.Tensor, tree: dict, workspace: Optional[torch.Tensor] = None,
-                stream=None) -> dict:
-    """sd_verify_tree. target [B, N, V] (bf16 or fp32); tree from build_tree."""
+                stream=None, out: Optional[dict] = None) -> dict:
+    """sd_verify_tree. target [B, N, V] (bf16 or fp32); tree from build_tree.
+    The walk needs no workspace (the argument is accepted and ignored)."""
     dev = target.device
     _check(target, "target", device=dev)
     dt = _dtype_code(target)
     B, N, V = (int(s) for s in target.shape)
     for k in ("token", "parent", "n_nodes"):
         _check(tree[k], k, torch.int32, dev)
-    path = torch.empty(B, N, dtype=torch.int32, device=dev)
-    A = torch.empty(B, dtype=torch.int32, device=dev)
-    nxt = torch.empty(B, dtype=torch.int32, device=dev)
-    ws = _workspace(workspace_bytes(OP_VERIFY_TREE, B, 0, V, 0, N), dev, workspace)
+    if tree["token"].numel() < B * N or tree["parent"].numel() < B * N or tree["n_nodes"].numel() < B:
+        raise ValueError("tree arrays do not cover [B, N]")
+    o = out or {}
+    path = _get(o, "path", lambda: torch.empty(B, N, dtype=torch.int32, device=dev))
+    A = _get(o, "accepted_len", lambda: torch.empty(B, dtype=torch.int32, device=dev))
+    nxt = _get(o, "next_token", lambda: torch.empty(B, dtype=torch.int32, device=dev))
     r = _load().sd_verify_tree(_ptr(target), dt, _ptr(tree["token"]), _ptr(tree["parent"]),
                                _ptr(tree["n_nodes"]), B, N, V, _ptr(path), _ptr(A), _ptr(nxt),
-                               _ptr(ws), ctypes.c_size_t(ws.numel()), _stream(stream))
+                               None, ctypes.c_size_t(0), _stream(stream))
     _raise(r, "sd_verify_tree")
     return {"path": path, "accepted_len": A, "next_token": nxt}
+
+
+def verify_tree_sampled(target: torch.Tensor, tree: dict, uniforms: Optional[torch.Tensor],
+                        temperature: float, top_k: int = 0, out: Optional[dict] = None,
+                        stream=None) -> dict:
+    """sd_verify_tree_sampled. target [B, N, V] (bf16 or fp32); tree from build_tree;
+    uniforms [B, N] float32 (None when temperature == 0)."""
+    dev = target.device
+    _check(target, "target", device=dev)
+    dt = _dtype_code(target)
+    B, N, V = (int(s) for s in target.shape)
+    for k in ("token", "parent", "n_nodes"):
+        _check(tree[k], k, torch.int32, dev)
+    if tree["token"].numel() < B * N or tree["parent"].numel() < B * N or tree["n_nodes"].numel() < B:
+        raise ValueError("tree arrays do not cover [B, N]")
+    if uniforms is not None:
+        _check(uniforms, "uniforms", torch.float32, dev)
+        if uniforms.numel() < B * N:
+            raise ValueError("uniforms needs one entry per (sequence, node)")
+    o = out or {}
+    path = _get(o, "path", lambda: torch.empty(B, N, dtype=torch.int32, device=dev))
+    A = _get(o, "accepted_len", lambda: torch.empty(B, dtype=torch.int32, device=dev))
+    nxt = _get(o, "next_token", lambda: torch.empty(B, dtype=torch.int32, device=dev))
+    st = _get(o, "status", lambda: torch.empty(B, dtype=torch.int32, device=dev))
+    r = _load().sd_verify_tree_sampled(_ptr(target), dt, _ptr(tree["token"]), _ptr(tree["parent"]),
+                                       _ptr(tree["n_nodes"]), _ptr(uniforms), B, N, V,
+                                       ctypes.c_float(float(temperature)), int(top_k), _ptr(path),
+                                       _ptr(A), _ptr(nxt), _ptr(st), _stream(stream))
+    _raise(r, "sd_verify_tree_sampled")
+    return {"path": path, "accepted_len": A, "next_token": nxt, "status": st}
 
 
 def select_len(conf: torch.Tensor, cost: float, out: Optional[dict] = None, stream=None) -> dict:

@@ -1,15 +1,14 @@
-// sd_greedy.hip -- greedy chain verification and the DDTree walk.
+// sd_greedy.hip -- greedy chain verification.
 //
 // Page "大模型投机解码：Medusa、MTP、EAGLE、DFlash、DDTree 与 DSpark"
-// (chzhyang.github.io): §1 (greedy results follow the target argmax; the first
-// mismatch ends the accepted prefix) and §5 DDTree (the walk follows the token
-// the target picks and stops at the first node without a matching child; that
-// token becomes the extra token).
+// (chzhyang.github.io), §1: greedy results follow the target argmax; the first
+// mismatch ends the accepted prefix.
 //
-// Both need the lowest-id argmax of many V-long rows: k_argmax streams each
-// (row, chunk) once with 16-byte loads and writes a (value, index) partial; a
-// one-wave kernel per sequence then combines partials and decides (ballot over
-// the chain, or a walk over at most 64 tree nodes).
+// Every position of a chain is tested at once, so every row is needed: k_argmax
+// streams each (row, chunk) once with 16-byte loads and writes a (value, index)
+// partial; a one-wave kernel per sequence then combines the partials and takes
+// the first mismatch by a ballot. (The tree walk needs only the rows on its
+// path and reads them on demand: sd_walk.hip.)
 #include "sd_device.hpp"
 #include "sd_internal.hpp"
 
@@ -43,11 +42,8 @@ __device__ __forceinline__ bool arg_better(float v, int i, float bv, int bi) {
     return v > bv || (v == bv && i < bi);
 }
 
-enum RowMapKind { kMapChain = 0, kMapTree = 1 };
-
-// grid: (sequence, slot, chunk). Chain: slot s <= k_b is target row cu[b]+b+s.
-// Tree: slot n < n_nodes[b] is row b*N+n.
-template <class E, bool VEC, int MAP>
+// grid: (sequence, slot, chunk); slot s <= k_b is target row cu[b]+b+s.
+template <class E, bool VEC>
 __global__ __launch_bounds__(kBlock) void k_argmax(const typename E::raw* __restrict__ rows,
                                                    const int32_t* __restrict__ aux, int slots,
                                                    int K_max, int V, int chunk, int n_chunks,
@@ -60,16 +56,10 @@ __global__ __launch_bounds__(kBlock) void k_argmax(const typename E::raw* __rest
     const int rest = blockIdx.x / n_chunks;
     const int s = rest % slots;
     const int b = rest / slots;
-    int64_t row;
-    if (MAP == kMapChain) {
-        int d0, k;
-        seq_range(aux, b, K_max, d0, k);
-        if (s > k) return;
-        row = (int64_t)d0 + b + s;
-    } else {
-        if (s >= aux[b]) return;
-        row = (int64_t)b * slots + s;
-    }
+    int d0, k;
+    seq_range(aux, b, K_max, d0, k);
+    if (s > k) return;
+    const int64_t row = (int64_t)d0 + b + s;
     const typename E::raw* rp = rows + row * (int64_t)V;
     const int beg = ch * chunk;
     const int end = min(V, beg + chunk);
@@ -211,52 +201,11 @@ __global__ __launch_bounds__(kWave) void k_greedy_decide(
     }
 }
 
-__global__ __launch_bounds__(kWave) void k_tree_walk(
-    const ArgPartial* __restrict__ part, const int32_t* __restrict__ node_token,
-    const int32_t* __restrict__ node_parent, const int32_t* __restrict__ n_nodes, int N,
-    int n_chunks, int32_t* __restrict__ path, int32_t* __restrict__ A_out,
-    int32_t* __restrict__ next_out) {
-    const int b = blockIdx.x;
-    const int lane = threadIdx.x;
-    const int nn = n_nodes[b];
-    int my_tok = -1, my_par = -2, my_g = -1;
-    if (lane < nn && lane < N) {
-        my_tok = node_token[(int64_t)b * N + lane];
-        my_par = node_parent[(int64_t)b * N + lane];
-        my_g = combine_arg(part + ((int64_t)b * N + lane) * n_chunks, n_chunks);
-    }
-    if (lane < N) path[(int64_t)b * N + lane] = -1;
-    int node = 0, len = 0, next = -1;
-    for (int step = 0; step < N; ++step) {
-        const int g = __shfl(my_g, node, kWave);
-        const bool hit = (lane >= 1) && (lane < nn) && (my_par == node) && (my_tok == g) && (g >= 0);
-        const unsigned long long m = __ballot(hit);
-        if (!m) {
-            next = g;
-            break;
-        }
-        const int child = __ffsll(m) - 1;
-        if (lane == 0) path[(int64_t)b * N + len] = child;
-        ++len;
-        node = child;
-    }
-    if (lane == 0) {
-        A_out[b] = len;
-        next_out[b] = next;
-    }
-}
-
 }  // namespace
 
 size_t greedy_ws_bytes(int B, int K_max, int V, int dtype) {
     Carve cv;
     cv.take((size_t)B * (K_max + 1) * arg_chunks(V, dtype) * sizeof(ArgPartial));
-    return cv.off;
-}
-
-size_t tree_verify_ws_bytes(int B, int N, int V, int dtype) {
-    Carve cv;
-    cv.take((size_t)B * N * arg_chunks(V, dtype) * sizeof(ArgPartial));
     return cv.off;
 }
 
@@ -268,7 +217,7 @@ static hipError_t greedy_impl(const void* target, const int32_t* tokens, const i
     const int chunk = arg_chunk(dtype);
     ArgPartial* part = static_cast<ArgPartial*>(ws);
     const unsigned grid = (unsigned)((size_t)B * (K_max + 1) * nc);
-    PassTimer::launch(k_argmax<E, VEC, kMapChain>, dim3(grid), dim3(kBlock), stream,
+    PassTimer::launch(k_argmax<E, VEC>, dim3(grid), dim3(kBlock), stream,
                       static_cast<const typename E::raw*>(target), cu, K_max + 1, K_max, V, chunk, nc,
                       part);
     hipLaunchKernelGGL(k_greedy_decide, dim3(B), dim3(kWave), 0, stream, part, tokens, cu, K_max, V,
@@ -292,39 +241,6 @@ hipError_t launch_greedy(const void* target, int dtype, const int32_t* tokens, c
                                       next_token, seq_status, cap, accepted_full, ws, stream);
     return greedy_impl<F32, false>(target, tokens, cu, B, K_max, V, dtype, accepted_len, next_token,
                                    seq_status, cap, accepted_full, ws, stream);
-}
-
-template <class E, bool VEC>
-static hipError_t tree_verify_impl(const void* target, const int32_t* tok, const int32_t* par,
-                                   const int32_t* nn, int B, int N, int V, int dtype, int32_t* path,
-                                   int32_t* A, int32_t* next, void* ws, hipStream_t stream) {
-    const int nc = arg_chunks(V, dtype);
-    const int chunk = arg_chunk(dtype);
-    ArgPartial* part = static_cast<ArgPartial*>(ws);
-    const unsigned grid = (unsigned)((size_t)B * N * nc);
-    PassTimer::launch(k_argmax<E, VEC, kMapTree>, dim3(grid), dim3(kBlock), stream,
-                      static_cast<const typename E::raw*>(target), nn, N, 0, V, chunk, nc, part);
-    hipLaunchKernelGGL(k_tree_walk, dim3(B), dim3(kWave), 0, stream, part, tok, par, nn, N, nc,
-                       path, A, next);
-    return hipGetLastError();
-}
-
-hipError_t launch_tree_verify(const void* target, int dtype, const int32_t* tok, const int32_t* par,
-                              const int32_t* n_nodes, int B, int N, int V, int32_t* path,
-                              int32_t* accepted_len, int32_t* next_token, void* ws,
-                              hipStream_t stream) {
-    if (dtype == 1) {
-        if (V % Bf16::kVec == 0)
-            return tree_verify_impl<Bf16, true>(target, tok, par, n_nodes, B, N, V, dtype, path,
-                                                accepted_len, next_token, ws, stream);
-        return tree_verify_impl<Bf16, false>(target, tok, par, n_nodes, B, N, V, dtype, path,
-                                             accepted_len, next_token, ws, stream);
-    }
-    if (V % F32::kVec == 0)
-        return tree_verify_impl<F32, true>(target, tok, par, n_nodes, B, N, V, dtype, path,
-                                           accepted_len, next_token, ws, stream);
-    return tree_verify_impl<F32, false>(target, tok, par, n_nodes, B, N, V, dtype, path,
-                                        accepted_len, next_token, ws, stream);
 }
 
 }  // namespace sd

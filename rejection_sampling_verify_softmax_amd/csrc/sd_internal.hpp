@@ -96,7 +96,6 @@ size_t chain_full_ws_bytes(int B, int K_max, int V, int dtype);
 size_t chain_topk_ws_bytes(int B, int K_max, int V, int top_k);
 size_t greedy_ws_bytes(int B, int K_max, int V, int dtype);
 size_t tree_build_ws_bytes(int B, int K, int V, int N);
-size_t tree_verify_ws_bytes(int B, int N, int V, int dtype);
 
 hipError_t launch_chain_full(const ChainArgs& a);
 hipError_t launch_chain_topk(const ChainArgs& a);
@@ -107,10 +106,11 @@ hipError_t launch_greedy(const void* target, int dtype, const int32_t* tokens, c
 hipError_t launch_tree_build(const float* marg, int B, int K, int V, int N, int32_t* tok,
                              int32_t* par, int32_t* dep, float* score, uint64_t* anc,
                              int32_t* n_nodes, void* ws, hipStream_t stream);
-hipError_t launch_tree_verify(const void* target, int dtype, const int32_t* tok, const int32_t* par,
-                              const int32_t* n_nodes, int B, int N, int V, int32_t* path,
-                              int32_t* accepted_len, int32_t* next_token, void* ws,
-                              hipStream_t stream);
+hipError_t launch_tree_walk_rows(const void* target, int dtype, const int32_t* tok,
+                                 const int32_t* par, const int32_t* n_nodes, const float* uniforms,
+                                 int B, int N, int V, float temperature, int32_t* path,
+                                 int32_t* accepted_len, int32_t* next_token, int32_t* seq_status,
+                                 hipStream_t stream);
 hipError_t launch_compact_kv(void* kv, int64_t row_bytes, int64_t n_rows, const int64_t* base,
                              const int32_t* path, const int32_t* accepted_len, int B, int N,
                              hipStream_t stream);

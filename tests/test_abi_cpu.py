@@ -29,6 +29,7 @@ def test_header_declares_the_five_calls():
     names = declared_symbols()
     for n in ("sd_verify_chain", "sd_verify_greedy", "sd_build_tree", "sd_verify_tree", "sd_select_len",
               "sd_verify_chain_capped", "sd_select_len_table", "sd_compact_kv", "sd_rerank_tree",
+              "sd_verify_tree_sampled",
               "sd_workspace_bytes", "sd_abi_version", "sd_status_str"):
         assert n in names
 
@@ -159,6 +160,28 @@ def test_rerank_tree_rejects_invalid_arguments(L):
     assert rr(N=65) == 1
     assert rr(first=None) == 1
     assert rr(out=None) == 1
+
+
+def test_tree_sampled_rejects_invalid_arguments(L):
+    one = ctypes.c_void_p(1)
+    f = ctypes.c_float
+
+    def ts(dtype=1, uni=one, B=2, N=8, V=100, T=1.0, top_k=0, out=one):
+        return L.sd_verify_tree_sampled(one, dtype, one, one, one, uni, B, N, V, f(T), top_k, out, one,
+                                        one, None, None)
+    assert ts(B=0) == 1
+    assert ts(N=1) == 1
+    assert ts(N=65) == 1
+    assert ts(V=0) == 1
+    assert ts(V=1 << 24) == 1
+    assert ts(dtype=5) == 1
+    assert ts(T=-0.5) == 1
+    assert ts(T=float("inf")) == 1
+    assert ts(top_k=-1) == 1
+    assert ts(uni=None) == 1              # uniforms are required when T > 0
+    assert ts(out=None) == 1
+    assert ts(top_k=50) == 2              # truncation under sampling is not built
+    assert ts(top_k=50, uni=None, T=0.0, out=None) == 1
 
 
 def test_binding_fails_loudly_without_gpu():

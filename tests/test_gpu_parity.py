@@ -519,6 +519,110 @@ def test_tree_walk_planted():
 
 
 # --------------------------------------------------------------------------
+# DDTree walk under a sampling target (rows read on demand, one per step)
+# --------------------------------------------------------------------------
+
+def _sampled_walk_check(tree, target, T, u):
+    B, N, V = (int(x) for x in target.shape)
+    out = sd.verify_tree_sampled(target, tree, u, T)
+    ref = oracle.verify_tree_sampled(wl.to_host_f32(target), tree["token"].cpu().numpy(),
+                                     tree["parent"].cpu().numpy(), tree["n_nodes"].cpu().numpy(),
+                                     (u.cpu().numpy() if u is not None else np.zeros((B, N), np.float32)),
+                                     B, N, V, T)
+    ok = ref["margin"] == 0
+    for kg, kr in (("accepted_len", "A"), ("next_token", "next"), ("status", "status")):
+        got = out[kg].cpu().numpy()
+        bad = np.nonzero(ok & (got != ref[kr]))[0]
+        assert len(bad) == 0, f"{kg}: seqs {bad[:5]} gpu {got[bad[:5]]} oracle {ref[kr][bad[:5]]}"
+    np.testing.assert_array_equal(out["path"].cpu().numpy()[ok], ref["path"][ok])
+    return out, ref
+
+
+@pytest.mark.parametrize("dtype,V,T", [("bf16", 32000, 1.0), ("bf16", 32000, 0.3), ("bf16", 70000, 0.8),
+                                       ("bf16", 32001, 0.6), ("f32", 40000, 1.2), ("f32", 999, 0.5),
+                                       ("bf16", 8, 1.0)])
+def test_tree_walk_sampled_matches_oracle(dtype, V, T):
+    B, K, N = 24, 16, 64
+    _say(f"sampled walk {dtype} V={V} T={T}")
+    case = wl.gen_config4(device="cuda", seed=31 + V, B=B, K=K, V=V, N=N)
+    tree = sd.build_tree(case.marginals, N)
+    target = case.target_for_depths(tree["depth"], tree["n_nodes"])
+    if dtype == "f32":
+        target = target.float()
+    u = wl.grid_uniforms((B, N), torch.Generator(device="cuda").manual_seed(V), "cuda")
+    out, ref = _sampled_walk_check(tree, target, T, u)
+    _say(f"  mean walk {ref['A'].mean():.2f}, max {ref['A'].max()}, margin {int((ref['margin'] != 0).sum())}")
+
+
+def test_tree_walk_sampled_T0_is_the_argmax_walk():
+    case = wl.gen_config4(device="cuda", seed=77, B=16, K=16, V=32000, N=64)
+    tree = sd.build_tree(case.marginals, 64)
+    target = case.target_for_depths(tree["depth"], tree["n_nodes"])
+    for tgt in (target, target.float()):
+        out, _ = _sampled_walk_check(tree, tgt, 0.0, None)
+        ref = sd.verify_tree(tgt, tree)
+        for k in ("path", "accepted_len", "next_token"):
+            assert torch.equal(out[k], ref[k]), k
+
+
+def test_config4_tree_sampled_full():
+    _say("config 4 shape, sampled walk: B=32 K=16 V=32000 N=64 T=1")
+    case = wl.gen_config4(device="cuda")
+    tree = sd.build_tree(case.marginals, case.N)
+    target = case.target_for_depths(tree["depth"], tree["n_nodes"])
+    u = wl.grid_uniforms((case.B, case.N), torch.Generator(device="cuda").manual_seed(1004), "cuda")
+    out, ref = _sampled_walk_check(tree, target, 1.0, u)
+    _say(f"  mean walk {ref['A'].mean():.2f}")
+
+
+def test_tree_walk_sampled_nonfinite_and_planted():
+    V, N, B = 12, 6, 3
+    tok = torch.tensor([[-1, 4, 7, 2, 9, -1]] * B, dtype=torch.int32, device="cuda")
+    par = torch.tensor([[-1, 0, 0, 1, 3, -1]] * B, dtype=torch.int32, device="cuda")
+    nn = torch.tensor([5] * B, dtype=torch.int32, device="cuda")
+    rows = torch.full((B, N, V), float("-inf"), device="cuda")
+    for b in range(B):
+        for n, t in enumerate([4, 2, 0, 9, 11, 0]):
+            rows[b, n, t] = 0.0                        # one-hot p: the draw is certain
+    rows[1, 3, :] = float("nan")                       # sequence 1 meets a NaN row at node 3
+    rows[2, 0, :] = float("inf")                       # sequence 2: no finite maximum at the root
+    u = torch.full((B, N), 0.5, device="cuda")
+    tree = {"token": tok, "parent": par, "n_nodes": nn}
+    out = sd.verify_tree_sampled(rows, tree, u, 0.9)
+    assert out["accepted_len"].tolist() == [3, 2, 0]
+    assert out["next_token"].tolist() == [11, -1, -1]
+    assert out["status"].tolist() == [0, 2, 2]
+    assert out["path"][0].tolist()[:4] == [1, 3, 4, -1]
+
+
+def test_gpu_sampled_walk_tokens_follow_target():
+    """One call over 2^18 copies of a small tree: the committed tokens follow
+    the target's rows (first token ~ p_root; second ~ p_child given the child)."""
+    from scipy import stats
+    P = np.array([[.1, .4, .2, .3], [.5, .1, .3, .1], [.25, .25, .25, .25],
+                  [.2, .6, .1, .1], [.7, .1, .1, .1], [.1, .1, .1, .7]])
+    tok0 = [-1, 1, 3, 0, 2, 1]
+    par0 = [-1, 0, 0, 1, 1, 3]
+    n, N, V = 1 << 18, 6, 4
+    rows = torch.log(torch.tensor(P, dtype=torch.float32, device="cuda"))[None].expand(n, N, V).contiguous()
+    tree = {"token": torch.tensor([tok0] * n, dtype=torch.int32, device="cuda"),
+            "parent": torch.tensor([par0] * n, dtype=torch.int32, device="cuda"),
+            "n_nodes": torch.full((n,), N, dtype=torch.int32, device="cuda")}
+    u = wl.grid_uniforms((n, N), torch.Generator(device="cuda").manual_seed(99), "cuda")
+    out = sd.verify_tree_sampled(rows, tree, u, 1.0)
+    A = out["accepted_len"].cpu().numpy()
+    path = out["path"].cpu().numpy()
+    nxt = out["next_token"].cpu().numpy()
+    tk = np.array(tok0)
+    first = np.where(A >= 1, tk[np.maximum(path[:, 0], 0)], nxt)
+    assert stats.chisquare(np.bincount(first, minlength=V), P[0] * n).pvalue >= 1e-3
+    for c in (1, 2):
+        sel = (A >= 1) & (path[:, 0] == c)
+        second = np.where(A[sel] >= 2, tk[np.maximum(path[sel, 1], 0)], nxt[sel])
+        assert stats.chisquare(np.bincount(second, minlength=V), P[c] * sel.sum()).pvalue >= 1e-3
+
+
+# --------------------------------------------------------------------------
 # DSpark length selection and the packed verify of the selected windows
 # --------------------------------------------------------------------------
 
