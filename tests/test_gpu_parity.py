@@ -373,6 +373,18 @@ def test_tree_build_small(B, K, V, N):
     _tree_compare(out, ref)
 
 
+# Peaked marginals make deep trees, where a child often beats the next
+# sibling: many build rounds of one or two pops each.
+@pytest.mark.parametrize("sigma", [4.0, 8.0])
+def test_tree_build_deep(sigma):
+    B, K, V, N = 16, 16, 2000, 64
+    case = wl.gen_config4(device="cuda", seed=17 + int(sigma), B=B, K=K, V=V, N=N, sigma=sigma)
+    out = sd.build_tree(case.marginals, N)
+    ref = oracle.build_tree(wl.to_host_f32(case.marginals), B, K, V, N)
+    _tree_compare(out, ref)
+    assert ref["depth"].max() >= 4
+
+
 def test_tree_build_ties():
     B, K, V, N = 3, 4, 40, 30
     m = torch.full((B, K, V), 1.0 / V, device="cuda")        # every score ties
