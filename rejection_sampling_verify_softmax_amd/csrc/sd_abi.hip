@@ -8,6 +8,8 @@
 
 #include <math.h>
 
+#include <algorithm>
+
 namespace {
 
 constexpr int kMaxB = 1 << 20;
@@ -62,20 +64,18 @@ sd_status_t sd_workspace_bytes(sd_op_t op, int32_t B, int32_t K_max, int32_t V, 
     switch (op) {
         case SD_OP_CHAIN:
             if (bad_size(B, K_max, V) || top_k < 0 || top_k > SD_MAX_TOPK) return SD_EINVAL;
-            // the larger of the full-vocabulary, top-k and greedy layouts for bf16
+            // the largest of the full-vocabulary, top-k and greedy layouts, either dtype
             {
-                size_t a = sd::chain_full_ws_bytes(B, K_max, V, 0);
-                size_t b = sd::chain_full_ws_bytes(B, K_max, V, 1);
-                size_t c = topk_on(top_k, V) ? sd::chain_topk_ws_bytes(B, K_max, V, top_k) : 0;
-                size_t d = sd::greedy_ws_bytes(B, K_max, V, 0);
-                size_t m = a > b ? a : b;
-                m = m > c ? m : c;
-                *bytes = m > d ? m : d;
+                size_t m = sd::chain_full_ws_bytes(B, K_max, V, 0);
+                m = std::max(m, sd::chain_full_ws_bytes(B, K_max, V, 1));
+                if (topk_on(top_k, V)) m = std::max(m, sd::chain_topk_ws_bytes(B, K_max, V, top_k));
+                m = std::max(m, sd::greedy_ws_bytes(B, K_max, V, 0));
+                *bytes = std::max(m, sd::greedy_ws_bytes(B, K_max, V, 1));
             }
             return SD_OK;
         case SD_OP_GREEDY:
             if (bad_size(B, K_max, V)) return SD_EINVAL;
-            *bytes = sd::greedy_ws_bytes(B, K_max, V, 0);   // f32 chunks are the smaller ones
+            *bytes = std::max(sd::greedy_ws_bytes(B, K_max, V, 0), sd::greedy_ws_bytes(B, K_max, V, 1));
             return SD_OK;
         case SD_OP_BUILD_TREE:
             if (B < 1 || B > kMaxB || K_max < 0 || K_max > SD_MAX_TREE_K || V < 1 || V > kMaxV ||
