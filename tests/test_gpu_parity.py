@@ -211,6 +211,38 @@ def test_chain_window_of_64_positions(mode):
     assert int(out["accepted_len"][0]) == K
 
 
+# The largest vocabulary the ABI accepts (V < 2^24): the 16-byte vector path
+# (V a multiple of 8) and the element-wise path (odd V), for the stochastic
+# chain, greedy verification and the sampled tree walk.
+@pytest.mark.parametrize("V", [(1 << 24) - 8, (1 << 24) - 1])
+def test_maximum_vocabulary(V):
+    B, K = 2, 2
+    _say(f"maximum vocabulary V={V}")
+    case = wl.gen_base_noise_chain(23, B=B, K=K, V=V, base_sigma=2.0, noise_sigma=0.6,
+                                   temperature=1.0, dtype="bf16", device="cuda")
+    info = compare_chain(run_chain(case), oracle_chain(case))
+    _say(f"  chain {info}")
+    # greedy: sequence 0 drafts the target argmax, sequence 1 the draft tokens
+    tok = case.tokens.clone()
+    rows0 = torch.arange(0, K, device="cuda")
+    tok[:K] = wl.first_argmax(case.target.index_select(0, rows0)).to(torch.int32)
+    g = sd.verify_greedy(case.target, tok, B=B, K_max=K)
+    host = wl.to_host_f32(case.target)
+    ref = oracle.verify_greedy(host, tok.cpu().numpy(), None, B, K, V)
+    np.testing.assert_array_equal(g["accepted_len"].cpu().numpy(), ref["A"])
+    np.testing.assert_array_equal(g["next_token"].cpu().numpy(), ref["next"])
+    assert ref["A"][0] == K
+    # sampled walk over a two-node tree whose child carries the root row's argmax
+    rows = case.target[:2].reshape(1, 2, V).contiguous()
+    tree = {"token": torch.tensor([[-1, int(wl.first_argmax(rows[0, :1])[0])]], dtype=torch.int32, device="cuda"),
+            "parent": torch.tensor([[-1, 0]], dtype=torch.int32, device="cuda"),
+            "n_nodes": torch.tensor([2], dtype=torch.int32, device="cuda")}
+    for T in (0.0, 0.05, 1.0):
+        u = torch.tensor([[0.25, 0.75]], device="cuda")
+        _sampled_walk_check(tree, rows, T, None if T == 0.0 else u)
+    del host
+
+
 def test_chain_run_twice_bit_identical():
     case = wl.gen_base_noise_chain(9, B=16, K=6, V=50000, base_sigma=2.0, noise_sigma=0.7,
                                    temperature=1.0, dtype="bf16", device="cuda")
