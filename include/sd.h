@@ -74,7 +74,8 @@ typedef enum {
     SD_OP_GREEDY = 1,
     SD_OP_BUILD_TREE = 2,
     SD_OP_VERIFY_TREE = 3,
-    SD_OP_SELECT_LEN = 4
+    SD_OP_SELECT_LEN = 4,
+    SD_OP_VERIFY_TREE_SAMPLED = 5
 } sd_op_t;
 
 /* seq_status bits */
@@ -237,20 +238,21 @@ sd_status_t sd_verify_tree(const void* target_logits, sd_dtype_t dtype,
  * it turns that token into the extra token; SD §1: temperature and truncation
  * belong inside p, and the chain's ratio test is not a rule for a tree]. At
  * node n the target selects its token by drawing from its own row: the inverse
- * CDF, in token-id order, of p_n = softmax(target row n / T) at
- * uniforms[b*N + n] (the first token whose running mass exceeds the uniform;
+ * CDF, in token-id order, of p_n = softmax(target row n / T) over its kept
+ * set (top_k below) at uniforms[b*N + n] (the first token whose running mass
+ * exceeds the uniform;
  * if rounding leaves none, the last token with positive mass). The tree's
  * nodes are fixed drafts, so no draft probability enters; a walk visits a node
  * at most once, so every draw has a fresh uniform and each committed token is
  * a draw from the target given the tokens before it. T == 0 takes the lowest-id
- * argmax instead, the walk of sd_verify_tree. Only the rows on the walk are
- * read, one per step.
+ * argmax instead, the walk of sd_verify_tree.
  *
  *   target_logits [B, N, V] dtype     row n: target distribution after node n
  *   node_token, node_parent [B, N] int32, n_nodes [B] int32 (as built)
  *   uniforms     [B, N] fp32 in [0, 1) (ignored and may be NULL when T == 0)
- *   temperature  T >= 0, finite; top_k 0 (or >= V) = no truncation; truncation
- *                with T > 0 is not built (SD_EUNSUPPORTED)
+ *   temperature  T >= 0, finite
+ *   top_k        0 (or >= V): no truncation; 1 .. SD_MAX_TOPK: p_n keeps the
+ *                top_k ids of row n by (logit desc, id asc), as in the chain
  *   path_nodes   [B, N] int32 out     accepted node ids in walk order (root
  *                                     excluded), -1 padded
  *   accepted_len [B] int32 out; next_token [B] int32 out (-1 when the row it
@@ -258,14 +260,18 @@ sd_status_t sd_verify_tree(const void* target_logits, sd_dtype_t dtype,
  *   seq_status   [B] int32 out or NULL: SD_SEQ_NONFINITE when a visited row is
  *                non-finite (no finite maximum, or a NaN in its sum); the walk
  *                stops there
- * Needs no workspace.
+ *   workspace    sd_workspace_bytes(SD_OP_VERIFY_TREE_SAMPLED, B, 0, V, top_k,
+ *                N) bytes: none (NULL allowed) without truncation. Without
+ *                truncation only the rows on the walk are read, one per step;
+ *                with it every node's row is reduced to its kept list first.
  */
 sd_status_t sd_verify_tree_sampled(const void* target_logits, sd_dtype_t dtype,
                                    const int32_t* node_token, const int32_t* node_parent,
                                    const int32_t* n_nodes, const float* uniforms, int32_t B,
                                    int32_t N, int32_t V, float temperature, int32_t top_k,
                                    int32_t* path_nodes, int32_t* accepted_len,
-                                   int32_t* next_token, int32_t* seq_status, void* hip_stream);
+                                   int32_t* next_token, int32_t* seq_status, void* workspace,
+                                   size_t workspace_bytes, void* hip_stream);
 
 /*
  * EAGLE-2-style verification tree [SD §4 EAGLE-2: candidates expanded along

@@ -27,7 +27,7 @@ LIB_PATH = os.path.join(_HERE, "libsd.so")
 
 SD_OK, SD_EINVAL, SD_EUNSUPPORTED, SD_EWORKSPACE, SD_EHIP = 0, 1, 2, 3, 4
 SD_F32, SD_BF16 = 0, 1
-OP_CHAIN, OP_GREEDY, OP_BUILD_TREE, OP_VERIFY_TREE, OP_SELECT_LEN = 0, 1, 2, 3, 4
+OP_CHAIN, OP_GREEDY, OP_BUILD_TREE, OP_VERIFY_TREE, OP_SELECT_LEN, OP_VERIFY_TREE_SAMPLED = 0, 1, 2, 3, 4, 5
 SEQ_BAD_TOKEN, SEQ_NONFINITE = 1, 2
 
 _lib = None
@@ -64,7 +64,7 @@ def _load():
     lib.sd_build_tree.restype = ctypes.c_int
     lib.sd_verify_tree.argtypes = [P, ctypes.c_int, P, P, P, I, I, I, P, P, P, P, Z, P]
     lib.sd_verify_tree.restype = ctypes.c_int
-    lib.sd_verify_tree_sampled.argtypes = [P, ctypes.c_int, P, P, P, P, I, I, I, F, I, P, P, P, P, P]
+    lib.sd_verify_tree_sampled.argtypes = [P, ctypes.c_int, P, P, P, P, I, I, I, F, I, P, P, P, P, P, Z, P]
     lib.sd_verify_tree_sampled.restype = ctypes.c_int
     lib.sd_select_len.argtypes = [P, I, I, F, P, P, P, P]
     lib.sd_select_len.restype = ctypes.c_int
@@ -366,9 +366,9 @@ def verify_tree(target: torch.Tensor, tree: dict, workspace: Optional[torch.Tens
 
 def verify_tree_sampled(target: torch.Tensor, tree: dict, uniforms: Optional[torch.Tensor],
                         temperature: float, top_k: int = 0, out: Optional[dict] = None,
-                        stream=None) -> dict:
+                        workspace: Optional[torch.Tensor] = None, stream=None) -> dict:
     """sd_verify_tree_sampled. target [B, N, V] (bf16 or fp32); tree from build_tree;
-    uniforms [B, N] float32 (None when temperature == 0)."""
+    uniforms [B, N] float32 (None when temperature == 0); top_k 0 = no truncation."""
     dev = target.device
     _check(target, "target", device=dev)
     dt = _dtype_code(target)
@@ -386,10 +386,13 @@ def verify_tree_sampled(target: torch.Tensor, tree: dict, uniforms: Optional[tor
     A = _get(o, "accepted_len", lambda: torch.empty(B, dtype=torch.int32, device=dev))
     nxt = _get(o, "next_token", lambda: torch.empty(B, dtype=torch.int32, device=dev))
     st = _get(o, "status", lambda: torch.empty(B, dtype=torch.int32, device=dev))
+    nbytes = workspace_bytes(OP_VERIFY_TREE_SAMPLED, B, 0, V, int(top_k), N)
+    ws = _workspace(nbytes, dev, workspace) if nbytes > 0 else None
     r = _load().sd_verify_tree_sampled(_ptr(target), dt, _ptr(tree["token"]), _ptr(tree["parent"]),
                                        _ptr(tree["n_nodes"]), _ptr(uniforms), B, N, V,
                                        ctypes.c_float(float(temperature)), int(top_k), _ptr(path),
-                                       _ptr(A), _ptr(nxt), _ptr(st), _stream(stream))
+                                       _ptr(A), _ptr(nxt), _ptr(st), _ptr(ws),
+                                       ctypes.c_size_t(0 if ws is None else ws.numel()), _stream(stream))
     _raise(r, "sd_verify_tree_sampled")
     return {"path": path, "accepted_len": A, "next_token": nxt, "status": st}
 

@@ -88,6 +88,12 @@ sd_status_t sd_workspace_bytes(sd_op_t op, int32_t B, int32_t K_max, int32_t V, 
                 return SD_EINVAL;
             *bytes = 0;   // the walk reads its rows on demand and keeps its state in LDS
             return SD_OK;
+        case SD_OP_VERIFY_TREE_SAMPLED:
+            if (B < 1 || B > kMaxB || V < 1 || V > kMaxV || N < 2 || N > SD_MAX_TREE_N || top_k < 0 ||
+                top_k > SD_MAX_TOPK)
+                return SD_EINVAL;
+            *bytes = topk_on(top_k, V) ? sd::tree_walk_topk_ws_bytes(B, N, top_k) : 0;
+            return SD_OK;
         case SD_OP_SELECT_LEN:
             if (B < 1 || B > kMaxB || K_max < 0 || K_max > SD_MAX_K) return SD_EINVAL;
             *bytes = 0;
@@ -233,18 +239,27 @@ sd_status_t sd_verify_tree_sampled(const void* target_logits, sd_dtype_t dtype,
                                    const int32_t* n_nodes, const float* uniforms, int32_t B,
                                    int32_t N, int32_t V, float temperature, int32_t top_k,
                                    int32_t* path_nodes, int32_t* accepted_len,
-                                   int32_t* next_token, int32_t* seq_status, void* hip_stream) {
+                                   int32_t* next_token, int32_t* seq_status, void* workspace,
+                                   size_t workspace_bytes, void* hip_stream) {
     if (B < 1 || B > kMaxB || V < 1 || V > kMaxV || N < 2 || N > SD_MAX_TREE_N || bad_dtype(dtype))
         return SD_EINVAL;
-    if (!isfinite(temperature) || temperature < 0.0f || top_k < 0) return SD_EINVAL;
+    if (!isfinite(temperature) || temperature < 0.0f || top_k < 0 || top_k > SD_MAX_TOPK)
+        return SD_EINVAL;
     if (!target_logits || !node_token || !node_parent || !n_nodes || !path_nodes || !accepted_len ||
         !next_token || (temperature > 0.0f && !uniforms))
         return SD_EINVAL;
-    if (temperature > 0.0f && top_k > 0 && top_k < V) return SD_EUNSUPPORTED;
+    const hipStream_t stream = static_cast<hipStream_t>(hip_stream);
+    if (temperature > 0.0f && topk_on(top_k, V)) {
+        if (!workspace) return SD_EINVAL;
+        if (workspace_bytes < sd::tree_walk_topk_ws_bytes(B, N, top_k)) return SD_EWORKSPACE;
+        return from_hip(sd::launch_tree_walk_topk(target_logits, (int)dtype, node_token, node_parent,
+                                                  n_nodes, uniforms, B, N, V, temperature, top_k,
+                                                  path_nodes, accepted_len, next_token, seq_status,
+                                                  workspace, stream));
+    }
     return from_hip(sd::launch_tree_walk_rows(target_logits, (int)dtype, node_token, node_parent,
                                               n_nodes, uniforms, B, N, V, temperature, path_nodes,
-                                              accepted_len, next_token, seq_status,
-                                              static_cast<hipStream_t>(hip_stream)));
+                                              accepted_len, next_token, seq_status, stream));
 }
 
 sd_status_t sd_select_len(const float* conf, int32_t B, int32_t K_max, float cost_per_position,

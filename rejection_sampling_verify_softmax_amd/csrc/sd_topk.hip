@@ -501,7 +501,7 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(4))) voi
     TopEntry* L = lists + (int64_t)task * topk;
     const bool stats = rowtop != nullptr;
     int y = -1;
-    if (stats) {                     // task = ((b * (K_max + 1) + s) * 2 + side)
+    if (stats && chain) {            // task = ((b * (K_max + 1) + s) * 2 + side)
         const int rest = task >> 1;
         const int s = rest % (K_max + 1);
         int d0, k;
@@ -729,6 +729,62 @@ __global__ __launch_bounds__(kBlock) void k_chain_topk_decide(
         if (A_full_out) A_full_out[b] = A_full;
         next_out[b] = next;
         if (R_out) R_out[b] = (float)R;
+        if (status_out) status_out[b] = status;
+    }
+}
+
+// ---------------------------------------------------------------------------
+// DDTree walk under a sampling target with top-k truncation [SD §5 DDTree,
+// SD §1]: k_topk_rows has written every node row's kept list and fp64 softmax
+// statistics; one wave per sequence walks, drawing the target's token at each
+// node from the node's kept list (token-id order, the node's uniform) and
+// moving to the child that carries it.
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(kBlock) void k_tree_walk_topk(
+    const TopEntry* __restrict__ lists, const RowTop* __restrict__ rowtop,
+    const int32_t* __restrict__ node_token, const int32_t* __restrict__ node_parent,
+    const int32_t* __restrict__ n_nodes, const float* __restrict__ uniforms, int B, int N, int topk,
+    float temperature, int32_t* __restrict__ path, int32_t* __restrict__ A_out,
+    int32_t* __restrict__ next_out, int32_t* __restrict__ status_out) {
+    __shared__ double wbuf_all[kWavesPerBlock][kMaxTopk];
+    __shared__ int ibuf_all[kWavesPerBlock][kMaxTopk];
+    __shared__ TopEntry pl_all[kWavesPerBlock][kMaxTopk];
+    const int w = threadIdx.x / kWave;
+    const int lane = threadIdx.x & (kWave - 1);
+    const int b = blockIdx.x * kWavesPerBlock + w;
+    if (b >= B) return;
+    int nn = n_nodes[b];
+    nn = nn < 1 ? 1 : (nn > N ? N : nn);
+    const int my_tok = lane < nn ? node_token[(int64_t)b * N + lane] : -1;
+    const int my_par = lane < nn ? node_parent[(int64_t)b * N + lane] : -2;
+    if (lane < N) path[(int64_t)b * N + lane] = -1;
+    const double T = (double)temperature;
+    int node = 0, len = 0, next = -1, status = 0;
+    for (int step = 0; step < N; ++step) {
+        const int64_t r = (int64_t)b * N + node;
+        const RowTop sp = rowtop[r];
+        if (!sp.valid) {
+            status |= 2;
+            next = -1;
+            break;
+        }
+        double unused;
+        const int g = list_inverse_cdf(lists + r * topk, sp, nullptr, sp, false, T, (double)uniforms[r],
+                                       wbuf_all[w], ibuf_all[w], pl_all[w], pl_all[w], &unused);
+        const unsigned long long h =
+            __ballot(g >= 0 && lane >= 1 && lane < nn && my_par == node && my_tok == g);
+        if (!h) {
+            next = g;
+            break;
+        }
+        const int child = __ffsll(h) - 1;
+        if (lane == 0) path[(int64_t)b * N + len] = child;
+        ++len;
+        node = child;
+    }
+    if (lane == 0) {
+        A_out[b] = len;
+        next_out[b] = next;
         if (status_out) status_out[b] = status;
     }
 }
@@ -1192,6 +1248,48 @@ hipError_t launch_chain_topk(const ChainArgs& a) {
     }
     if (a.V % F32::kVec == 0) return chain_topk_impl<F32, true>(a);
     return chain_topk_impl<F32, false>(a);
+}
+
+size_t tree_walk_topk_ws_bytes(int B, int N, int top_k) {
+    size_t bytes = 0;
+    topk_layout(nullptr, (size_t)B * N, top_k, nullptr, 0, &bytes);
+    return bytes;
+}
+
+hipError_t launch_tree_walk_topk(const void* target, int dtype, const int32_t* tok, const int32_t* par,
+                                 const int32_t* n_nodes, const float* uniforms, int B, int N, int V,
+                                 float temperature, int top_k, int32_t* path, int32_t* accepted_len,
+                                 int32_t* next_token, int32_t* seq_status, void* ws,
+                                 hipStream_t stream) {
+    const size_t tasks = (size_t)B * N;
+    TopkLayout L;
+    topk_layout(ws, tasks, top_k, &L, 0);
+    if (dtype == 1) {
+        const auto* rows = static_cast<const Bf16::raw*>(target);
+        if (V % Bf16::kVec == 0)
+            PassTimer::launch(k_topk_rows<Bf16, true>, dim3((unsigned)tasks), dim3(kBlock), stream, rows,
+                              rows, nullptr, 0, V, top_k, 0, nullptr, temperature, L.lists, L.counts,
+                              L.rowtop, 0, 1, nullptr, 0);
+        else
+            PassTimer::launch(k_topk_rows<Bf16, false>, dim3((unsigned)tasks), dim3(kBlock), stream, rows,
+                              rows, nullptr, 0, V, top_k, 0, nullptr, temperature, L.lists, L.counts,
+                              L.rowtop, 0, 1, nullptr, 0);
+    } else {
+        const auto* rows = static_cast<const F32::raw*>(target);
+        if (V % F32::kVec == 0)
+            PassTimer::launch(k_topk_rows<F32, true>, dim3((unsigned)tasks), dim3(kBlock), stream, rows,
+                              rows, nullptr, 0, V, top_k, 0, nullptr, temperature, L.lists, L.counts,
+                              L.rowtop, 0, 1, nullptr, 0);
+        else
+            PassTimer::launch(k_topk_rows<F32, false>, dim3((unsigned)tasks), dim3(kBlock), stream, rows,
+                              rows, nullptr, 0, V, top_k, 0, nullptr, temperature, L.lists, L.counts,
+                              L.rowtop, 0, 1, nullptr, 0);
+    }
+    const unsigned grid = (unsigned)((B + kWavesPerBlock - 1) / kWavesPerBlock);
+    hipLaunchKernelGGL(k_tree_walk_topk, dim3(grid), dim3(kBlock), 0, stream, L.lists, L.rowtop, tok, par,
+                       n_nodes, uniforms, B, N, top_k, temperature, path, accepted_len, next_token,
+                       seq_status);
+    return hipGetLastError();
 }
 
 hipError_t launch_tree_build(const float* marg, int B, int K, int V, int N, int32_t* tok,

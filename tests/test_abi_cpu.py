@@ -166,9 +166,9 @@ def test_tree_sampled_rejects_invalid_arguments(L):
     one = ctypes.c_void_p(1)
     f = ctypes.c_float
 
-    def ts(dtype=1, uni=one, B=2, N=8, V=100, T=1.0, top_k=0, out=one):
+    def ts(dtype=1, uni=one, B=2, N=8, V=100, T=1.0, top_k=0, out=one, ws=None, wsb=0):
         return L.sd_verify_tree_sampled(one, dtype, one, one, one, uni, B, N, V, f(T), top_k, out, one,
-                                        one, None, None)
+                                        one, None, ws, wsb, None)
     assert ts(B=0) == 1
     assert ts(N=1) == 1
     assert ts(N=65) == 1
@@ -180,8 +180,14 @@ def test_tree_sampled_rejects_invalid_arguments(L):
     assert ts(top_k=-1) == 1
     assert ts(uni=None) == 1              # uniforms are required when T > 0
     assert ts(out=None) == 1
-    assert ts(top_k=50) == 2              # truncation under sampling is not built
+    assert ts(top_k=257) == 1             # above SD_MAX_TOPK
+    assert ts(top_k=50) == 1              # truncation needs the workspace
+    assert ts(top_k=50, ws=one, wsb=64) == 3
     assert ts(top_k=50, uni=None, T=0.0, out=None) == 1
+    import rejection_sampling_verify_softmax_amd as sd
+    assert sd.workspace_bytes(sd.OP_VERIFY_TREE_SAMPLED, 32, 0, 32000, 0, 64) == 0
+    assert sd.workspace_bytes(sd.OP_VERIFY_TREE_SAMPLED, 32, 0, 32000, 50, 64) >= 32 * 64 * 50 * 8
+    assert sd.workspace_bytes(sd.OP_VERIFY_TREE_SAMPLED, 32, 0, 40, 50, 64) == 0    # top_k >= V: off
 
 
 def test_binding_fails_loudly_without_gpu():

@@ -566,13 +566,13 @@ def test_tree_walk_planted():
 # DDTree walk under a sampling target (rows read on demand, one per step)
 # --------------------------------------------------------------------------
 
-def _sampled_walk_check(tree, target, T, u):
+def _sampled_walk_check(tree, target, T, u, top_k=0):
     B, N, V = (int(x) for x in target.shape)
-    out = sd.verify_tree_sampled(target, tree, u, T)
+    out = sd.verify_tree_sampled(target, tree, u, T, top_k=top_k)
     ref = oracle.verify_tree_sampled(wl.to_host_f32(target), tree["token"].cpu().numpy(),
                                      tree["parent"].cpu().numpy(), tree["n_nodes"].cpu().numpy(),
                                      (u.cpu().numpy() if u is not None else np.zeros((B, N), np.float32)),
-                                     B, N, V, T)
+                                     B, N, V, T, top_k)
     ok = ref["margin"] == 0
     for kg, kr in (("accepted_len", "A"), ("next_token", "next"), ("status", "status")):
         got = out[kg].cpu().numpy()
@@ -596,6 +596,47 @@ def test_tree_walk_sampled_matches_oracle(dtype, V, T):
     u = wl.grid_uniforms((B, N), torch.Generator(device="cuda").manual_seed(V), "cuda")
     out, ref = _sampled_walk_check(tree, target, T, u)
     _say(f"  mean walk {ref['A'].mean():.2f}, max {ref['A'].max()}, margin {int((ref['margin'] != 0).sum())}")
+
+
+# Top-k truncation inside the sampled walk: every node row is reduced to its
+# kept list first (ties at the k-th value keep the lower ids).
+@pytest.mark.parametrize("dtype,V,T,top_k", [("bf16", 32000, 1.0, 50), ("bf16", 32001, 0.7, 256),
+                                             ("f32", 20000, 1.3, 1), ("bf16", 60, 1.0, 50),
+                                             ("f32", 999, 0.5, 7)])
+def test_tree_walk_sampled_topk_matches_oracle(dtype, V, T, top_k):
+    B, K, N = 24, 16, 64
+    _say(f"sampled walk top-k {top_k} {dtype} V={V} T={T}")
+    case = wl.gen_config4(device="cuda", seed=37 + V, B=B, K=K, V=V, N=N)
+    tree = sd.build_tree(case.marginals, N)
+    target = case.target_for_depths(tree["depth"], tree["n_nodes"])
+    if dtype == "f32":
+        target = target.float()
+    u = wl.grid_uniforms((B, N), torch.Generator(device="cuda").manual_seed(V + top_k), "cuda")
+    out, ref = _sampled_walk_check(tree, target, T, u, top_k=top_k)
+    if top_k == 1:                 # one kept id: the argmax walk for every uniform
+        g = sd.verify_tree(target, tree)
+        assert torch.equal(out["path"], g["path"]) and torch.equal(out["next_token"], g["next_token"])
+    _say(f"  mean walk {ref['A'].mean():.2f}, margin {int((ref['margin'] != 0).sum())}")
+
+
+def test_tree_walk_sampled_topk_ties_and_nonfinite():
+    V, N, B = 12, 6, 3
+    tok = torch.tensor([[-1, 4, 7, 2, 9, -1]] * B, dtype=torch.int32, device="cuda")
+    par = torch.tensor([[-1, 0, 0, 1, 3, -1]] * B, dtype=torch.int32, device="cuda")
+    nn = torch.tensor([5] * B, dtype=torch.int32, device="cuda")
+    rows = torch.zeros((B, N, V), device="cuda")
+    rows[:, :, 4] = 1.0                 # row max at id 4 ...
+    rows[:, :, 7] = 1.0                 # ... tied with id 7: top-1 keeps id 4
+    rows[1, 1, :] = float("nan")        # sequence 1: no kept finite entry at node 1
+    rows[2, 0, 3] = float("inf")        # sequence 2: an infinite maximum at the root
+    tree = {"token": tok, "parent": par, "n_nodes": nn}
+    u = torch.full((B, N), 0.9, device="cuda")
+    out = sd.verify_tree_sampled(rows, tree, u, 1.0, top_k=1)
+    ref = oracle.verify_tree_sampled(rows.cpu().numpy(), tok.cpu().numpy(), par.cpu().numpy(),
+                                     nn.cpu().numpy(), u.cpu().numpy(), B, N, V, 1.0, 1)
+    for kg, kr in (("accepted_len", "A"), ("next_token", "next"), ("status", "status")):
+        np.testing.assert_array_equal(out[kg].cpu().numpy(), ref[kr], err_msg=kg)
+    assert out["accepted_len"].tolist()[0] == 1 and out["status"].tolist() == [0, 2, 2]
 
 
 def test_tree_walk_sampled_T0_is_the_argmax_walk():

@@ -676,6 +676,22 @@ def test_sampled_walk_small_temperature_is_the_argmax_walk():
         assert (out["path"] == ref["path"]).all()
 
 
+def test_sampled_walk_top1_is_the_argmax_walk():
+    """Top-1 truncation keeps only the lowest-id maximum, so the sampled walk is
+    the argmax walk for every temperature and uniform (ties included)."""
+    rng = np.random.default_rng(59)
+    B, N, V = 48, 6, 7
+    rows = rng.integers(0, 4, size=(B, N, V)).astype(np.float32)     # many ties
+    tok = np.tile(WALK_TOKEN, (B, 1))
+    par = np.tile(WALK_PARENT, (B, 1))
+    nn = np.full(B, N, np.int32)
+    ref = oracle.verify_tree(rows, tok, par, nn, B, N, V)
+    for T in (0.3, 1.0, 5.0):
+        out = oracle.verify_tree_sampled(rows, tok, par, nn, grid_u(rng, (B, N)), B, N, V, T, 1)
+        assert (out["A"] == ref["A"]).all() and (out["next"] == ref["next"]).all()
+        assert (out["path"] == ref["path"]).all()
+
+
 def test_sampled_walk_nonfinite_row_and_one_hot_rows():
     N, V = WALK_P.shape
     # one-hot target rows spell the path root -> 1 -> 3 -> 5, then token 2
