@@ -11,8 +11,10 @@ resident in HBM when timing starts.
 
 Printed: one JSON line with the throughput in verified draft positions per
 second, the roofline of the dominant kernel (the streaming pass over the logit
-rows, timed with HIP events on its own stream) and the CPU oracle timed on a
-bounded sample of the same workload.
+rows, timed with HIP events on its own stream), the CPU oracle timed on a
+bounded sample of the same workload, and the parity of the timed step against
+that oracle run (verify lengths of every sequence, committed results of the
+sampled sequences; bit-exact outside the oracle's margin cases).
 
 Other workloads (--workload greedy|topk|tree|tree_sampled|chain1|kv|rerank) measure the other kernels
 for the design notes; their inputs are rotated across copies so that the
@@ -119,7 +121,8 @@ def setup_adaptive(torch, sd, wl):
         "mean_k": positions / B, "mean_A": float(A.mean()),
         "rows_streamed": rows1 + rows2, "rows_in_windows": R_t + R_d,
     }
-    cpu = {"case": case, "packed": packed, "k": sel["k"].cpu().numpy(), "cu": sel["cu"].cpu().numpy()}
+    cpu = {"case": case, "packed": packed, "k": sel["k"].cpu().numpy(), "cu": sel["cu"].cpu().numpy(),
+           "out": out}
     return step, meta, cpu
 
 
@@ -355,22 +358,42 @@ def run_cpu_baseline(cpu, target_seconds: float):
         di = torch.as_tensor(d_rows, device="cuda")
         lens = [int(cu[s + 1] - cu[s]) for s in seqs]
         groups.append(dict(
+            seqs=np.array(seqs),
             tgt=wl.to_host_f32(packed.target.index_select(0, ti)),
             dft=wl.to_host_f32(packed.draft.index_select(0, di)),
             tok=packed.tokens.index_select(0, di).cpu().numpy(),
             uni=packed.uniforms.index_select(0, ti).cpu().numpy(),
             cu=np.concatenate([[0], np.cumsum(lens)]).astype(np.int32),
             n=len(seqs), k_max=max(lens), pos=int(sum(lens))))
+    # Parity of the timed GPU step on the same inputs: its verify lengths for
+    # every sequence, and its committed results for the sampled sequences (the
+    # first visit of each group), bit-exact outside the oracle's margin cases.
+    out = cpu["out"]
+    A_g, nx_g = out["accepted_len"].cpu().numpy(), out["next_token"].cpu().numpy()
+    st_g = out["status"].cpu().numpy()
+    sel_margin = sel["margin"] != 0
+    par = {"select_len_sequences": int(B),
+           "select_len_mismatches": int(((cpu["k"] != sel["k"]) & ~sel_margin).sum()),
+           "select_len_margin_cases": int(sel_margin.sum()),
+           "verify_sequences": 0, "verify_mismatches": 0, "verify_margin_cases": 0}
     done_pos, done_seq, spent, calls = 0, 0, t_sel, 0
-    while spent < target_seconds:
+    while spent < target_seconds or calls < n_groups:
         g = groups[calls % n_groups]
         t0 = time.perf_counter()
-        oracle.verify_chain(g["tgt"], g["dft"], g["tok"], g["uni"], g["cu"], g["n"], g["k_max"], V,
-                            1.0, threads=threads, want_probs=False)
+        ref = oracle.verify_chain(g["tgt"], g["dft"], g["tok"], g["uni"], g["cu"], g["n"], g["k_max"], V,
+                                  1.0, threads=threads, want_probs=False)
         spent += time.perf_counter() - t0
+        if calls < n_groups:
+            sq, mg = g["seqs"], ref["margin"] != 0
+            bad = ~mg & ((A_g[sq] != ref["A"]) | (nx_g[sq] != ref["next"]) | (st_g[sq] != ref["status"]))
+            par["verify_sequences"] += len(sq)
+            par["verify_mismatches"] += int(bad.sum())
+            par["verify_margin_cases"] += int(mg.sum())
         done_pos += g["pos"]
         done_seq += g["n"]
         calls += 1
+    par["pass"] = par["select_len_mismatches"] == 0 and par["verify_mismatches"] == 0
+    cpu["parity"] = par
     return {"value": done_pos / spent, "unit": "positions/s", "cores": threads, "kind": "oracle",
             "sample": (f"CPU oracle (fp64 C, OpenMP over sequences): length selection for all {B} "
                        f"sequences, then packed chain verification of the first {n_groups * group} "
@@ -495,6 +518,7 @@ def main():
     if cpu is not None and not args.no_cpu_baseline:
         log("timing the CPU oracle on a bounded sample")
         result["cpu_baseline"] = run_cpu_baseline(cpu, args.cpu_seconds)
+        result["parity"] = cpu.get("parity")
     else:
         result["cpu_baseline"] = None
     print(json.dumps(result), flush=True)
