@@ -790,7 +790,10 @@ __global__ __launch_bounds__(kBlock) void k_tree_walk_topk(
 }
 
 // ---------------------------------------------------------------------------
-// DDTree best-first build: one wave per sequence. The frontier holds, for the
+// DDTree best-first build: one 256-thread workgroup per sequence. The tree is
+// the first N-1 prefixes in the pop order below; build_by_threshold finds them
+// directly in the common case, and otherwise wave 0 pops them one by one.
+// The frontier of the pop loop holds, for the
 // nodes popped so far, the first child and the next sibling not yet taken,
 // kept sorted best first under (Q desc, depth asc, rank tuple lexicographically
 // asc), one prefix per lane (lane 0 the best). A pop reads lane 0; its child
@@ -853,15 +856,174 @@ __device__ __forceinline__ unsigned long long shift_pick64(unsigned long long v,
     return ((unsigned long long)shift_pick((uint32_t)(v >> 32), nb) << 32) | shift_pick((uint32_t)v, nb);
 }
 
-__global__ __launch_bounds__(kWave) void k_tree_build(
+// The same tree by threshold, for the common case. With at least N-1 entries
+// in the depth-1 list, beta = the (N-1)-th of them is a lower bound on the
+// score of the (N-1)-th prefix (the N-1 depth-1 prefixes all reach it), so the
+// tree lies inside C = {prefixes with Q >= beta}. C is prefix-closed (a
+// child's score never exceeds its parent's), so it is enumerated level by
+// level: each member's children at the next depth are a prefix of that
+// depth's list, found by a binary search over the fp32 products. The members
+// are ranked by counting under the pop order, and the first N-1 are the tree
+// (every prefix before a tree node is itself in C). Returns false, having
+// written nothing, when the list is shorter or C exceeds kBuildCap; the pop
+// loop then builds the tree.
+constexpr int kBuildThreads = 256;
+constexpr int kBuildCap = 256;
+constexpr int kBuildWaves = kBuildThreads / kWave;
+static_assert(kBuildCap <= kBuildThreads, "one parent per thread when a level is expanded");
+
+__device__ __forceinline__ int cinfo(int depth, int rank, int parent_plus1) {
+    return depth | (rank << 5) | (parent_plus1 << 11);
+}
+
+__device__ bool build_by_threshold(const float (*qv)[64], const int (*tv)[64], const int* s_cnt, int K,
+                                   int N, int32_t* __restrict__ tok_out, int32_t* __restrict__ par_out,
+                                   int32_t* __restrict__ dep_out, float* __restrict__ score_out,
+                                   unsigned long long* __restrict__ anc_out, int32_t* __restrict__ nn_out) {
+    __shared__ float cQ[kBuildCap];
+    __shared__ int cInfo[kBuildCap];            // depth | rank << 5 | (parent candidate + 1) << 11
+    __shared__ unsigned long long cW0[kBuildCap], cW1[kBuildCap];
+    __shared__ int cRank[kBuildCap];
+    __shared__ int sOff[kBuildCap + 1];
+    __shared__ int wsum[kBuildWaves];
+    __shared__ int nTok[kWave], nPar[kWave], nDep[kWave];
+    __shared__ float nScore[kWave];
+    __shared__ unsigned long long nAnc[kWave];
+    const int tid = threadIdx.x;
+    const int lane = tid & (kWave - 1);
+    const int w = tid / kWave;
+    if (K < 1 || s_cnt[0] < N - 1) return false;
+    const float beta = qv[0][N - 2];
+    if (!(beta > 0.0f)) return false;
+    // depth 1: ranks 0 .. N-2
+    if (tid < N - 1) {
+        cQ[tid] = 1.0f * qv[0][tid];
+        cInfo[tid] = cinfo(1, tid, 0);
+        cW0[tid] = (unsigned long long)tid << 54;   // rank slot of depth 1
+        cW1[tid] = 0ull;
+    }
+    int nc = N - 1, lo = 0, hi = N - 1;
+    for (int d = 1; d < K; ++d) {               // members at depth d get children at depth d+1
+        __syncthreads();
+        const int nd = s_cnt[d];
+        const int i = lo + tid;
+        int c = 0;
+        if (i < hi && nd > 0) {
+            const float Qi = cQ[i];
+            int a = 0, z = nd;
+            while (a < z) {
+                const int mid = (a + z) >> 1;
+                if (Qi * qv[d][mid] >= beta) a = mid + 1;
+                else z = mid;
+            }
+            c = a;
+        }
+        // block scan of the child counts (members lo.. one per thread)
+        const int ws = wave_incl_scan_int(c);
+        if (lane == kWave - 1) wsum[w] = ws;
+        __syncthreads();
+        int total = 0, excl = ws - c;
+#pragma unroll
+        for (int k = 0; k < kBuildWaves; ++k) {
+            excl += k < w ? wsum[k] : 0;
+            total += wsum[k];
+        }
+        if (total == 0) break;
+        if (nc + total > kBuildCap) return false;
+        if (i < hi) sOff[tid] = excl;
+        if (tid == 0) sOff[hi - lo] = total;
+        __syncthreads();
+        // child slot j: its parent p is the last with sOff[p] <= j
+        for (int j = tid; j < total; j += kBuildThreads) {
+            int a = 0, z = hi - lo;
+            while (z - a > 1) {
+                const int mid = (a + z) >> 1;
+                if (sOff[mid] <= j) a = mid;
+                else z = mid;
+            }
+            const int ip = lo + a, sr = j - sOff[a], slot = nc + j;
+            cQ[slot] = cQ[ip] * qv[d][sr];
+            cInfo[slot] = cinfo(d + 1, sr, ip + 1);
+            Prefix t;
+            t.Q = 0.f;
+            t.meta = 0;
+            t.w0 = cW0[ip];
+            t.w1 = cW1[ip];
+            set_rank(t, d, sr);
+            cW0[slot] = t.w0;
+            cW1[slot] = t.w1;
+        }
+        lo = nc;
+        hi = nc + total;
+        nc += total;
+    }
+    __syncthreads();
+    // ranks by counting under the pop order
+    for (int i = tid; i < nc; i += kBuildThreads) {
+        Prefix me;
+        me.Q = cQ[i];
+        me.meta = cInfo[i] & 31;
+        me.w0 = cW0[i];
+        me.w1 = cW1[i];
+        int r = 0;
+        for (int j = 0; j < nc; ++j) {
+            Prefix o;
+            o.Q = cQ[j];
+            o.meta = cInfo[j] & 31;
+            o.w0 = cW0[j];
+            o.w1 = cW1[j];
+            r += prefix_before(o, me) ? 1 : 0;
+        }
+        cRank[i] = r;
+    }
+    __syncthreads();
+    // the first N-1 become nodes 1 .. N-1 in that order
+    for (int i = tid; i < nc; i += kBuildThreads) {
+        const int r = cRank[i];
+        if (r < N - 1) {
+            const int info = cInfo[i];
+            const int d = info & 31, sr = (info >> 5) & 63, pc = (info >> 11) - 1;
+            const int id = r + 1;
+            nTok[id] = tv[d - 1][sr];
+            nDep[id] = d;
+            nScore[id] = cQ[i];
+            nPar[id] = pc < 0 ? 0 : cRank[pc] + 1;
+        }
+    }
+    if (tid == 0) {
+        nTok[0] = -1;
+        nPar[0] = -1;
+        nDep[0] = 0;
+        nScore[0] = 1.0f;
+        nAnc[0] = 1ull;
+    }
+    __syncthreads();
+    // ancestor masks, one depth at a time (a parent sits one depth up)
+    for (int d = 1; d <= K; ++d) {
+        if (tid >= 1 && tid < N && nDep[tid] == d) nAnc[tid] = nAnc[nPar[tid]] | (1ull << tid);
+        __syncthreads();
+    }
+    if (tid < N) {
+        tok_out[tid] = nTok[tid];
+        par_out[tid] = nPar[tid];
+        dep_out[tid] = nDep[tid];
+        score_out[tid] = nScore[tid];
+        anc_out[tid] = nAnc[tid];
+    }
+    if (tid == 0) *nn_out = N;
+    return true;
+}
+
+__global__ __launch_bounds__(kBuildThreads) void k_tree_build(
     const TopEntry* __restrict__ lists, const int32_t* __restrict__ counts, int K, int N, int W,
     int32_t* __restrict__ node_token, int32_t* __restrict__ node_parent,
     int32_t* __restrict__ node_depth, float* __restrict__ node_score,
     unsigned long long* __restrict__ node_anc, int32_t* __restrict__ n_nodes) {
     __shared__ float qv[kMaxTreeK][64];
     __shared__ int tv[kMaxTreeK][64];
+    __shared__ int s_cnt[kMaxTreeK];
     const int b = blockIdx.x;
-    const int lane = threadIdx.x;
+    const int lane = threadIdx.x;        // (the pop loop runs on wave 0: lane < 64)
     // all loads first (one memory latency), then the LDS copies
     TopEntry e[kMaxTreeK];
 #pragma unroll
@@ -875,7 +1037,13 @@ __global__ __launch_bounds__(kWave) void k_tree_build(
             qv[d][lane] = e[d].x;
             tv[d][lane] = e[d].idx;
         }
+    if (lane < kMaxTreeK) s_cnt[lane] = cnt_d;
     __syncthreads();
+    if (build_by_threshold(qv, tv, s_cnt, K, N, node_token + (int64_t)b * N,
+                           node_parent + (int64_t)b * N, node_depth + (int64_t)b * N,
+                           node_score + (int64_t)b * N, node_anc + (int64_t)b * N, n_nodes + b))
+        return;
+    if (lane >= kWave) return;
     const float q0_d = lane < K ? qv[lane][0] : 0.f;
     // lane n: node n's outputs (node 0 is the root)
     int my_tok = -1, my_par = -1, my_dep = 0;
@@ -1319,7 +1487,7 @@ hipError_t launch_tree_build(const float* marg, int B, int K, int V, int N, int3
         PassTimer::mark_before(stream);
         PassTimer::mark_after(stream);
     }
-    hipLaunchKernelGGL(k_tree_build, dim3(B), dim3(kWave), 0, stream, L.lists, L.counts, K, N, W, tok,
+    hipLaunchKernelGGL(k_tree_build, dim3(B), dim3(kBuildThreads), 0, stream, L.lists, L.counts, K, N, W, tok,
                        par, dep, score, reinterpret_cast<unsigned long long*>(anc), n_nodes);
     return hipGetLastError();
 }

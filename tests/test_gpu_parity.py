@@ -417,6 +417,23 @@ def test_tree_build_deep(sigma):
     assert ref["depth"].max() >= 4
 
 
+def test_tree_build_candidate_overflow():
+    """Two heavy tokens per depth: the prefixes scoring at least the depth-1
+    list's last entry double at every depth, past what the threshold path
+    holds, so these trees come from the pop loop; a flat sequence beside them
+    takes the threshold path in the same launch."""
+    B, K, V, N = 3, 16, 200, 64
+    m = torch.full((B, K, V), 0.1 / (V - 2), device="cuda")
+    m[:, :, 3] = 0.45
+    m[:, :, 150] = 0.45
+    m[2] = torch.softmax(torch.randn(K, V, generator=torch.Generator(device="cuda").manual_seed(4),
+                                     device="cuda") * 0.5, dim=-1)
+    out = sd.build_tree(m, N)
+    ref = oracle.build_tree(m.cpu().numpy(), B, K, V, N)
+    _tree_compare(out, ref)
+    assert ref["depth"][0].max() >= 5
+
+
 def test_tree_build_ties():
     B, K, V, N = 3, 4, 40, 30
     m = torch.full((B, K, V), 1.0 / V, device="cuda")        # every score ties
