@@ -902,7 +902,7 @@ __device__ bool build_by_threshold(const float (*qv)[64], const int (*tv)[64], c
         cW0[tid] = (unsigned long long)tid << 54;   // rank slot of depth 1
         cW1[tid] = 0ull;
     }
-    int nc = N - 1, lo = 0, hi = N - 1;
+    int nc = N - 1, lo = 0, hi = N - 1, maxd = 1;
     for (int d = 1; d < K; ++d) {               // members at depth d get children at depth d+1
         __syncthreads();
         const int nd = s_cnt[d];
@@ -956,6 +956,7 @@ __device__ bool build_by_threshold(const float (*qv)[64], const int (*tv)[64], c
         lo = nc;
         hi = nc + total;
         nc += total;
+        maxd = d + 1;
     }
     __syncthreads();
     // ranks by counting under the pop order
@@ -999,7 +1000,7 @@ __device__ bool build_by_threshold(const float (*qv)[64], const int (*tv)[64], c
     }
     __syncthreads();
     // ancestor masks, one depth at a time (a parent sits one depth up)
-    for (int d = 1; d <= K; ++d) {
+    for (int d = 1; d <= maxd; ++d) {
         if (tid >= 1 && tid < N && nDep[tid] == d) nAnc[tid] = nAnc[nPar[tid]] | (1ull << tid);
         __syncthreads();
     }
