@@ -76,7 +76,7 @@ def load_traffic(kernel: str, workload: str):
 def setup_adaptive(torch, sd, wl):
     import numpy as np
 
-    case = wl.gen_config5(device="cuda")
+    case = wl.gen_adaptive_chain(device="cuda")
     sel = sd.select_len(case.conf, case.cost)
     torch.cuda.synchronize()
     packed = case.packed(sel["k"])
@@ -127,7 +127,7 @@ def setup_adaptive(torch, sd, wl):
 
 
 def setup_greedy(torch, sd, wl):
-    case = wl.gen_config2(device="cuda")
+    case = wl.gen_greedy_chain(device="cuda")
     B, K, V = case.B, case.K_max, case.V
     copies = [case.target] + [case.target.clone() for _ in range(7)]    # 8 x 66 MB > LLC
     ws = torch.empty(sd.workspace_bytes(sd.OP_GREEDY, B, K, V), dtype=torch.uint8, device="cuda")
@@ -148,7 +148,7 @@ def setup_greedy(torch, sd, wl):
 
 
 def setup_topk(torch, sd, wl):
-    case = wl.gen_config3(device="cuda")
+    case = wl.gen_topk_chain(device="cuda")
     B, K, V = case.B, case.K_max, case.V
     ws = torch.empty(sd.workspace_bytes(sd.OP_CHAIN, B, K, V, case.top_k), dtype=torch.uint8, device="cuda")
 
@@ -176,7 +176,7 @@ def setup_topk(torch, sd, wl):
 
 
 def setup_tree(torch, sd, wl):
-    case = wl.gen_config4(device="cuda")
+    case = wl.gen_tree(device="cuda")
     B, K, V, N = case.B, case.K, case.V, case.N
     tree = sd.build_tree(case.marginals, N)
     target = case.target_for_depths(tree["depth"], tree["n_nodes"])
@@ -208,7 +208,7 @@ def setup_tree(torch, sd, wl):
 def setup_tree_sampled(torch, sd, wl):
     # the tree workload's build, then the walk under a sampling target (T = 1):
     # at each node the target draws its own token; only the walk's rows are read
-    case = wl.gen_config4(device="cuda")
+    case = wl.gen_tree(device="cuda")
     B, K, V, N = case.B, case.K, case.V, case.N
     tree = sd.build_tree(case.marginals, N)
     target = case.target_for_depths(tree["depth"], tree["n_nodes"])
@@ -241,7 +241,7 @@ def setup_tree_sampled(torch, sd, wl):
 def setup_kv(torch, sd, wl):
     # accepted-path KV compaction after a tree walk of the tree workload: one
     # 128 KB row per token (32 layers x 8 KV heads x 128 x (K, V) x bf16)
-    case = wl.gen_config4(device="cuda")
+    case = wl.gen_tree(device="cuda")
     tree = sd.build_tree(case.marginals, case.N)
     walk = sd.verify_tree(case.target_for_depths(tree["depth"], tree["n_nodes"]), tree)
     B, N, row_bytes = case.B, case.N, 32 * 8 * 128 * 2 * 2
@@ -310,7 +310,7 @@ def setup_rerank(torch, sd, wl):
 
 
 def setup_chain1(torch, sd, wl):
-    case = wl.gen_config1(device="cuda")
+    case = wl.gen_chain_small(device="cuda")
     ws = torch.empty(sd.workspace_bytes(sd.OP_CHAIN, 1, 4, 1000), dtype=torch.uint8, device="cuda")
 
     def step(ev=None):

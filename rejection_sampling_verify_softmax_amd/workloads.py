@@ -24,20 +24,20 @@ an fp64 consumer see exactly the same value in [0, 1).
 
 Workload recipes (sigma is a standard deviation throughout):
 
-1. chain, B=1, K=4, V=1000, fp32: draft base D ~ N(0, 2) with K+1 rows; draft
-   rows are D[0..K-1]; target rows are D + N(0, 0.5); T = 1.
-2. greedy chain, B=64, K=3, V=128256, bf16 target ~ N(0, 3) with K+1 rows;
-   y_i is the target argmax (lowest id) with probability 0.7, otherwise a
-   uniform id.
-3. chain, B=256, K=5, V=151936, bf16 target N(0, 3) plus, per row, 20 distinct
-   uniformly chosen ids boosted by 12/r (r = 1..20) before rounding; draft rows
-   are bf16(target + N(0, 1)); T = 0.7, top-k 50 on both.
-4. tree, B=32, K=16, V=32000, N=64: Z ~ N(0, 2.5) per (sequence, depth);
-   marginals are softmax(Z) in fp32; the target row of a node at depth d < K is
-   bf16(Z[d] + N(0, 1)), and a node at depth K gets fresh N(0, 2.5).
-5. adaptive chain, B=512, K_max=8, V=128256: confidences c ~ Beta(5, 2) (the
-   5th smallest of 6 uniforms); draft base D ~ N(0, 2) with K_max+1 rows;
-   target = bf16(D + N(0, 0.7)); draft rows bf16(D); T = 1.
+* gen_chain_small -- chain, B=1, K=4, V=1000, fp32: draft base D ~ N(0, 2) with K+1 rows; draft
+  rows are D[0..K-1]; target rows are D + N(0, 0.5); T = 1.
+* gen_greedy_chain -- greedy chain, B=64, K=3, V=128256, bf16 target ~ N(0, 3) with K+1 rows;
+  y_i is the target argmax (lowest id) with probability 0.7, otherwise a
+  uniform id.
+* gen_topk_chain -- chain, B=256, K=5, V=151936, bf16 target N(0, 3) plus, per row, 20 distinct
+  uniformly chosen ids boosted by 12/r (r = 1..20) before rounding; draft rows
+  are bf16(target + N(0, 1)); T = 0.7, top-k 50 on both.
+* gen_tree -- tree, B=32, K=16, V=32000, N=64: Z ~ N(0, 2.5) per (sequence, depth);
+  marginals are softmax(Z) in fp32; the target row of a node at depth d < K is
+  bf16(Z[d] + N(0, 1)), and a node at depth K gets fresh N(0, 2.5).
+* gen_adaptive_chain -- adaptive chain, B=512, K_max=8, V=128256: confidences c ~ Beta(5, 2) (the
+  5th smallest of 6 uniforms); draft base D ~ N(0, 2) with K_max+1 rows;
+  target = bf16(D + N(0, 0.7)); draft rows bf16(D); T = 1.
 """
 from __future__ import annotations
 
@@ -236,7 +236,7 @@ class AdaptiveCase:
 def gen_base_noise_chain(seed: int, B: int, K: int, V: int, *, base_sigma: float,
                          noise_sigma: float, temperature: float, dtype: str,
                          top_k: int = 0, device="cpu", name: str = "") -> ChainCase:
-    """Workloads 1 and 5 recipe: D ~ N(0, base_sigma) with K+1 rows per sequence,
+    """The small and the adaptive chains' recipe: D ~ N(0, base_sigma) with K+1 rows per sequence,
     draft rows D[0..K-1], target rows D + N(0, noise_sigma), y ~ drafter."""
     gb, gn = _gen(seed, "base", device), _gen(seed, "noise", device)
     gs, gu = _gen(seed, "draft_sample", device), _gen(seed, "uniform", device)
@@ -253,13 +253,13 @@ def gen_base_noise_chain(seed: int, B: int, K: int, V: int, *, base_sigma: float
                      name=name)
 
 
-def gen_config1(device="cpu", seed: int = 1001, B: int = 1, K: int = 4, V: int = 1000) -> ChainCase:
+def gen_chain_small(device="cpu", seed: int = 1001, B: int = 1, K: int = 4, V: int = 1000) -> ChainCase:
     return gen_base_noise_chain(seed, B, K, V, base_sigma=2.0, noise_sigma=0.5,
                                 temperature=1.0, dtype="f32", device=device,
                                 name=f"chain-f32-B{B}-K{K}-V{V}")
 
 
-def gen_config2(device="cpu", seed: int = 1002, B: int = 64, K: int = 3, V: int = 128256) -> GreedyCase:
+def gen_greedy_chain(device="cpu", seed: int = 1002, B: int = 64, K: int = 3, V: int = 128256) -> GreedyCase:
     gb, gm, gs = _gen(seed, "base", device), _gen(seed, "accept_mix", device), _gen(seed, "draft_sample", device)
     tgt = (torch.randn(B, K + 1, V, generator=gb, device=device) * 3.0).to(torch.bfloat16)
     amax = first_argmax(tgt[:, :K].reshape(B * K, V))
@@ -270,7 +270,7 @@ def gen_config2(device="cpu", seed: int = 1002, B: int = 64, K: int = 3, V: int 
                       name=f"greedy-bf16-B{B}-K{K}-V{V}")
 
 
-def gen_config3(device="cpu", seed: int = 1003, B: int = 256, K: int = 5, V: int = 151936,
+def gen_topk_chain(device="cpu", seed: int = 1003, B: int = 256, K: int = 5, V: int = 151936,
                 top_k: int = 50, n_boost: int = 20, temperature: float = 0.7) -> ChainCase:
     gb, gn = _gen(seed, "base", device), _gen(seed, "noise", device)
     gx, gs, gu = _gen(seed, "boost", device), _gen(seed, "draft_sample", device), _gen(seed, "uniform", device)
@@ -297,7 +297,7 @@ def gen_config3(device="cpu", seed: int = 1003, B: int = 256, K: int = 5, V: int
                      name=f"chain-topk{top_k}-bf16-B{B}-K{K}-V{V}")
 
 
-def gen_config4(device="cpu", seed: int = 1004, B: int = 32, K: int = 16, V: int = 32000,
+def gen_tree(device="cpu", seed: int = 1004, B: int = 32, K: int = 16, V: int = 32000,
                 N: int = 64, sigma: float = 2.5) -> TreeCase:
     gb = _gen(seed, "base", device)
     Z = torch.randn(B, K, V, generator=gb, device=device) * sigma
@@ -306,7 +306,7 @@ def gen_config4(device="cpu", seed: int = 1004, B: int = 32, K: int = 16, V: int
                     name=f"tree-B{B}-K{K}-V{V}-N{N}")
 
 
-def gen_config5(device="cpu", seed: int = 1005, B: int = 512, K: int = 8, V: int = 128256,
+def gen_adaptive_chain(device="cpu", seed: int = 1005, B: int = 512, K: int = 8, V: int = 128256,
                 cost: float = 0.15) -> AdaptiveCase:
     gc = _gen(seed, "conf", device)
     six = torch.rand(B, K, 6, generator=gc, device=device)

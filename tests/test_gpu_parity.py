@@ -35,9 +35,9 @@ def run_chain(case, probs=True, **kw):
 # stochastic chain, full vocabulary
 # --------------------------------------------------------------------------
 
-def test_config1_chain_f32():
-    _say("config 1: B=1 K=4 V=1000 fp32")
-    case = wl.gen_config1(device="cuda")
+def test_chain_B1_K4_V1000_f32():
+    _say("chain: B=1 K=4 V=1000 fp32")
+    case = wl.gen_chain_small(device="cuda")
     out = run_chain(case)
     info = compare_chain(out, oracle_chain(case))
     _say(f"  {info}")
@@ -261,9 +261,9 @@ def _greedy_ref(case):
     return oracle.verify_greedy(h["target"], h["tokens"], h["cu"], case.B, case.K_max, case.V)
 
 
-def test_config2_greedy_full():
-    _say("config 2: greedy B=64 K=3 V=128256 bf16 (all sequences)")
-    case = wl.gen_config2(device="cuda")
+def test_greedy_B64_K3_V128256_full():
+    _say("greedy chain: B=64 K=3 V=128256 bf16 (all sequences)")
+    case = wl.gen_greedy_chain(device="cuda")
     out = sd.verify_greedy(case.target, case.tokens, K_max=case.K_max, B=case.B)
     ref = _greedy_ref(case)
     np.testing.assert_array_equal(out["accepted_len"].cpu().numpy(), ref["A"])
@@ -300,7 +300,7 @@ def test_greedy_ties_and_nan():
 @pytest.mark.parametrize("top_k,V", [(50, 3000), (1, 2000), (7, 151), (256, 40000), (50, 999)])
 def test_topk_small_all_sequences(top_k, V):
     _say(f"top-k {top_k} V={V}")
-    case = wl.gen_config3(device="cuda", seed=77 + top_k, B=12, K=4, V=V, top_k=top_k)
+    case = wl.gen_topk_chain(device="cuda", seed=77 + top_k, B=12, K=4, V=V, top_k=top_k)
     info = compare_chain(run_chain(case), oracle_chain(case))
     _say(f"  {info}")
 
@@ -310,7 +310,7 @@ def test_topk_phased_all_sequences(top_k):
     # 64 x 6 x 50000 >= 2^24 logits: without probabilities, verified in phases
     B, K, V = 64, 5, 50000
     assert B * (K + 1) * V >= 1 << 24
-    case = wl.gen_config3(device="cuda", seed=91 + top_k, B=B, K=K, V=V, top_k=top_k)
+    case = wl.gen_topk_chain(device="cuda", seed=91 + top_k, B=B, K=K, V=V, top_k=top_k)
     one = run_chain(case)
     ph = run_chain(case, probs=False)
     for key in ("accepted_len", "next_token", "status", "resid"):
@@ -371,9 +371,9 @@ def test_topk_structured_rows(layout):
     _say(f"  {info}")
 
 
-def test_config3_topk_full_sampled():
-    _say("config 3: B=256 K=5 V=151936 bf16 T=0.7 top-k 50 (sampled)")
-    case = wl.gen_config3(device="cuda")
+def test_topk_chain_B256_K5_V151936_sampled():
+    _say("top-k chain: B=256 K=5 V=151936 bf16 T=0.7 top-k 50 (sampled)")
+    case = wl.gen_topk_chain(device="cuda")
     out = run_chain(case)
     seqs = sample_seqs(case.B, 40, seed=3)
     info = compare_chain(out, oracle_chain(case, seqs))
@@ -399,7 +399,7 @@ def _tree_compare(out, ref):
 @pytest.mark.parametrize("B,K,V,N", [(4, 3, 5, 20), (6, 16, 700, 64), (3, 2, 3, 64), (5, 16, 31, 64),
                                      (2, 1, 1000, 10)])
 def test_tree_build_small(B, K, V, N):
-    case = wl.gen_config4(device="cuda", seed=5 + V, B=B, K=K, V=V, N=N, sigma=1.5)
+    case = wl.gen_tree(device="cuda", seed=5 + V, B=B, K=K, V=V, N=N, sigma=1.5)
     out = sd.build_tree(case.marginals, N)
     ref = oracle.build_tree(wl.to_host_f32(case.marginals), B, K, V, N)
     _tree_compare(out, ref)
@@ -410,7 +410,7 @@ def test_tree_build_small(B, K, V, N):
 @pytest.mark.parametrize("sigma", [4.0, 8.0])
 def test_tree_build_deep(sigma):
     B, K, V, N = 16, 16, 2000, 64
-    case = wl.gen_config4(device="cuda", seed=17 + int(sigma), B=B, K=K, V=V, N=N, sigma=sigma)
+    case = wl.gen_tree(device="cuda", seed=17 + int(sigma), B=B, K=K, V=V, N=N, sigma=sigma)
     out = sd.build_tree(case.marginals, N)
     ref = oracle.build_tree(wl.to_host_f32(case.marginals), B, K, V, N)
     _tree_compare(out, ref)
@@ -448,7 +448,7 @@ def test_tree_build_ties():
 @pytest.mark.parametrize("V", [32768, 32767, 32769, 40000])
 def test_tree_build_row_length_paths(V):
     B, K, N = 3, 4, 64
-    case = wl.gen_config4(device="cuda", seed=9 + V, B=B, K=K, V=V, N=N, sigma=2.5)
+    case = wl.gen_tree(device="cuda", seed=9 + V, B=B, K=K, V=V, N=N, sigma=2.5)
     out = sd.build_tree(case.marginals, N)
     ref = oracle.build_tree(wl.to_host_f32(case.marginals), B, K, V, N)
     _tree_compare(out, ref)
@@ -468,9 +468,9 @@ def test_tree_build_mass_ties():
     _tree_compare(out, ref)
 
 
-def test_config4_tree_full():
-    _say("config 4: tree B=32 K=16 V=32000 N=64")
-    case = wl.gen_config4(device="cuda")
+def test_tree_B32_K16_V32000_N64_full():
+    _say("tree: B=32 K=16 V=32000 N=64")
+    case = wl.gen_tree(device="cuda")
     tree = sd.build_tree(case.marginals, case.N)
     ref = oracle.build_tree(wl.to_host_f32(case.marginals), case.B, case.K, case.V, case.N)
     _tree_compare(tree, ref)
@@ -490,7 +490,7 @@ def test_compact_kv_matches_oracle(row_bytes):
     # chains where each destination is the previous move's source, full-depth
     # and empty paths, and a region past the buffer (left alone)
     g = torch.Generator(device="cuda").manual_seed(17)
-    case = wl.gen_config4(device="cuda", seed=23, B=6, K=16, V=3000, N=64, sigma=1.5)
+    case = wl.gen_tree(device="cuda", seed=23, B=6, K=16, V=3000, N=64, sigma=1.5)
     tree = sd.build_tree(case.marginals, case.N)
     walk = sd.verify_tree(case.target_for_depths(tree["depth"], tree["n_nodes"]), tree)
     B, N = 12, 64
@@ -605,7 +605,7 @@ def _sampled_walk_check(tree, target, T, u, top_k=0):
 def test_tree_walk_sampled_matches_oracle(dtype, V, T):
     B, K, N = 24, 16, 64
     _say(f"sampled walk {dtype} V={V} T={T}")
-    case = wl.gen_config4(device="cuda", seed=31 + V, B=B, K=K, V=V, N=N)
+    case = wl.gen_tree(device="cuda", seed=31 + V, B=B, K=K, V=V, N=N)
     tree = sd.build_tree(case.marginals, N)
     target = case.target_for_depths(tree["depth"], tree["n_nodes"])
     if dtype == "f32":
@@ -623,7 +623,7 @@ def test_tree_walk_sampled_matches_oracle(dtype, V, T):
 def test_tree_walk_sampled_topk_matches_oracle(dtype, V, T, top_k):
     B, K, N = 24, 16, 64
     _say(f"sampled walk top-k {top_k} {dtype} V={V} T={T}")
-    case = wl.gen_config4(device="cuda", seed=37 + V, B=B, K=K, V=V, N=N)
+    case = wl.gen_tree(device="cuda", seed=37 + V, B=B, K=K, V=V, N=N)
     tree = sd.build_tree(case.marginals, N)
     target = case.target_for_depths(tree["depth"], tree["n_nodes"])
     if dtype == "f32":
@@ -657,7 +657,7 @@ def test_tree_walk_sampled_topk_ties_and_nonfinite():
 
 
 def test_tree_walk_sampled_T0_is_the_argmax_walk():
-    case = wl.gen_config4(device="cuda", seed=77, B=16, K=16, V=32000, N=64)
+    case = wl.gen_tree(device="cuda", seed=77, B=16, K=16, V=32000, N=64)
     tree = sd.build_tree(case.marginals, 64)
     target = case.target_for_depths(tree["depth"], tree["n_nodes"])
     for tgt in (target, target.float()):
@@ -667,9 +667,9 @@ def test_tree_walk_sampled_T0_is_the_argmax_walk():
             assert torch.equal(out[k], ref[k]), k
 
 
-def test_config4_tree_sampled_full():
-    _say("config 4 shape, sampled walk: B=32 K=16 V=32000 N=64 T=1")
-    case = wl.gen_config4(device="cuda")
+def test_tree_sampled_walk_B32_V32000_full():
+    _say("sampled tree walk: B=32 K=16 V=32000 N=64 T=1")
+    case = wl.gen_tree(device="cuda")
     tree = sd.build_tree(case.marginals, case.N)
     target = case.target_for_depths(tree["depth"], tree["n_nodes"])
     u = wl.grid_uniforms((case.B, case.N), torch.Generator(device="cuda").manual_seed(1004), "cuda")
@@ -760,9 +760,9 @@ def test_select_len_table_parity():
 
 def _padded_case(mode, seed):
     if mode == "topk":
-        return wl.gen_config3(device="cuda", seed=seed, B=48, K=6, V=30000, top_k=20)
+        return wl.gen_topk_chain(device="cuda", seed=seed, B=48, K=6, V=30000, top_k=20)
     if mode == "greedy":
-        g = wl.gen_config2(device="cuda", seed=seed, B=48, K=6, V=30000)
+        g = wl.gen_greedy_chain(device="cuda", seed=seed, B=48, K=6, V=30000)
         return wl.ChainCase(B=g.B, K_max=g.K_max, V=g.V, temperature=0.0, top_k=0, target=g.target,
                             draft=None, tokens=g.tokens, uniforms=None)
     return wl.gen_base_noise_chain(seed, B=48, K=6, V=30000, base_sigma=2.0, noise_sigma=0.7,
@@ -820,9 +820,9 @@ def test_capped_commits_what_compact_commits(mode):
     _say(f"  margin cases {int((~ok).sum())}, mean committed {out['accepted_len'].float().mean().item():.2f}")
 
 
-def test_config5_adaptive_full_sampled():
-    _say("config 5: select_len + packed chain B=512 K_max=8 V=128256 bf16 (sampled)")
-    case = wl.gen_config5(device="cuda")
+def test_adaptive_chain_B512_K8_V128256_sampled():
+    _say("adaptive chain: select_len + packed chain B=512 K_max=8 V=128256 bf16 (sampled)")
+    case = wl.gen_adaptive_chain(device="cuda")
     sel = sd.select_len(case.conf, case.cost)
     ref_sel = oracle.select_len(case.conf.cpu().numpy(), case.B, case.K_max, case.cost)
     np.testing.assert_array_equal(sel["k"].cpu().numpy(), ref_sel["k"])
