@@ -1140,8 +1140,9 @@ __global__ __launch_bounds__(kBuildThreads) void k_tree_build(
 //     over the 8 waves (t) is reached by at least 64 > W tokens: every token
 //     of the top W has a value >= t.
 //  3. The tokens with a value >= t (about a hundred on a row of
-//     probabilities) go to LDS as keys by a block scan; each takes its rank
-//     by counting the larger keys, and the first W are written in rank order.
+//     probabilities) go to LDS as keys in one pass, placed by an LDS counter;
+//     each takes its rank by counting the larger keys, and the first W are
+//     written in rank order.
 //  4. Should more than kShortCap tokens reach t (mass ties), a key bound is
 //     found by bisection over the key space, reached by at least W and at
 //     most kShortCap keys (keys are distinct, so such a bound exists).
@@ -1162,6 +1163,7 @@ __global__ __launch_bounds__(kShortThreads) void k_topk_short(const typename E::
     __shared__ unsigned long long cand[kShortCap];
     __shared__ uint32_t wkey[kShortWaves];
     __shared__ int wsum[kShortWaves];
+    __shared__ int s_total;
     constexpr int EV = E::kVec;
     const int task = blockIdx.x;
     const typename E::raw* row = rows + (int64_t)task * V;
@@ -1197,18 +1199,6 @@ __global__ __launch_bounds__(kShortThreads) void k_topk_short(const typename E::
         *excl = before;
         return tot;
     };
-    // number of this thread's tokens with a value >= t (NaN never)
-    auto count_ge = [&](float t) __attribute__((always_inline)) -> int {
-        fresh();
-        int c = 0;
-#pragma unroll
-        for (int i = 0; i < kShortVecs; ++i) {
-#pragma unroll
-            for (int e = 0; e < EV; ++e) c += raw_elem<E>(v[i], e) >= t ? 1 : 0;
-            __builtin_amdgcn_sched_barrier(0);
-        }
-        return c;
-    };
     // number of this thread's keys >= k (k > 0), for the bisection; it reads
     // the row again, one vector at a time (the rare path keeps no second copy
     // of the row in registers)
@@ -1241,19 +1231,35 @@ __global__ __launch_bounds__(kShortThreads) void k_topk_short(const typename E::
         if (mine == rth) mine = 0u;
     }
     if (lane == 0) wkey[w] = rth;
+    if (tid == 0) s_total = 0;
     __syncthreads();
     uint32_t tb = wkey[0];
 #pragma unroll
     for (int i = 1; i < kShortWaves; ++i) tb = min(tb, wkey[i]);
     // a wave without kShortRth kept maxima: every kept token competes
     const float t = tb == 0u ? -INFINITY : from_ordered(tb);
-    int c = count_ge(t);
-    int off = 0;
-    int total = block_count(c, &off);
-    // candidate test: value >= t, or (after a bisection) key >= kb
-    bool by_key = false;
-    unsigned long long kb = 0ull;
+    // 3. the candidates (value >= t) to LDS in one pass, placed by an LDS
+    // counter (their order does not matter: ranks come from the keys); the
+    // count tells whether they fit
+    {
+        fresh();
+#pragma unroll
+        for (int i = 0; i < kShortVecs; ++i) {
+#pragma unroll
+            for (int e = 0; e < EV; ++e) {
+                const float x = raw_elem<E>(v[i], e);
+                if (x >= t) {
+                    const int at = atomicAdd(&s_total, 1);
+                    if (at < kShortCap) cand[at] = make_key(x, jb + i * kShortThreads * EV + e);
+                }
+            }
+            __builtin_amdgcn_sched_barrier(0);
+        }
+    }
+    __syncthreads();
+    int total = s_total;
     if (total > kShortCap) {
+        unsigned long long kb = 0ull;
         // 4. mass ties: bisection over keys for a bound reached by W ..
         // kShortCap keys; lo is reached by more than kShortCap keys, hi by none
         // (the key of t's value at token 0 is not below any key of value >= t)
@@ -1275,12 +1281,10 @@ __global__ __launch_bounds__(kShortThreads) void k_topk_short(const typename E::
                 hi = mid;
             }
         }
-        by_key = true;
-        c = count_key_ge(kb);
-        total = block_count(c, &off);
-    }
-    // 3. the candidates to LDS at their scanned offsets, then ranks by counting
-    {
+        // the candidates again, by key (between W and kShortCap of them)
+        __syncthreads();
+        if (tid == 0) s_total = 0;
+        __syncthreads();
         fresh();
 #pragma unroll
         for (int i = 0; i < kShortVecs; ++i) {
@@ -1289,13 +1293,17 @@ __global__ __launch_bounds__(kShortThreads) void k_topk_short(const typename E::
                 const float x = raw_elem<E>(v[i], e);
                 if (x >= t) {
                     const unsigned long long k = make_key(x, jb + i * kShortThreads * EV + e);
-                    if ((!by_key || k >= kb) && off < kShortCap) cand[off++] = k;
+                    if (k >= kb) {
+                        const int at = atomicAdd(&s_total, 1);
+                        if (at < kShortCap) cand[at] = k;
+                    }
                 }
             }
             __builtin_amdgcn_sched_barrier(0);
         }
+        __syncthreads();
+        total = s_total;
     }
-    __syncthreads();
     total = total < kShortCap ? total : kShortCap;
     TopEntry* L = lists + (int64_t)task * W;
     auto put = [&](unsigned long long k, int rank) __attribute__((always_inline)) {
