@@ -1107,7 +1107,7 @@ __global__ __launch_bounds__(kBuildThreads) void k_tree_build(
         const int fS = hasS ? ps + ((hasC && !s_first) ? 1 : 0) : -1;
         // lane j takes C, S, or the entry that lands on j: from lane j+1 when
         // neither was placed before j, lane j after one, lane j-1 after both
-        const int nb = ((fC >= 0) & (fC < lane) ? 1 : 0) + ((fS >= 0) & (fS < lane) ? 1 : 0);
+        const int nb = (((fC >= 0) & (fC < lane)) ? 1 : 0) + (((fS >= 0) & (fS < lane)) ? 1 : 0);
         const bool tc = lane == fC, ts = lane == fS;
         const float gQ = __builtin_bit_cast(float, shift_pick(__builtin_bit_cast(uint32_t, f.Q), nb));
         const int gm = (int)shift_pick((uint32_t)f.meta, nb);
