@@ -180,8 +180,11 @@ def setup_tree(torch, sd, wl):
     B, K, V, N = case.B, case.K, case.V, case.N
     tree = sd.build_tree(case.marginals, N)
     target = case.target_for_depths(tree["depth"], tree["n_nodes"])
-    margs = [case.marginals] + [case.marginals.clone() for _ in range(2)]
-    targets = [target] + [target.clone() for _ in range(2)]
+    # 8 copies: 8 x 65.5 MB of marginals pass between two uses of one copy, more
+    # than the 256 MB last-level cache, so neither the marginals nor the few
+    # target rows a walk visits are still cached when their copy comes round
+    margs = [case.marginals] + [case.marginals.clone() for _ in range(7)]
+    targets = [target] + [target.clone() for _ in range(7)]
     st = {"i": 0}
     ws_b = torch.empty(sd.workspace_bytes(sd.OP_BUILD_TREE, B, K, V, 0, N), dtype=torch.uint8, device="cuda")
     walk_out = sd.verify_tree(target, tree)
@@ -189,7 +192,7 @@ def setup_tree(torch, sd, wl):
     rows_read = int(A.sum()) + B              # the walk reads the rows on its path only
 
     def step(ev=None):
-        i = st["i"] % 3
+        i = st["i"] % len(margs)
         st["i"] += 1
         if ev is not None:
             sd.time_next_stream_pass(*ev)
@@ -213,8 +216,11 @@ def setup_tree_sampled(torch, sd, wl):
     tree = sd.build_tree(case.marginals, N)
     target = case.target_for_depths(tree["depth"], tree["n_nodes"])
     u = wl.grid_uniforms((B, N), torch.Generator(device="cuda").manual_seed(1004), "cuda")
-    margs = [case.marginals] + [case.marginals.clone() for _ in range(2)]
-    targets = [target] + [target.clone() for _ in range(2)]
+    # 8 copies: 8 x 65.5 MB of marginals pass between two uses of one copy, more
+    # than the 256 MB last-level cache, so neither the marginals nor the few
+    # target rows a walk visits are still cached when their copy comes round
+    margs = [case.marginals] + [case.marginals.clone() for _ in range(7)]
+    targets = [target] + [target.clone() for _ in range(7)]
     st = {"i": 0}
     ws_b = torch.empty(sd.workspace_bytes(sd.OP_BUILD_TREE, B, K, V, 0, N), dtype=torch.uint8, device="cuda")
     walk_out = sd.verify_tree_sampled(target, tree, u, 1.0)
@@ -222,7 +228,7 @@ def setup_tree_sampled(torch, sd, wl):
     rows_read = int(A.sum()) + B
 
     def step(ev=None):
-        i = st["i"] % 3
+        i = st["i"] % len(margs)
         st["i"] += 1
         sd.build_tree(margs[i], N, workspace=ws_b)
         if ev is not None:
