@@ -563,6 +563,32 @@ def test_rerank_tree_matches_oracle(M, layers, topk, N):
     np.testing.assert_array_equal(out["anc_mask"].cpu().numpy().view(np.uint64), ref["anc_mask"])
 
 
+def test_rerank_tree_then_walks():
+    """The re-ranked tree has the built tree's layout, so both walks take it:
+    target rows that favour each node's children, argmax and sampled walks
+    against the oracle on the same tree."""
+    rng = np.random.default_rng(7)
+    B, M, N, V = 8, 400, 64, 3000
+    par, tok, prob, n = _eagle2_candidates(rng, B, M, 6, 8, V=V)
+    t = lambda a: torch.as_tensor(a, device="cuda")
+    tree = sd.rerank_tree(t(par), t(tok), t(prob), t(n), N)
+    g = torch.Generator(device="cuda").manual_seed(11)
+    rows = torch.randn(B, N, V, generator=g, device="cuda")
+    tk, pr, nn = tree["token"].cpu().numpy(), tree["parent"].cpu().numpy(), tree["n_nodes"].cpu().numpy()
+    for b in range(B):
+        for c in range(1, int(nn[b])):
+            rows[b, int(pr[b, c]), int(tk[b, c])] += 4.0      # children's tokens likely under the target
+    rows = rows.to(torch.bfloat16)
+    w = sd.verify_tree(rows, tree)
+    ref = oracle.verify_tree(wl.to_host_f32(rows), tk, pr, nn, B, N, V)
+    np.testing.assert_array_equal(w["accepted_len"].cpu().numpy(), ref["A"])
+    np.testing.assert_array_equal(w["path"].cpu().numpy(), ref["path"])
+    np.testing.assert_array_equal(w["next_token"].cpu().numpy(), ref["next"])
+    u = wl.grid_uniforms((B, N), torch.Generator(device="cuda").manual_seed(12), "cuda")
+    _, sref = _sampled_walk_check(tree, rows, 1.0, u)
+    assert ref["A"].max() >= 2 and sref["A"].max() >= 1
+
+
 def test_tree_walk_planted():
     V, N, B = 12, 6, 2
     tok = torch.tensor([[-1, 4, 7, 2, 9, -1]] * B, dtype=torch.int32, device="cuda")
