@@ -503,6 +503,7 @@ def main():
             "unit": "GB/s",
             "frac": achieved / PEAK_HBM_GBPS,
             "traffic": traffic,
+            "traffic_GBps": (traffic / (kernel_ms_avg * 1e-3) / 1e9) if traffic else None,
             "kernel": meta["kernel"],
             "kernel_us": kernel_ms_avg * 1e3,
             "launches_timed": len(kernel_ms),
