@@ -198,3 +198,18 @@ def test_binding_fails_loudly_without_gpu():
     x = torch.zeros(8, 16)
     with pytest.raises(ValueError):
         sd.verify_chain(x, x, torch.zeros(4, dtype=torch.int32), torch.zeros(8), 1.0, K_max=1)
+
+
+def test_tree_binding_checks_inputs_without_gpu():
+    import torch
+    import rejection_sampling_verify_softmax_amd as sd
+    if torch.cuda.is_available():
+        pytest.skip("GPU present")
+    rows = torch.zeros(2, 4, 16)
+    tree = {"token": torch.zeros(2, 4, dtype=torch.int32), "parent": torch.zeros(2, 4, dtype=torch.int32),
+            "n_nodes": torch.zeros(2, dtype=torch.int32)}
+    with pytest.raises(ValueError):                    # host tensors
+        sd.verify_tree_sampled(rows, tree, torch.zeros(2, 4), 1.0)
+    with pytest.raises(ValueError):
+        sd.verify_tree(rows, tree)
+
