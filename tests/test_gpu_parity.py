@@ -243,6 +243,27 @@ def test_maximum_vocabulary(V):
     del host
 
 
+# Extreme temperatures: at T = 0.05 the exponent range per row is in the
+# hundreds of binary orders (most weights underflow), at T = 8 the weights are
+# nearly flat; both through the full-vocabulary chain (one pass and phases),
+# the top-k chain and the sampled tree walk.
+@pytest.mark.parametrize("T", [0.05, 8.0])
+def test_extreme_temperatures(T):
+    _say(f"extreme temperature T={T}")
+    case = wl.gen_base_noise_chain(29, B=24, K=5, V=40000, base_sigma=2.0, noise_sigma=0.6,
+                                   temperature=T, dtype="bf16", device="cuda")
+    info = compare_chain(run_chain(case), oracle_chain(case))
+    _say(f"  chain {info}")
+    tk = wl.gen_topk_chain(device="cuda", seed=31, B=16, K=4, V=30000, top_k=50, temperature=T)
+    info = compare_chain(run_chain(tk), oracle_chain(tk))
+    _say(f"  top-k {info}")
+    tr = wl.gen_tree(device="cuda", seed=33, B=16, K=16, V=32000, N=64)
+    tree = sd.build_tree(tr.marginals, 64)
+    target = tr.target_for_depths(tree["depth"], tree["n_nodes"])
+    u = wl.grid_uniforms((16, 64), torch.Generator(device="cuda").manual_seed(34), "cuda")
+    _sampled_walk_check(tree, target, T, u)
+
+
 def test_chain_run_twice_bit_identical():
     case = wl.gen_base_noise_chain(9, B=16, K=6, V=50000, base_sigma=2.0, noise_sigma=0.7,
                                    temperature=1.0, dtype="bf16", device="cuda")
