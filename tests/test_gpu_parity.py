@@ -264,6 +264,59 @@ def test_extreme_temperatures(T):
     _sampled_walk_check(tree, target, T, u)
 
 
+# The library only enqueues kernels on the caller's stream (no allocation, no
+# synchronisation, no memset), so a step can be captured in a HIP graph. The
+# graph is replayed several times, with eager work and synchronisations in
+# between, and every replay must equal the eager result.
+def test_graph_capture_replays_equal_eager():
+    case = wl.gen_adaptive_chain(device="cuda", seed=41, B=64, K=6, V=30000)
+    sel0 = sd.select_len(case.conf, case.cost)
+    torch.cuda.synchronize()
+    packed = case.packed(sel0["k"])
+    B, K, V = case.B, case.K_max, case.V
+    ws = torch.empty(sd.workspace_bytes(sd.OP_CHAIN, B, K, V), dtype=torch.uint8, device="cuda")
+    tr = wl.gen_tree(device="cuda", seed=42, B=8, K=16, V=20000, N=64)
+    ws_b = torch.empty(sd.workspace_bytes(sd.OP_BUILD_TREE, 8, 16, 20000, 0, 64), dtype=torch.uint8,
+                       device="cuda")
+    tree0 = sd.build_tree(tr.marginals, 64, workspace=ws_b)
+    target = tr.target_for_depths(tree0["depth"], tree0["n_nodes"])
+    u = wl.grid_uniforms((8, 64), torch.Generator(device="cuda").manual_seed(43), "cuda")
+
+    def step(o):
+        s = sd.select_len(case.conf, case.cost, out=o.get("sel"))
+        o["sel"] = s
+        o["chain"] = sd.verify_chain(packed.target, packed.draft, packed.tokens, packed.uniforms, 1.0,
+                                     cu=s["cu"], B=B, K_max=K, workspace=ws, out=o.get("chain"),
+                                     validate=False)
+        o["tree"] = sd.build_tree(tr.marginals, 64, workspace=ws_b)
+        o["walk"] = sd.verify_tree_sampled(target, o["tree"], u, 0.8, out=o.get("walk"))
+        return o
+
+    eager = step({})
+    torch.cuda.synchronize()
+    ref = {k: {kk: vv.clone() for kk, vv in v.items()} for k, v in eager.items()}
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        step(eager)                                  # warm-up on the capture stream
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        cap = step(eager)
+    for rep in range(4):
+        for v in cap.values():
+            for t in v.values():
+                t.fill_(-7)                           # eager work between replays
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        for k in ref:
+            for kk in ref[k]:
+                assert torch.equal(cap[k][kk], ref[k][kk]), (rep, k, kk)
+    del g
+
+
 def test_chain_run_twice_bit_identical():
     case = wl.gen_base_noise_chain(9, B=16, K=6, V=50000, base_sigma=2.0, noise_sigma=0.7,
                                    temperature=1.0, dtype="bf16", device="cuda")
