@@ -692,6 +692,33 @@ def test_sampled_walk_top1_is_the_argmax_walk():
         assert (out["path"] == ref["path"]).all()
 
 
+def test_sampled_walk_topk_follows_the_truncated_target():
+    """With top-k = 2 every pick follows the row's two largest probabilities,
+    renormalised; the other tokens are never committed."""
+    n = 200_000
+    rng = np.random.default_rng(61)
+    N, V = WALK_P.shape
+    rows = np.tile(logits_of(WALK_P)[None], (n, 1, 1))
+    u = grid_u(rng, (n, N))
+    out = oracle.verify_tree_sampled(rows, np.tile(WALK_TOKEN, (n, 1)), np.tile(WALK_PARENT, (n, 1)),
+                                     np.full(n, N, np.int32), u, n, N, V, 1.0, 2)
+    A, path = out["A"], out["path"]
+    first = np.where(A >= 1, WALK_TOKEN[np.maximum(path[:, 0], 0)], out["next"])
+    p0 = WALK_P[0].copy()
+    keep = np.argsort(-p0, kind="stable")[:2]
+    trunc = np.zeros_like(p0)
+    trunc[keep] = p0[keep] / p0[keep].sum()
+    assert _chi2_ok(np.bincount(first, minlength=V), trunc, n)
+    # given the walk reached node 1, the next pick follows node 1's truncated row
+    sel = (A >= 1) & (path[:, 0] == 1)
+    second = np.where(A[sel] >= 2, WALK_TOKEN[np.maximum(path[sel, 1], 0)], out["next"][sel])
+    p1 = WALK_P[1].copy()
+    keep1 = np.argsort(-p1, kind="stable")[:2]
+    t1 = np.zeros_like(p1)
+    t1[keep1] = p1[keep1] / p1[keep1].sum()
+    assert _chi2_ok(np.bincount(second, minlength=V), t1, int(sel.sum()))
+
+
 def test_sampled_walk_nonfinite_row_and_one_hot_rows():
     N, V = WALK_P.shape
     # one-hot target rows spell the path root -> 1 -> 3 -> 5, then token 2
