@@ -16,7 +16,8 @@ bounded sample of the same workload, and the parity of the timed step against
 that oracle run (verify lengths of every sequence, committed results of the
 sampled sequences; bit-exact outside the oracle's margin cases).
 
-Other workloads (--workload greedy|topk|tree|tree_sampled|chain1|kv|rerank) measure the other kernels
+Other workloads (--workload greedy|topk|tree|tree_sampled|tree_sampled_topk|chain1|kv|rerank)
+measure the other kernels
 for the design notes; their inputs are rotated across copies so that the
 working set exceeds the 256 MB last-level cache.
 """
@@ -42,12 +43,38 @@ def log(msg):
     print(msg, file=sys.stderr, flush=True)
 
 
+def _code_only(text: str) -> str:
+    """C++ source with comments removed and whitespace runs collapsed (string
+    and character literals kept), so that a comment edit keeps the digest."""
+    out, i, n = [], 0, len(text)
+    while i < n:
+        c = text[i]
+        if c in "\"'":
+            j = i + 1
+            while j < n and text[j] != c:
+                j += 2 if text[j] == "\\" else 1
+            out.append(text[i:j + 1])
+            i = j + 1
+        elif text.startswith("//", i):
+            j = text.find("\n", i)
+            i = n if j < 0 else j
+        elif text.startswith("/*", i):
+            j = text.find("*/", i + 2)
+            out.append(" ")
+            i = n if j < 0 else j + 2
+        else:
+            out.append(c)
+            i += 1
+    return " ".join("".join(out).split())
+
+
 def source_digest() -> str:
+    """Digest of the kernel sources' code (comments and layout ignored)."""
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "rejection_sampling_verify_softmax_amd", "csrc")
     for name in sorted(os.listdir(csrc)):
-        with open(os.path.join(csrc, name), "rb") as f:
-            h.update(name.encode() + b"\0" + f.read())
+        with open(os.path.join(csrc, name), encoding="utf-8") as f:
+            h.update(name.encode() + b"\0" + _code_only(f.read()).encode())
     return h.hexdigest()[:16]
 
 
@@ -244,6 +271,39 @@ def setup_tree_sampled(torch, sd, wl):
     return step, meta, None
 
 
+def setup_tree_sampled_topk(torch, sd, wl):
+    # the walk under a sampling target with top-k 50 (T = 1): at each visited
+    # node the workgroup takes the exact top-50 of that row on the fly; only
+    # the walk's rows are read. The tree itself is built once, outside the step
+    case = wl.gen_tree(device="cuda")
+    B, K, V, N = case.B, case.K, case.V, case.N
+    tree = sd.build_tree(case.marginals, N)
+    target = case.target_for_depths(tree["depth"], tree["n_nodes"])
+    # 8 copies (8 x 131 MB): the rows a walk visits are not still cached when
+    # their copy comes round
+    targets = [target] + [target.clone() for _ in range(7)]
+    u = wl.grid_uniforms((B, N), torch.Generator(device="cuda").manual_seed(1004), "cuda")
+    walk_out = sd.verify_tree_sampled(target, tree, u, 1.0, top_k=50)
+    A = walk_out["accepted_len"].cpu()
+    rows_read = int(A.sum()) + B
+    st = {"i": 0}
+
+    def step(ev=None):
+        i = st["i"] % len(targets)
+        st["i"] += 1
+        if ev is not None:
+            sd.time_next_stream_pass(*ev)
+        sd.verify_tree_sampled(targets[i], tree, u, 1.0, top_k=50, out=walk_out)
+
+    meta = {"workload": (f"DDTree walk under a sampling target with top-k 50 (T=1): B={B}, N={N}, "
+                         f"V={V} bf16 rows read on demand, the exact top-50 of each visited row"),
+            "global_batch": B, "V": V, "positions_per_step": B * (N - 1),
+            "kernel": "k_tree_walk_topk_rows", "kernel_bytes": rows_read * V * 2 + B * N * 12,
+            "step_bytes": rows_read * V * 2, "mean_A": float(A.float().mean()),
+            "rows_streamed": rows_read, "max_A": int(A.max())}
+    return step, meta, None
+
+
 def setup_kv(torch, sd, wl):
     # accepted-path KV compaction after a tree walk of the tree workload: one
     # 128 KB row per token (32 layers x 8 KV heads x 128 x (K, V) x bf16)
@@ -332,7 +392,8 @@ def setup_chain1(torch, sd, wl):
 
 
 WORKLOADS = {"adaptive": setup_adaptive, "greedy": setup_greedy, "topk": setup_topk,
-             "tree": setup_tree, "tree_sampled": setup_tree_sampled, "chain1": setup_chain1,
+             "tree": setup_tree, "tree_sampled": setup_tree_sampled,
+             "tree_sampled_topk": setup_tree_sampled_topk, "chain1": setup_chain1,
              "kv": setup_kv, "rerank": setup_rerank}
 
 
@@ -549,7 +610,7 @@ def main():
     for k in ("logits", "temperature", "mean_k"):
         if k in meta:
             result["config"][k] = meta[k]
-    for k in ("mean_A", "rows_streamed", "rows_in_windows"):
+    for k in ("mean_A", "max_A", "rows_streamed", "rows_in_windows"):
         if k in meta:
             result["step"][k] = meta[k]
     if cpu is not None and not args.no_cpu_baseline:

@@ -260,10 +260,11 @@ sd_status_t sd_verify_tree(const void* target_logits, sd_dtype_t dtype,
  *   seq_status   [B] int32 out or NULL: SD_SEQ_NONFINITE when a visited row is
  *                non-finite (no finite maximum, or a NaN in its sum); the walk
  *                stops there
- *   workspace    sd_workspace_bytes(SD_OP_VERIFY_TREE_SAMPLED, B, 0, V, top_k,
- *                N) bytes: none (NULL allowed) without truncation. Without
- *                truncation only the rows on the walk are read, one per step;
- *                with it every node's row is reduced to its kept list first.
+ *   workspace    unused (sd_workspace_bytes returns 0 for
+ *                SD_OP_VERIFY_TREE_SAMPLED; NULL is accepted)
+ *
+ * Only the rows on the walk are read, one per step; with truncation the step
+ * takes the exact top_k of its row on the fly.
  */
 sd_status_t sd_verify_tree_sampled(const void* target_logits, sd_dtype_t dtype,
                                    const int32_t* node_token, const int32_t* node_parent,

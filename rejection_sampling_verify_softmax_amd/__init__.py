@@ -368,7 +368,8 @@ def verify_tree_sampled(target: torch.Tensor, tree: dict, uniforms: Optional[tor
                         temperature: float, top_k: int = 0, out: Optional[dict] = None,
                         workspace: Optional[torch.Tensor] = None, stream=None) -> dict:
     """sd_verify_tree_sampled. target [B, N, V] (bf16 or fp32); tree from build_tree;
-    uniforms [B, N] float32 (None when temperature == 0); top_k 0 = no truncation."""
+    uniforms [B, N] float32 (None when temperature == 0); top_k 0 = no truncation.
+    The walk needs no workspace; the argument is accepted and ignored."""
     dev = target.device
     _check(target, "target", device=dev)
     dt = _dtype_code(target)
@@ -386,13 +387,11 @@ def verify_tree_sampled(target: torch.Tensor, tree: dict, uniforms: Optional[tor
     A = _get(o, "accepted_len", lambda: torch.empty(B, dtype=torch.int32, device=dev))
     nxt = _get(o, "next_token", lambda: torch.empty(B, dtype=torch.int32, device=dev))
     st = _get(o, "status", lambda: torch.empty(B, dtype=torch.int32, device=dev))
-    nbytes = workspace_bytes(OP_VERIFY_TREE_SAMPLED, B, 0, V, int(top_k), N)
-    ws = _workspace(nbytes, dev, workspace) if nbytes > 0 else None
     r = _load().sd_verify_tree_sampled(_ptr(target), dt, _ptr(tree["token"]), _ptr(tree["parent"]),
                                        _ptr(tree["n_nodes"]), _ptr(uniforms), B, N, V,
                                        ctypes.c_float(float(temperature)), int(top_k), _ptr(path),
-                                       _ptr(A), _ptr(nxt), _ptr(st), _ptr(ws),
-                                       ctypes.c_size_t(0 if ws is None else ws.numel()), _stream(stream))
+                                       _ptr(A), _ptr(nxt), _ptr(st), None, ctypes.c_size_t(0),
+                                       _stream(stream))
     _raise(r, "sd_verify_tree_sampled")
     return {"path": path, "accepted_len": A, "next_token": nxt, "status": st}
 

@@ -92,7 +92,7 @@ sd_status_t sd_workspace_bytes(sd_op_t op, int32_t B, int32_t K_max, int32_t V, 
             if (B < 1 || B > kMaxB || V < 1 || V > kMaxV || N < 2 || N > SD_MAX_TREE_N || top_k < 0 ||
                 top_k > SD_MAX_TOPK)
                 return SD_EINVAL;
-            *bytes = topk_on(top_k, V) ? sd::tree_walk_topk_ws_bytes(B, N, top_k) : 0;
+            *bytes = 0;   // both walks read their rows on demand and keep their state in LDS
             return SD_OK;
         case SD_OP_SELECT_LEN:
             if (B < 1 || B > kMaxB || K_max < 0 || K_max > SD_MAX_K) return SD_EINVAL;
@@ -248,15 +248,14 @@ sd_status_t sd_verify_tree_sampled(const void* target_logits, sd_dtype_t dtype,
     if (!target_logits || !node_token || !node_parent || !n_nodes || !path_nodes || !accepted_len ||
         !next_token || (temperature > 0.0f && !uniforms))
         return SD_EINVAL;
+    (void)workspace;
+    (void)workspace_bytes;
     const hipStream_t stream = static_cast<hipStream_t>(hip_stream);
-    if (temperature > 0.0f && topk_on(top_k, V)) {
-        if (!workspace) return SD_EINVAL;
-        if (workspace_bytes < sd::tree_walk_topk_ws_bytes(B, N, top_k)) return SD_EWORKSPACE;
+    if (temperature > 0.0f && topk_on(top_k, V))
         return from_hip(sd::launch_tree_walk_topk(target_logits, (int)dtype, node_token, node_parent,
                                                   n_nodes, uniforms, B, N, V, temperature, top_k,
                                                   path_nodes, accepted_len, next_token, seq_status,
-                                                  workspace, stream));
-    }
+                                                  stream));
     return from_hip(sd::launch_tree_walk_rows(target_logits, (int)dtype, node_token, node_parent,
                                               n_nodes, uniforms, B, N, V, temperature, path_nodes,
                                               accepted_len, next_token, seq_status, stream));

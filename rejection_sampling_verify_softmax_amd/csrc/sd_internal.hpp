@@ -111,12 +111,10 @@ hipError_t launch_tree_walk_rows(const void* target, int dtype, const int32_t* t
                                  int B, int N, int V, float temperature, int32_t* path,
                                  int32_t* accepted_len, int32_t* next_token, int32_t* seq_status,
                                  hipStream_t stream);
-size_t tree_walk_topk_ws_bytes(int B, int N, int top_k);
 hipError_t launch_tree_walk_topk(const void* target, int dtype, const int32_t* tok, const int32_t* par,
                                  const int32_t* n_nodes, const float* uniforms, int B, int N, int V,
                                  float temperature, int top_k, int32_t* path, int32_t* accepted_len,
-                                 int32_t* next_token, int32_t* seq_status, void* ws,
-                                 hipStream_t stream);
+                                 int32_t* next_token, int32_t* seq_status, hipStream_t stream);
 hipError_t launch_compact_kv(void* kv, int64_t row_bytes, int64_t n_rows, const int64_t* base,
                              const int32_t* path, const int32_t* accepted_len, int B, int N,
                              hipStream_t stream);

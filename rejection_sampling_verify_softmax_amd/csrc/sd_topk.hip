@@ -18,6 +18,10 @@
 // k_topk_short: rows of up to 32768 fp32 marginals (the tree's) are held in
 // the registers of one workgroup, which bounds the top W from its threads'
 // maxima and ranks the few tokens above the bound.
+//
+// k_tree_walk_topk_rows: the DDTree walk under a sampling target with top-k
+// truncation, one workgroup per sequence taking the exact top-k of each row
+// it visits (in registers when the row fits, else streamed as above).
 #include "sd_device.hpp"
 #include "sd_internal.hpp"
 
@@ -340,10 +344,30 @@ __device__ __forceinline__ int guess_rank(int topk, int sampled, int V) {
     return min(j, topk) - 1;
 }
 
-// One workgroup per row task: the exact top-k of the row in key order (value
-// desc, then lower id first), written as TopEntry; for the rows of a chain
-// also the row's softmax statistics over the kept set and p(y) of the
-// position's draft token (fp64).
+// LDS of one workgroup's exact top-k of one row.
+struct TopkSmem {
+    unsigned long long wbuf[kWavesPerBlock][kWaveCap];
+    int32_t qi[kWavesPerBlock][kQueue];
+    uint32_t smax[kWavesPerBlock][kWave];
+    uint32_t t_guess_b, t_safe_b;
+    int wcnt[kWavesPerBlock];
+    int wseen[kWavesPerBlock];
+    double red[kWavesPerBlock];
+};
+
+// What row_topk leaves besides the list: the kept count and, with stats, the
+// fp64 softmax statistics over the kept set at temperature T (m = max x/T,
+// S = sum exp(x/T - m), ey = the term of token y, 0 if y is not kept).
+struct KeptStats {
+    int kept;
+    double m;
+    double S;
+    double ey;
+};
+
+// The exact top-k of one row by one workgroup, in key order (value desc, then
+// lower id first), written as TopEntry to L[0 .. kept) (global memory or LDS);
+// uniform results in every thread.
 //  1. Every thread holds kTopkSample vectors of the row's start and takes
 //     their maximum. Ranked among the 256 maxima (distinct tokens), the
 //     topk-th is a guaranteed bound (at least topk tokens reach it) and a
@@ -359,36 +383,9 @@ __device__ __forceinline__ int guess_rank(int topk, int sampled, int V) {
 //  4. The waves' sorted lists are merged by rank (binary search in the other
 //     lists) and the first topk written.
 template <class E, bool VEC>
-__global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(4))) void k_topk_rows(const typename E::raw* __restrict__ tgt,
-                                                      const typename E::raw* __restrict__ dft,
-                                                      const int32_t* __restrict__ cu, int K_max,
-                                                      int V, int topk, int chain,
-                                                      const int32_t* __restrict__ tok, float temperature,
-                                                      TopEntry* __restrict__ lists,
-                                                      int32_t* __restrict__ counts,
-                                                      RowTop* __restrict__ rowtop, int slot_lo,
-                                                      int slot_span,
-                                                      const int32_t* __restrict__ state,
-                                                      int phase) {
-    __shared__ unsigned long long wbuf[kWavesPerBlock][kWaveCap];
-    __shared__ int32_t qi_all[kWavesPerBlock][kQueue];
-    __shared__ uint32_t smax[kWavesPerBlock][kWave];
-    __shared__ uint32_t t_guess_b, t_safe_b;
-    __shared__ int wcnt[kWavesPerBlock];
-    __shared__ int wseen[kWavesPerBlock];
-    __shared__ double red[kWavesPerBlock];
+__device__ __forceinline__ KeptStats row_topk(const typename E::raw* __restrict__ row, int V, int topk,
+                                              double T, int y, bool stats, TopEntry* L, TopkSmem& sm) {
     constexpr int EV = E::kVec;
-    // chain: block -> (sequence, slot in [slot_lo, slot_lo + slot_span), side);
-    // the row's task number keeps the layout of the whole window
-    int task = blockIdx.x;
-    if (chain) {
-        const int r = (int)blockIdx.x >> 1;
-        const int b = r / slot_span;
-        if (state != nullptr && state[b] != phase) return;     // decided in an earlier phase
-        task = ((b * (K_max + 1) + slot_lo + r % slot_span) << 1) | ((int)blockIdx.x & 1);
-    }
-    const typename E::raw* row = topk_row<E>(tgt, dft, cu, K_max, V, task, chain != 0);
-    if (row == nullptr) return;
     const int tid = threadIdx.x;
     const int w = tid / kWave;
     const int lane = tid & (kWave - 1);
@@ -433,10 +430,10 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(4))) voi
             const bool keep_hi = ((lane & k) == 0) == ((lane & j) == 0);
             sv = keep_hi ? max(sv, o) : min(sv, o);
         }
-    smax[w][lane] = sv;
+    sm.smax[w][lane] = sv;
     if (tid == 0) {
-        t_guess_b = 0u;
-        t_safe_b = 0u;
+        sm.t_guess_b = 0u;
+        sm.t_safe_b = 0u;
     }
     __syncthreads();
     if (any) {
@@ -446,42 +443,42 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(4))) voi
             int lo = 0, hi = kWave;
             while (lo < hi) {
                 const int mid = (lo + hi) >> 1;
-                if (smax[o][mid] > mb) lo = mid + 1;
+                if (sm.smax[o][mid] > mb) lo = mid + 1;
                 else hi = mid;
             }
             gt += lo;
             hi = kWave;
             while (lo < hi) {
                 const int mid = (lo + hi) >> 1;
-                if (smax[o][mid] >= mb) lo = mid + 1;
+                if (sm.smax[o][mid] >= mb) lo = mid + 1;
                 else hi = mid;
             }
             ge += lo;
         }
         // ranks gt .. ge-1 hold this value (equal maxima write the same bits)
-        if (gt <= jg && jg < ge) t_guess_b = mb;
-        if (gt <= topk - 1 && topk - 1 < ge) t_safe_b = mb;
+        if (gt <= jg && jg < ge) sm.t_guess_b = mb;
+        if (gt <= topk - 1 && topk - 1 < ge) sm.t_safe_b = mb;
     }
     __syncthreads();
-    const uint32_t gb = t_guess_b, sb = t_safe_b;
+    const uint32_t gb = sm.t_guess_b, sb = sm.t_safe_b;
     // 2. the pass from the guess
     const float tg = gb == 0u ? -INFINITY : from_ordered(gb);
     const float ts = sb == 0u ? -INFINITY : from_ordered(sb);
-    WaveTop st = tg > 0.f ? row_pass<E, VEC, true, true>(row, V, gvend, tg, hs, qi_all[w], wbuf[w], topk)
-                          : row_pass<E, VEC, false, true>(row, V, gvend, tg, hs, qi_all[w], wbuf[w], topk);
+    WaveTop st = tg > 0.f ? row_pass<E, VEC, true, true>(row, V, gvend, tg, hs, sm.qi[w], sm.wbuf[w], topk)
+                          : row_pass<E, VEC, false, true>(row, V, gvend, tg, hs, sm.qi[w], sm.wbuf[w], topk);
     if (lane == 0) {
-        wcnt[w] = st.cnt;
-        wseen[w] = st.seen;
+        sm.wcnt[w] = st.cnt;
+        sm.wseen[w] = st.seen;
     }
     __syncthreads();
     int seen = 0;
-    for (int i = 0; i < kWavesPerBlock; ++i) seen += wseen[i];
+    for (int i = 0; i < kWavesPerBlock; ++i) seen += sm.wseen[i];
     // 3. exact unless fewer than topk tokens reached a guess above the bound
     if (seen < topk && tg != -INFINITY && tg != ts) {
         __syncthreads();
-        st = ts > 0.f ? row_pass<E, VEC, true, false>(row, V, gvend, ts, hs, qi_all[w], wbuf[w], topk)
-                      : row_pass<E, VEC, false, false>(row, V, gvend, ts, hs, qi_all[w], wbuf[w], topk);
-        if (lane == 0) wcnt[w] = st.cnt;
+        st = ts > 0.f ? row_pass<E, VEC, true, false>(row, V, gvend, ts, hs, sm.qi[w], sm.wbuf[w], topk)
+                      : row_pass<E, VEC, false, false>(row, V, gvend, ts, hs, sm.qi[w], sm.wbuf[w], topk);
+        if (lane == 0) sm.wcnt[w] = st.cnt;
         __syncthreads();
     }
     // 4. merge the waves' lists by rank
@@ -489,16 +486,74 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(4))) voi
     float xmax = -INFINITY;
     bool have = false;
     for (int i = 0; i < kWavesPerBlock; ++i) {
-        const int c = wcnt[i];
+        const int c = sm.wcnt[i];
         total += c;
         if (c > 0) {
-            const float x0 = from_ordered((uint32_t)(wbuf[i][0] >> 32));
+            const float x0 = from_ordered((uint32_t)(sm.wbuf[i][0] >> 32));
             xmax = have ? fmaxf(xmax, x0) : x0;
             have = true;
         }
     }
-    const int kept = total < topk ? total : topk;
-    TopEntry* L = lists + (int64_t)task * topk;
+    KeptStats ks;
+    ks.kept = total < topk ? total : topk;
+    ks.m = have ? (double)xmax / T : 0.0;
+    double sum = 0.0, ey = 0.0;
+    const int own = sm.wcnt[w];
+    for (int i = lane; i < own; i += kWave) {
+        const unsigned long long key = sm.wbuf[w][i];
+        int rank = i;
+#pragma unroll
+        for (int o2 = 0; o2 < kWavesPerBlock; ++o2)
+            if (o2 != w) rank += count_above(sm.wbuf[o2], sm.wcnt[o2], key);
+        if (rank < topk) {
+            TopEntry te;
+            te.idx = (int32_t)(0xffffffffu - (uint32_t)(key & 0xffffffffull));
+            te.x = from_ordered((uint32_t)(key >> 32));
+            L[rank] = te;
+            if (stats) {
+                const double e = exp((double)te.x / T - ks.m);
+                sum += e;
+                if (te.idx == y) ey = e;
+            }
+        }
+    }
+    if (stats) {
+        sum = block_sum(sum, sm.red);
+        ey = block_sum(ey, sm.red);  // at most one thread holds y
+    }
+    ks.S = sum;
+    ks.ey = ey;
+    return ks;
+}
+
+// One workgroup per row task: row_topk's list written to the task's slot;
+// for the rows of a chain also the row's softmax statistics over the kept set
+// and p(y) of the position's draft token (fp64).
+template <class E, bool VEC>
+__global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(4))) void k_topk_rows(const typename E::raw* __restrict__ tgt,
+                                                      const typename E::raw* __restrict__ dft,
+                                                      const int32_t* __restrict__ cu, int K_max,
+                                                      int V, int topk, int chain,
+                                                      const int32_t* __restrict__ tok, float temperature,
+                                                      TopEntry* __restrict__ lists,
+                                                      int32_t* __restrict__ counts,
+                                                      RowTop* __restrict__ rowtop, int slot_lo,
+                                                      int slot_span,
+                                                      const int32_t* __restrict__ state,
+                                                      int phase) {
+    __shared__ TopkSmem sm;
+    // chain: block -> (sequence, slot in [slot_lo, slot_lo + slot_span), side);
+    // the row's task number keeps the layout of the whole window
+    int task = blockIdx.x;
+    if (chain) {
+        const int r = (int)blockIdx.x >> 1;
+        const int b = r / slot_span;
+        if (state != nullptr && state[b] != phase) return;     // decided in an earlier phase
+        task = ((b * (K_max + 1) + slot_lo + r % slot_span) << 1) | ((int)blockIdx.x & 1);
+    }
+    const typename E::raw* row = topk_row<E>(tgt, dft, cu, K_max, V, task, chain != 0);
+    if (row == nullptr) return;
+    const int tid = threadIdx.x;
     const bool stats = rowtop != nullptr;
     int y = -1;
     if (stats && chain) {            // task = ((b * (K_max + 1) + s) * 2 + side)
@@ -508,45 +563,22 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(4))) voi
         seq_range(cu, rest / (K_max + 1), K_max, d0, k);
         if (s < k) y = tok[d0 + s];
     }
-    const double T = (double)temperature;
-    const double mref = have ? (double)xmax / T : 0.0;
-    double sum = 0.0, ey = 0.0;
-    const int own = wcnt[w];
-    for (int i = lane; i < own; i += kWave) {
-        const unsigned long long key = wbuf[w][i];
-        int rank = i;
-#pragma unroll
-        for (int o2 = 0; o2 < kWavesPerBlock; ++o2)
-            if (o2 != w) rank += count_above(wbuf[o2], wcnt[o2], key);
-        if (rank < topk) {
-            TopEntry te;
-            te.idx = (int32_t)(0xffffffffu - (uint32_t)(key & 0xffffffffull));
-            te.x = from_ordered((uint32_t)(key >> 32));
-            L[rank] = te;
-            if (stats) {
-                const double e = exp((double)te.x / T - mref);
-                sum += e;
-                if (te.idx == y) ey = e;
-            }
-        }
-    }
-    for (int i = kept + tid; i < topk; i += kBlock) {
+    TopEntry* L = lists + (int64_t)task * topk;
+    const KeptStats ks = row_topk<E, VEC>(row, V, topk, (double)temperature, y, stats, L, sm);
+    for (int i = ks.kept + tid; i < topk; i += kBlock) {
         TopEntry te;
         te.idx = -1;
         te.x = -INFINITY;
         L[i] = te;
     }
-    if (tid == 0) counts[task] = kept;
-    if (!stats) return;
-    sum = block_sum(sum, red);
-    ey = block_sum(ey, red);         // at most one thread holds y
-    if (tid == 0) {
+    if (tid == 0) counts[task] = ks.kept;
+    if (stats && tid == 0) {
         RowTop r;
-        r.count = kept;
-        r.m = mref;
-        r.S = sum;
-        r.valid = (kept > 0 && isfinite(mref) && isfinite(sum) && sum > 0.0) ? 1 : 0;
-        r.py = (r.valid && y >= 0 && y < V) ? ey / sum : 0.0;
+        r.count = ks.kept;
+        r.m = ks.m;
+        r.S = ks.S;
+        r.valid = (ks.kept > 0 && isfinite(ks.m) && isfinite(ks.S) && ks.S > 0.0) ? 1 : 0;
+        r.py = (r.valid && y >= 0 && y < V) ? ks.ey / ks.S : 0.0;
         rowtop[task] = r;
     }
 }
@@ -563,8 +595,19 @@ __device__ int list_inverse_cdf(const TopEntry* P, const RowTop& sp, const TopEn
     const int lane = threadIdx.x & (kWave - 1);
     const int np = sp.count;
     const int nd = (residual && sq.valid) ? sq.count : 0;
-    for (int i = lane; i < np; i += kWave) pl[i] = P[i];
-    for (int i = lane; i < nd; i += kWave) dl[i] = D[i];
+    // copies padded to a multiple of 8 with ids no search matches (pl: above
+    // every id, dl: -1), so the searches below read 8 entries per wait
+    const int np8 = (np + 7) & ~7, nd8 = (nd + 7) & ~7;
+    for (int i = lane; i < np8; i += kWave) {
+        TopEntry e = {0x7fffffff, 0.f};
+        if (i < np) e = P[i];
+        pl[i] = e;
+    }
+    for (int i = lane; i < nd8; i += kWave) {
+        TopEntry e = {-1, 0.f};
+        if (i < nd) e = D[i];
+        dl[i] = e;
+    }
     wave_lds_sync();
     for (int i = lane; i < np; i += kWave) {
         const int id = pl[i].idx;
@@ -574,13 +617,25 @@ __device__ int list_inverse_cdf(const TopEntry* P, const RowTop& sp, const TopEn
             // search first, then one exp, so the wave never runs an exp per
             // list entry
             int jm = -1;
-            for (int j = 0; j < nd; ++j) jm = (dl[j].idx == id) ? j : jm;
+            for (int j = 0; j < nd8; j += 8) {
+                int d8[8];
+#pragma unroll
+                for (int q = 0; q < 8; ++q) d8[q] = dl[j + q].idx;
+#pragma unroll
+                for (int q = 0; q < 8; ++q) jm = (d8[q] == id) ? j + q : jm;
+            }
             const double q = jm >= 0 ? exp((double)dl[jm].x / T - sq.m) / sq.S : 0.0;
             wgt = wgt - q;
             if (!(wgt > 0.0)) wgt = 0.0;
         }
         int rank = 0;
-        for (int j = 0; j < np; ++j) rank += (pl[j].idx < id);
+        for (int j = 0; j < np8; j += 8) {
+            int p8[8];
+#pragma unroll
+            for (int q = 0; q < 8; ++q) p8[q] = pl[j + q].idx;
+#pragma unroll
+            for (int q = 0; q < 8; ++q) rank += (p8[q] < id) ? 1 : 0;
+        }
         wbuf[rank] = wgt;
         ibuf[rank] = id;
     }
@@ -735,54 +790,265 @@ __global__ __launch_bounds__(kBlock) void k_chain_topk_decide(
 
 // ---------------------------------------------------------------------------
 // DDTree walk under a sampling target with top-k truncation [SD §5 DDTree,
-// SD §1]: k_topk_rows has written every node row's kept list and fp64 softmax
-// statistics; one wave per sequence walks, drawing the target's token at each
-// node from the node's kept list (token-id order, the node's uniform) and
-// moving to the child that carries it.
+// SD §1]: one workgroup per sequence, reading only the rows on its walk. At
+// each node the workgroup takes the exact top-k of the node's row (the list
+// in LDS); wave 0 forms the softmax over the kept set, draws the target's
+// token from it (token-id order, the node's uniform) and moves to the child
+// that carries it. Wave 0 holds the node table, one node per lane.
+//
+// A row of at most kTileVecs 16-byte vectors is held in registers and its
+// top-k taken there (tile_topk); longer rows, and the rare tile whose bound
+// admits too many candidates, are streamed by row_topk.
 // ---------------------------------------------------------------------------
-__global__ __launch_bounds__(kBlock) void k_tree_walk_topk(
-    const TopEntry* __restrict__ lists, const RowTop* __restrict__ rowtop,
-    const int32_t* __restrict__ node_token, const int32_t* __restrict__ node_parent,
-    const int32_t* __restrict__ n_nodes, const float* __restrict__ uniforms, int B, int N, int topk,
-    float temperature, int32_t* __restrict__ path, int32_t* __restrict__ A_out,
-    int32_t* __restrict__ next_out, int32_t* __restrict__ status_out) {
-    __shared__ double wbuf_all[kWavesPerBlock][kMaxTopk];
-    __shared__ int ibuf_all[kWavesPerBlock][kMaxTopk];
-    __shared__ TopEntry pl_all[kWavesPerBlock][kMaxTopk];
-    const int w = threadIdx.x / kWave;
-    const int lane = threadIdx.x & (kWave - 1);
-    const int b = blockIdx.x * kWavesPerBlock + w;
-    if (b >= B) return;
+constexpr int kTileVecs = 16;                   // 16-byte vectors per thread
+constexpr int kTileSeg = 128;                   // candidates per wave (LDS segment)
+static_assert(kTileVecs <= 32 && kTileSeg % 8 == 0, "vector mask bits; 8-key reads");
+
+// The j-th largest (from 1) of the wave's 64 keys, bits LO and up (the rest
+// 0), 0 when fewer than j keys are nonzero: the largest r that at least j
+// keys reach, built bit by bit from the top.
+template <int LO>
+__device__ __forceinline__ uint32_t wave_jth_largest(uint32_t key, int j) {
+    uint32_t r = 0u;
+#pragma unroll
+    for (int bit = 31; bit >= LO; --bit) {
+        const uint32_t c = r | (1u << bit);
+        if (__popcll(__ballot(key >= c)) >= j) r = c;
+    }
+    return r;
+}
+
+// Vector k of v for a lane-varying k (a select chain, no indexed registers).
+__device__ __forceinline__ uint4 pick_vec(const uint4 (&v)[kTileVecs], int k) {
+    uint4 x = v[0];
+#pragma unroll
+    for (int i = 1; i < kTileVecs; ++i) {
+        const bool t = k == i;
+        x.x = t ? v[i].x : x.x;
+        x.y = t ? v[i].y : x.y;
+        x.z = t ? v[i].z : x.z;
+        x.w = t ? v[i].w : x.w;
+    }
+    return x;
+}
+
+// Exact top-k of a row held as v[i] = vector i * kBlock + tid: every token
+// below the bound is beaten by topk others, so the tokens at or above it
+// contain the top-k. Each wave gathers its candidates into its LDS segment,
+// working through the vectors that may hold one (lowest first, one per lane
+// per round) and their passing elements (one per lane per step, slots from a
+// ballot); the candidates are then ranked by counting (keys are distinct).
+// Writes lst[0 .. kept) in key order and returns kept, or returns -1 having
+// written nothing when a wave finds more than kTileSeg candidates.
+template <class E>
+__device__ __forceinline__ int tile_topk(const uint4 (&v)[kTileVecs], int topk, TopEntry* lst,
+                                         unsigned long long* cbuf, int* s_rank, uint32_t* s_bound,
+                                         int* s_wcnt) {
+    constexpr int EV = E::kVec;
+    const int tid = threadIdx.x;
+    const int w = tid / kWave;
+    const int lane = tid & (kWave - 1);
+    // 1. each vector's and each thread's maximum (NaN skipped; a thread with
+    //    none holds key 0)
+    float vmax[kTileVecs];
+    float m = NAN;
+#pragma unroll
+    for (int i = 0; i < kTileVecs; ++i) {
+        vmax[i] = NAN;
+#pragma unroll
+        for (int e = 0; e < EV; ++e) vmax[i] = fmaxf(vmax[i], raw_elem<E>(v[i], e));
+        m = fmaxf(m, vmax[i]);
+    }
+    const uint32_t mk = m == m ? ordered_bits(m) : 0u;
+    // 2. in each wave the j-th largest maximum (j = ceil(topk / waves)) is
+    //    reached by j of its tokens; the smallest over the waves by topk
+    //    tokens. 0 (a wave with fewer than j values) admits every token. A
+    //    bf16 key's value lives in its top 16 bits: the bound keeps those and
+    //    admits exactly the tokens of that bf16 value and above.
+    constexpr int kLo = EV == 8 ? 16 : 0;
+    const uint32_t tw = wave_jth_largest<kLo>(mk, (topk + kWavesPerBlock - 1) / kWavesPerBlock);
+    if (lane == 0) s_bound[w] = tw;
+    __syncthreads();
+    uint32_t tb = s_bound[0];
+#pragma unroll
+    for (int o = 1; o < kWavesPerBlock; ++o) tb = min(tb, s_bound[o]);
+    const float tf = tb == 0u ? -INFINITY : from_ordered(tb);
+    // 3. the candidates x >= tf (NaN never), in the vectors whose maximum
+    //    reaches the bound
+    uint32_t vm = 0u;
+#pragma unroll
+    for (int i = 0; i < kTileVecs; ++i) vm |= vmax[i] >= tf ? (1u << i) : 0u;
+    unsigned long long* seg = cbuf + w * kTileSeg;
+    int cnt = 0;                     // wave-uniform
+    while (__ballot(vm != 0u)) {
+        const int i = vm != 0u ? __builtin_ctz(vm) : 0;
+        const uint4 x = pick_vec(v, i);
+        uint32_t em = 0u;
+        if (vm != 0u) {
+#pragma unroll
+            for (int e = 0; e < EV; ++e) em |= raw_elem<E>(x, e) >= tf ? (1u << e) : 0u;
+        }
+        vm &= vm - 1u;
+        while (true) {
+            const bool has = em != 0u;
+            const unsigned long long bal = __ballot(has);
+            if (bal == 0ull) break;
+            if (has) {
+                const int e = __builtin_ctz(em);
+                em &= em - 1u;
+                const int slot = cnt + (int)__builtin_amdgcn_mbcnt_hi(
+                                           (uint32_t)(bal >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)bal, 0u));
+                if (slot < kTileSeg) seg[slot] = make_key(raw_elem<E>(x, e), (i * kBlock + tid) * EV + e);
+            }
+            cnt += __popcll(bal);
+        }
+    }
+    // pad the segment to a multiple of 8 with keys that beat nothing
+    if (cnt <= kTileSeg)
+        for (int a = cnt + lane; a < ((cnt + 7) & ~7); a += kWave) seg[a] = 0ull;
+    if (lane == 0) s_wcnt[w] = cnt;
+    for (int a = tid; a < kWavesPerBlock * kTileSeg; a += kBlock) s_rank[a] = 0;
+    __syncthreads();
+    static_assert(kWavesPerBlock == 4, "four wave segments");
+    const int wc0 = s_wcnt[0], wc1 = s_wcnt[1], wc2 = s_wcnt[2], wc3 = s_wcnt[3];
+    const int C = wc0 + wc1 + wc2 + wc3;
+    if (wc0 > kTileSeg || wc1 > kTileSeg || wc2 > kTileSeg || wc3 > kTileSeg) return -1;
+    // 4. rank by counting: one (candidate, segment) pair per thread and
+    //    round, 8 keys per read, the partial counts summed in LDS
+    for (int p = tid; p < kWavesPerBlock * C; p += kBlock) {
+        const int c = p / kWavesPerBlock;
+        const int o = p % kWavesPerBlock;
+        // candidate c -> slot a of its segment
+        const int a = c < wc0                   ? c
+                      : c < wc0 + wc1             ? kTileSeg + (c - wc0)
+                      : c < wc0 + wc1 + wc2       ? 2 * kTileSeg + (c - wc0 - wc1)
+                                                  : 3 * kTileSeg + (c - wc0 - wc1 - wc2);
+        const unsigned long long key = cbuf[a];
+        const unsigned long long* so = cbuf + o * kTileSeg;
+        const int n8 = ((o == 0 ? wc0 : o == 1 ? wc1 : o == 2 ? wc2 : wc3) + 7) & ~7;
+        int part = 0;
+        for (int j = 0; j < n8; j += 8) {
+            unsigned long long k8[8];
+#pragma unroll
+            for (int q = 0; q < 8; ++q) k8[q] = so[j + q];
+#pragma unroll
+            for (int q = 0; q < 8; ++q) part += k8[q] > key ? 1 : 0;
+        }
+        if (part > 0) atomicAdd(&s_rank[a], part);
+    }
+    __syncthreads();
+    for (int a = tid; a < kWavesPerBlock * kTileSeg; a += kBlock) {
+        const int rank = s_rank[a];
+        const int sa = a / kTileSeg;
+        if (a % kTileSeg < (sa == 0 ? wc0 : sa == 1 ? wc1 : sa == 2 ? wc2 : wc3) && rank < topk) {
+            const unsigned long long key = cbuf[a];
+            TopEntry te;
+            te.idx = (int32_t)(0xffffffffu - (uint32_t)(key & 0xffffffffull));
+            te.x = from_ordered((uint32_t)(key >> 32));
+            lst[rank] = te;
+        }
+    }
+    __syncthreads();
+    return C < topk ? C : topk;
+}
+
+// row_topk's list without statistics, out of line: the walk's tile path keeps
+// its registers to itself.
+template <class E, bool VEC>
+__device__ __noinline__ int row_topk_list(const typename E::raw* row, int V, int topk, TopEntry* lst,
+                                          TopkSmem* sm) {
+    const int kept = row_topk<E, VEC>(row, V, topk, 1.0, -1, false, lst, *sm).kept;
+    __syncthreads();
+    return kept;
+}
+
+template <class E, bool VEC>
+__global__ __launch_bounds__(kBlock) void k_tree_walk_topk_rows(
+    const typename E::raw* __restrict__ target, const int32_t* __restrict__ node_token,
+    const int32_t* __restrict__ node_parent, const int32_t* __restrict__ n_nodes,
+    const float* __restrict__ uniforms, int B, int N, int V, int topk, float temperature,
+    int32_t* __restrict__ path, int32_t* __restrict__ A_out, int32_t* __restrict__ next_out,
+    int32_t* __restrict__ status_out) {
+    __shared__ TopkSmem sm;
+    __shared__ unsigned long long cbuf[kWavesPerBlock * kTileSeg];
+    __shared__ int s_rank[kWavesPerBlock * kTileSeg];
+    __shared__ TopEntry lst[kMaxTopk];
+    __shared__ TopEntry pl[kMaxTopk];
+    __shared__ double cw[kMaxTopk];
+    __shared__ int ci[kMaxTopk];
+    __shared__ uint32_t s_bound[kWavesPerBlock];
+    __shared__ int s_wcnt[kWavesPerBlock];
+    __shared__ int s_pick[3];
+    constexpr int EV = E::kVec;
+    const int b = blockIdx.x;
+    const int tid = threadIdx.x;
+    const int lane = tid & (kWave - 1);
+    const bool w0 = tid < kWave;
+    const int gvend = (V + EV - 1) / EV;
+    const bool in_tile = gvend <= kTileVecs * kBlock;
     int nn = n_nodes[b];
     nn = nn < 1 ? 1 : (nn > N ? N : nn);
-    const int my_tok = lane < nn ? node_token[(int64_t)b * N + lane] : -1;
-    const int my_par = lane < nn ? node_parent[(int64_t)b * N + lane] : -2;
-    if (lane < N) path[(int64_t)b * N + lane] = -1;
+    const int my_tok = (w0 && lane < nn) ? node_token[(int64_t)b * N + lane] : -1;
+    const int my_par = (w0 && lane < nn) ? node_parent[(int64_t)b * N + lane] : -2;
+    for (int i = tid; i < N; i += kBlock) path[(int64_t)b * N + i] = -1;
     const double T = (double)temperature;
     int node = 0, len = 0, next = -1, status = 0;
     for (int step = 0; step < N; ++step) {
         const int64_t r = (int64_t)b * N + node;
-        const RowTop sp = rowtop[r];
-        if (!sp.valid) {
+        const typename E::raw* row = target + r * V;
+        int kept = -1;
+        if (in_tile) {
+            uint4 v[kTileVecs];
+#pragma unroll
+            for (int i = 0; i < kTileVecs; ++i) v[i] = topk_raw<E, VEC>(row, V, gvend, i * kBlock + tid);
+            kept = tile_topk<E>(v, topk, lst, cbuf, s_rank, s_bound, s_wcnt);
+        }
+        if (kept < 0) kept = row_topk_list<E, VEC>(row, V, topk, lst, &sm);   // uniform
+        if (w0) {
+            // softmax over the kept set (fp64), then the draw and the child
+            const double m = kept > 0 ? (double)lst[0].x / T : 0.0;
+            double S = 0.0;
+            for (int i = lane; i < kept; i += kWave) S += exp((double)lst[i].x / T - m);
+            S = wave_sum(S);
+            const bool valid = kept > 0 && isfinite(m) && isfinite(S) && S > 0.0;
+            int g = -1;
+            unsigned long long h = 0ull;
+            if (valid) {
+                RowTop sp;
+                sp.count = kept;
+                sp.valid = 1;
+                sp.m = m;
+                sp.S = S;
+                sp.py = 0.0;
+                double unused;
+                g = list_inverse_cdf(lst, sp, nullptr, sp, false, T, (double)uniforms[r], cw, ci, pl, pl,
+                                     &unused);
+                h = __ballot(g >= 0 && lane >= 1 && lane < nn && my_par == node && my_tok == g);
+            }
+            if (lane == 0) {
+                s_pick[0] = valid ? 1 : 0;
+                s_pick[1] = g;
+                s_pick[2] = h ? __ffsll(h) - 1 : -1;
+            }
+        }
+        // the next write of s_pick, lst or the row scratch follows the next
+        // row's first barrier, after every thread has read this step's pick
+        __syncthreads();
+        const int valid = s_pick[0], g = s_pick[1], child = s_pick[2];
+        if (!valid) {
             status |= 2;
             next = -1;
             break;
         }
-        double unused;
-        const int g = list_inverse_cdf(lists + r * topk, sp, nullptr, sp, false, T, (double)uniforms[r],
-                                       wbuf_all[w], ibuf_all[w], pl_all[w], pl_all[w], &unused);
-        const unsigned long long h =
-            __ballot(g >= 0 && lane >= 1 && lane < nn && my_par == node && my_tok == g);
-        if (!h) {
+        if (child < 0) {
             next = g;
             break;
         }
-        const int child = __ffsll(h) - 1;
-        if (lane == 0) path[(int64_t)b * N + len] = child;
+        if (tid == 0) path[(int64_t)b * N + len] = child;
         ++len;
         node = child;
     }
-    if (lane == 0) {
+    if (tid == 0) {
         A_out[b] = len;
         next_out[b] = next;
         if (status_out) status_out[b] = status;
@@ -1427,45 +1693,35 @@ hipError_t launch_chain_topk(const ChainArgs& a) {
     return chain_topk_impl<F32, false>(a);
 }
 
-size_t tree_walk_topk_ws_bytes(int B, int N, int top_k) {
-    size_t bytes = 0;
-    topk_layout(nullptr, (size_t)B * N, top_k, nullptr, 0, &bytes);
-    return bytes;
+template <class E, bool VEC>
+static void walk_topk_rows(const void* target, const int32_t* tok, const int32_t* par,
+                           const int32_t* n_nodes, const float* uniforms, int B, int N, int V,
+                           float temperature, int top_k, int32_t* path, int32_t* accepted_len,
+                           int32_t* next_token, int32_t* seq_status, hipStream_t stream) {
+    PassTimer::launch(k_tree_walk_topk_rows<E, VEC>, dim3((unsigned)B), dim3(kBlock), stream,
+                      static_cast<const typename E::raw*>(target), tok, par, n_nodes, uniforms, B, N, V,
+                      top_k, temperature, path, accepted_len, next_token, seq_status);
 }
 
 hipError_t launch_tree_walk_topk(const void* target, int dtype, const int32_t* tok, const int32_t* par,
                                  const int32_t* n_nodes, const float* uniforms, int B, int N, int V,
                                  float temperature, int top_k, int32_t* path, int32_t* accepted_len,
-                                 int32_t* next_token, int32_t* seq_status, void* ws,
-                                 hipStream_t stream) {
-    const size_t tasks = (size_t)B * N;
-    TopkLayout L;
-    topk_layout(ws, tasks, top_k, &L, 0);
+                                 int32_t* next_token, int32_t* seq_status, hipStream_t stream) {
     if (dtype == 1) {
-        const auto* rows = static_cast<const Bf16::raw*>(target);
         if (V % Bf16::kVec == 0)
-            PassTimer::launch(k_topk_rows<Bf16, true>, dim3((unsigned)tasks), dim3(kBlock), stream, rows,
-                              rows, nullptr, 0, V, top_k, 0, nullptr, temperature, L.lists, L.counts,
-                              L.rowtop, 0, 1, nullptr, 0);
+            walk_topk_rows<Bf16, true>(target, tok, par, n_nodes, uniforms, B, N, V, temperature, top_k, path,
+                                       accepted_len, next_token, seq_status, stream);
         else
-            PassTimer::launch(k_topk_rows<Bf16, false>, dim3((unsigned)tasks), dim3(kBlock), stream, rows,
-                              rows, nullptr, 0, V, top_k, 0, nullptr, temperature, L.lists, L.counts,
-                              L.rowtop, 0, 1, nullptr, 0);
+            walk_topk_rows<Bf16, false>(target, tok, par, n_nodes, uniforms, B, N, V, temperature, top_k, path,
+                                        accepted_len, next_token, seq_status, stream);
     } else {
-        const auto* rows = static_cast<const F32::raw*>(target);
         if (V % F32::kVec == 0)
-            PassTimer::launch(k_topk_rows<F32, true>, dim3((unsigned)tasks), dim3(kBlock), stream, rows,
-                              rows, nullptr, 0, V, top_k, 0, nullptr, temperature, L.lists, L.counts,
-                              L.rowtop, 0, 1, nullptr, 0);
+            walk_topk_rows<F32, true>(target, tok, par, n_nodes, uniforms, B, N, V, temperature, top_k, path,
+                                      accepted_len, next_token, seq_status, stream);
         else
-            PassTimer::launch(k_topk_rows<F32, false>, dim3((unsigned)tasks), dim3(kBlock), stream, rows,
-                              rows, nullptr, 0, V, top_k, 0, nullptr, temperature, L.lists, L.counts,
-                              L.rowtop, 0, 1, nullptr, 0);
+            walk_topk_rows<F32, false>(target, tok, par, n_nodes, uniforms, B, N, V, temperature, top_k, path,
+                                       accepted_len, next_token, seq_status, stream);
     }
-    const unsigned grid = (unsigned)((B + kWavesPerBlock - 1) / kWavesPerBlock);
-    hipLaunchKernelGGL(k_tree_walk_topk, dim3(grid), dim3(kBlock), 0, stream, L.lists, L.rowtop, tok, par,
-                       n_nodes, uniforms, B, N, top_k, temperature, path, accepted_len, next_token,
-                       seq_status);
     return hipGetLastError();
 }
 

@@ -736,6 +736,33 @@ def test_tree_walk_sampled_topk_matches_oracle(dtype, V, T, top_k):
     _say(f"  mean walk {ref['A'].mean():.2f}, margin {int((ref['margin'] != 0).sum())}")
 
 
+# The top-k walk holds a row of up to 4096 16-byte vectors in registers (bf16
+# V <= 32768, fp32 V <= 16384) and streams longer rows; a tile whose bound
+# admits too many candidates (heavy ties) is streamed too. Each case checks one
+# side of those limits: the largest tiles and one vector past them, rows of
+# negative log-probabilities, coarse ties, and flat rows (every id tied).
+@pytest.mark.parametrize("dtype,V,top_k,kind", [("bf16", 32768, 50, "normal"), ("bf16", 32776, 50, "normal"),
+                                                ("f32", 16384, 20, "normal"), ("f32", 16388, 20, "normal"),
+                                                ("bf16", 32000, 50, "logprob"), ("bf16", 32000, 200, "coarse"),
+                                                ("f32", 8000, 64, "flat"), ("bf16", 32000, 256, "flat")])
+def test_tree_walk_sampled_topk_tile_limits(dtype, V, top_k, kind):
+    B, K, N = 16, 16, 64
+    _say(f"sampled walk top-k {top_k} {dtype} V={V} rows {kind}")
+    case = wl.gen_tree(device="cuda", seed=91 + V + top_k, B=B, K=K, V=V, N=N)
+    tree = sd.build_tree(case.marginals, N)
+    target = case.target_for_depths(tree["depth"], tree["n_nodes"]).float()
+    if kind == "logprob":
+        target = torch.log_softmax(target, dim=-1)
+    elif kind == "coarse":
+        target = torch.round(target * 2.0) / 2.0
+    elif kind == "flat":
+        target[0::2] = 0.0             # even sequences: every row one tied value
+    target = target.to(torch.bfloat16) if dtype == "bf16" else target
+    u = wl.grid_uniforms((B, N), torch.Generator(device="cuda").manual_seed(V + 3), "cuda")
+    out, ref = _sampled_walk_check(tree, target, 1.0, u, top_k=top_k)
+    _say(f"  mean walk {ref['A'].mean():.2f}, margin {int((ref['margin'] != 0).sum())}")
+
+
 def test_tree_walk_sampled_topk_ties_and_nonfinite():
     V, N, B = 12, 6, 3
     tok = torch.tensor([[-1, 4, 7, 2, 9, -1]] * B, dtype=torch.int32, device="cuda")
