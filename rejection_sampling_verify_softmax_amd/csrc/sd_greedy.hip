@@ -67,11 +67,11 @@ __global__ __launch_bounds__(kBlock) void k_argmax(const typename E::raw* __rest
     float best = -INFINITY;
     int bidx = kNone;
     // the best of one vector's elements, first index on ties; NaN-only
-    // vectors leave vmax NaN and never win
+    // vectors leave vmax NaN and never win (fmaxf skips a NaN operand)
     auto consider = [&](const float (&f)[EV], int vi) {
         float vmax = f[0];
 #pragma unroll
-        for (int e = 1; e < EV; ++e) vmax = nmax(vmax, f[e]);
+        for (int e = 1; e < EV; ++e) vmax = fmaxf(vmax, f[e]);
         if (vmax > best || (bidx == kNone && vmax == vmax)) {
             int e_hit = EV - 1;
 #pragma unroll

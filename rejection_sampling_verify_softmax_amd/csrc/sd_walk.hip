@@ -229,22 +229,55 @@ __global__ __launch_bounds__(kWalkThreads) void k_tree_walk_rows(
             load_tile(t);
             if (step == 0 && t == 0) load_node_table();
             const int64_t v0 = (int64_t)t * S::kTileVec + (int64_t)w * S::kSegVec + lane;
+            if (GREEDY) {
+                // the thread's maximum over this tile (NaN skipped) from the
+                // vectors' maxima, then its first occurrence: the first vector
+                // that holds it, the first element there. Entries past the row
+                // read as -inf and come after the row's own in this order, so
+                // an occurrence past the row means the thread holds no value.
+                float vmx[R];
+                float M = NAN;
 #pragma unroll
-            for (int r = 0; r < R; ++r) {
-                float f[EV];
-                E::unpack(q[r], f);
-                if (GREEDY) {
+                for (int r = 0; r < R; ++r) {
+                    float f[EV];
+                    E::unpack(q[r], f);
+                    vmx[r] = f[0];
 #pragma unroll
-                    for (int e = 0; e < EV; ++e) {
-                        const int j = (int)((v0 + r * kWave) * EV + e);
-                        if (f[e] == f[e] && j < V && (f[e] > best || bidx == kNoIdx)) {
-                            best = f[e];
-                            bidx = j;
-                        }
+                    for (int e = 1; e < EV; ++e) vmx[r] = fmaxf(vmx[r], f[e]);
+                    M = fmaxf(M, vmx[r]);
+                }
+                if (M == M) {
+                    int rs = 0;
+#pragma unroll
+                    for (int r = R - 1; r >= 0; --r) rs = vmx[r] == M ? r : rs;
+                    uint4 qs = q[0];
+#pragma unroll
+                    for (int r = 1; r < R; ++r) {
+                        const bool t2 = rs == r;
+                        qs.x = t2 ? q[r].x : qs.x;
+                        qs.y = t2 ? q[r].y : qs.y;
+                        qs.z = t2 ? q[r].z : qs.z;
+                        qs.w = t2 ? q[r].w : qs.w;
                     }
-                } else {
+                    float f[EV];
+                    E::unpack(qs, f);
+                    int es = 0;
 #pragma unroll
-                    for (int e = 0; e < EV; ++e) best = nmax(best, f[e]);
+                    for (int e = EV - 1; e >= 0; --e) es = f[e] == M ? e : es;
+                    const int j = (int)((v0 + rs * kWave) * EV + es);
+                    if (j < V && (M > best || bidx == kNoIdx)) {
+                        best = M;
+                        bidx = j;
+                    }
+                }
+            } else {
+                // NaN skipped (fmaxf returns the other operand); past the row -inf
+#pragma unroll
+                for (int r = 0; r < R; ++r) {
+                    float f[EV];
+                    E::unpack(q[r], f);
+#pragma unroll
+                    for (int e = 0; e < EV; ++e) best = fmaxf(best, f[e]);
                 }
             }
         }
