@@ -276,7 +276,8 @@ __device__ __forceinline__ void offer_vecs(Offer& o, const uint4 (&v)[N], int vi
 // steps load without bounds checks; one checked step takes the ragged end.
 template <class E, bool VEC, bool POS>
 __device__ __forceinline__ void offer_range(Offer& o, const typename E::raw* row, int V, int gvend,
-                                            int v_start, int topk) {
+                                            int v_start, int topk, const uint4 (&pre)[kTopkU],
+                                            bool have_pre) {
     constexpr int kStep = kBlock * kTopkU;
     const int tid = threadIdx.x;
     const int nsteps = VEC ? (gvend - v_start) / kStep : 0;
@@ -284,6 +285,11 @@ __device__ __forceinline__ void offer_range(Offer& o, const typename E::raw* row
     pipelined_steps<kTopkU>(
         nsteps,
         [&](uint4 (&buf)[kTopkU], int st) {
+            if (st == 0 && have_pre) {       // the first step, loaded by the caller
+#pragma unroll
+                for (int u = 0; u < kTopkU; ++u) buf[u] = pre[u];
+                return;
+            }
 #pragma unroll
             for (int u = 0; u < kTopkU; ++u) buf[u] = load16(row, v_start + st * kStep + u * kBlock + tid);
         },
@@ -300,12 +306,14 @@ __device__ __forceinline__ void offer_range(Offer& o, const typename E::raw* row
 }
 
 // One pass over the row from threshold t: with SAMPLE, the held sample first
-// and then vectors from the end of the sample on; else the whole row. Leaves
+// and then vectors from the end of the sample on (the first whole step of
+// them already loaded into pre when have_pre); else the whole row. Leaves
 // each wave's best min(cnt, topk) keys sorted at the front of its buffer.
 template <class E, bool VEC, bool POS, bool SAMPLE>
 __device__ __forceinline__ WaveTop row_pass(const typename E::raw* row, int V, int gvend, float t,
                                             const uint4 (&hs)[kTopkSample], int32_t* qi,
-                                            unsigned long long* wb, int topk) {
+                                            unsigned long long* wb, int topk,
+                                            const uint4 (&pre)[kTopkU], bool have_pre) {
     Offer o;
     o.st.cnt = 0;
     o.st.seen = 0;
@@ -321,7 +329,7 @@ __device__ __forceinline__ WaveTop row_pass(const typename E::raw* row, int V, i
         offer_vecs<E, VEC, POS, kTopkSample, false>(o, hs, threadIdx.x, row, V, gvend, topk);
         v_start = kTopkSample * kBlock;
     }
-    offer_range<E, VEC, POS>(o, row, V, gvend, v_start, topk);
+    offer_range<E, VEC, POS>(o, row, V, gvend, v_start, topk, pre, SAMPLE && have_pre);
     return wave_compact(wb, o.st, topk);
 }
 
@@ -399,6 +407,19 @@ __device__ __forceinline__ KeptStats row_topk(const typename E::raw* __restrict_
 #pragma unroll
         for (int i = 0; i < kTopkSample; ++i) hs[i] = topk_raw<E, VEC>(row, V, gvend, i * kBlock + tid);
     }
+    // the streaming pass's first whole step, issued now so that its loads
+    // overlap the ranking of the thresholds below (bf16 rows: measured
+    // faster despite the extra spill; fp32 keeps its registers)
+    constexpr int kStep = kBlock * kTopkU;
+    const bool have_pre = VEC && EV == 8 && gvend - kTopkSample * kBlock >= kStep;
+    uint4 pre[kTopkU];
+    if (have_pre) {
+#pragma unroll
+        for (int u = 0; u < kTopkU; ++u) pre[u] = load16(row, kTopkSample * kBlock + u * kBlock + tid);
+    } else {
+#pragma unroll
+        for (int u = 0; u < kTopkU; ++u) pre[u] = make_uint4(0u, 0u, 0u, 0u);
+    }
     float m = NAN;                   // fmaxf skips NaN; stays NaN only if all are
 #pragma unroll
     for (int i = 0; i < kTopkSample; ++i) {
@@ -464,8 +485,10 @@ __device__ __forceinline__ KeptStats row_topk(const typename E::raw* __restrict_
     // 2. the pass from the guess
     const float tg = gb == 0u ? -INFINITY : from_ordered(gb);
     const float ts = sb == 0u ? -INFINITY : from_ordered(sb);
-    WaveTop st = tg > 0.f ? row_pass<E, VEC, true, true>(row, V, gvend, tg, hs, sm.qi[w], sm.wbuf[w], topk)
-                          : row_pass<E, VEC, false, true>(row, V, gvend, tg, hs, sm.qi[w], sm.wbuf[w], topk);
+    WaveTop st = tg > 0.f ? row_pass<E, VEC, true, true>(row, V, gvend, tg, hs, sm.qi[w], sm.wbuf[w], topk,
+                                                         pre, have_pre)
+                          : row_pass<E, VEC, false, true>(row, V, gvend, tg, hs, sm.qi[w], sm.wbuf[w], topk,
+                                                          pre, have_pre);
     if (lane == 0) {
         sm.wcnt[w] = st.cnt;
         sm.wseen[w] = st.seen;
@@ -476,8 +499,10 @@ __device__ __forceinline__ KeptStats row_topk(const typename E::raw* __restrict_
     // 3. exact unless fewer than topk tokens reached a guess above the bound
     if (seen < topk && tg != -INFINITY && tg != ts) {
         __syncthreads();
-        st = ts > 0.f ? row_pass<E, VEC, true, false>(row, V, gvend, ts, hs, sm.qi[w], sm.wbuf[w], topk)
-                      : row_pass<E, VEC, false, false>(row, V, gvend, ts, hs, sm.qi[w], sm.wbuf[w], topk);
+        st = ts > 0.f ? row_pass<E, VEC, true, false>(row, V, gvend, ts, hs, sm.qi[w], sm.wbuf[w], topk,
+                                                      pre, false)
+                      : row_pass<E, VEC, false, false>(row, V, gvend, ts, hs, sm.qi[w], sm.wbuf[w], topk,
+                                                       pre, false);
         if (lane == 0) sm.wcnt[w] = st.cnt;
         __syncthreads();
     }
