@@ -470,8 +470,10 @@ def _tree_compare(out, ref):
     np.testing.assert_array_equal(out["score"].cpu().numpy(), ref["score"])   # same fp32 products
 
 
+# (3, 3, ...) and (1, 1, ...): an odd number of rows, so the candidate kernel's
+# last workgroup (two rows each) holds one row
 @pytest.mark.parametrize("B,K,V,N", [(4, 3, 5, 20), (6, 16, 700, 64), (3, 2, 3, 64), (5, 16, 31, 64),
-                                     (2, 1, 1000, 10)])
+                                     (2, 1, 1000, 10), (3, 3, 500, 40), (1, 1, 50, 8)])
 def test_tree_build_small(B, K, V, N):
     case = wl.gen_tree(device="cuda", seed=5 + V, B=B, K=K, V=V, N=N, sigma=1.5)
     out = sd.build_tree(case.marginals, N)
