@@ -152,6 +152,20 @@ __device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
     return __builtin_amdgcn_readlane(v, kWave - 1);
 }
 
+// The j-th largest (from 1) of the wave's 64 keys, bits LO and up (the rest
+// 0), 0 when fewer than j keys are nonzero: the largest r that at least j
+// keys reach, built bit by bit from the top.
+template <int LO>
+__device__ __forceinline__ uint32_t wave_jth_largest(uint32_t key, int j) {
+    uint32_t r = 0u;
+#pragma unroll
+    for (int bit = 31; bit >= LO; --bit) {
+        const uint32_t c = r | (1u << bit);
+        if (__popcll(__ballot(key >= c)) >= j) r = c;
+    }
+    return r;
+}
+
 // Inclusive prefix sum across the wave (lane order) of non-negative counts.
 __device__ __forceinline__ int wave_incl_scan_int(int c) {
     uint32_t v = (uint32_t)c;

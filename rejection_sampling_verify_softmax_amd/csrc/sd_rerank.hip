@@ -14,9 +14,12 @@
 // parent under that order, so the kept set is closed under taking parents.
 // Nodes are numbered in that order, with the outputs of the DDTree build.
 //
-// One workgroup per sequence: level-synchronous confidences in LDS; each wave
-// sorts the 64-bit keys of its quarter of the candidates, and the four lists'
-// heads merge by rank into the kept nodes; then one thread per kept node.
+// One workgroup per sequence: confidences formed level by level in LDS, one
+// barrier per level (a level stamp per candidate tells a finished parent from
+// one formed in the same round); then the N-1 best keys by a bound from the
+// waves' best keys and ranking by counting of the few keys that reach it
+// (heavy ties: each wave sorts its keys and the four lists merge by rank);
+// then one thread per kept node.
 #include "sd_device.hpp"
 #include "sd_internal.hpp"
 
@@ -26,6 +29,7 @@ namespace {
 
 constexpr int kMaxCand = 1024;
 constexpr int kCandPerThread = kMaxCand / kBlock;
+constexpr int kSelCap = 256;     // candidates the threshold path ranks by counting
 
 __device__ __forceinline__ uint32_t conf_bits(float x) {
     // x in [0, 1]: its bits order it (no negatives, no NaN)
@@ -41,11 +45,15 @@ __global__ __launch_bounds__(kBlock) void k_rerank_tree(
     int32_t* __restrict__ n_nodes) {
     __shared__ float score[kMaxCand];
     __shared__ int par[kMaxCand];
-    __shared__ int depth[kMaxCand];
-    __shared__ unsigned char ready[kMaxCand];
+    __shared__ int lvl[kMaxCand];            // depth once the confidence is known, else -1
+    __shared__ int s_more[3];                // round l sets slot l % 3 when it formed a candidate
     __shared__ unsigned long long wkeys[kWavesPerBlock][kWave * kCandPerThread];
     __shared__ unsigned long long top[64];
     __shared__ int node_of[kMaxCand];
+    __shared__ int tok_s[kMaxCand];
+    __shared__ unsigned long long sel[kSelCap];
+    __shared__ uint32_t s_bound[kWavesPerBlock];
+    __shared__ int s_sel;
     const int b = blockIdx.x;
     const int tid = threadIdx.x;
     int nc = n_cand[b];
@@ -53,83 +61,141 @@ __global__ __launch_bounds__(kBlock) void k_rerank_tree(
     const int64_t o = (int64_t)b * M;
     // 1. candidates: a bad parent or probability leaves a candidate (and its
     //    subtree) out
-    float prob[kCandPerThread];
+    //    (each thread's own parent, state, confidence and depth stay in
+    //    registers; the LDS copies serve the children)
+    float prob[kCandPerThread], my_sc[kCandPerThread];
+    int my_par[kCandPerThread], my_dep[kCandPerThread];
+    bool my_rdy[kCandPerThread];
 #pragma unroll
     for (int j = 0; j < kCandPerThread; ++j) {
         const int i = j * kBlock + tid;
-        int p = -1;
+        int p = -1, t = -1;
         float q = 0.f;
+        if (i < nc) t = cand_token[o + i];   // read now: the outputs need the kept ones
         if (i < nc && i > 0) {
             p = cand_parent[o + i];
             q = cand_prob[o + i];
         }
         const bool ok = i > 0 && i < nc && p >= 0 && p < i && q >= 0.f && q <= 1.f;
-        par[i] = ok ? p : -1;
+        my_par[j] = ok ? p : -1;
         prob[j] = q;
-        ready[i] = (i == 0 && nc > 0) ? 1 : 0;
-        score[i] = (i == 0) ? 1.0f : 0.f;
-        depth[i] = 0;
+        my_rdy[j] = i == 0 && nc > 0;
+        my_sc[j] = (i == 0) ? 1.0f : 0.f;
+        my_dep[j] = 0;
+        par[i] = my_par[j];
+        lvl[i] = my_rdy[j] ? 0 : -1;
+        score[i] = my_sc[j];
         node_of[i] = (i == 0) ? 0 : -1;
+        tok_s[i] = t;
     }
+    if (tid < 3) s_more[tid] = 0;
     __syncthreads();
-    // 2. confidences level by level: a candidate is done once its parent is
-    //    (read, then write, so one level never sees its own updates)
+    // 2. confidences level by level, root first: in round l a candidate
+    //    whose parent was formed in an earlier round takes its parent's
+    //    confidence times its own probability and depth l. A parent formed in
+    //    this round reads as -1 or l, never below l, so one barrier per round
+    //    keeps every read on values finished before it. Round l clears slot
+    //    (l + 1) % 3 for the next round while slot (l - 1) % 3 may still be
+    //    read after the previous barrier.
     bool more = true;
-    while (more) {
-        bool mine[kCandPerThread];
-        float ns[kCandPerThread];
-        int nd[kCandPerThread];
+    for (int l = 1; more; ++l) {
         bool any = false;
+        if (tid == 0) s_more[(l + 1) % 3] = 0;
 #pragma unroll
         for (int j = 0; j < kCandPerThread; ++j) {
-            const int i = j * kBlock + tid;
-            const int p = par[i];
-            mine[j] = !ready[i] && p >= 0 && ready[p];
-            ns[j] = mine[j] ? score[p] * prob[j] : 0.f;
-            nd[j] = mine[j] ? depth[p] + 1 : 0;
-            any = any || mine[j];
-        }
-        __syncthreads();
-#pragma unroll
-        for (int j = 0; j < kCandPerThread; ++j) {
-            const int i = j * kBlock + tid;
-            if (mine[j]) {
-                score[i] = ns[j];
-                depth[i] = nd[j];
-                ready[i] = 1;
+            const int p = my_par[j];
+            if (!my_rdy[j] && p >= 0) {
+                const int lp = lvl[p];
+                if (lp >= 0 && lp < l) {
+                    const int i = j * kBlock + tid;
+                    my_sc[j] = score[p] * prob[j];
+                    my_dep[j] = l;
+                    my_rdy[j] = true;
+                    score[i] = my_sc[j];
+                    lvl[i] = l;
+                    any = true;
+                }
             }
         }
-        more = __syncthreads_or(any) != 0;
+        if (any) s_more[l % 3] = 1;
+        __syncthreads();
+        more = s_more[l % 3] != 0;
     }
     // 3. keys: (confidence desc, depth asc, index asc); 0 = not a candidate.
-    //    Each wave sorts its own candidates' keys; a key among the first N-1
-    //    of its wave's list takes its rank from its place there plus, by
-    //    binary search, the keys above it in the other waves' first N-1.
     const int w = tid / kWave, lane = tid & (kWave - 1);
-    unsigned long long* wk = wkeys[w];
+    const int kept_max = N - 1;
+    unsigned long long key[kCandPerThread];
+    unsigned long long kmax = 0ull;
 #pragma unroll
     for (int j = 0; j < kCandPerThread; ++j) {
         const int i = j * kBlock + tid;
-        wk[lane * kCandPerThread + j] =
-            (i > 0 && ready[i]) ? ((unsigned long long)conf_bits(score[i]) << 32) |
-                                      ((unsigned long long)(0xffff - depth[i]) << 16) |
-                                      (unsigned long long)(0xffff - i)
-                                : 0ull;
+        key[j] = (i > 0 && my_rdy[j]) ? ((unsigned long long)conf_bits(my_sc[j]) << 32) |
+                                            ((unsigned long long)(0xffff - my_dep[j]) << 16) |
+                                            (unsigned long long)(0xffff - i)
+                                      : 0ull;
+        kmax = key[j] > kmax ? key[j] : kmax;
     }
-    wave_sort_desc(wk, kWave * kCandPerThread);
-    const int kept_max = N - 1;
     if (tid < 64) top[tid] = 0ull;
+    // Threshold path: in each wave the ceil((N-1)/4)-th largest confidence
+    // among its threads' best keys is reached by that many keys, so the
+    // smallest of the four waves' values is reached by N-1 keys, and no key
+    // below it is kept. The keys at or above it are ranked by counting. With
+    // 0 (too few confidences above zero) every key competes.
+    const uint32_t tw = wave_jth_largest<0>((uint32_t)(kmax >> 32), (kept_max + kWavesPerBlock - 1) / kWavesPerBlock);
+    if (lane == 0) s_bound[w] = tw;
+    if (tid == 0) s_sel = 0;
     __syncthreads();
-    for (int p = lane; p < kept_max; p += kWave) {
-        const unsigned long long key = wk[p];
-        if (key != 0ull) {
-            int rank = p;
-            for (int o = 0; o < kWavesPerBlock; ++o)
-                if (o != w) rank += count_above(wkeys[o], kept_max, key);
-            if (rank < kept_max) top[rank] = key;
+    uint32_t tb = s_bound[0];
+#pragma unroll
+    for (int i = 1; i < kWavesPerBlock; ++i) tb = min(tb, s_bound[i]);
+#pragma unroll
+    for (int j = 0; j < kCandPerThread; ++j) {
+        if (key[j] != 0ull && (uint32_t)(key[j] >> 32) >= tb) {
+            const int at = atomicAdd(&s_sel, 1);
+            if (at < kSelCap) sel[at] = key[j];
         }
     }
     __syncthreads();
+    const int C = s_sel;
+    if (C <= kSelCap) {
+        // pad to a multiple of 8 with keys that beat nothing
+        const int C8 = (C + 7) & ~7;
+        if (tid >= C && tid < C8) sel[tid] = 0ull;
+        __syncthreads();
+        if (tid < C) {
+            const unsigned long long k = sel[tid];
+            int rank = 0;
+            for (int j = 0; j < C8; j += 8) {
+                unsigned long long k8[8];
+#pragma unroll
+                for (int q = 0; q < 8; ++q) k8[q] = sel[j + q];
+#pragma unroll
+                for (int q = 0; q < 8; ++q) rank += k8[q] > k ? 1 : 0;
+            }
+            if (rank < kept_max) top[rank] = k;
+        }
+        __syncthreads();
+    } else {
+        // Too many keys reach the bound (ties): each wave sorts its own
+        // candidates' keys; a key among the first N-1 of its wave's list
+        // takes its rank from its place there plus, by binary search, the
+        // keys above it in the other waves' first N-1.
+        unsigned long long* wk = wkeys[w];
+#pragma unroll
+        for (int j = 0; j < kCandPerThread; ++j) wk[lane * kCandPerThread + j] = key[j];
+        wave_sort_desc(wk, kWave * kCandPerThread);
+        __syncthreads();
+        for (int p = lane; p < kept_max; p += kWave) {
+            const unsigned long long k = wk[p];
+            if (k != 0ull) {
+                int rank = p;
+                for (int o2 = 0; o2 < kWavesPerBlock; ++o2)
+                    if (o2 != w) rank += count_above(wkeys[o2], kept_max, k);
+                if (rank < kept_max) top[rank] = k;
+            }
+        }
+        __syncthreads();
+    }
     // 4. the first N-1 keys are the kept nodes, numbered in order
     if (tid < kept_max && top[tid] != 0ull) node_of[0xffff - (int)(top[tid] & 0xffffull)] = tid + 1;
     __syncthreads();
@@ -142,9 +208,9 @@ __global__ __launch_bounds__(kBlock) void k_rerank_tree(
             const unsigned long long key = top[tid - 1];
             if (key != 0ull) {
                 cand = 0xffff - (int)(key & 0xffffull);
-                tok = cand_token[o + cand];
+                tok = tok_s[cand];
                 pn = node_of[par[cand]];
-                dep = depth[cand];
+                dep = lvl[cand];
                 sc = score[cand];
                 anc = 1ull << tid;
                 for (int c = par[cand]; c > 0; c = par[c]) anc |= 1ull << node_of[c];
@@ -162,10 +228,9 @@ __global__ __launch_bounds__(kBlock) void k_rerank_tree(
         node_anc[on + tid] = anc;
         if (node_cand) node_cand[on + tid] = cand;
     }
-    if (tid == 0) {
-        int k = 0;
-        while (k < kept_max && top[k] != 0ull) ++k;
-        n_nodes[b] = 1 + k;
+    if (tid < kWave) {               // the kept keys fill top[0 .. k): count them
+        const unsigned long long kb = __ballot(tid < kept_max && top[tid] != 0ull);
+        if (tid == 0) n_nodes[b] = 1 + __popcll(kb);
     }
 }
 

@@ -829,20 +829,6 @@ constexpr int kTileVecs = 16;                   // 16-byte vectors per thread
 constexpr int kTileSeg = 128;                   // candidates per wave (LDS segment)
 static_assert(kTileVecs <= 32 && kTileSeg % 8 == 0, "vector mask bits; 8-key reads");
 
-// The j-th largest (from 1) of the wave's 64 keys, bits LO and up (the rest
-// 0), 0 when fewer than j keys are nonzero: the largest r that at least j
-// keys reach, built bit by bit from the top.
-template <int LO>
-__device__ __forceinline__ uint32_t wave_jth_largest(uint32_t key, int j) {
-    uint32_t r = 0u;
-#pragma unroll
-    for (int bit = 31; bit >= LO; --bit) {
-        const uint32_t c = r | (1u << bit);
-        if (__popcll(__ballot(key >= c)) >= j) r = c;
-    }
-    return r;
-}
-
 // Vector k of v for a lane-varying k (a select chain, no indexed registers).
 __device__ __forceinline__ uint4 pick_vec(const uint4 (&v)[kTileVecs], int k) {
     uint4 x = v[0];

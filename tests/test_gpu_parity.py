@@ -639,6 +639,41 @@ def test_rerank_tree_matches_oracle(M, layers, topk, N):
     np.testing.assert_array_equal(out["anc_mask"].cpu().numpy().view(np.uint64), ref["anc_mask"])
 
 
+def test_rerank_tree_ties_and_short_lists():
+    """Sequence 0: a full 5-ary tree of four levels with every probability
+    0.2, so whole levels tie in confidence and more candidates reach the
+    selection bound than it ranks at once (the sort path). Sequence 1: 20
+    candidates, fewer than N - 1, some with probability 0 (every candidate
+    competes). Sequences 2-3: random expansions (the threshold path)."""
+    N, M, B = 64, 1024, 4
+    rng = np.random.default_rng(12)
+    par, tok, prob, n = _eagle2_candidates(rng, B, M, 6, 8)
+    par[0:2], tok[0:2], prob[0:2], n[0:2] = 0, 0, 0.0, 0
+    cand = [(-1, 1.0)]
+    level = [0]
+    for _ in range(4):
+        nxt = []
+        for c in level:
+            for _ in range(5):
+                cand.append((c, 0.2))
+                nxt.append(len(cand) - 1)
+        level = nxt
+    n[0] = len(cand)
+    for i, (p, q) in enumerate(cand):
+        par[0, i], prob[0, i], tok[0, i] = p, q, 1000 + i
+    n[1] = 20
+    for i in range(1, 20):
+        par[1, i], prob[1, i], tok[1, i] = (i - 1) // 3, (0.0 if i % 4 == 0 else 0.3), 50 + i
+    par[0, 0] = par[1, 0] = -1
+    ref = oracle.rerank_tree(par, tok, prob, n, B, M, N)
+    t = lambda a: torch.as_tensor(a, device="cuda")
+    out = sd.rerank_tree(t(par), t(tok), t(prob), t(n), N)
+    for key in ("token", "parent", "depth", "score", "cand", "n_nodes"):
+        np.testing.assert_array_equal(out[key].cpu().numpy(), ref[key], err_msg=key)
+    np.testing.assert_array_equal(out["anc_mask"].cpu().numpy().view(np.uint64), ref["anc_mask"])
+    assert ref["n_nodes"][0] == N and ref["n_nodes"][1] == 20
+
+
 def test_rerank_tree_then_walks():
     """The re-ranked tree has the built tree's layout, so both walks take it:
     target rows that favour each node's children, argmax and sampled walks
