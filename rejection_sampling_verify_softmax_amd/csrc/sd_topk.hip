@@ -1144,6 +1144,16 @@ __device__ __forceinline__ unsigned long long shift_pick64(unsigned long long v,
 // (every prefix before a tree node is itself in C). Returns false, having
 // written nothing, when the list is shorter or C exceeds kBuildCap; the pop
 // loop then builds the tree.
+// The pop order of the threshold path's members as one 64-bit key, larger
+// first: score (positive, so its bits order it), then lower depth, then lower
+// slot. Within a depth the members are enumerated in rank-tuple order (the
+// children of a level by parent slot, then by their own rank), so slot order
+// there is the tuple order.
+__device__ __forceinline__ unsigned long long pop_key(float Q, int depth, int slot) {
+    return ((unsigned long long)__float_as_uint(Q) << 32) | ((unsigned long long)(31 - depth) << 16) |
+           (unsigned long long)(0xffff - slot);
+}
+
 constexpr int kBuildThreads = 256;
 constexpr int kBuildCap = 256;
 constexpr int kBuildWaves = kBuildThreads / kWave;
@@ -1159,7 +1169,7 @@ __device__ bool build_by_threshold(const float (*qv)[64], const int (*tv)[64], c
                                    unsigned long long* __restrict__ anc_out, int32_t* __restrict__ nn_out) {
     __shared__ float cQ[kBuildCap];
     __shared__ int cInfo[kBuildCap];            // depth | rank << 5 | (parent candidate + 1) << 11
-    __shared__ unsigned long long cW0[kBuildCap], cW1[kBuildCap];
+    __shared__ unsigned long long cK[kBuildCap];  // pop-order key, larger first
     __shared__ int cRank[kBuildCap];
     __shared__ int sOff[kBuildCap + 1];
     __shared__ int wsum[kBuildWaves];
@@ -1176,8 +1186,7 @@ __device__ bool build_by_threshold(const float (*qv)[64], const int (*tv)[64], c
     if (tid < N - 1) {
         cQ[tid] = 1.0f * qv[0][tid];
         cInfo[tid] = cinfo(1, tid, 0);
-        cW0[tid] = (unsigned long long)tid << 54;   // rank slot of depth 1
-        cW1[tid] = 0ull;
+        cK[tid] = pop_key(cQ[tid], 1, tid);
     }
     int nc = N - 1, lo = 0, hi = N - 1, maxd = 1;
     for (int d = 1; d < K; ++d) {               // members at depth d get children at depth d+1
@@ -1219,38 +1228,31 @@ __device__ bool build_by_threshold(const float (*qv)[64], const int (*tv)[64], c
                 else z = mid;
             }
             const int ip = lo + a, sr = j - sOff[a], slot = nc + j;
-            cQ[slot] = cQ[ip] * qv[d][sr];
+            const float Qc = cQ[ip] * qv[d][sr];
+            cQ[slot] = Qc;
             cInfo[slot] = cinfo(d + 1, sr, ip + 1);
-            Prefix t;
-            t.Q = 0.f;
-            t.meta = 0;
-            t.w0 = cW0[ip];
-            t.w1 = cW1[ip];
-            set_rank(t, d, sr);
-            cW0[slot] = t.w0;
-            cW1[slot] = t.w1;
+            cK[slot] = pop_key(Qc, d + 1, slot);
         }
         lo = nc;
         hi = nc + total;
         nc += total;
         maxd = d + 1;
     }
+    // pad to a multiple of 8 with keys after every member, so the counting
+    // below reads 8 keys per wait
+    const int nc8 = (nc + 7) & ~7;
+    if (tid >= nc && tid < nc8) cK[tid] = 0ull;
     __syncthreads();
     // ranks by counting under the pop order
     for (int i = tid; i < nc; i += kBuildThreads) {
-        Prefix me;
-        me.Q = cQ[i];
-        me.meta = cInfo[i] & 31;
-        me.w0 = cW0[i];
-        me.w1 = cW1[i];
+        const unsigned long long me = cK[i];
         int r = 0;
-        for (int j = 0; j < nc; ++j) {
-            Prefix o;
-            o.Q = cQ[j];
-            o.meta = cInfo[j] & 31;
-            o.w0 = cW0[j];
-            o.w1 = cW1[j];
-            r += prefix_before(o, me) ? 1 : 0;
+        for (int j = 0; j < nc8; j += 8) {
+            unsigned long long k8[8];
+#pragma unroll
+            for (int q = 0; q < 8; ++q) k8[q] = cK[j + q];
+#pragma unroll
+            for (int q = 0; q < 8; ++q) r += k8[q] > me ? 1 : 0;
         }
         cRank[i] = r;
     }
