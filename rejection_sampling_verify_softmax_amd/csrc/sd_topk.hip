@@ -1495,12 +1495,17 @@ __global__ __launch_bounds__(kShortThreads) void k_topk_short(const typename E::
         }
         return c;
     };
-    // 1. the thread's largest value (fmaxf skips NaN; NaN only if all are)
+    // 1. each vector's and the thread's largest value (fmaxf skips NaN; NaN
+    // only if all are)
+    float vmax[kShortVecs];
     float m = NAN;
 #pragma unroll
-    for (int i = 0; i < kShortVecs; ++i)
+    for (int i = 0; i < kShortVecs; ++i) {
+        vmax[i] = NAN;
 #pragma unroll
-        for (int e = 0; e < EV; ++e) m = fmaxf(m, raw_elem<E>(v[i], e));
+        for (int e = 0; e < EV; ++e) vmax[i] = fmaxf(vmax[i], raw_elem<E>(v[i], e));
+        m = fmaxf(m, vmax[i]);
+    }
     // 2. each wave's kShortRth-th largest thread maximum, as order-preserving
     // bits (0: none); each round retires every thread at the round's maximum
     uint32_t mine = (m == m) ? ordered_bits(m) : 0u, rth = 0u;
@@ -1519,20 +1524,46 @@ __global__ __launch_bounds__(kShortThreads) void k_topk_short(const typename E::
     const float t = tb == 0u ? -INFINITY : from_ordered(tb);
     // 3. the candidates (value >= t) to LDS in one pass, placed by an LDS
     // counter (their order does not matter: ranks come from the keys); the
-    // count tells whether they fit
+    // count tells whether they fit. Only the vectors whose maximum reaches t
+    // are visited, one per lane per round (lowest first), and their passing
+    // elements one per lane per step, the wave's slots from one atomic.
     {
         fresh();
+        uint32_t vm = 0u;
 #pragma unroll
-        for (int i = 0; i < kShortVecs; ++i) {
+        for (int i = 0; i < kShortVecs; ++i) vm |= vmax[i] >= t ? (1u << i) : 0u;
+        while (__ballot(vm != 0u)) {
+            const int i = vm != 0u ? __builtin_ctz(vm) : 0;
+            uint4 x = v[0];
 #pragma unroll
-            for (int e = 0; e < EV; ++e) {
-                const float x = raw_elem<E>(v[i], e);
-                if (x >= t) {
-                    const int at = atomicAdd(&s_total, 1);
-                    if (at < kShortCap) cand[at] = make_key(x, jb + i * kShortThreads * EV + e);
+            for (int k = 1; k < kShortVecs; ++k) {
+                const bool sel = i == k;
+                x.x = sel ? v[k].x : x.x;
+                x.y = sel ? v[k].y : x.y;
+                x.z = sel ? v[k].z : x.z;
+                x.w = sel ? v[k].w : x.w;
+            }
+            uint32_t em = 0u;
+            if (vm != 0u) {
+#pragma unroll
+                for (int e = 0; e < EV; ++e) em |= raw_elem<E>(x, e) >= t ? (1u << e) : 0u;
+            }
+            vm &= vm - 1u;
+            while (true) {
+                const bool has = em != 0u;
+                const unsigned long long bal = __ballot(has);
+                if (bal == 0ull) break;
+                int base = 0;
+                if (lane == 0) base = atomicAdd(&s_total, (int)__popcll(bal));
+                base = __shfl(base, 0, kWave);
+                if (has) {
+                    const int e = __builtin_ctz(em);
+                    em &= em - 1u;
+                    const int at = base + (int)__builtin_amdgcn_mbcnt_hi(
+                                              (uint32_t)(bal >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)bal, 0u));
+                    if (at < kShortCap) cand[at] = make_key(raw_elem<E>(x, e), jb + i * kShortThreads * EV + e);
                 }
             }
-            __builtin_amdgcn_sched_barrier(0);
         }
     }
     __syncthreads();
