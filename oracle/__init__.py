@@ -72,6 +72,12 @@ def _load():
     lib.orc_compact_kv.restype = None
     lib.orc_rerank_tree.argtypes = [P, P, P, P, I, I, I, P, P, P, P, P, P, P]
     lib.orc_rerank_tree.restype = None
+    lib.orc_check_chain.argtypes = [P, P, P, P, P, I, I, I, D, I, D, P, P, P, P, I]
+    lib.orc_check_chain.restype = None
+    lib.orc_check_tree_sampled.argtypes = [P, P, P, P, P, I, I, I, D, I, D, P, P, P, P, I]
+    lib.orc_check_tree_sampled.restype = None
+    lib.orc_check_select_len.argtypes = [P, I, I, ctypes.c_float, D, P, P]
+    lib.orc_check_select_len.restype = None
     _lib = lib
     return lib
 
@@ -282,3 +288,57 @@ def rerank_tree(cand_parent, cand_token, cand_prob, n_cand, B, M, N):
                             _ptr(out["score"]), _ptr(out["anc_mask"]), _ptr(out["cand"]),
                             _ptr(out["n_nodes"]))
     return out
+
+
+CHECK_A = 1
+CHECK_NEXT = 2
+
+
+def check_chain(target, draft, tokens, uniforms, cu, B, K_max, V, temperature, A, nxt, top_k=0,
+                tol=MARGIN_REL, threads=None):
+    """Validity of another implementation's (A, next) per sequence, within the
+    rounding slack tol (see orc_check_chain). Returns (valid bits [B], status
+    bits the chain rule raises at that A [B])."""
+    t = _f32(target).reshape(-1)
+    d = _f32(draft).reshape(-1)
+    y = _i32(tokens).reshape(-1)
+    u = _f32(uniforms).reshape(-1)
+    c = None if cu is None else _i32(cu)
+    a = _i32(A)
+    n = _i32(nxt)
+    valid = np.zeros(B, np.int32)
+    st = np.zeros(B, np.int32)
+    _load().orc_check_chain(_ptr(t), _ptr(d), _ptr(y), _ptr(u), _ptr(c), int(B), int(K_max), int(V),
+                            _t32(temperature), int(top_k), float(tol), _ptr(a), _ptr(n), _ptr(valid),
+                            _ptr(st), int(threads or default_threads()))
+    return valid, st
+
+
+def check_tree_sampled(target, token, parent, n_nodes, uniforms, B, N, V, temperature, path, A, nxt,
+                       top_k=0, tol=MARGIN_REL, threads=None):
+    """1 per sequence whose sampled walk (path, A, next) is a valid walk within
+    the rounding slack tol (see orc_check_tree_sampled)."""
+    t = _f32(target).reshape(-1)
+    tok = _i32(token).reshape(-1)
+    par = _i32(parent).reshape(-1)
+    nn = _i32(n_nodes)
+    u = _f32(uniforms).reshape(-1)
+    pa = _i32(path).reshape(-1)
+    a = _i32(A)
+    n = _i32(nxt)
+    valid = np.zeros(B, np.int32)
+    _load().orc_check_tree_sampled(_ptr(t), _ptr(tok), _ptr(par), _ptr(nn), _ptr(u), int(B), int(N),
+                                   int(V), ctypes.c_double(temperature), int(top_k),
+                                   ctypes.c_double(tol), _ptr(pa), _ptr(a), _ptr(n), _ptr(valid),
+                                   int(threads or default_threads()))
+    return valid
+
+
+def check_select_len(conf, B, K, cost, k, tol=MARGIN_REL):
+    """1 per sequence whose verify length k is the rule's choice within slack tol."""
+    c = _f32(conf).reshape(-1)
+    kk = _i32(k)
+    valid = np.zeros(B, np.int32)
+    _load().orc_check_select_len(_ptr(c), int(B), int(K), ctypes.c_float(cost), float(tol), _ptr(kk),
+                                 _ptr(valid))
+    return valid

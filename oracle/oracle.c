@@ -709,3 +709,169 @@ void orc_select_len_table(const float* conf, int B, int K, const float* cost, in
         for (int b = 0; b < B; ++b) cu_sel[b + 1] = cu_sel[b] + k_sel[b];
     }
 }
+
+/* ------------------------------------------------------------------------ */
+/* Validity checks of another implementation's results where the oracle's  */
+/* own decision sits at a rounding margin. They re-evaluate the definitions */
+/* above in fp64 on this oracle's p and q, at the decision the other side   */
+/* took, and accept it when it is one of the results that rounding allows.  */
+/* ------------------------------------------------------------------------ */
+
+/*
+ * 1 when token j is a valid inverse-CDF draw from weights w (token-id order)
+ * at the scaled point x, allowing a slack of tol on the point: w_j > 0,
+ * C_{j-1} <= x + tol and C_j > x - tol, with C the running sum of w.
+ */
+static int orc_cdf_draw_ok(const double* w, int V, int j, double x, double tol) {
+    if (j < 0 || j >= V || !(w[j] > 0.0)) return 0;
+    double C = 0.0;
+    for (int t = 0; t < j; ++t) C += w[t];
+    return C <= x + tol && C + w[j] > x - tol;
+}
+
+/*
+ * Chain result check [SD §1: the ratio test alpha = min(1, p/q), nothing kept
+ * after the first rejection, the correction from the normalised [p - q]+, the
+ * extra token from p]. For sequence b (layout as orc_verify_chain, T > 0) and
+ * the pair (A_in[b], next_in[b]) to check:
+ *   bit 1 of valid_out[b]: 0 <= A <= k, every position i < A passes the test
+ *          with slack, p_i(y_i) > 0 and u_i q_i(y_i) <= p_i(y_i) (1 + tol),
+ *          and position A < k fails it with slack: the token or a row is bad,
+ *          p_A(y_A) == 0, or u_A q_A(y_A) > p_A(y_A) (1 - tol);
+ *   bit 2: next is the draw the chain rule makes at that A, within slack:
+ *          the final row's weights w (the residual max(p_A - q_A, 0) with
+ *          total R > 0 and point u_k R; p_A at u_k if R == 0; p_k at u_k
+ *          when A == k), checked by orc_cdf_draw_ok with tol times the
+ *          total; next == -1 exactly when that row is non-finite.
+ * status_out[b] receives the status bits the chain rule raises at that A.
+ */
+void orc_check_chain(const float* target, const float* draft, const int32_t* tokens,
+                     const float* uniforms, const int32_t* cu, int B, int K_max, int V, double T,
+                     int top_k, double tol, const int32_t* A_in, const int32_t* next_in,
+                     int32_t* valid_out, int32_t* status_out, int nthreads) {
+#pragma omp parallel for schedule(dynamic, 1) num_threads(nthreads > 0 ? nthreads : 1)
+    for (int b = 0; b < B; ++b) {
+        int d0 = cu ? cu[b] : b * K_max;
+        int k = cu ? cu[b + 1] - cu[b] : K_max;
+        int t0 = d0 + b;
+        int A = A_in[b], nx = next_in[b];
+        int valid = 0, status = 0;
+        double* p = (double*)malloc(sizeof(double) * (size_t)V);
+        double* q = (double*)malloc(sizeof(double) * (size_t)V);
+        if (A >= 0 && A <= k) {
+            int a_ok = 1;
+            for (int i = 0; i <= A && i < k; ++i) {
+                int vp = orc_transform_row(target + (size_t)(t0 + i) * V, V, T, top_k, p);
+                int vq = orc_transform_row(draft + (size_t)(d0 + i) * V, V, T, top_k, q);
+                int y = tokens[d0 + i];
+                int yok = (y >= 0 && y < V);
+                double py = yok ? p[y] : 0.0, qy = yok ? q[y] : 0.0;
+                double u = (double)uniforms[t0 + i];
+                int good = vp && vq && yok;
+                if (!yok) status |= ORC_BAD_TOKEN;
+                if (!vp || !vq) status |= ORC_NONFINITE;
+                if (i < A) {
+                    if (!(good && py > 0.0 && u * qy <= py * (1.0 + tol))) a_ok = 0;
+                } else {
+                    if (good && py > 0.0 && u * qy <= py * (1.0 - tol)) a_ok = 0;
+                }
+            }
+            if (a_ok) valid |= 1;
+            /* the final draw at this A */
+            double u_fin = (double)uniforms[t0 + k];
+            int row = t0 + A;
+            int vp = orc_transform_row(target + (size_t)row * V, V, T, top_k, p);
+            if (A == k && !vp) status |= ORC_NONFINITE;
+            if (!vp) {
+                if (nx == -1) valid |= 2;
+            } else if (A < k) {
+                int vq = orc_transform_row(draft + (size_t)(d0 + A) * V, V, T, top_k, q);
+                double R = 0.0;
+                for (int t = 0; t < V; ++t) {
+                    double d = p[t] - (vq ? q[t] : 0.0);
+                    q[t] = d > 0.0 ? d : 0.0;
+                    R += q[t];
+                }
+                if (R > 0.0 ? orc_cdf_draw_ok(q, V, nx, u_fin * R, tol * R)
+                            : orc_cdf_draw_ok(p, V, nx, u_fin, tol))
+                    valid |= 2;
+            } else if (orc_cdf_draw_ok(p, V, nx, u_fin, tol)) {
+                valid |= 2;
+            }
+        }
+        valid_out[b] = valid;
+        if (status_out) status_out[b] = status;
+        free(p); free(q);
+    }
+}
+
+/*
+ * Sampled tree walk check [SD §5 DDTree, the walk of orc_verify_tree_sampled].
+ * Follows the given path (path_in [B, N], A_in, next_in) from the root: at
+ * each visited node the committed token (the next node's token, or next at
+ * the end) must be a valid draw of that node's transformed row at its uniform
+ * (orc_cdf_draw_ok with slack tol), each path entry must be a child of the
+ * node before it carrying that token, the final token must have no child at
+ * the last node, and the path entries past A must be -1. A non-finite row
+ * ends the walk with next == -1. valid_out[b] = 1 when all hold.
+ */
+void orc_check_tree_sampled(const float* target, const int32_t* node_token,
+                            const int32_t* node_parent, const int32_t* n_nodes,
+                            const float* uniforms, int B, int N, int V, double T, int top_k,
+                            double tol, const int32_t* path_in, const int32_t* A_in,
+                            const int32_t* next_in, int32_t* valid_out, int nthreads) {
+#pragma omp parallel for schedule(dynamic, 1) num_threads(nthreads > 0 ? nthreads : 1)
+    for (int b = 0; b < B; ++b) {
+        const int32_t* tok = node_token + (size_t)b * N;
+        const int32_t* par = node_parent + (size_t)b * N;
+        const int32_t* path = path_in + (size_t)b * N;
+        int nn = n_nodes[b];
+        int A = A_in[b];
+        int ok = A >= 0 && A < N;
+        double* p = (double*)malloc(sizeof(double) * (size_t)V);
+        for (int i = (ok ? A : N); i < N; ++i)
+            if (path[i] != -1) ok = 0;
+        int node = 0;
+        for (int j = 0; ok && j <= A; ++j) {
+            int valid = orc_transform_row(target + ((size_t)b * N + node) * V, V, T, top_k, p);
+            double u = (double)uniforms[(size_t)b * N + node];
+            if (!valid) {
+                ok = (j == A && next_in[b] == -1);
+                break;
+            }
+            if (j < A) {
+                int c = path[j];
+                if (c < 1 || c >= nn || par[c] != node) { ok = 0; break; }
+                if (!orc_cdf_draw_ok(p, V, tok[c], u, tol)) ok = 0;
+                node = c;
+            } else {
+                int g = next_in[b];
+                if (!orc_cdf_draw_ok(p, V, g, u, tol)) ok = 0;
+                for (int c = 1; c < nn && ok; ++c)
+                    if (par[c] == node && tok[c] == g) ok = 0;
+            }
+        }
+        valid_out[b] = ok;
+        free(p);
+    }
+}
+
+/*
+ * Length choice check [SD §5 DSpark, the rule of orc_select_len]: k_in[b] is
+ * valid when every s_j, j <= k, exceeds cost - tol and s_{k+1} (if any) does
+ * not exceed cost + tol, with s the fp32 running product of the confidences.
+ */
+void orc_check_select_len(const float* conf, int B, int K, float cost, double tol,
+                          const int32_t* k_in, int32_t* valid_out) {
+    for (int b = 0; b < B; ++b) {
+        int k = k_in[b];
+        int ok = k >= 0 && k <= K;
+        float s = 1.0f;
+        for (int j = 1; ok && j <= K; ++j) {
+            s = s * conf[(size_t)b * K + (j - 1)];
+            if (j <= k && !((double)s > (double)cost - tol)) ok = 0;
+            if (j == k + 1 && (double)s > (double)cost + tol) ok = 0;
+        }
+        valid_out[b] = ok;
+    }
+}

@@ -913,3 +913,170 @@ def test_rerank_brute_force_and_bad_candidates():
     rr = oracle.rerank_tree(par[None], tok[None], prob[None], [7], 1, 7, 10)
     assert rr["n_nodes"][0] == 3
     np.testing.assert_array_equal(rr["cand"][0, :3], [0, 1, 2])
+
+
+# --------------------------------------------------------------------------
+# Tie order of the best-first tree across depths ([SD §5 DDTree])
+# --------------------------------------------------------------------------
+
+def test_tree_cross_depth_ties_golden():
+    """Hand-derived numbering where depth-1 and depth-2 prefixes tie in Q
+    (tests/golden/tree_cross_depth_ties.json states the derivation)."""
+    with open(os.path.join(GOLD, "tree_cross_depth_ties.json"), encoding="utf-8") as f:
+        g = json.load(f)
+    m = np.array(g["marginals"], np.float32)[None]
+    out = oracle.build_tree(m, 1, g["K"], g["V"], g["N"])
+    ex = g["expected"]
+    assert int(out["n_nodes"][0]) == ex["n_nodes"]
+    for key in ("token", "parent", "depth", "score"):
+        np.testing.assert_array_equal(out[key][0], np.array(ex[key]).astype(out[key].dtype), err_msg=key)
+    np.testing.assert_array_equal(out["anc_mask"][0].astype(np.int64), ex["anc_mask"])
+
+
+def _tied_marginals(kind, K, V, rng):
+    if kind == "uniform":
+        return np.full((K, V), 1.0 / V, np.float32)
+    if kind == "pairs":                 # every value appears twice in a row
+        half = special.softmax(rng.normal(0, 1.0, (K, (V + 1) // 2)), axis=-1) / 2
+        return np.repeat(half, 2, axis=1)[:, :V].astype(np.float32)
+    if kind == "certain":               # rows with a q = 1 entry: a child ties its parent
+        m = special.softmax(rng.normal(0, 1.0, (K, V)), axis=-1).astype(np.float32)
+        m[1::2] = 0.0
+        m[1::2, 0] = 1.0
+        return m
+    raise ValueError(kind)
+
+
+@pytest.mark.parametrize("kind", ["uniform", "pairs", "certain"])
+@pytest.mark.parametrize("N", [5, 13, 40])
+def test_rerank_of_the_full_trie_with_ties_is_the_ddtree(kind, N):
+    # with tied marginals the two orders must also agree on every tie across
+    # depths: (Q desc, depth asc, rank tuple asc) on the trie is the
+    # re-ranking's (confidence desc, depth asc, BFS index asc)
+    rng = np.random.default_rng(71 + N)
+    K, V = 4, 3
+    m = _tied_marginals(kind, K, V, rng)
+    par, tok, prob = _trie_candidates(m)
+    M = len(par)
+    rr = oracle.rerank_tree(par[None], tok[None], prob[None], [M], 1, M, N)
+    bt = oracle.build_tree(m[None], 1, K, V, N)
+    for key in ("token", "parent", "depth", "score", "anc_mask", "n_nodes"):
+        np.testing.assert_array_equal(rr[key], bt[key], err_msg=key)
+
+
+# --------------------------------------------------------------------------
+# Validity checks used where the oracle's decision sits at a rounding margin
+# --------------------------------------------------------------------------
+
+def _chain_case(rng, B, K, V, sig=2.0, noise=0.7):
+    d = (rng.standard_normal((B * K, V)) * sig).astype(np.float32)
+    t = np.zeros((B * (K + 1), V), np.float32)
+    for b in range(B):
+        t[b * (K + 1):b * (K + 1) + K] = d[b * K:(b + 1) * K] + rng.standard_normal((K, V)) * noise
+        t[b * (K + 1) + K] = rng.standard_normal(V) * sig
+    y = np.array([sample_from(rng, special.softmax(d[r].astype(np.float64)), 1)[0]
+                  for r in range(B * K)], np.int32)
+    u = grid_u(rng, B * (K + 1))
+    return t, d, y, u
+
+
+def test_check_chain_accepts_the_oracle_and_rejects_planted_mistakes():
+    rng = np.random.default_rng(41)
+    B, K, V = 300, 4, 40
+    t, d, y, u = _chain_case(rng, B, K, V)
+    ref = oracle.verify_chain(t, d, y, u, None, B, K, V, 1.0)
+    valid, st = oracle.check_chain(t, d, y, u, None, B, K, V, 1.0, ref["A"], ref["next"])
+    assert (valid == 3).all()
+    np.testing.assert_array_equal(st, ref["status"])
+    clear = ref["margin"] == 0
+    # A one position later than a clear rejection, or one earlier than a clear
+    # accept, fails the accept bits
+    later = ref["A"] < K
+    v2, _ = oracle.check_chain(t, d, y, u, None, B, K, V, 1.0, np.minimum(ref["A"] + 1, K), ref["next"])
+    assert ((v2 & oracle.CHECK_A) == 0)[later & clear].all()
+    earlier = ref["A"] > 0
+    v3, _ = oracle.check_chain(t, d, y, u, None, B, K, V, 1.0, np.maximum(ref["A"] - 1, 0), ref["next"])
+    assert ((v3 & oracle.CHECK_A) == 0)[earlier & clear].all()
+    # a neighbouring token is not the draw at that point
+    for shift in (1, -1):
+        nx = (ref["next"] + shift) % V
+        v4, _ = oracle.check_chain(t, d, y, u, None, B, K, V, 1.0, ref["A"], nx)
+        assert ((v4 & oracle.CHECK_NEXT) == 0)[clear].all()
+        assert (v4 & oracle.CHECK_A).all()
+    # the same with top-k truncation and a packed layout
+    cu = np.concatenate([[0], np.cumsum(rng.integers(0, K + 1, 60))]).astype(np.int32)
+    rows_t = np.concatenate([np.arange(b * (K + 1), b * (K + 1) + cu[b + 1] - cu[b] + 1) for b in range(60)])
+    rows_d = np.concatenate([np.arange(b * K, b * K + cu[b + 1] - cu[b]) for b in range(60)])
+    args = (t[rows_t], d[rows_d], y[rows_d], u[rows_t], cu, 60, K, V, 0.8)
+    r5 = oracle.verify_chain(*args, top_k=5)
+    v5, s5 = oracle.check_chain(*args, r5["A"], r5["next"], top_k=5)
+    assert (v5 == 3).all()
+    np.testing.assert_array_equal(s5, r5["status"])
+    v6, _ = oracle.check_chain(*args, r5["A"], (r5["next"] + 1) % V, top_k=5)
+    assert ((v6 & oracle.CHECK_NEXT) == 0)[r5["margin"] == 0].all()
+
+
+def test_check_chain_takes_either_side_of_a_margin():
+    # the margin cases of test_margin_flags: u*q == p exactly (accepting and
+    # rejecting are both within the slack) and a draw exactly on a CDF step
+    V = 2
+    tgt = np.stack([logits_of([.5, .5]), logits_of([.5, .5])])
+    dft = logits_of([1.0, 0.0])[None]
+    y = np.array([0], np.int32)
+    u = np.array([0.5, 0.3], np.float32)
+    for A, nx in ((1, 0), (0, 1)):
+        v, _ = oracle.check_chain(tgt, dft, y, u, None, 1, 1, V, 1.0, [A], [nx])
+        assert v[0] == 3, (A, nx)
+    # after a rejection the residual [p - q]+ is one-hot at id 1: id 0 is never drawn
+    v, _ = oracle.check_chain(tgt, dft, y, u, None, 1, 1, V, 1.0, [0], [0])
+    assert v[0] == oracle.CHECK_A
+    u = np.array([0.25, 0.5], np.float32)
+    for nx in (0, 1):
+        v, _ = oracle.check_chain(tgt, dft, y, u, None, 1, 1, V, 1.0, [1], [nx])
+        assert v[0] == 3, nx
+    v, _ = oracle.check_chain(tgt, dft, y, u, None, 1, 1, V, 1.0, [0], [1])
+    assert v[0] == oracle.CHECK_NEXT       # u*q = 0.25 < p = 0.5: a rejection is not allowed
+
+
+def test_check_tree_sampled_accepts_the_oracle_and_rejects_planted_mistakes():
+    rng = np.random.default_rng(42)
+    B, K, V, N = 40, 4, 6, 12
+    marg = special.softmax(rng.standard_normal((B, K, V)) * 1.5, axis=2).astype(np.float32)
+    tree = oracle.build_tree(marg, B, K, V, N)
+    target = (rng.standard_normal((B, N, V)) * 1.5).astype(np.float32)
+    u = grid_u(rng, (B, N))
+    ref = oracle.verify_tree_sampled(target, tree["token"], tree["parent"], tree["n_nodes"], u, B, N, V, 1.0)
+    args = (target, tree["token"], tree["parent"], tree["n_nodes"], u, B, N, V, 1.0)
+    assert (oracle.check_tree_sampled(*args, ref["path"], ref["A"], ref["next"]) == 1).all()
+    clear = ref["margin"] == 0
+    bad = oracle.check_tree_sampled(*args, ref["path"], ref["A"], (ref["next"] + 1) % V)
+    assert (bad[clear] == 0).all()
+    # a walk cut one step short names a child's token as the extra token
+    long = ref["A"] > 0
+    cut = ref["path"].copy()
+    A2 = np.maximum(ref["A"] - 1, 0)
+    nx2 = ref["next"].copy()
+    for b in np.nonzero(long)[0]:
+        nx2[b] = tree["token"][b, cut[b, A2[b]]]
+        cut[b, A2[b]] = -1
+    bad = oracle.check_tree_sampled(*args, cut, A2, nx2)
+    assert (bad[long] == 0).all()
+
+
+def test_check_select_len():
+    rng = np.random.default_rng(43)
+    B, K, cost = 400, 8, 0.15
+    conf = rng.beta(5, 2, (B, K)).astype(np.float32)
+    ref = oracle.select_len(conf, B, K, cost)
+    assert (oracle.check_select_len(conf, B, K, cost, ref["k"]) == 1).all()
+    clear = ref["margin"] == 0
+    for shift in (1, -1):
+        k2 = ref["k"] + shift
+        ok = oracle.check_select_len(conf, B, K, cost, k2)
+        inside = (k2 >= 0) & (k2 <= K)
+        assert (ok[clear & inside] == 0).all() and (ok[~inside] == 0).all()
+    # s_1 == cost exactly: k = 0 (the rule) and k = 1 are both within the slack
+    c = np.array([[0.5, 0.9]], np.float32)
+    assert oracle.check_select_len(c, 1, 2, 0.5, [0])[0] == 1
+    assert oracle.check_select_len(c, 1, 2, 0.5, [1])[0] == 1
+    assert oracle.check_select_len(c, 1, 2, 0.5, [2])[0] == 0
