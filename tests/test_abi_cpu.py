@@ -52,8 +52,8 @@ def test_version_and_status_strings(L):
 
 
 def _chain(L, **kw):
-    a = dict(target=1, draft=1, dtype=1, tokens=1, uni=1, cu=None, B=2, K=3, V=100, T=1.0, top_k=0,
-             A=1, nxt=1, probs=None, resid=None, st=None, ws=1, wsb=1 << 30, stream=None)
+    a = dict(target=16, draft=16, dtype=1, tokens=16, uni=16, cu=None, B=2, K=3, V=100, T=1.0, top_k=0,
+             A=16, nxt=16, probs=None, resid=None, st=None, ws=16, wsb=1 << 30, stream=None)
     a.update(kw)
     f = lambda v: None if v is None else ctypes.c_void_p(v)
     return L.sd_verify_chain(f(a["target"]), f(a["draft"]), a["dtype"], f(a["tokens"]), f(a["uni"]),
@@ -81,6 +81,25 @@ def test_workspace_too_small(L):
     assert _chain(L, wsb=16) == 3
 
 
+@pytest.mark.parametrize("which", ["target", "draft", "ws"])
+def test_chain_rejects_misaligned_rows(L, which):
+    # logit rows and the workspace are read in 16-byte vectors: a base pointer
+    # off a 16-byte boundary (a view at an odd storage offset) is refused
+    assert _chain(L, **{which: 16 + 2}) == 1
+    assert _chain(L, **{which: 16 + 8}) == 1
+
+
+def test_other_calls_reject_misaligned_rows(L):
+    v = ctypes.c_void_p
+    one, odd = v(16), v(18)
+    assert L.sd_verify_greedy(odd, 1, one, None, 2, 3, 100, one, one, None, one, 1 << 30, None) == 1
+    assert L.sd_build_tree(odd, 2, 4, 100, 8, one, one, one, one, one, one, one, 1 << 30, None) == 1
+    assert L.sd_verify_tree(odd, 1, one, one, one, 2, 8, 100, one, one, one, one, 1 << 30, None) == 1
+    assert L.sd_verify_tree_sampled(odd, 1, one, one, one, one, 2, 8, 100, ctypes.c_float(1.0), 0, one,
+                                    one, one, None, None, 0, None) == 1
+    assert L.sd_compact_kv(odd, 64, 10, one, one, one, 2, 8, None) == 1
+
+
 def test_workspace_bytes(L):
     import rejection_sampling_verify_softmax_amd as sd
     n = sd.workspace_bytes(sd.OP_CHAIN, 512, 8, 128256, 0)
@@ -98,7 +117,7 @@ def test_workspace_bytes(L):
 
 def test_other_calls_reject_invalid_arguments(L):
     v = ctypes.c_void_p
-    one = v(1)
+    one = v(16)
     # greedy
     assert L.sd_verify_greedy(None, 1, one, None, 2, 3, 100, one, one, None, one, 1 << 30, None) == 1
     assert L.sd_verify_greedy(one, 1, one, None, 2, 3, 100, one, one, None, one, 8, None) == 3
@@ -118,7 +137,7 @@ def test_other_calls_reject_invalid_arguments(L):
 
 
 def test_capped_and_cost_table_reject_invalid_arguments(L):
-    one = ctypes.c_void_p(1)
+    one = ctypes.c_void_p(16)
     f = ctypes.c_float
 
     def capped(cap=one, B=2, K=3, A=one, wsb=1 << 30, T=1.0):
@@ -138,7 +157,7 @@ def test_capped_and_cost_table_reject_invalid_arguments(L):
 
 
 def test_compact_kv_rejects_invalid_arguments(L):
-    one = ctypes.c_void_p(1)
+    one = ctypes.c_void_p(16)
     assert L.sd_compact_kv(None, 64, 10, one, one, one, 2, 8, None) == 1
     assert L.sd_compact_kv(one, 24, 10, one, one, one, 2, 8, None) == 1      # not a multiple of 16
     assert L.sd_compact_kv(one, 0, 10, one, one, one, 2, 8, None) == 1
@@ -149,7 +168,7 @@ def test_compact_kv_rejects_invalid_arguments(L):
 
 
 def test_rerank_tree_rejects_invalid_arguments(L):
-    one = ctypes.c_void_p(1)
+    one = ctypes.c_void_p(16)
 
     def rr(B=2, M=100, N=64, first=one, out=one):
         return L.sd_rerank_tree(first, one, one, one, B, M, N, out, one, one, one, one, None, one, None)
@@ -163,7 +182,7 @@ def test_rerank_tree_rejects_invalid_arguments(L):
 
 
 def test_tree_sampled_rejects_invalid_arguments(L):
-    one = ctypes.c_void_p(1)
+    one = ctypes.c_void_p(16)
     f = ctypes.c_float
 
     def ts(dtype=1, uni=one, B=2, N=8, V=100, T=1.0, top_k=0, out=one, ws=None, wsb=0):
