@@ -23,6 +23,10 @@
  *   streams when their workspaces and outputs are distinct.
  * - Rows are contiguous V-long vectors, row-major, int32 indices everywhere.
  *   Logits are fp32 (SD_F32) or bf16 (SD_BF16, raw 16-bit patterns).
+ * - Alignment. The kernels read logit rows, tree marginals, KV rows and the
+ *   workspace in 16-byte vectors, so those base pointers must be 16-byte
+ *   aligned (any fresh device allocation is); a misaligned one returns
+ *   SD_EINVAL before any HIP call.
  * - Batch layout of the chain calls. Sequence b has k_b draft positions:
  *   k_b = cu[b+1] - cu[b] when a `cu` array ([B+1], non-decreasing, cu[0] = 0)
  *   is given, else k_b = K_max with cu[b] = b*K_max. Draft row i of b is draft

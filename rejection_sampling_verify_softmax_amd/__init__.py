@@ -159,15 +159,18 @@ def _check_rows(t: Optional[torch.Tensor], name: str, rows: int, V: int):
         raise ValueError(f"{name} holds {t.numel()} elements, the batch layout needs {rows * V}")
 
 
-def _check_layout(target, draft, tokens, uniforms, cu, B, K_max, V, greedy, validate):
+def _check_layout(target, draft, tokens, uniforms, cu, B, K_max, V, greedy, validate, stream=None):
     """Size checks of the batch layout (include/sd.h) so that no kernel reads
-    past a tensor. A packed layout costs one device->host read of cu unless
-    validate=False (then the caller vouches for cu)."""
+    past a tensor. For a packed layout the row counts depend on cu, which lives
+    on the device: validate=True reads it on the host after the call's stream
+    has finished its earlier work (a synchronisation); with validate=False
+    (the default) the caller vouches for cu and nothing is read back."""
     if cu is not None:
         if cu.numel() != B + 1:
             raise ValueError(f"cu must hold B+1 = {B + 1} offsets")
         if not validate:
             return
+        (torch.cuda.current_stream() if stream is None else stream).synchronize()
         c = cu.cpu()
         lens = c[1:] - c[:-1]
         if int(c[0]) != 0 or (B > 0 and (int(lens.min()) < 0 or int(lens.max()) > K_max)):
@@ -187,9 +190,10 @@ def verify_chain(target: torch.Tensor, draft: Optional[torch.Tensor], tokens: to
                  cu: Optional[torch.Tensor] = None, B: Optional[int] = None,
                  K_max: Optional[int] = None, want_probs: bool = False,
                  want_resid: bool = False, workspace: Optional[torch.Tensor] = None,
-                 out: Optional[dict] = None, stream=None, validate: bool = True) -> dict:
+                 out: Optional[dict] = None, stream=None, validate: bool = False) -> dict:
     """sd_verify_chain. Dense batch (cu None): target [B*(K+1), V], draft [B*K, V],
-    tokens [B*K] (or [B, K]). Packed batch: pass cu [B+1] (device int32) and K_max.
+    tokens [B*K] (or [B, K]). Packed batch: pass cu [B+1] (device int32) and K_max
+    (required: the call never reads cu back to the host unless validate=True).
     Returns dict with accepted_len, next_token, status (+ probs [R_d, 2], resid)."""
     dev = target.device
     _check(target, "target", device=dev)
@@ -200,7 +204,7 @@ def verify_chain(target: torch.Tensor, draft: Optional[torch.Tensor], tokens: to
         if B is None:
             B = cu.numel() - 1
         if K_max is None:
-            K_max = int((cu[1:] - cu[:-1]).max().item()) if B > 0 else 0
+            raise ValueError("a packed batch (cu given) needs K_max, the largest draft length")
     else:
         if K_max is None:
             K_max = int(tokens.shape[-1]) if tokens.dim() == 2 else None
@@ -213,7 +217,7 @@ def verify_chain(target: torch.Tensor, draft: Optional[torch.Tensor], tokens: to
     if not greedy:
         _check(draft, "draft", target.dtype, dev)
         _check(uniforms, "uniforms", torch.float32, dev)
-    _check_layout(target, draft, tokens, uniforms, cu, B, K_max, V, greedy, validate)
+    _check_layout(target, draft, tokens, uniforms, cu, B, K_max, V, greedy, validate, stream)
     o = out or {}
     A = _get(o, "accepted_len", lambda: torch.empty(B, dtype=torch.int32, device=dev))
     nxt = _get(o, "next_token", lambda: torch.empty(B, dtype=torch.int32, device=dev))
@@ -288,8 +292,9 @@ def verify_chain_capped(target: torch.Tensor, draft: Optional[torch.Tensor], tok
 
 def verify_greedy(target: torch.Tensor, tokens: torch.Tensor, cu: Optional[torch.Tensor] = None,
                   B: Optional[int] = None, K_max: Optional[int] = None,
-                  workspace: Optional[torch.Tensor] = None, stream=None) -> dict:
-    """sd_verify_greedy; same layout as verify_chain."""
+                  workspace: Optional[torch.Tensor] = None, stream=None,
+                  validate: bool = False) -> dict:
+    """sd_verify_greedy; same layout as verify_chain (K_max required with cu)."""
     dev = target.device
     _check(target, "target", device=dev)
     _check(tokens, "tokens", torch.int32, dev)
@@ -299,14 +304,14 @@ def verify_greedy(target: torch.Tensor, tokens: torch.Tensor, cu: Optional[torch
         _check(cu, "cu", torch.int32, dev)
         B = cu.numel() - 1 if B is None else B
         if K_max is None:
-            K_max = int((cu[1:] - cu[:-1]).max().item()) if B > 0 else 0
+            raise ValueError("a packed batch (cu given) needs K_max, the largest draft length")
     else:
         if K_max is None:
             if tokens.dim() != 2:
                 raise ValueError("pass K_max (or 2-D tokens) for a dense batch")
             K_max = int(tokens.shape[-1])
         B = target.numel() // V // (K_max + 1) if B is None else B
-    _check_layout(target, None, tokens, None, cu, B, K_max, V, True, True)
+    _check_layout(target, None, tokens, None, cu, B, K_max, V, True, validate, stream)
     A = torch.empty(B, dtype=torch.int32, device=dev)
     nxt = torch.empty(B, dtype=torch.int32, device=dev)
     st = torch.empty(B, dtype=torch.int32, device=dev)

@@ -20,6 +20,9 @@ bool bad_size(int B, int K_max, int V) {
 }
 bool bad_dtype(sd_dtype_t dt) { return dt != SD_F32 && dt != SD_BF16; }
 bool topk_on(int top_k, int V) { return top_k >= 1 && top_k < V; }
+// Base pointers the kernels read in 16-byte vectors (NULL passes: the
+// separate NULL checks decide whether it is allowed).
+bool misaligned(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) != 0; }
 
 sd_status_t from_hip(hipError_t e) { return e == hipSuccess ? SD_OK : SD_EHIP; }
 
@@ -118,6 +121,7 @@ sd_status_t verify_chain(const void* target_logits, const void* draft_logits, sd
     if (!(temperature >= 0.0f) || !isfinite(temperature)) return SD_EINVAL;
     if (top_k < 0 || top_k > SD_MAX_TOPK) return SD_EINVAL;
     if (!target_logits || !accepted_len || !next_token || !workspace) return SD_EINVAL;
+    if (misaligned(target_logits) || misaligned(draft_logits) || misaligned(workspace)) return SD_EINVAL;
     const bool greedy = temperature == 0.0f;
     if (K_max > 0 && !draft_tokens) return SD_EINVAL;
     if (!greedy && (!uniforms || (K_max > 0 && !draft_logits))) return SD_EINVAL;
@@ -191,6 +195,7 @@ sd_status_t sd_verify_greedy(const void* target_logits, sd_dtype_t dtype,
                              void* hip_stream) {
     if (bad_size(B, K_max, V) || bad_dtype(dtype)) return SD_EINVAL;
     if (!target_logits || !accepted_len || !next_token || !workspace) return SD_EINVAL;
+    if (misaligned(target_logits) || misaligned(workspace)) return SD_EINVAL;
     if (K_max > 0 && !draft_tokens) return SD_EINVAL;
     if (workspace_bytes < sd::greedy_ws_bytes(B, K_max, V, (int)dtype)) return SD_EWORKSPACE;
     return from_hip(sd::launch_greedy(target_logits, (int)dtype, draft_tokens, cu_draft, B, K_max, V,
@@ -208,6 +213,7 @@ sd_status_t sd_build_tree(const float* marginals, int32_t B, int32_t K, int32_t 
     if ((K > 0 && !marginals) || !node_token || !node_parent || !node_depth || !node_score ||
         !node_anc_mask || !n_nodes)
         return SD_EINVAL;
+    if (misaligned(marginals) || misaligned(workspace)) return SD_EINVAL;
     const size_t need = sd::tree_build_ws_bytes(B, K, V, N);
     if (need > 0 && !workspace) return SD_EINVAL;
     if (workspace_bytes < need) return SD_EWORKSPACE;
@@ -226,6 +232,7 @@ sd_status_t sd_verify_tree(const void* target_logits, sd_dtype_t dtype, const in
     if (!target_logits || !node_token || !node_parent || !n_nodes || !path_nodes || !accepted_len ||
         !next_token)
         return SD_EINVAL;
+    if (misaligned(target_logits)) return SD_EINVAL;
     (void)workspace;
     (void)workspace_bytes;
     return from_hip(sd::launch_tree_walk_rows(target_logits, (int)dtype, node_token, node_parent,
@@ -248,6 +255,7 @@ sd_status_t sd_verify_tree_sampled(const void* target_logits, sd_dtype_t dtype,
     if (!target_logits || !node_token || !node_parent || !n_nodes || !path_nodes || !accepted_len ||
         !next_token || (temperature > 0.0f && !uniforms))
         return SD_EINVAL;
+    if (misaligned(target_logits)) return SD_EINVAL;
     (void)workspace;
     (void)workspace_bytes;
     const hipStream_t stream = static_cast<hipStream_t>(hip_stream);
@@ -287,6 +295,7 @@ sd_status_t sd_compact_kv(void* kv, int64_t row_bytes, int64_t n_rows, const int
     if (B < 1 || B > kMaxB || N < 2 || N > SD_MAX_TREE_N) return SD_EINVAL;
     if (row_bytes < 16 || row_bytes % 16 != 0 || n_rows < 1) return SD_EINVAL;
     if (!kv || !row_base || !path_nodes || !accepted_len) return SD_EINVAL;
+    if (misaligned(kv)) return SD_EINVAL;
     return from_hip(sd::launch_compact_kv(kv, row_bytes, n_rows, row_base, path_nodes, accepted_len, B,
                                           N, static_cast<hipStream_t>(hip_stream)));
 }
