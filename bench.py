@@ -148,8 +148,7 @@ def setup_adaptive(torch, sd, wl):
         "mean_k": positions / B, "mean_A": float(A.mean()),
         "rows_streamed": rows1 + rows2, "rows_in_windows": R_t + R_d,
     }
-    cpu = {"case": case, "packed": packed, "k": sel["k"].cpu().numpy(), "cu": sel["cu"].cpu().numpy(),
-           "out": out}
+    cpu = {"leg": cpu_leg_adaptive, "case": case, "packed": packed, "out": out, "sel": sel_out}
     return step, meta, cpu
 
 
@@ -165,13 +164,13 @@ def setup_greedy(torch, sd, wl):
             sd.time_next_stream_pass(*ev)
         t = copies[st["i"] % len(copies)]
         st["i"] += 1
-        sd.verify_greedy(t, case.tokens, B=B, K_max=K, workspace=ws)
+        st["out"] = sd.verify_greedy(t, case.tokens, B=B, K_max=K, workspace=ws)
 
     rows = B * (K + 1)
     meta = {"workload": f"greedy chain verify B={B} K={K} V={V} bf16 (8 rotated input copies)",
             "global_batch": B, "K_max": K, "V": V, "positions_per_step": B * K,
             "kernel": "k_argmax", "kernel_bytes": rows * V * 2, "step_bytes": rows * V * 2 + B * K * 4}
-    return step, meta, None
+    return step, meta, {"leg": cpu_leg_greedy, "case": case, "state": st}
 
 
 def setup_topk(torch, sd, wl):
@@ -179,11 +178,13 @@ def setup_topk(torch, sd, wl):
     B, K, V = case.B, case.K_max, case.V
     ws = torch.empty(sd.workspace_bytes(sd.OP_CHAIN, B, K, V, case.top_k), dtype=torch.uint8, device="cuda")
 
+    st = {}
+
     def step(ev=None):
         if ev is not None:
             sd.time_next_stream_pass(*ev)
-        sd.verify_chain(case.target, case.draft, case.tokens, case.uniforms, case.temperature,
-                        top_k=case.top_k, B=B, K_max=K, workspace=ws, validate=False)
+        st["out"] = sd.verify_chain(case.target, case.draft, case.tokens, case.uniforms, case.temperature,
+                                    top_k=case.top_k, B=B, K_max=K, workspace=ws)
 
     # rows streamed: slots 0-1 of every sequence, the rest only where both
     # first drafts were accepted (as in the adaptive workload)
@@ -199,7 +200,7 @@ def setup_topk(torch, sd, wl):
             "step_bytes": (rows1 + rows2) * V * 2 + B * K * 4 + B * (K + 1) * 4,
             "mean_A": float(A.float().mean()), "rows_streamed": rows1 + rows2,
             "rows_in_windows": B * (K + 1) + B * K}
-    return step, meta, None
+    return step, meta, {"leg": cpu_leg_chain, "case": case, "state": st}
 
 
 def setup_tree(torch, sd, wl):
@@ -223,16 +224,17 @@ def setup_tree(torch, sd, wl):
         st["i"] += 1
         if ev is not None:
             sd.time_next_stream_pass(*ev)
-        sd.build_tree(margs[i], N, workspace=ws_b)
-        sd.verify_tree(targets[i], tree, out=walk_out)
+        st["tree"] = sd.build_tree(margs[i], N, workspace=ws_b)
+        sd.verify_tree(targets[i], st["tree"], out=walk_out)
 
+    st["walk"] = walk_out
     meta = {"workload": (f"DDTree build (B={B}, K={K}, V={V} fp32 marginals, N={N}) + argmax walk over "
                          f"bf16 target rows (read on demand)"),
             "global_batch": B, "K_max": K, "V": V, "positions_per_step": B * (N - 1),
             "kernel": "k_topk_short<f32>", "kernel_bytes": B * K * V * 4,
             "step_bytes": B * K * V * 4 + rows_read * V * 2, "mean_A": float(A.float().mean()),
             "rows_streamed": rows_read}
-    return step, meta, None
+    return step, meta, {"leg": cpu_leg_tree, "case": case, "target": target, "state": st}
 
 
 def setup_tree_sampled(torch, sd, wl):
@@ -257,10 +259,12 @@ def setup_tree_sampled(torch, sd, wl):
     def step(ev=None):
         i = st["i"] % len(margs)
         st["i"] += 1
-        sd.build_tree(margs[i], N, workspace=ws_b)
+        st["tree"] = sd.build_tree(margs[i], N, workspace=ws_b)
         if ev is not None:
             sd.time_next_stream_pass(*ev)
-        sd.verify_tree_sampled(targets[i], tree, u, 1.0, out=walk_out)
+        sd.verify_tree_sampled(targets[i], st["tree"], u, 1.0, out=walk_out)
+
+    st["walk"] = walk_out
 
     meta = {"workload": (f"DDTree build (B={B}, K={K}, V={V} fp32 marginals, N={N}) + walk under a "
                          f"sampling target (T=1, bf16 rows read on demand)"),
@@ -268,7 +272,8 @@ def setup_tree_sampled(torch, sd, wl):
             "kernel": "k_tree_walk_rows", "kernel_bytes": rows_read * V * 2 + B * N * 12,
             "step_bytes": B * K * V * 4 + rows_read * V * 2, "mean_A": float(A.float().mean()),
             "rows_streamed": rows_read}
-    return step, meta, None
+    return step, meta, {"leg": cpu_leg_tree, "case": case, "target": target, "state": st, "u": u,
+                        "T": 1.0, "top_k": 0}
 
 
 def setup_tree_sampled_topk(torch, sd, wl):
@@ -288,6 +293,8 @@ def setup_tree_sampled_topk(torch, sd, wl):
     rows_read = int(A.sum()) + B
     st = {"i": 0}
 
+    st["tree"], st["walk"] = tree, walk_out
+
     def step(ev=None):
         i = st["i"] % len(targets)
         st["i"] += 1
@@ -301,7 +308,8 @@ def setup_tree_sampled_topk(torch, sd, wl):
             "kernel": "k_tree_walk_topk_rows", "kernel_bytes": rows_read * V * 2 + B * N * 12,
             "step_bytes": rows_read * V * 2, "mean_A": float(A.float().mean()),
             "rows_streamed": rows_read, "max_A": int(A.max())}
-    return step, meta, None
+    return step, meta, {"leg": cpu_leg_tree, "case": case, "target": target, "state": st, "u": u,
+                        "T": 1.0, "top_k": 50, "walk_only": True}
 
 
 def setup_kv(torch, sd, wl):
@@ -318,6 +326,10 @@ def setup_kv(torch, sd, wl):
     p, a = path.cpu(), alen.cpu()
     moved = sum(1 for b in range(B) for i in range(int(a[b])) if int(p[b, i]) - 1 != i)
 
+    g = torch.Generator(device="cuda").manual_seed(1007)
+    kv.copy_(torch.randint(0, 256, kv.shape, generator=g, device="cuda", dtype=torch.int32).to(torch.uint8))
+    kv0 = kv.clone()
+
     def step(ev=None):
         if ev is not None:
             sd.time_next_stream_pass(*ev)
@@ -328,7 +340,8 @@ def setup_kv(torch, sd, wl):
             "global_batch": B, "positions_per_step": int(a.sum()),
             "kernel": "k_compact_kv", "kernel_bytes": 2 * moved * row_bytes,
             "step_bytes": 2 * moved * row_bytes}
-    return step, meta, None
+    return step, meta, {"leg": cpu_leg_kv, "kv": kv, "kv0": kv0, "base": base, "path": path, "alen": alen,
+                        "B": B, "N": N}
 
 
 def setup_rerank(torch, sd, wl):
@@ -363,32 +376,37 @@ def setup_rerank(torch, sd, wl):
     t = lambda a: torch.as_tensor(a, device="cuda")
     par_t, tok_t, prob_t, n_t = t(par), t(tok), t(prob), t(n)
 
+    st = {}
+
     def step(ev=None):
         if ev is not None:
             sd.time_next_stream_pass(*ev)
-        sd.rerank_tree(par_t, tok_t, prob_t, n_t, N)
+        st["out"] = sd.rerank_tree(par_t, tok_t, prob_t, n_t, N)
 
     meta = {"workload": f"EAGLE-2-style tree choice: B={B}, {M} candidates, budget N={N}",
             "global_batch": B, "positions_per_step": B * (N - 1),
             "kernel": "k_rerank_tree", "kernel_bytes": B * M * 12 + B * N * 28,
             "step_bytes": B * M * 12 + B * N * 28}
-    return step, meta, None
+    return step, meta, {"leg": cpu_leg_rerank, "cand": (par, tok, prob, n), "B": B, "M": M, "N": N,
+                        "state": st}
 
 
 def setup_chain1(torch, sd, wl):
     case = wl.gen_chain_small(device="cuda")
     ws = torch.empty(sd.workspace_bytes(sd.OP_CHAIN, 1, 4, 1000), dtype=torch.uint8, device="cuda")
 
+    st = {}
+
     def step(ev=None):
         if ev is not None:
             sd.time_next_stream_pass(*ev)
-        sd.verify_chain(case.target, case.draft, case.tokens, case.uniforms, 1.0, B=1, K_max=4,
-                        workspace=ws, validate=False)
+        st["out"] = sd.verify_chain(case.target, case.draft, case.tokens, case.uniforms, 1.0, B=1,
+                                    K_max=4, workspace=ws)
 
     meta = {"workload": "chain verify B=1 K=4 V=1000 fp32 (latency-bound)", "global_batch": 1,
             "K_max": 4, "V": 1000, "positions_per_step": 4, "kernel": "k_chain_stats",
             "kernel_bytes": 9 * 1000 * 4 + 16, "step_bytes": 9 * 1000 * 4 + 16 + 20}
-    return step, meta, None
+    return step, meta, {"leg": cpu_leg_chain, "case": case, "state": st}
 
 
 WORKLOADS = {"adaptive": setup_adaptive, "greedy": setup_greedy, "topk": setup_topk,
@@ -397,76 +415,302 @@ WORKLOADS = {"adaptive": setup_adaptive, "greedy": setup_greedy, "topk": setup_t
              "kv": setup_kv, "rerank": setup_rerank}
 
 
-def run_cpu_baseline(cpu, target_seconds: float):
+# --------------------------------------------------------------------------
+# CPU oracle legs: each returns (sample, parity, about). sample(threads) runs
+# the oracle once on a bounded piece of the workload and returns the
+# positions it covered; parity() compares the timed step's GPU results with
+# the oracle on the whole batch (bit-exact, the oracle's margin cases checked
+# for validity instead); about says what the sample is. Only this leg of the
+# benchmark touches the oracle.
+# --------------------------------------------------------------------------
+
+def _groups(n, size):
+    return [list(range(g, min(n, g + size))) for g in range(0, n, size)]
+
+
+def _chain_parity(oracle, h, A, nx, st, V, T, top_k, threads):
+    """Oracle verification of host rows h (re-packed sequences) against the
+    GPU's A, next and status for those sequences: (sequences, mismatches,
+    margin cases)."""
+    import numpy as np
+    ref = oracle.verify_chain(h["target"], h["draft"], h["tokens"], h["uniforms"], h["cu"], h["B"],
+                              h["K_max"], V, T, top_k, threads=threads, want_probs=False)
+    mg = ref["margin"] != 0
+    bad = ~mg & ((A != ref["A"]) | (nx != ref["next"]) | (st != ref["status"]))
+    if mg.any() and T != 0.0:
+        valid, st_exp = oracle.check_chain(h["target"], h["draft"], h["tokens"], h["uniforms"], h["cu"],
+                                           h["B"], h["K_max"], V, T, A, nx, top_k=top_k, threads=threads)
+        sample_only = (ref["margin"] & oracle.MARGIN_ACCEPT) == 0
+        bad |= mg & ((valid != 3) | (st != st_exp) | (sample_only & (A != ref["A"])))
+    return len(A), int(bad.sum()), int(mg.sum())
+
+
+def _host_chain(case, seqs):
+    """Host float32 rows of sequences seqs of a chain case, re-packed."""
     import numpy as np
     import torch
+    from rejection_sampling_verify_softmax_amd import workloads as wl
+    cu = (np.arange(case.B + 1, dtype=np.int64) * case.K_max if case.cu is None
+          else case.cu.cpu().numpy().astype(np.int64))
+    t_rows = np.concatenate([np.arange(cu[b] + b, cu[b + 1] + b + 1) for b in seqs])
+    d_parts = [np.arange(cu[b], cu[b + 1]) for b in seqs]
+    d_rows = np.concatenate(d_parts)
+    lens = [int(cu[b + 1] - cu[b]) for b in seqs]
+    ti = torch.as_tensor(t_rows, device=case.target.device)
+    di = torch.as_tensor(d_rows, device=case.target.device)
+    h = {"target": wl.to_host_f32(case.target.index_select(0, ti)),
+         "tokens": case.tokens.index_select(0, di).cpu().numpy() if len(d_rows) else np.zeros(0, np.int32),
+         "cu": np.concatenate([[0], np.cumsum(lens)]).astype(np.int32), "B": len(seqs),
+         "K_max": max(lens), "pos": int(sum(lens)), "seqs": np.array(seqs)}
+    if case.draft is not None:
+        h["draft"] = wl.to_host_f32(case.draft.index_select(0, di))
+        h["uniforms"] = case.uniforms.index_select(0, ti).cpu().numpy()
+    else:
+        h["draft"], h["uniforms"] = None, np.zeros(len(t_rows), np.float32)
+    return h
 
+
+def cpu_leg_adaptive(cpu, threads):
+    import numpy as np
+    import oracle
+    case, packed = cpu["case"], cpu["packed"]
+    B, V = case.B, case.V
+    conf = case.conf.cpu().numpy()
+    groups = [_host_chain(packed, g) for g in _groups(B, 16)[:8]]     # the first 128 sequences
+    state = {"i": 0, "sel": True}
+
+    def sample(nt):
+        if state["sel"]:                    # length selection for the whole batch, once per pass
+            oracle.select_len(conf, B, case.K_max, case.cost)
+        g = groups[state["i"] % len(groups)]
+        state["i"] += 1
+        state["sel"] = state["i"] % len(groups) == 0
+        oracle.verify_chain(g["target"], g["draft"], g["tokens"], g["uniforms"], g["cu"], g["B"],
+                            g["K_max"], V, 1.0, threads=nt, want_probs=False)
+        return g["pos"]
+
+    def parity():
+        k_g = cpu["sel"]["k"].cpu().numpy()
+        sel = oracle.select_len(conf, B, case.K_max, case.cost)
+        sel_mg = sel["margin"] != 0
+        ok_sel = oracle.check_select_len(conf, B, case.K_max, case.cost, k_g) == 1
+        out = cpu["out"]
+        A, nx, st = (out[k].cpu().numpy() for k in ("accepted_len", "next_token", "status"))
+        par = {"select_len_sequences": B,
+               "select_len_mismatches": int(((k_g != sel["k"]) & ~sel_mg).sum() + (~ok_sel & sel_mg).sum()),
+               "select_len_margin_cases": int(sel_mg.sum()),
+               "verify_sequences": 0, "verify_mismatches": 0, "verify_margin_cases": 0}
+        for g in _groups(B, 64):
+            h = _host_chain(packed, g)
+            n, bad, mg = _chain_parity(oracle, h, A[g], nx[g], st[g], V, 1.0, 0, threads)
+            par["verify_sequences"] += n
+            par["verify_mismatches"] += bad
+            par["verify_margin_cases"] += mg
+        par["pass"] = par["select_len_mismatches"] == 0 and par["verify_mismatches"] == 0
+        return par
+
+    about = (f"length selection for all {B} sequences, then packed chain verification of the first "
+             f"{sum(g['B'] for g in groups)} sequences in groups of 16, cycled")
+    return sample, parity, about
+
+
+def cpu_leg_chain(cpu, threads):
+    import oracle
+    case = cpu["case"]
+    V, T, top_k = case.V, case.temperature, case.top_k
+    size = 1 if case.B == 1 else (4 if top_k else 16)
+    groups = [_host_chain(case, g) for g in _groups(case.B, size)[:8]]
+    state = {"i": 0}
+
+    def sample(nt):
+        g = groups[state["i"] % len(groups)]
+        state["i"] += 1
+        oracle.verify_chain(g["target"], g["draft"], g["tokens"], g["uniforms"], g["cu"], g["B"],
+                            g["K_max"], V, T, top_k, threads=nt, want_probs=False)
+        return g["pos"]
+
+    def parity():
+        out = cpu["state"]["out"]
+        A, nx, st = (out[k].cpu().numpy() for k in ("accepted_len", "next_token", "status"))
+        par = {"verify_sequences": 0, "verify_mismatches": 0, "verify_margin_cases": 0}
+        for g in _groups(case.B, 32):
+            n, bad, mg = _chain_parity(oracle, _host_chain(case, g), A[g], nx[g], st[g], V, T, top_k,
+                                       threads)
+            par["verify_sequences"] += n
+            par["verify_mismatches"] += bad
+            par["verify_margin_cases"] += mg
+        par["pass"] = par["verify_mismatches"] == 0
+        return par
+
+    about = (f"chain verification{' with top-k ' + str(top_k) if top_k else ''} of the first "
+             f"{sum(g['B'] for g in groups)} sequences in groups of {size}, cycled")
+    return sample, parity, about
+
+
+def cpu_leg_greedy(cpu, threads):
     import oracle
     from rejection_sampling_verify_softmax_amd import workloads as wl
+    case = cpu["case"]
+    B, K, V = case.B, case.K_max, case.V
+    host_t = wl.to_host_f32(case.target).reshape(B, K + 1, V)
+    host_y = case.tokens.cpu().numpy().reshape(B, K)
+    groups = _groups(B, 8)
+    state = {"i": 0}
 
-    case, packed = cpu["case"], cpu["packed"]
+    def sample(nt):
+        g = groups[state["i"] % len(groups)]
+        state["i"] += 1
+        oracle.verify_greedy(host_t[g[0]:g[-1] + 1], host_y[g[0]:g[-1] + 1], None, len(g), K, V, threads=nt)
+        return len(g) * K
+
+    def parity():
+        out = cpu["state"]["out"]
+        ref = oracle.verify_greedy(host_t, host_y, None, B, K, V, threads=threads)
+        bad = sum(int((out[kg].cpu().numpy() != ref[kr]).sum())
+                  for kg, kr in (("accepted_len", "A"), ("next_token", "next"), ("status", "status")))
+        return {"verify_sequences": B, "verify_mismatches": bad, "pass": bad == 0}
+
+    return sample, parity, f"greedy verification of all {B} sequences in groups of 8, cycled"
+
+
+def cpu_leg_tree(cpu, threads):
+    import numpy as np
+    import oracle
+    from rejection_sampling_verify_softmax_amd import workloads as wl
+    case, st = cpu["case"], cpu["state"]
+    B, K, V, N = case.B, case.K, case.V, case.N
+    marg = wl.to_host_f32(case.marginals)
+    tgt = wl.to_host_f32(cpu["target"])
+    T, top_k = cpu.get("T", 0.0), cpu.get("top_k", 0)
+    walk_only = cpu.get("walk_only", False)
+    u = cpu["u"].cpu().numpy() if "u" in cpu else None
+    groups = _groups(B, 4)
+    tree_h = {k: v.cpu().numpy() for k, v in st["tree"].items()}
+    state = {"i": 0}
+
+    def sample(nt):
+        g = groups[state["i"] % len(groups)]
+        state["i"] += 1
+        s = slice(g[0], g[-1] + 1)
+        tr = tree_h if walk_only else oracle.build_tree(marg[s], len(g), K, V, N, threads=nt)
+        tok, par_, nn = (tr[k][s] if walk_only else tr[k] for k in ("token", "parent", "n_nodes"))
+        if T == 0.0:
+            oracle.verify_tree(tgt[s], tok, par_, nn, len(g), N, V, threads=nt)
+        else:
+            oracle.verify_tree_sampled(tgt[s], tok, par_, nn, u[s], len(g), N, V, T, top_k, threads=nt)
+        return len(g) * (N - 1)
+
+    def parity():
+        tree = {k: v.cpu().numpy() for k, v in st["tree"].items()}
+        walk = {k: v.cpu().numpy() for k, v in st["walk"].items()}
+        bad = 0
+        if not walk_only:
+            ref_t = oracle.build_tree(marg, B, K, V, N, threads=threads)
+            for k in ("token", "parent", "depth", "score", "n_nodes"):
+                bad += int((tree[k] != ref_t[k]).reshape(B, -1).any(axis=1).sum())
+            bad += int((tree["anc_mask"].view(np.uint64) != ref_t["anc_mask"]).any(axis=1).sum())
+        margins = 0
+        if T == 0.0:
+            ref = oracle.verify_tree(tgt, tree["token"], tree["parent"], tree["n_nodes"], B, N, V,
+                                     threads=threads)
+            mg = np.zeros(B, bool)
+        else:
+            ref = oracle.verify_tree_sampled(tgt, tree["token"], tree["parent"], tree["n_nodes"], u, B, N,
+                                             V, T, top_k, threads=threads)
+            mg = ref["margin"] != 0
+            margins = int(mg.sum())
+        diff = ((walk["path"] != ref["path"]).any(axis=1) | (walk["accepted_len"] != ref["A"])
+                | (walk["next_token"] != ref["next"]))
+        bad += int((diff & ~mg).sum())
+        if mg.any():
+            valid = oracle.check_tree_sampled(tgt, tree["token"], tree["parent"], tree["n_nodes"], u, B, N, V,
+                                              T, walk["path"], walk["accepted_len"], walk["next_token"],
+                                              top_k=top_k, threads=threads)
+            bad += int((mg & (valid != 1)).sum())
+        return {"tree_sequences": B, "mismatches": bad, "walk_margin_cases": margins, "pass": bad == 0}
+
+    what = ("the sampled walk" + (f" with top-k {top_k}" if top_k else "") if T else "the argmax walk")
+    about = (("" if walk_only else "tree build and ") + what +
+             f" for all {B} sequences in groups of 4, cycled")
+    return sample, parity, about
+
+
+def cpu_leg_kv(cpu, threads):
+    import numpy as np
+    import oracle
+    kv0 = cpu["kv0"].cpu().numpy()
+    base, path, alen = (cpu[k].cpu().numpy() for k in ("base", "path", "alen"))
+    B, N = cpu["B"], cpu["N"]
+    state = {}
+
+    def sample(nt):
+        state["ref"] = oracle.compact_kv(kv0, base, path, alen, B, N)
+        return int(alen.sum())
+
+    def parity():
+        # the library moves rows in place: a step applied to the compacted rows
+        # again is not the one-step result, so compare one fresh call
+        import rejection_sampling_verify_softmax_amd as sd
+        import torch
+        kv = cpu["kv0"].clone()
+        sd.compact_kv(kv, cpu["base"], cpu["path"], cpu["alen"])
+        torch.cuda.synchronize()
+        ref = oracle.compact_kv(kv0, base, path, alen, B, N)
+        bad = int((kv.cpu().numpy() != ref).any(axis=1).sum())
+        return {"rows": int(kv0.shape[0]), "row_mismatches": bad, "pass": bad == 0}
+
+    return sample, parity, f"accepted-path KV compaction of all {B} sequences (host copy of the rows)"
+
+
+def cpu_leg_rerank(cpu, threads):
+    import numpy as np
+    import oracle
+    par, tok, prob, n = cpu["cand"]
+    B, M, N = cpu["B"], cpu["M"], cpu["N"]
+
+    def sample(nt):
+        oracle.rerank_tree(par, tok, prob, n, B, M, N)
+        return B * (N - 1)
+
+    def parity():
+        out = {k: v.cpu().numpy() for k, v in cpu["state"]["out"].items()}
+        ref = oracle.rerank_tree(par, tok, prob, n, B, M, N)
+        bad = 0
+        for k in ("token", "parent", "depth", "score", "cand", "n_nodes"):
+            bad += int((out[k] != ref[k]).reshape(B, -1).any(axis=1).sum())
+        bad += int((out["anc_mask"].view(np.uint64) != ref["anc_mask"]).any(axis=1).sum())
+        return {"tree_sequences": B, "mismatches": bad, "pass": bad == 0}
+
+    return sample, parity, f"re-ranking of all {B} candidate trees ({M} candidates each)"
+
+
+def run_cpu_baseline(cpu, target_seconds: float):
+    """The oracle timed on the host's cores on a bounded sample of the
+    workload (all cores, then one thread for a quarter of the time), and the
+    parity of the timed step against it. Returns (cpu_baseline, parity)."""
+    import oracle
+
     threads = int(os.environ.get("OMP_NUM_THREADS", "0")) or oracle.default_threads()
     threads = min(threads, oracle.default_threads())
-    conf = case.conf.cpu().numpy()
-    t0 = time.perf_counter()
-    sel = oracle.select_len(conf, case.B, case.K_max, case.cost)
-    t_sel = time.perf_counter() - t0
-    cu = sel["cu"].astype(np.int64)
-    B, V = case.B, case.V
-    group, n_groups = 16, min(8, (B + 15) // 16)
-    # the sample: the first n_groups * group sequences, copied to host once
-    # (fp32), then verified group after group, cycling, until the time is spent
-    groups = []
-    for g in range(n_groups):
-        seqs = [s for s in range(g * group, (g + 1) * group) if s < B]
-        t_rows = np.concatenate([np.arange(cu[s] + s, cu[s + 1] + s + 1) for s in seqs])
-        d_rows = np.concatenate([np.arange(cu[s], cu[s + 1]) for s in seqs])
-        ti = torch.as_tensor(t_rows, device="cuda")
-        di = torch.as_tensor(d_rows, device="cuda")
-        lens = [int(cu[s + 1] - cu[s]) for s in seqs]
-        groups.append(dict(
-            seqs=np.array(seqs),
-            tgt=wl.to_host_f32(packed.target.index_select(0, ti)),
-            dft=wl.to_host_f32(packed.draft.index_select(0, di)),
-            tok=packed.tokens.index_select(0, di).cpu().numpy(),
-            uni=packed.uniforms.index_select(0, ti).cpu().numpy(),
-            cu=np.concatenate([[0], np.cumsum(lens)]).astype(np.int32),
-            n=len(seqs), k_max=max(lens), pos=int(sum(lens))))
-    # Parity of the timed GPU step on the same inputs: its verify lengths for
-    # every sequence, and its committed results for the sampled sequences (the
-    # first visit of each group), bit-exact outside the oracle's margin cases.
-    out = cpu["out"]
-    A_g, nx_g = out["accepted_len"].cpu().numpy(), out["next_token"].cpu().numpy()
-    st_g = out["status"].cpu().numpy()
-    sel_margin = sel["margin"] != 0
-    par = {"select_len_sequences": int(B),
-           "select_len_mismatches": int(((cpu["k"] != sel["k"]) & ~sel_margin).sum()),
-           "select_len_margin_cases": int(sel_margin.sum()),
-           "verify_sequences": 0, "verify_mismatches": 0, "verify_margin_cases": 0}
-    done_pos, done_seq, spent, calls = 0, 0, t_sel, 0
-    while spent < target_seconds or calls < n_groups:
-        g = groups[calls % n_groups]
-        t0 = time.perf_counter()
-        ref = oracle.verify_chain(g["tgt"], g["dft"], g["tok"], g["uni"], g["cu"], g["n"], g["k_max"], V,
-                                  1.0, threads=threads, want_probs=False)
-        spent += time.perf_counter() - t0
-        if calls < n_groups:
-            sq, mg = g["seqs"], ref["margin"] != 0
-            bad = ~mg & ((A_g[sq] != ref["A"]) | (nx_g[sq] != ref["next"]) | (st_g[sq] != ref["status"]))
-            par["verify_sequences"] += len(sq)
-            par["verify_mismatches"] += int(bad.sum())
-            par["verify_margin_cases"] += int(mg.sum())
-        done_pos += g["pos"]
-        done_seq += g["n"]
-        calls += 1
-    par["pass"] = par["select_len_mismatches"] == 0 and par["verify_mismatches"] == 0
-    cpu["parity"] = par
-    return {"value": done_pos / spent, "unit": "positions/s", "cores": threads, "kind": "oracle",
-            "sample": (f"CPU oracle (fp64 C, OpenMP over sequences): length selection for all {B} "
-                       f"sequences, then packed chain verification of the first {n_groups * group} "
-                       f"sequences in groups of {group}, cycled ({done_seq} sequences, "
-                       f"{done_pos} draft positions), "
-                       f"{spent:.1f} s of oracle time; transfer and conversion not timed")}
+    sample, parity, about = cpu["leg"](cpu, threads)
+
+    def timed(nt, seconds):
+        units, spent, calls = 0, 0.0, 0
+        while spent < seconds or calls == 0:
+            t0 = time.perf_counter()
+            units += sample(nt)
+            spent += time.perf_counter() - t0
+            calls += 1
+        return units, spent
+
+    units, spent = timed(threads, target_seconds)
+    units1, spent1 = timed(1, target_seconds / 4)
+    base = {"value": units / spent, "unit": "positions/s", "cores": threads, "kind": "oracle",
+            "value_1thread": units1 / spent1,
+            "sample": (f"CPU oracle (fp64 C, OpenMP over sequences): {about}; {units} positions in "
+                       f"{spent:.1f} s on {threads} threads, {units1} positions in {spent1:.1f} s on one "
+                       f"thread; host copies and conversions not timed")}
+    return base, parity()
 
 
 def main():
@@ -614,9 +858,8 @@ def main():
         if k in meta:
             result["step"][k] = meta[k]
     if cpu is not None and not args.no_cpu_baseline:
-        log("timing the CPU oracle on a bounded sample")
-        result["cpu_baseline"] = run_cpu_baseline(cpu, args.cpu_seconds)
-        result["parity"] = cpu.get("parity")
+        log("timing the CPU oracle on a bounded sample; parity of the timed step against it")
+        result["cpu_baseline"], result["parity"] = run_cpu_baseline(cpu, args.cpu_seconds)
     else:
         result["cpu_baseline"] = None
     print(json.dumps(result), flush=True)
