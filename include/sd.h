@@ -179,6 +179,31 @@ sd_status_t sd_verify_chain_capped(const void* target_logits, const void* draft_
                                    void* workspace, size_t workspace_bytes, void* hip_stream);
 
 /*
+ * sd_verify_chain without a workspace argument, for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc). Same arguments, computation, outputs and
+ * errors as sd_verify_chain, but the scratch space is a file-scope device
+ * array of SD_NOALLOC_SCRATCH_BYTES inside the library (one per GPU, held
+ * until the process ends). The call allocates nothing: its first use on a
+ * device only looks up that device's copy of the array (hipGetSymbolAddress).
+ * A call whose path needs more than SD_NOALLOC_SCRATCH_BYTES of scratch
+ * (sd_workspace_bytes gives an upper bound) returns SD_EWORKSPACE with
+ * nothing launched; at V = 128256, K_max = 8 the full-vocabulary path fits
+ * up to B = 5108 with bf16 logits and B = 2606 with fp32 logits. Every call on one GPU shares that array, so two calls
+ * that overlap in time on the same GPU (different streams, or host threads)
+ * race: serialise them. The scratch needs no clearing between calls.
+ */
+#define SD_NOALLOC_SCRATCH_BYTES (16u << 20)
+sd_status_t sd_verify_chain_noalloc(const void* target_logits, const void* draft_logits,
+                                    sd_dtype_t dtype, const int32_t* draft_tokens,
+                                    const float* uniforms, const int32_t* cu_draft,
+                                    int32_t B, int32_t K_max, int32_t V,
+                                    float temperature, int32_t top_k,
+                                    int32_t* accepted_len, int32_t* next_token,
+                                    float* probs_out, float* resid_mass_out,
+                                    int32_t* seq_status, void* hip_stream);
+
+/*
  * Greedy chain verification [SD §1: greedy results follow the target argmax].
  * g_i = lowest-id argmax of raw target row i (NaN ignored); position i is
  * accepted iff y_i == g_i; A = first mismatch (or k_b); next_token = g_A.

@@ -77,6 +77,8 @@ def _load():
     lib.sd_compact_kv.restype = ctypes.c_int
     lib.sd_rerank_tree.argtypes = [P, P, P, P, I, I, I, P, P, P, P, P, P, P, P]
     lib.sd_rerank_tree.restype = ctypes.c_int
+    lib.sd_verify_chain_noalloc.argtypes = [P, P, ctypes.c_int, P, P, P, I, I, I, F, I, P, P, P, P, P, P]
+    lib.sd_verify_chain_noalloc.restype = ctypes.c_int
     lib.sd_time_next_stream_pass.argtypes = [P, P]
     lib.sd_time_next_stream_pass.restype = ctypes.c_int
     _lib = lib
@@ -236,6 +238,64 @@ def verify_chain(target: torch.Tensor, draft: Optional[torch.Tensor], tokens: to
                                 _ptr(nxt), _ptr(probs), _ptr(resid), _ptr(st), _ptr(ws),
                                 ctypes.c_size_t(ws.numel()), _stream(stream))
     _raise(r, "sd_verify_chain")
+    res = {"accepted_len": A, "next_token": nxt, "status": st}
+    if probs is not None:
+        res["probs"] = probs
+    if resid is not None:
+        res["resid"] = resid
+    return res
+
+
+def verify_chain_noalloc(target: torch.Tensor, draft: Optional[torch.Tensor], tokens: torch.Tensor,
+                         uniforms: Optional[torch.Tensor], temperature: float, top_k: int = 0,
+                         cu: Optional[torch.Tensor] = None, B: Optional[int] = None,
+                         K_max: Optional[int] = None, out: dict = None, want_probs: bool = False,
+                         want_resid: bool = False, stream=None) -> dict:
+    """sd_verify_chain_noalloc: verify_chain with the library's own static
+    scratch instead of a workspace. With every output passed in `out`
+    (accepted_len, next_token, status, and probs / resid when asked for) the
+    call allocates nothing, so it may run under graph capture."""
+    dev = target.device
+    _check(target, "target", device=dev)
+    dt = _dtype_code(target)
+    V = int(target.shape[-1])
+    if cu is not None:
+        _check(cu, "cu", torch.int32, dev)
+        B = cu.numel() - 1 if B is None else B
+        if K_max is None:
+            raise ValueError("a packed batch (cu given) needs K_max, the largest draft length")
+    else:
+        if K_max is None:
+            if tokens.dim() != 2:
+                raise ValueError("pass K_max (or 2-D tokens) for a dense batch")
+            K_max = int(tokens.shape[-1])
+        B = target.numel() // V // (K_max + 1) if B is None else B
+    _check(tokens, "tokens", torch.int32, dev)
+    greedy = float(temperature) == 0.0
+    if not greedy:
+        _check(draft, "draft", target.dtype, dev)
+        _check(uniforms, "uniforms", torch.float32, dev)
+    _check_layout(target, draft, tokens, uniforms, cu, B, K_max, V, greedy, False, stream)
+    o = out or {}
+    A = _get(o, "accepted_len", lambda: torch.empty(B, dtype=torch.int32, device=dev))
+    nxt = _get(o, "next_token", lambda: torch.empty(B, dtype=torch.int32, device=dev))
+    st = _get(o, "status", lambda: torch.empty(B, dtype=torch.int32, device=dev))
+    probs = None
+    if want_probs and not greedy:
+        probs = _get(o, "probs", lambda: torch.empty(max(tokens.numel(), 1), 2, dtype=torch.float32, device=dev))
+    resid = None
+    if want_resid and not greedy:
+        resid = _get(o, "resid", lambda: torch.empty(B, dtype=torch.float32, device=dev))
+    for t, n, name in ((A, B, "accepted_len"), (nxt, B, "next_token"), (st, B, "status")):
+        _check(t, name, torch.int32, dev)
+        if t.numel() < n:
+            raise ValueError(f"{name} needs {n} entries")
+    r = _load().sd_verify_chain_noalloc(_ptr(target), _ptr(draft) if not greedy else None, dt,
+                                        _ptr(tokens), _ptr(uniforms) if not greedy else None, _ptr(cu),
+                                        int(B), int(K_max), int(V), ctypes.c_float(float(temperature)),
+                                        int(top_k), _ptr(A), _ptr(nxt), _ptr(probs), _ptr(resid), _ptr(st),
+                                        _stream(stream))
+    _raise(r, "sd_verify_chain_noalloc")
     res = {"accepted_len": A, "next_token": nxt, "status": st}
     if probs is not None:
         res["probs"] = probs

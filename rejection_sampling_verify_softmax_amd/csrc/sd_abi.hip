@@ -9,6 +9,7 @@
 #include <math.h>
 
 #include <algorithm>
+#include <mutex>
 
 namespace {
 
@@ -33,6 +34,12 @@ size_t chain_ws(int B, int K_max, int V, int dtype, float T, int top_k) {
 }
 
 }  // namespace
+
+// Scratch space of sd_verify_chain_noalloc: a file-scope device array (each
+// GPU holds its own copy). Host code never passes `scratch` itself to a kernel
+// (on the host it only names the symbol): the per-device address from
+// hipGetSymbolAddress is looked up once per device and used instead.
+static __device__ __align__(256) unsigned char scratch[SD_NOALLOC_SCRATCH_BYTES];
 
 namespace sd {
 thread_local hipEvent_t PassTimer::start = nullptr;
@@ -109,6 +116,22 @@ sd_status_t sd_workspace_bytes(sd_op_t op, int32_t B, int32_t K_max, int32_t V, 
 
 namespace {
 
+// Argument checks shared by the chain entry points (no HIP call).
+sd_status_t chain_args_status(const void* target_logits, const void* draft_logits, sd_dtype_t dtype,
+                              const int32_t* draft_tokens, const float* uniforms, int32_t B,
+                              int32_t K_max, int32_t V, float temperature, int32_t top_k,
+                              const int32_t* accepted_len, const int32_t* next_token) {
+    if (bad_size(B, K_max, V) || bad_dtype(dtype)) return SD_EINVAL;
+    if (!(temperature >= 0.0f) || !isfinite(temperature)) return SD_EINVAL;
+    if (top_k < 0 || top_k > SD_MAX_TOPK) return SD_EINVAL;
+    if (!target_logits || !accepted_len || !next_token) return SD_EINVAL;
+    if (misaligned(target_logits) || misaligned(draft_logits)) return SD_EINVAL;
+    const bool greedy = temperature == 0.0f;
+    if (K_max > 0 && !draft_tokens) return SD_EINVAL;
+    if (!greedy && (!uniforms || (K_max > 0 && !draft_logits))) return SD_EINVAL;
+    return SD_OK;
+}
+
 // sd_verify_chain and sd_verify_chain_capped: checks, then the path's launches.
 sd_status_t verify_chain(const void* target_logits, const void* draft_logits, sd_dtype_t dtype,
                          const int32_t* draft_tokens, const float* uniforms, const int32_t* cu_draft,
@@ -117,14 +140,11 @@ sd_status_t verify_chain(const void* target_logits, const void* draft_logits, sd
                          int32_t* accepted_full, float* probs_out, float* resid_mass_out,
                          int32_t* seq_status, void* workspace, size_t workspace_bytes,
                          void* hip_stream) {
-    if (bad_size(B, K_max, V) || bad_dtype(dtype)) return SD_EINVAL;
-    if (!(temperature >= 0.0f) || !isfinite(temperature)) return SD_EINVAL;
-    if (top_k < 0 || top_k > SD_MAX_TOPK) return SD_EINVAL;
-    if (!target_logits || !accepted_len || !next_token || !workspace) return SD_EINVAL;
-    if (misaligned(target_logits) || misaligned(draft_logits) || misaligned(workspace)) return SD_EINVAL;
+    const sd_status_t bad = chain_args_status(target_logits, draft_logits, dtype, draft_tokens, uniforms,
+                                              B, K_max, V, temperature, top_k, accepted_len, next_token);
+    if (bad != SD_OK) return bad;
+    if (!workspace || misaligned(workspace)) return SD_EINVAL;
     const bool greedy = temperature == 0.0f;
-    if (K_max > 0 && !draft_tokens) return SD_EINVAL;
-    if (!greedy && (!uniforms || (K_max > 0 && !draft_logits))) return SD_EINVAL;
     const size_t need = chain_ws(B, K_max, V, (int)dtype, temperature, top_k);
     if (workspace_bytes < need) return SD_EWORKSPACE;
     hipStream_t st = static_cast<hipStream_t>(hip_stream);
@@ -157,9 +177,45 @@ sd_status_t verify_chain(const void* target_logits, const void* draft_logits, sd
     return from_hip(sd::launch_chain_full(a));
 }
 
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// Address of the current device's scratch array, or nullptr on a HIP error.
+void* scratch_address() {
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (g_scratch_ptr[dev] == nullptr) {
+        void* p = nullptr;
+        if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess) return nullptr;
+        g_scratch_ptr[dev] = p;
+    }
+    return g_scratch_ptr[dev];
+}
+
 }  // namespace
 
 extern "C" {
+
+sd_status_t sd_verify_chain_noalloc(const void* target_logits, const void* draft_logits,
+                                    sd_dtype_t dtype, const int32_t* draft_tokens,
+                                    const float* uniforms, const int32_t* cu_draft, int32_t B,
+                                    int32_t K_max, int32_t V, float temperature, int32_t top_k,
+                                    int32_t* accepted_len, int32_t* next_token, float* probs_out,
+                                    float* resid_mass_out, int32_t* seq_status, void* hip_stream) {
+    // every argument check before the first HIP call (the scratch lookup)
+    const sd_status_t bad = chain_args_status(target_logits, draft_logits, dtype, draft_tokens, uniforms,
+                                              B, K_max, V, temperature, top_k, accepted_len, next_token);
+    if (bad != SD_OK) return bad;
+    if (chain_ws(B, K_max, V, (int)dtype, temperature, top_k) > SD_NOALLOC_SCRATCH_BYTES)
+        return SD_EWORKSPACE;
+    void* ws = scratch_address();
+    if (ws == nullptr) return SD_EHIP;
+    return verify_chain(target_logits, draft_logits, dtype, draft_tokens, uniforms, cu_draft, nullptr,
+                        B, K_max, V, temperature, top_k, accepted_len, next_token, nullptr, probs_out,
+                        resid_mass_out, seq_status, ws, SD_NOALLOC_SCRATCH_BYTES, hip_stream);
+}
 
 sd_status_t sd_verify_chain(const void* target_logits, const void* draft_logits, sd_dtype_t dtype,
                             const int32_t* draft_tokens, const float* uniforms,

@@ -232,3 +232,23 @@ def test_tree_binding_checks_inputs_without_gpu():
     with pytest.raises(ValueError):
         sd.verify_tree(rows, tree)
 
+
+
+def test_noalloc_rejects_before_any_hip_call(L):
+    v, f = ctypes.c_void_p, ctypes.c_float
+    one = v(16)
+
+    def na(B=2, K=3, V=100, T=1.0, top_k=0, target=one, draft=one, A=one, uni=one, dtype=1):
+        return L.sd_verify_chain_noalloc(target, draft, dtype, one, uni, None, B, K, V, f(T), top_k, A, one,
+                                         None, None, None, None)
+    assert na(B=0) == 1
+    assert na(K=65) == 1
+    assert na(T=-1.0) == 1
+    assert na(top_k=300) == 1
+    assert na(target=None) == 1
+    assert na(A=None) == 1
+    assert na(uni=None) == 1
+    assert na(draft=v(24)) == 1                   # misaligned logit rows
+    # a batch whose scratch need exceeds the library's static array
+    assert na(B=5109, K=8, V=128256) == 3        # SD_EWORKSPACE, nothing launched (bf16 fits 5108)
+    assert na(B=2607, K=8, V=128256, dtype=0) == 3
