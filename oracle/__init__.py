@@ -72,6 +72,8 @@ def _load():
     lib.orc_compact_kv.restype = None
     lib.orc_rerank_tree.argtypes = [P, P, P, P, I, I, I, P, P, P, P, P, P, P]
     lib.orc_rerank_tree.restype = None
+    lib.orc_expand_tree.argtypes = [P, P, P, P, P, P, P, P, P, I, I, I, I]
+    lib.orc_expand_tree.restype = None
     lib.orc_check_chain.argtypes = [P, P, P, P, P, I, I, I, D, I, D, P, P, P, P, I]
     lib.orc_check_chain.restype = None
     lib.orc_check_tree_sampled.argtypes = [P, P, P, P, P, I, I, I, D, I, D, P, P, P, P, I]
@@ -342,3 +344,30 @@ def check_select_len(conf, B, K, cost, k, tol=MARGIN_REL):
     _load().orc_check_select_len(_ptr(c), int(B), int(K), ctypes.c_float(cost), float(tol), _ptr(kk),
                                  _ptr(valid))
     return valid
+
+
+def expand_tree(cand, expand_in, child_token, child_prob, B, M, W, C):
+    """One EAGLE-2-style expansion step on host copies (see orc_expand_tree).
+
+    cand: dict of parent, token, prob, conf ([B, M]) and n_cand ([B]); a new
+    dict is returned with the grown arrays and "expand" ([B, W])."""
+    out = {"parent": _i32(cand["parent"]).reshape(B, M).copy(),
+           "token": _i32(cand["token"]).reshape(B, M).copy(),
+           "prob": _f32(cand["prob"]).reshape(B, M).copy(),
+           "conf": _f32(cand["conf"]).reshape(B, M).copy(),
+           "n_cand": _i32(cand["n_cand"]).copy(),
+           "expand": np.zeros((B, W), np.int32)}
+    ei = _i32(expand_in).reshape(-1)
+    ct = _i32(child_token).reshape(-1)
+    cp = _f32(child_prob).reshape(-1)
+    _load().orc_expand_tree(_ptr(out["parent"]), _ptr(out["token"]), _ptr(out["prob"]), _ptr(out["conf"]),
+                            _ptr(out["n_cand"]), _ptr(ei), _ptr(out["expand"]), _ptr(ct), _ptr(cp),
+                            int(B), int(M), int(W), int(C))
+    return out
+
+
+def empty_candidates(B, M):
+    """Candidate arrays of B sequences before the first expansion step."""
+    return {"parent": np.full((B, M), -1, np.int32), "token": np.full((B, M), -1, np.int32),
+            "prob": np.zeros((B, M), np.float32), "conf": np.full((B, M), -1.0, np.float32),
+            "n_cand": np.zeros(B, np.int32)}

@@ -875,3 +875,87 @@ void orc_check_select_len(const float* conf, int B, int K, float cost, double to
         valid_out[b] = ok;
     }
 }
+
+/*
+ * EAGLE-2-style expansion step [SD §4 EAGLE-2: the candidate tree grows by
+ * expanding the branches of highest cumulative path confidence; the final
+ * tree is re-ranked from the candidates (orc_rerank_tree)].
+ *
+ * Candidates of sequence b live in [B, M] arrays in topological order, as in
+ * orc_rerank_tree, plus cand_conf, the cumulative confidence (-1 marks an
+ * unusable candidate). One call grows the tree by one layer:
+ *   - n_cand[b] == 0 starts the tree: candidate 0 is the root (parent -1,
+ *     token -1, prob 1, conf 1) and the root is the one node expanded.
+ *     Otherwise slot w < W names the node expand_in[b, w], which is expanded
+ *     when 0 <= id < n_cand[b] and cand_conf[b, id] >= 0.
+ *   - The children of the node in slot w are child_token[b, w, c] with
+ *     conditional probability child_prob[b, w, c], c < C. The expanded
+ *     slots' children are appended in slot order, C per slot, from n0 (the
+ *     count before the call, after the root) while the index stays below M.
+ *     A child's confidence is fl32(conf[parent] * prob) when prob lies in
+ *     [0, 1], else -1.
+ *   - n_cand[b] becomes the new count.
+ *   - expand_out[b, 0..W) receives the appended candidates with confidence
+ *     >= 0 ordered by (confidence desc, index asc), the first W, -1 padded:
+ *     the nodes the next call expands.
+ */
+typedef struct {
+    float conf;
+    int idx;
+} OrcExp;
+
+static int orc_exp_cmp(const void* a, const void* b) {
+    const OrcExp* x = (const OrcExp*)a;
+    const OrcExp* y = (const OrcExp*)b;
+    if (x->conf != y->conf) return x->conf > y->conf ? -1 : 1;
+    return x->idx < y->idx ? -1 : (x->idx > y->idx);
+}
+
+void orc_expand_tree(int32_t* cand_parent, int32_t* cand_token, float* cand_prob, float* cand_conf,
+                     int32_t* n_cand, const int32_t* expand_in, int32_t* expand_out,
+                     const int32_t* child_token, const float* child_prob, int B, int M, int W,
+                     int C) {
+    for (int b = 0; b < B; ++b) {
+        int32_t* par = cand_parent + (size_t)b * M;
+        int32_t* tok = cand_token + (size_t)b * M;
+        float* prob = cand_prob + (size_t)b * M;
+        float* conf = cand_conf + (size_t)b * M;
+        int n0 = n_cand[b];
+        if (n0 < 0) n0 = 0;
+        if (n0 > M) n0 = M;
+        /* the nodes expanded by this call, slot by slot (-1: slot not expanded) */
+        int* node = (int*)malloc(sizeof(int) * (size_t)(W > 0 ? W : 1));
+        for (int w = 0; w < W; ++w) node[w] = -1;
+        if (n0 == 0) {
+            par[0] = -1; tok[0] = -1; prob[0] = 1.0f; conf[0] = 1.0f;
+            n0 = 1;
+            if (W > 0) node[0] = 0;
+        } else {
+            for (int w = 0; w < W; ++w) {
+                int id = expand_in[(size_t)b * W + w];
+                if (id >= 0 && id < n0 && conf[id] >= 0.0f) node[w] = id;
+            }
+        }
+        int n = n0;
+        for (int w = 0; w < W; ++w) {
+            if (node[w] < 0) continue;
+            for (int c = 0; c < C && n < M; ++c) {
+                float q = child_prob[((size_t)b * W + w) * C + c];
+                par[n] = node[w];
+                tok[n] = child_token[((size_t)b * W + w) * C + c];
+                prob[n] = q;
+                conf[n] = (q >= 0.0f && q <= 1.0f) ? conf[node[w]] * q : -1.0f;
+                ++n;
+            }
+        }
+        n_cand[b] = n;
+        OrcExp* list = (OrcExp*)malloc(sizeof(OrcExp) * (size_t)(n - n0 + 1));
+        int nl = 0;
+        for (int i = n0; i < n; ++i)
+            if (conf[i] >= 0.0f) { list[nl].conf = conf[i]; list[nl].idx = i; ++nl; }
+        qsort(list, (size_t)nl, sizeof(OrcExp), orc_exp_cmp);
+        for (int w = 0; w < W; ++w) expand_out[(size_t)b * W + w] = w < nl ? list[w].idx : -1;
+        free(list);
+        free(node);
+    }
+}

@@ -1080,3 +1080,108 @@ def test_check_select_len():
     assert oracle.check_select_len(c, 1, 2, 0.5, [0])[0] == 1
     assert oracle.check_select_len(c, 1, 2, 0.5, [1])[0] == 1
     assert oracle.check_select_len(c, 1, 2, 0.5, [2])[0] == 0
+
+
+# --------------------------------------------------------------------------
+# EAGLE-2-style expansion ([SD §4 EAGLE-2]: expand by cumulative confidence)
+# --------------------------------------------------------------------------
+
+def _expand_full_trie(m, W):
+    """Expansion steps that expand every node: each expanded node's children
+    are all V tokens with the depth's marginal as their probability."""
+    K, V = m.shape
+    M = sum(V ** d for d in range(K + 1))
+    cand = oracle.empty_candidates(1, M)
+    exp_ids = np.full((1, W), -1, np.int32)
+    for d in range(K):
+        ct = np.tile(np.arange(V, dtype=np.int32), (1, W, 1))
+        cp = np.tile(m[d], (1, W, 1)).astype(np.float32)
+        cand = oracle.expand_tree(cand, exp_ids, ct, cp, 1, M, W, V)
+        exp_ids = cand["expand"]
+    return cand, M
+
+
+@pytest.mark.parametrize("N", [4, 9, 20, 40])
+def test_expanding_every_node_then_reranking_is_the_ddtree(N):
+    # with a budget that expands every node, the candidates are the whole
+    # factorised trie, and re-ranking them gives the best-first DDTree of the
+    # same marginals (itself pinned by brute force)
+    rng = np.random.default_rng(61 + N)
+    K, V = 3, 3
+    m = special.softmax(rng.normal(0, 1.5, (K, V)), axis=-1).astype(np.float32)
+    cand, M = _expand_full_trie(m, V ** (K - 1))
+    assert cand["n_cand"][0] == M
+    rr = oracle.rerank_tree(cand["parent"], cand["token"], cand["prob"], cand["n_cand"], 1, M, N)
+    bt = oracle.build_tree(m[None], 1, K, V, N)
+    for key in ("token", "parent", "depth", "score", "anc_mask", "n_nodes"):
+        np.testing.assert_array_equal(rr[key], bt[key], err_msg=key)
+    # the re-ranking's own confidences are the ones the expansion stored
+    np.testing.assert_array_equal(rr["score"][0, 1:], cand["conf"][0, rr["cand"][0, 1:]])
+
+
+def test_expansion_keeps_the_best_branches_brute_force():
+    rng = np.random.default_rng(62)
+    for trial in range(200):
+        W, C = int(rng.integers(1, 4)), int(rng.integers(1, 4))
+        M = 1 + W * C * 3
+        cand = oracle.empty_candidates(1, M)
+        ids = np.full((1, W), -1, np.int32)
+        for layer in range(3):
+            ct = rng.integers(0, 50, (1, W, C)).astype(np.int32)
+            cp = (rng.integers(0, 9, (1, W, C)) / 8.0).astype(np.float32)     # coarse: frequent ties
+            n0 = int(cand["n_cand"][0]) or 1
+            cand = oracle.expand_tree(cand, ids, ct, cp, 1, M, W, C)
+            new = list(range(n0, int(cand["n_cand"][0])))
+            ids = cand["expand"]
+            chosen = [int(i) for i in ids[0] if i >= 0]
+            conf = cand["conf"][0]
+            usable = [i for i in new if conf[i] >= 0]
+            assert len(chosen) == min(W, len(usable))
+            # the chosen set has the largest total confidence of any set of its size,
+            # listed best first, ties by the lower index
+            best = max((sum(float(conf[i]) for i in S) for S in itertools.combinations(usable, len(chosen))),
+                       default=0.0)
+            assert abs(sum(float(conf[i]) for i in chosen) - best) < 1e-7
+            keys = [(-float(conf[i]), i) for i in chosen]
+            assert keys == sorted(keys)
+            if len(chosen) < len(usable):
+                worst = min(float(conf[i]) for i in chosen)
+                assert all(float(conf[i]) <= worst for i in usable if i not in chosen)
+                assert all(i > max(j for j in chosen if conf[j] == worst)
+                           for i in usable if i not in chosen and conf[i] == worst)
+    # the candidates re-rank as usable trees (every parent precedes its child)
+    rr = oracle.rerank_tree(cand["parent"], cand["token"], cand["prob"], cand["n_cand"], 1, M, 8)
+    assert (rr["parent"][0, 1:rr["n_nodes"][0]] < np.arange(1, rr["n_nodes"][0])).all()
+
+
+def test_expansion_root_invalid_slots_and_capacity():
+    B, M, W, C = 1, 7, 2, 2
+    cand = oracle.empty_candidates(B, M)
+    # first step: the root is created and is the one node expanded (slot 1 ignored)
+    out = oracle.expand_tree(cand, [[5, 9]], [[[7, 8], [1, 2]]], [[[0.25, 0.5], [0.9, 0.9]]], B, M, W, C)
+    assert out["n_cand"][0] == 3
+    np.testing.assert_array_equal(out["parent"][0, :3], [-1, 0, 0])
+    np.testing.assert_array_equal(out["token"][0, :3], [-1, 7, 8])
+    np.testing.assert_array_equal(out["conf"][0, :3], [1.0, 0.25, 0.5])
+    np.testing.assert_array_equal(out["expand"][0], [2, 1])
+    # second step: slot 0 names candidate 2 (expanded), slot 1 an index past the
+    # candidates (skipped); a NaN probability is stored but never usable
+    out = oracle.expand_tree(out, [[2, 11]], [[[3, 4], [5, 6]]], [[[np.nan, 0.5], [0.5, 0.5]]], B, M, W, C)
+    assert out["n_cand"][0] == 5
+    np.testing.assert_array_equal(out["parent"][0, 3:5], [2, 2])
+    assert out["conf"][0, 3] == -1.0 and out["conf"][0, 4] == 0.25
+    np.testing.assert_array_equal(out["expand"][0], [4, -1])
+    out = oracle.expand_tree(out, [[4, 3]], [[[1, 2], [3, 4]]], [[[1.0, 1.0], [1.0, 1.0]]], B, M, W, C)
+    assert out["n_cand"][0] == 7                       # candidate 3 is unusable: only node 4 expands
+    np.testing.assert_array_equal(out["parent"][0, 5:7], [4, 4])
+    np.testing.assert_array_equal(out["expand"][0], [5, 6])      # equal confidences: lower index first
+    # full arrays: nothing more is appended and nothing is left to expand
+    out = oracle.expand_tree(out, [[5, 6]], [[[1, 2], [3, 4]]], [[[1.0, 1.0], [1.0, 1.0]]], B, M, W, C)
+    assert out["n_cand"][0] == 7
+    np.testing.assert_array_equal(out["expand"][0], [-1, -1])
+    # children past the end of the arrays are dropped
+    small = oracle.expand_tree(oracle.empty_candidates(1, 4), [[0, 0]], [[[1, 2, 3, 4, 5], [0] * 5]],
+                               [[[0.1, 0.2, 0.3, 0.4, 0.5], [0.0] * 5]], 1, 4, 2, 5)
+    assert small["n_cand"][0] == 4
+    np.testing.assert_array_equal(small["token"][0], [-1, 1, 2, 3])
+    np.testing.assert_array_equal(small["expand"][0], [3, 2])
