@@ -345,50 +345,34 @@ def setup_kv(torch, sd, wl):
 
 
 def setup_rerank(torch, sd, wl):
-    # EAGLE-2-style tree choice: 32 sequences, 1024 expanded candidates each
-    # (8 layers, the 10 best of each layer expanded 10 ways), budget 64
-    import numpy as np
-    B, M, N = 32, 1024, 64
-    rng = np.random.default_rng(1006)
-    par = np.full((B, M), -1, np.int32)
-    tok = np.zeros((B, M), np.int32)
-    prob = np.zeros((B, M), np.float32)
-    n = np.zeros(B, np.int32)
-    for b in range(B):
-        conf, pl, tl, ql, layer = [1.0], [-1], [-1], [1.0], [0]
-        for _ in range(8):
-            grow = sorted(layer, key=lambda c: (-conf[c], c))[:10]
-            layer = []
-            for c in grow:
-                z = rng.normal(0, 2.0, 64)
-                q = np.exp(z - z.max())
-                q = (q / q.sum()).astype(np.float32)
-                for r in np.argsort(-q, kind="stable")[:10]:
-                    if len(pl) >= M:
-                        break
-                    pl.append(c)
-                    tl.append(int(rng.integers(0, 128256)))
-                    ql.append(float(q[r]))
-                    conf.append(float(np.float32(conf[c] * q[r])))
-                    layer.append(len(pl) - 1)
-        k = len(pl)
-        par[b, :k], tok[b, :k], prob[b, :k], n[b] = pl, tl, ql, k
-    t = lambda a: torch.as_tensor(a, device="cuda")
-    par_t, tok_t, prob_t, n_t = t(par), t(tok), t(prob), t(n)
-
+    # EAGLE-2-style dynamic tree: 8 expansion steps (each expands the 10 best
+    # new candidates by cumulative confidence, 10 children each, from the
+    # stand-in drafter's proposals), then the re-ranking of the candidates into
+    # a verification tree of budget 64, for 32 sequences
+    B, M, N, layers, W, C = 32, 1024, 64, 8, 10, 10
+    kids = wl.gen_eagle_children(device="cuda", B=B, layers=layers, W=W, C=C)
+    cand = sd.empty_candidates(B, M)
+    exp = torch.empty(B, W, dtype=torch.int32, device="cuda")
     st = {}
 
     def step(ev=None):
+        cand["n_cand"].zero_()                  # a new tree: the first step writes the root
+        for ct, cp in kids:
+            sd.expand_tree(cand, exp, ct, cp, expand_out=exp)
         if ev is not None:
             sd.time_next_stream_pass(*ev)
-        st["out"] = sd.rerank_tree(par_t, tok_t, prob_t, n_t, N)
+        st["out"] = sd.rerank_tree(cand["parent"], cand["token"], cand["prob"], cand["n_cand"], N)
 
-    meta = {"workload": f"EAGLE-2-style tree choice: B={B}, {M} candidates, budget N={N}",
+    step()
+    torch.cuda.synchronize()
+    n_cand = int(cand["n_cand"].max())
+    meta = {"workload": (f"EAGLE-2-style dynamic tree: {layers} expansion steps (W={W} nodes x C={C} "
+                         f"children each) + re-ranking into a budget-{N} tree, B={B}, {n_cand} candidates"),
             "global_batch": B, "positions_per_step": B * (N - 1),
-            "kernel": "k_rerank_tree", "kernel_bytes": B * M * 12 + B * N * 28,
-            "step_bytes": B * M * 12 + B * N * 28}
-    return step, meta, {"leg": cpu_leg_rerank, "cand": (par, tok, prob, n), "B": B, "M": M, "N": N,
-                        "state": st}
+            "kernel": "k_rerank_tree", "kernel_bytes": B * n_cand * 12 + B * N * 28,
+            "step_bytes": B * n_cand * 12 + B * N * 28 + layers * B * W * C * 8}
+    return step, meta, {"leg": cpu_leg_rerank, "kids": kids, "cand": cand, "B": B, "M": M, "N": N,
+                        "W": W, "C": C, "state": st}
 
 
 def setup_chain1(torch, sd, wl):
@@ -659,29 +643,45 @@ def cpu_leg_kv(cpu, threads):
         bad = int((kv.cpu().numpy() != ref).any(axis=1).sum())
         return {"rows": int(kv0.shape[0]), "row_mismatches": bad, "pass": bad == 0}
 
-    return sample, parity, f"accepted-path KV compaction of all {B} sequences (host copy of the rows)"
+    return sample, parity, f"accepted-path KV compaction of all {B} sequences (host copy of the rows)", True
 
 
 def cpu_leg_rerank(cpu, threads):
     import numpy as np
     import oracle
-    par, tok, prob, n = cpu["cand"]
-    B, M, N = cpu["B"], cpu["M"], cpu["N"]
+    B, M, N, W, C = cpu["B"], cpu["M"], cpu["N"], cpu["W"], cpu["C"]
+    kids = [(t.cpu().numpy(), p.cpu().numpy()) for t, p in cpu["kids"]]
+
+    def run():
+        cand = oracle.empty_candidates(B, M)
+        exp = np.full((B, W), -1, np.int32)
+        for ct, cp in kids:
+            cand = oracle.expand_tree(cand, exp, ct, cp, B, M, W, C)
+            exp = cand["expand"]
+        return cand, oracle.rerank_tree(cand["parent"], cand["token"], cand["prob"], cand["n_cand"], B, M, N)
 
     def sample(nt):
-        oracle.rerank_tree(par, tok, prob, n, B, M, N)
+        run()
         return B * (N - 1)
 
     def parity():
+        ref_c, ref = run()
+        g = {k: v.cpu().numpy() for k, v in cpu["cand"].items()}
+        bad = int((g["n_cand"] != ref_c["n_cand"]).sum())
+        for b in range(B):
+            n = int(ref_c["n_cand"][b])
+            for k in ("parent", "token"):
+                bad += int((g[k][b, :n] != ref_c[k][b, :n]).any())
+            for k in ("prob", "conf"):
+                bad += int((g[k][b, :n].view(np.int32) != ref_c[k][b, :n].view(np.int32)).any())
         out = {k: v.cpu().numpy() for k, v in cpu["state"]["out"].items()}
-        ref = oracle.rerank_tree(par, tok, prob, n, B, M, N)
-        bad = 0
         for k in ("token", "parent", "depth", "score", "cand", "n_nodes"):
             bad += int((out[k] != ref[k]).reshape(B, -1).any(axis=1).sum())
         bad += int((out["anc_mask"].view(np.uint64) != ref["anc_mask"]).any(axis=1).sum())
         return {"tree_sequences": B, "mismatches": bad, "pass": bad == 0}
 
-    return sample, parity, f"re-ranking of all {B} candidate trees ({M} candidates each)"
+    return sample, parity, (f"{len(kids)} expansion steps and the re-ranking for all {B} sequences "
+                            f"(single-threaded C)"), True
 
 
 def run_cpu_baseline(cpu, target_seconds: float):
@@ -692,7 +692,10 @@ def run_cpu_baseline(cpu, target_seconds: float):
 
     threads = int(os.environ.get("OMP_NUM_THREADS", "0")) or oracle.default_threads()
     threads = min(threads, oracle.default_threads())
-    sample, parity, about = cpu["leg"](cpu, threads)
+    leg = cpu["leg"](cpu, threads)
+    sample, parity, about = leg[:3]
+    if len(leg) > 3 and leg[3]:         # a single-threaded oracle routine
+        threads = 1
 
     def timed(nt, seconds):
         units, spent, calls = 0, 0.0, 0
@@ -704,7 +707,7 @@ def run_cpu_baseline(cpu, target_seconds: float):
         return units, spent
 
     units, spent = timed(threads, target_seconds)
-    units1, spent1 = timed(1, target_seconds / 4)
+    units1, spent1 = (units, spent) if threads == 1 else timed(1, target_seconds / 4)
     base = {"value": units / spent, "unit": "positions/s", "cores": threads, "kind": "oracle",
             "value_1thread": units1 / spent1,
             "sample": (f"CPU oracle (fp64 C, OpenMP over sequences): {about}; {units} positions in "

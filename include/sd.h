@@ -92,6 +92,7 @@ typedef enum {
 #define SD_MAX_CANDIDATES 1024
 #define SD_MAX_TREE_K 16
 #define SD_MAX_TOPK 256
+#define SD_MAX_EXPAND 64
 
 /* Returns SD_ABI_VERSION. */
 int sd_abi_version(void);
@@ -302,6 +303,42 @@ sd_status_t sd_verify_tree_sampled(const void* target_logits, sd_dtype_t dtype,
                                    int32_t* path_nodes, int32_t* accepted_len,
                                    int32_t* next_token, int32_t* seq_status, void* workspace,
                                    size_t workspace_bytes, void* hip_stream);
+
+/*
+ * EAGLE-2-style expansion step [SD §4 EAGLE-2: the candidate tree grows by
+ * expanding the branches of highest cumulative path confidence; its
+ * candidates are then re-ranked by sd_rerank_tree]. Per sequence b the
+ * candidates sit in [B, M] arrays in topological order (the layout
+ * sd_rerank_tree reads) with cand_conf, each candidate's cumulative
+ * confidence (-1 for an unusable one). One call adds one layer:
+ *   - n_cand[b] == 0 starts the tree: candidate 0 becomes the root (parent -1,
+ *     token -1, prob 1, conf 1) and is the one node expanded. Otherwise slot
+ *     w < W expands node expand_in[b, w] when 0 <= id < n_cand[b] and
+ *     cand_conf[b, id] >= 0 (other slots are skipped).
+ *   - The children of the node in slot w are child_token[b, w, c] with
+ *     conditional draft probability child_prob[b, w, c] (c < C): the draft's
+ *     proposals for that node, an input. The expanded slots' children are
+ *     appended in slot order, C per slot, from n_cand[b] on, as long as the
+ *     index stays below M (the rest are dropped). A child's parent is its
+ *     node; its confidence is fl32(cand_conf[parent] * prob) when prob lies
+ *     in [0, 1], else -1 (never expanded, and left out by sd_rerank_tree).
+ *   - n_cand[b] is updated, and expand_out[b, 0..W) receives the appended
+ *     candidates with confidence >= 0 ordered by (confidence desc, index asc),
+ *     the first W of them, -1 padded: the nodes the next call expands.
+ *
+ *   cand_parent, cand_token [B, M] int32, cand_prob, cand_conf [B, M] fp32,
+ *   n_cand [B] int32: read and written (only entries from the old n_cand[b]
+ *   on are written, plus the root); expand_in [B, W] int32 (may be NULL when
+ *   every n_cand[b] is 0; may be the same array as expand_out, which is
+ *   written only after it is read); child_token [B, W, C] int32, child_prob
+ *   [B, W, C] fp32. Limits 1 <= M <= SD_MAX_CANDIDATES, 1 <= W <=
+ *   SD_MAX_EXPAND, 1 <= C <= SD_MAX_CANDIDATES. Needs no workspace.
+ */
+sd_status_t sd_expand_tree(int32_t* cand_parent, int32_t* cand_token, float* cand_prob,
+                           float* cand_conf, int32_t* n_cand, const int32_t* expand_in,
+                           int32_t* expand_out, const int32_t* child_token,
+                           const float* child_prob, int32_t B, int32_t M, int32_t W, int32_t C,
+                           void* hip_stream);
 
 /*
  * EAGLE-2-style verification tree [SD §4 EAGLE-2: candidates expanded along

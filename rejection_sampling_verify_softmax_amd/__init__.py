@@ -77,6 +77,8 @@ def _load():
     lib.sd_compact_kv.restype = ctypes.c_int
     lib.sd_rerank_tree.argtypes = [P, P, P, P, I, I, I, P, P, P, P, P, P, P, P]
     lib.sd_rerank_tree.restype = ctypes.c_int
+    lib.sd_expand_tree.argtypes = [P, P, P, P, P, P, P, P, P, I, I, I, I, P]
+    lib.sd_expand_tree.restype = ctypes.c_int
     lib.sd_verify_chain_noalloc.argtypes = [P, P, ctypes.c_int, P, P, P, I, I, I, F, I, P, P, P, P, P, P]
     lib.sd_verify_chain_noalloc.restype = ctypes.c_int
     lib.sd_time_next_stream_pass.argtypes = [P, P]
@@ -516,6 +518,52 @@ def compact_kv(kv: torch.Tensor, row_base: torch.Tensor, path: torch.Tensor,
                               _ptr(accepted_len), B, N, _stream(stream))
     _raise(r, "sd_compact_kv")
     return kv
+
+
+def empty_candidates(B: int, M: int, device="cuda") -> dict:
+    """Candidate arrays for sd_expand_tree before its first call: n_cand = 0
+    (the first call writes the root); the other arrays need no values."""
+    return {"parent": torch.empty(B, M, dtype=torch.int32, device=device),
+            "token": torch.empty(B, M, dtype=torch.int32, device=device),
+            "prob": torch.empty(B, M, dtype=torch.float32, device=device),
+            "conf": torch.empty(B, M, dtype=torch.float32, device=device),
+            "n_cand": torch.zeros(B, dtype=torch.int32, device=device)}
+
+
+def expand_tree(cand: dict, expand_in: Optional[torch.Tensor], child_token: torch.Tensor,
+                child_prob: torch.Tensor, expand_out: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    """sd_expand_tree: one EAGLE-2 expansion step, in place on the candidate
+    arrays of `cand` (parent, token, prob, conf [B, M]; n_cand [B]).
+    child_token / child_prob [B, W, C]: the draft's children of the node in
+    each expand_in slot. Returns expand_out [B, W] (may be expand_in itself)."""
+    dev = cand["parent"].device
+    for k, dt in (("parent", torch.int32), ("token", torch.int32), ("prob", torch.float32),
+                  ("conf", torch.float32), ("n_cand", torch.int32)):
+        _check(cand[k], k, dt, dev)
+    _check(child_token, "child_token", torch.int32, dev)
+    _check(child_prob, "child_prob", torch.float32, dev)
+    B, M = (int(x) for x in cand["parent"].shape)
+    if child_token.dim() != 3 or child_token.shape != child_prob.shape or int(child_token.shape[0]) != B:
+        raise ValueError("child_token and child_prob must both be [B, W, C]")
+    W, C = int(child_token.shape[1]), int(child_token.shape[2])
+    for k in ("token", "prob", "conf"):
+        if tuple(cand[k].shape) != (B, M):
+            raise ValueError(f"cand[{k!r}] must be [B, M] like cand['parent']")
+    if cand["n_cand"].numel() != B:
+        raise ValueError("n_cand needs one entry per sequence")
+    if expand_in is not None:
+        _check(expand_in, "expand_in", torch.int32, dev)
+        if expand_in.numel() != B * W:
+            raise ValueError("expand_in must be [B, W]")
+    out = torch.empty(B, W, dtype=torch.int32, device=dev) if expand_out is None else expand_out
+    _check(out, "expand_out", torch.int32, dev)
+    if out.numel() != B * W:
+        raise ValueError("expand_out must be [B, W]")
+    r = _load().sd_expand_tree(_ptr(cand["parent"]), _ptr(cand["token"]), _ptr(cand["prob"]),
+                               _ptr(cand["conf"]), _ptr(cand["n_cand"]), _ptr(expand_in), _ptr(out),
+                               _ptr(child_token), _ptr(child_prob), B, M, W, C, _stream(stream))
+    _raise(r, "sd_expand_tree")
+    return out
 
 
 def rerank_tree(cand_parent: torch.Tensor, cand_token: torch.Tensor, cand_prob: torch.Tensor,

@@ -345,6 +345,21 @@ sd_status_t sd_select_len_table(const float* conf, int32_t B, int32_t K_max,
                                           cu_sel, static_cast<hipStream_t>(hip_stream)));
 }
 
+sd_status_t sd_expand_tree(int32_t* cand_parent, int32_t* cand_token, float* cand_prob,
+                           float* cand_conf, int32_t* n_cand, const int32_t* expand_in,
+                           int32_t* expand_out, const int32_t* child_token, const float* child_prob,
+                           int32_t B, int32_t M, int32_t W, int32_t C, void* hip_stream) {
+    if (B < 1 || B > kMaxB || M < 1 || M > SD_MAX_CANDIDATES || W < 1 || W > SD_MAX_EXPAND ||
+        C < 1 || C > SD_MAX_CANDIDATES)
+        return SD_EINVAL;
+    if (!cand_parent || !cand_token || !cand_prob || !cand_conf || !n_cand || !expand_out ||
+        !child_token || !child_prob)
+        return SD_EINVAL;
+    return from_hip(sd::launch_expand_tree(cand_parent, cand_token, cand_prob, cand_conf, n_cand,
+                                           expand_in, expand_out, child_token, child_prob, B, M, W, C,
+                                           static_cast<hipStream_t>(hip_stream)));
+}
+
 sd_status_t sd_compact_kv(void* kv, int64_t row_bytes, int64_t n_rows, const int64_t* row_base,
                           const int32_t* path_nodes, const int32_t* accepted_len, int32_t B,
                           int32_t N, void* hip_stream) {

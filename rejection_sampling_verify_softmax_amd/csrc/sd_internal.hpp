@@ -122,6 +122,10 @@ hipError_t launch_rerank_tree(const int32_t* cand_parent, const int32_t* cand_to
                               const float* cand_prob, const int32_t* n_cand, int B, int M, int N,
                               int32_t* tok, int32_t* par, int32_t* dep, float* score, uint64_t* anc,
                               int32_t* node_cand, int32_t* n_nodes, hipStream_t stream);
+hipError_t launch_expand_tree(int32_t* cand_parent, int32_t* cand_token, float* cand_prob,
+                              float* cand_conf, int32_t* n_cand, const int32_t* expand_in,
+                              int32_t* expand_out, const int32_t* child_token, const float* child_prob,
+                              int B, int M, int W, int C, hipStream_t stream);
 hipError_t launch_select_len(const float* conf, int B, int K_max, float cost, const float* table,
                              int32_t* k_sel, float* adv, int32_t* cu_sel, hipStream_t stream);
 

@@ -32,8 +32,9 @@ constexpr int kCandPerThread = kMaxCand / kBlock;
 constexpr int kSelCap = 256;     // candidates the threshold path ranks by counting
 
 __device__ __forceinline__ uint32_t conf_bits(float x) {
-    // x in [0, 1]: its bits order it (no negatives, no NaN)
-    return __float_as_uint(x);
+    // x in [0, 1] (a -0 probability gives -0): its bits order it once -0
+    // counts as +0 (no other negatives, no NaN)
+    return x == 0.f ? 0u : __float_as_uint(x);
 }
 
 __global__ __launch_bounds__(kBlock) void k_rerank_tree(
@@ -234,7 +235,123 @@ __global__ __launch_bounds__(kBlock) void k_rerank_tree(
     }
 }
 
+// EAGLE-2 expansion step (same page, §4 EAGLE-2: branches are expanded along
+// high cumulative confidence). One workgroup per sequence: wave 0 lists the
+// expanded nodes in slot order (a ballot gives each its rank), every thread
+// appends children, C per expanded node, with confidence fl32(parent
+// confidence x probability) (-1 when the probability is not in [0, 1]); the
+// next nodes to expand are the W best new candidates by (confidence desc,
+// index asc), ranked by counting over 64-bit keys in LDS.
+constexpr int kMaxExpandW = 64;
+
+__global__ __launch_bounds__(kBlock) void k_expand_tree(
+    int32_t* __restrict__ cand_parent, int32_t* __restrict__ cand_token, float* __restrict__ cand_prob,
+    float* __restrict__ cand_conf, int32_t* __restrict__ n_cand, const int32_t* expand_in,
+    int32_t* expand_out, const int32_t* __restrict__ child_token,
+    const float* __restrict__ child_prob, int M, int W, int C) {
+    __shared__ int s_node[kMaxExpandW];        // the r-th expanded node, in slot order
+    __shared__ int s_slot[kMaxExpandW];        // its slot
+    __shared__ float s_pconf[kMaxExpandW];     // its confidence
+    __shared__ unsigned long long keys[kMaxCand];
+    __shared__ int s_n0, s_nexp;
+    __shared__ int s_cnt[kWavesPerBlock];
+    const int b = blockIdx.x;
+    const int tid = threadIdx.x;
+    const int64_t o = (int64_t)b * M;
+    // 1. the nodes expanded by this call (expand_in is read before any write
+    //    to expand_out, so the two may be one array)
+    if (tid < kWave) {
+        int n0 = n_cand[b];
+        n0 = n0 < 0 ? 0 : (n0 > M ? M : n0);
+        const bool root = n0 == 0;
+        int id = -1;
+        float pc = 0.f;
+        if (tid < W) {
+            if (root) {
+                id = tid == 0 ? 0 : -1;
+                pc = 1.0f;
+            } else if (expand_in != nullptr) {
+                id = expand_in[(int64_t)b * W + tid];
+                if (id >= 0 && id < n0) {
+                    pc = cand_conf[o + id];
+                    if (!(pc >= 0.f)) id = -1;
+                } else {
+                    id = -1;
+                }
+            }
+        }
+        if (root && tid == 0) {                 // the tree starts at its root
+            cand_parent[o] = -1;
+            cand_token[o] = -1;
+            cand_prob[o] = 1.0f;
+            cand_conf[o] = 1.0f;
+        }
+        const unsigned long long m = __ballot(id >= 0);
+        const int r = __popcll(m & ((1ull << tid) - 1ull));
+        if (id >= 0) {
+            s_node[r] = id;
+            s_slot[r] = tid;
+            s_pconf[r] = pc;
+        }
+        if (tid == 0) {
+            s_n0 = root ? 1 : n0;
+            s_nexp = __popcll(m);
+        }
+    }
+    __syncthreads();
+    const int n0 = s_n0;
+    const int room = M - n0;
+    const int nnew = min(s_nexp * C, room);
+    // 2. the children of the expanded nodes, appended in slot order
+    for (int j = tid; j < nnew; j += kBlock) {
+        const int r = j / C, c = j - (j / C) * C;
+        const int64_t src = ((int64_t)b * W + s_slot[r]) * C + c;
+        const float q = child_prob[src];
+        const float cf = (q >= 0.f && q <= 1.f) ? s_pconf[r] * q : -1.0f;
+        const int i = n0 + j;
+        cand_parent[o + i] = s_node[r];
+        cand_token[o + i] = child_token[src];
+        cand_prob[o + i] = q;
+        cand_conf[o + i] = cf;
+        // (confidence desc, index asc) as one key; +0 and -0 order alike; 0 = unusable
+        const uint32_t cb = conf_bits(cf);
+        keys[j] = cf >= 0.f ? (((unsigned long long)cb << 32) | (0xffffffffu - (uint32_t)i)) : 0ull;
+    }
+    __syncthreads();
+    // 3. the W best new candidates: rank = number of larger keys (keys are distinct)
+    int usable = 0;
+    for (int j = tid; j < nnew; j += kBlock) {
+        const unsigned long long k = keys[j];
+        if (k == 0ull) continue;
+        ++usable;
+        int rank = 0;
+        for (int i = 0; i < nnew; ++i) rank += keys[i] > k ? 1 : 0;
+        if (rank < W) expand_out[(int64_t)b * W + rank] = n0 + j;
+    }
+    // the usable count over the block; the slots past it get -1
+    int cnt = usable;
+#pragma unroll
+    for (int off = kWave / 2; off > 0; off >>= 1) cnt += __shfl_xor(cnt, off, kWave);
+    if ((tid & (kWave - 1)) == 0) s_cnt[tid / kWave] = cnt;
+    __syncthreads();
+    int total = 0;
+#pragma unroll
+    for (int w = 0; w < kWavesPerBlock; ++w) total += s_cnt[w];
+    if (tid < W && tid >= total) expand_out[(int64_t)b * W + tid] = -1;
+    if (tid == 0) n_cand[b] = n0 + nnew;
+}
+
 }  // namespace
+
+hipError_t launch_expand_tree(int32_t* cand_parent, int32_t* cand_token, float* cand_prob,
+                              float* cand_conf, int32_t* n_cand, const int32_t* expand_in,
+                              int32_t* expand_out, const int32_t* child_token, const float* child_prob,
+                              int B, int M, int W, int C, hipStream_t stream) {
+    hipLaunchKernelGGL(k_expand_tree, dim3(B), dim3(kBlock), 0, stream, cand_parent, cand_token,
+                       cand_prob, cand_conf, n_cand, expand_in, expand_out, child_token, child_prob, M,
+                       W, C);
+    return hipGetLastError();
+}
 
 hipError_t launch_rerank_tree(const int32_t* cand_parent, const int32_t* cand_token,
                               const float* cand_prob, const int32_t* n_cand, int B, int M, int N,

@@ -1145,12 +1145,13 @@ __device__ __forceinline__ unsigned long long shift_pick64(unsigned long long v,
 // written nothing, when the list is shorter or C exceeds kBuildCap; the pop
 // loop then builds the tree.
 // The pop order of the threshold path's members as one 64-bit key, larger
-// first: score (positive, so its bits order it), then lower depth, then lower
-// slot. Within a depth the members are enumerated in rank-tuple order (the
+// first: score (non-negative, so its bits order it once a -0 product counts
+// as +0), then lower depth, then lower slot. Within a depth the members are enumerated in rank-tuple order (the
 // children of a level by parent slot, then by their own rank), so slot order
 // there is the tuple order.
 __device__ __forceinline__ unsigned long long pop_key(float Q, int depth, int slot) {
-    return ((unsigned long long)__float_as_uint(Q) << 32) | ((unsigned long long)(31 - depth) << 16) |
+    return ((unsigned long long)(Q == 0.f ? 0u : __float_as_uint(Q)) << 32) |
+           ((unsigned long long)(31 - depth) << 16) |
            (unsigned long long)(0xffff - slot);
 }
 

@@ -12,7 +12,10 @@ outputs are the verify step's inputs:
   with the Gumbel-max trick (argmax of logit/T + Gumbel noise over its kept set),
   which never forms the probabilities themselves;
 * a block drafter whose per-position marginals are the softmax of Gaussian
-  logits (the DDTree workload feeds these marginals in as data).
+  logits (the DDTree workload feeds these marginals in as data);
+* an EAGLE-2-style drafter that proposes, for each node it is asked to
+  expand, C children with their conditional probabilities (the C largest of
+  a softmax of Gaussian logits over a few dozen proposals) and uniform ids.
 
 Every generator takes a torch device. Full-size workloads are drawn on the GPU
 (the host's RNG is far too slow for a billion draws); small test cases are drawn
@@ -35,6 +38,9 @@ Workload recipes (sigma is a standard deviation throughout):
 * gen_tree -- tree, B=32, K=16, V=32000, N=64: Z ~ N(0, 2.5) per (sequence, depth);
   marginals are softmax(Z) in fp32; the target row of a node at depth d < K is
   bf16(Z[d] + N(0, 1)), and a node at depth K gets fresh N(0, 2.5).
+* gen_eagle_children -- EAGLE-2 expansion, B=32 sequences, 8 layers, W=10 nodes expanded per
+  layer, C=10 children each: probabilities are the 10 largest of softmax(N(0, 2)) over 64
+  proposals (largest first), tokens uniform in [0, 128256).
 * gen_adaptive_chain -- adaptive chain, B=512, K_max=8, V=128256: confidences c ~ Beta(5, 2) (the
   5th smallest of 6 uniforms); draft base D ~ N(0, 2) with K_max+1 rows;
   target = bf16(D + N(0, 0.7)); draft rows bf16(D); T = 1.
@@ -304,6 +310,18 @@ def gen_tree(device="cpu", seed: int = 1004, B: int = 32, K: int = 16, V: int = 
     marg = torch.softmax(Z, dim=-1).to(torch.float32).contiguous()
     return TreeCase(B=B, K=K, V=V, N=N, marginals=marg, Z=Z, seed=seed,
                     name=f"tree-B{B}-K{K}-V{V}-N{N}")
+
+
+def gen_eagle_children(device="cpu", seed: int = 1006, B: int = 32, layers: int = 8, W: int = 10,
+                       C: int = 10, V: int = 128256, width: int = 64, sigma: float = 2.0):
+    """Stand-in drafter outputs for the EAGLE-2 expansion steps: per layer a pair
+    (child_token [B, W, C] int32, child_prob [B, W, C] fp32), slot w holding the
+    children of the node expanded in that slot."""
+    gb, gt = _gen(seed, "base", device), _gen(seed, "draft_sample", device)
+    z = torch.randn(layers, B, W, width, generator=gb, device=device) * sigma
+    probs = torch.topk(torch.softmax(z, dim=-1), C, dim=-1).values.to(torch.float32)
+    tokens = torch.randint(0, V, (layers, B, W, C), generator=gt, device=device, dtype=torch.int32)
+    return [(tokens[i].contiguous(), probs[i].contiguous()) for i in range(layers)]
 
 
 def gen_adaptive_chain(device="cpu", seed: int = 1005, B: int = 512, K: int = 8, V: int = 128256,

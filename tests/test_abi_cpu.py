@@ -252,3 +252,19 @@ def test_noalloc_rejects_before_any_hip_call(L):
     # a batch whose scratch need exceeds the library's static array
     assert na(B=5109, K=8, V=128256) == 3        # SD_EWORKSPACE, nothing launched (bf16 fits 5108)
     assert na(B=2607, K=8, V=128256, dtype=0) == 3
+
+
+def test_expand_tree_rejects_invalid_arguments(L):
+    one = ctypes.c_void_p(16)
+
+    def ex(B=2, M=100, W=10, C=10, first=one, kids=one, out=one):
+        return L.sd_expand_tree(first, one, one, one, one, None, out, kids, one, B, M, W, C, None)
+    assert ex(B=0) == 1
+    assert ex(M=0) == 1
+    assert ex(M=1025) == 1
+    assert ex(W=0) == 1
+    assert ex(W=65) == 1
+    assert ex(C=0) == 1
+    assert ex(first=None) == 1
+    assert ex(kids=None) == 1
+    assert ex(out=None) == 1

@@ -520,6 +520,16 @@ def test_tree_build_ties():
     out = sd.build_tree(m, N)
     ref = oracle.build_tree(m.cpu().numpy(), B, K, V, N)
     _tree_compare(out, ref)
+    # zero marginals, half of them -0 (the products tie with +0 ones): rows
+    # with fewer positive entries than the budget
+    z = torch.zeros(B, K, V, device="cuda")
+    z[:, :, 5:9] = 0.25
+    z[:, 1::2, 20:] = -0.0
+    z[2, 0] = -0.0
+    z[2, 0, 3] = 1.0
+    out = sd.build_tree(z, N)
+    ref = oracle.build_tree(z.cpu().numpy(), B, K, V, N)
+    _tree_compare(out, ref)
 
 
 # Rows of up to 32768 fp32 marginals take the register-resident top-k (one
@@ -675,6 +685,64 @@ def test_rerank_tree_ties_and_short_lists():
         np.testing.assert_array_equal(out[key].cpu().numpy(), ref[key], err_msg=key)
     np.testing.assert_array_equal(out["anc_mask"].cpu().numpy().view(np.uint64), ref["anc_mask"])
     assert ref["n_nodes"][0] == N and ref["n_nodes"][1] == 20
+
+
+def _cand_equal(g, ref, B):
+    np.testing.assert_array_equal(g["n_cand"].cpu().numpy(), ref["n_cand"])
+    gh = {k: g[k].cpu().numpy() for k in ("parent", "token", "prob", "conf")}
+    for b in range(B):
+        n = int(ref["n_cand"][b])
+        for k in ("parent", "token"):
+            np.testing.assert_array_equal(gh[k][b, :n], ref[k][b, :n], err_msg=f"{k} seq {b}")
+        for k in ("prob", "conf"):          # bit patterns: NaN, -0 and products exactly
+            np.testing.assert_array_equal(gh[k][b, :n].view(np.int32), ref[k][b, :n].view(np.int32),
+                                          err_msg=f"{k} seq {b}")
+
+
+@pytest.mark.parametrize("B,M,W,C,layers,kind", [(32, 1024, 10, 10, 8, "eagle"), (300, 200, 7, 5, 6, "coarse"),
+                                                 (5, 1024, 64, 16, 3, "coarse"), (9, 64, 3, 40, 4, "bad")])
+def test_expand_tree_matches_oracle(B, M, W, C, layers, kind):
+    _say(f"EAGLE-2 expansion B={B} M={M} W={W} C={C} layers={layers} {kind}")
+    g = torch.Generator(device="cuda").manual_seed(B + M + W + C)
+    if kind == "eagle":
+        kids = wl.gen_eagle_children(device="cuda", seed=B, B=B, layers=layers, W=W, C=C)
+    else:
+        kids = []
+        for _ in range(layers):
+            ct = torch.randint(0, 1000, (B, W, C), generator=g, device="cuda", dtype=torch.int32)
+            cp = torch.randint(0, 9, (B, W, C), generator=g, device="cuda").float() / 8   # ties
+            if kind == "bad":      # probabilities outside [0, 1], NaN and -0 (stored, never expanded)
+                r = torch.rand(B, W, C, generator=g, device="cuda")
+                cp = torch.where(r < 0.1, torch.full_like(cp, float("nan")), cp)
+                cp = torch.where((r >= 0.1) & (r < 0.2), cp + 1.5, cp)
+                cp = torch.where((r >= 0.2) & (r < 0.3), torch.full_like(cp, -0.0), cp)
+            kids.append((ct.contiguous(), cp.contiguous()))
+    cand = sd.empty_candidates(B, M)
+    ref = oracle.empty_candidates(B, M)
+    exp = torch.full((B, W), -1, dtype=torch.int32, device="cuda")
+    ref_exp = np.full((B, W), -1, np.int32)
+    for layer, (ct, cp) in enumerate(kids):
+        if kind == "bad" and layer == 2:   # slots naming nothing, past the candidates, or unusable
+            exp[:, 0] = -1
+            exp[:, 1] = M + 5
+            conf = cand["conf"].cpu().numpy()
+            unusable = [int(np.nonzero(conf[b, :int(ref["n_cand"][b])] < 0)[0][0])
+                        if (conf[b, :int(ref["n_cand"][b])] < 0).any() else 0 for b in range(B)]
+            exp[:, 2] = torch.tensor(unusable, dtype=torch.int32, device="cuda")
+            ref_exp = exp.cpu().numpy()
+        sd.expand_tree(cand, exp, ct, cp, expand_out=exp)
+        ref = oracle.expand_tree(ref, ref_exp, ct.cpu().numpy(), cp.cpu().numpy(), B, M, W, C)
+        ref_exp = ref["expand"]
+        _cand_equal(cand, ref, B)
+        np.testing.assert_array_equal(exp.cpu().numpy(), ref_exp, err_msg=f"expand, layer {layer}")
+    N = 64
+    out = sd.rerank_tree(cand["parent"], cand["token"], cand["prob"], cand["n_cand"], N)
+    rr = oracle.rerank_tree(ref["parent"], ref["token"], ref["prob"], ref["n_cand"], B, M, N)
+    for k in ("token", "parent", "depth", "score", "cand", "n_nodes"):
+        np.testing.assert_array_equal(out[k].cpu().numpy(), rr[k], err_msg=k)
+    np.testing.assert_array_equal(out["anc_mask"].cpu().numpy().view(np.uint64), rr["anc_mask"])
+    _say(f"  candidates {int(ref['n_cand'].min())}..{int(ref['n_cand'].max())}, "
+         f"tree nodes {int(rr['n_nodes'].min())}..{int(rr['n_nodes'].max())}")
 
 
 def test_rerank_tree_then_walks():
