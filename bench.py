@@ -16,7 +16,7 @@ bounded sample of the same workload, and the parity of the timed step against
 that oracle run (verify lengths of every sequence, committed results of the
 sampled sequences; bit-exact outside the oracle's margin cases).
 
-Other workloads (--workload greedy|topk|tree|tree_sampled|tree_sampled_topk|chain1|kv|rerank)
+Other workloads (--workload adaptive_table|greedy|topk|tree|tree_sampled|tree_sampled_topk|chain1|kv|rerank)
 measure the other kernels
 for the design notes; their inputs are rotated across copies so that the
 working set exceeds the 256 MB last-level cache.
@@ -100,6 +100,30 @@ def load_traffic(kernel: str, workload: str):
 # one step on the current stream.
 # --------------------------------------------------------------------------
 
+def adaptive_bytes(k_sel, A, B, K, V):
+    """Algorithmic bytes of a packed adaptive step (bf16 rows): (first-phase
+    streaming launch, whole step, rows of phase 1, rows of phase 2). Phase 1
+    streams positions 0 and 1 (and the extra-token row of a shorter draft) of
+    every sequence; phase 2 the rest of the window only for sequences whose
+    first two drafts were both accepted."""
+    import numpy as np
+    k_sel = k_sel.cpu().numpy().astype(np.int64)
+    A = A.cpu().numpy().astype(np.int64)
+    R_d = int(k_sel.sum())
+    R_t = R_d + B
+    split = 2
+    t1, d1 = np.minimum(k_sel + 1, split), np.minimum(k_sel, split)
+    alive = (k_sel >= split) & (A >= split)
+    t2 = np.where(alive, k_sel + 1 - split, 0)
+    d2 = np.where(alive, k_sel - split, 0)
+    rows1, rows2 = int(t1.sum() + d1.sum()), int(t2.sum() + d2.sum())
+    stats_bytes = rows1 * V * 2 + int(d1.sum()) * 4           # first-phase rows once + draft tokens
+    step_bytes = ((rows1 + rows2) * V * 2 + R_d * 4 + R_t * 4  # rows streamed, tokens, uniforms
+                  + B * K * 4 + B * (4 + 4 + 4) + (B + 1) * 4  # conf in; k, adv, cu out
+                  + B * 12)                                    # A, next, status out
+    return stats_bytes, step_bytes, rows1, rows2
+
+
 def setup_adaptive(torch, sd, wl):
     import numpy as np
 
@@ -115,21 +139,7 @@ def setup_adaptive(torch, sd, wl):
                                             validate=True).items()}
     ws = torch.empty(sd.workspace_bytes(sd.OP_CHAIN, B, K, V), dtype=torch.uint8, device="cuda")
     sel_out = {"k": sel["k"], "adv": sel["adv"], "cu": sel["cu"]}
-    # Rows the verification streams: positions 0 and 1 (and the extra-token
-    # row of a shorter draft) of every sequence in the first phase, the rest of
-    # the window only for sequences whose first two drafts were both accepted.
-    k_sel = sel["k"].cpu().numpy().astype(np.int64)
-    A = out["accepted_len"].cpu().numpy().astype(np.int64)
-    split = 2
-    t1, d1 = np.minimum(k_sel + 1, split), np.minimum(k_sel, split)
-    alive = (k_sel >= split) & (A >= split)
-    t2 = np.where(alive, k_sel + 1 - split, 0)
-    d2 = np.where(alive, k_sel - split, 0)
-    rows1, rows2 = int(t1.sum() + d1.sum()), int(t2.sum() + d2.sum())
-    stats_bytes = rows1 * V * 2 + int(d1.sum()) * 4           # first-phase rows once + draft tokens
-    step_bytes = ((rows1 + rows2) * V * 2 + R_d * 4 + R_t * 4  # rows streamed, tokens, uniforms
-                  + B * K * 4 + B * (4 + 4 + 4) + (B + 1) * 4  # conf in; k, adv, cu out
-                  + B * 12)                                    # A, next, status out
+    stats_bytes, step_bytes, rows1, rows2 = adaptive_bytes(sel["k"], out["accepted_len"], B, K, V)
 
     def step(ev=None):
         s = sd.select_len(case.conf, case.cost, out=sel_out)
@@ -145,10 +155,91 @@ def setup_adaptive(torch, sd, wl):
         "global_batch": B, "K_max": K, "V": V, "logits": "bf16", "temperature": 1.0,
         "positions_per_step": positions, "target_rows": R_t, "draft_rows": R_d,
         "kernel": "k_chain_stats", "kernel_bytes": stats_bytes, "step_bytes": step_bytes,
-        "mean_k": positions / B, "mean_A": float(A.mean()),
+        "mean_k": positions / B, "mean_A": out["accepted_len"].float().mean().item(),
         "rows_streamed": rows1 + rows2, "rows_in_windows": R_t + R_d,
     }
     cpu = {"leg": cpu_leg_adaptive, "case": case, "packed": packed, "out": out, "sel": sel_out}
+    return step, meta, cpu
+
+
+def measure_cost_table(torch, sd, case, reps=30):
+    """Per-position cost table of the verify step on this GPU (the DSpark
+    scheduler's table, profiled on the deployment that uses it). For every
+    fixed window k = 0..K_max the packed verification of all B sequences over
+    their first k positions is timed (median of `reps` calls, HIP events on the
+    stream it runs on); dt_j = t(j) - t(j-1) is the verify time that position
+    j adds to the batch. In tokens of advance, at the full window's operating
+    point (throughput E[adv(K)] * B / t(K) tokens per second, with the
+    expected advance from sd_select_len), position j costs
+    cost[j-1] = E[adv(K)] * dt_j / t(K) per sequence. Only the verify step's
+    own time is in it, not the target forward's."""
+    import statistics
+    B, K = case.B, case.K_max
+    times = []
+    for k in range(K + 1):
+        pk = case.packed(torch.full((B,), k, dtype=torch.int64))
+        ws = torch.empty(sd.workspace_bytes(sd.OP_CHAIN, B, k, case.V), dtype=torch.uint8, device="cuda")
+        out = sd.verify_chain(pk.target, pk.draft, pk.tokens, pk.uniforms, 1.0, cu=pk.cu, B=B, K_max=k,
+                              workspace=ws)
+        for _ in range(3):
+            sd.verify_chain(pk.target, pk.draft, pk.tokens, pk.uniforms, 1.0, cu=pk.cu, B=B, K_max=k,
+                            workspace=ws, out=out)
+        ms = []
+        for _ in range(reps):
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record()
+            sd.verify_chain(pk.target, pk.draft, pk.tokens, pk.uniforms, 1.0, cu=pk.cu, B=B, K_max=k,
+                            workspace=ws, out=out)
+            b.record()
+            b.synchronize()
+            ms.append(a.elapsed_time(b))
+        times.append(statistics.median(ms))
+        del pk, ws, out
+    adv_full = float(sd.select_len(case.conf, -1.0)["adv"].mean())     # every s_j > -1: k = K_max
+    dt = [times[j] - times[j - 1] for j in range(1, K + 1)]
+    table = [adv_full * d / times[K] for d in dt]
+    return {"t_ms": times, "dt_ms": dt, "adv_full_window": adv_full, "cost": table}
+
+
+def setup_adaptive_table(torch, sd, wl):
+    # the adaptive step with verify lengths chosen from the per-position cost
+    # table measured on this GPU (instead of the constant 0.15)
+    case = wl.gen_adaptive_chain(device="cuda")
+    log("measuring the per-position cost table (fixed windows k = 0..8)")
+    ct = measure_cost_table(torch, sd, case)
+    table = torch.tensor(ct["cost"], dtype=torch.float32, device="cuda")
+    log("cost table: " + " ".join(f"{c:.4f}" for c in ct["cost"]) +
+        "  (t(k) ms: " + " ".join(f"{t:.4f}" for t in ct["t_ms"]) + ")")
+    sel = sd.select_len_table(case.conf, table)
+    torch.cuda.synchronize()
+    packed = case.packed(sel["k"])
+    B, K, V = case.B, case.K_max, case.V
+    positions = int(sel["cu"][-1].item())
+    ws = torch.empty(sd.workspace_bytes(sd.OP_CHAIN, B, K, V), dtype=torch.uint8, device="cuda")
+    out = sd.verify_chain(packed.target, packed.draft, packed.tokens, packed.uniforms, 1.0, cu=sel["cu"],
+                          B=B, K_max=K, workspace=ws)
+    sel_out = {"k": sel["k"], "adv": sel["adv"], "cu": sel["cu"]}
+
+    def step(ev=None):
+        s = sd.select_len_table(case.conf, table, out=sel_out)
+        if ev is not None:
+            sd.time_next_stream_pass(*ev)
+        sd.verify_chain(packed.target, packed.draft, packed.tokens, packed.uniforms, 1.0,
+                        cu=s["cu"], B=B, K_max=K, workspace=ws, out=out)
+
+    torch.cuda.synchronize()
+    A = out["accepted_len"].float().mean().item()
+    stats_bytes, step_bytes, rows1, rows2 = adaptive_bytes(sel["k"], out["accepted_len"], B, K, V)
+    meta = {"workload": (f"DSpark-adaptive chain verify with a measured cost table: select_len_table "
+                         f"(per-position costs measured on this GPU) + packed stochastic verify, "
+                         f"B={B}, K_max={K}, V={V}, bf16 logits, T=1.0"),
+            "global_batch": B, "K_max": K, "V": V, "logits": "bf16", "temperature": 1.0,
+            "positions_per_step": positions, "kernel": "k_chain_stats",
+            "kernel_bytes": stats_bytes, "step_bytes": step_bytes, "mean_k": positions / B, "mean_A": A,
+            "mean_adv": float(sel["adv"].mean()), "cost_table": ct, "rows_streamed": rows1 + rows2,
+            "rows_in_windows": 2 * positions + B}
+    cpu = {"leg": cpu_leg_adaptive, "case": case, "packed": packed, "out": out, "sel": sel_out,
+           "table": table.cpu().numpy()}
     return step, meta, cpu
 
 
@@ -393,7 +484,7 @@ def setup_chain1(torch, sd, wl):
     return step, meta, {"leg": cpu_leg_chain, "case": case, "state": st}
 
 
-WORKLOADS = {"adaptive": setup_adaptive, "greedy": setup_greedy, "topk": setup_topk,
+WORKLOADS = {"adaptive": setup_adaptive, "adaptive_table": setup_adaptive_table, "greedy": setup_greedy, "topk": setup_topk,
              "tree": setup_tree, "tree_sampled": setup_tree_sampled,
              "tree_sampled_topk": setup_tree_sampled_topk, "chain1": setup_chain1,
              "kv": setup_kv, "rerank": setup_rerank}
@@ -463,9 +554,16 @@ def cpu_leg_adaptive(cpu, threads):
     groups = [_host_chain(packed, g) for g in _groups(B, 16)[:8]]     # the first 128 sequences
     state = {"i": 0, "sel": True}
 
+    table = cpu.get("table")
+
+    def select():
+        if table is None:
+            return oracle.select_len(conf, B, case.K_max, case.cost)
+        return oracle.select_len_table(conf, B, case.K_max, table)
+
     def sample(nt):
         if state["sel"]:                    # length selection for the whole batch, once per pass
-            oracle.select_len(conf, B, case.K_max, case.cost)
+            select()
         g = groups[state["i"] % len(groups)]
         state["i"] += 1
         state["sel"] = state["i"] % len(groups) == 0
@@ -475,9 +573,12 @@ def cpu_leg_adaptive(cpu, threads):
 
     def parity():
         k_g = cpu["sel"]["k"].cpu().numpy()
-        sel = oracle.select_len(conf, B, case.K_max, case.cost)
+        sel = select()
         sel_mg = sel["margin"] != 0
-        ok_sel = oracle.check_select_len(conf, B, case.K_max, case.cost, k_g) == 1
+        if table is None:
+            ok_sel = oracle.check_select_len(conf, B, case.K_max, case.cost, k_g) == 1
+        else:                               # no validity check for the table rule: margins must match
+            ok_sel = k_g == sel["k"]
         out = cpu["out"]
         A, nx, st = (out[k].cpu().numpy() for k in ("accepted_len", "next_token", "status"))
         par = {"select_len_sequences": B,
@@ -857,9 +958,11 @@ def main():
     for k in ("logits", "temperature", "mean_k"):
         if k in meta:
             result["config"][k] = meta[k]
-    for k in ("mean_A", "max_A", "rows_streamed", "rows_in_windows"):
+    for k in ("mean_A", "max_A", "rows_streamed", "rows_in_windows", "mean_adv"):
         if k in meta:
             result["step"][k] = meta[k]
+    if "cost_table" in meta:
+        result["cost_table"] = meta["cost_table"]
     if cpu is not None and not args.no_cpu_baseline:
         log("timing the CPU oracle on a bounded sample; parity of the timed step against it")
         result["cpu_baseline"], result["parity"] = run_cpu_baseline(cpu, args.cpu_seconds)
