@@ -975,7 +975,9 @@ def test_gpu_sampled_walk_tokens_follow_target():
 
 def test_select_len_parity():
     g = torch.Generator(device="cuda").manual_seed(8)
-    for B, K, cost in ((512, 8, 0.15), (3, 64, 0.01), (1000, 5, 0.5), (700, 0, 0.1)):
+    # up to 8192 sequences one workgroup; beyond, one thread per sequence and a scan workgroup
+    for B, K, cost in ((512, 8, 0.15), (3, 64, 0.01), (1000, 5, 0.5), (700, 0, 0.1), (8192, 8, 0.15),
+                       (8193, 8, 0.15), (300001, 8, 0.15), (1 << 20, 3, 0.3), (20000, 0, 0.1)):
         conf = torch.sort(torch.rand(B, K, 6, generator=g, device="cuda"), dim=-1).values[..., 4].contiguous() \
             if K > 0 else torch.zeros(B, 0, device="cuda")
         out = sd.select_len(conf, cost)
@@ -987,7 +989,7 @@ def test_select_len_parity():
 
 def test_select_len_table_parity():
     g = torch.Generator(device="cuda").manual_seed(9)
-    for B, K in ((512, 8), (5, 64), (300, 3), (40, 0)):
+    for B, K in ((512, 8), (5, 64), (300, 3), (40, 0), (70000, 8)):
         conf = torch.sort(torch.rand(B, K, 6, generator=g, device="cuda"), dim=-1).values[..., 4].contiguous() \
             if K > 0 else torch.zeros(B, 0, device="cuda")
         table = (torch.rand(max(K, 1), generator=g, device="cuda") * 0.4).contiguous()
