@@ -16,7 +16,8 @@ bounded sample of the same workload, and the parity of the timed step against
 that oracle run (verify lengths of every sequence, committed results of the
 sampled sequences; bit-exact outside the oracle's margin cases).
 
-Other workloads (--workload adaptive_table|greedy|topk|tree|tree_sampled|tree_sampled_topk|chain1|kv|rerank)
+Other workloads (--workload adaptive_table|greedy|topk|tree|tree_sampled|tree_sampled_topk|chain1|kv|rerank|
+readceiling_66m|readceiling_1g)
 measure the other kernels
 for the design notes; their inputs are rotated across copies so that the
 working set exceeds the 256 MB last-level cache.
@@ -484,10 +485,40 @@ def setup_chain1(torch, sd, wl):
     return step, meta, {"leg": cpu_leg_chain, "case": case, "state": st}
 
 
+def setup_readceiling(torch, sd, wl, nbytes, copies, n_blocks=2048):
+    # a plain streaming read of nbytes (16-byte non-temporal loads, the load of
+    # the row passes), rotated over `copies` buffers so that a copy is not still
+    # in the 256 MB last-level cache when its turn comes
+    bufs = [torch.empty(nbytes // 2, dtype=torch.bfloat16, device="cuda").fill_(1.0) for _ in range(copies)]
+    sink = torch.empty(n_blocks, dtype=torch.int32, device="cuda")
+    st = {"i": 0}
+
+    def step(ev=None):
+        if ev is not None:
+            sd.time_next_stream_pass(*ev)
+        sd.stream_read(bufs[st["i"] % copies], sink, n_blocks)
+        st["i"] += 1
+
+    meta = {"workload": (f"plain streaming read of {nbytes / 1e6:.1f} MB ({copies} rotated copies), "
+                         f"{n_blocks} workgroups x 256 threads, 16-byte non-temporal loads"),
+            "positions_per_step": 0, "kernel": "k_stream_read", "kernel_bytes": nbytes,
+            "step_bytes": nbytes}
+    return step, meta, None
+
+
+def setup_readceiling_66m(torch, sd, wl):
+    return setup_readceiling(torch, sd, wl, 64 * 4 * 128256 * 2, 8)     # the greedy workload's rows
+
+
+def setup_readceiling_1g(torch, sd, wl):
+    return setup_readceiling(torch, sd, wl, 1 << 30, 2)
+
+
 WORKLOADS = {"adaptive": setup_adaptive, "adaptive_table": setup_adaptive_table, "greedy": setup_greedy, "topk": setup_topk,
              "tree": setup_tree, "tree_sampled": setup_tree_sampled,
              "tree_sampled_topk": setup_tree_sampled_topk, "chain1": setup_chain1,
-             "kv": setup_kv, "rerank": setup_rerank}
+             "kv": setup_kv, "rerank": setup_rerank, "readceiling_66m": setup_readceiling_66m,
+             "readceiling_1g": setup_readceiling_1g}
 
 
 # --------------------------------------------------------------------------

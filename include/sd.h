@@ -421,6 +421,17 @@ sd_status_t sd_select_len_table(const float* conf, int32_t B, int32_t K_max,
                                 float* expected_advance, int32_t* cu_sel, void* hip_stream);
 
 /*
+ * Measurement support: a plain streaming read of `bytes` bytes (a multiple of
+ * 16, 16-byte aligned) of device memory by n_blocks workgroups of 256 threads,
+ * each reading one contiguous chunk, with the 16-byte loads the row passes use; sink [n_blocks] receives one
+ * word per workgroup (a fold of what it read). It is the read ceiling the
+ * verification kernels are compared with on the same device, and takes the
+ * events of sd_time_next_stream_pass like the row passes.
+ */
+sd_status_t sd_stream_read(const void* data, size_t bytes, uint32_t* sink, int32_t n_blocks,
+                           void* hip_stream);
+
+/*
  * Measurement support. The next sd_verify_chain, sd_verify_chain_capped,
  * sd_verify_greedy, sd_build_tree, sd_verify_tree, sd_compact_kv or
  * sd_rerank_tree call made by the calling host thread binds `start_event` and

@@ -81,6 +81,8 @@ def _load():
     lib.sd_expand_tree.restype = ctypes.c_int
     lib.sd_verify_chain_noalloc.argtypes = [P, P, ctypes.c_int, P, P, P, I, I, I, F, I, P, P, P, P, P, P]
     lib.sd_verify_chain_noalloc.restype = ctypes.c_int
+    lib.sd_stream_read.argtypes = [P, Z, P, I, P]
+    lib.sd_stream_read.restype = ctypes.c_int
     lib.sd_time_next_stream_pass.argtypes = [P, P]
     lib.sd_time_next_stream_pass.restype = ctypes.c_int
     _lib = lib
@@ -140,6 +142,17 @@ def time_next_stream_pass(start: Optional["torch.cuda.Event"], stop: Optional["t
     if (start is not None and not s.value) or (stop is not None and not e.value):
         raise ValueError("record() each event once before passing it (its HIP event is created lazily)")
     _raise(_load().sd_time_next_stream_pass(s, e), "sd_time_next_stream_pass")
+
+
+def stream_read(data: torch.Tensor, sink: torch.Tensor, n_blocks: int, stream=None):
+    """sd_stream_read: a plain streaming read of `data` (the device's read ceiling)."""
+    _check(data, "data")
+    _check(sink, "sink", torch.int32, data.device)
+    nbytes = data.numel() * data.element_size()
+    if sink.numel() < n_blocks:
+        raise ValueError("sink needs one word per workgroup")
+    _raise(_load().sd_stream_read(_ptr(data), ctypes.c_size_t(nbytes), _ptr(sink), int(n_blocks),
+                                  _stream(stream)), "sd_stream_read")
 
 
 def workspace_bytes(op: int, B: int, K_max: int = 0, V: int = 1, top_k: int = 0, N: int = 2) -> int:

@@ -360,6 +360,15 @@ sd_status_t sd_expand_tree(int32_t* cand_parent, int32_t* cand_token, float* can
                                            static_cast<hipStream_t>(hip_stream)));
 }
 
+sd_status_t sd_stream_read(const void* data, size_t bytes, uint32_t* sink, int32_t n_blocks,
+                           void* hip_stream) {
+    if (!data || !sink || misaligned(data) || bytes % 16 != 0 || bytes == 0 || n_blocks < 1 ||
+        n_blocks > (1 << 20))
+        return SD_EINVAL;
+    return from_hip(sd::launch_stream_read(data, (int64_t)bytes, sink, n_blocks,
+                                           static_cast<hipStream_t>(hip_stream)));
+}
+
 sd_status_t sd_compact_kv(void* kv, int64_t row_bytes, int64_t n_rows, const int64_t* row_base,
                           const int32_t* path_nodes, const int32_t* accepted_len, int32_t B,
                           int32_t N, void* hip_stream) {

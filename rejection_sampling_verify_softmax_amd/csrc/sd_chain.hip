@@ -42,6 +42,9 @@ constexpr int kModeResidual = 0;
 constexpr int kModeExtra = 1;
 constexpr int kModeNone = 2;
 constexpr int kU = SD_STATS_UNROLL;
+#ifndef SD_MASS_DPP
+#define SD_MASS_DPP 1
+#endif
 // Phase boundaries of a phased verification: phase i streams the slots
 // (positions) from the previous boundary up to this one; the last phase runs
 // to the end of the window.
@@ -64,6 +67,16 @@ struct ChainDesc {
     float O_p, O_q;     // row references (integers)
     float pad;
     double S_p, S_q;    // row sums relative to the references
+};
+
+// Per (sequence, slot), written by the chunk-0 workgroup of the slot: the two
+// logits at the draft token, that position's uniform and whether the token is
+// in range, so that the decision reads nothing that depends on the packed
+// offsets. The extra-token slot carries only its uniform.
+struct SlotRec {
+    float xt, xd;
+    float u;
+    int32_t yok;
 };
 
 struct RowStat {
@@ -221,9 +234,10 @@ __device__ void chunk_stats(const typename E::raw* const (&rows)[NR], int beg, i
 template <class E, bool VEC>
 __global__ __launch_bounds__(kBlock) void k_chain_stats(
     const typename E::raw* __restrict__ tgt, const typename E::raw* __restrict__ dft,
-    const int32_t* __restrict__ tok, const int32_t* __restrict__ cu, int K_max, int V, int chunk,
-    int n_chunks, float c, Partial* __restrict__ part_t, Partial* __restrict__ part_d,
-    float* __restrict__ xy, int slot_lo, int slot_span, const int32_t* __restrict__ alive) {
+    const int32_t* __restrict__ tok, const float* __restrict__ uni, const int32_t* __restrict__ cu,
+    int K_max, int V, int chunk, int n_chunks, float c, Partial* __restrict__ part_t,
+    Partial* __restrict__ part_d, SlotRec* __restrict__ rec, int slot_lo, int slot_span,
+    const int32_t* __restrict__ alive) {
     __shared__ double redd[kWavesPerBlock];
     __shared__ float redf[kWavesPerBlock];
     __shared__ int redi[kWavesPerBlock];
@@ -246,13 +260,14 @@ __global__ __launch_bounds__(kBlock) void k_chain_stats(
         const typename E::raw* dp = dft + d_row * (int64_t)V;
         if (ch == 0 && threadIdx.x == 0) {
             const int y = tok[d_row];
-            float xt = NAN, xd = NAN;
+            const float u = uni[t_row];
+            SlotRec r{NAN, NAN, u, 0};
             if (y >= 0 && y < V) {
-                xt = E::at(tp, y);
-                xd = E::at(dp, y);
+                r.xt = E::at(tp, y);
+                r.xd = E::at(dp, y);
+                r.yok = 1;
             }
-            xy[slot_id * 2] = xt;
-            xy[slot_id * 2 + 1] = xd;
+            rec[slot_id] = r;
         }
         const typename E::raw* rows[2] = {tp, dp};
         Partial out[2];
@@ -262,6 +277,7 @@ __global__ __launch_bounds__(kBlock) void k_chain_stats(
             part_d[slot_id * n_chunks + ch] = out[1];
         }
     } else {
+        if (ch == 0 && threadIdx.x == 0) rec[slot_id] = SlotRec{NAN, NAN, uni[t_row], 0};
         const typename E::raw* rows[1] = {tp};
         Partial out[1];
         chunk_stats<E, VEC, 1>(rows, beg, end, c, out, redd, redf, redi);
@@ -388,13 +404,14 @@ __device__ void mass_pass(const typename E::raw* tp, const typename E::raw* dp, 
     const typename E::raw* tb = tp + beg;
     const typename E::raw* db = dp + beg;
     static_assert(kMU == 2 || kMU == 4, "the piece reduction sums two or four pieces at once");
-    // loads of one round: kMU vectors of the target row, then kMU of the draft row
-    auto fetch = [&](uint4 (&v)[NR * kMU], int rd) {
+    // loads of one round: kMU vectors of the target row, then kMU of the draft
+    // row (only the last, partial round checks the row's end)
+    auto fetch = [&](uint4 (&v)[NR * kMU], int rd, bool check) {
 #pragma unroll
         for (int u = 0; u < kMU; ++u) {
             const int vi = rd * step + u * T + threadIdx.x;
             if (VEC) {
-                const bool in = vi < nvec;
+                const bool in = !check || vi < nvec;
                 v[u] = in ? load16(tb, vi) : E::neg_inf();
                 if (Q) v[NR * kMU - kMU + u] = in ? load16(db, vi) : E::neg_inf();
             }
@@ -441,29 +458,46 @@ __device__ void mass_pass(const typename E::raw* tp, const typename E::raw* dp, 
             t += r1;
             u = h32 ? 1 : 0;
         }
+#if SD_MASS_DPP
+        t = row_sum_f64(t);                 // the rest within each row of 16 lanes
+#else
 #pragma unroll
         for (int o = 8; o > 0; o >>= 1) t += __shfl_xor(t, o, kWave);
+#endif
         const int piece = p0 + (rd * kMU + u) * waves + w;
         if ((lane & (kWave / kMU - 1)) == 0 && piece < npieces) pieces[piece] = t;
     };
-    pipelined_steps<NR * kMU>(rounds, fetch, weigh);
+    const int full = VEC ? nvec / step : 0;
+    pipelined_steps<NR * kMU>(
+        full, [&](uint4 (&v)[NR * kMU], int rd) { fetch(v, rd, false); }, weigh);
+    for (int rd = full; rd < rounds; ++rd) {
+        uint4 v[NR * kMU];
+        fetch(v, rd, true);
+        weigh(v, rd);
+    }
 }
 
 // Scans one piece (64 lanes x one 16-byte vector, tokens e0 ..) from cumulative
 // mass `before`: the first token whose running mass exceeds `target`, or the
-// last token of the piece with positive weight. One wave.
-template <class E, bool Q>
+// last token of the piece with positive weight. One wave (all lanes active).
+template <class E, bool VEC, bool Q>
 __device__ int scan_piece(const typename E::raw* tp, const typename E::raw* dp, int e0, int V,
                           const WeightFn& wf, double before, double target, bool take_last) {
     constexpr int EV = E::kVec;
     const int lane = threadIdx.x & (kWave - 1);
     const int j0 = e0 + lane * EV;
     float fp[EV], fq[EV];
+    if (VEC) {                  // (e0 is a multiple of the piece size, V of the vector size)
+        const bool in = j0 < V;
+        E::unpack(in ? load16_cached(tp, j0 / EV) : E::neg_inf(), fp);
+        if (Q) E::unpack(in ? load16_cached(dp, j0 / EV) : E::neg_inf(), fq);
+    } else {
 #pragma unroll
-    for (int e = 0; e < EV; ++e) {
-        const int j = j0 + e;
-        fp[e] = (j < V) ? E::at(tp, j) : -INFINITY;
-        fq[e] = (Q && j < V) ? E::at(dp, j) : -INFINITY;
+        for (int e = 0; e < EV; ++e) {
+            const int j = j0 + e;
+            fp[e] = (j < V) ? E::at(tp, j) : -INFINITY;
+            fq[e] = (Q && j < V) ? E::at(dp, j) : -INFINITY;
+        }
     }
     float w[EV];
     float ls = 0.f;
@@ -474,9 +508,10 @@ __device__ int scan_piece(const typename E::raw* tp, const typename E::raw* dp, 
         ls += w[e];
         if (w[e] > 0.f) lastpos = j0 + e;
     }
-    const int last_any = wave_max_int(lastpos);
+    const int last_any = (int)wave_max_u32((uint32_t)(lastpos + 1)) - 1;
     if (take_last) return last_any;
-    const double start = before + wave_excl_scan((double)ls);
+    const double incl = wave_incl_scan_f64((double)ls);
+    const double start = before + (incl - (double)ls);
     const unsigned long long m = __ballot(start + (double)ls > target);
     if (!m) return last_any;
     const int L = __ffsll(m) - 1;
@@ -498,7 +533,7 @@ __device__ int scan_piece(const typename E::raw* tp, const typename E::raw* dp, 
 
 // Inverse CDF in token order from the piece masses: the first token whose
 // running mass exceeds u * total. One wave. Returns -1 when total is 0.
-template <class E, bool Q>
+template <class E, bool VEC, bool Q>
 __device__ int sample_from_pieces(const double* S, int npieces, const typename E::raw* tp,
                                   const typename E::raw* dp, int V, const WeightFn& wf, double u,
                                   double* total_out) {
@@ -512,8 +547,9 @@ __device__ int sample_from_pieces(const double* S, int npieces, const typename E
         mine += S[i];
         if (S[i] > 0.0) lastpos = i;
     }
-    const double excl = wave_excl_scan(mine);
-    const double total = __shfl(excl + mine, kWave - 1, kWave);
+    const double incl = wave_incl_scan_f64(mine);
+    const double excl = incl - mine;
+    const double total = __shfl(incl, kWave - 1, kWave);
     *total_out = total;
     if (!(total > 0.0)) return -1;
     const double target = u * total;
@@ -535,10 +571,10 @@ __device__ int sample_from_pieces(const double* S, int npieces, const typename E
         piece = __shfl(hit, L, kWave);
         before = __shfl(before, L, kWave);
     } else {
-        piece = wave_max_int(lastpos);      // rounding left the point past the end
+        piece = (int)wave_max_u32((uint32_t)(lastpos + 1)) - 1;   // rounding left the point past the end
         take_last = true;
     }
-    return scan_piece<E, Q>(tp, dp, piece * kWave * EV, V, wf, before, target, take_last);
+    return scan_piece<E, VEC, Q>(tp, dp, piece * kWave * EV, V, wf, before, target, take_last);
 }
 
 // Inverse CDF over the whole decision row with the piece masses computed on
@@ -571,10 +607,10 @@ __device__ int sample_by_rescan(const typename E::raw* tp, int V, const WeightFn
     double run = 0.0;
     for (int i = 0; i < np; ++i) {
         const double m = piece_mass(i);
-        if (run + m > target && m > 0.0) return scan_piece<E, false>(tp, tp, i * pe, V, wf, run, target, false);
+        if (run + m > target && m > 0.0) return scan_piece<E, false, false>(tp, tp, i * pe, V, wf, run, target, false);
         run += m;
     }
-    return scan_piece<E, false>(tp, tp, last * pe, V, wf, 0.0, target, true);
+    return scan_piece<E, false, false>(tp, tp, last * pe, V, wf, 0.0, target, true);
 }
 
 constexpr int kSeqPerBlock = kBlock / kWave;    // decide / sample: one wave per sequence
@@ -583,8 +619,7 @@ constexpr int kSeqPerBlock = kBlock / kWave;    // decide / sample: one wave per
 struct DecideArgs {
     const Partial* part_t;
     const Partial* part_d;
-    const float* xy;
-    const int32_t* tok;
+    const SlotRec* rec;
     const float* uni;
     const int32_t* cu;
     int K_max, V, n_chunks;
@@ -607,8 +642,7 @@ struct DecideArgs {
 __device__ __forceinline__ bool decide_sequence(const DecideArgs& g, int b, ChainDesc& d) {
     const Partial* __restrict__ part_t = g.part_t;
     const Partial* __restrict__ part_d = g.part_d;
-    const float* __restrict__ xy = g.xy;
-    const int32_t* __restrict__ tok = g.tok;
+    const SlotRec* __restrict__ rec = g.rec;
     const float* __restrict__ uni = g.uni;
     const int K_max = g.K_max, V = g.V, n_chunks = g.n_chunks, hi = g.hi;
     const float c = g.c;
@@ -618,29 +652,29 @@ __device__ __forceinline__ bool decide_sequence(const DecideArgs& g, int b, Chai
     const int slots = K_max + 1;
     const int64_t slot0 = (int64_t)b * slots;
     // Lane s combines the partials of slot s (target, and draft below K_max)
-    // for every slot streamed so far; these loads do not wait for cu.
+    // and reads the slot's record, for every slot streamed so far; none of
+    // these loads waits for cu (one round trip; a lane past the sequence's
+    // slots reads a record that is never used).
     const int ns = slots < hi ? slots : hi;
     RowStat rp{-INFINITY, 0.0, false}, rq{-INFINITY, 0.0, false};
-    float xt = 0.f, xd = 0.f;
+    SlotRec r{0.f, 0.f, 0.f, 0};
     if (lane < ns) {
         rp = combine_row(part_t + (slot0 + lane) * n_chunks, n_chunks);
-        if (lane < K_max) {
-            rq = combine_row(part_d + (slot0 + lane) * n_chunks, n_chunks);
-            xt = xy[(slot0 + lane) * 2];
-            xd = xy[(slot0 + lane) * 2 + 1];
-        }
+        r = rec[slot0 + lane];
+        if (lane < K_max) rq = combine_row(part_d + (slot0 + lane) * n_chunks, n_chunks);
     }
     int d0, k;
     seq_range(g.cu, b, K_max, d0, k);
     // positions evaluated so far: those of the slots streamed up to this phase
     const int kk = k < hi ? k : hi;
-    // uniform of position `lane` (lane k_b's is the final draw's for an uncapped window)
-    const float u_lane = lane <= k ? uni[d0 + b + lane] : 0.f;
+    // uniform of position `lane` (streamed slots; lane k_b's is the final draw's
+    // for an uncapped window)
+    const float u_lane = (lane <= k && lane < ns) ? r.u : 0.f;
+    const float xt = r.xt, xd = r.xd;
     bool acc = true;
     int st = 0;
     if (lane < kk) {
-        const int y = tok[d0 + lane];
-        const bool yok = (y >= 0 && y < V);
+        const bool yok = r.yok != 0;
         double py = 0.0, qy = 0.0;
         // the summed terms' fp32 reference, evaluated exactly in fp64
         if (yok && rp.valid) py = exp2((double)xt * (double)c - (double)rp.O) / rp.S;
@@ -666,8 +700,10 @@ __device__ __forceinline__ bool decide_sequence(const DecideArgs& g, int b, Chai
 #pragma unroll
     for (int o = kWave / 2; o > 0; o >>= 1) mine |= __shfl_xor(mine, o, kWave);
     d.A = A;
-    // (a 64-position window puts its final uniform and extra row past the lanes)
-    d.u = kc < kWave ? __shfl(u_lane, kc, kWave) : uni[d0 + b + kc];
+    // the final draw's uniform: from its slot's record when that slot was
+    // streamed (and is a lane), else from the uniforms (a window rejected
+    // before its later slots were streamed, or a 64-position window)
+    d.u = (kc < ns && kc < kWave) ? __shfl(u_lane, kc, kWave) : uni[d0 + b + kc];
     d.pad = 0.f;
     if (A < kc) {
         const float Op = __shfl(rp.O, A, kWave);
@@ -766,8 +802,8 @@ __global__ __launch_bounds__(kBlock) void k_chain_sample(
         const WeightFn wf = weight_fn(d, c, false);
         const typename E::raw* dp = wf.has_q ? dft + (int64_t)d.d_row * V : tp;
         const double* pieces = piece_ws + (int64_t)b * npieces;
-        next = wf.has_q ? sample_from_pieces<E, true>(pieces, npieces, tp, dp, V, wf, (double)d.u, &total)
-                        : sample_from_pieces<E, false>(pieces, npieces, tp, dp, V, wf, (double)d.u, &total);
+        next = wf.has_q ? sample_from_pieces<E, VEC, true>(pieces, npieces, tp, dp, V, wf, (double)d.u, &total)
+                        : sample_from_pieces<E, VEC, false>(pieces, npieces, tp, dp, V, wf, (double)d.u, &total);
         if (d.mode == kModeResidual && !(total > 0.0))
             next = sample_by_rescan<E>(tp, V, weight_fn(d, c, true), (double)d.u);
     }
@@ -818,8 +854,8 @@ __global__ __launch_bounds__(kFusedThreads) void k_chain_resolve(
     __syncthreads();
     if (threadIdx.x >= kWave) return;
     double total = 0.0;
-    int next = wf.has_q ? sample_from_pieces<E, true>(pieces, npieces, tp, dp, V, wf, (double)d.u, &total)
-                        : sample_from_pieces<E, false>(pieces, npieces, tp, dp, V, wf, (double)d.u, &total);
+    int next = wf.has_q ? sample_from_pieces<E, VEC, true>(pieces, npieces, tp, dp, V, wf, (double)d.u, &total)
+                        : sample_from_pieces<E, VEC, false>(pieces, npieces, tp, dp, V, wf, (double)d.u, &total);
     if (d.mode == kModeResidual && !(total > 0.0))
         next = sample_by_rescan<E>(tp, V, weight_fn(d, g.c, true), (double)d.u);
     if (lane == 0) {
@@ -838,7 +874,7 @@ size_t chain_full_ws_bytes(int B, int K_max, int V, int dtype) {
     Carve cv;
     cv.take(slots * nc * sizeof(Partial));          // part_t
     cv.take(slots * nc * sizeof(Partial));          // part_d
-    cv.take(slots * 2 * sizeof(float));             // xy
+    cv.take(slots * sizeof(SlotRec));               // slot records
     cv.take((size_t)B * npieces * sizeof(double));  // piece masses
     cv.take((size_t)B * sizeof(ChainDesc));         // decisions
     cv.take((size_t)B * sizeof(int32_t));           // still undecided after a phase
@@ -855,7 +891,7 @@ static hipError_t chain_full_impl(const ChainArgs& a) {
     char* ws = static_cast<char*>(a.ws);
     Partial* part_t = reinterpret_cast<Partial*>(ws + cv.take(slots * nc * sizeof(Partial)));
     Partial* part_d = reinterpret_cast<Partial*>(ws + cv.take(slots * nc * sizeof(Partial)));
-    float* xy = reinterpret_cast<float*>(ws + cv.take(slots * 2 * sizeof(float)));
+    SlotRec* rec = reinterpret_cast<SlotRec*>(ws + cv.take(slots * sizeof(SlotRec)));
     double* pieces = reinterpret_cast<double*>(ws + cv.take((size_t)a.B * npieces * sizeof(double)));
     ChainDesc* desc = reinterpret_cast<ChainDesc*>(ws + cv.take((size_t)a.B * sizeof(ChainDesc)));
     int32_t* alive = reinterpret_cast<int32_t*>(ws + cv.take((size_t)a.B * sizeof(int32_t)));
@@ -888,8 +924,7 @@ static hipError_t chain_full_impl(const ChainArgs& a) {
     DecideArgs g;
     g.part_t = part_t;
     g.part_d = part_d;
-    g.xy = xy;
-    g.tok = a.tokens;
+    g.rec = rec;
     g.uni = a.uniforms;
     g.cu = a.cu;
     g.K_max = a.K_max;
@@ -907,11 +942,11 @@ static hipError_t chain_full_impl(const ChainArgs& a) {
         const unsigned grid1 = (unsigned)((size_t)a.B * (hi - lo) * nc);
         if (ph == 0)
             PassTimer::launch(k_chain_stats<E, VEC>, dim3(grid1), dim3(kBlock), a.stream, tgt, dft,
-                              a.tokens, a.cu, a.K_max, a.V, chunk, nc, c, part_t, part_d, xy, lo,
+                              a.tokens, a.uniforms, a.cu, a.K_max, a.V, chunk, nc, c, part_t, part_d, rec, lo,
                               hi - lo, (int32_t*)nullptr);
         else
             hipLaunchKernelGGL((k_chain_stats<E, VEC>), dim3(grid1), dim3(kBlock), 0, a.stream, tgt,
-                               dft, a.tokens, a.cu, a.K_max, a.V, chunk, nc, c, part_t, part_d, xy,
+                               dft, a.tokens, a.uniforms, a.cu, a.K_max, a.V, chunk, nc, c, part_t, part_d, rec,
                                lo, hi - lo, alive);
         g.hi = hi;
         if (fused && ph == n_phases - 1) {

@@ -141,6 +141,39 @@ __device__ __forceinline__ uint32_t dpp_from(uint32_t v) {
     return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, CTRL, ROWS, 0xf, false);
 }
 
+// Sum of a double over each row of 16 lanes by DPP rotations (no LDS round
+// trip): every lane receives its row's sum (lanes may differ in the last bit,
+// the order of the additions depending on the lane). The whole wave must be
+// active.
+// (lanes a DPP operation does not write, or whose source lies outside the
+// row, receive +0.0)
+template <int CTRL, int ROWS = 0xf>
+__device__ __forceinline__ double dpp_f64(double v) {
+    const unsigned long long b = __double_as_longlong(v);
+    const uint32_t lo = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)(uint32_t)b, CTRL, ROWS, 0xf, false);
+    const uint32_t hi = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)(uint32_t)(b >> 32), CTRL, ROWS, 0xf, false);
+    return __longlong_as_double((long long)(((unsigned long long)hi << 32) | lo));
+}
+
+// Inclusive prefix sum of a double across the wave (lane order) on DPP row
+// shifts and row broadcasts. The whole wave must be active.
+__device__ __forceinline__ double wave_incl_scan_f64(double v) {
+    v += dpp_f64<0x111>(v);         // row_shr:1
+    v += dpp_f64<0x112>(v);         // row_shr:2
+    v += dpp_f64<0x114>(v);         // row_shr:4
+    v += dpp_f64<0x118>(v);         // row_shr:8
+    v += dpp_f64<0x142, 0xa>(v);    // row_bcast:15 into rows 1 and 3
+    v += dpp_f64<0x143, 0xc>(v);    // row_bcast:31 into rows 2 and 3
+    return v;
+}
+__device__ __forceinline__ double row_sum_f64(double v) {
+    v += dpp_f64<0x128>(v);     // row_ror:8
+    v += dpp_f64<0x124>(v);     // row_ror:4
+    v += dpp_f64<0x122>(v);     // row_ror:2
+    v += dpp_f64<0x121>(v);     // row_ror:1
+    return v;
+}
+
 // Maximum over the wave, returned to every lane.
 __device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
     v = max(v, dpp_from<0x111, 0xf>(v));
