@@ -23,11 +23,14 @@ struct ArgPartial {
     int32_t i;    // lowest index reaching it; kNone if the chunk is all NaN
 };
 constexpr int32_t kNone = 0x7fffffff;
-constexpr int kArgUnroll = 1;
+#ifndef SD_ARG_UNROLL
+#define SD_ARG_UNROLL 2
+#endif
+constexpr int kArgUnroll = SD_ARG_UNROLL;
 // Tokens per argmax workgroup: short rows of few sequences still give the
 // launch thousands of workgroups.
 #ifndef SD_ARG_CHUNK_BF16
-#define SD_ARG_CHUNK_BF16 32768
+#define SD_ARG_CHUNK_BF16 16384
 #endif
 #ifndef SD_ARG_CHUNK_F32
 #define SD_ARG_CHUNK_F32 16384
@@ -84,9 +87,14 @@ __global__ __launch_bounds__(kBlock) void k_argmax(const typename E::raw* __rest
             }
         }
     };
-    // whole steps: unchecked loads, the next step in flight
+    // whole steps: unchecked loads, the next step in flight. The same rule as
+    // consider(), without branches: the lane keeps the best vector's maximum,
+    // its index and its raw bits; the element is found once, after the steps.
     constexpr int kStep = kBlock * U;
     const int nsteps = VEC ? nvec / kStep : 0;
+    float fbest = -INFINITY;
+    int fvi = -1;
+    uint4 fraw = make_uint4(0u, 0u, 0u, 0u);
     pipelined_steps<U>(
         nsteps,
         [&](uint4 (&buf)[U], int st) {
@@ -98,9 +106,28 @@ __global__ __launch_bounds__(kBlock) void k_argmax(const typename E::raw* __rest
             for (int u = 0; u < U; ++u) {
                 float f[EV];
                 E::unpack(buf[u], f);
-                consider(f, st * kStep + u * kBlock + threadIdx.x);
+                float vmax = f[0];
+#pragma unroll
+                for (int e = 1; e < EV; ++e) vmax = fmaxf(vmax, f[e]);
+                const bool take = vmax > fbest || (fvi < 0 && vmax == vmax);
+                fbest = take ? vmax : fbest;
+                fvi = take ? st * kStep + u * kBlock + (int)threadIdx.x : fvi;
+                fraw.x = take ? buf[u].x : fraw.x;
+                fraw.y = take ? buf[u].y : fraw.y;
+                fraw.z = take ? buf[u].z : fraw.z;
+                fraw.w = take ? buf[u].w : fraw.w;
             }
         });
+    if (fvi >= 0) {
+        float f[EV];
+        E::unpack(fraw, f);
+        int e_hit = EV - 1;
+#pragma unroll
+        for (int e = EV - 1; e >= 0; --e)
+            if (f[e] == fbest) e_hit = e;
+        best = fbest;
+        bidx = beg + fvi * EV + e_hit;
+    }
     // the ragged end (all of it in the element-wise path)
     for (int vi = nsteps * kStep + threadIdx.x; vi < nvec; vi += kBlock) {
         float f[EV];
