@@ -328,41 +328,51 @@ __device__ RowStat combine_row(const Partial* p, int n_chunks) {
 
 // Sampling weight of one token in fp32: the normalised residual max(p - q, 0)
 // (Q), or p itself (!Q: the extra token, and a residual whose q counts as 0,
-// since max(p - 0, 0) rounds to p). The mass pass and the final scan use this
-// one definition, so both see bit-identical values. Q is a template argument:
-// the streaming loops hold no per-token branch on the row kind.
+// since max(p - 0, 0) rounds to p). It is computed as scale * u with the
+// unscaled u = max(e_p * r - e_q, 0), r = S_q / S_p, scale = 1 / S_q (Q), or
+// u = e_p, scale = 1 / S_p (!Q), where e = 2^(x c - O): one multiply per
+// 16-byte vector instead of one per token. The mass pass and the final scan
+// form a lane's sum the same way (scale times the fp32 sum of u), so both see
+// bit-identical lane sums. Q is a template argument: the streaming loops hold
+// no per-token branch on the row kind.
 struct WeightFn {
-    float c, Op, ip, Oq, iq;
+    float c, Op, Oq, r, scale;
     bool has_q;
 };
 
 template <bool Q>
-__device__ __forceinline__ float weight(const WeightFn& w, float xp, float xq) {
+__device__ __forceinline__ float weight_u(const WeightFn& w, float xp, float xq) {
     const float ep = fast_exp2(__builtin_fmaf(xp, w.c, -w.Op));
-    if (!Q) return ep * w.ip;
-    const float q = fast_exp2(__builtin_fmaf(xq, w.c, -w.Oq)) * w.iq;
-    return fmaxf(__builtin_fmaf(ep, w.ip, -q), 0.f);          // max(p - q, 0)
+    if (!Q) return ep;
+    const float eq = fast_exp2(__builtin_fmaf(xq, w.c, -w.Oq));
+    return fmaxf(__builtin_fmaf(ep, w.r, -eq), 0.f);          // S_q * max(p - q, 0)
+}
+
+template <bool Q>
+__device__ __forceinline__ float weight(const WeightFn& w, float xp, float xq) {
+    return weight_u<Q>(w, xp, xq) * w.scale;
 }
 
 __device__ __forceinline__ WeightFn weight_fn(const ChainDesc& d, float c, bool use_p) {
     WeightFn w;
     w.c = c;
     w.Op = d.O_p;
-    w.ip = (float)(1.0 / d.S_p);
     w.has_q = !use_p && d.mode == kModeResidual && d.d_row >= 0;
     w.Oq = d.O_q;
-    w.iq = w.has_q ? (float)(1.0 / d.S_q) : 0.f;
+    w.r = w.has_q ? (float)(d.S_q / d.S_p) : 0.f;
+    w.scale = w.has_q ? (float)(1.0 / d.S_q) : (float)(1.0 / d.S_p);
     return w;
 }
 
-// Sum of the weights of one lane's 16-byte vector, in element order.
+// Sum of the weights of one lane's 16-byte vector: scale times the fp32 sum
+// of the unscaled weights in element order.
 template <class E, bool Q>
 __device__ __forceinline__ float lane_weight_sum(const float (&fp)[E::kVec], const float (&fq)[E::kVec],
                                                  const WeightFn& wf) {
     float s = 0.f;
 #pragma unroll
-    for (int e = 0; e < E::kVec; ++e) s += weight<Q>(wf, fp[e], fq[e]);
-    return s;
+    for (int e = 0; e < E::kVec; ++e) s += weight_u<Q>(wf, fp[e], fq[e]);
+    return s * wf.scale;
 }
 
 constexpr int kResolveThreads = kBlock;
@@ -500,14 +510,16 @@ __device__ int scan_piece(const typename E::raw* tp, const typename E::raw* dp, 
         }
     }
     float w[EV];
-    float ls = 0.f;
+    float us = 0.f;
     int lastpos = -1;
 #pragma unroll
     for (int e = 0; e < EV; ++e) {
-        w[e] = weight<Q>(wf, fp[e], fq[e]);
-        ls += w[e];
+        const float uw = weight_u<Q>(wf, fp[e], fq[e]);
+        us += uw;
+        w[e] = uw * wf.scale;
         if (w[e] > 0.f) lastpos = j0 + e;
     }
+    const float ls = us * wf.scale;         // the lane sum exactly as the mass pass formed it
     const int last_any = (int)wave_max_u32((uint32_t)(lastpos + 1)) - 1;
     if (take_last) return last_any;
     const double incl = wave_incl_scan_f64((double)ls);
