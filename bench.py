@@ -17,7 +17,7 @@ that oracle run (verify lengths of every sequence, committed results of the
 sampled sequences; bit-exact outside the oracle's margin cases).
 
 Other workloads (--workload adaptive_table|greedy|topk|tree|tree_sampled|tree_sampled_topk|chain1|kv|rerank|
-readceiling_66m|readceiling_1g)
+readceiling_66m|readceiling_523m|readceiling_523m_64k|readceiling_1g)
 measure the other kernels
 for the design notes; their inputs are rotated across copies so that the
 working set exceeds the 256 MB last-level cache.
@@ -485,10 +485,11 @@ def setup_chain1(torch, sd, wl):
     return step, meta, {"leg": cpu_leg_chain, "case": case, "state": st}
 
 
-def setup_readceiling(torch, sd, wl, nbytes, copies, n_blocks=2048):
+def setup_readceiling(torch, sd, wl, nbytes, copies, chunk=16384):
     # a plain streaming read of nbytes (16-byte non-temporal loads, the load of
     # the row passes), rotated over `copies` buffers so that a copy is not still
     # in the 256 MB last-level cache when its turn comes
+    n_blocks = nbytes // chunk          # 16 KB per workgroup: the fastest chunk measured
     bufs = [torch.empty(nbytes // 2, dtype=torch.bfloat16, device="cuda").fill_(1.0) for _ in range(copies)]
     sink = torch.empty(n_blocks, dtype=torch.int32, device="cuda")
     st = {"i": 0}
@@ -500,7 +501,7 @@ def setup_readceiling(torch, sd, wl, nbytes, copies, n_blocks=2048):
         st["i"] += 1
 
     meta = {"workload": (f"plain streaming read of {nbytes / 1e6:.1f} MB ({copies} rotated copies), "
-                         f"{n_blocks} workgroups x 256 threads, 16-byte non-temporal loads"),
+                         f"{n_blocks} workgroups x 256 threads ({chunk // 1024} KB each), 16-byte non-temporal loads"),
             "positions_per_step": 0, "kernel": "k_stream_read", "kernel_bytes": nbytes,
             "step_bytes": nbytes}
     return step, meta, None
@@ -514,11 +515,22 @@ def setup_readceiling_1g(torch, sd, wl):
     return setup_readceiling(torch, sd, wl, 1 << 30, 2)
 
 
+def setup_readceiling_523m(torch, sd, wl):
+    # the bytes of the adaptive step's first streaming launch
+    return setup_readceiling(torch, sd, wl, 523032028 // 16 * 16, 2)
+
+
+def setup_readceiling_523m_64k(torch, sd, wl):
+    # the same bytes in the row passes' chunk size (64 KB per workgroup and row)
+    return setup_readceiling(torch, sd, wl, 523032028 // 16 * 16, 2, chunk=65536)
+
+
 WORKLOADS = {"adaptive": setup_adaptive, "adaptive_table": setup_adaptive_table, "greedy": setup_greedy, "topk": setup_topk,
              "tree": setup_tree, "tree_sampled": setup_tree_sampled,
              "tree_sampled_topk": setup_tree_sampled_topk, "chain1": setup_chain1,
              "kv": setup_kv, "rerank": setup_rerank, "readceiling_66m": setup_readceiling_66m,
-             "readceiling_1g": setup_readceiling_1g}
+             "readceiling_1g": setup_readceiling_1g, "readceiling_523m": setup_readceiling_523m,
+             "readceiling_523m_64k": setup_readceiling_523m_64k}
 
 
 # --------------------------------------------------------------------------

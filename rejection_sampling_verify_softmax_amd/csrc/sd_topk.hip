@@ -357,7 +357,6 @@ struct TopkSmem {
     unsigned long long wbuf[kWavesPerBlock][kWaveCap];
     int32_t qi[kWavesPerBlock][kQueue];
     uint32_t smax[kWavesPerBlock][kWave];
-    uint32_t t_guess_b, t_safe_b;
     int wcnt[kWavesPerBlock];
     int wseen[kWavesPerBlock];
     double red[kWavesPerBlock];
@@ -379,7 +378,8 @@ struct KeptStats {
 //  1. Every thread holds kTopkSample vectors of the row's start and takes
 //     their maximum. Ranked among the 256 maxima (distinct tokens), the
 //     topk-th is a guaranteed bound (at least topk tokens reach it) and a
-//     higher one is a guess.
+//     higher one is a guess; both come from ballot bisections over all 256
+//     maxima in every wave.
 //  2. With the guess as threshold, each wave streams its share of the row.
 //     A vector whose largest element may reach the threshold is queued; full
 //     queues are processed one vector per lane, appending each element that
@@ -434,54 +434,33 @@ __device__ __forceinline__ KeptStats row_topk(const typename E::raw* __restrict_
     for (int i = 0; i < kTopkSample; ++i)
         asm volatile("" : "+v"(hs[i].x), "+v"(hs[i].y), "+v"(hs[i].z), "+v"(hs[i].w));
     const bool any = m == m;
-    // The maxima's ranks (value desc; NaN not ranked) without comparing every
-    // pair: each wave sorts its 64 maxima as order-preserving bits (0 = none)
-    // in registers, and a lane finds the range of ranks its value holds among
-    // all four sorted lists by binary search. The value at rank jg is the
-    // guess; the one at rank topk - 1 is reached by topk sampled tokens, a
-    // guaranteed bound.
+    // The values at ranks jg (the guess) and topk - 1 (reached by topk
+    // sampled tokens: a guaranteed bound) among the 256 maxima (value desc;
+    // NaN not ranked): after one exchange through LDS every wave holds all 256
+    // maxima as order-preserving bits (0 = none), four per lane, and builds
+    // each value bit by bit from the top with ballots -- the largest r that
+    // at least j maxima reach is the j-th largest. Every wave computes the
+    // same two values, so no second barrier is needed.
     const int jg = guess_rank(topk, min(V, kTopkSample * kBlock * EV), V);
     const uint32_t mb = any ? ordered_bits(m) : 0u;
-    uint32_t sv = mb;
-#pragma unroll
-    for (int k = 2; k <= kWave; k <<= 1)
-#pragma unroll
-        for (int j = k >> 1; j > 0; j >>= 1) {
-            const uint32_t o = (uint32_t)__shfl_xor((int)sv, j, kWave);
-            const bool keep_hi = ((lane & k) == 0) == ((lane & j) == 0);
-            sv = keep_hi ? max(sv, o) : min(sv, o);
-        }
-    sm.smax[w][lane] = sv;
-    if (tid == 0) {
-        sm.t_guess_b = 0u;
-        sm.t_safe_b = 0u;
-    }
+    sm.smax[w][lane] = mb;
     __syncthreads();
-    if (any) {
-        int gt = 0, ge = 0;          // maxima above mb, and at or above it
+    uint32_t km[kWavesPerBlock];
 #pragma unroll
-        for (int o = 0; o < kWavesPerBlock; ++o) {
-            int lo = 0, hi = kWave;
-            while (lo < hi) {
-                const int mid = (lo + hi) >> 1;
-                if (sm.smax[o][mid] > mb) lo = mid + 1;
-                else hi = mid;
-            }
-            gt += lo;
-            hi = kWave;
-            while (lo < hi) {
-                const int mid = (lo + hi) >> 1;
-                if (sm.smax[o][mid] >= mb) lo = mid + 1;
-                else hi = mid;
-            }
-            ge += lo;
-        }
-        // ranks gt .. ge-1 hold this value (equal maxima write the same bits)
-        if (gt <= jg && jg < ge) sm.t_guess_b = mb;
-        if (gt <= topk - 1 && topk - 1 < ge) sm.t_safe_b = mb;
+    for (int o = 0; o < kWavesPerBlock; ++o) km[o] = sm.smax[o][lane];
+    auto reach = [&](uint32_t c) __attribute__((always_inline)) {
+        int n = 0;
+#pragma unroll
+        for (int o = 0; o < kWavesPerBlock; ++o) n += __popcll(__ballot(km[o] >= c));
+        return n;
+    };
+    uint32_t gb = 0u, sb = 0u;
+#pragma unroll 4
+    for (int bit = 31; bit >= 0; --bit) {
+        const uint32_t cg = gb | (1u << bit), cs = sb | (1u << bit);
+        if (reach(cg) >= jg + 1) gb = cg;
+        if (reach(cs) >= topk) sb = cs;
     }
-    __syncthreads();
-    const uint32_t gb = sm.t_guess_b, sb = sm.t_safe_b;
     // 2. the pass from the guess
     const float tg = gb == 0u ? -INFINITY : from_ordered(gb);
     const float ts = sb == 0u ? -INFINITY : from_ordered(sb);
