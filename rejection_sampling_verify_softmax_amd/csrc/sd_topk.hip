@@ -362,6 +362,32 @@ struct TopkSmem {
     double red[kWavesPerBlock];
 };
 
+// The j-th largest (j >= 1) of the 256 order-preserving keys smax[4][64]
+// (0 = none; 0 if fewer than j are nonzero), the same in every wave: each lane
+// holds four keys and the value is built from the top bit down, one ballot
+// count per candidate. The maxima of bf16 rows are bf16 values, whose keys
+// end in 16 zero bits (value >= +0) or 16 one bits (below it), so their top
+// 16 bits decide and the rest follows from the sign.
+template <class E>
+__device__ __forceinline__ uint32_t rank_value(const uint32_t (&smax)[kWavesPerBlock][kWave], int lane,
+                                               int j) {
+    constexpr int kLowBit = E::kVec == 8 ? 16 : 0;
+    uint32_t km[kWavesPerBlock];
+#pragma unroll
+    for (int o = 0; o < kWavesPerBlock; ++o) km[o] = smax[o][lane];
+    uint32_t g = 0u;
+#pragma unroll 4
+    for (int bit = 31; bit >= kLowBit; --bit) {
+        const uint32_t c = g | (1u << bit);
+        int n = 0;
+#pragma unroll
+        for (int o = 0; o < kWavesPerBlock; ++o) n += __popcll(__ballot(km[o] >= c));
+        if (n >= j) g = c;
+    }
+    if (kLowBit != 0 && g != 0u && !(g & 0x80000000u)) g |= (1u << kLowBit) - 1u;
+    return g;
+}
+
 // What row_topk leaves besides the list: the kept count and, with stats, the
 // fp64 softmax statistics over the kept set at temperature T (m = max x/T,
 // S = sum exp(x/T - m), ey = the term of token y, 0 if y is not kept).
@@ -434,36 +460,21 @@ __device__ __forceinline__ KeptStats row_topk(const typename E::raw* __restrict_
     for (int i = 0; i < kTopkSample; ++i)
         asm volatile("" : "+v"(hs[i].x), "+v"(hs[i].y), "+v"(hs[i].z), "+v"(hs[i].w));
     const bool any = m == m;
-    // The values at ranks jg (the guess) and topk - 1 (reached by topk
-    // sampled tokens: a guaranteed bound) among the 256 maxima (value desc;
-    // NaN not ranked): after one exchange through LDS every wave holds all 256
-    // maxima as order-preserving bits (0 = none), four per lane, and builds
-    // each value bit by bit from the top with ballots -- the largest r that
-    // at least j maxima reach is the j-th largest. Every wave computes the
-    // same two values, so no second barrier is needed.
+    // The value at rank jg (the guess) among the 256 maxima (value desc; NaN
+    // not ranked), and on a retry the one at rank topk - 1 (reached by topk
+    // sampled tokens: a guaranteed bound): after one exchange through LDS
+    // every wave holds all 256 maxima as order-preserving bits (0 = none),
+    // four per lane, and builds the value bit by bit from the top with
+    // ballots -- the largest r that at least j maxima reach is the j-th
+    // largest. Every wave computes the same value, so no second barrier is
+    // needed.
     const int jg = guess_rank(topk, min(V, kTopkSample * kBlock * EV), V);
     const uint32_t mb = any ? ordered_bits(m) : 0u;
     sm.smax[w][lane] = mb;
     __syncthreads();
-    uint32_t km[kWavesPerBlock];
-#pragma unroll
-    for (int o = 0; o < kWavesPerBlock; ++o) km[o] = sm.smax[o][lane];
-    auto reach = [&](uint32_t c) __attribute__((always_inline)) {
-        int n = 0;
-#pragma unroll
-        for (int o = 0; o < kWavesPerBlock; ++o) n += __popcll(__ballot(km[o] >= c));
-        return n;
-    };
-    uint32_t gb = 0u, sb = 0u;
-#pragma unroll 4
-    for (int bit = 31; bit >= 0; --bit) {
-        const uint32_t cg = gb | (1u << bit), cs = sb | (1u << bit);
-        if (reach(cg) >= jg + 1) gb = cg;
-        if (reach(cs) >= topk) sb = cs;
-    }
+    const uint32_t gb = rank_value<E>(sm.smax, lane, jg + 1);
     // 2. the pass from the guess
     const float tg = gb == 0u ? -INFINITY : from_ordered(gb);
-    const float ts = sb == 0u ? -INFINITY : from_ordered(sb);
     WaveTop st = tg > 0.f ? row_pass<E, VEC, true, true>(row, V, gvend, tg, hs, sm.qi[w], sm.wbuf[w], topk,
                                                          pre, have_pre)
                           : row_pass<E, VEC, false, true>(row, V, gvend, tg, hs, sm.qi[w], sm.wbuf[w], topk,
@@ -476,14 +487,18 @@ __device__ __forceinline__ KeptStats row_topk(const typename E::raw* __restrict_
     int seen = 0;
     for (int i = 0; i < kWavesPerBlock; ++i) seen += sm.wseen[i];
     // 3. exact unless fewer than topk tokens reached a guess above the bound
-    if (seen < topk && tg != -INFINITY && tg != ts) {
-        __syncthreads();
-        st = ts > 0.f ? row_pass<E, VEC, true, false>(row, V, gvend, ts, hs, sm.qi[w], sm.wbuf[w], topk,
-                                                      pre, false)
-                      : row_pass<E, VEC, false, false>(row, V, gvend, ts, hs, sm.qi[w], sm.wbuf[w], topk,
-                                                       pre, false);
-        if (lane == 0) sm.wcnt[w] = st.cnt;
-        __syncthreads();
+    if (seen < topk && tg != -INFINITY && jg + 1 < topk) {
+        const uint32_t sb = rank_value<E>(sm.smax, lane, topk);    // the same in every wave
+        const float ts = sb == 0u ? -INFINITY : from_ordered(sb);
+        if (tg != ts) {
+            __syncthreads();
+            st = ts > 0.f ? row_pass<E, VEC, true, false>(row, V, gvend, ts, hs, sm.qi[w], sm.wbuf[w], topk,
+                                                          pre, false)
+                          : row_pass<E, VEC, false, false>(row, V, gvend, ts, hs, sm.qi[w], sm.wbuf[w], topk,
+                                                           pre, false);
+            if (lane == 0) sm.wcnt[w] = st.cnt;
+            __syncthreads();
+        }
     }
     // 4. merge the waves' lists by rank
     int total = 0;
@@ -547,13 +562,18 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(4))) voi
                                                       int phase) {
     __shared__ TopkSmem sm;
     // chain: block -> (sequence, slot in [slot_lo, slot_lo + slot_span), side);
-    // the row's task number keeps the layout of the whole window
+    // the row's task number keeps the layout of the whole window. Sequence
+    // b's 2 * slot_span rows take its blocks rotated by b: consecutive blocks
+    // go to the XCDs in turn, so each kind of row (the bonus row's empty draft
+    // side, a late slot) is spread over all of them instead of always landing
+    // on the same XCD.
     int task = blockIdx.x;
     if (chain) {
-        const int r = (int)blockIdx.x >> 1;
-        const int b = r / slot_span;
+        const int n = 2 * slot_span;
+        const int b = (int)blockIdx.x / n;
         if (state != nullptr && state[b] != phase) return;     // decided in an earlier phase
-        task = ((b * (K_max + 1) + slot_lo + r % slot_span) << 1) | ((int)blockIdx.x & 1);
+        const int j = ((int)blockIdx.x - b * n + n - b % n) % n;
+        task = ((b * (K_max + 1) + slot_lo + (j >> 1)) << 1) | (j & 1);
     }
     const typename E::raw* row = topk_row<E>(tgt, dft, cu, K_max, V, task, chain != 0);
     if (row == nullptr) return;
