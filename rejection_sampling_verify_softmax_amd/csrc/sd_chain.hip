@@ -656,7 +656,7 @@ __device__ __forceinline__ bool decide_sequence(const DecideArgs& g, int b, Chai
     const Partial* __restrict__ part_d = g.part_d;
     const SlotRec* __restrict__ rec = g.rec;
     const float* __restrict__ uni = g.uni;
-    const int K_max = g.K_max, V = g.V, n_chunks = g.n_chunks, hi = g.hi;
+    const int K_max = g.K_max, n_chunks = g.n_chunks, hi = g.hi;
     const float c = g.c;
     float* __restrict__ probs_out = g.probs_out;
     int32_t* __restrict__ alive = g.alive;

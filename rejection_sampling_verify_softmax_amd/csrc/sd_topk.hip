@@ -558,21 +558,30 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(4))) voi
                                                       int32_t* __restrict__ counts,
                                                       RowTop* __restrict__ rowtop, int slot_lo,
                                                       int slot_span,
-                                                      const int32_t* __restrict__ state,
-                                                      int phase) {
+                                                      const int32_t* __restrict__ live,
+                                                      int32_t* __restrict__ live_n) {
     __shared__ TopkSmem sm;
     // chain: block -> (sequence, slot in [slot_lo, slot_lo + slot_span), side);
-    // the row's task number keeps the layout of the whole window. Sequence
-    // b's 2 * slot_span rows take its blocks rotated by b: consecutive blocks
-    // go to the XCDs in turn, so each kind of row (the bonus row's empty draft
+    // the row's task number keeps the layout of the whole window. Group g's
+    // 2 * slot_span rows take its blocks rotated by g: consecutive blocks go
+    // to the XCDs in turn, so each kind of row (the bonus row's empty draft
     // side, a late slot) is spread over all of them instead of always landing
-    // on the same XCD.
+    // on the same XCD. In the second phase group g is the g-th sequence still
+    // undecided (count and entry loaded together), so that the live
+    // workgroups are the first ones dispatched and spread evenly over the CUs.
     int task = blockIdx.x;
     if (chain) {
         const int n = 2 * slot_span;
-        const int b = (int)blockIdx.x / n;
-        if (state != nullptr && state[b] != phase) return;     // decided in an earlier phase
-        const int j = ((int)blockIdx.x - b * n + n - b % n) % n;
+        const int g = (int)blockIdx.x / n;
+        int b = g;
+        if (live != nullptr) {
+            const int cnt = *live_n, e = live[g];
+            if (g >= cnt) return;
+            b = e;
+        } else if (live_n != nullptr && blockIdx.x == 0 && threadIdx.x == 0) {
+            *live_n = 0;             // the first phase: the second phase's list starts empty
+        }
+        const int j = ((int)blockIdx.x - g * n + n - g % n) % n;
         task = ((b * (K_max + 1) + slot_lo + (j >> 1)) << 1) | (j & 1);
     }
     const typename E::raw* row = topk_row<E>(tgt, dft, cu, K_max, V, task, chain != 0);
@@ -721,7 +730,8 @@ __global__ __launch_bounds__(kBlock) void k_chain_topk_decide(
     int B, int K_max, int V, int topk, float temperature, int32_t* __restrict__ A_out,
     int32_t* __restrict__ next_out, float* __restrict__ probs_out, float* __restrict__ R_out,
     int32_t* __restrict__ status_out, const int32_t* __restrict__ cap,
-    int32_t* __restrict__ A_full_out, int hi, int32_t* __restrict__ state, int phase) {
+    int32_t* __restrict__ A_full_out, int hi, int32_t* __restrict__ state, int phase,
+    int32_t* __restrict__ live, int32_t* __restrict__ live_n) {
     __shared__ double wbuf_all[kWavesPerBlock][kMaxTopk];
     __shared__ int ibuf_all[kWavesPerBlock][kMaxTopk];
     __shared__ TopEntry pl_all[kWavesPerBlock][kMaxTopk];
@@ -762,7 +772,10 @@ __global__ __launch_bounds__(kBlock) void k_chain_topk_decide(
     const unsigned long long rej = __ballot(!acc);
     // state[b]: p + 1 while undecided after phase p, -(p + 1) once decided in it
     if (rej == 0ull && k >= hi) {                       // every position so far passed: next phase
-        if (lane == 0) state[b] = phase + 1;
+        if (lane == 0) {
+            state[b] = phase + 1;
+            live[atomicAdd(live_n, 1)] = b;                 // streamed in the next phase (any order)
+        }
         return;
     }
     if (state != nullptr && lane == 0) state[b] = -(phase + 1);
@@ -1657,6 +1670,7 @@ struct TopkLayout {
     TopEntry* lists;
     int32_t* counts;
     RowTop* rowtop;
+    int32_t* live;      // sequences undecided after the first phase, then their count
 };
 
 // Carves the workspace: per row task its kept list, count and statistics,
@@ -1669,12 +1683,14 @@ static int32_t* topk_layout(void* ws, size_t tasks, int topk, TopkLayout* L, siz
     const size_t o_counts = cv.take(tasks * sizeof(int32_t));
     const size_t o_rowtop = cv.take(tasks * sizeof(RowTop));
     const size_t o_state = cv.take(n_state * sizeof(int32_t));
+    const size_t o_live = cv.take((n_state + 1) * sizeof(int32_t));
     if (bytes) *bytes = cv.off;
     if (L == nullptr) return nullptr;
     char* w = static_cast<char*>(ws);
     L->lists = reinterpret_cast<TopEntry*>(w + o_lists);
     L->counts = reinterpret_cast<int32_t*>(w + o_counts);
     L->rowtop = reinterpret_cast<RowTop*>(w + o_rowtop);
+    L->live = reinterpret_cast<int32_t*>(w + o_live);
     return reinterpret_cast<int32_t*>(w + o_state);
 }
 
@@ -1710,20 +1726,23 @@ static hipError_t chain_topk_impl(const ChainArgs& a) {
     for (int ph = 0; ph < n_phases; ++ph) {
         const int lo = bounds[ph], hi = bounds[ph + 1];
         const unsigned grid = (unsigned)((size_t)a.B * (hi - lo) * 2);
+        int32_t* live_n = L.live + a.B;
         if (ph == 0)
             PassTimer::launch(k_topk_rows<E, VEC>, dim3(grid), dim3(kBlock), a.stream,
                               static_cast<const raw*>(a.target), static_cast<const raw*>(a.draft),
                               a.cu, a.K_max, a.V, a.top_k, 1, a.tokens, a.temperature, L.lists,
-                              L.counts, L.rowtop, lo, hi - lo, (int32_t*)nullptr, ph);
+                              L.counts, L.rowtop, lo, hi - lo, (const int32_t*)nullptr,
+                              phased ? live_n : nullptr);
         else
             hipLaunchKernelGGL((k_topk_rows<E, VEC>), dim3(grid), dim3(kBlock), 0, a.stream,
                                static_cast<const raw*>(a.target), static_cast<const raw*>(a.draft),
                                a.cu, a.K_max, a.V, a.top_k, 1, a.tokens, a.temperature, L.lists,
-                               L.counts, L.rowtop, lo, hi - lo, state, ph);
+                               L.counts, L.rowtop, lo, hi - lo, (const int32_t*)L.live, live_n);
         hipLaunchKernelGGL(k_chain_topk_decide, dim3(seq_blocks), dim3(kBlock), 0, a.stream, L.lists,
                            L.rowtop, a.tokens, a.uniforms, a.cu, a.B, a.K_max, a.V, a.top_k,
                            a.temperature, a.accepted_len, a.next_token, a.probs_out,
-                           a.resid_mass_out, a.seq_status, a.cap, a.accepted_full, hi, state, ph);
+                           a.resid_mass_out, a.seq_status, a.cap, a.accepted_full, hi, state, ph, L.live,
+                           live_n);
     }
     return hipGetLastError();
 }
@@ -1787,11 +1806,11 @@ hipError_t launch_tree_build(const float* marg, int B, int K, int V, int N, int3
         if (V % F32::kVec == 0)
             PassTimer::launch(k_topk_rows<F32, true>, dim3((unsigned)tasks), dim3(kBlock), stream, marg,
                               marg, nullptr, 0, V, W, 0, nullptr, 1.0f, L.lists, L.counts, nullptr, 0,
-                              1, nullptr, 0);
+                              1, (const int32_t*)nullptr, (int32_t*)nullptr);
         else
             PassTimer::launch(k_topk_rows<F32, false>, dim3((unsigned)tasks), dim3(kBlock), stream, marg,
                               marg, nullptr, 0, V, W, 0, nullptr, 1.0f, L.lists, L.counts, nullptr, 0,
-                              1, nullptr, 0);
+                              1, (const int32_t*)nullptr, (int32_t*)nullptr);
     } else {
         PassTimer::mark_before(stream);
         PassTimer::mark_after(stream);
