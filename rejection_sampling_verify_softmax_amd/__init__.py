@@ -162,13 +162,18 @@ def workspace_bytes(op: int, B: int, K_max: int = 0, V: int = 1, top_k: int = 0,
     return int(out.value)
 
 
-def _workspace(nbytes: int, device, ws: Optional[torch.Tensor]):
+def _workspace(nbytes: int, device, ws: Optional[torch.Tensor], stream=None):
     n = max(int(nbytes), 256)
     if ws is not None:
         if ws.numel() * ws.element_size() < n:
             raise ValueError(f"workspace of {ws.numel() * ws.element_size()} bytes < {n} needed")
         return ws
-    return torch.empty(n, dtype=torch.uint8, device=device)
+    t = torch.empty(n, dtype=torch.uint8, device=device)
+    if stream is not None:
+        # allocated on the current stream, used on `stream`: the allocator
+        # must not hand the block out again before `stream` is done with it
+        t.record_stream(stream)
+    return t
 
 
 def _check_rows(t: Optional[torch.Tensor], name: str, rows: int, V: int):
@@ -246,7 +251,7 @@ def verify_chain(target: torch.Tensor, draft: Optional[torch.Tensor], tokens: to
     if want_resid and not greedy:
         resid = _get(o, "resid", lambda: torch.empty(B, dtype=torch.float32, device=dev))
     nbytes = workspace_bytes(OP_CHAIN, B, K_max, V, top_k)
-    ws = _workspace(nbytes, dev, workspace)
+    ws = _workspace(nbytes, dev, workspace, stream)
     r = _load().sd_verify_chain(_ptr(target), _ptr(draft) if not greedy else None, dt, _ptr(tokens),
                                 _ptr(uniforms) if not greedy else None, _ptr(cu), int(B), int(K_max),
                                 int(V), ctypes.c_float(float(temperature)), int(top_k), _ptr(A),
@@ -349,7 +354,7 @@ def verify_chain_capped(target: torch.Tensor, draft: Optional[torch.Tensor], tok
     st = torch.empty(B, dtype=torch.int32, device=dev)
     probs = torch.empty(max(B * K, 1), 2, dtype=torch.float32, device=dev) if want_probs and not greedy else None
     resid = torch.empty(B, dtype=torch.float32, device=dev) if want_resid and not greedy else None
-    ws = _workspace(workspace_bytes(OP_CHAIN, B, K, V, top_k), dev, workspace)
+    ws = _workspace(workspace_bytes(OP_CHAIN, B, K, V, top_k), dev, workspace, stream)
     r = _load().sd_verify_chain_capped(_ptr(target), _ptr(draft) if not greedy else None, dt,
                                        _ptr(tokens), _ptr(uniforms) if not greedy else None,
                                        _ptr(k_cap), B, K, V, ctypes.c_float(float(temperature)),
@@ -390,7 +395,7 @@ def verify_greedy(target: torch.Tensor, tokens: torch.Tensor, cu: Optional[torch
     A = torch.empty(B, dtype=torch.int32, device=dev)
     nxt = torch.empty(B, dtype=torch.int32, device=dev)
     st = torch.empty(B, dtype=torch.int32, device=dev)
-    ws = _workspace(workspace_bytes(OP_GREEDY, B, K_max, V), dev, workspace)
+    ws = _workspace(workspace_bytes(OP_GREEDY, B, K_max, V), dev, workspace, stream)
     r = _load().sd_verify_greedy(_ptr(target), dt, _ptr(tokens), _ptr(cu), int(B), int(K_max), int(V),
                                  _ptr(A), _ptr(nxt), _ptr(st), _ptr(ws), ctypes.c_size_t(ws.numel()),
                                  _stream(stream))
@@ -412,7 +417,7 @@ def build_tree(marginals: torch.Tensor, N: int, workspace: Optional[torch.Tensor
         "anc_mask": torch.empty(B, N, dtype=torch.int64, device=dev),
         "n_nodes": torch.empty(B, dtype=torch.int32, device=dev),
     }
-    ws = _workspace(workspace_bytes(OP_BUILD_TREE, B, K, V, 0, N), dev, workspace)
+    ws = _workspace(workspace_bytes(OP_BUILD_TREE, B, K, V, 0, N), dev, workspace, stream)
     r = _load().sd_build_tree(_ptr(marginals), B, K, V, int(N), _ptr(out["token"]), _ptr(out["parent"]),
                               _ptr(out["depth"]), _ptr(out["score"]), _ptr(out["anc_mask"]),
                               _ptr(out["n_nodes"]), _ptr(ws), ctypes.c_size_t(ws.numel()),

@@ -194,7 +194,7 @@ __device__ __forceinline__ uint32_t wave_jth_largest(uint32_t key, int j) {
 #pragma unroll
     for (int bit = 31; bit >= LO; --bit) {
         const uint32_t c = r | (1u << bit);
-        if (__popcll(__ballot(key >= c)) >= j) r = c;
+        if ((int)__popcll(__ballot(key >= c)) >= j) r = c;
     }
     return r;
 }

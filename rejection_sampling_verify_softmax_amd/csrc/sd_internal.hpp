@@ -26,10 +26,6 @@ static_assert(kChunkBf16 % (256 * 8) == 0, "bf16 chunk: whole workgroup rounds o
 static_assert(kChunkF32 % (256 * 4) == 0, "fp32 chunk: whole workgroup rounds of 16-byte vectors");
 
 inline int chunk_elems(int dtype) { return dtype == 1 ? kChunkBf16 : kChunkF32; }
-// Sub-block: one wave's 64 consecutive 16-byte vectors (512 bf16 or 256 fp32
-// elements). Residual masses are kept per sub-block.
-inline int sub_block_elems(int dtype) { return dtype == 1 ? 512 : 256; }
-inline int sub_blocks_per_chunk(int dtype) { return chunk_elems(dtype) / sub_block_elems(dtype); }
 inline int n_chunks_for(int V, int dtype) {
     const int c = chunk_elems(dtype);
     return (V + c - 1) / c;

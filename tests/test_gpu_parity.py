@@ -318,6 +318,40 @@ def test_graph_capture_replays_equal_eager():
     del g
 
 
+def test_calls_on_a_side_stream_match_the_current_stream():
+    # every call given `stream=` runs there, its internally allocated workspace
+    # held for that stream; results equal those of the same calls on the
+    # current stream, while the current stream keeps allocating and writing
+    case = wl.gen_adaptive_chain(device="cuda", seed=51, B=64, K=6, V=30000)
+    tr = wl.gen_tree(device="cuda", seed=52, B=8, K=16, V=20000, N=64)
+    gr = wl.gen_greedy_chain(device="cuda", seed=53, B=8, K=3, V=20000)
+    _say("side stream: select_len + packed chain, greedy, build_tree")
+    packed = case.packed(sd.select_len(case.conf, case.cost)["k"])
+    torch.cuda.synchronize()
+    B, K = case.B, case.K_max
+
+    def run(stream):
+        sel = sd.select_len(case.conf, case.cost, stream=stream)
+        ch = sd.verify_chain(packed.target, packed.draft, packed.tokens, packed.uniforms, 1.0, cu=sel["cu"],
+                             B=B, K_max=K, stream=stream)
+        g = sd.verify_greedy(gr.target, gr.tokens, K_max=gr.K_max, stream=stream)
+        t = sd.build_tree(tr.marginals, 64, stream=stream)
+        return {"sel": sel, "chain": ch, "greedy": g, "tree": t}
+
+    ref = run(None)
+    torch.cuda.synchronize()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    side = run(s)
+    junk = [torch.full((1 << 20,), 3, dtype=torch.uint8, device="cuda") for _ in range(16)]
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    del junk
+    for k in ref:
+        for kk in ref[k]:
+            assert torch.equal(side[k][kk], ref[k][kk]), (k, kk)
+
+
 def test_chain_run_twice_bit_identical():
     case = wl.gen_base_noise_chain(9, B=16, K=6, V=50000, base_sigma=2.0, noise_sigma=0.7,
                                    temperature=1.0, dtype="bf16", device="cuda")
