@@ -10,8 +10,9 @@
 // per-position cost (or maximises the objective of a cost table); the packed
 // offsets cu_sel are the exclusive scan of the lengths, on the device, ready
 // for a packed chain verify on the same stream without a host round trip.
-// Batches up to 8192 sequences: one workgroup does both. Larger batches: one
-// thread per sequence for the lengths, then one workgroup scans them.
+// Batches up to 8192 sequences: one 1024-thread workgroup does both. Larger
+// batches: one thread per sequence for the lengths, then one workgroup scans
+// them.
 #include "sd_device.hpp"
 #include "sd_internal.hpp"
 
@@ -19,9 +20,9 @@ namespace sd {
 
 namespace {
 
-constexpr int kSelectLds = 4096;         // lengths kept in LDS for the offsets
-// Up to this many sequences one workgroup does everything; larger batches
-// take one thread per sequence for the lengths, then a scan workgroup.
+// Up to this many sequences one workgroup does everything (their lengths kept
+// in LDS for the offsets); larger batches take one thread per sequence for
+// the lengths, then a scan workgroup.
 constexpr int kOneBlockMaxB = 8192;
 constexpr int kScanThreads = 1024;
 
@@ -65,38 +66,51 @@ __device__ __forceinline__ int seq_len(const float* __restrict__ conf, int64_t b
     return k;
 }
 
-// One workgroup: each thread takes a contiguous run of sequences, then a
-// block scan turns the lengths into packed offsets cu_sel (ready for a packed
-// chain verify on the same stream, without a host round trip).
-__global__ __launch_bounds__(kBlock) void k_select_len(const float* __restrict__ conf, int B,
-                                                       int K_max, float cost,
-                                                       const float* __restrict__ table,
-                                                       int32_t* __restrict__ k_sel,
-                                                       float* __restrict__ adv,
-                                                       int32_t* __restrict__ cu_sel) {
-    __shared__ double scan_scratch[kWavesPerBlock];
-    __shared__ int32_t sk[kSelectLds];       // the lengths again, for the offsets
-    const int per = (B + kBlock - 1) / kBlock;
-    const int b0 = threadIdx.x * per;
+// One workgroup: each thread takes a contiguous run of sequences (one while
+// B <= 1024), then a block scan of the per-thread sums turns the lengths into
+// packed offsets cu_sel (ready for a packed chain verify on the same stream,
+// without a host round trip).
+__global__ __launch_bounds__(kScanThreads) void k_select_len(const float* __restrict__ conf, int B,
+                                                             int K_max, float cost,
+                                                             const float* __restrict__ table,
+                                                             int32_t* __restrict__ k_sel,
+                                                             float* __restrict__ adv,
+                                                             int32_t* __restrict__ cu_sel) {
+    constexpr int kWaves = kScanThreads / kWave;
+    __shared__ int wsum[kWaves];
+    __shared__ int32_t sk[kOneBlockMaxB];     // the lengths again, for the offsets
+    const int tid = threadIdx.x;
+    const int lane = tid & (kWave - 1);
+    const int w = tid / kWave;
+    const int per = (B + kScanThreads - 1) / kScanThreads;
+    const int b0 = tid * per;
     const int b1 = min(B, b0 + per);
     int local = 0;
     for (int b = b0; b < b1; ++b) {
         double sum;
         const int k = seq_len(conf, b, K_max, cost, table, &sum);
         k_sel[b] = k;
-        if (b < kSelectLds) sk[b] = k;
+        sk[b] = k;
         if (adv) adv[b] = (float)(1.0 + sum);
         local += k;
     }
     if (cu_sel == nullptr) return;
-    double total;
-    const double excl = block_exclusive_scan((double)local, scan_scratch, &total);
-    int run = (int)excl;
+    const int incl = wave_incl_scan_int(local);
+    if (lane == kWave - 1) wsum[w] = incl;
+    __syncthreads();
+    int before = 0, total = 0;
+#pragma unroll
+    for (int i = 0; i < kWaves; ++i) {
+        const int t = wsum[i];
+        before += i < w ? t : 0;
+        total += t;
+    }
+    int run = before + incl - local;
     for (int b = b0; b < b1; ++b) {
         cu_sel[b] = run;
-        run += b < kSelectLds ? sk[b] : k_sel[b];    // (this thread's own stores)
+        run += sk[b];                // (this thread's own stores)
     }
-    if (threadIdx.x == kBlock - 1) cu_sel[B] = (int)total;
+    if (tid == 0) cu_sel[B] = total;
 }
 
 // Large batches, step 1: one thread per sequence.
@@ -156,8 +170,8 @@ __global__ __launch_bounds__(kScanThreads) void k_scan_lengths(const int32_t* __
 hipError_t launch_select_len(const float* conf, int B, int K_max, float cost, const float* table,
                              int32_t* k_sel, float* adv, int32_t* cu_sel, hipStream_t stream) {
     if (B <= kOneBlockMaxB) {
-        hipLaunchKernelGGL(k_select_len, dim3(1), dim3(kBlock), 0, stream, conf, B, K_max, cost, table,
-                           k_sel, adv, cu_sel);
+        hipLaunchKernelGGL(k_select_len, dim3(1), dim3(kScanThreads), 0, stream, conf, B, K_max, cost,
+                           table, k_sel, adv, cu_sel);
         return hipGetLastError();
     }
     hipLaunchKernelGGL(k_select_len_wide, dim3((unsigned)((B + kBlock - 1) / kBlock)), dim3(kBlock), 0,

@@ -77,7 +77,10 @@ __device__ const typename E::raw* topk_row(const typename E::raw* tgt, const typ
 }
 
 constexpr int kTopkSample = 8;           // vectors per thread held in registers for the threshold
-constexpr int kTopkU = 4;                // vectors per thread per main-pass step (as many more in flight)
+#ifndef SD_TOPK_U
+#define SD_TOPK_U 4
+#endif
+constexpr int kTopkU = SD_TOPK_U;        // vectors per thread per main-pass step (as many more in flight)
 constexpr int kWaveCap = 512;            // per-wave candidate buffer (64-bit keys)
 constexpr int kTopkPhaseSplit = 2;       // slots streamed before the first decision
 constexpr size_t kTopkPhaseMinElems = size_t(1) << 24;   // smaller windows: one phase
