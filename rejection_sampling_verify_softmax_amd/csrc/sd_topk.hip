@@ -1430,14 +1430,14 @@ __global__ __launch_bounds__(kBuildThreads) void k_tree_build(
 // order above (value desc, id asc; NaN never kept).
 //  1. Every thread loads its vectors (all in flight together) and takes its
 //     largest value.
-//  2. Each wave's 8th-largest thread maximum (equal maxima leave together)
-//     is reached by at least 8 of the wave's tokens, so the smallest of them
-//     over the 8 waves (t) is reached by at least 64 > W tokens: every token
-//     of the top W has a value >= t.
+//  2. Each wave's 8th-largest thread maximum, rounded down to 16 key bits
+//     (a ballot bisection), is reached by at least 8 of the wave's tokens, so
+//     the smallest of them over the 8 waves (t) is reached by at least 64 > W
+//     tokens: every token of the top W has a value >= t.
 //  3. The tokens with a value >= t (about a hundred on a row of
 //     probabilities) go to LDS as keys in one pass, placed by an LDS counter;
-//     each takes its rank by counting the larger keys, and the first W are
-//     written in rank order.
+//     each key takes its rank by counting the larger keys (8 per LDS wait),
+//     and the first W are written in rank order.
 //  4. Should more than kShortCap tokens reach t (mass ties), a key bound is
 //     found by bisection over the key space, reached by at least W and at
 //     most kShortCap keys (keys are distinct, so such a bound exists).
@@ -1522,14 +1522,10 @@ __global__ __launch_bounds__(kShortThreads) void k_topk_short(const typename E::
         for (int e = 0; e < EV; ++e) vmax[i] = fmaxf(vmax[i], raw_elem<E>(v[i], e));
         m = fmaxf(m, vmax[i]);
     }
-    // 2. each wave's kShortRth-th largest thread maximum, as order-preserving
-    // bits (0: none); each round retires every thread at the round's maximum
-    uint32_t mine = (m == m) ? ordered_bits(m) : 0u, rth = 0u;
-#pragma unroll
-    for (int r = 0; r < kShortRth; ++r) {
-        rth = wave_max_u32(mine);
-        if (mine == rth) mine = 0u;
-    }
+    // 2. each wave's kShortRth-th largest thread maximum as order-preserving
+    // bits, kept to its top 16 bits (rounded down: still reached by at least
+    // kShortRth of the wave's maxima; 0: fewer than kShortRth kept)
+    const uint32_t rth = wave_jth_largest<16>((m == m) ? ordered_bits(m) : 0u, kShortRth);
     if (lane == 0) wkey[w] = rth;
     if (tid == 0) s_total = 0;
     __syncthreads();
@@ -1640,12 +1636,27 @@ __global__ __launch_bounds__(kShortThreads) void k_topk_short(const typename E::
             L[rank] = te;
         }
     };
+    // keys past the candidates read as 0, which no key beats: the counts
+    // below read 8 keys per LDS wait
+    const int padded = (total + 31) & ~31;
+    for (int i = total + tid; i < padded; i += kShortThreads) cand[i] = 0ull;
+    __syncthreads();
+    auto count_above8 = [&](int j, unsigned long long k) __attribute__((always_inline)) -> int {
+        unsigned long long c8[8];
+#pragma unroll
+        for (int q = 0; q < 8; ++q) c8[q] = cand[j + q];
+        int r = 0;
+#pragma unroll
+        for (int q = 0; q < 8; ++q) r += c8[q] > k ? 1 : 0;
+        return r;
+    };
     if (total <= kShortThreads / 4) {
-        // four threads (a DPP quad) count a quarter of the larger keys each
+        // four threads (a DPP quad) count the larger keys in a quarter of the
+        // 8-key blocks each
         const int ci = tid >> 2, part = tid & 3;
         const unsigned long long k = ci < total ? cand[ci] : ~0ull;
         int r = 0;
-        for (int j = part; j < total; j += 4) r += cand[j] > k ? 1 : 0;
+        for (int j = part * 8; j < padded; j += 32) r += count_above8(j, k);
         r += __builtin_amdgcn_update_dpp(0, r, 0xb1, 0xf, 0xf, false);   // quad_perm [1,0,3,2]
         r += __builtin_amdgcn_update_dpp(0, r, 0x4e, 0xf, 0xf, false);   // quad_perm [2,3,0,1]
         if (ci < total && part == 0) put(k, r);
@@ -1653,7 +1664,7 @@ __global__ __launch_bounds__(kShortThreads) void k_topk_short(const typename E::
         for (int ci = tid; ci < total; ci += kShortThreads) {
             const unsigned long long k = cand[ci];
             int rank = 0;
-            for (int j = 0; j < total; ++j) rank += cand[j] > k ? 1 : 0;
+            for (int j = 0; j < padded; j += 8) rank += count_above8(j, k);
             put(k, rank);
         }
     }
