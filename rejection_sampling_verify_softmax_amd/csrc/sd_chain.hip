@@ -625,7 +625,10 @@ __device__ int sample_by_rescan(const typename E::raw* tp, int V, const WeightFn
     return scan_piece<E, false, false>(tp, tp, last * pe, V, wf, 0.0, target, true);
 }
 
-constexpr int kSeqPerBlock = kBlock / kWave;    // decide / sample: one wave per sequence
+#ifndef SD_DECIDE_SEQS
+#define SD_DECIDE_SEQS 2
+#endif
+constexpr int kSeqPerBlock = SD_DECIDE_SEQS;     // decide / sample: one wave per sequence
 
 // Inputs and outputs of the per-sequence decision.
 struct DecideArgs {
@@ -760,7 +763,7 @@ __device__ __forceinline__ bool decide_sequence(const DecideArgs& g, int b, Chai
 
 // One wave per sequence: the decision after a phase; the descriptor goes to
 // the workspace for the launches that draw the final token.
-__global__ __launch_bounds__(kBlock) void k_chain_decide(DecideArgs g, int B, int alive_in,
+__global__ __launch_bounds__(kSeqPerBlock * kWave) void k_chain_decide(DecideArgs g, int B, int alive_in,
                                                          ChainDesc* __restrict__ desc) {
     const int b = blockIdx.x * kSeqPerBlock + threadIdx.x / kWave;
     if (b >= B) return;
@@ -797,7 +800,7 @@ __global__ __launch_bounds__(kResolveThreads) void k_chain_mass(
 // token order at u_k times the total). The rare case of a residual with no
 // mass (rounding) is redrawn from p of the decision row by the same wave.
 template <class E, bool VEC>
-__global__ __launch_bounds__(kBlock) void k_chain_sample(
+__global__ __launch_bounds__(kSeqPerBlock * kWave) void k_chain_sample(
     const typename E::raw* __restrict__ tgt, const typename E::raw* __restrict__ dft,
     const ChainDesc* __restrict__ desc, const double* __restrict__ piece_ws, int B, int V,
     float c, int32_t* __restrict__ next_out, float* __restrict__ R_out) {
@@ -967,13 +970,13 @@ static hipError_t chain_full_impl(const ChainArgs& a) {
                                a.resid_mass_out);
             return hipGetLastError();
         }
-        hipLaunchKernelGGL(k_chain_decide, dim3(seq_blocks), dim3(kBlock), 0, a.stream, g, a.B,
+        hipLaunchKernelGGL(k_chain_decide, dim3(seq_blocks), dim3(kSeqPerBlock * kWave), 0, a.stream, g, a.B,
                            ph > 0 ? 1 : 0, desc);
     }
     hipLaunchKernelGGL((k_chain_mass<E, VEC>), dim3((unsigned)((size_t)a.B * n_mchunks)),
                        dim3(kResolveThreads), 0, a.stream, tgt, dft, desc, a.V, mchunk, n_mchunks, c,
                        pieces);
-    hipLaunchKernelGGL((k_chain_sample<E, VEC>), dim3(seq_blocks), dim3(kBlock), 0, a.stream, tgt,
+    hipLaunchKernelGGL((k_chain_sample<E, VEC>), dim3(seq_blocks), dim3(kSeqPerBlock * kWave), 0, a.stream, tgt,
                        dft, desc, pieces, a.B, a.V, c, a.next_token, a.resid_mass_out);
     return hipGetLastError();
 }

@@ -727,7 +727,12 @@ __device__ __forceinline__ RowTop shfl_rowtop(const RowTop& r, int src) {
     return o;
 }
 
-__global__ __launch_bounds__(kBlock) void k_chain_topk_decide(
+#ifndef SD_TOPK_DECIDE_SEQS
+#define SD_TOPK_DECIDE_SEQS 1
+#endif
+constexpr int kDecideSeqs = SD_TOPK_DECIDE_SEQS;     // sequences (waves) per workgroup
+
+__global__ __launch_bounds__(kDecideSeqs * kWave) void k_chain_topk_decide(
     const TopEntry* __restrict__ lists, const RowTop* __restrict__ rowtop,
     const int32_t* __restrict__ tok, const float* __restrict__ uni, const int32_t* __restrict__ cu,
     int B, int K_max, int V, int topk, float temperature, int32_t* __restrict__ A_out,
@@ -735,13 +740,13 @@ __global__ __launch_bounds__(kBlock) void k_chain_topk_decide(
     int32_t* __restrict__ status_out, const int32_t* __restrict__ cap,
     int32_t* __restrict__ A_full_out, int hi, int32_t* __restrict__ state, int phase,
     int32_t* __restrict__ live, int32_t* __restrict__ live_n) {
-    __shared__ double wbuf_all[kWavesPerBlock][kMaxTopk];
-    __shared__ int ibuf_all[kWavesPerBlock][kMaxTopk];
-    __shared__ TopEntry pl_all[kWavesPerBlock][kMaxTopk];
-    __shared__ TopEntry dl_all[kWavesPerBlock][kMaxTopk];
+    __shared__ double wbuf_all[kDecideSeqs][kMaxTopk];
+    __shared__ int ibuf_all[kDecideSeqs][kMaxTopk];
+    __shared__ TopEntry pl_all[kDecideSeqs][kMaxTopk];
+    __shared__ TopEntry dl_all[kDecideSeqs][kMaxTopk];
     const int w = threadIdx.x / kWave;
     const int lane = threadIdx.x & (kWave - 1);
-    const int b = blockIdx.x * kWavesPerBlock + w;
+    const int b = blockIdx.x * kDecideSeqs + w;
     if (b >= B) return;
     if (phase > 0 && state[b] != phase) return;        // decided in an earlier phase
     const int slots = K_max + 1;
@@ -1736,7 +1741,7 @@ static hipError_t chain_topk_impl(const ChainArgs& a) {
     const int bounds[3] = {0, phased ? kTopkPhaseSplit : a.K_max + 1, a.K_max + 1};
     const int n_phases = phased ? 2 : 1;
     int32_t* state = phased ? phase_state : nullptr;
-    const unsigned seq_blocks = (unsigned)((a.B + kWavesPerBlock - 1) / kWavesPerBlock);
+    const unsigned seq_blocks = (unsigned)((a.B + kDecideSeqs - 1) / kDecideSeqs);
     for (int ph = 0; ph < n_phases; ++ph) {
         const int lo = bounds[ph], hi = bounds[ph + 1];
         const unsigned grid = (unsigned)((size_t)a.B * (hi - lo) * 2);
@@ -1752,7 +1757,7 @@ static hipError_t chain_topk_impl(const ChainArgs& a) {
                                static_cast<const raw*>(a.target), static_cast<const raw*>(a.draft),
                                a.cu, a.K_max, a.V, a.top_k, 1, a.tokens, a.temperature, L.lists,
                                L.counts, L.rowtop, lo, hi - lo, (const int32_t*)L.live, live_n);
-        hipLaunchKernelGGL(k_chain_topk_decide, dim3(seq_blocks), dim3(kBlock), 0, a.stream, L.lists,
+        hipLaunchKernelGGL(k_chain_topk_decide, dim3(seq_blocks), dim3(kDecideSeqs * kWave), 0, a.stream, L.lists,
                            L.rowtop, a.tokens, a.uniforms, a.cu, a.B, a.K_max, a.V, a.top_k,
                            a.temperature, a.accepted_len, a.next_token, a.probs_out,
                            a.resid_mass_out, a.seq_status, a.cap, a.accepted_full, hi, state, ph, L.live,
