@@ -73,7 +73,7 @@ struct ChainDesc {
 // logits at the draft token, that position's uniform and whether the token is
 // in range, so that the decision reads nothing that depends on the packed
 // offsets. The extra-token slot carries only its uniform.
-struct SlotRec {
+struct alignas(16) SlotRec {
     float xt, xd;
     float u;
     int32_t yok;
@@ -285,26 +285,31 @@ __global__ __launch_bounds__(kBlock) void k_chain_stats(
     }
 }
 
-// Row statistics from its chunk partials. References are integers, so each
-// partial is rescaled exactly by a power of two (fixed chunk order, fp64).
-__device__ RowStat combine_row(const Partial* p, int n_chunks) {
-    // the first kReg partials are loaded together (one memory latency)
-    constexpr int kReg = 8;
-    Partial q[kReg];
+constexpr int kRegChunks = 8;          // partials of a row loaded together
+
+// The first kRegChunks partials of a row (n_chunks >= 1), loaded without
+// branches so that several rows' loads are in flight together: an index past
+// the row's chunks reads its last chunk again, and that copy is ignored.
+__device__ __forceinline__ void load_partials(const Partial* p, int n_chunks, Partial (&q)[kRegChunks]) {
 #pragma unroll
-    for (int i = 0; i < kReg; ++i)
-        if (i < n_chunks) q[i] = p[i];
+    for (int i = 0; i < kRegChunks; ++i) q[i] = p[i < n_chunks ? i : n_chunks - 1];
+}
+
+// Row statistics from its chunk partials (the first kRegChunks in q, the rest
+// read from p). References are integers, so each partial is rescaled exactly
+// by a power of two (fixed chunk order, fp64).
+__device__ RowStat combine_loaded(const Partial (&q)[kRegChunks], const Partial* p, int n_chunks) {
     RowStat r;
     r.O = -INFINITY;
     r.S = 0.0;
     r.valid = true;
 #pragma unroll
-    for (int i = 0; i < kReg; ++i)
+    for (int i = 0; i < kRegChunks; ++i)
         if (i < n_chunks) {
             if (!isfinite(q[i].S)) r.valid = false;
             if (q[i].S > 0.0) r.O = fmaxf(r.O, q[i].o);
         }
-    for (int i = kReg; i < n_chunks; ++i) {
+    for (int i = kRegChunks; i < n_chunks; ++i) {
         const Partial t = p[i];
         if (!isfinite(t.S)) r.valid = false;
         if (t.S > 0.0) r.O = fmaxf(r.O, t.o);
@@ -315,15 +320,21 @@ __device__ RowStat combine_row(const Partial* p, int n_chunks) {
     }
     double S = 0.0;
 #pragma unroll
-    for (int i = 0; i < kReg; ++i)
+    for (int i = 0; i < kRegChunks; ++i)
         if (i < n_chunks && q[i].S > 0.0) S += ldexp(q[i].S, (int)fmaxf(q[i].o - r.O, -4096.f));
-    for (int i = kReg; i < n_chunks; ++i) {
+    for (int i = kRegChunks; i < n_chunks; ++i) {
         const Partial t = p[i];
         if (t.S > 0.0) S += ldexp(t.S, (int)fmaxf(t.o - r.O, -4096.f));
     }
     r.S = S;
     r.valid = isfinite(S) && S > 0.0;
     return r;
+}
+
+__device__ RowStat combine_row(const Partial* p, int n_chunks) {
+    Partial q[kRegChunks];
+    load_partials(p, n_chunks, q);
+    return combine_loaded(q, p, n_chunks);
 }
 
 // Sampling weight of one token in fp32: the normalised residual max(p - q, 0)
@@ -667,19 +678,25 @@ __device__ __forceinline__ bool decide_sequence(const DecideArgs& g, int b, Chai
     const int slots = K_max + 1;
     const int64_t slot0 = (int64_t)b * slots;
     // Lane s combines the partials of slot s (target, and draft below K_max)
-    // and reads the slot's record, for every slot streamed so far; none of
-    // these loads waits for cu (one round trip; a lane past the sequence's
-    // slots reads a record that is never used).
+    // and reads the slot's record, for every slot streamed so far. Every lane
+    // issues its loads at once, with no branch between them (a lane past the
+    // streamed slots reads the last one's, a slot without a draft row reads
+    // memory it never uses), and none of them waits for cu: one round trip.
     const int ns = slots < hi ? slots : hi;
+    const int ls = lane < ns ? lane : ns - 1;
+    Partial qt[kRegChunks], qd[kRegChunks];
+    load_partials(part_t + (slot0 + ls) * n_chunks, n_chunks, qt);
+    load_partials(part_d + (slot0 + ls) * n_chunks, n_chunks, qd);
+    const SlotRec r_ls = rec[slot0 + ls];
+    int d0, k;
+    seq_range(g.cu, b, K_max, d0, k);
     RowStat rp{-INFINITY, 0.0, false}, rq{-INFINITY, 0.0, false};
     SlotRec r{0.f, 0.f, 0.f, 0};
     if (lane < ns) {
-        rp = combine_row(part_t + (slot0 + lane) * n_chunks, n_chunks);
-        r = rec[slot0 + lane];
-        if (lane < K_max) rq = combine_row(part_d + (slot0 + lane) * n_chunks, n_chunks);
+        rp = combine_loaded(qt, part_t + (slot0 + lane) * n_chunks, n_chunks);
+        r = r_ls;
+        if (lane < K_max) rq = combine_loaded(qd, part_d + (slot0 + lane) * n_chunks, n_chunks);
     }
-    int d0, k;
-    seq_range(g.cu, b, K_max, d0, k);
     // positions evaluated so far: those of the slots streamed up to this phase
     const int kk = k < hi ? k : hi;
     // uniform of position `lane` (streamed slots; lane k_b's is the final draw's

@@ -354,7 +354,7 @@ __device__ __forceinline__ int committed_len(const int32_t* cap, int b, int k) {
 // where the reference o is an fp32 value (normally fl32(m*c) for some logit m).
 // Partials of disjoint sets combine exactly in fp64 (see combine()).
 // ---------------------------------------------------------------------------
-struct Partial {
+struct alignas(16) Partial {
     float o;        // reference (fp32); -inf for an empty set
     float pad;
     double S;       // sum relative to o; 0 for an empty set, non-finite for a bad set
