@@ -158,6 +158,13 @@ def setup_adaptive(torch, sd, wl):
         "kernel": "k_chain_stats", "kernel_bytes": stats_bytes, "step_bytes": step_bytes,
         "mean_k": positions / B, "mean_A": out["accepted_len"].float().mean().item(),
         "rows_streamed": rows1 + rows2, "rows_in_windows": R_t + R_d,
+        # the step's two calls, timed alone after the timed region
+        "parts": {
+            "select_len": lambda: sd.select_len(case.conf, case.cost, out=sel_out),
+            "verify": lambda: sd.verify_chain(packed.target, packed.draft, packed.tokens, packed.uniforms, 1.0,
+                                              cu=sel_out["cu"], B=B, K_max=K, workspace=ws, out=out,
+                                              validate=False),
+        },
     }
     cpu = {"leg": cpu_leg_adaptive, "case": case, "packed": packed, "out": out, "sel": sel_out}
     return step, meta, cpu
@@ -238,7 +245,12 @@ def setup_adaptive_table(torch, sd, wl):
             "positions_per_step": positions, "kernel": "k_chain_stats",
             "kernel_bytes": stats_bytes, "step_bytes": step_bytes, "mean_k": positions / B, "mean_A": A,
             "mean_adv": float(sel["adv"].mean()), "cost_table": ct, "rows_streamed": rows1 + rows2,
-            "rows_in_windows": 2 * positions + B}
+            "rows_in_windows": 2 * positions + B,
+            "parts": {
+                "select_len": lambda: sd.select_len_table(case.conf, table, out=sel_out),
+                "verify": lambda: sd.verify_chain(packed.target, packed.draft, packed.tokens, packed.uniforms,
+                                                  1.0, cu=sel_out["cu"], B=B, K_max=K, workspace=ws, out=out),
+            }}
     cpu = {"leg": cpu_leg_adaptive, "case": case, "packed": packed, "out": out, "sel": sel_out,
            "table": table.cpu().numpy()}
     return step, meta, cpu
@@ -870,6 +882,8 @@ def main():
     ap.add_argument("--event-every", type=int, default=5,
                     help="time the dominant kernel with events on every n-th timed step")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--skip-parts", action="store_true",
+                    help="do not time the step's calls alone after the timed region")
     ap.add_argument("--graph", action="store_true",
                     help="time the steps as HIP-graph replays (8 captured steps, cycled); the "
                          "dominant kernel is still timed live on eager steps")
@@ -1006,6 +1020,20 @@ def main():
             result["step"][k] = meta[k]
     if "cost_table" in meta:
         result["cost_table"] = meta["cost_table"]
+    result["roofline"]["kernel_us_median"] = sorted(kernel_ms)[len(kernel_ms) // 2] * 1e3
+    if "parts" in meta and not args.skip_parts:
+        # each call of the step alone, 100 back to back between two events
+        # after 5 warm-ups (outside the timed region; same inputs and outputs)
+        for name, fn in meta["parts"].items():
+            for _ in range(5):
+                fn()
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record()
+            for _ in range(100):
+                fn()
+            b.record()
+            b.synchronize()
+            result["step"][f"{name}_us"] = a.elapsed_time(b) * 1e3 / 100
     if cpu is not None and not args.no_cpu_baseline:
         log("timing the CPU oracle on a bounded sample; parity of the timed step against it")
         result["cpu_baseline"], result["parity"] = run_cpu_baseline(cpu, args.cpu_seconds)
