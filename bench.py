@@ -465,7 +465,8 @@ def setup_rerank(torch, sd, wl):
             sd.expand_tree(cand, exp, ct, cp, expand_out=exp)
         if ev is not None:
             sd.time_next_stream_pass(*ev)
-        st["out"] = sd.rerank_tree(cand["parent"], cand["token"], cand["prob"], cand["n_cand"], N)
+        st["out"] = sd.rerank_tree(cand["parent"], cand["token"], cand["prob"], cand["n_cand"], N,
+                                   out=st.get("out"))
 
     step()
     torch.cuda.synchronize()

@@ -190,7 +190,7 @@ sd_status_t sd_verify_chain_capped(const void* target_logits, const void* draft_
  * A call whose path needs more than SD_NOALLOC_SCRATCH_BYTES of scratch
  * (sd_workspace_bytes gives an upper bound) returns SD_EWORKSPACE with
  * nothing launched; at V = 128256, K_max = 8 the full-vocabulary path fits
- * up to B = 5108 with bf16 logits and B = 2606 with fp32 logits. Every call on one GPU shares that array, so two calls
+ * up to B = 4999 with bf16 logits and B = 2577 with fp32 logits. Every call on one GPU shares that array, so two calls
  * that overlap in time on the same GPU (different streams, or host threads)
  * race: serialise them. The scratch needs no clearing between calls.
  */

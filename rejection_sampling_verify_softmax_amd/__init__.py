@@ -17,6 +17,7 @@ Functions mirror the C entry points:
 from __future__ import annotations
 
 import ctypes
+import functools
 import os
 from typing import Optional
 
@@ -94,12 +95,16 @@ def lib():
 
 
 def _ptr(t: Optional[torch.Tensor]):
-    return None if t is None else ctypes.c_void_p(t.data_ptr())
+    # a device address as a plain int (the entry points' argtypes take ints)
+    return None if t is None else t.data_ptr()
 
 
 def _stream(stream=None):
-    s = torch.cuda.current_stream() if stream is None else stream
-    return ctypes.c_void_p(s.cuda_stream)
+    """The HIP stream handle (an int) a call runs on: `stream`, else torch's
+    current stream on the current device."""
+    if stream is not None:
+        return stream.cuda_stream
+    return torch._C._cuda_getCurrentRawStream(torch.cuda.current_device())
 
 
 def _dtype_code(t: torch.Tensor) -> int:
@@ -123,9 +128,19 @@ def _check(t: Optional[torch.Tensor], name: str, dtype=None, device=None):
         raise ValueError(f"{name} is on {t.device}, expected {device}")
 
 
-def _get(d: dict, key: str, make):
-    t = d.get(key)
-    return make() if t is None else t
+def _out(o: dict, key: str, shape, dtype, dev):
+    """An output tensor: o[key] when the caller passed one (checked, so that no
+    kernel writes past it), else a new one."""
+    t = o.get(key)
+    if t is None:
+        return torch.empty(shape, dtype=dtype, device=dev)
+    _check(t, key, dtype, dev)
+    n = 1
+    for d in (shape if isinstance(shape, tuple) else (shape,)):
+        n *= d
+    if t.numel() < n:
+        raise ValueError(f"out[{key!r}] holds {t.numel()} elements, {n} needed")
+    return t
 
 
 def _raise(status: int, where: str):
@@ -151,14 +166,19 @@ def stream_read(data: torch.Tensor, sink: torch.Tensor, n_blocks: int, stream=No
     nbytes = data.numel() * data.element_size()
     if sink.numel() < n_blocks:
         raise ValueError("sink needs one word per workgroup")
-    _raise(_load().sd_stream_read(_ptr(data), ctypes.c_size_t(nbytes), _ptr(sink), int(n_blocks),
+    _raise(_load().sd_stream_read(_ptr(data), nbytes, _ptr(sink), int(n_blocks),
                                   _stream(stream)), "sd_stream_read")
 
 
 def workspace_bytes(op: int, B: int, K_max: int = 0, V: int = 1, top_k: int = 0, N: int = 2) -> int:
+    return _workspace_bytes(int(op), int(B), int(K_max), int(V), int(top_k), int(N))
+
+
+@functools.lru_cache(maxsize=256)
+def _workspace_bytes(op: int, B: int, K_max: int, V: int, top_k: int, N: int) -> int:
+    # a pure function of its sizes: remembered, so repeated calls skip the query
     out = ctypes.c_size_t(0)
-    _raise(_load().sd_workspace_bytes(int(op), int(B), int(K_max), int(V), int(top_k), int(N),
-                                      ctypes.byref(out)), "sd_workspace_bytes")
+    _raise(_load().sd_workspace_bytes(op, B, K_max, V, top_k, N, ctypes.byref(out)), "sd_workspace_bytes")
     return int(out.value)
 
 
@@ -241,22 +261,22 @@ def verify_chain(target: torch.Tensor, draft: Optional[torch.Tensor], tokens: to
         _check(uniforms, "uniforms", torch.float32, dev)
     _check_layout(target, draft, tokens, uniforms, cu, B, K_max, V, greedy, validate, stream)
     o = out or {}
-    A = _get(o, "accepted_len", lambda: torch.empty(B, dtype=torch.int32, device=dev))
-    nxt = _get(o, "next_token", lambda: torch.empty(B, dtype=torch.int32, device=dev))
-    st = _get(o, "status", lambda: torch.empty(B, dtype=torch.int32, device=dev))
+    A = _out(o, "accepted_len", B, torch.int32, dev)
+    nxt = _out(o, "next_token", B, torch.int32, dev)
+    st = _out(o, "status", B, torch.int32, dev)
     probs = None
     if want_probs and not greedy:
-        probs = _get(o, "probs", lambda: torch.empty(max(tokens.numel(), 1), 2, dtype=torch.float32, device=dev))
+        probs = _out(o, "probs", (max(tokens.numel(), 1), 2), torch.float32, dev)
     resid = None
     if want_resid and not greedy:
-        resid = _get(o, "resid", lambda: torch.empty(B, dtype=torch.float32, device=dev))
+        resid = _out(o, "resid", B, torch.float32, dev)
     nbytes = workspace_bytes(OP_CHAIN, B, K_max, V, top_k)
     ws = _workspace(nbytes, dev, workspace, stream)
     r = _load().sd_verify_chain(_ptr(target), _ptr(draft) if not greedy else None, dt, _ptr(tokens),
                                 _ptr(uniforms) if not greedy else None, _ptr(cu), int(B), int(K_max),
-                                int(V), ctypes.c_float(float(temperature)), int(top_k), _ptr(A),
+                                int(V), float(temperature), int(top_k), _ptr(A),
                                 _ptr(nxt), _ptr(probs), _ptr(resid), _ptr(st), _ptr(ws),
-                                ctypes.c_size_t(ws.numel()), _stream(stream))
+                                ws.numel(), _stream(stream))
     _raise(r, "sd_verify_chain")
     res = {"accepted_len": A, "next_token": nxt, "status": st}
     if probs is not None:
@@ -297,22 +317,18 @@ def verify_chain_noalloc(target: torch.Tensor, draft: Optional[torch.Tensor], to
         _check(uniforms, "uniforms", torch.float32, dev)
     _check_layout(target, draft, tokens, uniforms, cu, B, K_max, V, greedy, False, stream)
     o = out or {}
-    A = _get(o, "accepted_len", lambda: torch.empty(B, dtype=torch.int32, device=dev))
-    nxt = _get(o, "next_token", lambda: torch.empty(B, dtype=torch.int32, device=dev))
-    st = _get(o, "status", lambda: torch.empty(B, dtype=torch.int32, device=dev))
+    A = _out(o, "accepted_len", B, torch.int32, dev)
+    nxt = _out(o, "next_token", B, torch.int32, dev)
+    st = _out(o, "status", B, torch.int32, dev)
     probs = None
     if want_probs and not greedy:
-        probs = _get(o, "probs", lambda: torch.empty(max(tokens.numel(), 1), 2, dtype=torch.float32, device=dev))
+        probs = _out(o, "probs", (max(tokens.numel(), 1), 2), torch.float32, dev)
     resid = None
     if want_resid and not greedy:
-        resid = _get(o, "resid", lambda: torch.empty(B, dtype=torch.float32, device=dev))
-    for t, n, name in ((A, B, "accepted_len"), (nxt, B, "next_token"), (st, B, "status")):
-        _check(t, name, torch.int32, dev)
-        if t.numel() < n:
-            raise ValueError(f"{name} needs {n} entries")
+        resid = _out(o, "resid", B, torch.float32, dev)
     r = _load().sd_verify_chain_noalloc(_ptr(target), _ptr(draft) if not greedy else None, dt,
                                         _ptr(tokens), _ptr(uniforms) if not greedy else None, _ptr(cu),
-                                        int(B), int(K_max), int(V), ctypes.c_float(float(temperature)),
+                                        int(B), int(K_max), int(V), float(temperature),
                                         int(top_k), _ptr(A), _ptr(nxt), _ptr(probs), _ptr(resid), _ptr(st),
                                         _stream(stream))
     _raise(r, "sd_verify_chain_noalloc")
@@ -357,9 +373,9 @@ def verify_chain_capped(target: torch.Tensor, draft: Optional[torch.Tensor], tok
     ws = _workspace(workspace_bytes(OP_CHAIN, B, K, V, top_k), dev, workspace, stream)
     r = _load().sd_verify_chain_capped(_ptr(target), _ptr(draft) if not greedy else None, dt,
                                        _ptr(tokens), _ptr(uniforms) if not greedy else None,
-                                       _ptr(k_cap), B, K, V, ctypes.c_float(float(temperature)),
+                                       _ptr(k_cap), B, K, V, float(temperature),
                                        int(top_k), _ptr(A), _ptr(nxt), _ptr(Af), _ptr(probs),
-                                       _ptr(resid), _ptr(st), _ptr(ws), ctypes.c_size_t(ws.numel()),
+                                       _ptr(resid), _ptr(st), _ptr(ws), ws.numel(),
                                        _stream(stream))
     _raise(r, "sd_verify_chain_capped")
     res = {"accepted_len": A, "next_token": nxt, "accepted_full": Af, "status": st}
@@ -397,7 +413,7 @@ def verify_greedy(target: torch.Tensor, tokens: torch.Tensor, cu: Optional[torch
     st = torch.empty(B, dtype=torch.int32, device=dev)
     ws = _workspace(workspace_bytes(OP_GREEDY, B, K_max, V), dev, workspace, stream)
     r = _load().sd_verify_greedy(_ptr(target), dt, _ptr(tokens), _ptr(cu), int(B), int(K_max), int(V),
-                                 _ptr(A), _ptr(nxt), _ptr(st), _ptr(ws), ctypes.c_size_t(ws.numel()),
+                                 _ptr(A), _ptr(nxt), _ptr(st), _ptr(ws), ws.numel(),
                                  _stream(stream))
     _raise(r, "sd_verify_greedy")
     return {"accepted_len": A, "next_token": nxt, "status": st}
@@ -420,7 +436,7 @@ def build_tree(marginals: torch.Tensor, N: int, workspace: Optional[torch.Tensor
     ws = _workspace(workspace_bytes(OP_BUILD_TREE, B, K, V, 0, N), dev, workspace, stream)
     r = _load().sd_build_tree(_ptr(marginals), B, K, V, int(N), _ptr(out["token"]), _ptr(out["parent"]),
                               _ptr(out["depth"]), _ptr(out["score"]), _ptr(out["anc_mask"]),
-                              _ptr(out["n_nodes"]), _ptr(ws), ctypes.c_size_t(ws.numel()),
+                              _ptr(out["n_nodes"]), _ptr(ws), ws.numel(),
                               _stream(stream))
     _raise(r, "sd_build_tree")
     return out
@@ -439,12 +455,12 @@ def verify_tree(target: torch.Tensor, tree: dict, workspace: Optional[torch.Tens
     if tree["token"].numel() < B * N or tree["parent"].numel() < B * N or tree["n_nodes"].numel() < B:
         raise ValueError("tree arrays do not cover [B, N]")
     o = out or {}
-    path = _get(o, "path", lambda: torch.empty(B, N, dtype=torch.int32, device=dev))
-    A = _get(o, "accepted_len", lambda: torch.empty(B, dtype=torch.int32, device=dev))
-    nxt = _get(o, "next_token", lambda: torch.empty(B, dtype=torch.int32, device=dev))
+    path = _out(o, "path", (B, N), torch.int32, dev)
+    A = _out(o, "accepted_len", B, torch.int32, dev)
+    nxt = _out(o, "next_token", B, torch.int32, dev)
     r = _load().sd_verify_tree(_ptr(target), dt, _ptr(tree["token"]), _ptr(tree["parent"]),
                                _ptr(tree["n_nodes"]), B, N, V, _ptr(path), _ptr(A), _ptr(nxt),
-                               None, ctypes.c_size_t(0), _stream(stream))
+                               None, 0, _stream(stream))
     _raise(r, "sd_verify_tree")
     return {"path": path, "accepted_len": A, "next_token": nxt}
 
@@ -468,14 +484,14 @@ def verify_tree_sampled(target: torch.Tensor, tree: dict, uniforms: Optional[tor
         if uniforms.numel() < B * N:
             raise ValueError("uniforms needs one entry per (sequence, node)")
     o = out or {}
-    path = _get(o, "path", lambda: torch.empty(B, N, dtype=torch.int32, device=dev))
-    A = _get(o, "accepted_len", lambda: torch.empty(B, dtype=torch.int32, device=dev))
-    nxt = _get(o, "next_token", lambda: torch.empty(B, dtype=torch.int32, device=dev))
-    st = _get(o, "status", lambda: torch.empty(B, dtype=torch.int32, device=dev))
+    path = _out(o, "path", (B, N), torch.int32, dev)
+    A = _out(o, "accepted_len", B, torch.int32, dev)
+    nxt = _out(o, "next_token", B, torch.int32, dev)
+    st = _out(o, "status", B, torch.int32, dev)
     r = _load().sd_verify_tree_sampled(_ptr(target), dt, _ptr(tree["token"]), _ptr(tree["parent"]),
                                        _ptr(tree["n_nodes"]), _ptr(uniforms), B, N, V,
-                                       ctypes.c_float(float(temperature)), int(top_k), _ptr(path),
-                                       _ptr(A), _ptr(nxt), _ptr(st), None, ctypes.c_size_t(0),
+                                       float(temperature), int(top_k), _ptr(path),
+                                       _ptr(A), _ptr(nxt), _ptr(st), None, 0,
                                        _stream(stream))
     _raise(r, "sd_verify_tree_sampled")
     return {"path": path, "accepted_len": A, "next_token": nxt, "status": st}
@@ -487,10 +503,10 @@ def select_len(conf: torch.Tensor, cost: float, out: Optional[dict] = None, stre
     _check(conf, "conf", torch.float32, dev)
     B, K = (int(s) for s in conf.shape)
     o = out or {}
-    k = _get(o, "k", lambda: torch.empty(B, dtype=torch.int32, device=dev))
-    adv = _get(o, "adv", lambda: torch.empty(B, dtype=torch.float32, device=dev))
-    cu = _get(o, "cu", lambda: torch.empty(B + 1, dtype=torch.int32, device=dev))
-    r = _load().sd_select_len(_ptr(conf), B, K, ctypes.c_float(float(cost)), _ptr(k), _ptr(adv),
+    k = _out(o, "k", B, torch.int32, dev)
+    adv = _out(o, "adv", B, torch.float32, dev)
+    cu = _out(o, "cu", B + 1, torch.int32, dev)
+    r = _load().sd_select_len(_ptr(conf), B, K, float(cost), _ptr(k), _ptr(adv),
                               _ptr(cu), _stream(stream))
     _raise(r, "sd_select_len")
     return {"k": k, "adv": adv, "cu": cu}
@@ -506,9 +522,9 @@ def select_len_table(conf: torch.Tensor, cost_table: torch.Tensor, out: Optional
     if cost_table.numel() < K:
         raise ValueError("cost_table needs one entry per position")
     o = out or {}
-    k = _get(o, "k", lambda: torch.empty(B, dtype=torch.int32, device=dev))
-    adv = _get(o, "adv", lambda: torch.empty(B, dtype=torch.float32, device=dev))
-    cu = _get(o, "cu", lambda: torch.empty(B + 1, dtype=torch.int32, device=dev))
+    k = _out(o, "k", B, torch.int32, dev)
+    adv = _out(o, "adv", B, torch.float32, dev)
+    cu = _out(o, "cu", B + 1, torch.int32, dev)
     r = _load().sd_select_len_table(_ptr(conf), B, K, _ptr(cost_table), _ptr(k), _ptr(adv), _ptr(cu),
                                     _stream(stream))
     _raise(r, "sd_select_len_table")
@@ -584,10 +600,16 @@ def expand_tree(cand: dict, expand_in: Optional[torch.Tensor], child_token: torc
     return out
 
 
+_RERANK_OUT = (("token", torch.int32), ("parent", torch.int32), ("depth", torch.int32),
+               ("score", torch.float32), ("anc_mask", torch.int64), ("cand", torch.int32))
+
+
 def rerank_tree(cand_parent: torch.Tensor, cand_token: torch.Tensor, cand_prob: torch.Tensor,
-                n_cand: torch.Tensor, N: int, stream=None) -> dict:
+                n_cand: torch.Tensor, N: int, stream=None, out: Optional[dict] = None) -> dict:
     """sd_rerank_tree. cand_* [B, M] (int32, int32, float32) and n_cand [B] int32 on the GPU.
-    Returns the tree as build_tree does, plus "cand" (the candidate behind each node)."""
+    Returns the tree as build_tree does, plus "cand" (the candidate behind each node).
+    `out` may hold the output tensors of an earlier call of the same sizes, to be
+    overwritten instead of allocated."""
     dev = cand_parent.device
     _check(cand_parent, "cand_parent", torch.int32, dev)
     _check(cand_token, "cand_token", torch.int32, dev)
@@ -596,10 +618,14 @@ def rerank_tree(cand_parent: torch.Tensor, cand_token: torch.Tensor, cand_prob: 
     B, M = (int(x) for x in cand_parent.shape)
     if cand_token.shape != cand_parent.shape or cand_prob.shape != cand_parent.shape or n_cand.numel() != B:
         raise ValueError("candidate arrays must be [B, M] and n_cand [B]")
-    out = {k: torch.empty(B, N, dtype=t, device=dev) for k, t in
-           (("token", torch.int32), ("parent", torch.int32), ("depth", torch.int32),
-            ("score", torch.float32), ("anc_mask", torch.int64), ("cand", torch.int32))}
-    out["n_nodes"] = torch.empty(B, dtype=torch.int32, device=dev)
+    if out is None:
+        out = {k: torch.empty(B, N, dtype=t, device=dev) for k, t in _RERANK_OUT}
+        out["n_nodes"] = torch.empty(B, dtype=torch.int32, device=dev)
+    else:
+        for k, t in _RERANK_OUT + (("n_nodes", torch.int32),):
+            _check(out[k], k, t, dev)
+            if out[k].numel() != (B if k == "n_nodes" else B * N):
+                raise ValueError(f"out[{k!r}] must be [B, N] ([B] for n_nodes)")
     r = _load().sd_rerank_tree(_ptr(cand_parent), _ptr(cand_token), _ptr(cand_prob), _ptr(n_cand), B, M,
                                int(N), _ptr(out["token"]), _ptr(out["parent"]), _ptr(out["depth"]),
                                _ptr(out["score"]), _ptr(out["anc_mask"]), _ptr(out["cand"]),

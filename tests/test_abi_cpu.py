@@ -250,8 +250,14 @@ def test_noalloc_rejects_before_any_hip_call(L):
     assert na(uni=None) == 1
     assert na(draft=v(24)) == 1                   # misaligned logit rows
     # a batch whose scratch need exceeds the library's static array
-    assert na(B=5109, K=8, V=128256) == 3        # SD_EWORKSPACE, nothing launched (bf16 fits 5108)
-    assert na(B=2607, K=8, V=128256, dtype=0) == 3
+    # (V = 128256, K = 8: bf16 fits up to B = 4999, fp32 up to B = 2577)
+    assert na(B=5000, K=8, V=128256) == 3        # SD_EWORKSPACE, nothing launched
+    assert na(B=2578, K=8, V=128256, dtype=0) == 3
+    ws = ctypes.c_size_t()
+    assert L.sd_workspace_bytes(0, 2577, 8, 128256, 0, 0, ctypes.byref(ws)) == 0   # fp32 needs the most
+    assert ws.value <= 16 << 20
+    assert L.sd_workspace_bytes(0, 2578, 8, 128256, 0, 0, ctypes.byref(ws)) == 0
+    assert ws.value > 16 << 20
 
 
 def test_expand_tree_rejects_invalid_arguments(L):

@@ -57,6 +57,6 @@ def test_noalloc_rejects_a_batch_beyond_its_scratch():
     import ctypes
     r = lib.sd_verify_chain_noalloc(ctypes.c_void_p(x.data_ptr()), ctypes.c_void_p(x.data_ptr()), sd.SD_BF16,
                                     ctypes.c_void_p(tok.data_ptr()), ctypes.c_void_p(u.data_ptr()), None,
-                                    5109, 8, 128256, ctypes.c_float(1.0), 0, ctypes.c_void_p(tok.data_ptr()),
+                                    5000, 8, 128256, ctypes.c_float(1.0), 0, ctypes.c_void_p(tok.data_ptr()),
                                     ctypes.c_void_p(tok.data_ptr()), None, None, None, None)
     assert r == sd.SD_EWORKSPACE
