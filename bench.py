@@ -27,6 +27,7 @@ from __future__ import annotations
 import argparse
 import hashlib
 import json
+import math
 import os
 import sys
 import time
@@ -876,12 +877,15 @@ def run_cpu_baseline(cpu, target_seconds: float):
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--steps", type=int, default=None,
+                    help="timed steps (default: at least 200, and enough for 40 steps with kernel "
+                         "events at the default event spacing)")
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default="adaptive", choices=sorted(WORKLOADS))
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
-    ap.add_argument("--event-every", type=int, default=5,
-                    help="time the dominant kernel with events on every n-th timed step")
+    ap.add_argument("--event-every", type=int, default=None,
+                    help="time the dominant kernel with events on every n-th timed step (default: "
+                         "spaced so that the events add about 1 %% to the timed region, at least 5)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--skip-parts", action="store_true",
                     help="do not time the step's calls alone after the timed region")
@@ -925,7 +929,31 @@ def main():
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
-    log(f"warmup {args.warmup} done; timing {args.steps} steps")
+    # The step's own time, without events, sets how far apart the evented steps
+    # are: a launch bound to an event pair costs the step about 10-80 us (the
+    # stream idles around it, and the host issues it more slowly), which would
+    # dominate a launch-bound step of a few microseconds if every fifth step
+    # carried one.
+    n_cal = 1
+    while True:
+        t0 = time.perf_counter()
+        for _ in range(n_cal):
+            step()
+        torch.cuda.synchronize()
+        cal = time.perf_counter() - t0
+        if cal >= 0.01 or n_cal >= 1 << 16:
+            break
+        n_cal *= 2
+    t_step = cal / n_cal
+    event_cost_s = 50e-6
+    if args.event_every is None:
+        args.event_every = max(5, math.ceil(event_cost_s / (0.01 * t_step)))
+        if args.steps is not None:
+            args.event_every = min(args.event_every, max(5, args.steps // 20))
+    if args.steps is None:
+        args.steps = min(max(200, 40 * args.event_every), max(200, int(2.0 / t_step)))
+    log(f"warmup {args.warmup} done ({t_step * 1e6:.1f} us per step without events); timing "
+        f"{args.steps} steps, events on every {args.event_every}")
 
     # The dominant kernel is timed by a pair of events on every event_every-th
     # step of the timed region (each bound event leaves the stream idle for a
@@ -1004,12 +1032,14 @@ def main():
             "kernel": meta["kernel"],
             "kernel_us": kernel_ms_avg * 1e3,
             "launches_timed": len(kernel_ms),
+            "event_every": args.event_every,
             "algorithmic_bytes_per_launch": meta["kernel_bytes"],
         },
         "step": {
             "positions_per_step": positions,
             "algorithmic_bytes": meta["step_bytes"],
             "effective_GBps": meta["step_bytes"] / (ms_per_step * 1e-3) / 1e9,
+            "us_per_step_without_events": t_step * 1e6,
         },
     }
     result["config"]["parallelism"] = "none (one GPU)"
