@@ -8,10 +8,12 @@
 // p; temperature is folded into both p and q.
 //
 // Launches on the caller's stream:
-//   1. k_chain_stats  grid (sequence, slot, chunk): the one pass over every row.
-//      Slot i < k_b streams target row i and draft row i together; slot k_b
-//      streams the extra-token row. Each workgroup writes the softmax partial
-//      (o, S) of its chunk of each row and, for chunk 0, the two logits at y_i.
+//   1. k_chain_stats  grid (sequence, slot, [row,] chunk): the one pass over
+//      every row. Slot i < k_b has target row i and draft row i, streamed by
+//      one workgroup per row in the first phase and together in later phases;
+//      slot k_b has the extra-token row. Each workgroup writes the softmax
+//      partial (o, S) of its chunk of each of its rows and, for chunk 0 of the
+//      target row, the two logits at y_i.
 //   2. k_chain_decide one wave per sequence: combines the partials of each row
 //      exactly (integer references: a power-of-two rescale), evaluates
 //      p_i(y_i), q_i(y_i) in fp64, the accept bits and A (wave ballot), and the
@@ -54,6 +56,12 @@ constexpr int kU = SD_STATS_UNROLL;
 constexpr int kPhaseBounds[] = {SD_PHASE_BOUNDS};
 constexpr int kMaxPhases = (int)(sizeof(kPhaseBounds) / sizeof(int)) + 1;
 constexpr size_t kPhaseMinElems = size_t(1) << 24;     // logits in the window
+// The first phase of a phased verification streams one row per workgroup (1)
+// or a slot's target and draft rows together (0).
+#ifndef SD_SPLIT_FIRST_PHASE
+#define SD_SPLIT_FIRST_PHASE 1
+#endif
+constexpr int kSplitFirstPhase = SD_SPLIT_FIRST_PHASE;
 // A one-pass chunk sum is kept only below 2^64 (its reference was then close
 // enough to the chunk's maximum); otherwise the exact two-pass path runs.
 constexpr double kFastSumLimit = 18446744073709551616.0;
@@ -236,39 +244,43 @@ __global__ __launch_bounds__(kBlock) void k_chain_stats(
     const typename E::raw* __restrict__ tgt, const typename E::raw* __restrict__ dft,
     const int32_t* __restrict__ tok, const float* __restrict__ uni, const int32_t* __restrict__ cu,
     int K_max, int V, int chunk, int n_chunks, float c, Partial* __restrict__ part_t,
-    Partial* __restrict__ part_d, SlotRec* __restrict__ rec, int slot_lo, int slot_span,
+    Partial* __restrict__ part_d, SlotRec* __restrict__ rec, int slot_lo, int slot_span, int split,
     const int32_t* __restrict__ alive) {
     __shared__ double redd[kWavesPerBlock];
     __shared__ float redf[kWavesPerBlock];
     __shared__ int redi[kWavesPerBlock];
     const int slots = K_max + 1;
     const int ch = blockIdx.x % n_chunks;
-    const int rest = blockIdx.x / n_chunks;
+    // split: one row per workgroup (kind 0 the target row, kind 1 the draft
+    // row); else the slot's target and draft rows in one workgroup (kind 2)
+    const int kind = split ? (blockIdx.x / n_chunks) & 1 : 2;
+    const int rest = blockIdx.x / n_chunks / (split ? 2 : 1);
     const int s = slot_lo + rest % slot_span;
     const int b = rest / slot_span;
     if (alive != nullptr && alive[b] == 0) return;     // decided in an earlier phase
     int d0, k;
     seq_range(cu, b, K_max, d0, k);
-    if (s > k) return;
+    if (s > k || (kind == 1 && s == k)) return;        // the extra row has no draft row
     const int64_t slot_id = (int64_t)b * slots + s;
     const int64_t t_row = (int64_t)d0 + b + s;
+    const int64_t d_row = (int64_t)d0 + s;
     const int beg = ch * chunk;
     const int end = min(V, beg + chunk);
     const typename E::raw* tp = tgt + t_row * (int64_t)V;
-    if (s < k) {
-        const int64_t d_row = (int64_t)d0 + s;
-        const typename E::raw* dp = dft + d_row * (int64_t)V;
-        if (ch == 0 && threadIdx.x == 0) {
+    const typename E::raw* dp = s < k ? dft + d_row * (int64_t)V : nullptr;
+    if (kind != 1 && ch == 0 && threadIdx.x == 0) {
+        SlotRec r{NAN, NAN, uni[t_row], 0};
+        if (s < k) {
             const int y = tok[d_row];
-            const float u = uni[t_row];
-            SlotRec r{NAN, NAN, u, 0};
             if (y >= 0 && y < V) {
                 r.xt = E::at(tp, y);
                 r.xd = E::at(dp, y);
                 r.yok = 1;
             }
-            rec[slot_id] = r;
         }
+        rec[slot_id] = r;
+    }
+    if (kind == 2 && s < k) {
         const typename E::raw* rows[2] = {tp, dp};
         Partial out[2];
         chunk_stats<E, VEC, 2>(rows, beg, end, c, out, redd, redf, redi);
@@ -277,11 +289,10 @@ __global__ __launch_bounds__(kBlock) void k_chain_stats(
             part_d[slot_id * n_chunks + ch] = out[1];
         }
     } else {
-        if (ch == 0 && threadIdx.x == 0) rec[slot_id] = SlotRec{NAN, NAN, uni[t_row], 0};
-        const typename E::raw* rows[1] = {tp};
+        const typename E::raw* rows[1] = {kind == 1 ? dp : tp};
         Partial out[1];
         chunk_stats<E, VEC, 1>(rows, beg, end, c, out, redd, redf, redi);
-        if (threadIdx.x == 0) part_t[slot_id * n_chunks + ch] = out[0];
+        if (threadIdx.x == 0) (kind == 1 ? part_d : part_t)[slot_id * n_chunks + ch] = out[0];
     }
 }
 
@@ -971,15 +982,19 @@ static hipError_t chain_full_impl(const ChainArgs& a) {
     g.alive = n_phases > 1 ? alive : nullptr;
     for (int ph = 0; ph < n_phases; ++ph) {
         const int lo = bounds[ph], hi = bounds[ph + 1];
-        const unsigned grid1 = (unsigned)((size_t)a.B * (hi - lo) * nc);
+        // The first phase streams every sequence's rows with one row per
+        // workgroup; later phases keep a slot's two rows in one workgroup, so
+        // that half as many workgroups exit at once for decided sequences.
+        const int split = ph == 0 && n_phases > 1 ? kSplitFirstPhase : 0;
+        const unsigned grid1 = (unsigned)((size_t)a.B * (hi - lo) * nc * (split ? 2 : 1));
         if (ph == 0)
             PassTimer::launch(k_chain_stats<E, VEC>, dim3(grid1), dim3(kBlock), a.stream, tgt, dft,
                               a.tokens, a.uniforms, a.cu, a.K_max, a.V, chunk, nc, c, part_t, part_d, rec, lo,
-                              hi - lo, (int32_t*)nullptr);
+                              hi - lo, split, (int32_t*)nullptr);
         else
             hipLaunchKernelGGL((k_chain_stats<E, VEC>), dim3(grid1), dim3(kBlock), 0, a.stream, tgt,
                                dft, a.tokens, a.uniforms, a.cu, a.K_max, a.V, chunk, nc, c, part_t, part_d, rec,
-                               lo, hi - lo, alive);
+                               lo, hi - lo, split, alive);
         g.hi = hi;
         if (fused && ph == n_phases - 1) {
             hipLaunchKernelGGL((k_chain_resolve<E, VEC>), dim3((unsigned)a.B), dim3(kFusedThreads), 0,
