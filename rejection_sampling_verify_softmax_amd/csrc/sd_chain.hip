@@ -155,15 +155,15 @@ __device__ Partial chunk_stats_exact(const typename E::raw* row, int beg, int en
     return p;
 }
 
-template <class E, int NR>
-__device__ __forceinline__ void accumulate(const uint4 (&v)[NR * kU], const float (&o)[NR], float c,
+template <class E, int NR, int U>
+__device__ __forceinline__ void accumulate(const uint4 (&v)[NR * U], const float (&o)[NR], float c,
                                            float (&acc)[NR][E::kVec]) {
 #pragma unroll
-    for (int u = 0; u < kU; ++u)
+    for (int u = 0; u < U; ++u)
 #pragma unroll
         for (int r = 0; r < NR; ++r) {
             float f[E::kVec];
-            E::unpack(v[r * kU + u], f);
+            E::unpack(v[r * U + u], f);
 #pragma unroll
             for (int e = 0; e < E::kVec; ++e) acc[r][e] += fast_exp2(__builtin_fmaf(f[e], c, -o[r]));
         }
@@ -173,7 +173,7 @@ __device__ __forceinline__ void accumulate(const uint4 (&v)[NR * kU], const floa
 // integer floor(m0 * c), m0 the largest logit of the chunk's first 16-byte
 // vector (every lane reads that one cache line). A non-finite sum, a non-finite
 // reference or a sum beyond 2^64 sends that row to the exact two-pass path.
-template <class E, bool VEC, int NR>
+template <class E, bool VEC, int NR, int U = kU>
 __device__ void chunk_stats(const typename E::raw* const (&rows)[NR], int beg, int end, float c,
                             Partial (&out)[NR], double* redd, float* redf, int* redi) {
     constexpr int EV = E::kVec;
@@ -196,21 +196,21 @@ __device__ void chunk_stats(const typename E::raw* const (&rows)[NR], int beg, i
 
     int vdone = 0;
     if (VEC) {
-        constexpr int step = kBlock * kU;
+        constexpr int step = kBlock * U;
         const int full = nvec / step;
         const typename E::raw* base[NR];
 #pragma unroll
         for (int r = 0; r < NR; ++r) base[r] = rows[r] + beg;
-        pipelined_steps<NR * kU>(
+        pipelined_steps<NR * U>(
             full,
-            [&](uint4 (&buf)[NR * kU], int rd) {
+            [&](uint4 (&buf)[NR * U], int rd) {
 #pragma unroll
-                for (int u = 0; u < kU; ++u)
+                for (int u = 0; u < U; ++u)
 #pragma unroll
                     for (int r = 0; r < NR; ++r)
-                        buf[r * kU + u] = load16(base[r], rd * step + u * kBlock + threadIdx.x);
+                        buf[r * U + u] = load16(base[r], rd * step + u * kBlock + threadIdx.x);
             },
-            [&](const uint4 (&buf)[NR * kU], int) { accumulate<E, NR>(buf, o, c, acc); });
+            [&](const uint4 (&buf)[NR * U], int) { accumulate<E, NR, U>(buf, o, c, acc); });
         vdone = full * step;
     }
     // ragged tail (the whole range in the element-wise path)
@@ -239,22 +239,27 @@ __device__ void chunk_stats(const typename E::raw* const (&rows)[NR], int beg, i
     }
 }
 
-template <class E, bool VEC>
+#ifndef SD_SPLIT_UNROLL
+#define SD_SPLIT_UNROLL SD_STATS_UNROLL
+#endif
+constexpr int kSplitU = SD_SPLIT_UNROLL;
+
+template <class E, bool VEC, bool SPLIT>
 __global__ __launch_bounds__(kBlock) void k_chain_stats(
     const typename E::raw* __restrict__ tgt, const typename E::raw* __restrict__ dft,
     const int32_t* __restrict__ tok, const float* __restrict__ uni, const int32_t* __restrict__ cu,
     int K_max, int V, int chunk, int n_chunks, float c, Partial* __restrict__ part_t,
-    Partial* __restrict__ part_d, SlotRec* __restrict__ rec, int slot_lo, int slot_span, int split,
+    Partial* __restrict__ part_d, SlotRec* __restrict__ rec, int slot_lo, int slot_span,
     const int32_t* __restrict__ alive) {
     __shared__ double redd[kWavesPerBlock];
     __shared__ float redf[kWavesPerBlock];
     __shared__ int redi[kWavesPerBlock];
     const int slots = K_max + 1;
     const int ch = blockIdx.x % n_chunks;
-    // split: one row per workgroup (kind 0 the target row, kind 1 the draft
+    // SPLIT: one row per workgroup (kind 0 the target row, kind 1 the draft
     // row); else the slot's target and draft rows in one workgroup (kind 2)
-    const int kind = split ? (blockIdx.x / n_chunks) & 1 : 2;
-    const int rest = blockIdx.x / n_chunks / (split ? 2 : 1);
+    const int kind = SPLIT ? (blockIdx.x / n_chunks) & 1 : 2;
+    const int rest = blockIdx.x / n_chunks / (SPLIT ? 2 : 1);
     const int s = slot_lo + rest % slot_span;
     const int b = rest / slot_span;
     if (alive != nullptr && alive[b] == 0) return;     // decided in an earlier phase
@@ -280,7 +285,7 @@ __global__ __launch_bounds__(kBlock) void k_chain_stats(
         }
         rec[slot_id] = r;
     }
-    if (kind == 2 && s < k) {
+    if (!SPLIT && s < k) {
         const typename E::raw* rows[2] = {tp, dp};
         Partial out[2];
         chunk_stats<E, VEC, 2>(rows, beg, end, c, out, redd, redf, redi);
@@ -291,7 +296,7 @@ __global__ __launch_bounds__(kBlock) void k_chain_stats(
     } else {
         const typename E::raw* rows[1] = {kind == 1 ? dp : tp};
         Partial out[1];
-        chunk_stats<E, VEC, 1>(rows, beg, end, c, out, redd, redf, redi);
+        chunk_stats<E, VEC, 1, SPLIT ? kSplitU : kU>(rows, beg, end, c, out, redd, redf, redi);
         if (threadIdx.x == 0) (kind == 1 ? part_d : part_t)[slot_id * n_chunks + ch] = out[0];
     }
 }
@@ -985,16 +990,16 @@ static hipError_t chain_full_impl(const ChainArgs& a) {
         // The first phase streams every sequence's rows with one row per
         // workgroup; later phases keep a slot's two rows in one workgroup, so
         // that half as many workgroups exit at once for decided sequences.
-        const int split = ph == 0 && n_phases > 1 ? kSplitFirstPhase : 0;
+        const bool split = ph == 0 && n_phases > 1 && kSplitFirstPhase;
         const unsigned grid1 = (unsigned)((size_t)a.B * (hi - lo) * nc * (split ? 2 : 1));
         if (ph == 0)
-            PassTimer::launch(k_chain_stats<E, VEC>, dim3(grid1), dim3(kBlock), a.stream, tgt, dft,
-                              a.tokens, a.uniforms, a.cu, a.K_max, a.V, chunk, nc, c, part_t, part_d, rec, lo,
-                              hi - lo, split, (int32_t*)nullptr);
+            PassTimer::launch(split ? k_chain_stats<E, VEC, true> : k_chain_stats<E, VEC, false>, dim3(grid1),
+                              dim3(kBlock), a.stream, tgt, dft, a.tokens, a.uniforms, a.cu, a.K_max, a.V, chunk,
+                              nc, c, part_t, part_d, rec, lo, hi - lo, (int32_t*)nullptr);
         else
-            hipLaunchKernelGGL((k_chain_stats<E, VEC>), dim3(grid1), dim3(kBlock), 0, a.stream, tgt,
+            hipLaunchKernelGGL((k_chain_stats<E, VEC, false>), dim3(grid1), dim3(kBlock), 0, a.stream, tgt,
                                dft, a.tokens, a.uniforms, a.cu, a.K_max, a.V, chunk, nc, c, part_t, part_d, rec,
-                               lo, hi - lo, split, alive);
+                               lo, hi - lo, alive);
         g.hi = hi;
         if (fused && ph == n_phases - 1) {
             hipLaunchKernelGGL((k_chain_resolve<E, VEC>), dim3((unsigned)a.B), dim3(kFusedThreads), 0,
