@@ -272,9 +272,11 @@ def setup_greedy(torch, sd, wl):
         st["out"] = sd.verify_greedy(t, case.tokens, B=B, K_max=K, workspace=ws)
 
     rows = B * (K + 1)
+    A = sd.verify_greedy(case.target, case.tokens, B=B, K_max=K, workspace=ws)["accepted_len"].cpu()
     meta = {"workload": f"greedy chain verify B={B} K={K} V={V} bf16 (8 rotated input copies)",
             "global_batch": B, "K_max": K, "V": V, "positions_per_step": B * K,
-            "kernel": "k_argmax", "kernel_bytes": rows * V * 2, "step_bytes": rows * V * 2 + B * K * 4}
+            "kernel": "k_argmax", "kernel_bytes": rows * V * 2, "step_bytes": rows * V * 2 + B * K * 4,
+            "mean_A": float(A.float().mean())}
     return step, meta, {"leg": cpu_leg_greedy, "case": case, "state": st}
 
 
@@ -493,9 +495,12 @@ def setup_chain1(torch, sd, wl):
         st["out"] = sd.verify_chain(case.target, case.draft, case.tokens, case.uniforms, 1.0, B=1,
                                     K_max=4, workspace=ws)
 
+    A = sd.verify_chain(case.target, case.draft, case.tokens, case.uniforms, 1.0, B=1, K_max=4,
+                        workspace=ws)["accepted_len"].cpu()
     meta = {"workload": "chain verify B=1 K=4 V=1000 fp32 (latency-bound)", "global_batch": 1,
             "K_max": 4, "V": 1000, "positions_per_step": 4, "kernel": "k_chain_stats",
-            "kernel_bytes": 9 * 1000 * 4 + 16, "step_bytes": 9 * 1000 * 4 + 16 + 20}
+            "kernel_bytes": 9 * 1000 * 4 + 16, "step_bytes": 9 * 1000 * 4 + 16 + 20,
+            "mean_A": float(A.float().mean())}
     return step, meta, {"leg": cpu_leg_chain, "case": case, "state": st}
 
 
