@@ -903,7 +903,10 @@ __device__ __forceinline__ int tile_topk(const uint4 (&v)[kTileVecs], int topk, 
     uint32_t tb = s_bound[0];
 #pragma unroll
     for (int o = 1; o < kWavesPerBlock; ++o) tb = min(tb, s_bound[o]);
-    const float tf = tb == 0u ? -INFINITY : from_ordered(tb);
+    // (a bound kept to 16 bits below -inf's key decodes to a NaN: every value
+    // reaches -inf, so -inf is the bound then)
+    float tf = tb == 0u ? -INFINITY : from_ordered(tb);
+    if (tf != tf) tf = -INFINITY;
     // 3. the candidates x >= tf (NaN never), in the vectors whose maximum
     //    reaches the bound
     uint32_t vm = 0u;
@@ -1537,8 +1540,10 @@ __global__ __launch_bounds__(kShortThreads) void k_topk_short(const typename E::
     uint32_t tb = wkey[0];
 #pragma unroll
     for (int i = 1; i < kShortWaves; ++i) tb = min(tb, wkey[i]);
-    // a wave without kShortRth kept maxima: every kept token competes
-    const float t = tb == 0u ? -INFINITY : from_ordered(tb);
+    // a wave without kShortRth kept maxima: every kept token competes (and a
+    // bound kept to 16 bits below -inf's key, which decodes to a NaN, is -inf)
+    float t = tb == 0u ? -INFINITY : from_ordered(tb);
+    if (t != t) t = -INFINITY;
     // 3. the candidates (value >= t) to LDS in one pass, placed by an LDS
     // counter (their order does not matter: ranks come from the keys); the
     // count tells whether they fit. Only the vectors whose maximum reaches t

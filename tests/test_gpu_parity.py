@@ -935,6 +935,26 @@ def test_tree_walk_sampled_topk_ties_and_nonfinite():
     assert out["accepted_len"].tolist()[0] == 1 and out["status"].tolist() == [0, 2, 2]
 
 
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32])
+def test_tree_walk_sampled_topk_rows_mostly_neg_inf(dtype):
+    # rows of -inf but for 30 finite logits, top-k 50: the kept set holds the 30
+    # and 20 of the -inf entries (lowest ids); the register tile's bound sits
+    # at -inf there
+    V, N, B = 4096, 6, 4
+    g = torch.Generator(device="cuda").manual_seed(21)
+    tok = torch.tensor([[-1, 104, 117, 110, 121, -1]] * B, dtype=torch.int32, device="cuda")
+    par = torch.tensor([[-1, 0, 0, 1, 3, -1]] * B, dtype=torch.int32, device="cuda")
+    nn = torch.tensor([5] * B, dtype=torch.int32, device="cuda")
+    rows = torch.full((B, N, V), float("-inf"), device="cuda")
+    rows[:, :, 100:130] = torch.randn(B, N, 30, generator=g, device="cuda")
+    rows[:, :, 104] += 2.0
+    rows = rows.to(dtype)
+    tree = {"token": tok, "parent": par, "n_nodes": nn}
+    u = wl.grid_uniforms((B, N), g, "cuda")
+    out, ref = _sampled_walk_check(tree, rows, 1.0, u, top_k=50)
+    assert (out["status"] == 0).all()
+
+
 def test_tree_walk_sampled_T0_is_the_argmax_walk():
     case = wl.gen_tree(device="cuda", seed=77, B=16, K=16, V=32000, N=64)
     tree = sd.build_tree(case.marginals, 64)
