@@ -352,6 +352,37 @@ def test_calls_on_a_side_stream_match_the_current_stream():
             assert torch.equal(side[k][kk], ref[k][kk]), (k, kk)
 
 
+def test_binding_rejects_unfit_output_tensors():
+    # outputs passed in are checked before any launch: a tensor too small, of
+    # the wrong type, on the host or not contiguous raises, and the outputs
+    # that were given are left as they were
+    case = wl.gen_chain_small(device="cuda")
+    good = sd.verify_chain(case.target, case.draft, case.tokens, case.uniforms, 1.0, B=1, K_max=4)
+    A = torch.full((1,), -7, dtype=torch.int32, device="cuda")
+    bad = [{"accepted_len": torch.empty(0, dtype=torch.int32, device="cuda")},
+           {"accepted_len": torch.empty(1, dtype=torch.int64, device="cuda")},
+           {"accepted_len": torch.empty(1, dtype=torch.int32)},
+           {"next_token": torch.empty(2, 2, dtype=torch.int32, device="cuda").t()[0]},
+           {"accepted_len": A, "probs": torch.empty(3, 2, dtype=torch.float32, device="cuda")}]
+    for out in bad:
+        with pytest.raises((ValueError, TypeError)):
+            sd.verify_chain(case.target, case.draft, case.tokens, case.uniforms, 1.0, B=1, K_max=4, out=out,
+                            want_probs=True)
+    torch.cuda.synchronize()
+    assert int(A[0]) == -7
+    sel = sd.select_len(case.conf if hasattr(case, "conf") else torch.rand(1, 4, device="cuda"), 0.1)
+    with pytest.raises(ValueError):
+        sd.select_len(torch.rand(4, 8, device="cuda"), 0.1, out={"cu": torch.empty(4, dtype=torch.int32,
+                                                                                       device="cuda")})
+    tree_out = {"path": torch.empty(1, 2, dtype=torch.int32, device="cuda")}
+    tc = wl.gen_tree(device="cuda", seed=3, B=2, K=2, V=64, N=4)
+    tree = sd.build_tree(tc.marginals, 4)
+    target = tc.target_for_depths(tree["depth"], tree["n_nodes"])
+    with pytest.raises(ValueError):
+        sd.verify_tree(target, tree, out=tree_out)
+    assert good["accepted_len"].numel() == 1 and int(sel["cu"][0]) == 0
+
+
 def test_chain_run_twice_bit_identical():
     case = wl.gen_base_noise_chain(9, B=16, K=6, V=50000, base_sigma=2.0, noise_sigma=0.7,
                                    temperature=1.0, dtype="bf16", device="cuda")
