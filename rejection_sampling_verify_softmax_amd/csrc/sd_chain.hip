@@ -73,7 +73,7 @@ struct ChainDesc {
     int32_t d_row;      // draft row of the residual; -1 when q counts as 0
     float u;            // the final uniform
     float O_p, O_q;     // row references (integers)
-    float pad;
+    int32_t slot;       // extra token: the slot index (b * (K_max + 1) + kc) of its row; else -1
     double S_p, S_q;    // row sums relative to the references
 };
 
@@ -575,7 +575,7 @@ __device__ int scan_piece(const typename E::raw* tp, const typename E::raw* dp, 
 template <class E, bool VEC, bool Q>
 __device__ int sample_from_pieces(const double* S, int npieces, const typename E::raw* tp,
                                   const typename E::raw* dp, int V, const WeightFn& wf, double u,
-                                  double* total_out) {
+                                  double* total_out, int p_base = 0) {
     constexpr int EV = E::kVec;
     const int lane = threadIdx.x & (kWave - 1);
     const int per = (npieces + kWave - 1) / kWave;
@@ -613,7 +613,43 @@ __device__ int sample_from_pieces(const double* S, int npieces, const typename E
         piece = (int)wave_max_u32((uint32_t)(lastpos + 1)) - 1;   // rounding left the point past the end
         take_last = true;
     }
-    return scan_piece<E, VEC, Q>(tp, dp, piece * kWave * EV, V, wf, before, target, take_last);
+    return scan_piece<E, VEC, Q>(tp, dp, (p_base + piece) * kWave * EV, V, wf, before, target, take_last);
+}
+
+// The chunk of an extra-token row that holds its draw, from the row's chunk
+// partials: the chunk masses relative to the row reference O (as the row's
+// sum combines them), their running sum in chunk order, and the first chunk
+// whose running mass passes u times the total. *frac gets the draw's place
+// within that chunk (in [0, 1]); -1 when no chunk has mass. One wave.
+__device__ int extra_chunk(const Partial* p, int n_chunks, float O, double u, double* frac) {
+    const int lane = threadIdx.x & (kWave - 1);
+    auto mass = [&](int i) -> double {
+        if (i >= n_chunks) return 0.0;
+        const Partial q = p[i];
+        return q.S > 0.0 ? ldexp(q.S, (int)fmaxf(q.o - O, -4096.f)) : 0.0;
+    };
+    double total = 0.0;
+    for (int base = 0; base < n_chunks; base += kWave) total += wave_sum(mass(base + lane));
+    const double target = u * total;
+    double run = 0.0;
+    int last = -1;
+    for (int base = 0; base < n_chunks; base += kWave) {
+        const double m = mass(base + lane);
+        const double incl = wave_incl_scan_f64(m);
+        const double start = run + (incl - m);
+        const unsigned long long hit = __ballot(m > 0.0 && start + m > target);
+        if (hit) {
+            const int L = __ffsll(hit) - 1;
+            const double ms = __shfl(m, L, kWave), st = __shfl(start, L, kWave);
+            const double f = (target - st) / ms;
+            *frac = f < 0.0 ? 0.0 : (f > 1.0 ? 1.0 : f);
+            return base + L;
+        }
+        last = max(last, (int)wave_max_u32((uint32_t)(m > 0.0 ? base + lane + 1 : 0)) - 1);
+        run += __shfl(incl, kWave - 1, kWave);
+    }
+    *frac = 1.0;                        // rounding left the point past the end
+    return last;
 }
 
 // Inverse CDF over the whole decision row with the piece masses computed on
@@ -664,7 +700,7 @@ struct DecideArgs {
     const SlotRec* rec;
     const float* uni;
     const int32_t* cu;
-    int K_max, V, n_chunks;
+    int K_max, V, n_chunks, chunk;
     float c;
     int32_t* A_out;
     float* probs_out;
@@ -752,7 +788,7 @@ __device__ __forceinline__ bool decide_sequence(const DecideArgs& g, int b, Chai
     // streamed (and is a lane), else from the uniforms (a window rejected
     // before its later slots were streamed, or a 64-position window)
     d.u = (kc < ns && kc < kWave) ? __shfl(u_lane, kc, kWave) : uni[d0 + b + kc];
-    d.pad = 0.f;
+    d.slot = -1;
     if (A < kc) {
         const float Op = __shfl(rp.O, A, kWave);
         const double Sp = __shfl(rp.S, A, kWave);
@@ -779,6 +815,7 @@ __device__ __forceinline__ bool decide_sequence(const DecideArgs& g, int b, Chai
         }
         d.mode = rb.valid ? kModeExtra : kModeNone;
         if (!rb.valid) mine |= 2;
+        d.slot = (int32_t)(slot0 + kc);
         d.t_row = d0 + b + kc;
         d.d_row = -1;
         d.O_p = rb.O;
@@ -874,16 +911,29 @@ __global__ __launch_bounds__(kFusedThreads) void k_chain_resolve(
     constexpr int EV = E::kVec;
     __shared__ ChainDesc sdesc;
     __shared__ double spieces[kLdsPieces];
+    __shared__ int s_xc;
+    __shared__ double s_frac;
     const int b = blockIdx.x;
     const int lane = threadIdx.x & (kWave - 1);
     if (threadIdx.x < kWave) {
         ChainDesc d;
         if (alive_in && g.alive[b] == 0) d = desc[b];   // decided in an earlier phase
         else decide_sequence(g, b, d);                  // the window ends here: always decides
-        if (lane == 0) sdesc = d;
+        // an extra token is drawn from p of one row: the row's chunk partials
+        // say which chunk holds the draw, and only that chunk is weighed
+        int xc = -1;
+        double fr = 0.0;
+        if (d.mode == kModeExtra)
+            xc = extra_chunk(g.part_t + (int64_t)d.slot * g.n_chunks, g.n_chunks, d.O_p, (double)d.u, &fr);
+        if (lane == 0) {
+            sdesc = d;
+            s_xc = xc;
+            s_frac = fr;
+        }
     }
     __syncthreads();
     const ChainDesc d = sdesc;
+    const int xc = s_xc;
     if (d.mode == kModeNone) {
         if (threadIdx.x == 0) {
             next_out[b] = -1;
@@ -897,15 +947,33 @@ __global__ __launch_bounds__(kFusedThreads) void k_chain_resolve(
     const WeightFn wf = weight_fn(d, g.c, false);
     const typename E::raw* dp = wf.has_q ? dft + (int64_t)d.d_row * V : tp;
     double* pieces = npieces <= kLdsPieces ? spieces : piece_ws + (int64_t)b * npieces;
-    if (wf.has_q) mass_pass<E, VEC, kFusedThreads, true>(tp, dp, 0, V, wf, pieces, npieces);
-    else mass_pass<E, VEC, kFusedThreads, false>(tp, dp, 0, V, wf, pieces, npieces);
+    if (xc >= 0) {
+        // (a chunk is a whole number of pieces)
+        const int beg = xc * g.chunk;
+        const int end = min(V, beg + g.chunk);
+        mass_pass<E, VEC, kFusedThreads, false>(tp, dp, beg, end, wf, pieces, (end + kWave * EV - 1) / (kWave * EV));
+    } else if (wf.has_q) {
+        mass_pass<E, VEC, kFusedThreads, true>(tp, dp, 0, V, wf, pieces, npieces);
+    } else {
+        mass_pass<E, VEC, kFusedThreads, false>(tp, dp, 0, V, wf, pieces, npieces);
+    }
     __syncthreads();
     if (threadIdx.x >= kWave) return;
     double total = 0.0;
-    int next = wf.has_q ? sample_from_pieces<E, VEC, true>(pieces, npieces, tp, dp, V, wf, (double)d.u, &total)
+    int next;
+    if (xc >= 0) {
+        const int p0 = xc * g.chunk / (kWave * EV);
+        const int p1 = (min(V, (xc + 1) * g.chunk) + kWave * EV - 1) / (kWave * EV);
+        next = sample_from_pieces<E, VEC, false>(pieces + p0, p1 - p0, tp, dp, V, wf, s_frac, &total, p0);
+        // no fp32 weight in the chunk (its mass is below fp32's range): the
+        // whole row, one wave
+        if (next < 0) next = sample_by_rescan<E>(tp, V, wf, (double)d.u);
+    } else {
+        next = wf.has_q ? sample_from_pieces<E, VEC, true>(pieces, npieces, tp, dp, V, wf, (double)d.u, &total)
                         : sample_from_pieces<E, VEC, false>(pieces, npieces, tp, dp, V, wf, (double)d.u, &total);
-    if (d.mode == kModeResidual && !(total > 0.0))
-        next = sample_by_rescan<E>(tp, V, weight_fn(d, g.c, true), (double)d.u);
+        if (d.mode == kModeResidual && !(total > 0.0))
+            next = sample_by_rescan<E>(tp, V, weight_fn(d, g.c, true), (double)d.u);
+    }
     if (lane == 0) {
         next_out[b] = next;
         if (R_out) R_out[b] = (d.mode == kModeResidual) ? (float)total : 0.f;
@@ -978,6 +1046,7 @@ static hipError_t chain_full_impl(const ChainArgs& a) {
     g.K_max = a.K_max;
     g.V = a.V;
     g.n_chunks = nc;
+    g.chunk = chunk;
     g.c = c;
     g.A_out = a.accepted_len;
     g.probs_out = a.probs_out;
