@@ -920,10 +920,11 @@ __global__ __launch_bounds__(kFusedThreads) void k_chain_resolve(
         if (alive_in && g.alive[b] == 0) d = desc[b];   // decided in an earlier phase
         else decide_sequence(g, b, d);                  // the window ends here: always decides
         // an extra token is drawn from p of one row: the row's chunk partials
-        // say which chunk holds the draw, and only that chunk is weighed
+        // say which chunk holds the draw, and only that chunk is weighed (a
+        // row of one chunk is weighed whole)
         int xc = -1;
         double fr = 0.0;
-        if (d.mode == kModeExtra)
+        if (d.mode == kModeExtra && g.n_chunks > 1)
             xc = extra_chunk(g.part_t + (int64_t)d.slot * g.n_chunks, g.n_chunks, d.O_p, (double)d.u, &fr);
         if (lane == 0) {
             sdesc = d;
