@@ -17,7 +17,7 @@ that oracle run (verify lengths of every sequence, committed results of the
 sampled sequences; bit-exact outside the oracle's margin cases).
 
 Other workloads (--workload adaptive_table|greedy|topk|tree|tree_sampled|tree_sampled_topk|chain1|kv|rerank|
-readceiling_66m|readceiling_523m|readceiling_523m_64k|readceiling_1g)
+readceiling_66m|readceiling_523m|readceiling_523m_64k|readceiling_523m_rows|readceiling_1g)
 measure the other kernels
 for the design notes; their inputs are rotated across copies so that the
 working set exceeds the 256 MB last-level cache.
@@ -544,12 +544,37 @@ def setup_readceiling_523m_64k(torch, sd, wl):
     return setup_readceiling(torch, sd, wl, 523032028 // 16 * 16, 2, chunk=65536)
 
 
+def setup_readceiling_523m_rows(torch, sd, wl):
+    # the adaptive step's first launch as a plain read: its 2039 bf16 rows of
+    # V = 128256 (a 256,512-byte pitch), one workgroup per 64 KB chunk of a row
+    rows, V, copies = 2039, 128256, 2
+    bufs = [torch.empty(rows, V, dtype=torch.bfloat16, device="cuda").fill_(1.0) for _ in range(copies)]
+    n_chunks = -(-V * 2 // 65536)
+    sink = torch.empty(rows * n_chunks, dtype=torch.int32, device="cuda")
+    st = {"i": 0}
+
+    def step(ev=None):
+        if ev is not None:
+            sd.time_next_stream_pass(*ev)
+        sd.stream_read_rows(bufs[st["i"] % copies], 65536, sink)
+        st["i"] += 1
+
+    nbytes = rows * V * 2
+    meta = {"workload": (f"plain streaming read of {rows} bf16 rows of V = {V} ({nbytes / 1e6:.1f} MB, "
+                         f"{copies} rotated copies), one workgroup x 256 threads per 64 KB chunk of a row "
+                         f"({rows * n_chunks} workgroups, the row passes' grid), 16-byte non-temporal loads"),
+            "positions_per_step": 0, "kernel": "k_stream_read_rows", "kernel_bytes": nbytes,
+            "step_bytes": nbytes}
+    return step, meta, None
+
+
 WORKLOADS = {"adaptive": setup_adaptive, "adaptive_table": setup_adaptive_table, "greedy": setup_greedy, "topk": setup_topk,
              "tree": setup_tree, "tree_sampled": setup_tree_sampled,
              "tree_sampled_topk": setup_tree_sampled_topk, "chain1": setup_chain1,
              "kv": setup_kv, "rerank": setup_rerank, "readceiling_66m": setup_readceiling_66m,
              "readceiling_1g": setup_readceiling_1g, "readceiling_523m": setup_readceiling_523m,
-             "readceiling_523m_64k": setup_readceiling_523m_64k}
+             "readceiling_523m_64k": setup_readceiling_523m_64k,
+             "readceiling_523m_rows": setup_readceiling_523m_rows}
 
 
 # --------------------------------------------------------------------------

@@ -432,6 +432,21 @@ sd_status_t sd_stream_read(const void* data, size_t bytes, uint32_t* sink, int32
                            void* hip_stream);
 
 /*
+ * Measurement support: the same plain read over a row-major matrix of n_rows
+ * rows of row_bytes bytes each (row r starts at data + r * row_bytes; both a
+ * multiple of 16, data 16-byte aligned), each row split into chunks of
+ * chunk_bytes (a multiple of 16; the last chunk of a row is shorter), one
+ * 256-thread workgroup per (row, chunk): the grid the row passes use. sink
+ * [n_rows * ceil(row_bytes / chunk_bytes)] receives each workgroup's fold
+ * (the XOR of every 32-bit word of its chunk), row-major. SD_EINVAL for NULL
+ * pointers, misalignment, zero or non-multiple-of-16 sizes, row_bytes above
+ * 2^32 or more than 2^24 workgroups. Takes the events of
+ * sd_time_next_stream_pass.
+ */
+sd_status_t sd_stream_read_rows(const void* data, size_t row_bytes, int32_t n_rows, size_t chunk_bytes,
+                                uint32_t* sink, void* hip_stream);
+
+/*
  * Measurement support. The next sd_verify_chain, sd_verify_chain_capped,
  * sd_verify_greedy, sd_build_tree, sd_verify_tree, sd_compact_kv or
  * sd_rerank_tree call made by the calling host thread binds `start_event` and

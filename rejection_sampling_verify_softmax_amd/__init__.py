@@ -84,6 +84,8 @@ def _load():
     lib.sd_verify_chain_noalloc.restype = ctypes.c_int
     lib.sd_stream_read.argtypes = [P, Z, P, I, P]
     lib.sd_stream_read.restype = ctypes.c_int
+    lib.sd_stream_read_rows.argtypes = [P, Z, I, Z, P, P]
+    lib.sd_stream_read_rows.restype = ctypes.c_int
     lib.sd_time_next_stream_pass.argtypes = [P, P]
     lib.sd_time_next_stream_pass.restype = ctypes.c_int
     _lib = lib
@@ -168,6 +170,21 @@ def stream_read(data: torch.Tensor, sink: torch.Tensor, n_blocks: int, stream=No
         raise ValueError("sink needs one word per workgroup")
     _raise(_load().sd_stream_read(_ptr(data), nbytes, _ptr(sink), int(n_blocks),
                                   _stream(stream)), "sd_stream_read")
+
+
+def stream_read_rows(data: torch.Tensor, chunk_bytes: int, sink: torch.Tensor, stream=None):
+    """sd_stream_read_rows: a plain read of the rows of `data` (2-D, row-major),
+    one workgroup per (row, chunk of chunk_bytes): the row passes' grid."""
+    _check(data, "data")
+    _check(sink, "sink", torch.int32, data.device)
+    if data.dim() != 2:
+        raise ValueError("data must be 2-D (rows)")
+    row_bytes = data.shape[1] * data.element_size()
+    chunks = -(-row_bytes // int(chunk_bytes))
+    if sink.numel() < data.shape[0] * chunks:
+        raise ValueError("sink needs one word per (row, chunk)")
+    _raise(_load().sd_stream_read_rows(_ptr(data), row_bytes, int(data.shape[0]), int(chunk_bytes),
+                                       _ptr(sink), _stream(stream)), "sd_stream_read_rows")
 
 
 def workspace_bytes(op: int, B: int, K_max: int = 0, V: int = 1, top_k: int = 0, N: int = 2) -> int:

@@ -369,6 +369,17 @@ sd_status_t sd_stream_read(const void* data, size_t bytes, uint32_t* sink, int32
                                            static_cast<hipStream_t>(hip_stream)));
 }
 
+sd_status_t sd_stream_read_rows(const void* data, size_t row_bytes, int32_t n_rows, size_t chunk_bytes,
+                                uint32_t* sink, void* hip_stream) {
+    if (!data || !sink || misaligned(data) || row_bytes == 0 || row_bytes % 16 != 0 || chunk_bytes == 0 ||
+        chunk_bytes % 16 != 0 || n_rows < 1 || row_bytes > ((size_t)1 << 32))
+        return SD_EINVAL;
+    const size_t chunks = (row_bytes + chunk_bytes - 1) / chunk_bytes;
+    if ((size_t)n_rows * chunks > ((size_t)1 << 24)) return SD_EINVAL;
+    return from_hip(sd::launch_stream_read_rows(data, (int64_t)row_bytes, n_rows, (int64_t)chunk_bytes, sink,
+                                                static_cast<hipStream_t>(hip_stream)));
+}
+
 sd_status_t sd_compact_kv(void* kv, int64_t row_bytes, int64_t n_rows, const int64_t* row_base,
                           const int32_t* path_nodes, const int32_t* accepted_len, int32_t B,
                           int32_t N, void* hip_stream) {

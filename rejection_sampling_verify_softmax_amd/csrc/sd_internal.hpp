@@ -124,6 +124,8 @@ hipError_t launch_expand_tree(int32_t* cand_parent, int32_t* cand_token, float* 
                               int B, int M, int W, int C, hipStream_t stream);
 hipError_t launch_stream_read(const void* data, int64_t bytes, uint32_t* sink, int n_blocks,
                               hipStream_t stream);
+hipError_t launch_stream_read_rows(const void* data, int64_t row_bytes, int n_rows, int64_t chunk_bytes,
+                                   uint32_t* sink, hipStream_t stream);
 hipError_t launch_select_len(const float* conf, int B, int K_max, float cost, const float* table,
                              int32_t* k_sel, float* adv, int32_t* cu_sel, hipStream_t stream);
 

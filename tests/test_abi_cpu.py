@@ -274,3 +274,26 @@ def test_expand_tree_rejects_invalid_arguments(L):
     assert ex(first=None) == 1
     assert ex(kids=None) == 1
     assert ex(out=None) == 1
+
+
+def test_stream_reads_reject_invalid_arguments(L):
+    v, z = ctypes.c_void_p, ctypes.c_size_t
+    one, odd = v(16), v(18)
+    assert L.sd_stream_read(None, z(1024), one, 4, None) == 1
+    assert L.sd_stream_read(odd, z(1024), one, 4, None) == 1
+    assert L.sd_stream_read(one, z(1000), one, 4, None) == 1          # not a multiple of 16
+    assert L.sd_stream_read(one, z(1024), None, 4, None) == 1
+    assert L.sd_stream_read(one, z(1024), one, 0, None) == 1
+
+    def rows(data=one, row_bytes=4096, n_rows=8, chunk=1024, sink=one):
+        return L.sd_stream_read_rows(data, z(row_bytes), n_rows, z(chunk), sink, None)
+    assert rows(data=None) == 1
+    assert rows(data=odd) == 1
+    assert rows(sink=None) == 1
+    assert rows(row_bytes=0) == 1
+    assert rows(row_bytes=4100) == 1
+    assert rows(chunk=0) == 1
+    assert rows(chunk=1000) == 1
+    assert rows(n_rows=0) == 1
+    assert rows(row_bytes=(1 << 32) + 16) == 1
+    assert rows(row_bytes=1 << 20, n_rows=1 << 16, chunk=16) == 1    # more than 2^24 workgroups
