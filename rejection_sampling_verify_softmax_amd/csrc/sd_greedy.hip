@@ -173,14 +173,29 @@ __global__ __launch_bounds__(kBlock) void k_argmax(const typename E::raw* __rest
     }
 }
 
+// The row's argmax from its chunk partials, in chunk order. The first
+// kArgRegChunks partials are loaded together, without branches (an index past
+// the row's chunks reads its last chunk again, and that copy is ignored), so
+// that a row of up to that many chunks costs one round trip; longer rows
+// continue one partial at a time.
+constexpr int kArgRegChunks = 8;
 __device__ int combine_arg(const ArgPartial* p, int n_chunks) {
+    ArgPartial q[kArgRegChunks];
+#pragma unroll
+    for (int i = 0; i < kArgRegChunks; ++i) q[i] = p[i < n_chunks ? i : n_chunks - 1];
     float bv = -INFINITY;
     int bi = kNone;
-    for (int i = 0; i < n_chunks; ++i) {
-        const ArgPartial q = p[i];
-        if (arg_better(q.v, q.i, bv, bi)) {
-            bv = q.v;
-            bi = q.i;
+#pragma unroll
+    for (int i = 0; i < kArgRegChunks; ++i)
+        if (i < n_chunks && arg_better(q[i].v, q[i].i, bv, bi)) {
+            bv = q[i].v;
+            bi = q[i].i;
+        }
+    for (int i = kArgRegChunks; i < n_chunks; ++i) {
+        const ArgPartial t = p[i];
+        if (arg_better(t.v, t.i, bv, bi)) {
+            bv = t.v;
+            bi = t.i;
         }
     }
     return bi == kNone ? -1 : bi;
@@ -199,8 +214,10 @@ __global__ __launch_bounds__(kWave) void k_greedy_decide(
     const int64_t slot0 = (int64_t)b * slots;
     bool acc = true;
     int st = 0, g = -1;
+    // lane s <= k combines slot s's argmax (slot k: the extra row), all in
+    // one round of loads with the tokens
+    if (lane <= k) g = combine_arg(part + (slot0 + lane) * n_chunks, n_chunks);
     if (lane < k) {
-        g = combine_arg(part + (slot0 + lane) * n_chunks, n_chunks);
         const int y = tok[d0 + lane];
         const bool yok = (y >= 0 && y < V);
         acc = yok && g >= 0 && y == g;
@@ -213,12 +230,9 @@ __global__ __launch_bounds__(kWave) void k_greedy_decide(
     int mine = (lane < kc && lane <= A) ? st : 0;
 #pragma unroll
     for (int o = kWave / 2; o > 0; o >>= 1) mine |= __shfl_xor(mine, o, kWave);
-    int next;
-    if (A < kc) {
-        next = __shfl(g, A, kWave);
-    } else {
-        next = combine_arg(part + (slot0 + kc) * n_chunks, n_chunks);
-    }
+    // A <= kc <= k: the correction is the argmax at A, and after a full
+    // accept the extra token is slot kc's
+    int next = A < kWave ? __shfl(g, A, kWave) : combine_arg(part + (slot0 + A) * n_chunks, n_chunks);
     if (next < 0) mine |= 2;
     if (lane == 0) {
         A_out[b] = A;
