@@ -98,6 +98,33 @@ def test_chain_large_batch_all_sequences(dtype, V, T, B, K):
     assert (A < K).any() and (A == K).any()
 
 
+def test_chain_extra_token_in_every_chunk():
+    # drafts equal to the targets: every position is accepted and every
+    # sequence draws its extra token from p of its last row, whose chunk the
+    # last launch finds from the row's chunk partials; V spans four 32K-token
+    # chunks (the last one short) and the uniforms a grid, so the draws land
+    # in every chunk, in the phased and the one-pass launches
+    B, K, V = 256, 2, 3 * 32768 + 1000
+    _say(f"chain extra token across chunks B={B} K={K} V={V} bf16")
+    g = torch.Generator(device="cuda").manual_seed(41)
+    target = (torch.randn(B * (K + 1), V, generator=g, device="cuda") * 2.0).to(torch.bfloat16)
+    rows = torch.arange(B * (K + 1), device="cuda").view(B, K + 1)[:, :K].reshape(-1)
+    draft = target[rows].contiguous()
+    tokens = torch.randint(0, V, (B * K,), generator=g, device="cuda", dtype=torch.int32)
+    uniforms = wl.grid_uniforms((B * (K + 1),), g, "cuda")
+    case = wl.ChainCase(B=B, K_max=K, V=V, temperature=1.0, top_k=0, target=target, draft=draft,
+                        tokens=tokens, uniforms=uniforms)
+    one = run_chain(case)
+    ph = run_chain(case, probs=False)
+    for key in ("accepted_len", "next_token", "status", "resid"):
+        assert torch.equal(one[key], ph[key]), key
+    assert (one["accepted_len"].cpu().numpy() == K).all()
+    info = compare_chain(one, oracle_chain(case))
+    chunks = np.bincount(one["next_token"].cpu().numpy() // 32768, minlength=4)
+    _say(f"  {info}, draws per chunk {chunks.tolist()}")
+    assert (chunks > 0).all()
+
+
 def test_chain_phased_ragged():
     lengths = [0, 3, 1, 5, 0, 2, 8, 4, 1, 0, 6, 7, 8, 8, 2, 2, 3, 8, 1, 5]
     V = 100000
