@@ -51,8 +51,7 @@ __global__ __launch_bounds__(kBlock) void k_argmax(const typename E::raw* __rest
                                                    const int32_t* __restrict__ aux, int slots,
                                                    int K_max, int V, int chunk, int n_chunks,
                                                    ArgPartial* __restrict__ out) {
-    __shared__ float sv[kWavesPerBlock];
-    __shared__ int si[kWavesPerBlock];
+    __shared__ unsigned long long skey[kWavesPerBlock];
     constexpr int EV = E::kVec;
     constexpr int U = kArgUnroll;
     const int ch = blockIdx.x % n_chunks;
@@ -142,33 +141,29 @@ __global__ __launch_bounds__(kBlock) void k_argmax(const typename E::raw* __rest
         }
         consider(f, vi);
     }
-    // wave then block reduction of (value desc, index asc)
-#pragma unroll
-    for (int o = kWave / 2; o > 0; o >>= 1) {
-        const float ov = __shfl_xor(best, o, kWave);
-        const int oi = __shfl_xor(bidx, o, kWave);
-        if (arg_better(ov, oi, best, bidx)) {
-            best = ov;
-            bidx = oi;
-        }
+    // wave then block reduction of (value desc, index asc) as one 64-bit key,
+    // larger is better (0: no value), on DPP row operations
+    uint32_t khi = 0u, klo = 0u;
+    if (bidx != kNone) {
+        const uint32_t u = __float_as_uint(best == 0.f ? 0.f : best);
+        khi = (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+        klo = 0xffffffffu - (uint32_t)bidx;
     }
-    const int w = threadIdx.x / kWave;
-    if ((threadIdx.x & (kWave - 1)) == 0) {
-        sv[w] = best;
-        si[w] = bidx;
-    }
+    wave_max_key64(khi, klo);
+    if ((threadIdx.x & (kWave - 1)) == 0) skey[threadIdx.x / kWave] = ((unsigned long long)khi << 32) | klo;
     __syncthreads();
     if (threadIdx.x == 0) {
-        float bv = sv[0];
-        int bi = si[0];
-        for (int i = 1; i < kWavesPerBlock; ++i)
-            if (arg_better(sv[i], si[i], bv, bi)) {
-                bv = sv[i];
-                bi = si[i];
-            }
+        unsigned long long k = skey[0];
+#pragma unroll
+        for (int i = 1; i < kWavesPerBlock; ++i) k = skey[i] > k ? skey[i] : k;
         ArgPartial p;
-        p.v = bv;
-        p.i = bi;
+        p.v = -INFINITY;
+        p.i = kNone;
+        if (k != 0ull) {
+            const uint32_t h = (uint32_t)(k >> 32);
+            p.v = __uint_as_float((h & 0x80000000u) ? (h & 0x7fffffffu) : ~h);
+            p.i = (int32_t)(0xffffffffu - (uint32_t)k);
+        }
         out[((int64_t)b * slots + s) * n_chunks + ch] = p;
     }
 }

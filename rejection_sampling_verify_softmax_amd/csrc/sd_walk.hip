@@ -85,28 +85,6 @@ __device__ __forceinline__ float vec_weight(const uint4& q, float c, float mc) {
     return s;
 }
 
-// The wave's largest (hi, lo) pair, compared as one 64-bit key, returned to
-// every lane: row_shr steps within each row of 16, then the last lanes of the
-// earlier rows, then lane 63 read back.
-template <int CTRL, int ROWS>
-__device__ __forceinline__ void key64_step(uint32_t& hi, uint32_t& lo) {
-    const uint32_t h = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)hi, CTRL, ROWS, 0xf, false);
-    const uint32_t l = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)lo, CTRL, ROWS, 0xf, false);
-    const bool take = h > hi || (h == hi && l > lo);
-    hi = take ? h : hi;
-    lo = take ? l : lo;
-}
-__device__ __forceinline__ void wave_max_key64(uint32_t& hi, uint32_t& lo) {
-    key64_step<0x111, 0xf>(hi, lo);
-    key64_step<0x112, 0xf>(hi, lo);
-    key64_step<0x114, 0xf>(hi, lo);
-    key64_step<0x118, 0xf>(hi, lo);
-    key64_step<0x142, 0xa>(hi, lo);
-    key64_step<0x143, 0xc>(hi, lo);
-    hi = __builtin_amdgcn_readlane(hi, kWave - 1);
-    lo = __builtin_amdgcn_readlane(lo, kWave - 1);
-}
-
 __device__ __forceinline__ bool idx_better(float v, int i, float bv, int bi) {
     // (value desc, index asc); an empty candidate never wins
     if (i == kNoIdx) return false;
