@@ -24,7 +24,8 @@
 //   4. k_chain_sample one wave per sequence: prefix over the piece masses, then
 //      one piece scan for the final token.
 // A large batch runs 2-4 of the last phase as one launch, k_chain_resolve,
-// one workgroup per sequence. Phases: the positions are streamed in slot
+// one workgroup per sequence; there an extra token's row is weighed only in
+// the chunk that the row's chunk partials show to hold the draw. Phases: the positions are streamed in slot
 // ranges (1 and 2 per range); a sequence rejected in an early range streams
 // none of its later rows.
 #include "sd_device.hpp"
